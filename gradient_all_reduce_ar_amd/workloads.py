@@ -1,0 +1,77 @@
+"""Seeded synthetic inputs for the all-reduce workloads.
+
+This module only draws numbers: it holds none of the all-reduce arithmetic, so
+both the GPU library's tests and the CPU oracle can take their inputs from it.
+
+Workloads (shapes from "Chapter 7. Data-center networks", section 7.2.1,
+which uses the fp32 [12288, 4096] FFN gate-projection gradient of Qwen3-8B,
+192 MiB per rank; values are synthetic, no gradients or weights are used):
+
+  uniform  : x_r ~ U[-1, 1) fp32 from default_rng([seed, r])
+  normal   : x_r ~ N(0, sigma) fp32 from default_rng([seed, r]); for bf16 the
+             fp32 draw is rounded to bf16 by torch's conversion
+  bucketed : 300 tensors whose byte sizes are lognormal (median 256 KiB),
+             values N(0, 1e-3) per (rank, tensor), bf16
+"""
+import numpy as np
+
+GATE_PROJ_ELEMS = 12288 * 4096  # 50,331,648 fp32 elements = 192 MiB
+BF16_192MIB_ELEMS = 2 * GATE_PROJ_ELEMS  # 100,663,296 bf16 elements = 192 MiB
+
+
+def _to_bf16_bits(x):
+    """fp32 numpy array -> uint16 array of bf16 bits (torch's conversion)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def uniform_rank(r, count, seed=0):
+    rng = np.random.default_rng([seed, r])
+    return (rng.random(count, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)).astype(np.float32)
+
+
+def normal_rank(r, count, seed=0, sigma=1e-3, dtype="fp32"):
+    rng = np.random.default_rng([seed, r])
+    x = rng.standard_normal(count, dtype=np.float32) * np.float32(sigma)
+    return x if dtype == "fp32" else _to_bf16_bits(x)
+
+
+def uniform_inputs(nranks, count, seed=0, dtype="fp32"):
+    xs = [uniform_rank(r, count, seed) for r in range(nranks)]
+    return xs if dtype == "fp32" else [_to_bf16_bits(x) for x in xs]
+
+
+def normal_inputs(nranks, count, seed=0, sigma=1e-3, dtype="fp32"):
+    return [normal_rank(r, count, seed, sigma, dtype) for r in range(nranks)]
+
+
+def integer_inputs(nranks, count, seed=0, lo=-8, hi=8, dtype="fp32"):
+    """Small integers (exactly representable partial sums for small N)."""
+    xs = []
+    for r in range(nranks):
+        rng = np.random.default_rng([seed, r, 17])
+        xs.append(rng.integers(lo, hi, count).astype(np.float32))
+    return xs if dtype == "fp32" else [_to_bf16_bits(x) for x in xs]
+
+
+def bucketed_tensor_sizes(ntensors=300, seed=7, median_bytes=262144, sigma=2.0,
+                          min_bytes=512, max_bytes=64 << 20, elem_bytes=2):
+    """Element counts of the gradient tensors of one rank.
+
+    Byte sizes are lognormal(ln median, sigma), clipped to [min, max], rounded
+    to whole elements; the largest tensor is then set to exactly max_bytes.
+    """
+    rng = np.random.default_rng(seed)
+    b = rng.lognormal(np.log(median_bytes), sigma, ntensors)
+    b = np.clip(b, min_bytes, max_bytes)
+    counts = np.maximum(1, np.round(b / elem_bytes)).astype(np.int64)
+    counts[int(np.argmax(counts))] = max_bytes // elem_bytes
+    return counts
+
+
+def bucketed_tensor_values(r, t, count, seed=0, sigma=1e-3, dtype="bf16"):
+    rng = np.random.default_rng([seed, r, t])
+    x = rng.standard_normal(int(count), dtype=np.float32) * np.float32(sigma)
+    return x if dtype == "fp32" else _to_bf16_bits(x)

@@ -1,0 +1,94 @@
+"""Closed-form summation orders of the schedules, element by element.
+
+Independent of the oracle's simulation: these folds state, per element, the
+sum that each schedule produces, as derived from the pages' index rules.  They
+are pure Python over numpy float32 scalars (each + is one binary32 add) and
+are only practical for tiny inputs.
+
+  ring          element in chunk c: ((x_c + x_{c+1}) + ...) + x_{c+N-1}
+                (ranks mod N; the chunk is first sent by rank c at
+                reduce-scatter step 0)
+  rabenseifner  the balanced pairwise tree over ranks in index order
+  hierarchical  group partial of slice k: ((x_{g,k+1} + x_{g,k+2}) + ...) + x_{g,k};
+                then, for sub-chunk j of the slice, a ring fold over groups
+                starting at group j
+"""
+import numpy as np
+
+
+def part(length, k, c):
+    return (c * length) // k, ((c + 1) * length) // k
+
+
+def chunk_of(e, length, k):
+    for c in range(k):
+        lo, hi = part(length, k, c)
+        if lo <= e < hi:
+            return c, lo
+    raise ValueError
+
+
+def ring_fold(vals, start):
+    n = len(vals)
+    acc = np.float32(vals[start % n])
+    for t in range(1, n):
+        acc = np.float32(acc + np.float32(vals[(start + t) % n]))
+    return acc
+
+
+def tree_fold(vals):
+    level = [np.float32(v) for v in vals]
+    while len(level) > 1:
+        level = [np.float32(level[2 * m] + level[2 * m + 1]) for m in range(len(level) // 2)]
+    return level[0]
+
+
+def expected_fp32(xs, schedule, group_size=1):
+    """xs: list of N float32 arrays.  Returns the float32 result array."""
+    n = len(xs)
+    count = len(xs[0])
+    out = np.zeros(count, np.float32)
+    for e in range(count):
+        col = [xs[r][e] for r in range(n)]
+        if n == 1:
+            out[e] = col[0]
+        elif schedule == "ring":
+            c, _ = chunk_of(e, count, n)
+            out[e] = ring_fold(col, c)
+        elif schedule == "rabenseifner":
+            out[e] = tree_fold(col)
+        elif schedule == "hierarchical":
+            g_sz = group_size
+            m_groups = n // g_sz
+            k, slo = chunk_of(e, count, g_sz)
+            _, shi = part(count, g_sz, k)
+            partials = []
+            for g in range(m_groups):
+                local = [col[g * g_sz + l] for l in range(g_sz)]
+                partials.append(ring_fold(local, k + 1) if g_sz > 1 else np.float32(local[0]))
+            j, _ = chunk_of(e - slo, shi - slo, m_groups)
+            out[e] = ring_fold(partials, j) if m_groups > 1 else partials[0]
+        else:
+            raise ValueError(schedule)
+    return out
+
+
+def widen(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_bf16_bits(x):
+    """Round-to-nearest-even via torch's conversion (a library routine)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def expected_bf16(bits_list, schedule, group_size=1):
+    """bf16 bits in, bf16 bits out: fp32 fold of the widened inputs, one rounding."""
+    n = len(bits_list)
+    if n == 1:
+        return np.asarray(bits_list[0], np.uint16).copy()
+    xs = [widen(b) for b in bits_list]
+    return to_bf16_bits(expected_fp32(xs, schedule, group_size))

@@ -1,0 +1,270 @@
+"""The CPU oracle against what the pages print.
+
+Every expected value here is transcribed from the pages (fixtures under
+tests/golden/, each citing its source) or is a closed form the pages state.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+MiB = 1 << 20
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _chunk_index(lo, count, n):
+    for c in range(n):
+        if (c * count) // n == lo:
+            return c
+    raise AssertionError(lo)
+
+
+# ---------------------------------------------------------------- ring ----
+
+@pytest.mark.parametrize("schedule,group", [("ring", 1), ("ring", 2), ("hierarchical", 2),
+                                            ("hierarchical", 4), ("hierarchical", 1),
+                                            ("rabenseifner", 1)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_worked_example_four_gpus(schedule, group, dtype):
+    """Scaling ML systems ch. 06, "Ring AllReduce: step-by-step trace (4 GPUs)":
+    [1,5,3,7] + [2,6,4,8] + [3,7,5,9] + [4,8,6,10] = [10,26,18,34] on every
+    rank.  All partial sums are small integers, so every schedule gets the
+    exact sum in fp32 and in bf16."""
+    rows = _rows("ring_worked_example_n4.txt")
+    ins = [np.array(r[1:], np.float32) for r in rows if r[0] == "input"]
+    want = np.array([r[1:] for r in rows if r[0] == "sum"][0], np.float32)
+    if dtype == "fp32":
+        bufs = [x.copy() for x in ins]
+    else:
+        bufs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in ins]  # exact: small ints
+    oracle.run(bufs, dtype, schedule, group_size=group)
+    for b in bufs:
+        got = b if dtype == "fp32" else (b.astype(np.uint32) << 16).view(np.float32)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_ring_send_table_n4():
+    """Primer ch. 4, Figure 4.2: the chunk each rank sends in each of the six
+    steps, (i - s) mod 4 in reduce-scatter and (i + 1 - s) mod 4 in all-gather."""
+    m = oracle.messages(4, 4, "ring")
+    for row in _rows("ring_send_table_n4.txt"):
+        src, dst, chunks = int(row[0]), int(row[1]), [int(v) for v in row[2:]]
+        for step, c in enumerate(chunks):
+            sel = (m["step"] == step) & (m["src"] == src)
+            assert sel.sum() == 1
+            j = np.flatnonzero(sel)[0]
+            assert m["dst"][j] == dst
+            assert _chunk_index(m["lo"][j], 4, 4) == c
+            assert m["kind"][j] == (oracle.REDUCE if step < 3 else oracle.COPY)
+
+
+def test_ring_count_grids_n4():
+    """Primer ch. 4, Figure 4.3: the per-(rank, chunk) count grids after each
+    of the six steps.  All-ones fp32 input makes the buffers equal the counts."""
+    rows = _rows("ring_count_grids_n4.txt")
+    grids, k = {}, None
+    for r in rows:
+        if r[0] == "step":
+            k = int(r[1])
+            grids[k] = []
+        else:
+            grids[k].append([float(v) for v in r])
+    assert sorted(grids) == list(range(7))
+    for k, grid in grids.items():
+        bufs = [np.ones(4, np.float32) for _ in range(4)]
+        oracle.run(bufs, "fp32", "ring", max_steps=k)
+        for rank in range(4):
+            np.testing.assert_array_equal(bufs[rank], np.array(grid[rank], np.float32),
+                                          err_msg=f"after step {k}, rank {rank}")
+
+
+def test_ring_ownership_after_reduce_scatter():
+    """Primer ch. 4, Figure 4.1: after the three reduce-scatter steps P0 owns
+    segment 1, P1 segment 2, P2 segment 3, P3 segment 0; section 4.2 states
+    the rule: rank i holds the complete chunk (i + 1) mod N."""
+    for n in (4, 5, 8):
+        bufs = [np.ones(n, np.float32) for _ in range(n)]
+        oracle.run(bufs, "fp32", "ring", max_steps=n - 1)
+        for i in range(n):
+            assert np.flatnonzero(bufs[i] == n).tolist() == [(i + 1) % n]
+    bufs = [np.ones(4, np.float32) for _ in range(4)]
+    oracle.run(bufs, "fp32", "ring", max_steps=3)
+    assert [int(np.flatnonzero(b == 4)[0]) for b in bufs] == [1, 2, 3, 0]
+
+
+def test_ring_partial_count_rule():
+    """Primer ch. 4, section 4.2: after reduce-scatter step s the chunk rank i
+    has just received holds the contributions of s + 2 ranks."""
+    n = 6
+    m = oracle.messages(n, n, "ring")
+    for s in range(n - 1):
+        bufs = [np.ones(n, np.float32) for _ in range(n)]
+        oracle.run(bufs, "fp32", "ring", max_steps=s + 1)
+        sel = m["step"] == s
+        for j in np.flatnonzero(sel):
+            assert bufs[m["dst"][j]][m["lo"][j]] == s + 2
+
+
+def test_ring_bytes_and_steps():
+    """Ring sends 2(N-1)/N * S per rank in 2(N-1) steps (Primer ch. 4,
+    section 4.2; Data-center networks 7.2.1).  For the 16-rank, 192 MiB
+    fp32 gradient: 360 MiB per rank, 5760 MiB in total, 30 rounds."""
+    count = 12288 * 4096
+    sent, cross, steps = oracle.stats(16, count, "fp32", "ring", group_size=8)
+    assert steps == 30
+    assert all(int(b) == 360 * MiB for b in sent)
+    assert int(sent.sum()) == 5760 * MiB
+    # contiguous placement on two servers: only 7->8 and 15->0 cross, 360 MiB
+    # each, 720 MiB in total (Data-center networks 7.2.1, problem 7.2)
+    assert cross == 720 * MiB
+    for n in (2, 3, 4, 8, 64):
+        e = n * 1000
+        sent, _, steps = oracle.stats(n, e, "fp32", "ring")
+        assert steps == 2 * (n - 1)
+        assert all(int(b) == 2 * (n - 1) * (e // n) * 4 for b in sent)
+
+
+def test_hierarchical_bytes_and_steps():
+    """Data-center networks 7.2.1: 2 servers x 8 ranks, 192 MiB: 7 + 2 + 7 = 16
+    rounds; per rank 336 MiB over the local links and 24 MiB across servers;
+    384 MiB crosses between servers in total.  Primer ch. 4 section 4.4,
+    Animation 4.3: (G-1)/G*S per intra phase and 2(M-1)/M*S/G across."""
+    count = 12288 * 4096
+    sent, cross, steps = oracle.stats(16, count, "fp32", "hierarchical", group_size=8)
+    assert steps == 16
+    assert all(int(b) == 360 * MiB for b in sent)
+    assert cross == 384 * MiB
+    m = oracle.messages(16, count, "hierarchical", group_size=8)
+    for r in range(16):
+        mine = m["src"] == r
+        crossing = (m["src"] // 8) != (m["dst"] // 8)
+        local_b = int(((m["hi"] - m["lo"])[mine & ~crossing]).sum()) * 4
+        cross_b = int(((m["hi"] - m["lo"])[mine & crossing]).sum()) * 4
+        assert local_b == 336 * MiB and cross_b == 24 * MiB
+    for n, g in ((8, 4), (16, 4), (32, 8), (64, 8)):
+        mg = n // g
+        e = n * g * 64
+        sent, _, steps = oracle.stats(n, e, "fp32", "hierarchical", group_size=g)
+        assert steps == 2 * (g - 1) + 2 * (mg - 1)
+        want = (2 * (g - 1) * (e // g) + 2 * (mg - 1) * (e // g // mg)) * 4
+        assert all(int(b) == want for b in sent)
+
+
+def test_hierarchical_slice_ownership():
+    """Primer ch. 4, Animation 4.3: the slice order is chosen so that GPU k
+    ends phase 1 owning slice k; Figure 4.8: only slice k of GPU k leaves the
+    server, and only to GPU k of the other server."""
+    n, g = 16, 8
+    e = 64
+    bufs = [np.ones(e, np.float32) for _ in range(n)]
+    oracle.run(bufs, "fp32", "hierarchical", group_size=g, max_steps=g - 1)
+    for r in range(n):
+        k = r % g
+        lo, hi = (k * e) // g, ((k + 1) * e) // g
+        assert np.all(bufs[r][lo:hi] == g)
+        assert np.all(np.delete(bufs[r], np.arange(lo, hi)) < g)
+    m = oracle.messages(n, e, "hierarchical", group_size=g)
+    crossing = (m["src"] // g) != (m["dst"] // g)
+    for j in np.flatnonzero(crossing):
+        k = m["src"][j] % g
+        assert m["dst"][j] % g == k
+        assert (k * e) // g <= m["lo"][j] and m["hi"][j] <= ((k + 1) * e) // g
+
+
+def test_rabenseifner_pairs_n8():
+    """Scaling ML systems ch. 06, "Recursive halving and doubling": round-k
+    partners i xor 2^k; (0,1)(2,3)(4,5)(6,7), then (0,2)(1,3)(4,6)(5,7), ...
+    The all-gather runs the same pairs in reverse order (Primer Animation 4.2)."""
+    m = oracle.messages(8, 64, "rabenseifner")
+    assert oracle.steps(8, "rabenseifner") == 6
+    for row in _rows("rabenseifner_pairs_n8.txt"):
+        k = int(row[1])
+        pairs = {tuple(sorted(map(int, p.split("-")))) for p in row[2:]}
+        for step in (k, 5 - k):
+            sel = m["step"] == step
+            got = {tuple(sorted((int(a), int(b)))) for a, b in zip(m["src"][sel], m["dst"][sel])}
+            assert got == pairs
+            assert sel.sum() == 8  # both directions of every pair
+
+
+def test_rabenseifner_ownership_bit_reversal():
+    """Primer ch. 4, Animation 4.2: rank i ends the reduce-scatter owning the
+    chunk whose index is i with its bits reversed (rank 1 owns chunk E, index
+    4, when N = 8); Figure 4.5: counts 1, 2, 4, 8 after each round."""
+    def bitrev(i, bits):
+        return int(format(i, f"0{bits}b")[::-1], 2) if bits else 0
+
+    for n in (2, 4, 8, 16):
+        L = n.bit_length() - 1
+        for k in range(L + 1):
+            bufs = [np.ones(n, np.float32) for _ in range(n)]
+            oracle.run(bufs, "fp32", "rabenseifner", max_steps=k)
+            for i in range(n):
+                assert bufs[i].max() == 2 ** k
+                assert (bufs[i] == 2 ** k).sum() == n >> k
+        for i in range(n):
+            assert np.flatnonzero(bufs[i] == n).tolist() == [bitrev(i, L)]
+    bufs = [np.ones(8, np.float32) for _ in range(8)]
+    oracle.run(bufs, "fp32", "rabenseifner", max_steps=3)
+    assert int(np.flatnonzero(bufs[1] == 8)[0]) == ord("E") - ord("A")
+
+
+def test_rabenseifner_bytes_and_steps():
+    """Primer ch. 4 section 4.3 and Figure 4.5: 2 log2 N steps; the halving
+    reduce-scatter sends 7/8 S on 8 ranks; in total 2(N-1)/N * S per rank."""
+    for n in (2, 4, 8, 16, 64):
+        e = n * 96
+        sent, _, steps = oracle.stats(n, e, "fp32", "rabenseifner")
+        assert steps == 2 * (n.bit_length() - 1)
+        assert all(int(b) == 2 * (n - 1) * (e // n) * 4 for b in sent)
+    m = oracle.messages(8, 8 * 96, "rabenseifner")
+    rs = m["kind"] == oracle.REDUCE
+    for r in range(8):
+        assert int(((m["hi"] - m["lo"])[rs & (m["src"] == r)]).sum()) == 7 * 96
+    with pytest.raises(oracle.OracleError):
+        oracle.steps(12, "rabenseifner")
+
+
+def test_every_step_moves_each_chunk_once():
+    """Primer ch. 4, Figure 4.2: each column of the send table holds every
+    chunk once, so no two transfers of a step touch the same range."""
+    for sched, n, g in (("ring", 7, 1), ("hierarchical", 8, 4), ("rabenseifner", 8, 1)):
+        m = oracle.messages(n, 840, sched, group_size=g)
+        for s in np.unique(m["step"]):
+            sel = np.flatnonzero(m["step"] == s)
+            written = {}
+            for j in sel:
+                d = int(m["dst"][j])
+                for (lo, hi) in written.get(d, []):
+                    assert m["hi"][j] <= lo or hi <= m["lo"][j]
+                written.setdefault(d, []).append((int(m["lo"][j]), int(m["hi"][j])))
+
+
+def test_alpha_beta_times_printed_on_pages():
+    """The analytic times of Data-center networks 7.2.1 / 7.6.3 and of
+    Scaling ML systems ch. 06 (fixture alpha_beta_pages.txt)."""
+    for row in _rows("alpha_beta_pages.txt"):
+        name, sched = row[0], row[1]
+        n, g, nbytes, eb = (int(v) for v in row[2:6])
+        alpha_us, bwi, bwc, want_ms, tol = (float(v) for v in row[6:11])
+        t = oracle.cost(n, nbytes // eb, eb, sched, alpha_us * 1e-6, bwi * 1e9, bwc * 1e9,
+                        group_size=g)
+        assert abs(t * 1e3 - want_ms) <= tol * want_ms, (name, t * 1e3, want_ms)
+
+
+def test_ring_lower_bound_matches():
+    """Scaling ML systems ch. 06, "bandwidth-optimal lower bound":
+    T_min = 2(N-1)/N * M / beta; the ring reaches it exactly when alpha = 0."""
+    for n in (2, 4, 16):
+        e = n * 4096
+        t = oracle.cost(n, e, 4, "ring", 0.0, 1e9, 1e9)
+        assert t == pytest.approx(2 * (n - 1) / n * e * 4 / 1e9, rel=1e-12)
+        t = oracle.cost(n, e, 4, "rabenseifner", 0.0, 1e9, 1e9)
+        assert t == pytest.approx(2 * (n - 1) / n * e * 4 / 1e9, rel=1e-12)
