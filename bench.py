@@ -1,0 +1,308 @@
+"""Benchmark: 16-rank, 192 MiB-per-rank fp32 ring all-reduce on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5r16|c5g16|c5r64|c5g64]
+                [--exec steps|steps_unfused|onepass]
+
+A step is one whole all-reduce (every launch of the schedule) over the N
+virtual ranks' buffers, which are resident in HBM before timing starts.  The
+W warm-up calls are untimed; the K timed calls run back to back between two
+device synchronisations.  Each call is in place, so values grow by about N
+per call; the kernels' work does not depend on the values.
+
+Prints ONE JSON line.  value = busbw = algbw * 2(N-1)/N with algbw = S / T
+(S = bytes per rank, GB = 1e9; the nccl-tests convention of the AI training
+network primer, ch. 4 section 4.8).  roofline: the kernel kind with the
+largest share of GPU time, its algorithmic bytes per launch over its mean
+launch duration (HIP events recorded by the library around every launch of
+the timed calls, on the call's stream), against 8 TB/s.  cpu_baseline: the
+CPU oracle (plain single-threaded C) timed on the host on the same inputs.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective busbw GB/s and % of HBM peak, 16-rank 192 MiB all-reduce"
+
+WORKLOADS = {
+    # name: (description, schedule, nranks, group, dtype, count or None for bucketed)
+    "c2": ("ring all-reduce, 16 virtual ranks x 192 MiB fp32 (50,331,648 elements each), N(0,1e-3)",
+           "ring", 16, 8, "fp32", 12288 * 4096),
+    "c3": ("ring all-reduce, 16 virtual ranks x 192 MiB bf16 (100,663,296 elements each), N(0,1e-3), "
+           "fp32 accumulate", "ring", 16, 8, "bf16", 2 * 12288 * 4096),
+    "c4": ("hierarchical all-reduce, 2 groups x 8 ranks x 192 MiB fp32, N(0,1e-3)",
+           "hierarchical", 16, 8, "fp32", 12288 * 4096),
+    "c5r16": ("Rabenseifner, 16 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "rabenseifner", 16, 1,
+              "bf16", None),
+    "c5g16": ("ring, 16 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "ring", 16, 1, "bf16", None),
+    "c5r64": ("Rabenseifner, 64 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "rabenseifner", 64, 1,
+              "bf16", None),
+    "c5g64": ("ring, 64 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "ring", 64, 1, "bf16", None),
+}
+
+KIND_NAMES = {0x100: "chunk_reduce", 0x200: "chunk_copy", 0x300: "onepass_ring", 0x400: "onepass_hier",
+              0x500: "onepass_tree"}
+
+
+def kernel_label(kind):
+    """Kernel name with its template arguments, as rocprofv3 reports it."""
+    fam = kind & 0xF00
+    if fam == 0x100:
+        return f"chunk_reduce<{kind & 0xF}>"
+    if fam == 0x200:
+        return f"chunk_copy<{kind & 0xFF}>"
+    return f"{KIND_NAMES[fam]}<{'bf16' if kind & 1 else 'fp32'}>"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def launch_bytes(B, plan, i, nranks, elem):
+    """Algorithmic device bytes of launch i (read + write of every operand)."""
+    kind, _ = B.ar_plan_launch_info(plan, i)
+    ops = B.ar_plan_launch_ops(plan, i)
+    n = (ops["hi"] - ops["lo"]).astype("int64")
+    fam = kind & 0xF00
+    if fam == B.KIND_REDUCE:
+        if elem == 4:
+            per = 3 * 4 + (4 if kind & 8 else 0)
+        else:
+            a = 2 if kind & 1 else 4
+            b = 2 if kind & 2 else 4
+            o = 2 if kind & 4 else 4
+            per = a + b + o + (o if kind & 8 else 0)
+        return int(n.sum()) * per, kind
+    if fam == B.KIND_COPY:
+        return int(n.sum()) * 2 * elem, kind
+    return int(n.sum()) * 2 * elem * nranks, kind
+
+
+def traffic_record(kernel_name, workload, exec_mode):
+    """Counter-measured HBM bytes per launch from a committed rocprofv3 summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    src = open(os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc", "kernels.hip"), "rb").read()
+    digest = hashlib.sha256(src).hexdigest()
+    try:
+        recs = json.load(open(path))
+    except ValueError:
+        return None
+    for r in recs:
+        if (r.get("kernel") == kernel_name and r.get("workload") == workload and r.get("exec") == exec_mode
+                and r.get("kernels_sha256") == digest):
+            return r.get("bytes_per_launch")
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--exec", default="steps", choices=["steps", "steps_unfused", "onepass"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the one-pass comparison run")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the N virtual ranks live in one GPU's HBM; "
+              "there is no multi-GPU path to measure (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gradient_all_reduce_ar_amd import _binding as B
+    from gradient_all_reduce_ar_amd import workloads
+
+    desc, sched, n, group, dtype, count = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    elem = 4 if dtype == "fp32" else 2
+    view = np.float32 if dtype == "fp32" else np.int16
+
+    # ---- inputs, resident in HBM before timing
+    t0 = time.time()
+    bucketed = count is None
+    if bucketed:
+        sizes = workloads.bucketed_tensor_sizes(elem_bytes=elem)
+        plan = B.ar_bucket_plan_create(n, group, sizes, dtype, sched, 25 << 20)
+        B.ar_bucket_set_exec(plan, args.exec)
+        offsets, arena = B.ar_bucket_layout(plan, len(sizes))
+        host = []
+        for r in range(n):
+            a = np.zeros(arena, np.uint16 if dtype == "bf16" else np.float32)
+            for t, c in enumerate(sizes):
+                a[offsets[t]:offsets[t] + c] = workloads.bucketed_tensor_values(r, t, c, dtype=dtype)
+            host.append(a)
+        count_logical = int(sum(int(c) for c in sizes))
+    else:
+        plan = B.ar_plan_create(n, group, count, dtype, sched)
+        B.ar_plan_set_exec(plan, args.exec)
+        host = workloads.normal_inputs(n, count, seed=0, dtype=dtype)
+        count_logical = count
+    bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: {desc}")
+
+    stream = torch.cuda.current_stream(dev)
+    run = (lambda: B.ar_bucket_allreduce(plan, bufs, stream)) if bucketed else \
+        (lambda: B.ar_allreduce(plan, bufs, stream))
+    subplans = []
+    if bucketed:
+        # per-bucket plans are internal; profile by timing each call with events
+        pass
+    else:
+        B.ar_plan_set_profiling(plan, max(args.steps, 1))
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    if not bucketed:
+        B.ar_plan_launch_times(plan)  # clear the warm-up entries
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall_ms = (t_end - t_start) * 1e3 / max(args.steps, 1)
+    ev_ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    ms = wall_ms
+
+    S = count_logical * elem
+    algbw = S / (ms * 1e-3) / 1e9
+    busbw = algbw * 2 * (n - 1) / n
+    stats = B.ar_bucket_stats(plan) if bucketed else B.ar_plan_stats(plan)
+    model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
+
+    roofline = None
+    per_kind = {}
+    if not bucketed:
+        times = B.ar_plan_launch_times(plan)
+        nl = B.ar_plan_num_launches(plan)
+        lb = [launch_bytes(B, plan, i, n, elem) for i in range(nl)]
+        for call in times:
+            for i, t in enumerate(call):
+                nbytes, kind = lb[i]
+                k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "kinds": set()})
+                k["ms"] += t
+                k["launches"] += 1
+                k["bytes"] += nbytes
+                k["kinds"].add(hex(kind))
+        dom = max(per_kind, key=lambda f: per_kind[f]["ms"])
+        d = per_kind[dom]
+        avg_ms = d["ms"] / d["launches"]
+        bytes_per_launch = d["bytes"] / d["launches"]
+        achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+        traffic = traffic_record(kernel_label(dom), args.workload, args.exec)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "kernel": kernel_label(dom),
+                    "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                    "launches_timed": d["launches"]}
+        log("per kernel:", {kernel_label(f): {"ms_total": round(v["ms"], 3), "launches": v["launches"],
+                                                  "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                                  for f, v in per_kind.items()})
+        sum_launch_ms = sum(sum(c) for c in times) / max(len(times), 1)
+    else:
+        sum_launch_ms = None
+
+    # ---- one-pass comparison on the same buffers (bit-identical results)
+    extra = {}
+    if not args.no_extra and args.exec != "onepass" and not bucketed:
+        B.ar_plan_set_profiling(plan, 0)
+        B.ar_plan_set_exec(plan, "onepass")
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        op_ms = (time.perf_counter() - t_a) * 1e3 / max(args.steps, 1)
+        op_alg = S / (op_ms * 1e-3) / 1e9
+        op_stats = B.ar_plan_stats(plan)
+        extra["onepass"] = {"ms_per_step": round(op_ms, 4), "busbw_GBps": round(op_alg * 2 * (n - 1) / n, 1),
+                            "algbw_GBps": round(op_alg, 1),
+                            "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
+
+    # ---- CPU oracle on the same inputs (single-threaded C)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        del bufs
+        torch.cuda.empty_cache()
+        if bucketed:
+            sample_buckets = list(range(min(4, B.ar_bucket_count(plan))))
+            t_c = time.perf_counter()
+            done = 0
+            for b in sample_buckets:
+                off, cnt = B.ar_bucket_range(plan, b)
+                oracle.run([h[off:off + cnt].copy() for h in host], dtype, sched, group_size=group)
+                done += cnt
+            cpu_s = time.perf_counter() - t_c
+            sample = f"first {len(sample_buckets)} buckets ({done} elements per rank), one all-reduce each"
+        else:
+            t_c = time.perf_counter()
+            oracle.run(host, dtype, sched, group_size=group)
+            cpu_s = time.perf_counter() - t_c
+            done = count
+            sample = "the whole workload, one all-reduce"
+        cpu_alg = done * elem / cpu_s / 1e9
+        cpu = {"value": round(cpu_alg * 2 * (n - 1) / n, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": sample, "seconds": round(cpu_s, 2), "host_cpus": os.cpu_count()}
+
+    out = {
+        "metric": METRIC,
+        "value": round(busbw, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if dtype == "fp32" else "bf16 (f32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,
+            "count_per_rank": count_logical, "bytes_per_rank": S, "exec": args.exec,
+            "algbw_GBps": round(algbw, 1), "busbw_GBps": round(busbw, 1),
+            "hbm_model_bytes": stats["hbm_bytes_model"], "hbm_model_GBps": round(model_gbps, 1),
+            "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),
+            "launches_per_step": stats["launches"], "schedule_steps": stats["steps"],
+            "event_ms_per_step": round(ev_ms, 4),
+            "sum_of_launch_ms_per_step": None if sum_launch_ms is None else round(sum_launch_ms, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        out["config"]["compare"] = extra
+    if bucketed:
+        out["config"]["buckets"] = B.ar_bucket_count(plan)
+        B.ar_bucket_plan_destroy(plan)
+    else:
+        B.ar_plan_destroy(plan)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

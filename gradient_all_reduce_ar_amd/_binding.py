@@ -1,0 +1,288 @@
+"""ctypes binding of libar.so: the C ABI of include/ar.h under the same names.
+
+Argument marshalling only: every step of the all-reduce runs in the HIP
+kernels of libar.so.  There is no fallback; if the library is missing or
+fails to load, every call raises.
+
+Device pointers may be passed as ints or as objects with a ``data_ptr()``
+method (torch tensors); streams as ints, None (default stream) or objects
+with a ``cuda_stream`` attribute (torch streams).
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libar.so")
+
+AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP = range(5)
+AR_FLOAT32, AR_BFLOAT16 = 0, 1
+AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER = 0, 1, 2
+AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
+AR_MAX_RANKS = 64
+
+DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16}
+SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER}
+EXECS = {"steps": AR_EXEC_STEPS, "steps_unfused": AR_EXEC_STEPS_UNFUSED, "onepass": AR_EXEC_ONEPASS}
+
+# kernel kind codes reported by ar_plan_launch_info
+KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE = 0x100, 0x200, 0x300, 0x400, 0x500
+LOC_SCRATCH = 1000
+
+
+class ArError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"ar status {status}: {message}")
+        self.status = status
+
+
+class ar_stats_t(ctypes.Structure):
+    _fields_ = [
+        ("nranks", ctypes.c_int32), ("group_size", ctypes.c_int32),
+        ("steps", ctypes.c_uint32), ("launches", ctypes.c_uint32),
+        ("count", ctypes.c_uint64), ("elem_bytes", ctypes.c_uint64),
+        ("bytes_sent", ctypes.POINTER(ctypes.c_uint64)),
+        ("bytes_sent_max", ctypes.c_uint64), ("bytes_sent_total", ctypes.c_uint64),
+        ("cross_group_bytes_total", ctypes.c_uint64),
+        ("hbm_bytes_model", ctypes.c_uint64),
+        ("scratch_bytes", ctypes.c_uint64),
+        ("exec", ctypes.c_int32),
+    ]
+
+    def to_dict(self):
+        d = {k: getattr(self, k) for k, _ in self._fields_ if k != "bytes_sent"}
+        d["bytes_sent"] = [self.bytes_sent[i] for i in range(self.nranks)] if self.bytes_sent else []
+        return d
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _declare(L):
+    P, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    sz, dbl = ctypes.c_size_t, ctypes.c_double
+    pi32, pi64, pf, psz = (ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                           ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_size_t))
+    sig = {
+        "ar_plan_create": ([ctypes.c_int, ctypes.c_int, sz, ctypes.c_int, ctypes.c_int], P),
+        "ar_plan_set_exec": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_prepare": ([P], ctypes.c_int),
+        "ar_allreduce": ([P, P, P], ctypes.c_int),
+        "ar_plan_stats": ([P], ar_stats_t),
+        "ar_plan_cost_alpha_beta": ([P, dbl, dbl, dbl], dbl),
+        "ar_plan_destroy": ([P], None),
+        "ar_last_error": ([], ctypes.c_char_p),
+        "ar_last_status": ([], ctypes.c_int),
+        "ar_plan_transfers": ([P, pi32, pi32, pi32, pi64, pi64, pi32, i64], i64),
+        "ar_plan_num_launches": ([P], i32),
+        "ar_plan_launch_info": ([P, i32, pi32, pi32], ctypes.c_int),
+        "ar_plan_launch_ops": ([P, i32, pi64, pi64, pi32, pi32, pi32, pi32, pi32], ctypes.c_int),
+        "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_launch_times": ([P, pf, i32, pi32], ctypes.c_int),
+        "ar_bucket_plan_create": ([ctypes.c_int, ctypes.c_int, psz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz], P),
+        "ar_bucket_layout": ([P, psz, psz], ctypes.c_int),
+        "ar_bucket_count": ([P], i32),
+        "ar_bucket_range": ([P, i32, psz, psz], ctypes.c_int),
+        "ar_bucket_set_exec": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_bucket_allreduce": ([P, P, P], ctypes.c_int),
+        "ar_bucket_stats": ([P], ar_stats_t),
+        "ar_bucket_plan_destroy": ([P], None),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    del u64
+    return L
+
+
+def _raise():
+    L = lib()
+    raise ArError(L.ar_last_status(), L.ar_last_error().decode())
+
+
+def _check(st):
+    if st != AR_OK:
+        _raise()
+
+
+def _ptr(x):
+    if x is None:
+        return 0
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _ptr_array(bufs):
+    return (ctypes.c_void_p * max(len(bufs), 1))(*[_ptr(b) for b in bufs])
+
+
+def _code(table, v):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+# ------------------------------------------------------------------ plans
+
+def ar_plan_create(nranks, group_size, count, dtype, schedule):
+    p = lib().ar_plan_create(nranks, group_size, count, _code(DTYPES, dtype), _code(SCHEDULES, schedule))
+    if not p:
+        _raise()
+    return p
+
+
+def ar_plan_set_exec(plan, exec_mode):
+    _check(lib().ar_plan_set_exec(plan, _code(EXECS, exec_mode)))
+
+
+def ar_plan_prepare(plan):
+    _check(lib().ar_plan_prepare(plan))
+
+
+def ar_allreduce(plan, rank_bufs, stream=None):
+    arr = _ptr_array(rank_bufs)
+    _check(lib().ar_allreduce(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def ar_plan_stats(plan):
+    s = lib().ar_plan_stats(plan)
+    return s.to_dict()
+
+
+def ar_plan_cost_alpha_beta(plan, alpha_s, bw_intra_Bps, bw_cross_Bps):
+    t = lib().ar_plan_cost_alpha_beta(plan, alpha_s, bw_intra_Bps, bw_cross_Bps)
+    if t < 0:
+        _raise()
+    return t
+
+
+def ar_plan_destroy(plan):
+    lib().ar_plan_destroy(plan)
+
+
+def ar_last_error():
+    return lib().ar_last_error().decode()
+
+
+def ar_last_status():
+    return lib().ar_last_status()
+
+
+def ar_plan_transfers(plan):
+    import numpy as np
+
+    L = lib()
+    n = L.ar_plan_transfers(plan, None, None, None, None, None, None, 0)
+    if n < 0:
+        _raise()
+    cols = {k: np.zeros(max(n, 1), np.int32) for k in ("step", "src", "dst", "kind")}
+    cols.update({k: np.zeros(max(n, 1), np.int64) for k in ("lo", "hi")})
+    c = lambda a, t: a.ctypes.data_as(ctypes.POINTER(t))  # noqa: E731
+    L.ar_plan_transfers(plan, c(cols["step"], ctypes.c_int32), c(cols["src"], ctypes.c_int32),
+                        c(cols["dst"], ctypes.c_int32), c(cols["lo"], ctypes.c_int64),
+                        c(cols["hi"], ctypes.c_int64), c(cols["kind"], ctypes.c_int32), n)
+    return {k: v[:n] for k, v in cols.items()}
+
+
+def ar_plan_num_launches(plan):
+    n = lib().ar_plan_num_launches(plan)
+    if n < 0:
+        _raise()
+    return n
+
+
+def ar_plan_launch_info(plan, i):
+    kind, nops = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ar_plan_launch_info(plan, i, ctypes.byref(kind), ctypes.byref(nops)))
+    return kind.value, nops.value
+
+
+def ar_plan_launch_ops(plan, i):
+    import numpy as np
+
+    _, nops = ar_plan_launch_info(plan, i)
+    cols = {k: np.zeros(max(nops, 1), np.int64) for k in ("lo", "hi")}
+    cols.update({k: np.zeros(max(nops, 1), np.int32) for k in ("a", "b", "o", "o2", "aux")})
+    c = lambda a, t: a.ctypes.data_as(ctypes.POINTER(t))  # noqa: E731
+    _check(lib().ar_plan_launch_ops(plan, i, c(cols["lo"], ctypes.c_int64), c(cols["hi"], ctypes.c_int64),
+                                    *[c(cols[k], ctypes.c_int32) for k in ("a", "b", "o", "o2", "aux")]))
+    return {k: v[:nops] for k, v in cols.items()}
+
+
+def ar_plan_set_profiling(plan, max_calls):
+    _check(lib().ar_plan_set_profiling(plan, int(max_calls)))
+
+
+def ar_plan_launch_times(plan):
+    """Per-launch ms of the logged calls, as a list of per-call lists."""
+    n = ctypes.c_int32()
+    _check(lib().ar_plan_launch_times(plan, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check(lib().ar_plan_launch_times(plan, buf, n.value, ctypes.byref(n)))
+    L = ar_plan_num_launches(plan)
+    flat = [buf[i] for i in range(n.value)]
+    return [flat[c * L:(c + 1) * L] for c in range(n.value // L)] if L else []
+
+
+# ---------------------------------------------------------------- buckets
+
+def ar_bucket_plan_create(nranks, group_size, tensor_counts, dtype, schedule, bucket_cap_bytes):
+    counts = (ctypes.c_size_t * max(len(tensor_counts), 1))(*[int(c) for c in tensor_counts])
+    p = lib().ar_bucket_plan_create(nranks, group_size, counts, len(tensor_counts), _code(DTYPES, dtype),
+                                    _code(SCHEDULES, schedule), bucket_cap_bytes)
+    if not p:
+        _raise()
+    return p
+
+
+def ar_bucket_layout(bp, ntensors):
+    offs = (ctypes.c_size_t * max(ntensors, 1))()
+    arena = ctypes.c_size_t()
+    _check(lib().ar_bucket_layout(bp, offs, ctypes.byref(arena)))
+    return [offs[i] for i in range(ntensors)], arena.value
+
+
+def ar_bucket_count(bp):
+    n = lib().ar_bucket_count(bp)
+    if n < 0:
+        _raise()
+    return n
+
+
+def ar_bucket_range(bp, b):
+    off, cnt = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().ar_bucket_range(bp, b, ctypes.byref(off), ctypes.byref(cnt)))
+    return off.value, cnt.value
+
+
+def ar_bucket_set_exec(bp, exec_mode):
+    _check(lib().ar_bucket_set_exec(bp, _code(EXECS, exec_mode)))
+
+
+def ar_bucket_allreduce(bp, rank_arenas, stream=None):
+    arr = _ptr_array(rank_arenas)
+    _check(lib().ar_bucket_allreduce(bp, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def ar_bucket_stats(bp):
+    return lib().ar_bucket_stats(bp).to_dict()
+
+
+def ar_bucket_plan_destroy(bp):
+    lib().ar_bucket_plan_destroy(bp)

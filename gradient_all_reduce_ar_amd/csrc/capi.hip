@@ -1,0 +1,525 @@
+// capi.hip -- C ABI (include/ar.h) and executor of the all-reduce library.
+//
+// A plan is built on the host (plan.cpp).  On first use it uploads its op
+// tables to the device and, for bf16, allocates the fp32 partial-sum
+// scratch.  ar_allreduce then launches one kernel per launch of the plan on
+// the caller's stream, passing the caller's rank pointers by value; nothing
+// is allocated or copied on the hot path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/ar.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local ar_status_t g_status = AR_OK;
+
+ar_status_t fail(ar_status_t st, const std::string &msg) {
+  g_status = st;
+  g_err = msg;
+  return st;
+}
+
+ar_status_t hip_fail(hipError_t e, const char *what) {
+  return fail(AR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+struct ar_plan {
+  ar::Plan p;
+  int device = -1;
+  bool prepared = false;
+  ar_dev::DevOp *d_ops = nullptr;
+  std::vector<int64_t> op_offset;  // per launch: index of its first op in d_ops
+  std::vector<uint32_t> grid_x;    // per launch
+  float *scratch = nullptr;        // owned unless external_scratch
+  size_t scratch_bytes = 0;
+  float *external_scratch = nullptr;
+  size_t external_scratch_bytes = 0;
+  int32_t prof_calls = 0;           // capacity of the event log in calls
+  int64_t prof_logged = 0;          // calls recorded since the log was last read
+  std::vector<hipEvent_t> events;   // prof_calls * (launches + 1)
+
+  size_t need_scratch_bytes() const {
+    return static_cast<size_t>(p.nslots) * static_cast<size_t>(p.slot_stride) * sizeof(float);
+  }
+
+  void release_device() {
+    if (d_ops) (void)hipFree(d_ops);
+    if (scratch) (void)hipFree(scratch);
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    d_ops = nullptr;
+    scratch = nullptr;
+    scratch_bytes = 0;
+    events.clear();
+    prepared = false;
+  }
+};
+
+struct ar_bucket_plan {
+  int nranks = 0, group_size = 1;
+  ar_dtype_t dtype = AR_FLOAT32;
+  std::vector<int64_t> tensor_offsets, bucket_offset, bucket_count;
+  int64_t arena_count = 0;
+  std::vector<ar_plan_t *> plans;
+  std::vector<uint64_t> bytes_sent;
+  float *scratch = nullptr;
+  size_t scratch_bytes = 0;
+};
+
+namespace {
+
+ar_status_t prepare(ar_plan_t *pl) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (pl->prepared) {
+    if (dev != pl->device) return fail(AR_ERR_INVALID_ARG, "plan was prepared on another device");
+    return AR_OK;
+  }
+  pl->release_device();
+  pl->device = dev;
+  std::vector<ar_dev::DevOp> host_ops;
+  pl->op_offset.clear();
+  pl->grid_x.clear();
+  for (const ar::Launch &L : pl->p.launches) {
+    pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
+    const int64_t tile = ar_dev::tile_elems(L.kind);
+    int64_t gx = 0;
+    for (const ar::Op &o : L.ops) {
+      host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
+      gx = std::max(gx, (o.hi + tile - 1) / tile - o.lo / tile);
+    }
+    if (gx > 0x7fffffff) return fail(AR_ERR_UNSUPPORTED, "op too large for one grid");
+    pl->grid_x.push_back(static_cast<uint32_t>(gx));
+  }
+  if (!host_ops.empty()) {
+    e = hipMalloc(reinterpret_cast<void **>(&pl->d_ops), host_ops.size() * sizeof(ar_dev::DevOp));
+    if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("op table allocation: ") + hipGetErrorString(e));
+    e = hipMemcpy(pl->d_ops, host_ops.data(), host_ops.size() * sizeof(ar_dev::DevOp), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      pl->release_device();
+      return hip_fail(e, "op table upload");
+    }
+  }
+  const size_t need = pl->need_scratch_bytes();
+  if (need > 0 && !pl->external_scratch) {
+    e = hipMalloc(reinterpret_cast<void **>(&pl->scratch), need);
+    if (e != hipSuccess) {
+      pl->release_device();
+      return fail(AR_ERR_OOM, std::string("scratch allocation: ") + hipGetErrorString(e));
+    }
+    pl->scratch_bytes = need;
+  }
+  if (need > 0 && pl->external_scratch && pl->external_scratch_bytes < need) {
+    pl->release_device();
+    return fail(AR_ERR_INVALID_ARG, "external scratch too small");
+  }
+  if (pl->prof_calls > 0) {
+    pl->events.resize(static_cast<size_t>(pl->prof_calls) * (pl->p.launches.size() + 1));
+    for (hipEvent_t &ev : pl->events) {
+      e = hipEventCreate(&ev);
+      if (e != hipSuccess) {
+        ev = nullptr;
+        pl->release_device();
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+  }
+  pl->prepared = true;
+  return AR_OK;
+}
+
+ar_status_t check_rank_pointers(const ar_plan_t *pl, void *const *rank_bufs) {
+  if (!rank_bufs) return fail(AR_ERR_INVALID_ARG, "rank_bufs is NULL");
+  const int n = pl->p.nranks;
+  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::elem_bytes(pl->p.dtype));
+  for (int r = 0; r < n; ++r) {
+    const uintptr_t v = reinterpret_cast<uintptr_t>(rank_bufs[r]);
+    if (!v) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is NULL");
+    if (v % 16) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is not 16-byte aligned");
+  }
+  if (bytes > 0)
+    for (int r = 0; r < n; ++r)
+      for (int q = r + 1; q < n; ++q) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
+        const uintptr_t b = reinterpret_cast<uintptr_t>(rank_bufs[q]);
+        if (a < b + bytes && b < a + bytes)
+          return fail(AR_ERR_INVALID_ARG,
+                      "rank buffers " + std::to_string(r) + " and " + std::to_string(q) + " overlap");
+      }
+  return AR_OK;
+}
+
+ar_stats_t stats_of(const ar::Plan &p) {
+  ar_stats_t s{};
+  s.nranks = p.nranks;
+  s.group_size = p.group_size;
+  s.steps = static_cast<uint32_t>(p.nsteps);
+  s.launches = static_cast<uint32_t>(p.launches.size());
+  s.count = static_cast<uint64_t>(p.count);
+  s.elem_bytes = static_cast<uint64_t>(ar::elem_bytes(p.dtype));
+  s.bytes_sent = p.bytes_sent.data();
+  for (uint64_t b : p.bytes_sent) {
+    s.bytes_sent_max = std::max(s.bytes_sent_max, b);
+    s.bytes_sent_total += b;
+  }
+  s.cross_group_bytes_total = p.cross_group_bytes;
+  s.hbm_bytes_model = p.hbm_bytes;
+  s.scratch_bytes = static_cast<uint64_t>(p.nslots) * static_cast<uint64_t>(p.slot_stride) * 4;
+  s.exec = p.exec;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ar_last_error(void) { return g_err.c_str(); }
+ar_status_t ar_last_status(void) { return g_status; }
+
+ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype, ar_schedule_t schedule) {
+  if (count > static_cast<size_t>(INT64_MAX / 8)) {
+    fail(AR_ERR_INVALID_ARG, "count too large");
+    return nullptr;
+  }
+  ar_plan_t *pl = new (std::nothrow) ar_plan_t;
+  if (!pl) {
+    fail(AR_ERR_OOM, "host allocation failed");
+    return nullptr;
+  }
+  bool unsupported = false;
+  const std::string err = ar::build_plan(pl->p, nranks, group_size, static_cast<int64_t>(count),
+                                         static_cast<ar::Dtype>(dtype), static_cast<ar::Sched>(schedule),
+                                         ar::kSteps, &unsupported);
+  if (!err.empty()) {
+    delete pl;
+    fail(unsupported ? AR_ERR_UNSUPPORTED : AR_ERR_INVALID_ARG, err);
+    return nullptr;
+  }
+  g_status = AR_OK;
+  return pl;
+}
+
+ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (exec == static_cast<ar_exec_t>(plan->p.exec) && plan->prepared) return AR_OK;
+  ar::Plan trial = plan->p;
+  const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
+  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
+  if (plan->prepared) (void)hipDeviceSynchronize();
+  plan->release_device();
+  plan->p = std::move(trial);
+  return AR_OK;
+}
+
+ar_status_t ar_plan_prepare(ar_plan_t *plan) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  return prepare(plan);
+}
+
+ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  ar_status_t st = check_rank_pointers(plan, rank_bufs);
+  if (st != AR_OK) return st;
+  st = prepare(plan);
+  if (st != AR_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ar_dev::KArgs args{};
+  for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
+  args.scratch = plan->external_scratch ? plan->external_scratch : plan->scratch;
+  args.slot_stride = plan->p.slot_stride;
+  args.nranks = plan->p.nranks;
+  args.group_size = plan->p.group_size;
+  const bool prof = plan->prof_calls > 0 && !plan->events.empty();
+  hipEvent_t *ev = nullptr;
+  if (prof) {
+    ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * (plan->p.launches.size() + 1);
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  for (size_t i = 0; i < plan->p.launches.size(); ++i) {
+    const ar::Launch &L = plan->p.launches[i];
+    args.ops = plan->d_ops + plan->op_offset[i];
+    const dim3 grid(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
+    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    if (prof) {
+      e = hipEventRecord(ev[i + 1], s);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+  }
+  if (prof) ++plan->prof_logged;
+  return AR_OK;
+}
+
+ar_stats_t ar_plan_stats(const ar_plan_t *plan) {
+  if (!plan) {
+    fail(AR_ERR_INVALID_ARG, "plan is NULL");
+    return ar_stats_t{};
+  }
+  return stats_of(plan->p);
+}
+
+double ar_plan_cost_alpha_beta(const ar_plan_t *plan, double alpha_s, double bw_intra_Bps, double bw_cross_Bps) {
+  if (!plan || !(bw_intra_Bps > 0) || !(bw_cross_Bps > 0) || alpha_s < 0) {
+    fail(AR_ERR_INVALID_ARG, "bad cost-model arguments");
+    return -1.0;
+  }
+  return ar::cost_alpha_beta(plan->p, alpha_s, bw_intra_Bps, bw_cross_Bps);
+}
+
+void ar_plan_destroy(ar_plan_t *plan) {
+  if (!plan) return;
+  if (plan->prepared) (void)hipDeviceSynchronize();
+  plan->release_device();
+  delete plan;
+}
+
+int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, int32_t *dst, int64_t *lo,
+                          int64_t *hi, int32_t *kind, int64_t cap) {
+  if (!plan) {
+    fail(AR_ERR_INVALID_ARG, "plan is NULL");
+    return -1;
+  }
+  const auto &x = plan->p.xfers;
+  const int64_t n = static_cast<int64_t>(x.size());
+  for (int64_t i = 0; i < std::min(n, cap); ++i) {
+    if (step) step[i] = x[i].step;
+    if (src) src[i] = x[i].src;
+    if (dst) dst[i] = x[i].dst;
+    if (lo) lo[i] = x[i].lo;
+    if (hi) hi[i] = x[i].hi;
+    if (kind) kind[i] = x[i].kind;
+  }
+  return n;
+}
+
+int32_t ar_plan_num_launches(const ar_plan_t *plan) {
+  if (!plan) {
+    fail(AR_ERR_INVALID_ARG, "plan is NULL");
+    return -1;
+  }
+  return static_cast<int32_t>(plan->p.launches.size());
+}
+
+ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops) {
+  if (!plan || i < 0 || i >= static_cast<int32_t>(plan->p.launches.size()))
+    return fail(AR_ERR_INVALID_ARG, "bad plan or launch index");
+  if (kind) *kind = plan->p.launches[i].kind;
+  if (nops) *nops = static_cast<int32_t>(plan->p.launches[i].ops.size());
+  return AR_OK;
+}
+
+ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, int64_t *hi, int32_t *a, int32_t *b,
+                               int32_t *o, int32_t *o2, int32_t *aux) {
+  if (!plan || i < 0 || i >= static_cast<int32_t>(plan->p.launches.size()))
+    return fail(AR_ERR_INVALID_ARG, "bad plan or launch index");
+  const auto &ops = plan->p.launches[i].ops;
+  for (size_t k = 0; k < ops.size(); ++k) {
+    if (lo) lo[k] = ops[k].lo;
+    if (hi) hi[k] = ops[k].hi;
+    if (a) a[k] = ops[k].a;
+    if (b) b[k] = ops[k].b;
+    if (o) o[k] = ops[k].o;
+    if (o2) o2[k] = ops[k].o2;
+    if (aux) aux[k] = ops[k].aux;
+  }
+  return AR_OK;
+}
+
+ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls) {
+  if (!plan || max_calls < 0) return fail(AR_ERR_INVALID_ARG, "bad profiling arguments");
+  if (plan->prepared) (void)hipDeviceSynchronize();
+  plan->release_device();
+  plan->prof_calls = max_calls;
+  plan->prof_logged = 0;
+  return AR_OK;
+}
+
+ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n) {
+  if (!plan || !n) return fail(AR_ERR_INVALID_ARG, "bad arguments");
+  if (plan->prof_calls <= 0) return fail(AR_ERR_INVALID_ARG, "profiling is off");
+  const int64_t L = static_cast<int64_t>(plan->p.launches.size());
+  const int64_t calls = std::min<int64_t>(plan->prof_logged, plan->prof_calls);
+  *n = static_cast<int32_t>(calls * L);
+  if (!ms || cap < *n) return AR_OK;  // size query
+  const int64_t first = plan->prof_logged - calls;
+  for (int64_t c = 0; c < calls; ++c) {
+    const hipEvent_t *ev = plan->events.data() + ((first + c) % plan->prof_calls) * (L + 1);
+    for (int64_t i = 0; i < L; ++i) {
+      hipError_t e = hipEventElapsedTime(&ms[c * L + i], ev[i], ev[i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    }
+  }
+  plan->prof_logged = 0;
+  return AR_OK;
+}
+
+// ---------------------------------------------------------------- buckets
+
+ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t *tensor_counts, int ntensors,
+                                        ar_dtype_t dtype, ar_schedule_t schedule, size_t bucket_cap_bytes) {
+  if (ntensors < 0 || (ntensors > 0 && !tensor_counts) || bucket_cap_bytes == 0) {
+    fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
+    return nullptr;
+  }
+  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16) {
+    fail(AR_ERR_INVALID_ARG, "unknown dtype");
+    return nullptr;
+  }
+  auto *bp = new (std::nothrow) ar_bucket_plan_t;
+  if (!bp) {
+    fail(AR_ERR_OOM, "host allocation failed");
+    return nullptr;
+  }
+  bp->nranks = nranks;
+  bp->group_size = group_size;
+  bp->dtype = dtype;
+  const int64_t eb = dtype == AR_BFLOAT16 ? 2 : 4;
+  std::vector<int64_t> counts(tensor_counts, tensor_counts + ntensors);
+  for (int64_t c : counts)
+    if (c < 0) {
+      delete bp;
+      fail(AR_ERR_INVALID_ARG, "negative tensor count");
+      return nullptr;
+    }
+  ar::assign_buckets(counts, static_cast<int64_t>(bucket_cap_bytes) / eb, 256 / eb, bp->tensor_offsets,
+                     bp->bucket_offset, bp->bucket_count, bp->arena_count);
+  bp->bytes_sent.assign(nranks > 0 ? nranks : 0, 0);
+  for (size_t b = 0; b < bp->bucket_count.size(); ++b) {
+    ar_plan_t *pl = ar_plan_create(nranks, group_size, static_cast<size_t>(bp->bucket_count[b]), dtype, schedule);
+    if (!pl) {
+      const ar_status_t st = g_status;
+      const std::string msg = g_err;
+      ar_bucket_plan_destroy(bp);
+      fail(st, "bucket " + std::to_string(b) + ": " + msg);
+      return nullptr;
+    }
+    bp->plans.push_back(pl);
+  }
+  g_status = AR_OK;
+  return bp;
+}
+
+ar_status_t ar_bucket_layout(const ar_bucket_plan_t *bp, size_t *tensor_offsets, size_t *arena_count) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  if (tensor_offsets)
+    for (size_t t = 0; t < bp->tensor_offsets.size(); ++t) tensor_offsets[t] = static_cast<size_t>(bp->tensor_offsets[t]);
+  if (arena_count) *arena_count = static_cast<size_t>(bp->arena_count);
+  return AR_OK;
+}
+
+int32_t ar_bucket_count(const ar_bucket_plan_t *bp) {
+  if (!bp) {
+    fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+    return -1;
+  }
+  return static_cast<int32_t>(bp->bucket_count.size());
+}
+
+ar_status_t ar_bucket_range(const ar_bucket_plan_t *bp, int32_t b, size_t *offset, size_t *count) {
+  if (!bp || b < 0 || b >= static_cast<int32_t>(bp->bucket_count.size()))
+    return fail(AR_ERR_INVALID_ARG, "bad bucket plan or index");
+  if (offset) *offset = static_cast<size_t>(bp->bucket_offset[b]);
+  if (count) *count = static_cast<size_t>(bp->bucket_count[b]);
+  return AR_OK;
+}
+
+ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  for (ar_plan_t *pl : bp->plans) {
+    const ar_status_t st = ar_plan_set_exec(pl, exec);
+    if (st != AR_OK) return st;
+  }
+  return AR_OK;
+}
+
+ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream) {
+  if (!bp || !rank_arenas) return fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
+  // one scratch shared by all buckets: they run one after another on one stream
+  size_t need = 0;
+  for (ar_plan_t *pl : bp->plans) need = std::max(need, pl->need_scratch_bytes());
+  if (need > bp->scratch_bytes) {
+    if (bp->scratch) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(bp->scratch);
+      bp->scratch = nullptr;
+      bp->scratch_bytes = 0;
+    }
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&bp->scratch), need);
+    if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("bucket scratch: ") + hipGetErrorString(e));
+    bp->scratch_bytes = need;
+  }
+  const int64_t eb = bp->dtype == AR_BFLOAT16 ? 2 : 4;
+  std::vector<void *> ptrs(static_cast<size_t>(bp->nranks));
+  for (size_t b = 0; b < bp->plans.size(); ++b) {
+    ar_plan_t *pl = bp->plans[b];
+    if (pl->external_scratch != bp->scratch) {
+      pl->external_scratch = bp->scratch;
+      pl->external_scratch_bytes = bp->scratch_bytes;
+      pl->prepared = pl->prepared && pl->need_scratch_bytes() == 0;
+    }
+    pl->external_scratch_bytes = bp->scratch_bytes;
+    for (int r = 0; r < bp->nranks; ++r)
+      ptrs[r] = static_cast<char *>(rank_arenas[r]) + bp->bucket_offset[b] * eb;
+    const ar_status_t st = ar_allreduce(pl, ptrs.data(), stream);
+    if (st != AR_OK) return fail(st, "bucket " + std::to_string(b) + ": " + g_err);
+  }
+  return AR_OK;
+}
+
+ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
+  ar_stats_t s{};
+  if (!bp) {
+    fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+    return s;
+  }
+  auto *mut = const_cast<ar_bucket_plan_t *>(bp);
+  std::fill(mut->bytes_sent.begin(), mut->bytes_sent.end(), 0);
+  for (ar_plan_t *pl : bp->plans) {
+    const ar_stats_t t = stats_of(pl->p);
+    s.steps += t.steps;
+    s.launches += t.launches;
+    s.count += t.count;
+    s.cross_group_bytes_total += t.cross_group_bytes_total;
+    s.hbm_bytes_model += t.hbm_bytes_model;
+    s.scratch_bytes = std::max(s.scratch_bytes, t.scratch_bytes);
+    s.exec = t.exec;
+    for (int r = 0; r < bp->nranks; ++r) mut->bytes_sent[r] += pl->p.bytes_sent[r];
+  }
+  s.nranks = bp->nranks;
+  s.group_size = bp->group_size;
+  s.elem_bytes = bp->dtype == AR_BFLOAT16 ? 2 : 4;
+  s.bytes_sent = bp->bytes_sent.data();
+  for (uint64_t b : bp->bytes_sent) {
+    s.bytes_sent_max = std::max(s.bytes_sent_max, b);
+    s.bytes_sent_total += b;
+  }
+  return s;
+}
+
+void ar_bucket_plan_destroy(ar_bucket_plan_t *bp) {
+  if (!bp) return;
+  for (ar_plan_t *pl : bp->plans) {
+    pl->external_scratch = nullptr;
+    ar_plan_destroy(pl);
+  }
+  if (bp->scratch) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(bp->scratch);
+  }
+  delete bp;
+}
+
+}  // extern "C"

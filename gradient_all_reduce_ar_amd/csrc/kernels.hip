@@ -1,0 +1,461 @@
+// kernels.hip -- HIP kernels for gfx950 (CDNA4) that execute the all-reduce
+// schedules over N virtual ranks held in one GPU's HBM.
+//
+// The work is a stream over HBM (one add per 8-12 bytes moved), so the
+// kernels are built for bandwidth: every wavefront instruction moves a
+// contiguous 1 KiB (fp32) or 512 B (bf16) span, each thread keeps UNROLL
+// independent 16-byte loads in flight, and no LDS or MFMA is involved --
+// nothing is reused, so staging through LDS would only add a round trip.
+//
+// Launch geometry: grid = (tiles per op, ops).  blockIdx.y selects the op
+// (one transfer of the step); blockIdx.x walks the op's element range in
+// tiles that are aligned to the tile size in absolute element coordinates,
+// so every rank buffer, every scratch slot and every vector access of a tile
+// share the same alignment.  Only the first and last tile of an op can be
+// partial; they take a per-element path.
+//
+// Summation order.  Each output element is produced by exactly one thread
+// from its inputs in the schedule's order with IEEE binary32 adds (packed
+// fp32 ops disabled at build time, no contraction, denormals kept), so the
+// bits equal a step-by-step execution of the schedule.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace ar_dev {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__device__ __forceinline__ const char *src_ptr(const KArgs &a, int32_t loc) {
+  return loc >= kLocScratchDev
+             ? reinterpret_cast<const char *>(a.scratch + static_cast<int64_t>(loc - kLocScratchDev) * a.slot_stride)
+             : static_cast<const char *>(a.rank[loc]);
+}
+__device__ __forceinline__ char *dst_ptr(const KArgs &a, int32_t loc) {
+  return loc >= kLocScratchDev
+             ? reinterpret_cast<char *>(a.scratch + static_cast<int64_t>(loc - kLocScratchDev) * a.slot_stride)
+             : static_cast<char *>(a.rank[loc]);
+}
+
+// bf16 <-> fp32.  Widening is exact (the bf16 bits are the top half of the
+// fp32 pattern).  Narrowing rounds to nearest, ties to even, computed on the
+// bit pattern: add 0x7fff plus the lowest kept bit, drop the low 16 bits.
+// NaN keeps its sign and top payload bits and is forced quiet.
+__device__ __forceinline__ float widen(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t narrow(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rounded;
+}
+
+// 4-element units: fp32 = 16 B (float4), bf16 = 8 B (uint2).
+template <bool BF>
+__device__ __forceinline__ float4 load4(const char *base, int64_t e) {
+  if constexpr (BF) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(base + e * 2);
+    return make_float4(widen(v.x & 0xffffu), widen(v.x >> 16), widen(v.y & 0xffffu), widen(v.y >> 16));
+  } else {
+    return *reinterpret_cast<const float4 *>(base + e * 4);
+  }
+}
+
+template <bool BF>
+__device__ __forceinline__ float load1(const char *base, int64_t e) {
+  if constexpr (BF) return widen(*reinterpret_cast<const uint16_t *>(base + e * 2));
+  else return *reinterpret_cast<const float *>(base + e * 4);
+}
+
+__device__ __forceinline__ uint2 pack4(float4 v) {
+  return make_uint2(narrow(v.x) | (narrow(v.y) << 16), narrow(v.z) | (narrow(v.w) << 16));
+}
+
+template <bool BF>
+__device__ __forceinline__ void store4(char *base, int64_t e, float4 v) {
+  if constexpr (BF) *reinterpret_cast<uint2 *>(base + e * 2) = pack4(v);
+  else *reinterpret_cast<float4 *>(base + e * 4) = v;
+}
+
+template <bool BF>
+__device__ __forceinline__ void store1(char *base, int64_t e, float v) {
+  if constexpr (BF) *reinterpret_cast<uint16_t *>(base + e * 2) = static_cast<uint16_t>(narrow(v));
+  else *reinterpret_cast<float *>(base + e * 4) = v;
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// ---------------------------------------------------------------------------
+// Chunk reduce: o[e] = a[e] + b[e] over the op's range, optionally also
+// written to o2 (the fused forwarding copy of the chunk just completed).
+// FLAGS: 1 a is bf16, 2 b is bf16, 4 outputs are bf16 (rounded once), 8 o2.
+// ---------------------------------------------------------------------------
+template <int FLAGS, int UNROLL>
+__global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
+  constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const DevOp op = args.ops[blockIdx.y];
+  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
+  if (base >= op.hi) return;
+  const char *A = src_ptr(args, op.a);
+  const char *B = src_ptr(args, op.b);
+  char *O = dst_ptr(args, op.o);
+  char *O2 = kO2 ? dst_ptr(args, op.o2) : nullptr;
+  if (base >= op.lo && base + kTile <= op.hi) {
+    float4 a[UNROLL], b[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
+      a[u] = load4<kABf>(A, e);
+      b[u] = load4<kBBf>(B, e);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
+      const float4 s = add4(a[u], b[u]);
+      if constexpr (kOBf) {
+        const uint2 bits = pack4(s);
+        *reinterpret_cast<uint2 *>(O + e * 2) = bits;
+        if constexpr (kO2) *reinterpret_cast<uint2 *>(O2 + e * 2) = bits;
+      } else {
+        store4<false>(O, e, s);
+        if constexpr (kO2) store4<false>(O2, e, s);
+      }
+    }
+  } else {
+    for (int u = 0; u < UNROLL; ++u)
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+        if (e < op.lo || e >= op.hi) continue;
+        const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
+        store1<kOBf>(O, e, s);
+        if constexpr (kO2) store1<kOBf>(O2, e, s);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk copy: o[e] = a[e], bit copy of ES-byte elements in 16-byte units.
+// ---------------------------------------------------------------------------
+template <int ES, int UNROLL>
+__global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
+  constexpr int64_t kPerUnit = 16 / ES;
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPerUnit * UNROLL;
+  using Elem = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
+  const DevOp op = args.ops[blockIdx.y];
+  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
+  if (base >= op.hi) return;
+  const char *A = src_ptr(args, op.a);
+  char *O = dst_ptr(args, op.o);
+  if (base >= op.lo && base + kTile <= op.hi) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+      v[u] = *reinterpret_cast<const uint4 *>(A + e * ES);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+      *reinterpret_cast<uint4 *>(O + e * ES) = v[u];
+    }
+  } else {
+    for (int u = 0; u < UNROLL; ++u)
+      for (int k = 0; k < kPerUnit; ++k) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit + k;
+        if (e < op.lo || e >= op.hi) continue;
+        *reinterpret_cast<Elem *>(O + e * ES) = *reinterpret_cast<const Elem *>(A + e * ES);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-pass folds: read every rank once, fold in registers in the schedule's
+// order, write the finished value to every rank.
+// ---------------------------------------------------------------------------
+
+// Loads the 4-element unit at e of rank r for each of UNROLL slots.
+template <bool BF, int UNROLL>
+__device__ __forceinline__ void load_units(const KArgs &args, int r, int64_t base, float4 (&x)[UNROLL]) {
+  const char *p = static_cast<const char *>(args.rank[r]);
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u)
+    x[u] = load4<BF>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4);
+}
+
+template <bool BF, int UNROLL>
+__device__ __forceinline__ void store_all(const KArgs &args, int64_t base, const float4 (&acc)[UNROLL]) {
+  if constexpr (BF) {
+    uint2 bits[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) bits[u] = pack4(acc[u]);
+    for (int r = 0; r < args.nranks; ++r) {
+      char *p = static_cast<char *>(args.rank[r]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        *reinterpret_cast<uint2 *>(p + (base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4) * 2) = bits[u];
+    }
+  } else {
+    for (int r = 0; r < args.nranks; ++r) {
+      char *p = static_cast<char *>(args.rank[r]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        *reinterpret_cast<float4 *>(p + (base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4) * 4) = acc[u];
+    }
+  }
+}
+
+// acc (+)= x_r for r = first, first+1, ... (count ranks, wrapping at `wrap_n`
+// inside the block of ranks starting at `rank0`), four ranks' loads in flight
+// at a time; the adds stay in order.
+template <bool BF, int UNROLL>
+__device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, int wrap_n, int first, int count,
+                                                int64_t base, float4 (&acc)[UNROLL], bool init) {
+  int r = first;
+  int t = 0;
+  if (init) {
+    load_units<BF, UNROLL>(args, rank0 + r, base, acc);
+    r = (r + 1 == wrap_n) ? 0 : r + 1;
+    t = 1;
+  }
+  for (; t + 4 <= count; t += 4) {
+    float4 x0[UNROLL], x1[UNROLL], x2[UNROLL], x3[UNROLL];
+    const int r1 = (r + 1 == wrap_n) ? 0 : r + 1;
+    const int r2 = (r1 + 1 == wrap_n) ? 0 : r1 + 1;
+    const int r3 = (r2 + 1 == wrap_n) ? 0 : r2 + 1;
+    load_units<BF, UNROLL>(args, rank0 + r, base, x0);
+    load_units<BF, UNROLL>(args, rank0 + r1, base, x1);
+    load_units<BF, UNROLL>(args, rank0 + r2, base, x2);
+    load_units<BF, UNROLL>(args, rank0 + r3, base, x3);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc[u] = add4(add4(add4(add4(acc[u], x0[u]), x1[u]), x2[u]), x3[u]);
+    r = (r3 + 1 == wrap_n) ? 0 : r3 + 1;
+  }
+  for (; t < count; ++t) {
+    float4 x[UNROLL];
+    load_units<BF, UNROLL>(args, rank0 + r, base, x);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[u]);
+    r = (r + 1 == wrap_n) ? 0 : r + 1;
+  }
+}
+
+__device__ __forceinline__ float ring_fold1(const KArgs &args, bool bf, int rank0, int wrap_n, int first,
+                                            int count, int64_t e) {
+  auto ld = [&](int r) {
+    const char *p = static_cast<const char *>(args.rank[rank0 + r]);
+    return bf ? load1<true>(p, e) : load1<false>(p, e);
+  };
+  int r = first;
+  float acc = ld(r);
+  for (int t = 1; t < count; ++t) {
+    r = (r + 1 == wrap_n) ? 0 : r + 1;
+    acc = acc + ld(r);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e, float v) {
+  for (int r = 0; r < args.nranks; ++r) {
+    char *p = static_cast<char *>(args.rank[r]);
+    if (bf) store1<true>(p, e, v);
+    else store1<false>(p, e, v);
+  }
+}
+
+// Ring: element in chunk c is ((x_c + x_{c+1}) + ...) + x_{c+N-1}; aux = c.
+template <bool BF, int UNROLL>
+__global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const DevOp op = args.ops[blockIdx.y];
+  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
+  if (base >= op.hi) return;
+  const int n = args.nranks;
+  if (base >= op.lo && base + kTile <= op.hi) {
+    float4 acc[UNROLL];
+    ring_fold_units<BF, UNROLL>(args, 0, n, op.aux, n, base, acc, true);
+    store_all<BF, UNROLL>(args, base, acc);
+  } else {
+    for (int u = 0; u < UNROLL; ++u)
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+        if (e < op.lo || e >= op.hi) continue;
+        store_all1(args, BF, e, ring_fold1(args, BF, 0, n, op.aux, n, e));
+      }
+  }
+}
+
+// Hierarchical: group partial of slice k, ((x_{g,k+1} + x_{g,k+2}) + ...) +
+// x_{g,k}; sub-chunk j folds the group partials P_j + P_{j+1} + ... in ring
+// order.  aux = ((k + 1) mod G) | (j << 8).
+template <bool BF, int UNROLL>
+__global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const DevOp op = args.ops[blockIdx.y];
+  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
+  if (base >= op.hi) return;
+  const int G = args.group_size, M = args.nranks / G;
+  const int lstart = op.aux & 0xff, j = op.aux >> 8;
+  if (base >= op.lo && base + kTile <= op.hi) {
+    float4 acc[UNROLL];
+    int g = j;
+    for (int m = 0; m < M; ++m) {
+      float4 part[UNROLL];
+      ring_fold_units<BF, UNROLL>(args, g * G, G, lstart, G, base, part, true);
+      if (m == 0) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc[u] = part[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], part[u]);
+      }
+      g = (g + 1 == M) ? 0 : g + 1;
+    }
+    store_all<BF, UNROLL>(args, base, acc);
+  } else {
+    for (int u = 0; u < UNROLL; ++u)
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+        if (e < op.lo || e >= op.hi) continue;
+        float acc = 0.f;
+        int g = j;
+        for (int m = 0; m < M; ++m) {
+          const float part = ring_fold1(args, BF, g * G, G, lstart, G, e);
+          acc = (m == 0) ? part : acc + part;
+          g = (g + 1 == M) ? 0 : g + 1;
+        }
+        store_all1(args, BF, e, acc);
+      }
+  }
+}
+
+// Rabenseifner: the balanced pairwise tree over ranks in index order, formed
+// batch by batch (8 ranks at a time) and merged like a binary counter.
+template <bool BF, int N, int UNROLL>
+__global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
+  constexpr int kB = N < 8 ? N : 8;
+  constexpr int kBatches = N / kB;
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const DevOp op = args.ops[blockIdx.y];
+  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
+  if (base >= op.hi) return;
+  if (base >= op.lo && base + kTile <= op.hi) {
+    // each batch is an aligned block of kB ranks, so the tree over batch
+    // results in index order completes the balanced tree over all N ranks
+    float4 res[kBatches][UNROLL];
+#pragma unroll
+    for (int bi = 0; bi < kBatches; ++bi) {
+      float4 v[kB][UNROLL];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
+#pragma unroll
+      for (int w = kB; w > 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i)
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) v[i][u] = add4(v[2 * i][u], v[2 * i + 1][u]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
+    }
+#pragma unroll
+    for (int w = kBatches; w > 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) res[i][u] = add4(res[2 * i][u], res[2 * i + 1][u]);
+    store_all<BF, UNROLL>(args, base, res[0]);
+  } else {
+    for (int u = 0; u < UNROLL; ++u)
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+        if (e < op.lo || e >= op.hi) continue;
+        float level[N];
+        for (int r = 0; r < N; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
+        for (int w = N; w > 1; w /= 2)
+          for (int i = 0; i < w / 2; ++i) level[i] = level[2 * i] + level[2 * i + 1];
+        store_all1(args, BF, e, level[0]);
+      }
+  }
+}
+
+constexpr int kReduceUnroll = AR_REDUCE_UNROLL;
+constexpr int kCopyUnroll = AR_COPY_UNROLL;
+constexpr int kOnePassUnroll = AR_ONEPASS_UNROLL;
+
+template <int FLAGS>
+hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool BF>
+hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (n) {
+    case 2: hipLaunchKernelGGL((onepass_tree<BF, 2, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((onepass_tree<BF, 4, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((onepass_tree<BF, 8, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((onepass_tree<BF, 16, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((onepass_tree<BF, 32, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((onepass_tree<BF, 64, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t tile_elems(int32_t kind) {
+  switch (kind & 0xF00) {
+    case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * kReduceUnroll;
+    case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * kCopyUnroll;
+    default: return static_cast<int64_t>(kBlock) * 4 * kOnePassUnroll;
+  }
+}
+
+hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (kind & 0xF00) {
+    case kKindReduce:
+      switch (kind & 0xF) {
+        case 0: return launch_reduce<0>(grid, a, s);
+        case 1: return launch_reduce<1>(grid, a, s);
+        case 2: return launch_reduce<2>(grid, a, s);
+        case 3: return launch_reduce<3>(grid, a, s);
+        case 4: return launch_reduce<4>(grid, a, s);
+        case 5: return launch_reduce<5>(grid, a, s);
+        case 6: return launch_reduce<6>(grid, a, s);
+        case 7: return launch_reduce<7>(grid, a, s);
+        case 8: return launch_reduce<8>(grid, a, s);
+        case 9: return launch_reduce<9>(grid, a, s);
+        case 10: return launch_reduce<10>(grid, a, s);
+        case 11: return launch_reduce<11>(grid, a, s);
+        case 12: return launch_reduce<12>(grid, a, s);
+        case 13: return launch_reduce<13>(grid, a, s);
+        case 14: return launch_reduce<14>(grid, a, s);
+        case 15: return launch_reduce<15>(grid, a, s);
+      }
+      break;
+    case kKindCopy:
+      if ((kind & 0xFF) == 2) hipLaunchKernelGGL((chunk_copy<2, kCopyUnroll>), grid, dim3(kBlock), 0, s, a);
+      else if ((kind & 0xFF) == 4) hipLaunchKernelGGL((chunk_copy<4, kCopyUnroll>), grid, dim3(kBlock), 0, s, a);
+      else return hipErrorInvalidValue;
+      return hipGetLastError();
+    case kKindRing:
+      if (kind & 1) hipLaunchKernelGGL((onepass_ring<true, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((onepass_ring<false, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      return hipGetLastError();
+    case kKindHier:
+      if (kind & 1) hipLaunchKernelGGL((onepass_hier<true, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((onepass_hier<false, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      return hipGetLastError();
+    case kKindTree:
+      return (kind & 1) ? launch_tree<true>(a.nranks, grid, a, s) : launch_tree<false>(a.nranks, grid, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ar_dev

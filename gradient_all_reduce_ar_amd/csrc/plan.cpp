@@ -1,0 +1,457 @@
+// plan.cpp -- schedule builders, lowering to kernel launches, statistics.
+//
+// Sources, cited by short tag:
+//   [PRIMER]  "Collective communication: algorithms, cost and the library that
+//             runs them", AI training network primer, chapter 4.
+//   [SCALING] "Collective communication", Scaling ML systems, chapter 06.
+//   [DCN]     "Chapter 7. Data-center networks", AI infrastructure book.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <map>
+
+namespace ar {
+
+int64_t elem_bytes(Dtype d) { return d == kBF16 ? 2 : 4; }
+
+namespace {
+
+// Part c of a range [base, base+len) cut into k parts: the floor-balanced
+// contiguous split (the pages cut the buffer "into N equal parts"; sizes that
+// do not divide are split at floor(c*len/k)).
+struct Cut {
+  int64_t base, len, k;
+  int64_t lo(int64_t c) const { return base + static_cast<int64_t>((static_cast<__int128>(c) * len) / k); }
+  int64_t hi(int64_t c) const { return lo(c + 1); }
+};
+
+inline int wrap(int v, int n) { return ((v % n) + n) % n; }
+
+// Ring over `ring` (ring position -> rank), data range cut into ring.size()
+// chunks.  [PRIMER] 4.2: reduce-scatter step s sends chunk (i - s) mod n from
+// position i to i+1, which adds; all-gather step s sends chunk (i + 1 - s)
+// mod n and the receiver stores it.  `shift` rotates chunk numbering
+// (chunk index = rule index + shift), used by the hierarchical phases.
+struct RingPhase {
+  std::vector<int> ring;
+  Cut cut;
+  int shift;
+};
+
+void emit_ring_rs(std::vector<Transfer> &out, const RingPhase &r, int step0, bool completes_last) {
+  const int n = static_cast<int>(r.ring.size());
+  for (int s = 0; s + 1 < n; ++s)
+    for (int i = 0; i < n; ++i) {
+      const int c = wrap(i - s + r.shift, n);
+      out.push_back({step0 + s, r.ring[i], r.ring[(i + 1) % n], r.cut.lo(c), r.cut.hi(c), kReduce,
+                     completes_last && s == n - 2});
+    }
+}
+
+void emit_ring_ag(std::vector<Transfer> &out, const RingPhase &r, int step0) {
+  const int n = static_cast<int>(r.ring.size());
+  for (int s = 0; s + 1 < n; ++s)
+    for (int i = 0; i < n; ++i) {
+      const int c = wrap(i + 1 - s + r.shift, n);
+      out.push_back({step0 + s, r.ring[i], r.ring[(i + 1) % n], r.cut.lo(c), r.cut.hi(c), kCopy, false});
+    }
+}
+
+int build_ring(std::vector<Transfer> &out, int n, int64_t count) {
+  RingPhase r{{}, Cut{0, count, n}, 0};
+  for (int i = 0; i < n; ++i) r.ring.push_back(i);
+  emit_ring_rs(out, r, 0, true);
+  emit_ring_ag(out, r, n - 1);
+  return 2 * (n - 1);
+}
+
+// [PRIMER] 4.4 / Animation 4.3, [DCN] 7.2.1.  Group g = ranks g*G .. g*G+G-1.
+// Phase 1 is the group ring with chunk numbering shifted by -1 (local l sends
+// slice (l - 1 - s) mod G), so local k ends owning slice k.  Phase 2 runs a
+// flat ring all-reduce of slice l over the M ranks {m*G + l}.  Phase 3 is the
+// group all-gather in which local l first sends slice l.
+int build_hier(std::vector<Transfer> &out, int n, int g_size, int64_t count) {
+  const int groups = n / g_size;
+  const Cut slices{0, count, g_size};
+  int step = 0;
+  for (int g = 0; g < groups; ++g) {
+    RingPhase r{{}, slices, -1};
+    for (int l = 0; l < g_size; ++l) r.ring.push_back(g * g_size + l);
+    emit_ring_rs(out, r, step, groups == 1);
+  }
+  step += g_size - 1;
+  for (int l = 0; l < g_size; ++l) {
+    RingPhase r{{}, Cut{slices.lo(l), slices.hi(l) - slices.lo(l), groups}, 0};
+    for (int m = 0; m < groups; ++m) r.ring.push_back(m * g_size + l);
+    emit_ring_rs(out, r, step, true);
+    emit_ring_ag(out, r, step + groups - 1);
+  }
+  step += 2 * (groups - 1);
+  for (int g = 0; g < groups; ++g) {
+    // all-gather rule (i + 1 - s) shifted by -1 gives slice (l - s) mod G
+    RingPhase r{{}, slices, -1};
+    for (int l = 0; l < g_size; ++l) r.ring.push_back(g * g_size + l);
+    emit_ring_ag(out, r, step);
+  }
+  step += g_size - 1;
+  return step;
+}
+
+// [PRIMER] 4.3 (Figure 4.5, Animation 4.2), [SCALING] "Recursive halving and
+// doubling".  N = 2^L.  Reduce-scatter round k = 1..L pairs i with
+// i ^ 2^(k-1); the held chunk range halves, the lower half kept when bit k-1
+// of i is 0 (so rank i ends owning chunk bitrev(i)).  The all-gather runs the
+// rounds in reverse; each rank sends all it holds and the partner stores it.
+int build_raben(std::vector<Transfer> &out, int n, int64_t count) {
+  int levels = 0;
+  while ((1 << levels) < n) ++levels;
+  const Cut chunks{0, count, n};
+  // held[k][i] = chunk range [first, last) of rank i after reduce-scatter round k
+  std::vector<std::vector<std::pair<int, int>>> held(levels + 1, std::vector<std::pair<int, int>>(n));
+  for (int i = 0; i < n; ++i) held[0][i] = {0, n};
+  for (int k = 1; k <= levels; ++k) {
+    const int bit = 1 << (k - 1);
+    for (int i = 0; i < n; ++i) {
+      const auto [first, last] = held[k - 1][i];
+      const int mid = (first + last) / 2;
+      held[k][i] = (i & bit) ? std::make_pair(mid, last) : std::make_pair(first, mid);
+    }
+    for (int i = 0; i < n; ++i) {
+      const int partner = i ^ bit;
+      const auto [f, l] = held[k][partner];  // i sends what its partner keeps
+      out.push_back({k - 1, i, partner, chunks.lo(f), chunks.lo(l), kReduce, k == levels});
+    }
+  }
+  for (int k = levels; k >= 1; --k) {
+    const int step = levels + (levels - k);
+    for (int i = 0; i < n; ++i) {
+      const auto [f, l] = held[k][i];
+      out.push_back({step, i, i ^ (1 << (k - 1)), chunks.lo(f), chunks.lo(l), kCopy, false});
+    }
+  }
+  return 2 * levels;
+}
+
+// Scratch slot holding rank r's fp32 partial sums.  Two ranks share a slot
+// only when their partial ranges can never overlap while both are live:
+//   ring: one live partial per chunk (it travels round the ring) -> 1 slot;
+//   hierarchical: per group, partials of distinct slices           -> M slots;
+//   Rabenseifner: ranks 2m and 2m+1 keep disjoint halves from round 1 on
+//                 and later ranges nest inside those halves         -> N/2 slots.
+int slot_of(const Plan &p, int r) {
+  switch (p.sched) {
+    case kRing: return 0;
+    case kHier: return (p.group_size == 1 || p.group_size == p.nranks) ? 0 : r / p.group_size;
+    case kRaben: return r >> 1;
+  }
+  return 0;
+}
+
+// Per-rank record of the element ranges whose current value is an fp32
+// partial sum in scratch (bf16 lowering).
+struct PartialMap {
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> ranges;
+  explicit PartialMap(int n) : ranges(n) {}
+  // 1: [lo,hi) entirely partial, 0: entirely original input, -1: mixed.
+  int state(int r, int64_t lo, int64_t hi) const {
+    int64_t covered = 0;
+    for (const auto &x : ranges[r]) covered += std::max<int64_t>(0, std::min(hi, x.second) - std::max(lo, x.first));
+    if (covered == 0) return 0;
+    return covered == hi - lo ? 1 : -1;
+  }
+  void mark(int r, int64_t lo, int64_t hi) {
+    if (state(r, lo, hi) == 0) ranges[r].push_back({lo, hi});
+  }
+};
+
+std::string lower_steps(Plan &p, bool fuse) {
+  p.launches.clear();
+  const bool bf = p.dtype == kBF16;
+  PartialMap partial(p.nranks);
+  std::vector<bool> finals;  // per launch: all its reduces complete their range
+  int max_slot = -1;
+  size_t j = 0;
+  while (j < p.xfers.size()) {
+    size_t j1 = j;
+    while (j1 < p.xfers.size() && p.xfers[j1].step == p.xfers[j].step) ++j1;
+    // split the round by (kind, operand types, completion) so each launch is
+    // uniform; key bit 16 marks reduces that complete their range
+    std::map<int32_t, Launch> by_kind;
+    std::vector<size_t> to_mark;
+    for (size_t t = j; t < j1; ++t) {
+      const Transfer &x = p.xfers[t];
+      if (x.hi <= x.lo) continue;
+      Op op{x.lo, x.hi, kLocNone, kLocNone, kLocNone, kLocNone, 0};
+      int32_t kind;
+      if (x.kind == kCopy) {
+        kind = kKCopy | static_cast<int32_t>(elem_bytes(p.dtype));
+        op.a = x.src;
+        op.o = x.dst;
+      } else if (!bf) {
+        kind = kKReduce;
+        op.a = x.src;
+        op.b = x.dst;
+        op.o = x.dst;
+      } else {
+        const int sa = partial.state(x.src, x.lo, x.hi), sb = partial.state(x.dst, x.lo, x.hi);
+        if (sa < 0 || sb < 0) return "internal: reduce over a range that is partly partial";
+        kind = kKReduce;
+        op.a = sa ? kLocScratch + slot_of(p, x.src) : x.src;
+        op.b = sb ? kLocScratch + slot_of(p, x.dst) : x.dst;
+        if (!sa) kind |= kFlagABf;
+        if (!sb) kind |= kFlagBBf;
+        if (sa) max_slot = std::max(max_slot, slot_of(p, x.src));
+        if (sb) max_slot = std::max(max_slot, slot_of(p, x.dst));
+        if (x.final_sum) {
+          kind |= kFlagOBf;
+          op.o = x.dst;
+        } else {
+          op.o = kLocScratch + slot_of(p, x.dst);
+          max_slot = std::max(max_slot, slot_of(p, x.dst));
+          to_mark.push_back(t);
+        }
+      }
+      const int32_t key = kind | ((x.kind == kReduce && x.final_sum) ? 0x10000 : 0);
+      Launch &L = by_kind[key];
+      L.kind = kind;
+      L.ops.push_back(op);
+    }
+    // partial sums written this round become visible to the next round
+    for (size_t t : to_mark) partial.mark(p.xfers[t].dst, p.xfers[t].lo, p.xfers[t].hi);
+    for (auto &kv : by_kind) {
+      finals.push_back((kv.first & 0x10000) != 0);
+      p.launches.push_back(std::move(kv.second));
+    }
+    j = j1;
+  }
+  p.nslots = max_slot + 1;
+
+  if (fuse) {
+    // The reduce that completes a chunk, followed by the copy that first
+    // forwards it ([PRIMER] 4.2: all-gather step 0 sends the chunk the
+    // sender has just completed), becomes one launch whose ops write the
+    // finished value to the receiver and to the next rank.
+    std::vector<Launch> fused;
+    for (size_t i = 0; i < p.launches.size(); ++i) {
+      Launch &L = p.launches[i];
+      if (finals[i] && i + 1 < p.launches.size() && (p.launches[i + 1].kind & 0xF00) == kKCopy &&
+          p.launches[i + 1].ops.size() == L.ops.size()) {
+        Launch trial = L;
+        bool ok = true;
+        for (const Op &c : p.launches[i + 1].ops) {
+          bool found = false;
+          for (Op &r : trial.ops)
+            if (r.o == c.a && r.lo == c.lo && r.hi == c.hi && r.o2 == kLocNone) {
+              r.o2 = c.o;
+              found = true;
+              break;
+            }
+          if (!found) { ok = false; break; }
+        }
+        if (ok) {
+          trial.kind |= kFlagO2;
+          fused.push_back(std::move(trial));
+          ++i;  // the copy launch is absorbed
+          continue;
+        }
+      }
+      fused.push_back(std::move(L));
+    }
+    p.launches = std::move(fused);
+  }
+  return "";
+}
+
+std::string lower_onepass(Plan &p) {
+  p.launches.clear();
+  p.nslots = 0;
+  if (p.nranks == 1 || p.count == 0) return "";
+  const int32_t dt = p.dtype;
+  if (p.sched == kRing) {
+    // element in chunk c: ((x_c + x_{c+1}) + ...) + x_{c+N-1} -- chunk c is
+    // first sent by rank c at reduce-scatter step 0 and gains one rank per step
+    Launch L{kKRing | dt, {}};
+    const Cut cut{0, p.count, p.nranks};
+    for (int c = 0; c < p.nranks; ++c)
+      if (cut.hi(c) > cut.lo(c)) L.ops.push_back({cut.lo(c), cut.hi(c), kLocNone, kLocNone, kLocNone, kLocNone, c});
+    p.launches.push_back(std::move(L));
+  } else if (p.sched == kHier) {
+    // slice k of group g: ((x_{g,k+1} + x_{g,k+2}) + ...) + x_{g,k}; then sub-chunk
+    // j of the slice folds the group partials as a ring starting at group j
+    const int G = p.group_size, M = p.nranks / p.group_size;
+    Launch L{kKHier | dt, {}};
+    const Cut slices{0, p.count, G};
+    for (int k = 0; k < G; ++k) {
+      const Cut sub{slices.lo(k), slices.hi(k) - slices.lo(k), M};
+      for (int jj = 0; jj < M; ++jj)
+        if (sub.hi(jj) > sub.lo(jj))
+          L.ops.push_back({sub.lo(jj), sub.hi(jj), kLocNone, kLocNone, kLocNone, kLocNone,
+                           ((k + 1) % G) | (jj << 8)});
+    }
+    p.launches.push_back(std::move(L));
+  } else {
+    // balanced pairwise tree over ranks in index order, the same for every
+    // element: ((x0 + x1) + (x2 + x3)) + ...
+    Launch L{kKTree | dt, {}};
+    L.ops.push_back({0, p.count, kLocNone, kLocNone, kLocNone, kLocNone, 0});
+    p.launches.push_back(std::move(L));
+  }
+  return "";
+}
+
+uint64_t loc_bytes(const Plan &p, int32_t loc, bool bf16_flag) {
+  if (loc == kLocNone) return 0;
+  if (p.dtype == kF32) return 4;
+  return bf16_flag ? 2 : 4;
+}
+
+void compute_stats(Plan &p) {
+  p.bytes_sent.assign(p.nranks, 0);
+  p.cross_group_bytes = 0;
+  const uint64_t eb = static_cast<uint64_t>(elem_bytes(p.dtype));
+  for (const Transfer &x : p.xfers) {
+    const uint64_t b = static_cast<uint64_t>(x.hi - x.lo) * eb;
+    p.bytes_sent[x.src] += b;
+    if (x.src / p.group_size != x.dst / p.group_size) p.cross_group_bytes += b;
+  }
+  uint64_t h = 0;
+  for (const Launch &L : p.launches) {
+    const int32_t fam = L.kind & 0xF00;
+    for (const Op &op : L.ops) {
+      const uint64_t len = static_cast<uint64_t>(op.hi - op.lo);
+      if (fam == kKReduce) {
+        const bool obf = L.kind & kFlagOBf;
+        h += len * (loc_bytes(p, op.a, L.kind & kFlagABf) + loc_bytes(p, op.b, L.kind & kFlagBBf) +
+                    loc_bytes(p, op.o, obf) + loc_bytes(p, op.o2, obf));
+      } else if (fam == kKCopy) {
+        h += len * 2 * eb;
+      } else {
+        h += len * 2 * eb * static_cast<uint64_t>(p.nranks);
+      }
+    }
+  }
+  p.hbm_bytes = h;
+}
+
+std::string lower(Plan &p, Exec exec) {
+  p.exec = exec;
+  std::string err;
+  if (exec == kOnePass) err = lower_onepass(p);
+  else err = lower_steps(p, exec == kSteps);
+  if (!err.empty()) return err;
+  p.slot_stride = (p.count + 63) / 64 * 64;
+  compute_stats(p);
+  return check_hazards(p);
+}
+
+}  // namespace
+
+std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype, Sched sched,
+                       Exec exec, bool *unsupported) {
+  *unsupported = false;
+  if (nranks < 1 || nranks > 64) return "nranks must be in [1, 64]";
+  if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
+  if (count < 0) return "count must be >= 0";
+  if (dtype != kF32 && dtype != kBF16) return "unknown dtype";
+  if (sched != kRing && sched != kHier && sched != kRaben) return "unknown schedule";
+  if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
+  if (sched == kRaben && (nranks & (nranks - 1))) {
+    *unsupported = true;
+    return "Rabenseifner needs a power-of-two number of ranks";
+  }
+  p = Plan{};
+  p.nranks = nranks;
+  p.group_size = group_size;
+  p.count = count;
+  p.dtype = dtype;
+  p.sched = sched;
+  if (sched == kRing) p.nsteps = build_ring(p.xfers, nranks, count);
+  else if (sched == kHier) p.nsteps = build_hier(p.xfers, nranks, group_size, count);
+  else p.nsteps = build_raben(p.xfers, nranks, count);
+  std::stable_sort(p.xfers.begin(), p.xfers.end(),
+                   [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
+  return lower(p, exec);
+}
+
+std::string relower(Plan &p, Exec exec) {
+  if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
+  return lower(p, exec);
+}
+
+double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw_cross) {
+  // [DCN] 7.2.1: rounds run one after another; within a round the slowest
+  // transfer sets the time, and every round pays its start-up alpha.
+  std::vector<double> slowest(static_cast<size_t>(p.nsteps), 0.0);
+  const double eb = static_cast<double>(elem_bytes(p.dtype));
+  for (const Transfer &x : p.xfers) {
+    const bool cross = x.src / p.group_size != x.dst / p.group_size;
+    const double t = static_cast<double>(x.hi - x.lo) * eb / (cross ? bw_cross : bw_intra);
+    slowest[x.step] = std::max(slowest[x.step], t);
+  }
+  double total = 0;
+  for (double t : slowest) total += alpha_s + t;
+  return total;
+}
+
+std::string check_hazards(const Plan &p) {
+  struct Acc { int32_t loc; int64_t lo, hi; bool write; };
+  for (size_t li = 0; li < p.launches.size(); ++li) {
+    const Launch &L = p.launches[li];
+    const int32_t fam = L.kind & 0xF00;
+    if (fam != kKReduce && fam != kKCopy) continue;  // one-pass ops touch disjoint ranges by construction
+    std::vector<std::vector<Acc>> acc(L.ops.size());
+    for (size_t i = 0; i < L.ops.size(); ++i) {
+      const Op &o = L.ops[i];
+      for (int32_t r : {o.a, o.b})
+        if (r != kLocNone) acc[i].push_back({r, o.lo, o.hi, false});
+      for (int32_t w : {o.o, o.o2})
+        if (w != kLocNone) acc[i].push_back({w, o.lo, o.hi, true});
+    }
+    for (size_t i = 0; i < acc.size(); ++i)
+      for (size_t k = i + 1; k < acc.size(); ++k)
+        for (const Acc &x : acc[i])
+          for (const Acc &y : acc[k])
+            if ((x.write || y.write) && x.loc == y.loc && x.lo < y.hi && y.lo < x.hi) {
+              char buf[160];
+              std::snprintf(buf, sizeof buf, "hazard in launch %zu: ops %zu and %zu touch location %d", li, i, k,
+                            x.loc);
+              return buf;
+            }
+  }
+  return "";
+}
+
+void assign_buckets(const std::vector<int64_t> &tensor_counts, int64_t cap_elems, int64_t align_elems,
+                    std::vector<int64_t> &tensor_offsets, std::vector<int64_t> &bucket_offset,
+                    std::vector<int64_t> &bucket_count, int64_t &arena_count) {
+  // [SCALING] "Bucket fusion": parameters go into buckets in the reverse of
+  // their forward order, the order their gradients become ready in backward.
+  const int n = static_cast<int>(tensor_counts.size());
+  tensor_offsets.assign(n, 0);
+  bucket_offset.clear();
+  bucket_count.clear();
+  int64_t cursor = 0, fill = -1;  // fill < 0: no open bucket
+  for (int t = n - 1; t >= 0; --t) {
+    const int64_t c = tensor_counts[t];
+    if (fill >= 0 && fill > 0 && fill + c > cap_elems) {  // close the open bucket
+      bucket_count.push_back(fill);
+      cursor = bucket_offset.back() + fill;
+      fill = -1;
+    }
+    if (fill < 0) {
+      cursor = (cursor + align_elems - 1) / align_elems * align_elems;
+      bucket_offset.push_back(cursor);
+      fill = 0;
+    }
+    tensor_offsets[t] = bucket_offset.back() + fill;
+    fill += c;
+  }
+  if (fill >= 0) {
+    bucket_count.push_back(fill);
+    cursor = bucket_offset.back() + fill;
+  }
+  arena_count = cursor;
+}
+
+}  // namespace ar

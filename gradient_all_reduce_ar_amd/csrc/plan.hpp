@@ -1,0 +1,101 @@
+// plan.hpp -- host-side schedule planner of the gradient all-reduce library.
+//
+// The planner turns (nranks, group_size, count, dtype, schedule) into
+//   1. the logical transfers of the schedule, round by round, and
+//   2. the kernel launches that execute them on one GPU, with every operand
+//      resolved to a rank buffer or an fp32 scratch slot.
+// It is plain C++17 and touches no device.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace ar {
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+enum Sched : int32_t { kRing = 0, kHier = 1, kRaben = 2 };
+enum Exec : int32_t { kSteps = 0, kStepsUnfused = 1, kOnePass = 2 };
+enum XferKind : int32_t { kReduce = 0, kCopy = 1 };
+
+// One message of the schedule: in round `step`, rank `src` sends elements
+// [lo, hi) to rank `dst`, which adds them to its own copy (kReduce) or stores
+// them (kCopy).  `final_sum` marks the reduce that leaves the receiver's
+// range complete.
+struct Transfer {
+  int32_t step, src, dst;
+  int64_t lo, hi;
+  int32_t kind;
+  bool final_sum;
+};
+
+// Operand location codes.
+constexpr int32_t kLocNone = -1;
+constexpr int32_t kLocScratch = 1000;  // 1000 + s: fp32 scratch slot s
+
+// Kernel kind codes.
+//   kKReduce | flags: out = A + B (fp32 add), written to o and optionally o2.
+//     flag 1: A is bf16, 2: B is bf16, 4: outputs are bf16 (rounded), 8: has o2.
+//   kKCopy | elem_bytes: o = a, bit copy.
+//   kKRing / kKHier / kKTree | dtype: one-pass fold over all ranks.
+constexpr int32_t kKReduce = 0x100;
+constexpr int32_t kKCopy = 0x200;
+constexpr int32_t kKRing = 0x300;
+constexpr int32_t kKHier = 0x400;
+constexpr int32_t kKTree = 0x500;
+constexpr int32_t kFlagABf = 1, kFlagBBf = 2, kFlagOBf = 4, kFlagO2 = 8;
+
+struct Op {
+  int64_t lo, hi;
+  int32_t a, b, o, o2;
+  int32_t aux;  // one-pass folds: start rank (ring) or packed starts (hier)
+};
+
+struct Launch {
+  int32_t kind;
+  std::vector<Op> ops;
+};
+
+struct Plan {
+  int32_t nranks = 0, group_size = 1;
+  int64_t count = 0;
+  Dtype dtype = kF32;
+  Sched sched = kRing;
+  Exec exec = kSteps;
+  int32_t nsteps = 0;
+  std::vector<Transfer> xfers;   // ordered by step
+  std::vector<Launch> launches;  // for `exec`
+  int32_t nslots = 0;            // fp32 scratch slots used by `launches`
+  int64_t slot_stride = 0;       // elements per slot (multiple of 64)
+  std::vector<uint64_t> bytes_sent;
+  uint64_t cross_group_bytes = 0;
+  uint64_t hbm_bytes = 0;        // algorithmic device bytes of `launches`
+};
+
+int64_t elem_bytes(Dtype d);
+
+// Builds the transfers and the launches for `exec`.  Returns an empty string
+// on success, else the reason for failure; *unsupported is set when the
+// request is valid but not supported (Rabenseifner with N not 2^k).
+std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype,
+                       Sched sched, Exec exec, bool *unsupported);
+
+// Re-lowers an existing plan for another exec mode.
+std::string relower(Plan &p, Exec exec);
+
+// Per-round alpha-beta model over the transfers (seconds).
+double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw_cross);
+
+// Checks that within every launch no op writes a (location, range) that
+// another op of the same launch reads or writes.  Empty string if clean.
+std::string check_hazards(const Plan &p);
+
+// Bucket fuser: assigns tensors (element counts) to buckets in reverse
+// tensor order under `cap_elems`; fills per-tensor arena offsets, bucket
+// ranges and the arena length.  Buckets start on `align_elems` boundaries.
+void assign_buckets(const std::vector<int64_t> &tensor_counts, int64_t cap_elems,
+                    int64_t align_elems, std::vector<int64_t> &tensor_offsets,
+                    std::vector<int64_t> &bucket_offset, std::vector<int64_t> &bucket_count,
+                    int64_t &arena_count);
+
+}  // namespace ar

@@ -13,6 +13,8 @@ which uses the fp32 [12288, 4096] FFN gate-projection gradient of Qwen3-8B,
   bucketed : 300 tensors whose byte sizes are lognormal (median 256 KiB),
              values N(0, 1e-3) per (rank, tensor), bf16
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GATE_PROJ_ELEMS = 12288 * 4096  # 50,331,648 fp32 elements = 192 MiB
@@ -38,13 +40,21 @@ def normal_rank(r, count, seed=0, sigma=1e-3, dtype="fp32"):
     return x if dtype == "fp32" else _to_bf16_bits(x)
 
 
+def _per_rank(fn, nranks):
+    # each rank draws from its own generator, so threads give the same numbers
+    if nranks <= 1:
+        return [fn(r) for r in range(nranks)]
+    with ThreadPoolExecutor(min(8, nranks)) as ex:
+        return list(ex.map(fn, range(nranks)))
+
+
 def uniform_inputs(nranks, count, seed=0, dtype="fp32"):
-    xs = [uniform_rank(r, count, seed) for r in range(nranks)]
+    xs = _per_rank(lambda r: uniform_rank(r, count, seed), nranks)
     return xs if dtype == "fp32" else [_to_bf16_bits(x) for x in xs]
 
 
 def normal_inputs(nranks, count, seed=0, sigma=1e-3, dtype="fp32"):
-    return [normal_rank(r, count, seed, sigma, dtype) for r in range(nranks)]
+    return _per_rank(lambda r: normal_rank(r, count, seed, sigma, dtype), nranks)
 
 
 def integer_inputs(nranks, count, seed=0, lo=-8, hi=8, dtype="fp32"):

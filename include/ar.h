@@ -1,0 +1,227 @@
+/*
+ * ar.h -- C ABI of the MI355X gradient all-reduce library (libar.so).
+ *
+ * N virtual ranks' gradient buffers live in one GPU's HBM.  The library runs
+ * the chunked reduce and copy schedules of gradient all-reduce on them, in
+ * place, with hand-written HIP kernels for gfx950:
+ *
+ *   AR_RING          ring reduce-scatter followed by ring all-gather.
+ *                    "Collective communication: algorithms, cost and the
+ *                    library that runs them" (AI training network primer,
+ *                    ch. 4), section 4.2, the two index rules and Figures
+ *                    4.1-4.3; "Collective communication" (Scaling ML systems,
+ *                    ch. 06), the "Ring AllReduce" algorithm box.
+ *   AR_HIERARCHICAL  intra-group ring reduce-scatter, all-reduce of each slice
+ *                    among the ranks with the same local index across groups,
+ *                    intra-group ring all-gather.  Primer ch. 4 section 4.4
+ *                    (Figure 4.8, Animation 4.3); "Chapter 7. Data-center
+ *                    networks" (AI infrastructure book), section 7.2.1.
+ *   AR_RABENSEIFNER  recursive-halving reduce-scatter then recursive-doubling
+ *                    all-gather.  Primer ch. 4 section 4.3 (Figure 4.5,
+ *                    Animation 4.2); Scaling ML systems ch. 06, "Recursive
+ *                    halving and doubling (butterfly)".
+ *
+ * Result.  On completion every rank buffer holds G_0 + ... + G_{N-1}
+ * (Scaling ML systems ch. 06, the algorithm box's output), summed in the
+ * exact per-element order of the chosen schedule: floating-point addition is
+ * not associative, so the schedule fixes the low bits.
+ *
+ * Datatypes.  AR_FLOAT32: one IEEE binary32 add per reduction, denormals
+ * kept.  AR_BFLOAT16: inputs widen exactly to fp32, partial sums are kept in
+ * fp32 (in plan-owned device scratch), and each element is rounded to bf16
+ * (nearest, ties to even; NaN stays NaN with its sign) once, when its chunk
+ * is complete; all-gather copies bf16 bits.
+ *
+ * Partition.  A range of L elements cut into K parts gives part c the
+ * elements [floor(c*L/K), floor((c+1)*L/K)).
+ *
+ * Conventions.  All calls are thread-compatible, not thread-safe per plan.
+ * Errors never abort: a failing call returns a status (or NULL / a negative
+ * value) and sets a thread-local message readable with ar_last_error().
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AR_OK = 0,
+  AR_ERR_INVALID_ARG = 1, /* bad argument: sizes, NULL or misaligned pointers */
+  AR_ERR_UNSUPPORTED = 2, /* e.g. Rabenseifner with N not a power of two       */
+  AR_ERR_OOM = 3,         /* device scratch or table allocation failed         */
+  AR_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed         */
+} ar_status_t;
+
+typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1 } ar_dtype_t;
+
+typedef enum { AR_RING = 0, AR_HIERARCHICAL = 1, AR_RABENSEIFNER = 2 } ar_schedule_t;
+
+/*
+ * How a plan is executed.  Every mode gives bit-identical results.
+ *   AR_EXEC_STEPS          one kernel launch per step of the schedule; the
+ *                          reduce-scatter step that completes a chunk is fused
+ *                          with the all-gather step that first forwards it
+ *                          (the receiver writes the finished chunk to itself
+ *                          and to the next rank).  Default.
+ *   AR_EXEC_STEPS_UNFUSED  one kernel launch per step, no fusion.
+ *   AR_EXEC_ONEPASS        one launch for the whole all-reduce: every element
+ *                          is read once from each rank, folded in registers in
+ *                          the schedule's exact order, and written once to
+ *                          each rank.
+ */
+typedef enum { AR_EXEC_STEPS = 0, AR_EXEC_STEPS_UNFUSED = 1, AR_EXEC_ONEPASS = 2 } ar_exec_t;
+
+/* Maximum number of virtual ranks per plan. */
+#define AR_MAX_RANKS 64
+
+typedef struct ar_plan ar_plan_t;
+
+typedef struct {
+  int32_t nranks, group_size;
+  uint32_t steps;                   /* sequential rounds of the schedule            */
+  uint32_t launches;                /* kernel launches per call in the exec mode    */
+  uint64_t count, elem_bytes;
+  const uint64_t *bytes_sent;       /* [nranks], plan-owned: logical bytes each rank
+                                       sends, in the buffer's dtype                 */
+  uint64_t bytes_sent_max, bytes_sent_total;
+  uint64_t cross_group_bytes_total; /* bytes whose sender and receiver lie in
+                                       different groups of group_size contiguous
+                                       ranks (Data-center networks 7.2.1)          */
+  uint64_t hbm_bytes_model;         /* device bytes read + written per call in the
+                                       exec mode (algorithmic count)               */
+  uint64_t scratch_bytes;           /* fp32 partial-sum scratch the plan owns       */
+  int32_t exec;                     /* ar_exec_t in effect                          */
+} ar_stats_t;
+
+/*
+ * Builds the schedule for nranks virtual ranks of `count` elements each.
+ * Host only: no device memory is touched until the first ar_allreduce (or
+ * ar_plan_prepare).  group_size: ranks g*G .. g*G+G-1 form group g; it must
+ * divide nranks.  For AR_HIERARCHICAL it sets the intra-group size; for the
+ * other schedules it only labels groups for cross_group_bytes_total.
+ * Returns NULL on error: nranks outside [1, AR_MAX_RANKS], group_size < 1 or
+ * not dividing nranks, unknown dtype or schedule (AR_ERR_INVALID_ARG);
+ * Rabenseifner with nranks not a power of two (AR_ERR_UNSUPPORTED).
+ */
+ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype,
+                          ar_schedule_t schedule);
+
+/* Selects the execution mode (see ar_exec_t).  Host only. */
+ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
+
+/*
+ * Allocates the plan's device op tables and, for bf16, its fp32 scratch on
+ * the current HIP device, and uploads the tables (synchronously).  Called
+ * implicitly by the first ar_allreduce; call it explicitly before capturing
+ * ar_allreduce into a HIP graph.  AR_ERR_OOM / AR_ERR_HIP on failure.  A plan
+ * is bound to the device current at its first prepare.
+ */
+ar_status_t ar_plan_prepare(ar_plan_t *plan);
+
+/*
+ * All-reduce, in place.  rank_bufs: host array of nranks device pointers,
+ * read during the call only; buffer r holds >= count elements of the plan's
+ * dtype, is 16-byte aligned and overlaps no other rank's buffer.  stream: a
+ * hipStream_t (NULL = default stream).  Enqueues the kernels and returns;
+ * the result is visible after stream synchronisation (the initiating call of
+ * a collective returns before completion -- Scaling ML systems ch. 06).
+ * Calls that share a plan must not overlap in time (they share scratch).
+ * AR_ERR_INVALID_ARG for NULL/misaligned pointers or a different device than
+ * the plan's; AR_ERR_HIP if a launch fails.
+ */
+ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream);
+
+/* Statistics of the plan (valid until the plan is destroyed or re-moded). */
+ar_stats_t ar_plan_stats(const ar_plan_t *plan);
+
+/*
+ * Per-round alpha-beta time in seconds (Data-center networks 7.2.1):
+ *   T = sum over rounds r of (alpha + max over transfers e of V_{r,e} / B_e),
+ * B_e = bw_intra_Bps within a group, bw_cross_Bps across groups; every rank
+ * has its own link of each class.  Negative on error.
+ */
+double ar_plan_cost_alpha_beta(const ar_plan_t *plan, double alpha_s, double bw_intra_Bps,
+                               double bw_cross_Bps);
+
+/* Releases the plan and its device memory (synchronises the device first). */
+void ar_plan_destroy(ar_plan_t *plan);
+
+/* Thread-local message and status of the last failing call. */
+const char *ar_last_error(void);
+ar_status_t ar_last_status(void);
+
+/* ---- Plan inspection (host only; used to check the planner on a CPU) ---- */
+
+/* Logical transfers of the schedule: per transfer its round, sender,
+ * receiver, element range and kind (0 = reduce, 1 = copy).  Returns the total
+ * number of transfers (writes at most cap), or -1 on error. */
+int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, int32_t *dst,
+                          int64_t *lo, int64_t *hi, int32_t *kind, int64_t cap);
+
+/*
+ * Kernel launches of the exec mode.  ar_plan_launch_info gives launch i's
+ * kernel kind code and op count.  ar_plan_launch_ops writes its ops: element
+ * range [lo, hi), and operand locations a, b (inputs), o, o2 (outputs):
+ * a location 0..nranks-1 is that rank's buffer, 1000+s is fp32 scratch slot s,
+ * -1 is unused.  aux is the fold start (one-pass kernels).  Host only.
+ */
+int32_t ar_plan_num_launches(const ar_plan_t *plan);
+ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);
+ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, int64_t *hi,
+                               int32_t *a, int32_t *b, int32_t *o, int32_t *o2, int32_t *aux);
+
+/* ---- Timing ---- */
+
+/* Per-launch timing.  With max_calls > 0, each ar_allreduce records a HIP
+ * event on its stream before its first launch and after every launch, into a
+ * log holding the events of the last max_calls calls (older calls are
+ * overwritten); max_calls = 0 turns it off.  Events are allocated here, not
+ * on the hot path. */
+ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls);
+
+/* Durations in ms of every launch of the logged calls, oldest call first:
+ * ms[c * launches + i] is launch i of logged call c.  The caller must have
+ * synchronised the stream.  *n receives calls * launches; the log is then
+ * cleared. */
+ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n);
+
+/* ---- Bucket fuser (Scaling ML systems ch. 06, "Bucket fusion") ----
+ *
+ * Gradient tensors are assigned to buckets in reverse tensor order (the
+ * order backward produces them).  A bucket is closed before a tensor that
+ * would take it past bucket_cap_bytes; a tensor larger than the cap gets a
+ * bucket of its own.  Within a bucket tensors are packed back to back in
+ * assignment order; every bucket starts 256-byte aligned in a per-rank
+ * arena.  One all-reduce plan runs per bucket, in bucket order, on one
+ * stream; the gaps between buckets are never touched.
+ */
+typedef struct ar_bucket_plan ar_bucket_plan_t;
+
+ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t *tensor_counts,
+                                        int ntensors, ar_dtype_t dtype, ar_schedule_t schedule,
+                                        size_t bucket_cap_bytes);
+/* tensor_offsets[t]: element offset of tensor t in each rank's arena;
+ * *arena_count: arena length in elements. */
+ar_status_t ar_bucket_layout(const ar_bucket_plan_t *bp, size_t *tensor_offsets,
+                             size_t *arena_count);
+int32_t ar_bucket_count(const ar_bucket_plan_t *bp);
+/* Element offset and length of bucket b in the arena. */
+ar_status_t ar_bucket_range(const ar_bucket_plan_t *bp, int32_t b, size_t *offset, size_t *count);
+ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec);
+/* All-reduces every bucket of the nranks arenas (16-byte aligned device
+ * pointers of arena_count elements), in place, on `stream`. */
+ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream);
+/* Sum of the per-bucket statistics (bytes, steps, launches). */
+ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp);
+void ar_bucket_plan_destroy(ar_bucket_plan_t *bp);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

@@ -1,0 +1,83 @@
+"""Test-side interpreter of the library's launch list (numpy, CPU).
+
+It executes the ops the planner hands to the GPU -- operand locations, fp32
+scratch slots, bf16 flags, fused second outputs, one-pass folds -- with numpy
+float32 arithmetic, so that the planner's lowering can be checked against the
+oracle on a machine without a GPU.  It is neither the oracle nor a fallback:
+nothing in the library calls it.
+"""
+import numpy as np
+
+from gradient_all_reduce_ar_amd import _binding as B
+from tests.folds import to_bf16_bits, widen
+
+
+def _read(loc, lo, hi, bf_flag, bufs, scratch, fp32_mode):
+    if loc >= B.LOC_SCRATCH:
+        return scratch[loc - B.LOC_SCRATCH][lo:hi].copy()
+    if fp32_mode:
+        return bufs[loc][lo:hi].copy()
+    assert bf_flag, "bf16 plan reads a rank buffer as fp32"
+    return widen(bufs[loc][lo:hi])
+
+
+def _write(loc, lo, hi, vals, out_bf, bufs, scratch, fp32_mode):
+    if loc >= B.LOC_SCRATCH:
+        assert not out_bf
+        scratch[loc - B.LOC_SCRATCH][lo:hi] = vals
+    elif fp32_mode:
+        bufs[loc][lo:hi] = vals
+    else:
+        assert out_bf, "bf16 plan writes fp32 into a rank buffer"
+        bufs[loc][lo:hi] = to_bf16_bits(vals)
+
+
+def run(plan, bufs, dtype, group_size):
+    fp32_mode = dtype == "fp32"
+    count = len(bufs[0])
+    n = len(bufs)
+    stats = B.ar_plan_stats(plan)
+    nslots = stats["scratch_bytes"] // (4 * max(1, ((count + 63) // 64) * 64)) if count else 0
+    scratch = [np.full(count, np.nan, np.float32) for _ in range(nslots)]
+    for i in range(B.ar_plan_num_launches(plan)):
+        kind, _ = B.ar_plan_launch_info(plan, i)
+        ops = B.ar_plan_launch_ops(plan, i)
+        fam = kind & 0xF00
+        for k in range(len(ops["lo"])):
+            lo, hi = int(ops["lo"][k]), int(ops["hi"][k])
+            a, b, o, o2, aux = (int(ops[x][k]) for x in ("a", "b", "o", "o2", "aux"))
+            if fam == B.KIND_REDUCE:
+                va = _read(a, lo, hi, kind & 1, bufs, scratch, fp32_mode)
+                vb = _read(b, lo, hi, kind & 2, bufs, scratch, fp32_mode)
+                s = (va + vb).astype(np.float32)
+                _write(o, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode)
+                if kind & 8:
+                    _write(o2, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode)
+            elif fam == B.KIND_COPY:
+                bufs[o][lo:hi] = bufs[a][lo:hi]
+            else:
+                cols = [bufs[r][lo:hi].copy() if fp32_mode else widen(bufs[r][lo:hi]) for r in range(n)]
+                if fam == B.KIND_RING:
+                    acc = cols[aux % n]
+                    for t in range(1, n):
+                        acc = (acc + cols[(aux + t) % n]).astype(np.float32)
+                elif fam == B.KIND_TREE:
+                    level = cols
+                    while len(level) > 1:
+                        level = [(level[2 * m] + level[2 * m + 1]).astype(np.float32) for m in range(len(level) // 2)]
+                    acc = level[0]
+                else:
+                    G = group_size
+                    M = n // G
+                    ls, j = aux & 0xFF, aux >> 8
+                    acc = None
+                    for mi in range(M):
+                        g = (j + mi) % M
+                        part = cols[g * G + ls]
+                        for t in range(1, G):
+                            part = (part + cols[g * G + (ls + t) % G]).astype(np.float32)
+                        acc = part if acc is None else (acc + part).astype(np.float32)
+                res = acc if fp32_mode else to_bf16_bits(acc)
+                for r in range(n):
+                    bufs[r][lo:hi] = res
+    return bufs

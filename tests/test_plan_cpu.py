@@ -1,0 +1,174 @@
+"""The library's host planner, checked on the CPU (no GPU needed).
+
+* Its transfers equal the oracle's messages (same rounds, senders, receivers,
+  ranges, kinds), and its per-rank bytes, cross-group bytes, step counts and
+  alpha-beta times equal the oracle's.
+* Its kernel launch list, executed by a numpy interpreter (tests/plan_interp),
+  gives bit-for-bit the oracle's result in every exec mode -- this checks the
+  lowering (scratch slots, bf16 rounding point, fused forwarding copy,
+  one-pass fold orders) before any kernel runs.
+* Its byte model matches the closed forms of the step-faithful design.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_ar_amd import _binding as B
+from gradient_all_reduce_ar_amd import workloads
+from tests import plan_interp
+
+SCHEDS = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
+         [("ring", 16, 8), ("ring", 64, 8)] + \
+         [("hierarchical", n, g) for n, g in ((2, 1), (4, 2), (4, 4), (6, 3), (6, 2), (8, 4), (16, 8),
+                                              (16, 4), (12, 3), (64, 8), (9, 3))] + \
+         [("rabenseifner", n, 1) for n in (1, 2, 4, 8, 16, 64)]
+
+
+def _plan(n, g, count, dtype, sched):
+    return B.ar_plan_create(n, g, count, dtype, sched)
+
+
+def _sorted(d):
+    order = np.lexsort((d["src"], d["step"]))
+    return {k: v[order] for k, v in d.items()}
+
+
+@pytest.mark.parametrize("sched,n,g", SCHEDS)
+def test_transfers_equal_oracle(sched, n, g):
+    for count in (0, 1, n - 1 if n > 1 else 2, 97, 1000, 4096):
+        p = _plan(n, g, count, "fp32", sched)
+        try:
+            mine = _sorted(B.ar_plan_transfers(p))
+            ref = _sorted(oracle.messages(n, count, sched, group_size=g))
+            assert len(mine["step"]) == len(ref["step"])
+            for k in ("step", "src", "dst", "lo", "hi", "kind"):
+                np.testing.assert_array_equal(mine[k], ref[k], err_msg=f"{sched} n={n} g={g} count={count} {k}")
+            st = B.ar_plan_stats(p)
+            for dt, eb in (("fp32", 4),):
+                sent, cross, steps = oracle.stats(n, count, dt, sched, group_size=g)
+                assert st["steps"] == steps
+                assert st["bytes_sent"] == [int(x) for x in sent]
+                assert st["cross_group_bytes_total"] == cross
+            t = B.ar_plan_cost_alpha_beta(p, 1e-6, 400e9, 50e9)
+            assert t == pytest.approx(oracle.cost(n, count, 4, sched, 1e-6, 400e9, 50e9, group_size=g), rel=1e-12)
+        finally:
+            B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n,g", SCHEDS)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused", "onepass"])
+def test_launch_list_matches_oracle(sched, n, g, dtype, mode):
+    for count in (0, 3, 37, 1031):
+        xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype=dtype)
+        ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+        p = _plan(n, g, count, dtype, sched)
+        try:
+            B.ar_plan_set_exec(p, mode)
+            got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+        finally:
+            B.ar_plan_destroy(p)
+        for r in range(n):
+            np.testing.assert_array_equal(got[r].view(np.uint32 if dtype == "fp32" else np.uint16),
+                                          ref[r].view(np.uint32 if dtype == "fp32" else np.uint16),
+                                          err_msg=f"{sched} n={n} g={g} {dtype} {mode} count={count} rank={r}")
+
+
+def test_byte_model_closed_forms():
+    """Device bytes per call: step-faithful fp32 moves 5(N-1)S (reduce steps
+    read 2 and write 1 slice, copy steps read 1 and write 1); fusing the last
+    reduce-scatter step with the first all-gather step saves S; one-pass
+    moves 2NS.  bf16 with fp32 partials: (14N-18)E bytes unfused, 2E less
+    fused."""
+    n, e = 16, 12288 * 4096
+    S = 4 * e
+    for sched, g in (("ring", 8), ("hierarchical", 8), ("rabenseifner", 1)):
+        p = _plan(n, g, e, "fp32", sched)
+        try:
+            assert B.ar_plan_stats(p)["hbm_bytes_model"] == (5 * n - 6) * S
+            B.ar_plan_set_exec(p, "steps_unfused")
+            assert B.ar_plan_stats(p)["hbm_bytes_model"] == 5 * (n - 1) * S
+            B.ar_plan_set_exec(p, "onepass")
+            assert B.ar_plan_stats(p)["hbm_bytes_model"] == 2 * n * S
+            assert B.ar_plan_stats(p)["launches"] == 1
+        finally:
+            B.ar_plan_destroy(p)
+    e16 = 2 * e
+    p = _plan(n, 8, e16, "bf16", "ring")
+    try:
+        assert B.ar_plan_stats(p)["hbm_bytes_model"] == (14 * n - 18 - 2) * e16
+        B.ar_plan_set_exec(p, "steps_unfused")
+        assert B.ar_plan_stats(p)["hbm_bytes_model"] == (14 * n - 18) * e16
+        assert B.ar_plan_stats(p)["scratch_bytes"] == 4 * e16
+    finally:
+        B.ar_plan_destroy(p)
+
+
+def test_launch_counts():
+    for n in (2, 4, 16, 64):
+        p = _plan(n, 1, 4096, "fp32", "ring")
+        assert B.ar_plan_stats(p)["steps"] == 2 * (n - 1)
+        assert B.ar_plan_stats(p)["launches"] == 2 * (n - 1) - 1
+        B.ar_plan_destroy(p)
+    p = _plan(16, 8, 4096, "fp32", "hierarchical")
+    assert B.ar_plan_stats(p)["steps"] == 16 and B.ar_plan_stats(p)["launches"] == 15
+    B.ar_plan_destroy(p)
+    p = _plan(64, 1, 4096, "bf16", "rabenseifner")
+    assert B.ar_plan_stats(p)["steps"] == 12 and B.ar_plan_stats(p)["launches"] == 11
+    B.ar_plan_destroy(p)
+
+
+def test_bf16_scratch_slots():
+    """Ring keeps one live partial per chunk (1 slot), hierarchical one per
+    group (M slots), Rabenseifner one per pair of ranks (N/2 slots)."""
+    e = 1024
+    for sched, n, g, slots in (("ring", 16, 8, 1), ("hierarchical", 16, 8, 2), ("hierarchical", 16, 16, 1),
+                               ("rabenseifner", 16, 1, 8), ("rabenseifner", 2, 1, 0)):
+        p = _plan(n, g, e, "bf16", sched)
+        assert B.ar_plan_stats(p)["scratch_bytes"] == slots * 4 * e, sched
+        B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
+    ((65, 1, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
+    ((4, 3, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
+    ((4, 0, 10, "fp32", "hierarchical"), B.AR_ERR_INVALID_ARG),
+    ((4, 1, 10, 7, "ring"), B.AR_ERR_INVALID_ARG),
+    ((4, 1, 10, "fp32", 9), B.AR_ERR_INVALID_ARG),
+    ((6, 1, 10, "fp32", "rabenseifner"), B.AR_ERR_UNSUPPORTED),
+])
+def test_create_errors(args, status):
+    with pytest.raises(B.ArError) as ei:
+        B.ar_plan_create(*args)
+    assert ei.value.status == status
+    assert B.ar_last_status() == status
+    assert B.ar_last_error()
+
+
+def test_allreduce_rejects_bad_pointers_without_launching():
+    p = B.ar_plan_create(4, 1, 1024, "fp32", "ring")
+    try:
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce(p, [4096, 0, 8192, 12288])
+        assert ei.value.status == B.AR_ERR_INVALID_ARG and "NULL" in str(ei.value)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce(p, [4096, 8200, 1 << 20, 1 << 21])
+        assert "aligned" in str(ei.value)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce(p, [1 << 20, (1 << 20) + 1024, 1 << 24, 1 << 25])
+        assert "overlap" in str(ei.value)
+    finally:
+        B.ar_plan_destroy(p)
+
+
+def test_plan_is_hazard_free_and_each_round_touches_each_chunk_once():
+    """Within a launch no op writes what another op reads or writes (the
+    planner refuses plans that would); creating every schedule here would
+    have raised otherwise."""
+    for sched, n, g in SCHEDS:
+        for dtype in ("fp32", "bf16"):
+            p = _plan(n, g, 4099, dtype, sched)
+            for mode in ("steps", "steps_unfused", "onepass"):
+                B.ar_plan_set_exec(p, mode)
+            B.ar_plan_destroy(p)
