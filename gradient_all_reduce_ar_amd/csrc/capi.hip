@@ -144,20 +144,19 @@ ar_status_t check_rank_pointers(const ar_plan_t *pl, void *const *rank_bufs) {
   if (!rank_bufs) return fail(AR_ERR_INVALID_ARG, "rank_bufs is NULL");
   const int n = pl->p.nranks;
   const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::elem_bytes(pl->p.dtype));
+  if (bytes == 0) return AR_OK;  // nothing is read or written
   for (int r = 0; r < n; ++r) {
     const uintptr_t v = reinterpret_cast<uintptr_t>(rank_bufs[r]);
     if (!v) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is NULL");
     if (v % 16) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is not 16-byte aligned");
   }
-  if (bytes > 0)
-    for (int r = 0; r < n; ++r)
-      for (int q = r + 1; q < n; ++q) {
-        const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
-        const uintptr_t b = reinterpret_cast<uintptr_t>(rank_bufs[q]);
-        if (a < b + bytes && b < a + bytes)
-          return fail(AR_ERR_INVALID_ARG,
-                      "rank buffers " + std::to_string(r) + " and " + std::to_string(q) + " overlap");
-      }
+  for (int r = 0; r < n; ++r)
+    for (int q = r + 1; q < n; ++q) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
+      const uintptr_t b = reinterpret_cast<uintptr_t>(rank_bufs[q]);
+      if (a < b + bytes && b < a + bytes)
+        return fail(AR_ERR_INVALID_ARG, "rank buffers " + std::to_string(r) + " and " + std::to_string(q) + " overlap");
+    }
   return AR_OK;
 }
 

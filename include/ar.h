@@ -126,7 +126,8 @@ ar_status_t ar_plan_prepare(ar_plan_t *plan);
 /*
  * All-reduce, in place.  rank_bufs: host array of nranks device pointers,
  * read during the call only; buffer r holds >= count elements of the plan's
- * dtype, is 16-byte aligned and overlaps no other rank's buffer.  stream: a
+ * dtype, is 16-byte aligned and overlaps no other rank's buffer (with
+ * count == 0 nothing is touched and the pointers may be NULL).  stream: a
  * hipStream_t (NULL = default stream).  Enqueues the kernels and returns;
  * the result is visible after stream synchronisation (the initiating call of
  * a collective returns before completion -- Scaling ML systems ch. 06).
