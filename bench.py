@@ -90,7 +90,8 @@ def traffic_record(kernel_name, workload, exec_mode):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc", "kernels.hip"), "rb").read()
+    csrc = os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc")
+    src = open(os.path.join(csrc, "kernels.hip"), "rb").read() + open(os.path.join(csrc, "kernels.hpp"), "rb").read()
     digest = hashlib.sha256(src).hexdigest()
     try:
         recs = json.load(open(path))
@@ -112,6 +113,9 @@ def main():
     ap.add_argument("--exec", default="steps", choices=["steps", "steps_unfused", "onepass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the one-pass comparison run")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a plain 1 GiB device-to-device torch copy three times, so that "
+                         "hardware counters of the same run can be scaled by a copy of known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -130,6 +134,15 @@ def main():
     torch.cuda.set_device(dev)
     elem = 4 if dtype == "fp32" else 2
     view = np.float32 if dtype == "fp32" else np.int16
+
+    if args.calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
 
     # ---- inputs, resident in HBM before timing
     t0 = time.time()

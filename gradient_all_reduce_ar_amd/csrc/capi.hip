@@ -251,7 +251,8 @@ ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) 
     const ar::Launch &L = plan->p.launches[i];
     args.ops = plan->d_ops + plan->op_offset[i];
     const dim3 grid(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
-    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s);
+    const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
+    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s, out_scratch);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     if (prof) {
       e = hipEventRecord(ev[i + 1], s);

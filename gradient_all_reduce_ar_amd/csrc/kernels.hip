@@ -28,7 +28,32 @@ namespace ar_dev {
 
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = AR_BLOCK;
+constexpr bool kOnePassNTS = AR_NTS_ONEPASS;
+
+// Native vector types: 16-byte and 8-byte accesses compile to single
+// global_load/store_dwordx4 / dwordx2 instructions.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming accesses.  Every input byte is read once per kernel, so loads
+// carry the non-temporal hint (AR_NTL).  Stores carry it where measurement
+// says it pays: into fp32 scratch and in the one-pass kernels, not into rank
+// buffers written by a step (AR_NTS_*).  The hints never change results.
+template <typename T>
+__device__ __forceinline__ T ld(const char *p) {
+#if AR_NTL
+  return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+#else
+  return *reinterpret_cast<const T *>(p);
+#endif
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st(char *p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<T *>(p));
+  else *reinterpret_cast<T *>(p) = v;
+}
 
 __device__ __forceinline__ const char *src_ptr(const KArgs &a, int32_t loc) {
   return loc >= kLocScratchDev
@@ -57,10 +82,11 @@ __device__ __forceinline__ uint32_t narrow(float f) {
 template <bool BF>
 __device__ __forceinline__ float4 load4(const char *base, int64_t e) {
   if constexpr (BF) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(base + e * 2);
+    const u32x2 v = ld<u32x2>(base + e * 2);
     return make_float4(widen(v.x & 0xffffu), widen(v.x >> 16), widen(v.y & 0xffffu), widen(v.y >> 16));
   } else {
-    return *reinterpret_cast<const float4 *>(base + e * 4);
+    const f32x4 v = ld<f32x4>(base + e * 4);
+    return make_float4(v.x, v.y, v.z, v.w);
   }
 }
 
@@ -70,14 +96,28 @@ __device__ __forceinline__ float load1(const char *base, int64_t e) {
   else return *reinterpret_cast<const float *>(base + e * 4);
 }
 
-__device__ __forceinline__ uint2 pack4(float4 v) {
-  return make_uint2(narrow(v.x) | (narrow(v.y) << 16), narrow(v.z) | (narrow(v.w) << 16));
+__device__ __forceinline__ u32x2 pack4(float4 v) {
+  u32x2 r;
+  r.x = narrow(v.x) | (narrow(v.y) << 16);
+  r.y = narrow(v.z) | (narrow(v.w) << 16);
+  return r;
 }
 
-template <bool BF>
+template <bool NT>
+__device__ __forceinline__ void store_bits4(char *base, int64_t e, u32x2 bits) { st<NT, u32x2>(base + e * 2, bits); }
+
+template <bool BF, bool NT>
 __device__ __forceinline__ void store4(char *base, int64_t e, float4 v) {
-  if constexpr (BF) *reinterpret_cast<uint2 *>(base + e * 2) = pack4(v);
-  else *reinterpret_cast<float4 *>(base + e * 4) = v;
+  if constexpr (BF) {
+    store_bits4<NT>(base, e, pack4(v));
+  } else {
+    f32x4 w;
+    w.x = v.x;
+    w.y = v.y;
+    w.z = v.z;
+    w.w = v.w;
+    st<NT, f32x4>(base + e * 4, w);
+  }
 }
 
 template <bool BF>
@@ -94,8 +134,9 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 // Chunk reduce: o[e] = a[e] + b[e] over the op's range, optionally also
 // written to o2 (the fused forwarding copy of the chunk just completed).
 // FLAGS: 1 a is bf16, 2 b is bf16, 4 outputs are bf16 (rounded once), 8 o2.
+// NTS: non-temporal stores (the host sets it when the outputs are scratch).
 // ---------------------------------------------------------------------------
-template <int FLAGS, int UNROLL>
+template <int FLAGS, int UNROLL, bool NTS>
 __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
@@ -119,12 +160,12 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
       const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
       const float4 s = add4(a[u], b[u]);
       if constexpr (kOBf) {
-        const uint2 bits = pack4(s);
-        *reinterpret_cast<uint2 *>(O + e * 2) = bits;
-        if constexpr (kO2) *reinterpret_cast<uint2 *>(O2 + e * 2) = bits;
+        const u32x2 bits = pack4(s);
+        store_bits4<NTS>(O, e, bits);
+        if constexpr (kO2) store_bits4<NTS>(O2, e, bits);
       } else {
-        store4<false>(O, e, s);
-        if constexpr (kO2) store4<false>(O2, e, s);
+        store4<false, NTS>(O, e, s);
+        if constexpr (kO2) store4<false, NTS>(O2, e, s);
       }
     }
   } else {
@@ -142,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
 // ---------------------------------------------------------------------------
 // Chunk copy: o[e] = a[e], bit copy of ES-byte elements in 16-byte units.
 // ---------------------------------------------------------------------------
-template <int ES, int UNROLL>
+template <int ES, int UNROLL, bool NTS>
 __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
   constexpr int64_t kPerUnit = 16 / ES;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPerUnit * UNROLL;
@@ -153,16 +194,16 @@ __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
   const char *A = src_ptr(args, op.a);
   char *O = dst_ptr(args, op.o);
   if (base >= op.lo && base + kTile <= op.hi) {
-    uint4 v[UNROLL];
+    u32x4 v[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
-      v[u] = *reinterpret_cast<const uint4 *>(A + e * ES);
+      v[u] = ld<u32x4>(A + e * ES);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
-      *reinterpret_cast<uint4 *>(O + e * ES) = v[u];
+      st<NTS, u32x4>(O + e * ES, v[u]);
     }
   } else {
     for (int u = 0; u < UNROLL; ++u)
@@ -191,29 +232,29 @@ __device__ __forceinline__ void load_units(const KArgs &args, int r, int64_t bas
 template <bool BF, int UNROLL>
 __device__ __forceinline__ void store_all(const KArgs &args, int64_t base, const float4 (&acc)[UNROLL]) {
   if constexpr (BF) {
-    uint2 bits[UNROLL];
+    u32x2 bits[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) bits[u] = pack4(acc[u]);
     for (int r = 0; r < args.nranks; ++r) {
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        *reinterpret_cast<uint2 *>(p + (base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4) * 2) = bits[u];
+        store_bits4<kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4, bits[u]);
     }
   } else {
     for (int r = 0; r < args.nranks; ++r) {
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        *reinterpret_cast<float4 *>(p + (base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4) * 4) = acc[u];
+        store4<false, kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4, acc[u]);
     }
   }
 }
 
 // acc (+)= x_r for r = first, first+1, ... (count ranks, wrapping at `wrap_n`
-// inside the block of ranks starting at `rank0`), four ranks' loads in flight
+// inside the block of ranks starting at `rank0`), kFB ranks' loads in flight
 // at a time; the adds stay in order.
-template <bool BF, int UNROLL>
+template <bool BF, int UNROLL, int kFB>
 __device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, int wrap_n, int first, int count,
                                                 int64_t base, float4 (&acc)[UNROLL], bool init) {
   int r = first;
@@ -223,25 +264,36 @@ __device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, in
     r = (r + 1 == wrap_n) ? 0 : r + 1;
     t = 1;
   }
-  for (; t + 4 <= count; t += 4) {
-    float4 x0[UNROLL], x1[UNROLL], x2[UNROLL], x3[UNROLL];
-    const int r1 = (r + 1 == wrap_n) ? 0 : r + 1;
-    const int r2 = (r1 + 1 == wrap_n) ? 0 : r1 + 1;
-    const int r3 = (r2 + 1 == wrap_n) ? 0 : r2 + 1;
-    load_units<BF, UNROLL>(args, rank0 + r, base, x0);
-    load_units<BF, UNROLL>(args, rank0 + r1, base, x1);
-    load_units<BF, UNROLL>(args, rank0 + r2, base, x2);
-    load_units<BF, UNROLL>(args, rank0 + r3, base, x3);
+  // kFB: ranks whose loads are in flight together
+  for (; t + kFB <= count; t += kFB) {
+    float4 x[kFB][UNROLL];
+    int rr[kFB];
+    rr[0] = r;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) acc[u] = add4(add4(add4(add4(acc[u], x0[u]), x1[u]), x2[u]), x3[u]);
-    r = (r3 + 1 == wrap_n) ? 0 : r3 + 1;
+    for (int q = 1; q < kFB; ++q) rr[q] = (rr[q - 1] + 1 == wrap_n) ? 0 : rr[q - 1] + 1;
+#pragma unroll
+    for (int q = 0; q < kFB; ++q) load_units<BF, UNROLL>(args, rank0 + rr[q], base, x[q]);
+#pragma unroll
+    for (int q = 0; q < kFB; ++q)
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[q][u]);
+    r = (rr[kFB - 1] + 1 == wrap_n) ? 0 : rr[kFB - 1] + 1;
   }
-  for (; t < count; ++t) {
-    float4 x[UNROLL];
-    load_units<BF, UNROLL>(args, rank0 + r, base, x);
+  const int rem = count - t;  // fewer than kFB ranks left: one predicated batch
+  if (rem > 0) {
+    float4 x[kFB][UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[u]);
-    r = (r + 1 == wrap_n) ? 0 : r + 1;
+    for (int q = 0; q + 1 < kFB; ++q)
+      if (q < rem) {
+        load_units<BF, UNROLL>(args, rank0 + r, base, x[q]);
+        r = (r + 1 == wrap_n) ? 0 : r + 1;
+      }
+#pragma unroll
+    for (int q = 0; q + 1 < kFB; ++q)
+      if (q < rem) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[q][u]);
+      }
   }
 }
 
@@ -269,7 +321,7 @@ __device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e
 }
 
 // Ring: element in chunk c is ((x_c + x_{c+1}) + ...) + x_{c+N-1}; aux = c.
-template <bool BF, int UNROLL>
+template <bool BF, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
   const DevOp op = args.ops[blockIdx.y];
@@ -278,7 +330,7 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
   const int n = args.nranks;
   if (base >= op.lo && base + kTile <= op.hi) {
     float4 acc[UNROLL];
-    ring_fold_units<BF, UNROLL>(args, 0, n, op.aux, n, base, acc, true);
+    ring_fold_units<BF, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
     store_all<BF, UNROLL>(args, base, acc);
   } else {
     for (int u = 0; u < UNROLL; ++u)
@@ -293,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
 // Hierarchical: group partial of slice k, ((x_{g,k+1} + x_{g,k+2}) + ...) +
 // x_{g,k}; sub-chunk j folds the group partials P_j + P_{j+1} + ... in ring
 // order.  aux = ((k + 1) mod G) | (j << 8).
-template <bool BF, int UNROLL>
+template <bool BF, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
   const DevOp op = args.ops[blockIdx.y];
@@ -306,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
     int g = j;
     for (int m = 0; m < M; ++m) {
       float4 part[UNROLL];
-      ring_fold_units<BF, UNROLL>(args, g * G, G, lstart, G, base, part, true);
+      ring_fold_units<BF, UNROLL, FB>(args, g * G, G, lstart, G, base, part, true);
       if (m == 0) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) acc[u] = part[u];
@@ -385,23 +437,34 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
 
 constexpr int kReduceUnroll = AR_REDUCE_UNROLL;
 constexpr int kCopyUnroll = AR_COPY_UNROLL;
-constexpr int kOnePassUnroll = AR_ONEPASS_UNROLL;
+// one-pass shapes per dtype (measured): fp32 2 units x 8 ranks in flight,
+// bf16 1 unit x 16 ranks
+constexpr int kOnePassUnrollF32 = AR_ONEPASS_UNROLL_F32, kFoldBatchF32 = AR_FOLD_BATCH_F32;
+constexpr int kOnePassUnrollBF16 = AR_ONEPASS_UNROLL_BF16, kFoldBatchBF16 = AR_FOLD_BATCH_BF16;
+constexpr bool kNtsRank = AR_NTS_RANK;
+constexpr bool kNtsScratch = AR_NTS_SCRATCH;
 
 template <int FLAGS>
-hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll>), grid, dim3(kBlock), 0, s, a);
+hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
+  if (out_scratch && kNtsScratch)
+    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, true>), grid, dim3(kBlock), 0, s, a);
+  else if (!out_scratch && kNtsRank)
+    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, true>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, false>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template <bool BF>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
+  constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
   switch (n) {
-    case 2: hipLaunchKernelGGL((onepass_tree<BF, 2, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((onepass_tree<BF, 4, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((onepass_tree<BF, 8, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((onepass_tree<BF, 16, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((onepass_tree<BF, 32, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((onepass_tree<BF, 64, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((onepass_tree<BF, 2, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((onepass_tree<BF, 4, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((onepass_tree<BF, 8, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((onepass_tree<BF, 16, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((onepass_tree<BF, 32, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((onepass_tree<BF, 64, U>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -413,44 +476,48 @@ int64_t tile_elems(int32_t kind) {
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * kReduceUnroll;
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * kCopyUnroll;
-    default: return static_cast<int64_t>(kBlock) * 4 * kOnePassUnroll;
+    default: return static_cast<int64_t>(kBlock) * 4 * ((kind & 1) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }
 }
 
-hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
   switch (kind & 0xF00) {
     case kKindReduce:
       switch (kind & 0xF) {
-        case 0: return launch_reduce<0>(grid, a, s);
-        case 1: return launch_reduce<1>(grid, a, s);
-        case 2: return launch_reduce<2>(grid, a, s);
-        case 3: return launch_reduce<3>(grid, a, s);
-        case 4: return launch_reduce<4>(grid, a, s);
-        case 5: return launch_reduce<5>(grid, a, s);
-        case 6: return launch_reduce<6>(grid, a, s);
-        case 7: return launch_reduce<7>(grid, a, s);
-        case 8: return launch_reduce<8>(grid, a, s);
-        case 9: return launch_reduce<9>(grid, a, s);
-        case 10: return launch_reduce<10>(grid, a, s);
-        case 11: return launch_reduce<11>(grid, a, s);
-        case 12: return launch_reduce<12>(grid, a, s);
-        case 13: return launch_reduce<13>(grid, a, s);
-        case 14: return launch_reduce<14>(grid, a, s);
-        case 15: return launch_reduce<15>(grid, a, s);
+        case 0: return launch_reduce<0>(grid, a, s, out_scratch);
+        case 1: return launch_reduce<1>(grid, a, s, out_scratch);
+        case 2: return launch_reduce<2>(grid, a, s, out_scratch);
+        case 3: return launch_reduce<3>(grid, a, s, out_scratch);
+        case 4: return launch_reduce<4>(grid, a, s, out_scratch);
+        case 5: return launch_reduce<5>(grid, a, s, out_scratch);
+        case 6: return launch_reduce<6>(grid, a, s, out_scratch);
+        case 7: return launch_reduce<7>(grid, a, s, out_scratch);
+        case 8: return launch_reduce<8>(grid, a, s, out_scratch);
+        case 9: return launch_reduce<9>(grid, a, s, out_scratch);
+        case 10: return launch_reduce<10>(grid, a, s, out_scratch);
+        case 11: return launch_reduce<11>(grid, a, s, out_scratch);
+        case 12: return launch_reduce<12>(grid, a, s, out_scratch);
+        case 13: return launch_reduce<13>(grid, a, s, out_scratch);
+        case 14: return launch_reduce<14>(grid, a, s, out_scratch);
+        case 15: return launch_reduce<15>(grid, a, s, out_scratch);
       }
       break;
     case kKindCopy:
-      if ((kind & 0xFF) == 2) hipLaunchKernelGGL((chunk_copy<2, kCopyUnroll>), grid, dim3(kBlock), 0, s, a);
-      else if ((kind & 0xFF) == 4) hipLaunchKernelGGL((chunk_copy<4, kCopyUnroll>), grid, dim3(kBlock), 0, s, a);
+      if ((kind & 0xFF) == 2) hipLaunchKernelGGL((chunk_copy<2, kCopyUnroll, kNtsRank>), grid, dim3(kBlock), 0, s, a);
+      else if ((kind & 0xFF) == 4) hipLaunchKernelGGL((chunk_copy<4, kCopyUnroll, kNtsRank>), grid, dim3(kBlock), 0, s, a);
       else return hipErrorInvalidValue;
       return hipGetLastError();
     case kKindRing:
-      if (kind & 1) hipLaunchKernelGGL((onepass_ring<true, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
-      else hipLaunchKernelGGL((onepass_ring<false, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      if (kind & 1)
+        hipLaunchKernelGGL((onepass_ring<true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      else
+        hipLaunchKernelGGL((onepass_ring<false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
       return hipGetLastError();
     case kKindHier:
-      if (kind & 1) hipLaunchKernelGGL((onepass_hier<true, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
-      else hipLaunchKernelGGL((onepass_hier<false, kOnePassUnroll>), grid, dim3(kBlock), 0, s, a);
+      if (kind & 1)
+        hipLaunchKernelGGL((onepass_hier<true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      else
+        hipLaunchKernelGGL((onepass_hier<false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
       return hipGetLastError();
     case kKindTree:
       return (kind & 1) ? launch_tree<true>(a.nranks, grid, a, s) : launch_tree<false>(a.nranks, grid, a, s);

@@ -7,14 +7,38 @@
 
 #include "plan.hpp"
 
+#ifndef AR_BLOCK
+#define AR_BLOCK 256
+#endif
+#ifndef AR_NTL
+#define AR_NTL 1
+#endif
+#ifndef AR_NTS_RANK
+#define AR_NTS_RANK 0
+#endif
+#ifndef AR_NTS_SCRATCH
+#define AR_NTS_SCRATCH 1
+#endif
+#ifndef AR_NTS_ONEPASS
+#define AR_NTS_ONEPASS 1
+#endif
+#ifndef AR_FOLD_BATCH_F32
+#define AR_FOLD_BATCH_F32 8
+#endif
+#ifndef AR_FOLD_BATCH_BF16
+#define AR_FOLD_BATCH_BF16 16
+#endif
 #ifndef AR_REDUCE_UNROLL
-#define AR_REDUCE_UNROLL 4
+#define AR_REDUCE_UNROLL 2
 #endif
 #ifndef AR_COPY_UNROLL
-#define AR_COPY_UNROLL 4
+#define AR_COPY_UNROLL 2
 #endif
-#ifndef AR_ONEPASS_UNROLL
-#define AR_ONEPASS_UNROLL 2
+#ifndef AR_ONEPASS_UNROLL_F32
+#define AR_ONEPASS_UNROLL_F32 2
+#endif
+#ifndef AR_ONEPASS_UNROLL_BF16
+#define AR_ONEPASS_UNROLL_BF16 1
 #endif
 
 namespace ar_dev {
@@ -46,7 +70,8 @@ struct KArgs {
 // (max over ops of tiles spanned, number of ops).
 int64_t tile_elems(int32_t kind);
 
-// Launches the kernel of `kind` on stream s.
-hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s);
+// Launches the kernel of `kind` on stream s.  out_scratch: the launch's
+// outputs are fp32 scratch slots (selects the store cache policy).
+hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch);
 
 }  // namespace ar_dev
