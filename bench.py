@@ -152,12 +152,7 @@ def main():
         plan = B.ar_bucket_plan_create(n, group, sizes, dtype, sched, 25 << 20)
         B.ar_bucket_set_exec(plan, args.exec)
         offsets, arena = B.ar_bucket_layout(plan, len(sizes))
-        host = []
-        for r in range(n):
-            a = np.zeros(arena, np.uint16 if dtype == "bf16" else np.float32)
-            for t, c in enumerate(sizes):
-                a[offsets[t]:offsets[t] + c] = workloads.bucketed_tensor_values(r, t, c, dtype=dtype)
-            host.append(a)
+        host = workloads.bucketed_arenas(n, sizes, offsets, arena, dtype=dtype)
         count_logical = int(sum(int(c) for c in sizes))
     else:
         plan = B.ar_plan_create(n, group, count, dtype, sched)

@@ -85,3 +85,13 @@ def bucketed_tensor_values(r, t, count, seed=0, sigma=1e-3, dtype="bf16"):
     rng = np.random.default_rng([seed, r, t])
     x = rng.standard_normal(int(count), dtype=np.float32) * np.float32(sigma)
     return x if dtype == "fp32" else _to_bf16_bits(x)
+
+
+def bucketed_arenas(nranks, sizes, offsets, arena_count, seed=0, sigma=1e-3, dtype="bf16"):
+    """Per-rank arenas with tensor t of rank r at offsets[t]; gaps are zero."""
+    def fill(r):
+        a = np.zeros(arena_count, np.float32 if dtype == "fp32" else np.uint16)
+        for t, c in enumerate(sizes):
+            a[offsets[t]:offsets[t] + int(c)] = bucketed_tensor_values(r, t, c, seed, sigma, dtype)
+        return a
+    return _per_rank(fill, nranks)

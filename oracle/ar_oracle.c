@@ -402,18 +402,23 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
     }
   }
 
-  /* Message payload store, sized for the largest step. */
-  int64_t j0 = 0;
+  /* Message payload store, sized once for the largest step. */
+  int64_t biggest = 1;
+  for (int64_t j = 0, step_total = 0; j < L.n; ++j) {
+    step_total = (j > 0 && L.m[j].step == L.m[j - 1].step ? step_total : 0) + (L.m[j].hi - L.m[j].lo);
+    if (step_total > biggest) biggest = step_total;
+  }
   float *pay = NULL;
   uint16_t *pay16 = NULL;
+  if (!err) {
+    pay = (float *)malloc(sizeof(float) * (size_t)biggest);
+    pay16 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)biggest);
+    if (!pay || !pay16) err = 1;
+  }
+  int64_t j0 = 0;
   while (!err && j0 < L.n && L.m[j0].step < nsteps) {
     int64_t j1 = j0;
-    int64_t total = 0;
-    while (j1 < L.n && L.m[j1].step == L.m[j0].step) { total += L.m[j1].hi - L.m[j1].lo; ++j1; }
-    free(pay); free(pay16);
-    pay = (float *)malloc(sizeof(float) * (size_t)(total > 0 ? total : 1));
-    pay16 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(total > 0 ? total : 1));
-    if (!pay || !pay16) { err = 1; break; }
+    while (j1 < L.n && L.m[j1].step == L.m[j0].step) ++j1;
     /* 1) every sender copies its payload out of the pre-step state */
     int64_t off = 0;
     for (int64_t j = j0; j < j1; ++j) {

@@ -1,0 +1,105 @@
+"""Bucket fuser ("Collective communication", Scaling ML systems ch. 06,
+"Bucket fusion"): tensors go into buckets in reverse order, each bucket gets
+one all-reduce.  The layout rules beyond "reverse order, about 25 MB" are a
+reading (parity unpinned by the pages): close a bucket before a tensor that
+would exceed the cap, a tensor larger than the cap gets its own bucket,
+tensors are packed back to back, buckets start 256-byte aligned."""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_ar_amd import _binding as B
+from gradient_all_reduce_ar_amd import workloads
+
+CAP = 25 << 20
+
+
+def _brute_layout(sizes, cap_elems, align):
+    """Independent restatement of the rules, for comparison."""
+    buckets, cur = [], []
+    for t in reversed(range(len(sizes))):
+        if cur and sum(sizes[i] for i in cur) + sizes[t] > cap_elems:
+            buckets.append(cur)
+            cur = []
+        cur.append(t)
+    if cur:
+        buckets.append(cur)
+    offsets, ranges, pos = {}, [], 0
+    for b in buckets:
+        pos = (pos + align - 1) // align * align
+        start = pos
+        for t in b:
+            offsets[t] = pos
+            pos += sizes[t]
+        ranges.append((start, pos - start))
+    return [offsets[t] for t in range(len(sizes))], ranges, pos
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_layout_matches_rules(dtype):
+    eb = 2 if dtype == "bf16" else 4
+    for sizes in (workloads.bucketed_tensor_sizes(elem_bytes=eb), [5, 7, 3], [CAP // eb + 1, 3, CAP // eb, 1],
+                  [1] * 50, []):
+        sizes = [int(s) for s in sizes]
+        bp = B.ar_bucket_plan_create(4, 1, sizes, dtype, "ring", CAP)
+        try:
+            offs, arena = B.ar_bucket_layout(bp, len(sizes))
+            ranges = [B.ar_bucket_range(bp, b) for b in range(B.ar_bucket_count(bp))]
+            want_offs, want_ranges, want_arena = _brute_layout(sizes, CAP // eb, 256 // eb)
+            assert offs == want_offs and ranges == want_ranges and arena == want_arena
+            for off, cnt in ranges:
+                assert (off * eb) % 256 == 0
+                assert cnt * eb <= CAP or cnt == max(sizes)
+        finally:
+            B.ar_bucket_plan_destroy(bp)
+
+
+def test_reverse_order_and_c5_shape():
+    sizes = [int(s) for s in workloads.bucketed_tensor_sizes()]
+    assert len(sizes) == 300 and max(sizes) * 2 == 64 << 20
+    bp = B.ar_bucket_plan_create(16, 1, sizes, "bf16", "rabenseifner", CAP)
+    try:
+        offs, _ = B.ar_bucket_layout(bp, len(sizes))
+        # the last tensor (first ready in backward) sits at the arena start
+        assert offs[-1] == 0
+        assert all(offs[t] > offs[t + 1] for t in range(len(sizes) - 1))
+        st = B.ar_bucket_stats(bp)
+        nb = B.ar_bucket_count(bp)
+        assert st["steps"] == nb * 8 and st["launches"] == nb * 7
+        assert st["count"] == sum(B.ar_bucket_range(bp, b)[1] for b in range(nb)) == sum(sizes)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n,sched", [(16, "rabenseifner"), (16, "ring"), (64, "rabenseifner"), (64, "ring")])
+def test_bucketed_bf16_parity(n, sched):
+    """C5: 300 lognormal bf16 tensors per rank, 25 MiB buckets, one
+    all-reduce per bucket; bit-exact per bucket against the oracle, all ranks
+    identical, gaps between buckets untouched."""
+    import torch
+
+    print(f"case bucketed n={n} {sched}", flush=True)
+    sizes = [int(s) for s in workloads.bucketed_tensor_sizes()]
+    bp = B.ar_bucket_plan_create(n, 1, sizes, "bf16", sched, CAP)
+    try:
+        offs, arena = B.ar_bucket_layout(bp, len(sizes))
+        host = workloads.bucketed_arenas(n, sizes, offs, arena)
+        bufs = [torch.from_numpy(h.view(np.int16)).to("cuda:0") for h in host]
+        B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for r in range(1, n):
+            assert torch.equal(bufs[r], bufs[0]), f"rank {r} differs from rank 0"
+        got = bufs[0].cpu().numpy().view(np.uint16)
+        del bufs
+        covered = np.zeros(arena, bool)
+        for b in range(B.ar_bucket_count(bp)):
+            off, cnt = B.ar_bucket_range(bp, b)
+            covered[off:off + cnt] = True
+            ref = oracle.run([h[off:off + cnt].copy() for h in host], "bf16", sched)
+            assert np.array_equal(got[off:off + cnt], ref[0]), f"bucket {b}"
+            print(f"  bucket {b}: {cnt} elements bit-exact", flush=True)
+        assert np.all(got[~covered] == 0)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
