@@ -42,6 +42,7 @@ struct ar_plan {
   ar_dev::DevOp *d_ops = nullptr;
   std::vector<int64_t> op_offset;  // per launch: index of its first op in d_ops
   std::vector<uint32_t> grid_x;    // per launch
+  std::vector<uint8_t> cold;       // per launch: streaming kernel shape
   float *scratch = nullptr;        // owned unless external_scratch
   size_t scratch_bytes = 0;
   float *external_scratch = nullptr;
@@ -79,6 +80,17 @@ struct ar_bucket_plan {
 
 namespace {
 
+// Bytes a launch writes (both outputs of fused ops).
+int64_t launch_written_bytes(const ar::Plan &p, const ar::Launch &L) {
+  const int32_t fam = L.kind & 0xF00;
+  int64_t elems = 0;
+  for (const ar::Op &o : L.ops) elems += (o.hi - o.lo) * ((o.o2 != ar::kLocNone) ? 2 : 1);
+  int64_t eb = ar::elem_bytes(p.dtype);
+  if (fam == ar::kKReduce && p.dtype == ar::kBF16 && !(L.kind & ar::kFlagOBf)) eb = 4;  // fp32 partials
+  if (fam != ar::kKReduce && fam != ar::kKCopy) elems *= p.nranks;
+  return elems * eb;
+}
+
 ar_status_t prepare(ar_plan_t *pl) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -92,15 +104,19 @@ ar_status_t prepare(ar_plan_t *pl) {
   std::vector<ar_dev::DevOp> host_ops;
   pl->op_offset.clear();
   pl->grid_x.clear();
+  pl->cold.clear();
   for (const ar::Launch &L : pl->p.launches) {
     pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
-    const int64_t tile = ar_dev::tile_elems(L.kind);
+    const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
+    const bool cold = ar_dev::is_cold(launch_written_bytes(pl->p, L), out_scratch);
+    pl->cold.push_back(cold);
+    const int64_t tile = ar_dev::tile_elems(L.kind, cold);
     int64_t gx = 0;
     for (const ar::Op &o : L.ops) {
       host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
       gx = std::max(gx, (o.hi + tile - 1) / tile - o.lo / tile);
     }
-    if (gx > 0x7fffffff) return fail(AR_ERR_UNSUPPORTED, "op too large for one grid");
+    if (gx * static_cast<int64_t>(L.ops.size()) > 0x7fffffff) return fail(AR_ERR_UNSUPPORTED, "op too large for one grid");
     pl->grid_x.push_back(static_cast<uint32_t>(gx));
   }
   if (!host_ops.empty()) {
@@ -250,9 +266,10 @@ ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) 
   for (size_t i = 0; i < plan->p.launches.size(); ++i) {
     const ar::Launch &L = plan->p.launches[i];
     args.ops = plan->d_ops + plan->op_offset[i];
-    const dim3 grid(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
+    args.nops = static_cast<int32_t>(L.ops.size());
+    const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
     const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
-    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s, out_scratch);
+    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     if (prof) {
       e = hipEventRecord(ev[i + 1], s);

@@ -7,8 +7,8 @@
 // independent 16-byte loads in flight, and no LDS or MFMA is involved --
 // nothing is reused, so staging through LDS would only add a round trip.
 //
-// Launch geometry: grid = (tiles per op, ops).  blockIdx.y selects the op
-// (one transfer of the step); blockIdx.x walks the op's element range in
+// Launch geometry: every block takes one tile of one op (one transfer of the
+// step; see block_coord for the block -> (op, tile) order); a tile walks the op's element range in
 // tiles that are aligned to the tile size in absolute element coordinates,
 // so every rank buffer, every scratch slot and every vector access of a tile
 // share the same alignment.  Only the first and last tile of an op can be
@@ -53,6 +53,26 @@ template <bool NT, typename T>
 __device__ __forceinline__ void st(char *p, T v) {
   if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<T *>(p));
   else *reinterpret_cast<T *>(p) = v;
+}
+
+// Block -> (op, tile).  With AR_GRID_INTERLEAVE the ops of a launch are
+// interleaved block by block, so the resident blocks stream from every op at
+// once; otherwise blockIdx.y is the op and blockIdx.x the tile.
+// A block handles tiles tile, tile + stride, ... of its op (grid-stride when
+// the grid is capped by AR_PERSIST_X blocks per op).
+struct BlockCoord {
+  int op;
+  int64_t tile, stride;
+};
+__device__ __forceinline__ BlockCoord block_coord(const KArgs &a) {
+#if AR_GRID_INTERLEAVE
+  return {static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.nops)),
+          static_cast<int64_t>(blockIdx.x / static_cast<uint32_t>(a.nops)),
+          static_cast<int64_t>(gridDim.x / static_cast<uint32_t>(a.nops))};
+#else
+  (void)a;
+  return {static_cast<int>(blockIdx.y), static_cast<int64_t>(blockIdx.x), static_cast<int64_t>(gridDim.x)};
+#endif
 }
 
 __device__ __forceinline__ const char *src_ptr(const KArgs &a, int32_t loc) {
@@ -140,43 +160,46 @@ template <int FLAGS, int UNROLL, bool NTS>
 __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
-  const DevOp op = args.ops[blockIdx.y];
-  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
-  if (base >= op.hi) return;
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
   const char *A = src_ptr(args, op.a);
   const char *B = src_ptr(args, op.b);
   char *O = dst_ptr(args, op.o);
   char *O2 = kO2 ? dst_ptr(args, op.o2) : nullptr;
-  if (base >= op.lo && base + kTile <= op.hi) {
-    float4 a[UNROLL], b[UNROLL];
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      float4 a[UNROLL], b[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
-      a[u] = load4<kABf>(A, e);
-      b[u] = load4<kBBf>(B, e);
-    }
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
+        a[u] = load4<kABf>(A, e);
+        b[u] = load4<kBBf>(B, e);
+      }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
-      const float4 s = add4(a[u], b[u]);
-      if constexpr (kOBf) {
-        const u32x2 bits = pack4(s);
-        store_bits4<NTS>(O, e, bits);
-        if constexpr (kO2) store_bits4<NTS>(O2, e, bits);
-      } else {
-        store4<false, NTS>(O, e, s);
-        if constexpr (kO2) store4<false, NTS>(O2, e, s);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
+        const float4 s = add4(a[u], b[u]);
+        if constexpr (kOBf) {
+          const u32x2 bits = pack4(s);
+          store_bits4<NTS>(O, e, bits);
+          if constexpr (kO2) store_bits4<NTS>(O2, e, bits);
+        } else {
+          store4<false, NTS>(O, e, s);
+          if constexpr (kO2) store4<false, NTS>(O2, e, s);
+        }
       }
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
+          store1<kOBf>(O, e, s);
+          if constexpr (kO2) store1<kOBf>(O2, e, s);
+        }
     }
-  } else {
-    for (int u = 0; u < UNROLL; ++u)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
-        if (e < op.lo || e >= op.hi) continue;
-        const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
-        store1<kOBf>(O, e, s);
-        if constexpr (kO2) store1<kOBf>(O2, e, s);
-      }
   }
 }
 
@@ -188,30 +211,33 @@ __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
   constexpr int64_t kPerUnit = 16 / ES;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPerUnit * UNROLL;
   using Elem = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
-  const DevOp op = args.ops[blockIdx.y];
-  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
-  if (base >= op.hi) return;
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
   const char *A = src_ptr(args, op.a);
   char *O = dst_ptr(args, op.o);
-  if (base >= op.lo && base + kTile <= op.hi) {
-    u32x4 v[UNROLL];
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
-      v[u] = ld<u32x4>(A + e * ES);
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
-      st<NTS, u32x4>(O + e * ES, v[u]);
-    }
-  } else {
-    for (int u = 0; u < UNROLL; ++u)
-      for (int k = 0; k < kPerUnit; ++k) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit + k;
-        if (e < op.lo || e >= op.hi) continue;
-        *reinterpret_cast<Elem *>(O + e * ES) = *reinterpret_cast<const Elem *>(A + e * ES);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+        v[u] = ld<u32x4>(A + e * ES);
       }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+        st<NTS, u32x4>(O + e * ES, v[u]);
+      }
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < kPerUnit; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit + k;
+          if (e < op.lo || e >= op.hi) continue;
+          *reinterpret_cast<Elem *>(O + e * ES) = *reinterpret_cast<const Elem *>(A + e * ES);
+        }
+    }
   }
 }
 
@@ -324,21 +350,24 @@ __device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e
 template <bool BF, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
-  const DevOp op = args.ops[blockIdx.y];
-  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
-  if (base >= op.hi) return;
-  const int n = args.nranks;
-  if (base >= op.lo && base + kTile <= op.hi) {
-    float4 acc[UNROLL];
-    ring_fold_units<BF, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
-    store_all<BF, UNROLL>(args, base, acc);
-  } else {
-    for (int u = 0; u < UNROLL; ++u)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
-        if (e < op.lo || e >= op.hi) continue;
-        store_all1(args, BF, e, ring_fold1(args, BF, 0, n, op.aux, n, e));
-      }
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    const int n = args.nranks;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      float4 acc[UNROLL];
+      ring_fold_units<BF, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
+      store_all<BF, UNROLL>(args, base, acc);
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          store_all1(args, BF, e, ring_fold1(args, BF, 0, n, op.aux, n, e));
+        }
+    }
   }
 }
 
@@ -348,41 +377,44 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
 template <bool BF, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
-  const DevOp op = args.ops[blockIdx.y];
-  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
-  if (base >= op.hi) return;
-  const int G = args.group_size, M = args.nranks / G;
-  const int lstart = op.aux & 0xff, j = op.aux >> 8;
-  if (base >= op.lo && base + kTile <= op.hi) {
-    float4 acc[UNROLL];
-    int g = j;
-    for (int m = 0; m < M; ++m) {
-      float4 part[UNROLL];
-      ring_fold_units<BF, UNROLL, FB>(args, g * G, G, lstart, G, base, part, true);
-      if (m == 0) {
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    const int G = args.group_size, M = args.nranks / G;
+    const int lstart = op.aux & 0xff, j = op.aux >> 8;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      float4 acc[UNROLL];
+      int g = j;
+      for (int m = 0; m < M; ++m) {
+        float4 part[UNROLL];
+        ring_fold_units<BF, UNROLL, FB>(args, g * G, G, lstart, G, base, part, true);
+        if (m == 0) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) acc[u] = part[u];
-      } else {
+          for (int u = 0; u < UNROLL; ++u) acc[u] = part[u];
+        } else {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], part[u]);
-      }
-      g = (g + 1 == M) ? 0 : g + 1;
-    }
-    store_all<BF, UNROLL>(args, base, acc);
-  } else {
-    for (int u = 0; u < UNROLL; ++u)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
-        if (e < op.lo || e >= op.hi) continue;
-        float acc = 0.f;
-        int g = j;
-        for (int m = 0; m < M; ++m) {
-          const float part = ring_fold1(args, BF, g * G, G, lstart, G, e);
-          acc = (m == 0) ? part : acc + part;
-          g = (g + 1 == M) ? 0 : g + 1;
+          for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], part[u]);
         }
-        store_all1(args, BF, e, acc);
+        g = (g + 1 == M) ? 0 : g + 1;
       }
+      store_all<BF, UNROLL>(args, base, acc);
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          float acc = 0.f;
+          int g = j;
+          for (int m = 0; m < M; ++m) {
+            const float part = ring_fold1(args, BF, g * G, G, lstart, G, e);
+            acc = (m == 0) ? part : acc + part;
+            g = (g + 1 == M) ? 0 : g + 1;
+          }
+          store_all1(args, BF, e, acc);
+        }
+    }
   }
 }
 
@@ -393,65 +425,86 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
   constexpr int kB = N < 8 ? N : 8;
   constexpr int kBatches = N / kB;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
-  const DevOp op = args.ops[blockIdx.y];
-  const int64_t base = (op.lo / kTile + blockIdx.x) * kTile;
-  if (base >= op.hi) return;
-  if (base >= op.lo && base + kTile <= op.hi) {
-    // each batch is an aligned block of kB ranks, so the tree over batch
-    // results in index order completes the balanced tree over all N ranks
-    float4 res[kBatches][UNROLL];
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      // each batch is an aligned block of kB ranks, so the tree over batch
+      // results in index order completes the balanced tree over all N ranks
+      float4 res[kBatches][UNROLL];
 #pragma unroll
-    for (int bi = 0; bi < kBatches; ++bi) {
-      float4 v[kB][UNROLL];
+      for (int bi = 0; bi < kBatches; ++bi) {
+        float4 v[kB][UNROLL];
 #pragma unroll
-      for (int i = 0; i < kB; ++i) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
+        for (int i = 0; i < kB; ++i) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
 #pragma unroll
-      for (int w = kB; w > 1; w /= 2)
+        for (int w = kB; w > 1; w /= 2)
+#pragma unroll
+          for (int i = 0; i < w / 2; ++i)
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[i][u] = add4(v[2 * i][u], v[2 * i + 1][u]);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
+      }
+#pragma unroll
+      for (int w = kBatches; w > 1; w /= 2)
 #pragma unroll
         for (int i = 0; i < w / 2; ++i)
 #pragma unroll
-          for (int u = 0; u < UNROLL; ++u) v[i][u] = add4(v[2 * i][u], v[2 * i + 1][u]);
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
+          for (int u = 0; u < UNROLL; ++u) res[i][u] = add4(res[2 * i][u], res[2 * i + 1][u]);
+      store_all<BF, UNROLL>(args, base, res[0]);
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          float level[N];
+          for (int r = 0; r < N; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
+          for (int w = N; w > 1; w /= 2)
+            for (int i = 0; i < w / 2; ++i) level[i] = level[2 * i] + level[2 * i + 1];
+          store_all1(args, BF, e, level[0]);
+        }
     }
-#pragma unroll
-    for (int w = kBatches; w > 1; w /= 2)
-#pragma unroll
-      for (int i = 0; i < w / 2; ++i)
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) res[i][u] = add4(res[2 * i][u], res[2 * i + 1][u]);
-    store_all<BF, UNROLL>(args, base, res[0]);
-  } else {
-    for (int u = 0; u < UNROLL; ++u)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
-        if (e < op.lo || e >= op.hi) continue;
-        float level[N];
-        for (int r = 0; r < N; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
-        for (int w = N; w > 1; w /= 2)
-          for (int i = 0; i < w / 2; ++i) level[i] = level[2 * i] + level[2 * i + 1];
-        store_all1(args, BF, e, level[0]);
-      }
   }
 }
 
-constexpr int kReduceUnroll = AR_REDUCE_UNROLL;
-constexpr int kCopyUnroll = AR_COPY_UNROLL;
+// Step kernels come in two shapes: 2 units per thread, and 1 unit per thread
+// (more waves in flight).  The 1-unit shape is faster (measured on MI355X)
+// for launches that write more into rank buffers than the 256 MB Infinity
+// Cache holds, so that the next step streams from DRAM; the 2-unit shape is
+// faster for smaller launches, whose inputs the previous step left in the
+// cache, and for launches writing fp32 scratch with non-temporal stores.
+constexpr int kUnrollWarm = AR_REDUCE_UNROLL;
+constexpr int kUnrollCold = AR_COLD_UNROLL;
 // one-pass shapes per dtype (measured): fp32 2 units x 8 ranks in flight,
 // bf16 1 unit x 16 ranks
 constexpr int kOnePassUnrollF32 = AR_ONEPASS_UNROLL_F32, kFoldBatchF32 = AR_FOLD_BATCH_F32;
 constexpr int kOnePassUnrollBF16 = AR_ONEPASS_UNROLL_BF16, kFoldBatchBF16 = AR_FOLD_BATCH_BF16;
 constexpr bool kNtsRank = AR_NTS_RANK;
+constexpr int64_t kCacheBytes = AR_CACHE_BYTES;
 constexpr bool kNtsScratch = AR_NTS_SCRATCH;
 
-template <int FLAGS>
-hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
-  if (out_scratch && kNtsScratch)
-    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, true>), grid, dim3(kBlock), 0, s, a);
-  else if (!out_scratch && kNtsRank)
-    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, true>), grid, dim3(kBlock), 0, s, a);
+template <int FLAGS, int U>
+hipError_t launch_reduce_u(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
+  if ((out_scratch && kNtsScratch) || (!out_scratch && kNtsRank))
+    hipLaunchKernelGGL((chunk_reduce<FLAGS, U, true>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_reduce<FLAGS, kReduceUnroll, false>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((chunk_reduce<FLAGS, U, false>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FLAGS>
+hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch, bool cold) {
+  return cold ? launch_reduce_u<FLAGS, kUnrollCold>(grid, a, s, out_scratch)
+              : launch_reduce_u<FLAGS, kUnrollWarm>(grid, a, s, out_scratch);
+}
+
+template <int ES>
+hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
+  if (cold) hipLaunchKernelGGL((chunk_copy<ES, kUnrollCold, kNtsRank>), grid, dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((chunk_copy<ES, kUnrollWarm, kNtsRank>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -472,41 +525,52 @@ hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int64_t tile_elems(int32_t kind) {
+dim3 grid_for(uint32_t tiles, uint32_t nops) {
+  if (AR_PERSIST_X > 0 && tiles > static_cast<uint32_t>(AR_PERSIST_X)) tiles = AR_PERSIST_X;
+#if AR_GRID_INTERLEAVE
+  return dim3(tiles * nops, 1);
+#else
+  return dim3(tiles, nops);
+#endif
+}
+
+bool is_cold(int64_t written_bytes, bool out_scratch) { return !out_scratch && written_bytes > kCacheBytes; }
+
+int64_t tile_elems(int32_t kind, bool cold) {
+  const int64_t u = cold ? kUnrollCold : kUnrollWarm;
   switch (kind & 0xF00) {
-    case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * kReduceUnroll;
-    case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * kCopyUnroll;
+    case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * u;
+    case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
     default: return static_cast<int64_t>(kBlock) * 4 * ((kind & 1) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }
 }
 
-hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
+hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch, bool cold) {
   switch (kind & 0xF00) {
     case kKindReduce:
       switch (kind & 0xF) {
-        case 0: return launch_reduce<0>(grid, a, s, out_scratch);
-        case 1: return launch_reduce<1>(grid, a, s, out_scratch);
-        case 2: return launch_reduce<2>(grid, a, s, out_scratch);
-        case 3: return launch_reduce<3>(grid, a, s, out_scratch);
-        case 4: return launch_reduce<4>(grid, a, s, out_scratch);
-        case 5: return launch_reduce<5>(grid, a, s, out_scratch);
-        case 6: return launch_reduce<6>(grid, a, s, out_scratch);
-        case 7: return launch_reduce<7>(grid, a, s, out_scratch);
-        case 8: return launch_reduce<8>(grid, a, s, out_scratch);
-        case 9: return launch_reduce<9>(grid, a, s, out_scratch);
-        case 10: return launch_reduce<10>(grid, a, s, out_scratch);
-        case 11: return launch_reduce<11>(grid, a, s, out_scratch);
-        case 12: return launch_reduce<12>(grid, a, s, out_scratch);
-        case 13: return launch_reduce<13>(grid, a, s, out_scratch);
-        case 14: return launch_reduce<14>(grid, a, s, out_scratch);
-        case 15: return launch_reduce<15>(grid, a, s, out_scratch);
+        case 0: return launch_reduce<0>(grid, a, s, out_scratch, cold);
+        case 1: return launch_reduce<1>(grid, a, s, out_scratch, cold);
+        case 2: return launch_reduce<2>(grid, a, s, out_scratch, cold);
+        case 3: return launch_reduce<3>(grid, a, s, out_scratch, cold);
+        case 4: return launch_reduce<4>(grid, a, s, out_scratch, cold);
+        case 5: return launch_reduce<5>(grid, a, s, out_scratch, cold);
+        case 6: return launch_reduce<6>(grid, a, s, out_scratch, cold);
+        case 7: return launch_reduce<7>(grid, a, s, out_scratch, cold);
+        case 8: return launch_reduce<8>(grid, a, s, out_scratch, cold);
+        case 9: return launch_reduce<9>(grid, a, s, out_scratch, cold);
+        case 10: return launch_reduce<10>(grid, a, s, out_scratch, cold);
+        case 11: return launch_reduce<11>(grid, a, s, out_scratch, cold);
+        case 12: return launch_reduce<12>(grid, a, s, out_scratch, cold);
+        case 13: return launch_reduce<13>(grid, a, s, out_scratch, cold);
+        case 14: return launch_reduce<14>(grid, a, s, out_scratch, cold);
+        case 15: return launch_reduce<15>(grid, a, s, out_scratch, cold);
       }
       break;
     case kKindCopy:
-      if ((kind & 0xFF) == 2) hipLaunchKernelGGL((chunk_copy<2, kCopyUnroll, kNtsRank>), grid, dim3(kBlock), 0, s, a);
-      else if ((kind & 0xFF) == 4) hipLaunchKernelGGL((chunk_copy<4, kCopyUnroll, kNtsRank>), grid, dim3(kBlock), 0, s, a);
-      else return hipErrorInvalidValue;
-      return hipGetLastError();
+      if ((kind & 0xFF) == 2) return launch_copy<2>(grid, a, s, cold);
+      if ((kind & 0xFF) == 4) return launch_copy<4>(grid, a, s, cold);
+      return hipErrorInvalidValue;
     case kKindRing:
       if (kind & 1)
         hipLaunchKernelGGL((onepass_ring<true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);

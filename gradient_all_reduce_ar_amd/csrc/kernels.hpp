@@ -7,6 +7,12 @@
 
 #include "plan.hpp"
 
+#ifndef AR_PERSIST_X
+#define AR_PERSIST_X 0  // > 0: at most this many blocks per op, each looping over tiles
+#endif
+#ifndef AR_GRID_INTERLEAVE
+#define AR_GRID_INTERLEAVE 0
+#endif
 #ifndef AR_BLOCK
 #define AR_BLOCK 256
 #endif
@@ -31,8 +37,11 @@
 #ifndef AR_REDUCE_UNROLL
 #define AR_REDUCE_UNROLL 2
 #endif
-#ifndef AR_COPY_UNROLL
-#define AR_COPY_UNROLL 2
+#ifndef AR_COLD_UNROLL
+#define AR_COLD_UNROLL 1
+#endif
+#ifndef AR_CACHE_BYTES
+#define AR_CACHE_BYTES (256ll << 20)  // MI355X Infinity Cache (MALL) capacity
 #endif
 #ifndef AR_ONEPASS_UNROLL_F32
 #define AR_ONEPASS_UNROLL_F32 2
@@ -64,14 +73,22 @@ struct KArgs {
   int64_t slot_stride;    // elements per slot
   const DevOp *ops;       // this launch's ops
   int32_t nranks, group_size;
+  int32_t nops;           // ops in this launch
 };
 
-// Tile (elements per block) of a kernel kind; the grid is
-// (max over ops of tiles spanned, number of ops).
-int64_t tile_elems(int32_t kind);
+// Whether a step launch takes the streaming (cold) shape: it writes more
+// into rank buffers than the Infinity Cache holds.
+bool is_cold(int64_t written_bytes, bool out_scratch);
+
+// Tile (elements per block) of a kernel kind in the warm or cold shape.
+int64_t tile_elems(int32_t kind, bool cold);
+
+// Grid of a launch whose ops span at most `tiles` tiles each.
+dim3 grid_for(uint32_t tiles, uint32_t nops);
 
 // Launches the kernel of `kind` on stream s.  out_scratch: the launch's
-// outputs are fp32 scratch slots (selects the store cache policy).
-hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch);
+// outputs are fp32 scratch slots (selects the store cache policy); cold: the
+// streaming shape (see is_cold).
+hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch, bool cold);
 
 }  // namespace ar_dev
