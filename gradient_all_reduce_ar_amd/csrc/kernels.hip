@@ -69,6 +69,14 @@ __device__ __forceinline__ BlockCoord block_coord(const KArgs &a) {
   return {static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.nops)),
           static_cast<int64_t>(blockIdx.x / static_cast<uint32_t>(a.nops)),
           static_cast<int64_t>(gridDim.x / static_cast<uint32_t>(a.nops))};
+#elif AR_XCD_REMAP
+  // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; this
+  // remap hands each XCD one contiguous run of (op, tile) pairs instead.
+  (void)a;
+  const uint32_t total = gridDim.x * gridDim.y;
+  uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
+  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  return {static_cast<int>(lin / gridDim.x), static_cast<int64_t>(lin % gridDim.x), static_cast<int64_t>(gridDim.x)};
 #else
   (void)a;
   return {static_cast<int>(blockIdx.y), static_cast<int64_t>(blockIdx.x), static_cast<int64_t>(gridDim.x)};

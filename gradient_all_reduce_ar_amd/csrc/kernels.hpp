@@ -10,6 +10,9 @@
 #ifndef AR_PERSIST_X
 #define AR_PERSIST_X 0  // > 0: at most this many blocks per op, each looping over tiles
 #endif
+#ifndef AR_XCD_REMAP
+#define AR_XCD_REMAP 0
+#endif
 #ifndef AR_GRID_INTERLEAVE
 #define AR_GRID_INTERLEAVE 0
 #endif
