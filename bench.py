@@ -36,6 +36,8 @@ WORKLOADS = {
            "ring", 16, 8, "fp32", 12288 * 4096),
     "c3": ("ring all-reduce, 16 virtual ranks x 192 MiB bf16 (100,663,296 elements each), N(0,1e-3), "
            "fp32 accumulate", "ring", 16, 8, "bf16", 2 * 12288 * 4096),
+    "c3e": ("ring all-reduce, 16 virtual ranks x 192 MiB bf16, N(0,1e-3), every partial sum rounded to bf16",
+            "ring", 16, 8, "bf16_each", 2 * 12288 * 4096),
     "c4": ("hierarchical all-reduce, 2 groups x 8 ranks x 192 MiB fp32, N(0,1e-3)",
            "hierarchical", 16, 8, "fp32", 12288 * 4096),
     "c5r16": ("Rabenseifner, 16 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "rabenseifner", 16, 1,
@@ -134,6 +136,7 @@ def main():
     torch.cuda.set_device(dev)
     elem = 4 if dtype == "fp32" else 2
     view = np.float32 if dtype == "fp32" else np.int16
+    gen_dtype = "fp32" if dtype == "fp32" else "bf16"
 
     if args.calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -152,12 +155,12 @@ def main():
         plan = B.ar_bucket_plan_create(n, group, sizes, dtype, sched, 25 << 20)
         B.ar_bucket_set_exec(plan, args.exec)
         offsets, arena = B.ar_bucket_layout(plan, len(sizes))
-        host = workloads.bucketed_arenas(n, sizes, offsets, arena, dtype=dtype)
+        host = workloads.bucketed_arenas(n, sizes, offsets, arena, dtype=gen_dtype)
         count_logical = int(sum(int(c) for c in sizes))
     else:
         plan = B.ar_plan_create(n, group, count, dtype, sched)
         B.ar_plan_set_exec(plan, args.exec)
-        host = workloads.normal_inputs(n, count, seed=0, dtype=dtype)
+        host = workloads.normal_inputs(n, count, seed=0, dtype=gen_dtype)
         count_logical = count
     bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
     torch.cuda.synchronize()
@@ -287,7 +290,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if dtype == "fp32" else "bf16 (f32 accumulate)",
+        "dtype": {"fp32": "f32", "bf16": "bf16 (f32 accumulate)", "bf16_each": "bf16 (rounded each add)"}[dtype],
         "data": "synthetic",
         "config": {
             "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,

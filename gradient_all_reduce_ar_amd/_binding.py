@@ -15,12 +15,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libar.so")
 
 AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP = range(5)
-AR_FLOAT32, AR_BFLOAT16 = 0, 1
+AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP = 0, 1, 2
 AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER = 0, 1, 2
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
 AR_MAX_RANKS = 64
 
-DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16}
+DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP}
 SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER}
 EXECS = {"steps": AR_EXEC_STEPS, "steps_unfused": AR_EXEC_STEPS_UNFUSED, "onepass": AR_EXEC_ONEPASS}
 

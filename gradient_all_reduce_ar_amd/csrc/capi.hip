@@ -391,7 +391,7 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
     fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
     return nullptr;
   }
-  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16) {
+  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_BFLOAT16_EACH_STEP) {
     fail(AR_ERR_INVALID_ARG, "unknown dtype");
     return nullptr;
   }
@@ -403,7 +403,7 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
   bp->nranks = nranks;
   bp->group_size = group_size;
   bp->dtype = dtype;
-  const int64_t eb = dtype == AR_BFLOAT16 ? 2 : 4;
+  const int64_t eb = dtype == AR_FLOAT32 ? 4 : 2;
   std::vector<int64_t> counts(tensor_counts, tensor_counts + ntensors);
   for (int64_t c : counts)
     if (c < 0) {
@@ -478,7 +478,7 @@ ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, 
     if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("bucket scratch: ") + hipGetErrorString(e));
     bp->scratch_bytes = need;
   }
-  const int64_t eb = bp->dtype == AR_BFLOAT16 ? 2 : 4;
+  const int64_t eb = bp->dtype == AR_FLOAT32 ? 4 : 2;
   std::vector<void *> ptrs(static_cast<size_t>(bp->nranks));
   for (size_t b = 0; b < bp->plans.size(); ++b) {
     ar_plan_t *pl = bp->plans[b];
@@ -517,7 +517,7 @@ ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
   }
   s.nranks = bp->nranks;
   s.group_size = bp->group_size;
-  s.elem_bytes = bp->dtype == AR_BFLOAT16 ? 2 : 4;
+  s.elem_bytes = bp->dtype == AR_FLOAT32 ? 4 : 2;
   s.bytes_sent = bp->bytes_sent.data();
   for (uint64_t b : bp->bytes_sent) {
     s.bytes_sent_max = std::max(s.bytes_sent_max, b);

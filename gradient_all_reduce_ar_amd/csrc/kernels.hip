@@ -158,6 +158,20 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// One fold step of a one-pass kernel; EACH rounds the partial sum to bf16 at
+// once (the round-each-step bf16 mode), else it stays fp32.
+__device__ __forceinline__ float round_keep(float v) { return widen(narrow(v)); }
+template <bool EACH>
+__device__ __forceinline__ float4 fold4(float4 a, float4 b) {
+  const float4 s = add4(a, b);
+  if constexpr (EACH) return make_float4(round_keep(s.x), round_keep(s.y), round_keep(s.z), round_keep(s.w));
+  return s;
+}
+__device__ __forceinline__ float fold1(bool each, float a, float b) {
+  const float s = a + b;
+  return each ? round_keep(s) : s;
+}
+
 // ---------------------------------------------------------------------------
 // Chunk reduce: o[e] = a[e] + b[e] over the op's range, optionally also
 // written to o2 (the fused forwarding copy of the chunk just completed).
@@ -288,7 +302,7 @@ __device__ __forceinline__ void store_all(const KArgs &args, int64_t base, const
 // acc (+)= x_r for r = first, first+1, ... (count ranks, wrapping at `wrap_n`
 // inside the block of ranks starting at `rank0`), kFB ranks' loads in flight
 // at a time; the adds stay in order.
-template <bool BF, int UNROLL, int kFB>
+template <bool BF, bool EACH, int UNROLL, int kFB>
 __device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, int wrap_n, int first, int count,
                                                 int64_t base, float4 (&acc)[UNROLL], bool init) {
   int r = first;
@@ -310,7 +324,7 @@ __device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, in
 #pragma unroll
     for (int q = 0; q < kFB; ++q)
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[q][u]);
+      for (int u = 0; u < UNROLL; ++u) acc[u] = fold4<EACH>(acc[u], x[q][u]);
     r = (rr[kFB - 1] + 1 == wrap_n) ? 0 : rr[kFB - 1] + 1;
   }
   const int rem = count - t;  // fewer than kFB ranks left: one predicated batch
@@ -326,13 +340,13 @@ __device__ __forceinline__ void ring_fold_units(const KArgs &args, int rank0, in
     for (int q = 0; q + 1 < kFB; ++q)
       if (q < rem) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], x[q][u]);
+        for (int u = 0; u < UNROLL; ++u) acc[u] = fold4<EACH>(acc[u], x[q][u]);
       }
   }
 }
 
-__device__ __forceinline__ float ring_fold1(const KArgs &args, bool bf, int rank0, int wrap_n, int first,
-                                            int count, int64_t e) {
+__device__ __forceinline__ float ring_fold1(const KArgs &args, bool bf, bool each, int rank0, int wrap_n,
+                                            int first, int count, int64_t e) {
   auto ld = [&](int r) {
     const char *p = static_cast<const char *>(args.rank[rank0 + r]);
     return bf ? load1<true>(p, e) : load1<false>(p, e);
@@ -341,7 +355,7 @@ __device__ __forceinline__ float ring_fold1(const KArgs &args, bool bf, int rank
   float acc = ld(r);
   for (int t = 1; t < count; ++t) {
     r = (r + 1 == wrap_n) ? 0 : r + 1;
-    acc = acc + ld(r);
+    acc = fold1(each, acc, ld(r));
   }
   return acc;
 }
@@ -355,7 +369,7 @@ __device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e
 }
 
 // Ring: element in chunk c is ((x_c + x_{c+1}) + ...) + x_{c+N-1}; aux = c.
-template <bool BF, int UNROLL, int FB>
+template <bool BF, bool EACH, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
   const BlockCoord bc = block_coord(args);
@@ -366,14 +380,14 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
     const int n = args.nranks;
     if (base >= op.lo && base + kTile <= op.hi) {
       float4 acc[UNROLL];
-      ring_fold_units<BF, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
+      ring_fold_units<BF, EACH, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
       store_all<BF, UNROLL>(args, base, acc);
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
           const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
-          store_all1(args, BF, e, ring_fold1(args, BF, 0, n, op.aux, n, e));
+          store_all1(args, BF, e, ring_fold1(args, BF, EACH, 0, n, op.aux, n, e));
         }
     }
   }
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
 // Hierarchical: group partial of slice k, ((x_{g,k+1} + x_{g,k+2}) + ...) +
 // x_{g,k}; sub-chunk j folds the group partials P_j + P_{j+1} + ... in ring
 // order.  aux = ((k + 1) mod G) | (j << 8).
-template <bool BF, int UNROLL, int FB>
+template <bool BF, bool EACH, int UNROLL, int FB>
 __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
   const BlockCoord bc = block_coord(args);
@@ -397,13 +411,13 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
       int g = j;
       for (int m = 0; m < M; ++m) {
         float4 part[UNROLL];
-        ring_fold_units<BF, UNROLL, FB>(args, g * G, G, lstart, G, base, part, true);
+        ring_fold_units<BF, EACH, UNROLL, FB>(args, g * G, G, lstart, G, base, part, true);
         if (m == 0) {
 #pragma unroll
           for (int u = 0; u < UNROLL; ++u) acc[u] = part[u];
         } else {
 #pragma unroll
-          for (int u = 0; u < UNROLL; ++u) acc[u] = add4(acc[u], part[u]);
+          for (int u = 0; u < UNROLL; ++u) acc[u] = fold4<EACH>(acc[u], part[u]);
         }
         g = (g + 1 == M) ? 0 : g + 1;
       }
@@ -416,8 +430,8 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
           float acc = 0.f;
           int g = j;
           for (int m = 0; m < M; ++m) {
-            const float part = ring_fold1(args, BF, g * G, G, lstart, G, e);
-            acc = (m == 0) ? part : acc + part;
+            const float part = ring_fold1(args, BF, EACH, g * G, G, lstart, G, e);
+            acc = (m == 0) ? part : fold1(EACH, acc, part);
             g = (g + 1 == M) ? 0 : g + 1;
           }
           store_all1(args, BF, e, acc);
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
 
 // Rabenseifner: the balanced pairwise tree over ranks in index order, formed
 // batch by batch (8 ranks at a time) and merged like a binary counter.
-template <bool BF, int N, int UNROLL>
+template <bool BF, bool EACH, int N, int UNROLL>
 __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
   constexpr int kB = N < 8 ? N : 8;
   constexpr int kBatches = N / kB;
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
 #pragma unroll
           for (int i = 0; i < w / 2; ++i)
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) v[i][u] = add4(v[2 * i][u], v[2 * i + 1][u]);
+            for (int u = 0; u < UNROLL; ++u) v[i][u] = fold4<EACH>(v[2 * i][u], v[2 * i + 1][u]);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
       }
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
 #pragma unroll
         for (int i = 0; i < w / 2; ++i)
 #pragma unroll
-          for (int u = 0; u < UNROLL; ++u) res[i][u] = add4(res[2 * i][u], res[2 * i + 1][u]);
+          for (int u = 0; u < UNROLL; ++u) res[i][u] = fold4<EACH>(res[2 * i][u], res[2 * i + 1][u]);
       store_all<BF, UNROLL>(args, base, res[0]);
     } else {
       for (int u = 0; u < UNROLL; ++u)
@@ -471,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
           float level[N];
           for (int r = 0; r < N; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
           for (int w = N; w > 1; w /= 2)
-            for (int i = 0; i < w / 2; ++i) level[i] = level[2 * i] + level[2 * i + 1];
+            for (int i = 0; i < w / 2; ++i) level[i] = fold1(EACH, level[2 * i], level[2 * i + 1]);
           store_all1(args, BF, e, level[0]);
         }
     }
@@ -516,20 +530,21 @@ hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
   return hipGetLastError();
 }
 
-template <bool BF>
+template <bool BF, bool EACH>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
   switch (n) {
-    case 2: hipLaunchKernelGGL((onepass_tree<BF, 2, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((onepass_tree<BF, 4, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((onepass_tree<BF, 8, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((onepass_tree<BF, 16, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((onepass_tree<BF, 32, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((onepass_tree<BF, 64, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+
 
 }  // namespace
 
@@ -549,7 +564,7 @@ int64_t tile_elems(int32_t kind, bool cold) {
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * u;
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
-    default: return static_cast<int64_t>(kBlock) * 4 * ((kind & 1) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
+    default: return static_cast<int64_t>(kBlock) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }
 }
 
@@ -580,19 +595,25 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
       if ((kind & 0xFF) == 4) return launch_copy<4>(grid, a, s, cold);
       return hipErrorInvalidValue;
     case kKindRing:
-      if (kind & 1)
-        hipLaunchKernelGGL((onepass_ring<true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      if ((kind & 3) == 2)
+        hipLaunchKernelGGL((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      else if ((kind & 3) == 1)
+        hipLaunchKernelGGL((onepass_ring<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_ring<false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_ring<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
       return hipGetLastError();
     case kKindHier:
-      if (kind & 1)
-        hipLaunchKernelGGL((onepass_hier<true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      if ((kind & 3) == 2)
+        hipLaunchKernelGGL((onepass_hier<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+      else if ((kind & 3) == 1)
+        hipLaunchKernelGGL((onepass_hier<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_hier<false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_hier<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
       return hipGetLastError();
     case kKindTree:
-      return (kind & 1) ? launch_tree<true>(a.nranks, grid, a, s) : launch_tree<false>(a.nranks, grid, a, s);
+      if ((kind & 3) == 2) return launch_tree<true, true>(a.nranks, grid, a, s);
+      if ((kind & 3) == 1) return launch_tree<true, false>(a.nranks, grid, a, s);
+      return launch_tree<false, false>(a.nranks, grid, a, s);
   }
   return hipErrorInvalidValue;
 }

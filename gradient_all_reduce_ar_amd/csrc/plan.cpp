@@ -13,7 +13,7 @@
 
 namespace ar {
 
-int64_t elem_bytes(Dtype d) { return d == kBF16 ? 2 : 4; }
+int64_t elem_bytes(Dtype d) { return d == kF32 ? 4 : 2; }
 
 namespace {
 
@@ -167,7 +167,7 @@ struct PartialMap {
 
 std::string lower_steps(Plan &p, bool fuse) {
   p.launches.clear();
-  const bool bf = p.dtype == kBF16;
+  const bool bf = p.dtype == kBF16;  // fp32 partials in scratch
   PartialMap partial(p.nranks);
   std::vector<bool> finals;  // per launch: all its reduces complete their range
   int max_slot = -1;
@@ -189,7 +189,9 @@ std::string lower_steps(Plan &p, bool fuse) {
         op.a = x.src;
         op.o = x.dst;
       } else if (!bf) {
-        kind = kKReduce;
+        // fp32, or bf16 rounded at every add: the rank buffers hold the
+        // partial sums themselves
+        kind = kKReduce | (p.dtype == kBF16Each ? (kFlagABf | kFlagBBf | kFlagOBf) : 0);
         op.a = x.src;
         op.b = x.dst;
         op.o = x.dst;
@@ -303,7 +305,7 @@ std::string lower_onepass(Plan &p) {
 uint64_t loc_bytes(const Plan &p, int32_t loc, bool bf16_flag) {
   if (loc == kLocNone) return 0;
   if (p.dtype == kF32) return 4;
-  return bf16_flag ? 2 : 4;
+  return bf16_flag ? 2 : 4;  // bf16 operand, or an fp32 partial in scratch
 }
 
 void compute_stats(Plan &p) {
@@ -353,7 +355,7 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   if (nranks < 1 || nranks > 64) return "nranks must be in [1, 64]";
   if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
   if (count < 0) return "count must be >= 0";
-  if (dtype != kF32 && dtype != kBF16) return "unknown dtype";
+  if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each) return "unknown dtype";
   if (sched != kRing && sched != kHier && sched != kRaben) return "unknown schedule";
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
   if (sched == kRaben && (nranks & (nranks - 1))) {

@@ -57,7 +57,11 @@ typedef enum {
   AR_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed         */
 } ar_status_t;
 
-typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1 } ar_dtype_t;
+/* AR_BFLOAT16: fp32 partial sums, each element rounded once (see above).
+ * AR_BFLOAT16_EACH_STEP: bf16 buffers whose every partial sum is rounded to
+ * bf16 (nearest, ties to even) as it is formed, as when each message of the
+ * schedule carries bf16 values; no scratch is used. */
+typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_BFLOAT16_EACH_STEP = 2 } ar_dtype_t;
 
 typedef enum { AR_RING = 0, AR_HIERARCHICAL = 1, AR_RABENSEIFNER = 2 } ar_schedule_t;
 

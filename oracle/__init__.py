@@ -6,7 +6,9 @@ library: the simulation itself is plain C in ar_oracle.c.
 
 Schedules and datatypes use the oracle's own numbering:
   schedule: "ring" | "hierarchical" | "rabenseifner"
-  dtype:    "fp32" (numpy float32 buffers) | "bf16" (numpy uint16 buffers of bf16 bits)
+  dtype:    "fp32" (numpy float32 buffers) | "bf16" (numpy uint16 buffers of bf16 bits,
+            fp32 partial sums, one rounding) | "bf16_each" (uint16 buffers, every
+            partial sum rounded to bf16 as it is formed)
 """
 import ctypes
 import os
@@ -16,8 +18,8 @@ import numpy as np
 from . import build as _build
 
 _SCHED = {"ring": 0, "hierarchical": 1, "rabenseifner": 2}
-_DTYPE = {"fp32": 0, "bf16": 1}
-_ELEM = {"fp32": 4, "bf16": 2}
+_DTYPE = {"fp32": 0, "bf16": 1, "bf16_each": 2}
+_ELEM = {"fp32": 4, "bf16": 2, "bf16_each": 2}
 REDUCE, COPY = 0, 1
 
 _lib = None

@@ -34,6 +34,9 @@
  *         by the receiver of the REDUCE that completes its chunk; COPY
  *         messages carry bf16 bits.  (Reading: the pages do not discuss
  *         reduced precision; fp32 accumulation with one final rounding.)
+ *   bf16, rounded each step: every message carries bf16 bits, and every
+ *         REDUCE widens both operands, adds in fp32 and rounds the sum to
+ *         bf16 at once -- what a wire of bf16 values gives.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -41,6 +44,7 @@
 
 #define ARO_FP32 0
 #define ARO_BF16 1
+#define ARO_BF16_EACH 2
 
 #define ARO_RING 0
 #define ARO_HIER 1
@@ -380,7 +384,7 @@ double aro_cost(int nranks, int group_size, long long count, int elem_bytes, int
  */
 int aro_run(int nranks, int group_size, long long count, int dtype, int schedule,
             void **bufs, int max_steps) {
-  if (dtype != ARO_FP32 && dtype != ARO_BF16) return -1;
+  if (dtype != ARO_FP32 && dtype != ARO_BF16 && dtype != ARO_BF16_EACH) return -1;
   aro_list L;
   int rc = build(&L, nranks, group_size, count, schedule);
   if (rc) return rc;
@@ -394,6 +398,8 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
   for (int r = 0; r < nranks && !err; ++r) {
     if (dtype == ARO_FP32) {
       w[r] = (float *)bufs[r];
+    } else if (dtype == ARO_BF16_EACH) {
+      w[r] = NULL; /* no fp32 state: the buffers are the state */
     } else {
       w[r] = (float *)malloc(sizeof(float) * (size_t)(count > 0 ? count : 1));
       if (!w[r]) { err = 1; break; }
@@ -424,7 +430,7 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
     for (int64_t j = j0; j < j1; ++j) {
       const aro_msg *x = &L.m[j];
       for (int64_t e = x->lo; e < x->hi; ++e, ++off) {
-        if (dtype == ARO_BF16 && x->kind == ARO_COPY)
+        if (dtype == ARO_BF16_EACH || (dtype == ARO_BF16 && x->kind == ARO_COPY))
           pay16[off] = ((const uint16_t *)bufs[x->src])[e];
         else
           pay[off] = w[x->src][e];
@@ -435,7 +441,15 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
     for (int64_t j = j0; j < j1; ++j) {
       const aro_msg *x = &L.m[j];
       for (int64_t e = x->lo; e < x->hi; ++e, ++off) {
-        if (x->kind == ARO_REDUCE) {
+        if (dtype == ARO_BF16_EACH) {
+          uint16_t *d = (uint16_t *)bufs[x->dst];
+          if (x->kind == ARO_REDUCE) {
+            float wide = widen_bf16(pay16[off]) + widen_bf16(d[e]);
+            d[e] = round_bf16(wide);
+          } else {
+            d[e] = pay16[off];
+          }
+        } else if (x->kind == ARO_REDUCE) {
           float sum = pay[off] + w[x->dst][e];
           w[x->dst][e] = sum;
           if (dtype == ARO_BF16 && x->completes)
@@ -450,7 +464,7 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
     j0 = j1;
   }
   free(pay); free(pay16);
-  if (dtype == ARO_BF16)
+  if (dtype != ARO_FP32)
     for (int r = 0; r < nranks; ++r) free(w[r]);
   free(w);
   free(L.m);

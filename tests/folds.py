@@ -28,22 +28,26 @@ def chunk_of(e, length, k):
     raise ValueError
 
 
-def ring_fold(vals, start):
+def add32(a, b):
+    return np.float32(np.float32(a) + np.float32(b))
+
+
+def ring_fold(vals, start, add=add32):
     n = len(vals)
     acc = np.float32(vals[start % n])
     for t in range(1, n):
-        acc = np.float32(acc + np.float32(vals[(start + t) % n]))
+        acc = add(acc, vals[(start + t) % n])
     return acc
 
 
-def tree_fold(vals):
+def tree_fold(vals, add=add32):
     level = [np.float32(v) for v in vals]
     while len(level) > 1:
-        level = [np.float32(level[2 * m] + level[2 * m + 1]) for m in range(len(level) // 2)]
+        level = [add(level[2 * m], level[2 * m + 1]) for m in range(len(level) // 2)]
     return level[0]
 
 
-def expected_fp32(xs, schedule, group_size=1):
+def expected_fp32(xs, schedule, group_size=1, add=add32):
     """xs: list of N float32 arrays.  Returns the float32 result array."""
     n = len(xs)
     count = len(xs[0])
@@ -54,9 +58,9 @@ def expected_fp32(xs, schedule, group_size=1):
             out[e] = col[0]
         elif schedule == "ring":
             c, _ = chunk_of(e, count, n)
-            out[e] = ring_fold(col, c)
+            out[e] = ring_fold(col, c, add)
         elif schedule == "rabenseifner":
-            out[e] = tree_fold(col)
+            out[e] = tree_fold(col, add)
         elif schedule == "hierarchical":
             g_sz = group_size
             m_groups = n // g_sz
@@ -65,9 +69,9 @@ def expected_fp32(xs, schedule, group_size=1):
             partials = []
             for g in range(m_groups):
                 local = [col[g * g_sz + l] for l in range(g_sz)]
-                partials.append(ring_fold(local, k + 1) if g_sz > 1 else np.float32(local[0]))
+                partials.append(ring_fold(local, k + 1, add) if g_sz > 1 else np.float32(local[0]))
             j, _ = chunk_of(e - slo, shi - slo, m_groups)
-            out[e] = ring_fold(partials, j) if m_groups > 1 else partials[0]
+            out[e] = ring_fold(partials, j, add) if m_groups > 1 else partials[0]
         else:
             raise ValueError(schedule)
     return out
@@ -92,3 +96,16 @@ def expected_bf16(bits_list, schedule, group_size=1):
         return np.asarray(bits_list[0], np.uint16).copy()
     xs = [widen(b) for b in bits_list]
     return to_bf16_bits(expected_fp32(xs, schedule, group_size))
+
+
+def add_bf16_each(a, b):
+    """One add of the round-each-step mode: fp32 add of bf16 values, then RNE
+    to bf16 (torch's conversion), returned widened."""
+    return widen(to_bf16_bits(np.array([np.float32(a) + np.float32(b)], np.float32)))[0]
+
+
+def expected_bf16_each(bits_list, schedule, group_size=1):
+    if len(bits_list) == 1:
+        return np.asarray(bits_list[0], np.uint16).copy()
+    xs = [widen(b) for b in bits_list]
+    return to_bf16_bits(expected_fp32(xs, schedule, group_size, add=add_bf16_each))

@@ -6,7 +6,7 @@ from gradient_all_reduce_ar_amd import _binding as B
 
 
 def storage_view(dtype):
-    return np.float32 if dtype == "fp32" else np.int16
+    return np.float32 if dtype == "fp32" else np.int16  # bf16 modes: 16-bit storage
 
 
 def bits_view(dtype):

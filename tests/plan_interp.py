@@ -56,15 +56,21 @@ def run(plan, bufs, dtype, group_size):
             elif fam == B.KIND_COPY:
                 bufs[o][lo:hi] = bufs[a][lo:hi]
             else:
+                each = (kind & 3) == 2  # bf16 rounded at every add
+
+                def fold(a, b):
+                    s_ = (a + b).astype(np.float32)
+                    return widen(to_bf16_bits(s_)) if each else s_
+
                 cols = [bufs[r][lo:hi].copy() if fp32_mode else widen(bufs[r][lo:hi]) for r in range(n)]
                 if fam == B.KIND_RING:
                     acc = cols[aux % n]
                     for t in range(1, n):
-                        acc = (acc + cols[(aux + t) % n]).astype(np.float32)
+                        acc = fold(acc, cols[(aux + t) % n])
                 elif fam == B.KIND_TREE:
                     level = cols
                     while len(level) > 1:
-                        level = [(level[2 * m] + level[2 * m + 1]).astype(np.float32) for m in range(len(level) // 2)]
+                        level = [fold(level[2 * m], level[2 * m + 1]) for m in range(len(level) // 2)]
                     acc = level[0]
                 else:
                     G = group_size
@@ -75,8 +81,8 @@ def run(plan, bufs, dtype, group_size):
                         g = (j + mi) % M
                         part = cols[g * G + ls]
                         for t in range(1, G):
-                            part = (part + cols[g * G + (ls + t) % G]).astype(np.float32)
-                        acc = part if acc is None else (acc + part).astype(np.float32)
+                            part = fold(part, cols[g * G + (ls + t) % G])
+                        acc = part if acc is None else fold(acc, part)
                 res = acc if fp32_mode else to_bf16_bits(acc)
                 for r in range(n):
                     bufs[r][lo:hi] = res

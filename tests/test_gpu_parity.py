@@ -53,12 +53,12 @@ SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
 
 
 @pytest.mark.parametrize("sched,n,g", SMALL)
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
 def test_small_sizes_all_modes(sched, n, g, dtype):
     # 0 and tiny sizes, one that is not a multiple of anything, and one that
     # spans several 4096-element tiles per op with a ragged tail
     for count in (0, 1, 5, 4099, 100003):
-        xs = workloads.normal_inputs(n, count, seed=count, sigma=1.0, dtype=dtype)
+        xs = workloads.normal_inputs(n, count, seed=count, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
         for mode in MODES:
             _check(xs, dtype, sched, g, mode)
 
@@ -82,7 +82,8 @@ def test_special_values_fp32():
                 assert same.all(), (sched, mode, r)
 
 
-def test_special_values_bf16():
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_each"])
+def test_special_values_bf16(dtype):
     n, count = 4, 4096 + 16
     vals = np.array([1e-40, -1e-40, 0.0, -0.0, np.inf, -np.inf, 3.3e38, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8],
                     np.float32)
@@ -90,9 +91,9 @@ def test_special_values_bf16():
     xs = [workloads._to_bf16_bits(vals[rng.integers(0, len(vals), count)]) for _ in range(n)]
     for sched, g in (("ring", 1), ("hierarchical", 2), ("rabenseifner", 1)):
         for mode in MODES:
-            _say(f"special bf16 {sched} {mode}")
-            got = gpu_allreduce(xs, "bf16", sched, g, mode)
-            ref = oracle.run([x.copy() for x in xs], "bf16", sched, group_size=g)
+            _say(f"special {dtype} {sched} {mode}")
+            got = gpu_allreduce(xs, dtype, sched, g, mode)
+            ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
             for r in range(n):
                 a, b = widen(got[r]), widen(ref[r])
                 same = (got[r] == ref[r]) | (np.isnan(a) & np.isnan(b))
@@ -136,7 +137,7 @@ E16 = workloads.BF16_192MIB_ELEMS
 def _full(dtype, sched, group, modes, fp64_check=False):
     count = E32 if dtype == "fp32" else E16
     _say(f"full-size inputs {dtype} n=16 count={count}")
-    xs = workloads.normal_inputs(16, count, seed=0, dtype=dtype)
+    xs = workloads.normal_inputs(16, count, seed=0, dtype="fp32" if dtype == "fp32" else "bf16")
     ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=group)
     bv = bits_view(dtype)
     for mode in modes:
@@ -170,3 +171,7 @@ def test_full_c4_hierarchical_fp32_2x8x192MiB():
 
 def test_full_rabenseifner_fp32_16x192MiB():
     _full("fp32", "rabenseifner", 1, ["steps"])
+
+
+def test_full_ring_bf16_each_step_16x192MiB():
+    _full("bf16_each", "ring", 8, ["steps", "onepass"])

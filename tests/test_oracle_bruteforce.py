@@ -45,6 +45,32 @@ def test_bf16_matches_closed_form(schedule, n, g):
                                           err_msg=f"{schedule} n={n} g={g} count={count} rank={r}")
 
 
+@pytest.mark.parametrize("schedule,n,g", CASES)
+def test_bf16_each_matches_closed_form(schedule, n, g):
+    """Round-each-step bf16: every partial sum is rounded to bf16 as formed."""
+    for count in (0, 1, 5, 9, 16, 33):
+        xs = workloads.uniform_inputs(n, count, seed=200 + count, dtype="bf16")
+        want = folds.expected_bf16_each(xs, schedule, g)
+        bufs = [x.copy() for x in xs]
+        oracle.run(bufs, "bf16_each", schedule, group_size=g)
+        for r in range(n):
+            np.testing.assert_array_equal(bufs[r], want,
+                                          err_msg=f"{schedule} n={n} g={g} count={count} rank={r}")
+
+
+def test_bf16_each_loses_what_once_keeps():
+    """1 + 2^-9 + 2^-9 + 2^-9: rounded once, the sum 1.005859375 goes to the
+    nearest bf16, 1.0078125; rounded at every step each 2^-9 (a quarter of
+    bf16's 2^-7 spacing at 1) is lost and the result stays 1.0."""
+    xs32 = [np.full(4, 1.0 if r == 0 else 2.0 ** -9, np.float32) for r in range(4)]
+    xs = [folds.to_bf16_bits(x) for x in xs32]
+    once = oracle.run([x.copy() for x in xs], "bf16", "ring")
+    each = oracle.run([x.copy() for x in xs], "bf16_each", "ring")
+    # ring: chunk c starts at rank c; for chunk 0 the 1.0 is added first
+    assert np.all(folds.widen(once[0]) == np.float32(1.0078125))
+    assert folds.widen(each[0])[0] == np.float32(1.0)
+
+
 def test_orders_really_differ():
     """The three schedules fold in different orders, so their low bits differ
     on generic data (Scaling ML systems ch. 06: reproducibility needs a fixed
@@ -63,19 +89,24 @@ def test_orders_really_differ():
 @pytest.mark.parametrize("schedule,n,g", [("ring", 5, 1), ("ring", 16, 8), ("hierarchical", 16, 8),
                                           ("hierarchical", 12, 3), ("rabenseifner", 16, 1),
                                           ("rabenseifner", 64, 1), ("ring", 64, 8)])
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
 def test_integer_inputs_give_exact_sum(schedule, n, g, dtype):
     count = 1000 + n
-    xs = workloads.integer_inputs(n, count, seed=n, dtype=dtype)
+    lo, hi = (-8, 8) if dtype == "fp32" else (-3, 4)
+    xs = workloads.integer_inputs(n, count, seed=n, lo=lo, hi=hi, dtype="fp32" if dtype == "fp32" else "bf16")
     exact = np.zeros(count, np.float64)
+    absum = np.zeros(count, np.float64)
     for x in xs:
-        exact += (folds.widen(x) if dtype == "bf16" else x).astype(np.float64)
-    if dtype == "bf16":
-        assert np.abs(exact).max() < 256  # every partial sum is exact in bf16's 8 bits
+        v = (x if dtype == "fp32" else folds.widen(x)).astype(np.float64)
+        exact += v
+        absum += np.abs(v)
+    # every partial sum is an integer of magnitude <= sum|x|, exact in the
+    # format: below 2^24 for fp32, below 2^8 for bf16 (8 significant bits)
+    assert absum.max() < (2 ** 24 if dtype == "fp32" else 256)
     bufs = [x.copy() for x in xs]
     oracle.run(bufs, dtype, schedule, group_size=g)
     for b in bufs:
-        got = folds.widen(b) if dtype == "bf16" else b
+        got = b if dtype == "fp32" else folds.widen(b)
         np.testing.assert_array_equal(got.astype(np.float64), exact)
 
 

@@ -56,11 +56,11 @@ def test_transfers_equal_oracle(sched, n, g):
 
 
 @pytest.mark.parametrize("sched,n,g", SCHEDS)
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
 @pytest.mark.parametrize("mode", ["steps", "steps_unfused", "onepass"])
 def test_launch_list_matches_oracle(sched, n, g, dtype, mode):
     for count in (0, 3, 37, 1031):
-        xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype=dtype)
+        xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
         ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
         p = _plan(n, g, count, dtype, sched)
         try:
@@ -94,6 +94,13 @@ def test_byte_model_closed_forms():
         finally:
             B.ar_plan_destroy(p)
     e16 = 2 * e
+    p = _plan(n, 8, e16, "bf16_each", "ring")
+    try:
+        # round-each-step bf16 is fp32's byte model at half the element size
+        assert B.ar_plan_stats(p)["hbm_bytes_model"] == (5 * n - 6) * 2 * e16
+        assert B.ar_plan_stats(p)["scratch_bytes"] == 0
+    finally:
+        B.ar_plan_destroy(p)
     p = _plan(n, 8, e16, "bf16", "ring")
     try:
         assert B.ar_plan_stats(p)["hbm_bytes_model"] == (14 * n - 18 - 2) * e16
@@ -167,7 +174,7 @@ def test_plan_is_hazard_free_and_each_round_touches_each_chunk_once():
     planner refuses plans that would); creating every schedule here would
     have raised otherwise."""
     for sched, n, g in SCHEDS:
-        for dtype in ("fp32", "bf16"):
+        for dtype in ("fp32", "bf16", "bf16_each"):
             p = _plan(n, g, 4099, dtype, sched)
             for mode in ("steps", "steps_unfused", "onepass"):
                 B.ar_plan_set_exec(p, mode)
