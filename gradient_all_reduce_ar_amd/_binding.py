@@ -19,6 +19,7 @@ AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP = 0, 1, 2
 AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER = 0, 1, 2
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
 AR_MAX_RANKS = 64
+AR_MAX_PLAN_RANKS = 1024
 
 DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP}
 SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER}
@@ -33,6 +34,12 @@ class ArError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"ar status {status}: {message}")
         self.status = status
+
+
+class ar_cost_params_t(ctypes.Structure):
+    _fields_ = [("alpha_intra_s", ctypes.c_double), ("alpha_cross_s", ctypes.c_double),
+                ("bw_intra_Bps", ctypes.c_double), ("bw_cross_Bps", ctypes.c_double),
+                ("bw_group_egress_Bps", ctypes.c_double), ("egress_share", ctypes.c_double)]
 
 
 class ar_stats_t(ctypes.Structure):
@@ -78,6 +85,7 @@ def _declare(L):
         "ar_allreduce": ([P, P, P], ctypes.c_int),
         "ar_plan_stats": ([P], ar_stats_t),
         "ar_plan_cost_alpha_beta": ([P, dbl, dbl, dbl], dbl),
+        "ar_plan_cost_alpha_beta_ex": ([P, ctypes.POINTER(ar_cost_params_t)], dbl),
         "ar_plan_destroy": ([P], None),
         "ar_last_error": ([], ctypes.c_char_p),
         "ar_last_status": ([], ctypes.c_int),
@@ -167,6 +175,15 @@ def ar_plan_stats(plan):
 
 def ar_plan_cost_alpha_beta(plan, alpha_s, bw_intra_Bps, bw_cross_Bps):
     t = lib().ar_plan_cost_alpha_beta(plan, alpha_s, bw_intra_Bps, bw_cross_Bps)
+    if t < 0:
+        _raise()
+    return t
+
+
+def ar_plan_cost_alpha_beta_ex(plan, alpha_intra_s, alpha_cross_s, bw_intra_Bps, bw_cross_Bps,
+                               bw_group_egress_Bps=0.0, egress_share=1.0):
+    c = ar_cost_params_t(alpha_intra_s, alpha_cross_s, bw_intra_Bps, bw_cross_Bps, bw_group_egress_Bps, egress_share)
+    t = lib().ar_plan_cost_alpha_beta_ex(plan, ctypes.byref(c))
     if t < 0:
         _raise()
     return t

@@ -240,11 +240,15 @@ ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
 
 ar_status_t ar_plan_prepare(ar_plan_t *plan) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->p.nranks > ar::kMaxExecRanks)
+    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
   return prepare(plan);
 }
 
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->p.nranks > ar::kMaxExecRanks)
+    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
   ar_status_t st = check_rank_pointers(plan, rank_bufs);
   if (st != AR_OK) return st;
   st = prepare(plan);
@@ -294,6 +298,16 @@ double ar_plan_cost_alpha_beta(const ar_plan_t *plan, double alpha_s, double bw_
     return -1.0;
   }
   return ar::cost_alpha_beta(plan->p, alpha_s, bw_intra_Bps, bw_cross_Bps);
+}
+
+double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t *c) {
+  if (!plan || !c || !(c->bw_intra_Bps > 0) || !(c->bw_cross_Bps > 0) || c->alpha_intra_s < 0 ||
+      c->alpha_cross_s < 0 || c->bw_group_egress_Bps < 0 || !(c->egress_share >= 1)) {
+    fail(AR_ERR_INVALID_ARG, "bad cost-model arguments");
+    return -1.0;
+  }
+  return ar::cost_alpha_beta_ex(plan->p, c->alpha_intra_s, c->alpha_cross_s, c->bw_intra_Bps, c->bw_cross_Bps,
+                                c->bw_group_egress_Bps, c->egress_share);
 }
 
 void ar_plan_destroy(ar_plan_t *plan) {

@@ -338,6 +338,13 @@ void compute_stats(Plan &p) {
 
 std::string lower(Plan &p, Exec exec) {
   p.exec = exec;
+  if (p.nranks > kMaxExecRanks) {  // described (stats, cost model) but not executable
+    p.launches.clear();
+    p.nslots = 0;
+    p.slot_stride = 0;
+    compute_stats(p);
+    return "";
+  }
   std::string err;
   if (exec == kOnePass) err = lower_onepass(p);
   else err = lower_steps(p, exec == kSteps);
@@ -352,7 +359,7 @@ std::string lower(Plan &p, Exec exec) {
 std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype, Sched sched,
                        Exec exec, bool *unsupported) {
   *unsupported = false;
-  if (nranks < 1 || nranks > 64) return "nranks must be in [1, 64]";
+  if (nranks < 1 || nranks > kMaxPlanRanks) return "nranks must be in [1, 1024]";
   if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
   if (count < 0) return "count must be >= 0";
   if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each) return "unknown dtype";
@@ -393,6 +400,35 @@ double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw
   }
   double total = 0;
   for (double t : slowest) total += alpha_s + t;
+  return total;
+}
+
+double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross, double bw_intra, double bw_cross,
+                          double bw_egress, double egress_share) {
+  // [DCN] 7.2.1: T = sum over rounds of (start-up + max over resources e of
+  // V_{r,e} / B_e).  Resources: each rank's own intra and cross links, and,
+  // when bw_egress > 0, each group's shared egress ([DCN] 7.6.4, T_grad).
+  const int groups = p.nranks / p.group_size;
+  std::vector<double> link(static_cast<size_t>(p.nsteps), 0.0);
+  std::vector<std::vector<double>> egress(static_cast<size_t>(p.nsteps), std::vector<double>(groups, 0.0));
+  std::vector<bool> crosses(static_cast<size_t>(p.nsteps), false);
+  const double eb = static_cast<double>(elem_bytes(p.dtype));
+  for (const Transfer &x : p.xfers) {
+    const double bytes = static_cast<double>(x.hi - x.lo) * eb;
+    const bool cross = x.src / p.group_size != x.dst / p.group_size;
+    link[x.step] = std::max(link[x.step], bytes / (cross ? bw_cross : bw_intra));
+    if (cross) {
+      crosses[x.step] = true;
+      egress[x.step][x.src / p.group_size] += bytes * egress_share;
+    }
+  }
+  double total = 0;
+  for (int r = 0; r < p.nsteps; ++r) {
+    double t = link[r];
+    if (bw_egress > 0)
+      for (double v : egress[r]) t = std::max(t, v / bw_egress);
+    total += (crosses[r] ? alpha_cross : alpha_intra) + t;
+  }
   return total;
 }
 

@@ -59,6 +59,9 @@ struct Launch {
   std::vector<Op> ops;
 };
 
+constexpr int32_t kMaxExecRanks = 64;    // ranks a plan can execute on the GPU
+constexpr int32_t kMaxPlanRanks = 1024;  // ranks a plan can describe (stats, cost)
+
 struct Plan {
   int32_t nranks = 0, group_size = 1;
   int64_t count = 0;
@@ -88,6 +91,14 @@ std::string relower(Plan &p, Exec exec);
 
 // Per-round alpha-beta model over the transfers (seconds).
 double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw_cross);
+
+// The same with separate start-up costs for rounds without and with
+// cross-group transfers, and an optional egress resource per group of
+// bandwidth bw_egress (0 = unlimited) shared by `egress_share` identical
+// instances of the collective (every group's cross-group bytes of a round,
+// times egress_share, pass through it).
+double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross, double bw_intra, double bw_cross,
+                          double bw_egress, double egress_share);
 
 // Checks that within every launch no op writes a (location, range) that
 // another op of the same launch reads or writes.  Empty string if clean.

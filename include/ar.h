@@ -80,8 +80,12 @@ typedef enum { AR_RING = 0, AR_HIERARCHICAL = 1, AR_RABENSEIFNER = 2 } ar_schedu
  */
 typedef enum { AR_EXEC_STEPS = 0, AR_EXEC_STEPS_UNFUSED = 1, AR_EXEC_ONEPASS = 2 } ar_exec_t;
 
-/* Maximum number of virtual ranks per plan. */
+/* Maximum number of virtual ranks a plan can run on the GPU. */
 #define AR_MAX_RANKS 64
+/* Maximum number of ranks a plan can describe: plans of more than
+ * AR_MAX_RANKS ranks give transfers, statistics and the cost model only
+ * (ar_allreduce returns AR_ERR_UNSUPPORTED for them). */
+#define AR_MAX_PLAN_RANKS 1024
 
 typedef struct ar_plan ar_plan_t;
 
@@ -108,7 +112,7 @@ typedef struct {
  * ar_plan_prepare).  group_size: ranks g*G .. g*G+G-1 form group g; it must
  * divide nranks.  For AR_HIERARCHICAL it sets the intra-group size; for the
  * other schedules it only labels groups for cross_group_bytes_total.
- * Returns NULL on error: nranks outside [1, AR_MAX_RANKS], group_size < 1 or
+ * Returns NULL on error: nranks outside [1, AR_MAX_PLAN_RANKS], group_size < 1 or
  * not dividing nranks, unknown dtype or schedule (AR_ERR_INVALID_ARG);
  * Rabenseifner with nranks not a power of two (AR_ERR_UNSUPPORTED).
  */
@@ -152,6 +156,24 @@ ar_stats_t ar_plan_stats(const ar_plan_t *plan);
  */
 double ar_plan_cost_alpha_beta(const ar_plan_t *plan, double alpha_s, double bw_intra_Bps,
                                double bw_cross_Bps);
+
+/*
+ * Resource model of Data-center networks 7.6.4 (T_grad), a generalisation
+ * of the above: a round costs alpha_cross_s if it has any cross-group
+ * transfer, else alpha_intra_s, plus the slowest resource of the round:
+ * each rank's intra and cross links, and -- when bw_group_egress_Bps > 0 --
+ * one egress per group that carries the group's cross-group bytes of the
+ * round times egress_share (the number of identical collectives that share
+ * the egress, e.g. one per tensor-parallel coordinate).
+ */
+typedef struct {
+  double alpha_intra_s, alpha_cross_s;
+  double bw_intra_Bps, bw_cross_Bps;
+  double bw_group_egress_Bps; /* 0: no egress limit */
+  double egress_share;        /* >= 1 */
+} ar_cost_params_t;
+
+double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t *params);
 
 /* Releases the plan and its device memory (synchronises the device first). */
 void ar_plan_destroy(ar_plan_t *plan);

@@ -54,6 +54,8 @@ def _bind(L):
     L.aro_stats.restype = i32
     L.aro_cost.argtypes = [i32, i32, i64, i32, i32, dbl, dbl, dbl]
     L.aro_cost.restype = dbl
+    L.aro_cost_ex.argtypes = [i32, i32, i64, i32, i32, dbl, dbl, dbl, dbl, dbl, dbl]
+    L.aro_cost_ex.restype = dbl
     L.aro_run.argtypes = [i32, i32, i64, i32, i32, P, i32]
     L.aro_run.restype = i32
     return L
@@ -108,6 +110,16 @@ def cost(nranks, count_bytes_elems, elem_bytes, schedule, alpha_s, bw_intra, bw_
                               alpha_s, bw_intra, bw_cross)
     if t < 0:
         raise OracleError(f"aro_cost failed ({t})")
+    return t
+
+
+def cost_ex(nranks, count, elem_bytes, schedule, alpha_intra, alpha_cross, bw_intra, bw_cross,
+            bw_egress=0.0, share=1.0, group_size=1, L=None):
+    """[DCN] 7.6.4 resource model: per-round start-up by link class, shared group egress."""
+    t = (L or lib()).aro_cost_ex(nranks, group_size, count, elem_bytes, _SCHED[schedule], alpha_intra, alpha_cross,
+                                 bw_intra, bw_cross, bw_egress, share)
+    if t < 0:
+        raise OracleError(f"aro_cost_ex failed ({t})")
     return t
 
 

@@ -377,6 +377,55 @@ double aro_cost(int nranks, int group_size, long long count, int elem_bytes, int
 }
 
 /*
+ * Resource model of [DCN] section 7.6.4 (the hierarchical gradient time
+ * T_grad): a round costs alpha_cross if any of its messages crosses between
+ * groups, else alpha_intra, plus the largest V/B over the round's resources.
+ * Resources are each message's own link (bw_intra or bw_cross) and, when
+ * bw_egress > 0, one egress per group carrying all bytes the group sends to
+ * other groups in the round, multiplied by `share` (identical collectives
+ * running side by side through the same egress).  Seconds; < 0 on error.
+ */
+double aro_cost_ex(int nranks, int group_size, long long count, int elem_bytes, int schedule,
+                   double alpha_intra, double alpha_cross, double bw_intra, double bw_cross,
+                   double bw_egress, double share) {
+  aro_list L;
+  int rc = build(&L, nranks, group_size, count, schedule);
+  if (rc) return (double)rc;
+  int ngroups = nranks / group_size;
+  int nrounds = L.nsteps > 0 ? L.nsteps : 1;
+  double *round_t = (double *)calloc((size_t)nrounds, sizeof(double));
+  int *round_cross = (int *)calloc((size_t)nrounds, sizeof(int));
+  double *out_bytes = (double *)calloc((size_t)nrounds * (size_t)ngroups, sizeof(double));
+  if (!round_t || !round_cross || !out_bytes) {
+    free(round_t); free(round_cross); free(out_bytes); free(L.m);
+    return -3.0;
+  }
+  for (int64_t j = 0; j < L.n; ++j) {
+    const aro_msg *x = &L.m[j];
+    double bytes = (double)(x->hi - x->lo) * elem_bytes;
+    int gs = x->src / group_size, gd = x->dst / group_size;
+    double t = bytes / (gs != gd ? bw_cross : bw_intra);
+    if (t > round_t[x->step]) round_t[x->step] = t;
+    if (gs != gd) {
+      round_cross[x->step] = 1;
+      out_bytes[(size_t)x->step * ngroups + gs] += bytes;
+    }
+  }
+  double total = 0.0;
+  for (int r = 0; r < L.nsteps; ++r) {
+    double t = round_t[r];
+    if (bw_egress > 0)
+      for (int g = 0; g < ngroups; ++g) {
+        double te = out_bytes[(size_t)r * ngroups + g] * share / bw_egress;
+        if (te > t) t = te;
+      }
+    total += (round_cross[r] ? alpha_cross : alpha_intra) + t;
+  }
+  free(round_t); free(round_cross); free(out_bytes); free(L.m);
+  return total;
+}
+
+/*
  * Runs the schedule in place on host buffers bufs[0..nranks-1] (float* for
  * fp32, uint16_t* holding bf16 bits for bf16).  Only the first max_steps
  * rounds are simulated when max_steps >= 0 (used to inspect intermediate

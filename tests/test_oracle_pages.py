@@ -268,3 +268,38 @@ def test_ring_lower_bound_matches():
         assert t == pytest.approx(2 * (n - 1) / n * e * 4 / 1e9, rel=1e-12)
         t = oracle.cost(n, e, 4, "rabenseifner", 0.0, 1e9, 1e9)
         assert t == pytest.approx(2 * (n - 1) / n * e * 4 / 1e9, rel=1e-12)
+
+
+def test_hierarchical_gradient_time_and_egress_bytes():
+    """Data-center networks 7.6.4 (fixture hierarchical_grad_pages.txt): the
+    per-supernode cross bytes V_out = 2 (H-1)/H * 8G and the hierarchical
+    gradient time T_grad = 2(q-1)a_L + 2(q-1)G/(q B_L) + 2(H-1)a_R
+    + max(2(H-1)G/(H q B_NIC), V_out/B_out) for the printed supernode sizes."""
+    G = 8e9  # bytes per GPU shard (bf16)
+    for row in _rows("hierarchical_grad_pages.txt"):
+        S, q, H = int(row[0]), int(row[1]), int(row[2])
+        vout_gb, egress, want_ms, tol = float(row[3]), float(row[4]), float(row[5]), float(row[6])
+        n = q * H
+        count = int(G) // 2
+        _, cross, _ = oracle.stats(n, count, "bf16", "hierarchical", group_size=q)
+        # one DP instance's cross bytes per supernode, times 8 TP coordinates
+        assert cross / H * 8 == pytest.approx(vout_gb * 1e9, rel=1e-9)
+        t = oracle.cost_ex(n, count, 2, "hierarchical", 0.83e-6, 0.83e-6, 450e9, 50e9, egress * 1e9, 8.0,
+                           group_size=q)
+        assert t * 1e3 == pytest.approx(want_ms, rel=tol), (S, t * 1e3)
+    # the cross-domain term for S = 128 is about 17.5 ms, and 52.5 ms when
+    # 3:1 oversubscription cuts the egress to a third
+    for egress, want in ((128 * 50e9, 17.5e-3), (128 * 50e9 / 3, 52.5e-3)):
+        q, H = 16, 8
+        full = oracle.cost_ex(q * H, int(G) // 2, 2, "hierarchical", 0.0, 0.0, 450e9, 50e9, egress, 8.0, group_size=q)
+        local_only = 2 * (q - 1) * G / (q * 450e9)
+        assert full - local_only == pytest.approx(want, rel=0.01)
+
+
+def test_latency_terms_for_1024_gpus():
+    """Primer ch. 4 section 4.3 and Panel 4.3: 1,024 ranks and alpha = 22 us:
+    the ring spends 2,046 x 22 us = 45 ms in latency; the doubling tree's 10
+    steps take about 0.4 ms for a 1 MB message at 50 GB/s."""
+    t = oracle.cost(1024, 0, 4, "ring", 22e-6, 50e9, 50e9)
+    assert t == pytest.approx(2046 * 22e-6, rel=1e-12) and round(t * 1e3) == 45
+    assert oracle.steps(1024, "ring") == 2046 and oracle.steps(1024, "rabenseifner") == 20

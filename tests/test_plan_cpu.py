@@ -138,7 +138,7 @@ def test_bf16_scratch_slots():
 
 @pytest.mark.parametrize("args,status", [
     ((0, 1, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
-    ((65, 1, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
+    ((1025, 1, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
     ((4, 3, 10, "fp32", "ring"), B.AR_ERR_INVALID_ARG),
     ((4, 0, 10, "fp32", "hierarchical"), B.AR_ERR_INVALID_ARG),
     ((4, 1, 10, 7, "ring"), B.AR_ERR_INVALID_ARG),
@@ -179,3 +179,43 @@ def test_plan_is_hazard_free_and_each_round_touches_each_chunk_once():
             for mode in ("steps", "steps_unfused", "onepass"):
                 B.ar_plan_set_exec(p, mode)
             B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n,g", [("ring", 16, 8), ("hierarchical", 16, 8), ("hierarchical", 128, 16),
+                                       ("hierarchical", 64, 8), ("rabenseifner", 256, 16), ("ring", 128, 1)])
+def test_extended_cost_model_equals_oracle(sched, n, g):
+    count = 4_000_000_000 // 8 if n >= 128 else 1 << 20
+    p = _plan(n, g, count, "bf16", sched)
+    try:
+        for args in ((0.83e-6, 0.83e-6, 450e9, 50e9, 0.0, 1.0), (1e-6, 5e-6, 450e9, 50e9, 400e9, 8.0),
+                     (0.0, 0.0, 900e9, 25e9, 3200e9, 8.0)):
+            mine = B.ar_plan_cost_alpha_beta_ex(p, *args)
+            ref = oracle.cost_ex(n, count, 2, sched, *args, group_size=g)
+            assert mine == pytest.approx(ref, rel=1e-12)
+    finally:
+        B.ar_plan_destroy(p)
+
+
+def test_large_plans_describe_but_do_not_run():
+    """Plans of up to 1024 ranks give transfers, stats and the cost model;
+    running them is refused without touching any device."""
+    p = B.ar_plan_create(1024, 8, 1 << 20, "fp32", "ring")
+    try:
+        st = B.ar_plan_stats(p)
+        assert st["steps"] == 2046 and st["launches"] == 0
+        assert B.ar_plan_cost_alpha_beta(p, 22e-6, 50e9, 50e9) > 2046 * 22e-6
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce(p, [1 << 20] * 1024)
+        assert ei.value.status == B.AR_ERR_UNSUPPORTED
+    finally:
+        B.ar_plan_destroy(p)
+    mine = B.ar_plan_create(128, 16, 4096, "fp32", "hierarchical")
+    try:
+        got = _sorted(B.ar_plan_transfers(mine))
+        ref = _sorted(oracle.messages(128, 4096, "hierarchical", group_size=16))
+        for k in ("step", "src", "dst", "lo", "hi", "kind"):
+            np.testing.assert_array_equal(got[k], ref[k])
+    finally:
+        B.ar_plan_destroy(mine)
+    with pytest.raises(B.ArError):
+        B.ar_plan_create(1025, 1, 10, "fp32", "ring")
