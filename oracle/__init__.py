@@ -5,7 +5,8 @@ CPU-baseline leg may import this package.  It shares no code with the GPU
 library: the simulation itself is plain C in ar_oracle.c.
 
 Schedules and datatypes use the oracle's own numbering:
-  schedule: "ring" | "hierarchical" | "rabenseifner"
+  schedule: "ring" | "hierarchical" | "rabenseifner" | "recursive_doubling" | "tree" |
+            "double_tree"
   dtype:    "fp32" (numpy float32 buffers) | "bf16" (numpy uint16 buffers of bf16 bits,
             fp32 partial sums, one rounding) | "bf16_each" (uint16 buffers, every
             partial sum rounded to bf16 as it is formed)
@@ -17,7 +18,8 @@ import numpy as np
 
 from . import build as _build
 
-_SCHED = {"ring": 0, "hierarchical": 1, "rabenseifner": 2}
+_SCHED = {"ring": 0, "hierarchical": 1, "rabenseifner": 2, "recursive_doubling": 3, "tree": 4,
+          "double_tree": 5}
 _DTYPE = {"fp32": 0, "bf16": 1, "bf16_each": 2}
 _ELEM = {"fp32": 4, "bf16": 2, "bf16_each": 2}
 REDUCE, COPY = 0, 1

@@ -49,6 +49,9 @@
 #define ARO_RING 0
 #define ARO_HIER 1
 #define ARO_RABEN 2
+#define ARO_RDOUBLE 3
+#define ARO_TREE 4
+#define ARO_DTREE 5
 
 #define ARO_REDUCE 0
 #define ARO_COPY 1
@@ -229,6 +232,104 @@ static int build_raben(aro_list *L, int N, int64_t count) {
   return step;
 }
 
+/*
+ * Recursive doubling, [PRIMER] section 4.3 ("Trees: latency-optimal,
+ * bandwidth-poor", Figure 4.5) and [SCALING] "Tree AllReduce": in step k
+ * (k = 0..log2 N - 1) every rank exchanges its whole buffer with rank
+ * i xor 2^k and both add; after log2 N steps every rank holds the sum.
+ * N must be a power of two.
+ */
+static int build_rdouble(aro_list *L, int N, int64_t count) {
+  int lg = 0;
+  while ((1 << lg) < N) ++lg;
+  for (int k = 0; k < lg; ++k)
+    for (int i = 0; i < N; ++i)
+      if (push(L, k, i, i ^ (1 << k), 0, count, ARO_REDUCE, k == lg - 1)) return -1;
+  return lg;
+}
+
+/*
+ * Binary tree all-reduce, [SCALING] "Tree AllReduce": a reduce phase in
+ * which values climb to the root in log2 N steps, then a broadcast phase in
+ * which the root's result descends in log2 N steps; every message carries
+ * the whole buffer ([PRIMER] 4.3, Figure 4.7's table: "up to the root, then
+ * back down").  Reading: the binomial tree rooted at rank 0 -- in reduce
+ * step k the ranks whose index has bit k set and no lower bit send to
+ * i - 2^k, which adds; the broadcast runs the same edges in reverse, parent
+ * to child.  Works for any N (ceil(log2 N) steps each way).
+ */
+static int build_tree(aro_list *L, int N, int64_t count) {
+  int lg = 0;
+  while ((1 << lg) < N) ++lg;
+  int step = 0;
+  for (int k = 0; k < lg; ++k, ++step)
+    for (int i = 0; i < N; ++i)
+      if ((i & ((2 << k) - 1)) == (1 << k))
+        if (push(L, step, i, i - (1 << k), 0, count, ARO_REDUCE, k == lg - 1)) return -1;
+  for (int k = lg - 1; k >= 0; --k, ++step)
+    for (int i = 0; i < N; ++i)
+      if ((i & ((2 << k) - 1)) == 0 && i + (1 << k) < N)
+        if (push(L, step, i, i + (1 << k), 0, count, ARO_COPY, 0)) return -1;
+  return step;
+}
+
+/*
+ * Double binary tree, [SCALING] "Double binary tree" and [PRIMER] Figure
+ * 4.6: two trees, the second the mirror image of the first (node r becomes
+ * N-1-r), each reducing and broadcasting half of the buffer at the same
+ * time.  Tree 1 (read from Figure 4.6 for N = 8: 0 <- 4 <- {2, 6} <-
+ * {1, 3, 5, 7}): rank 0 is the root with the single child N/2; a node r > 0
+ * whose lowest set bit is b has children r - b/2 and r + b/2 when b > 1.
+ * N must be a power of two.  A node sends up in the round equal to its
+ * height (log2 b; the root's child N/2 in round log2 N - 1); the broadcast
+ * mirrors the rounds.  Messages are emitted by increasing sender rank, so a
+ * node that hears from two children in one round adds the lower-ranked
+ * child's part first: ((own + lower child) + higher child).
+ */
+static int tree1_parent(int r, int N) {
+  if (r == N / 2) return 0;
+  int b = r & -r;
+  return (r & (b << 1)) ? r - b : r + b;
+}
+
+static int tree1_height(int r, int N) { /* 0 for leaves; root's child: log2 N - 1 */
+  int b = r & -r, h = 0;
+  while ((1 << h) < b) ++h;
+  (void)N;
+  return h;
+}
+
+static int build_dtree(aro_list *L, int N, int64_t count) {
+  int lg = 0;
+  while ((1 << lg) < N) ++lg;
+  int64_t half = part_lo(count, 2, 1);
+  /* reduce rounds 0..lg-1, broadcast rounds lg..2lg-1 */
+  for (int round = 0; round < lg; ++round)
+    for (int s = 0; s < N; ++s)
+      for (int t = 0; t < 2; ++t) {
+        /* in tree 2 the sender s plays the part of node N-1-s of tree 1 */
+        int node = t == 0 ? s : N - 1 - s;
+        if (node == 0 || tree1_height(node, N) != round) continue;
+        int par = tree1_parent(node, N);
+        int dst = t == 0 ? par : N - 1 - par;
+        int64_t lo = t == 0 ? 0 : half, hi = t == 0 ? half : count;
+        if (push(L, round, s, dst, lo, hi, ARO_REDUCE, round == lg - 1)) return -1;
+      }
+  for (int round = 0; round < lg; ++round)
+    for (int s = 0; s < N; ++s)
+      for (int t = 0; t < 2; ++t) {
+        /* the parent sends down in the mirror of the round its child sent up */
+        int node = t == 0 ? s : N - 1 - s;
+        for (int c = 1; c < N; ++c) {
+          if (tree1_parent(c, N) != node || tree1_height(c, N) != lg - 1 - round) continue;
+          int dst = t == 0 ? c : N - 1 - c;
+          int64_t lo = t == 0 ? 0 : half, hi = t == 0 ? half : count;
+          if (push(L, lg + round, s, dst, lo, hi, ARO_COPY, 0)) return -1;
+        }
+      }
+  return 2 * lg;
+}
+
 static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 
 /* Validates arguments and builds the message list.  0 on success. */
@@ -250,6 +351,13 @@ static int build(aro_list *L, int N, int G, int64_t count, int schedule) {
     if (!is_pow2(N)) return -2;
     if (G < 1 || N % G) return -1;
     end = build_raben(L, N, count);
+  } else if (schedule == ARO_RDOUBLE || schedule == ARO_DTREE) {
+    if (!is_pow2(N)) return -2;
+    if (G < 1 || N % G) return -1;
+    end = schedule == ARO_RDOUBLE ? build_rdouble(L, N, count) : build_dtree(L, N, count);
+  } else if (schedule == ARO_TREE) {
+    if (G < 1 || N % G) return -1;
+    end = build_tree(L, N, count);
   } else {
     return -1;
   }

@@ -9,6 +9,9 @@ are only practical for tiny inputs.
                 (ranks mod N; the chunk is first sent by rank c at
                 reduce-scatter step 0)
   rabenseifner  the balanced pairwise tree over ranks in index order
+  recursive_doubling  the same balanced tree (each pair's sum is commutative)
+  tree          binomial tree to rank 0 (left-complete for N not 2^k)
+  double_tree   half 0 by tree 1, half 1 by its mirror (see dtree_fold)
   hierarchical  group partial of slice k: ((x_{g,k+1} + x_{g,k+2}) + ...) + x_{g,k};
                 then, for sub-chunk j of the slice, a ring fold over groups
                 starting at group j
@@ -47,6 +50,37 @@ def tree_fold(vals, add=add32):
     return level[0]
 
 
+def binomial_fold(vals, add=add32):
+    """Binomial tree to rank 0: blocks of 2^k ranks merge pairwise; a block
+    without a right neighbour is carried up unchanged (any N)."""
+    level = [np.float32(v) for v in vals]
+    while len(level) > 1:
+        nxt = []
+        for m in range(0, len(level), 2):
+            nxt.append(add(level[m], level[m + 1]) if m + 1 < len(level) else level[m])
+        level = nxt
+    return level[0]
+
+
+def dtree_fold(vals, half, add=add32):
+    """Double binary tree (N = 2^L): half 0 climbs tree 1, rooted at 0 with
+    the single child N/2; half 1 climbs its mirror, rooted at N-1 with the
+    child N/2 - 1.  A node c whose subtree spans 2b-1 ranks adds its own
+    value, then its lower child's (c - b/2), then its higher child's (c + b/2)."""
+    n = len(vals)
+
+    def sub(c, b):
+        if b == 1:
+            return np.float32(vals[c])
+        return add(add(vals[c], sub(c - b // 2, b // 2)), sub(c + b // 2, b // 2))
+
+    if n == 1:
+        return np.float32(vals[0])
+    if half == 0:
+        return add(vals[0], sub(n // 2, n // 2))
+    return add(vals[n - 1], sub(n // 2 - 1, n // 2))
+
+
 def expected_fp32(xs, schedule, group_size=1, add=add32):
     """xs: list of N float32 arrays.  Returns the float32 result array."""
     n = len(xs)
@@ -59,8 +93,12 @@ def expected_fp32(xs, schedule, group_size=1, add=add32):
         elif schedule == "ring":
             c, _ = chunk_of(e, count, n)
             out[e] = ring_fold(col, c, add)
-        elif schedule == "rabenseifner":
+        elif schedule in ("rabenseifner", "recursive_doubling"):
             out[e] = tree_fold(col, add)
+        elif schedule == "tree":
+            out[e] = binomial_fold(col, add)
+        elif schedule == "double_tree":
+            out[e] = dtree_fold(col, 0 if e < count // 2 else 1, add)
         elif schedule == "hierarchical":
             g_sz = group_size
             m_groups = n // g_sz

@@ -18,7 +18,10 @@ from tests import folds
 
 CASES = [("ring", n, 1) for n in (1, 2, 3, 4)] + \
         [("hierarchical", n, g) for n, g in ((2, 1), (2, 2), (4, 2), (4, 1), (4, 4), (6, 3), (6, 2))] + \
-        [("rabenseifner", n, 1) for n in (1, 2, 4, 8)]
+        [("rabenseifner", n, 1) for n in (1, 2, 4, 8)] + \
+        [("recursive_doubling", n, 1) for n in (1, 2, 4, 8)] + \
+        [("tree", n, 1) for n in (1, 2, 3, 4, 5, 7, 8)] + \
+        [("double_tree", n, 1) for n in (1, 2, 4, 8, 16)]
 
 
 @pytest.mark.parametrize("schedule,n,g", CASES)
@@ -71,6 +74,15 @@ def test_bf16_each_loses_what_once_keeps():
     assert folds.widen(each[0])[0] == np.float32(1.0)
 
 
+def test_recursive_doubling_equals_rabenseifner_bits():
+    """Both sum every element by the balanced pairwise tree in rank order."""
+    xs = workloads.normal_inputs(16, 5000, seed=9)
+    a = oracle.run([x.copy() for x in xs], "fp32", "recursive_doubling")
+    b = oracle.run([x.copy() for x in xs], "fp32", "rabenseifner")
+    for r in range(16):
+        np.testing.assert_array_equal(a[r].view(np.uint32), b[r].view(np.uint32))
+
+
 def test_orders_really_differ():
     """The three schedules fold in different orders, so their low bits differ
     on generic data (Scaling ML systems ch. 06: reproducibility needs a fixed
@@ -88,7 +100,8 @@ def test_orders_really_differ():
 
 @pytest.mark.parametrize("schedule,n,g", [("ring", 5, 1), ("ring", 16, 8), ("hierarchical", 16, 8),
                                           ("hierarchical", 12, 3), ("rabenseifner", 16, 1),
-                                          ("rabenseifner", 64, 1), ("ring", 64, 8)])
+                                          ("rabenseifner", 64, 1), ("ring", 64, 8), ("tree", 13, 1),
+                                          ("tree", 64, 1), ("recursive_doubling", 32, 1), ("double_tree", 64, 1)])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
 def test_integer_inputs_give_exact_sum(schedule, n, g, dtype):
     count = 1000 + n

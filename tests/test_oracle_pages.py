@@ -303,3 +303,73 @@ def test_latency_terms_for_1024_gpus():
     t = oracle.cost(1024, 0, 4, "ring", 22e-6, 50e9, 50e9)
     assert t == pytest.approx(2046 * 22e-6, rel=1e-12) and round(t * 1e3) == 45
     assert oracle.steps(1024, "ring") == 2046 and oracle.steps(1024, "rabenseifner") == 20
+
+
+
+def test_double_tree_structure_n8():
+    """Primer ch. 4, Figure 4.6: the reduce messages of the double binary
+    tree follow the two printed trees; tree 1 carries the first half of the
+    buffer and tree 2 (the mirror) the second; every node forwards in at most
+    one tree."""
+    m = oracle.messages(8, 64, "double_tree")
+    up = m["kind"] == oracle.REDUCE
+    got = {(1 if m["lo"][j] == 0 else 2, int(m["src"][j]), int(m["dst"][j])) for j in np.flatnonzero(up)}
+    want = {tuple(int(v) for v in row) for row in _rows("double_tree_n8.txt")}
+    assert got == want
+    inner1 = {p for t, c, p in want if t == 1}
+    inner2 = {p for t, c, p in want if t == 2}
+    assert inner1 == {0, 2, 4, 6} and inner2 == {1, 3, 5, 7}
+    assert oracle.steps(8, "double_tree") == 6
+
+
+def test_tree_and_doubling_steps_and_bytes():
+    """Scaling ML systems ch. 06 "Tree AllReduce": log2 N steps up and log2 N
+    down, each carrying the whole message; Primer Figure 4.5: recursive
+    doubling sends the whole buffer in each of its log2 N steps (3S for 8
+    ranks), against 7S/8 for the halving reduce-scatter."""
+    S = 8 * 1024
+    assert oracle.steps(64, "tree") == 12 and oracle.steps(8, "recursive_doubling") == 3
+    sent, _, _ = oracle.stats(8, S, "fp32", "recursive_doubling")
+    assert all(int(b) == 3 * S * 4 for b in sent)
+    m = oracle.messages(64, S, "tree")
+    assert np.all(m["hi"] - m["lo"] == S)
+    with pytest.raises(oracle.OracleError):
+        oracle.steps(12, "recursive_doubling")
+
+
+def test_tree_and_doubling_times_printed_on_pages():
+    """Scaling ML systems ch. 06, "Ring-tree crossover" example: 1 MB on 64
+    GPUs, alpha = 10 us, beta = 10 GB/s: ring 1456.9 us, tree 1320 us.
+    Primer ch. 4, "Two worked examples": 1 MB on 8 GPUs at 450 GB/s with
+    alpha = 5 us: ring about 74 us, doubling tree about 22 us; Panel 4.3:
+    1 MB on 1,024 GPUs at 50 GB/s, alpha = 22 us: the tree about 0.4 ms."""
+    mb = 1_000_000
+    assert oracle.cost(64, mb // 4, 4, "ring", 10e-6, 10e9, 10e9) * 1e6 == pytest.approx(1456.9, abs=0.05)
+    assert oracle.cost(64, mb // 4, 4, "tree", 10e-6, 10e9, 10e9) * 1e6 == pytest.approx(1320.0, rel=1e-9)
+    assert round(oracle.cost(8, mb // 4, 4, "ring", 5e-6, 450e9, 450e9) * 1e6) == 74
+    assert round(oracle.cost(8, mb // 4, 4, "recursive_doubling", 5e-6, 450e9, 450e9) * 1e6) == 22
+    assert round(oracle.cost(1024, mb // 4, 4, "recursive_doubling", 22e-6, 50e9, 50e9) * 1e3, 1) == 0.4
+
+
+def _crossover(n, sched_a, sched_b, alpha, bw, lo=1e3, hi=1e12):
+    """Message size (bytes, multiple of 4 n) where the two modelled times meet."""
+    f = lambda size: (oracle.cost(n, int(size) // 4, 4, sched_a, alpha, bw, bw)
+                      - oracle.cost(n, int(size) // 4, 4, sched_b, alpha, bw, bw))
+    for _ in range(80):
+        mid = (lo * hi) ** 0.5
+        if (f(mid) > 0) == (f(lo) > 0):
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def test_crossovers_printed_on_pages():
+    """Primer ch. 4 Figure 4.7: for N = 128, alpha = 22 us, 400 Gb/s the ring
+    and doubling curves cross at S* of about 54 MB; Scaling ML systems ch. 06:
+    for alpha = 5 us, beta = 50 GB/s, N = 100 the ring-tree crossover is
+    about 3.8 MB (the page's approximation N alpha beta / log2 N)."""
+    s = _crossover(128, "ring", "recursive_doubling", 22e-6, 50e9)
+    assert s / 1e6 == pytest.approx(54.2, rel=0.01)
+    s = _crossover(100, "ring", "tree", 5e-6, 50e9)
+    assert s / 1e6 == pytest.approx(3.8, rel=0.02)
