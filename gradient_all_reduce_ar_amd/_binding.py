@@ -16,17 +16,18 @@ LIB_PATH = os.path.join(_HERE, "libar.so")
 
 AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP = range(5)
 AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP = 0, 1, 2
-AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER = 0, 1, 2
+AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER, AR_RECURSIVE_DOUBLING, AR_TREE, AR_DOUBLE_TREE = range(6)
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
 AR_MAX_RANKS = 64
 AR_MAX_PLAN_RANKS = 1024
 
 DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP}
-SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER}
+SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER,
+             "recursive_doubling": AR_RECURSIVE_DOUBLING, "tree": AR_TREE, "double_tree": AR_DOUBLE_TREE}
 EXECS = {"steps": AR_EXEC_STEPS, "steps_unfused": AR_EXEC_STEPS_UNFUSED, "onepass": AR_EXEC_ONEPASS}
 
 # kernel kind codes reported by ar_plan_launch_info
-KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE = 0x100, 0x200, 0x300, 0x400, 0x500
+KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE, KIND_DTREE = 0x100, 0x200, 0x300, 0x400, 0x500, 0x600
 LOC_SCRATCH = 1000
 
 

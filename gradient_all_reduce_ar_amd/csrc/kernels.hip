@@ -440,53 +440,135 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
   }
 }
 
-// Rabenseifner: the balanced pairwise tree over ranks in index order, formed
-// batch by batch (8 ranks at a time) and merged like a binary counter.
-template <bool BF, bool EACH, int N, int UNROLL>
+// Tree fold over ranks in index order: blocks of 2^k ranks merge pairwise,
+// a block without a right neighbour (ranks >= N) is carried up unchanged.
+// For N = 2^L this is the balanced tree of Rabenseifner and recursive
+// doubling; otherwise it is the binomial tree's left-complete order.  Formed
+// batch by batch (8 ranks at a time); NMAX = N rounded up to a power of two.
+template <bool BF, bool EACH, int NMAX, int UNROLL>
 __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
-  constexpr int kB = N < 8 ? N : 8;
-  constexpr int kBatches = N / kB;
+  constexpr int kB = NMAX < 8 ? NMAX : 8;
+  constexpr int kBatches = NMAX / kB;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const int n = args.nranks;
   const BlockCoord bc = block_coord(args);
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
     const int64_t base = t * kTile;
     if (base >= op.lo && base + kTile <= op.hi) {
-      // each batch is an aligned block of kB ranks, so the tree over batch
-      // results in index order completes the balanced tree over all N ranks
       float4 res[kBatches][UNROLL];
 #pragma unroll
       for (int bi = 0; bi < kBatches; ++bi) {
+        if (bi * kB >= n) continue;
         float4 v[kB][UNROLL];
 #pragma unroll
-        for (int i = 0; i < kB; ++i) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
+        for (int i = 0; i < kB; ++i)
+          if (bi * kB + i < n) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
 #pragma unroll
-        for (int w = kB; w > 1; w /= 2)
+        for (int w = kB, span = 1; w > 1; w /= 2, span *= 2)
 #pragma unroll
           for (int i = 0; i < w / 2; ++i)
+            if (bi * kB + (2 * i + 1) * span < n) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) v[i][u] = fold4<EACH>(v[2 * i][u], v[2 * i + 1][u]);
+              for (int u = 0; u < UNROLL; ++u) v[i][u] = fold4<EACH>(v[2 * i][u], v[2 * i + 1][u]);
+            } else if (i > 0) {
+#pragma unroll
+              for (int u = 0; u < UNROLL; ++u) v[i][u] = v[2 * i][u];
+            }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
       }
 #pragma unroll
-      for (int w = kBatches; w > 1; w /= 2)
+      for (int w = kBatches, span = kB; w > 1; w /= 2, span *= 2)
 #pragma unroll
         for (int i = 0; i < w / 2; ++i)
+          if ((2 * i + 1) * span < n) {
 #pragma unroll
-          for (int u = 0; u < UNROLL; ++u) res[i][u] = fold4<EACH>(res[2 * i][u], res[2 * i + 1][u]);
+            for (int u = 0; u < UNROLL; ++u) res[i][u] = fold4<EACH>(res[2 * i][u], res[2 * i + 1][u]);
+          } else if (i > 0 && 2 * i * span < n) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) res[i][u] = res[2 * i][u];
+          }
       store_all<BF, UNROLL>(args, base, res[0]);
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
           const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
-          float level[N];
-          for (int r = 0; r < N; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
-          for (int w = N; w > 1; w /= 2)
-            for (int i = 0; i < w / 2; ++i) level[i] = fold1(EACH, level[2 * i], level[2 * i + 1]);
+          float level[NMAX];
+          for (int r = 0; r < n; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
+          for (int w = NMAX, span = 1; w > 1; w /= 2, span *= 2)
+            for (int i = 0; i < w / 2; ++i)
+              if ((2 * i + 1) * span < n) level[i] = fold1(EACH, level[2 * i], level[2 * i + 1]);
+              else if (2 * i * span < n) level[i] = level[2 * i];
           store_all1(args, BF, e, level[0]);
+        }
+    }
+  }
+}
+
+// Double binary tree, one half per op (aux = 0: tree 1, 1: its mirror).
+// D(c, b) = (x_c + D(c - b/2, b/2)) + D(c + b/2, b/2), D(c, 1) = x_c; tree 1
+// gives x_0 + D(N/2, N/2), tree 2 gives x_{N-1} + D(N/2 - 1, N/2).
+template <bool BF, bool EACH, int UNROLL, int C, int B>
+struct DTreeFold {
+  static __device__ __forceinline__ void run(const KArgs &args, int64_t base, float4 (&out)[UNROLL]) {
+    load_units<BF, UNROLL>(args, C, base, out);
+    if constexpr (B > 1) {
+      float4 lo[UNROLL], hi[UNROLL];
+      DTreeFold<BF, EACH, UNROLL, C - B / 2, B / 2>::run(args, base, lo);
+      DTreeFold<BF, EACH, UNROLL, C + B / 2, B / 2>::run(args, base, hi);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) out[u] = fold4<EACH>(fold4<EACH>(out[u], lo[u]), hi[u]);
+    }
+  }
+  static __device__ __forceinline__ float run1(const KArgs &args, int64_t e) {
+    const float own = load1<BF>(static_cast<const char *>(args.rank[C]), e);
+    if constexpr (B == 1) {
+      return own;
+    } else {
+      const float lo = DTreeFold<BF, EACH, UNROLL, C - B / 2, B / 2>::run1(args, e);
+      const float hi = DTreeFold<BF, EACH, UNROLL, C + B / 2, B / 2>::run1(args, e);
+      return fold1(EACH, fold1(EACH, own, lo), hi);
+    }
+  }
+};
+
+template <bool BF, bool EACH, int N, int UNROLL>
+__global__ __launch_bounds__(kBlock) void onepass_dtree(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  const BlockCoord bc = block_coord(args);
+  const DevOp op = args.ops[bc.op];
+  const bool second = op.aux != 0;
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      float4 root[UNROLL], sub[UNROLL];
+      if (!second) {
+        load_units<BF, UNROLL>(args, 0, base, root);
+        DTreeFold<BF, EACH, UNROLL, N / 2, N / 2>::run(args, base, sub);
+      } else {
+        load_units<BF, UNROLL>(args, N - 1, base, root);
+        DTreeFold<BF, EACH, UNROLL, N / 2 - 1, N / 2>::run(args, base, sub);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) root[u] = fold4<EACH>(root[u], sub[u]);
+      store_all<BF, UNROLL>(args, base, root);
+    } else {
+      for (int u = 0; u < UNROLL; ++u)
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          float v;
+          if (!second)
+            v = fold1(EACH, load1<BF>(static_cast<const char *>(args.rank[0]), e),
+                      DTreeFold<BF, EACH, UNROLL, N / 2, N / 2>::run1(args, e));
+          else
+            v = fold1(EACH, load1<BF>(static_cast<const char *>(args.rank[N - 1]), e),
+                      DTreeFold<BF, EACH, UNROLL, N / 2 - 1, N / 2>::run1(args, e));
+          store_all1(args, BF, e, v);
         }
     }
   }
@@ -533,13 +615,26 @@ hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
 template <bool BF, bool EACH>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
+  if (n <= 2) hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a);
+  else if (n <= 4) hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a);
+  else if (n <= 8) hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a);
+  else if (n <= 16) hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a);
+  else if (n <= 32) hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a);
+  else if (n <= 64) hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <bool BF, bool EACH>
+hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
+  constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
   switch (n) {
-    case 2: hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -614,6 +709,10 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
       if ((kind & 3) == 2) return launch_tree<true, true>(a.nranks, grid, a, s);
       if ((kind & 3) == 1) return launch_tree<true, false>(a.nranks, grid, a, s);
       return launch_tree<false, false>(a.nranks, grid, a, s);
+    case kKindDTree:
+      if ((kind & 3) == 2) return launch_dtree<true, true>(a.nranks, grid, a, s);
+      if ((kind & 3) == 1) return launch_dtree<true, false>(a.nranks, grid, a, s);
+      return launch_dtree<false, false>(a.nranks, grid, a, s);
   }
   return hipErrorInvalidValue;
 }

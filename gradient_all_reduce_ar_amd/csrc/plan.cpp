@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <map>
+#include <tuple>
 
 namespace ar {
 
@@ -133,19 +134,101 @@ int build_raben(std::vector<Transfer> &out, int n, int64_t count) {
   return 2 * levels;
 }
 
+// Recursive doubling ([PRIMER] 4.3, Figure 4.5): in step k every rank and its
+// partner i ^ 2^k exchange whole buffers and both add.  N = 2^L.
+int build_rdouble(std::vector<Transfer> &out, int n, int64_t count) {
+  int levels = 0;
+  while ((1 << levels) < n) ++levels;
+  for (int k = 0; k < levels; ++k)
+    for (int i = 0; i < n; ++i) out.push_back({k, i, i ^ (1 << k), 0, count, kReduce, k + 1 == levels});
+  return levels;
+}
+
+// Binary tree ([SCALING] "Tree AllReduce"): whole-buffer reduce up a
+// binomial tree rooted at rank 0 (in step k, rank r = m * 2^(k+1) receives
+// from r + 2^k), then the broadcast down the same edges in reverse.
+int build_tree(std::vector<Transfer> &out, int n, int64_t count) {
+  int levels = 0;
+  while ((1 << levels) < n) ++levels;
+  int step = 0;
+  for (int k = 0; k < levels; ++k, ++step)
+    for (int r = 0; r + (1 << k) < n; r += 2 << k)
+      out.push_back({step, r + (1 << k), r, 0, count, kReduce, k + 1 == levels});
+  for (int k = levels - 1; k >= 0; --k, ++step)
+    for (int r = 0; r + (1 << k) < n; r += 2 << k) out.push_back({step, r, r + (1 << k), 0, count, kCopy, false});
+  return step;
+}
+
+// Double binary tree ([SCALING] "Double binary tree", [PRIMER] Figure 4.6):
+// tree 1 roots at rank 0, whose only child is N/2; the subtree of a node c
+// spanning 2b - 1 ranks has the children c - b/2 and c + b/2.  Tree 2 is its
+// mirror (rank r plays node N-1-r).  Tree 1 reduces and broadcasts the first
+// half of the buffer, tree 2 the second, in the same rounds: a node sends up
+// in the round equal to its height and hears from its parent in the mirror
+// round.  Children are listed lower rank first, so a node with two children
+// adds ((own + lower) + higher).  N = 2^L.
+int build_dtree(std::vector<Transfer> &out, int n, int64_t count) {
+  int levels = 0;
+  while ((1 << levels) < n) ++levels;
+  if (n < 2) return 0;
+  std::vector<int> parent(n, -1), height(n, 0);
+  // walk tree 1 from the root's child down; height of a span-(2b-1) node = log2 b
+  std::vector<std::pair<int, int>> stack{{n / 2, n / 2}};
+  parent[n / 2] = 0;
+  while (!stack.empty()) {
+    const auto [c, b] = stack.back();
+    stack.pop_back();
+    int h = 0;
+    while ((1 << h) < b) ++h;
+    height[c] = h;
+    if (b > 1)
+      for (int child : {c - b / 2, c + b / 2}) {
+        parent[child] = c;
+        stack.push_back({child, b / 2});
+      }
+  }
+  const Cut halves{0, count, 2};
+  for (int round = 0; round < levels; ++round)
+    for (int tree = 0; tree < 2; ++tree)
+      for (int c = 1; c < n; ++c)  // tree-1 node ids, ascending
+        if (height[c] == round) {
+          const int src = tree == 0 ? c : n - 1 - c, dst = tree == 0 ? parent[c] : n - 1 - parent[c];
+          out.push_back({round, src, dst, halves.lo(tree), halves.hi(tree), kReduce, round + 1 == levels});
+        }
+  // children of a tree-2 node come in descending tree-1 id order; reorder the
+  // round's tree-2 reduces so each receiver hears its lower-ranked child first
+  for (auto it = out.begin(); it != out.end();) {
+    auto end = it;
+    while (end != out.end() && end->step == it->step) ++end;
+    std::stable_sort(it, end, [](const Transfer &a, const Transfer &b) {
+      return a.lo != b.lo ? a.lo < b.lo : a.src < b.src;
+    });
+    it = end;
+  }
+  for (int round = 0; round < levels; ++round)
+    for (int tree = 0; tree < 2; ++tree)
+      for (int c = 1; c < n; ++c)
+        if (height[c] == levels - 1 - round) {
+          const int dst = tree == 0 ? c : n - 1 - c, src = tree == 0 ? parent[c] : n - 1 - parent[c];
+          out.push_back({levels + round, src, dst, halves.lo(tree), halves.hi(tree), kCopy, false});
+        }
+  return 2 * levels;
+}
+
 // Scratch slot holding rank r's fp32 partial sums.  Two ranks share a slot
 // only when their partial ranges can never overlap while both are live:
 //   ring: one live partial per chunk (it travels round the ring) -> 1 slot;
 //   hierarchical: per group, partials of distinct slices           -> M slots;
 //   Rabenseifner: ranks 2m and 2m+1 keep disjoint halves from round 1 on
-//                 and later ranges nest inside those halves         -> N/2 slots.
+//                 and later ranges nest inside those halves         -> N/2 slots;
+//   recursive doubling and the trees: one slot per rank              -> N slots.
 int slot_of(const Plan &p, int r) {
   switch (p.sched) {
     case kRing: return 0;
     case kHier: return (p.group_size == 1 || p.group_size == p.nranks) ? 0 : r / p.group_size;
     case kRaben: return r >> 1;
+    default: return r;  // doubling and trees: every rank's partial covers a whole buffer or half
   }
-  return 0;
 }
 
 // Per-rank record of the element ranges whose current value is an fp32
@@ -175,55 +258,102 @@ std::string lower_steps(Plan &p, bool fuse) {
   while (j < p.xfers.size()) {
     size_t j1 = j;
     while (j1 < p.xfers.size() && p.xfers[j1].step == p.xfers[j].step) ++j1;
-    // split the round by (kind, operand types, completion) so each launch is
-    // uniform; key bit 16 marks reduces that complete their range
-    std::map<int32_t, Launch> by_kind;
-    std::vector<size_t> to_mark;
-    for (size_t t = j; t < j1; ++t) {
-      const Transfer &x = p.xfers[t];
-      if (x.hi <= x.lo) continue;
-      Op op{x.lo, x.hi, kLocNone, kLocNone, kLocNone, kLocNone, 0};
-      int32_t kind;
-      if (x.kind == kCopy) {
-        kind = kKCopy | static_cast<int32_t>(elem_bytes(p.dtype));
-        op.a = x.src;
-        op.o = x.dst;
-      } else if (!bf) {
-        // fp32, or bf16 rounded at every add: the rank buffers hold the
-        // partial sums themselves
-        kind = kKReduce | (p.dtype == kBF16Each ? (kFlagABf | kFlagBBf | kFlagOBf) : 0);
-        op.a = x.src;
-        op.b = x.dst;
-        op.o = x.dst;
-      } else {
-        const int sa = partial.state(x.src, x.lo, x.hi), sb = partial.state(x.dst, x.lo, x.hi);
-        if (sa < 0 || sb < 0) return "internal: reduce over a range that is partly partial";
-        kind = kKReduce;
-        op.a = sa ? kLocScratch + slot_of(p, x.src) : x.src;
-        op.b = sb ? kLocScratch + slot_of(p, x.dst) : x.dst;
-        if (!sa) kind |= kFlagABf;
-        if (!sb) kind |= kFlagBBf;
-        if (sa) max_slot = std::max(max_slot, slot_of(p, x.src));
-        if (sb) max_slot = std::max(max_slot, slot_of(p, x.dst));
-        if (x.final_sum) {
-          kind |= kFlagOBf;
-          op.o = x.dst;
-        } else {
-          op.o = kLocScratch + slot_of(p, x.dst);
-          max_slot = std::max(max_slot, slot_of(p, x.dst));
-          to_mark.push_back(t);
+    // Reduces that exchange the same range in both directions (recursive
+    // doubling) become one op writing the sum to both ranks (a + b == b + a
+    // bit for bit); the k-th reduce into the same receiver range runs in the
+    // round's k-th sub-launch, so a node hearing from two children adds them
+    // in order.  Every sub-launch reads only what earlier rounds wrote, or its
+    // own receiver's accumulating sum.
+    std::vector<size_t> items;
+    for (size_t t = j; t < j1; ++t)
+      if (p.xfers[t].hi > p.xfers[t].lo) items.push_back(t);
+    std::vector<long> partner(items.size(), -1);
+    for (size_t u = 0; u < items.size(); ++u) {
+      const Transfer &x = p.xfers[items[u]];
+      if (x.kind != kReduce || partner[u] >= 0) continue;
+      for (size_t v = u + 1; v < items.size(); ++v) {
+        const Transfer &y = p.xfers[items[v]];
+        if (y.kind == kReduce && partner[v] < 0 && y.src == x.dst && y.dst == x.src && y.lo == x.lo && y.hi == x.hi) {
+          partner[u] = static_cast<long>(v);
+          partner[v] = static_cast<long>(u);
+          break;
         }
       }
-      const int32_t key = kind | ((x.kind == kReduce && x.final_sum) ? 0x10000 : 0);
-      Launch &L = by_kind[key];
-      L.kind = kind;
-      L.ops.push_back(op);
     }
-    // partial sums written this round become visible to the next round
-    for (size_t t : to_mark) partial.mark(p.xfers[t].dst, p.xfers[t].lo, p.xfers[t].hi);
-    for (auto &kv : by_kind) {
-      finals.push_back((kv.first & 0x10000) != 0);
-      p.launches.push_back(std::move(kv.second));
+    std::map<std::tuple<int, int64_t, int64_t>, int> heard;  // (receiver, range) -> reduces so far
+    std::vector<int> sub(items.size(), 0);
+    int nsub = 1;
+    for (size_t u = 0; u < items.size(); ++u) {
+      const Transfer &x = p.xfers[items[u]];
+      if (x.kind != kReduce || (partner[u] >= 0 && partner[u] < static_cast<long>(u))) continue;
+      int &cnt = heard[{x.dst, x.lo, x.hi}];
+      sub[u] = cnt++;
+      if (partner[u] >= 0) heard[{x.src, x.lo, x.hi}]++;
+      nsub = std::max(nsub, sub[u] + 1);
+    }
+    for (int sr = 0; sr < nsub; ++sr) {
+      // split by (kind, operand types, completion) so each launch is uniform;
+      // key bit 16 marks reduces that complete their range
+      std::map<int32_t, Launch> by_kind;
+      std::vector<std::pair<int, std::pair<int64_t, int64_t>>> to_mark;
+      for (size_t u = 0; u < items.size(); ++u) {
+        if (sub[u] != sr || (partner[u] >= 0 && partner[u] < static_cast<long>(u))) continue;
+        const Transfer &x = p.xfers[items[u]];
+        const bool pair = partner[u] >= 0;
+        Op op{x.lo, x.hi, kLocNone, kLocNone, kLocNone, kLocNone, 0};
+        int32_t kind;
+        if (x.kind == kCopy) {
+          kind = kKCopy | static_cast<int32_t>(elem_bytes(p.dtype));
+          op.a = x.src;
+          op.o = x.dst;
+        } else if (!bf) {
+          // fp32, or bf16 rounded at every add: the rank buffers hold the
+          // partial sums themselves
+          kind = kKReduce | (p.dtype == kBF16Each ? (kFlagABf | kFlagBBf | kFlagOBf) : 0);
+          op.a = x.src;
+          op.b = x.dst;
+          op.o = x.dst;
+          if (pair) {
+            op.o2 = x.src;
+            kind |= kFlagO2;
+          }
+        } else {
+          const int sa = partial.state(x.src, x.lo, x.hi), sb = partial.state(x.dst, x.lo, x.hi);
+          if (sa < 0 || sb < 0) return "internal: reduce over a range that is partly partial";
+          kind = kKReduce;
+          op.a = sa ? kLocScratch + slot_of(p, x.src) : x.src;
+          op.b = sb ? kLocScratch + slot_of(p, x.dst) : x.dst;
+          if (!sa) kind |= kFlagABf;
+          if (!sb) kind |= kFlagBBf;
+          if (sa) max_slot = std::max(max_slot, slot_of(p, x.src));
+          if (sb) max_slot = std::max(max_slot, slot_of(p, x.dst));
+          if (x.final_sum) {
+            kind |= kFlagOBf;
+            op.o = x.dst;
+            if (pair) op.o2 = x.src;
+          } else {
+            op.o = kLocScratch + slot_of(p, x.dst);
+            max_slot = std::max(max_slot, slot_of(p, x.dst));
+            to_mark.push_back({x.dst, {x.lo, x.hi}});
+            if (pair) {
+              op.o2 = kLocScratch + slot_of(p, x.src);
+              max_slot = std::max(max_slot, slot_of(p, x.src));
+              to_mark.push_back({x.src, {x.lo, x.hi}});
+            }
+          }
+          if (pair) kind |= kFlagO2;
+        }
+        const int32_t key = kind | ((x.kind == kReduce && x.final_sum) ? 0x10000 : 0);
+        Launch &L = by_kind[key];
+        L.kind = kind;
+        L.ops.push_back(op);
+      }
+      // partial sums written by this sub-launch are visible to the next one
+      for (const auto &m : to_mark) partial.mark(m.first, m.second.first, m.second.second);
+      for (auto &kv : by_kind) {
+        finals.push_back((kv.first & 0x10000) != 0 && !(kv.second.kind & kFlagO2));
+        p.launches.push_back(std::move(kv.second));
+      }
     }
     j = j1;
   }
@@ -292,9 +422,19 @@ std::string lower_onepass(Plan &p) {
                            ((k + 1) % G) | (jj << 8)});
     }
     p.launches.push_back(std::move(L));
+  } else if (p.sched == kDTree) {
+    // half h follows tree h: tree 1 = x_0 + D(N/2, N/2), tree 2 = x_{N-1} +
+    // D(N/2 - 1, N/2), D(c, b) = (x_c + D(c - b/2, b/2)) + D(c + b/2, b/2)
+    Launch L{kKDTree | dt, {}};
+    const Cut halves{0, p.count, 2};
+    for (int h = 0; h < 2; ++h)
+      if (halves.hi(h) > halves.lo(h))
+        L.ops.push_back({halves.lo(h), halves.hi(h), kLocNone, kLocNone, kLocNone, kLocNone, h});
+    p.launches.push_back(std::move(L));
   } else {
-    // balanced pairwise tree over ranks in index order, the same for every
-    // element: ((x0 + x1) + (x2 + x3)) + ...
+    // Rabenseifner and recursive doubling: the balanced pairwise tree over
+    // ranks in index order, ((x0 + x1) + (x2 + x3)) + ...; the binomial tree
+    // gives the same when N is 2^k and a left-complete tree otherwise
     Launch L{kKTree | dt, {}};
     L.ops.push_back({0, p.count, kLocNone, kLocNone, kLocNone, kLocNone, 0});
     p.launches.push_back(std::move(L));
@@ -363,11 +503,11 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
   if (count < 0) return "count must be >= 0";
   if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each) return "unknown dtype";
-  if (sched != kRing && sched != kHier && sched != kRaben) return "unknown schedule";
+  if (sched < kRing || sched > kDTree) return "unknown schedule";
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
-  if (sched == kRaben && (nranks & (nranks - 1))) {
+  if ((sched == kRaben || sched == kRDouble || sched == kDTree) && (nranks & (nranks - 1))) {
     *unsupported = true;
-    return "Rabenseifner needs a power-of-two number of ranks";
+    return "this schedule needs a power-of-two number of ranks";
   }
   p = Plan{};
   p.nranks = nranks;
@@ -377,7 +517,10 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   p.sched = sched;
   if (sched == kRing) p.nsteps = build_ring(p.xfers, nranks, count);
   else if (sched == kHier) p.nsteps = build_hier(p.xfers, nranks, group_size, count);
-  else p.nsteps = build_raben(p.xfers, nranks, count);
+  else if (sched == kRaben) p.nsteps = build_raben(p.xfers, nranks, count);
+  else if (sched == kRDouble) p.nsteps = build_rdouble(p.xfers, nranks, count);
+  else if (sched == kTree) p.nsteps = build_tree(p.xfers, nranks, count);
+  else p.nsteps = build_dtree(p.xfers, nranks, count);
   std::stable_sort(p.xfers.begin(), p.xfers.end(),
                    [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
   return lower(p, exec);

@@ -16,7 +16,7 @@ namespace ar {
 // kBF16: fp32 partial sums, one rounding per element; kBF16Each: every
 // partial sum rounded to bf16 as it is formed (bf16 on the wire).
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kBF16Each = 2 };
-enum Sched : int32_t { kRing = 0, kHier = 1, kRaben = 2 };
+enum Sched : int32_t { kRing = 0, kHier = 1, kRaben = 2, kRDouble = 3, kTree = 4, kDTree = 5 };
 enum Exec : int32_t { kSteps = 0, kStepsUnfused = 1, kOnePass = 2 };
 enum XferKind : int32_t { kReduce = 0, kCopy = 1 };
 
@@ -39,13 +39,16 @@ constexpr int32_t kLocScratch = 1000;  // 1000 + s: fp32 scratch slot s
 //   kKReduce | flags: out = A + B (fp32 add), written to o and optionally o2.
 //     flag 1: A is bf16, 2: B is bf16, 4: outputs are bf16 (rounded), 8: has o2.
 //   kKCopy | elem_bytes: o = a, bit copy.
-//   kKRing / kKHier / kKTree | dtype (0 fp32, 1 bf16, 2 bf16 rounded each
-//     add): one-pass fold over all ranks.
+//   kKRing / kKHier / kKTree / kKDTree | dtype (0 fp32, 1 bf16, 2 bf16
+//     rounded each add): one-pass fold over all ranks.  kKTree folds the
+//     binomial (left-complete) tree, which is the balanced tree when N is a
+//     power of two; kKDTree folds one half by one of the two double trees.
 constexpr int32_t kKReduce = 0x100;
 constexpr int32_t kKCopy = 0x200;
 constexpr int32_t kKRing = 0x300;
 constexpr int32_t kKHier = 0x400;
 constexpr int32_t kKTree = 0x500;
+constexpr int32_t kKDTree = 0x600;
 constexpr int32_t kFlagABf = 1, kFlagBBf = 2, kFlagOBf = 4, kFlagO2 = 8;
 
 struct Op {

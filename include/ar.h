@@ -20,6 +20,22 @@
  *                    all-gather.  Primer ch. 4 section 4.3 (Figure 4.5,
  *                    Animation 4.2); Scaling ML systems ch. 06, "Recursive
  *                    halving and doubling (butterfly)".
+ *   AR_RECURSIVE_DOUBLING  log2 N steps; in step k every rank exchanges its
+ *                    whole buffer with rank i xor 2^k and both add.  Primer
+ *                    ch. 4 section 4.3 ("Trees: latency-optimal,
+ *                    bandwidth-poor", Figure 4.5).  N a power of two.
+ *   AR_TREE          binary tree: the whole buffer is reduced up a binomial
+ *                    tree rooted at rank 0 (in step k, rank m*2^(k+1) adds
+ *                    what rank m*2^(k+1) + 2^k sends), then broadcast down
+ *                    the same edges.  Scaling ML systems ch. 06, "Tree
+ *                    AllReduce".  Any N; ceil(log2 N) steps each way.
+ *   AR_DOUBLE_TREE   two complementary binary trees, the second the mirror
+ *                    of the first (rank r plays node N-1-r), each reducing
+ *                    and broadcasting half of the buffer.  Scaling ML systems
+ *                    ch. 06, "Double binary tree"; Primer Figure 4.6 (tree 1
+ *                    for N = 8: 0 <- 4 <- {2, 6} <- {1, 3, 5, 7}).  A node
+ *                    adds its lower-ranked child's part before the higher.
+ *                    N a power of two.
  *
  * Result.  On completion every rank buffer holds G_0 + ... + G_{N-1}
  * (Scaling ML systems ch. 06, the algorithm box's output), summed in the
@@ -63,7 +79,14 @@ typedef enum {
  * schedule carries bf16 values; no scratch is used. */
 typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_BFLOAT16_EACH_STEP = 2 } ar_dtype_t;
 
-typedef enum { AR_RING = 0, AR_HIERARCHICAL = 1, AR_RABENSEIFNER = 2 } ar_schedule_t;
+typedef enum {
+  AR_RING = 0,
+  AR_HIERARCHICAL = 1,
+  AR_RABENSEIFNER = 2,
+  AR_RECURSIVE_DOUBLING = 3,
+  AR_TREE = 4,
+  AR_DOUBLE_TREE = 5
+} ar_schedule_t;
 
 /*
  * How a plan is executed.  Every mode gives bit-identical results.
@@ -114,7 +137,8 @@ typedef struct {
  * other schedules it only labels groups for cross_group_bytes_total.
  * Returns NULL on error: nranks outside [1, AR_MAX_PLAN_RANKS], group_size < 1 or
  * not dividing nranks, unknown dtype or schedule (AR_ERR_INVALID_ARG);
- * Rabenseifner with nranks not a power of two (AR_ERR_UNSUPPORTED).
+ * Rabenseifner, recursive doubling or the double tree with nranks not a
+ * power of two (AR_ERR_UNSUPPORTED).
  */
 ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype,
                           ar_schedule_t schedule);

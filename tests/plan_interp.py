@@ -70,8 +70,15 @@ def run(plan, bufs, dtype, group_size):
                 elif fam == B.KIND_TREE:
                     level = cols
                     while len(level) > 1:
-                        level = [fold(level[2 * m], level[2 * m + 1]) for m in range(len(level) // 2)]
+                        level = [fold(level[m], level[m + 1]) if m + 1 < len(level) else level[m]
+                                 for m in range(0, len(level), 2)]
                     acc = level[0]
+                elif fam == B.KIND_DTREE:
+                    def sub(c, b):
+                        if b == 1:
+                            return cols[c]
+                        return fold(fold(cols[c], sub(c - b // 2, b // 2)), sub(c + b // 2, b // 2))
+                    acc = fold(cols[0], sub(n // 2, n // 2)) if aux == 0 else fold(cols[n - 1], sub(n // 2 - 1, n // 2))
                 else:
                     G = group_size
                     M = n // G

@@ -49,7 +49,10 @@ def test_c1_ring_fp32_n4():
 
 SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
         [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (8, 4), (16, 8), (16, 4), (12, 3), (8, 8), (8, 1))] + \
-        [("rabenseifner", n, 1) for n in (2, 4, 8, 16, 64)]
+        [("rabenseifner", n, 1) for n in (2, 4, 8, 16, 64)] + \
+        [("recursive_doubling", n, 1) for n in (2, 8, 64)] + \
+        [("tree", n, 1) for n in (2, 5, 8, 13, 64)] + \
+        [("double_tree", n, 1) for n in (2, 8, 16, 64)]
 
 
 @pytest.mark.parametrize("sched,n,g", SMALL)
@@ -171,6 +174,14 @@ def test_full_c4_hierarchical_fp32_2x8x192MiB():
 
 def test_full_rabenseifner_fp32_16x192MiB():
     _full("fp32", "rabenseifner", 1, ["steps"])
+
+
+def test_full_recursive_doubling_fp32_16x192MiB():
+    _full("fp32", "recursive_doubling", 1, ["steps", "onepass"])
+
+
+def test_full_double_tree_bf16_16x192MiB():
+    _full("bf16", "double_tree", 1, ["steps", "onepass"])
 
 
 def test_full_ring_bf16_each_step_16x192MiB():

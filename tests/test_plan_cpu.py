@@ -21,7 +21,10 @@ SCHEDS = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
          [("ring", 16, 8), ("ring", 64, 8)] + \
          [("hierarchical", n, g) for n, g in ((2, 1), (4, 2), (4, 4), (6, 3), (6, 2), (8, 4), (16, 8),
                                               (16, 4), (12, 3), (64, 8), (9, 3))] + \
-         [("rabenseifner", n, 1) for n in (1, 2, 4, 8, 16, 64)]
+         [("rabenseifner", n, 1) for n in (1, 2, 4, 8, 16, 64)] + \
+         [("recursive_doubling", n, 1) for n in (1, 2, 4, 16, 64)] + \
+         [("tree", n, 1) for n in (1, 2, 3, 5, 8, 13, 16, 64)] + \
+         [("double_tree", n, 1) for n in (2, 4, 8, 16, 64)]
 
 
 def _plan(n, g, count, dtype, sched):
