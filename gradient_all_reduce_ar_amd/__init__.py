@@ -12,5 +12,5 @@ from ._binding import (  # noqa: F401
     ar_plan_cost_alpha_beta_ex,
     ar_plan_create, ar_plan_destroy, ar_plan_launch_info, ar_plan_launch_ops, ar_plan_launch_times,
     ar_plan_num_launches, ar_plan_prepare, ar_plan_set_exec, ar_plan_set_profiling, ar_plan_stats,
-    ar_plan_transfers,
+    ar_plan_transfers, ar_select_schedule,
 )

@@ -88,6 +88,8 @@ def _declare(L):
         "ar_plan_cost_alpha_beta": ([P, dbl, dbl, dbl], dbl),
         "ar_plan_cost_alpha_beta_ex": ([P, ctypes.POINTER(ar_cost_params_t)], dbl),
         "ar_plan_destroy": ([P], None),
+        "ar_select_schedule": ([ctypes.c_int, ctypes.c_int, sz, ctypes.c_int, ctypes.POINTER(ar_cost_params_t),
+                                ctypes.c_uint32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "ar_last_error": ([], ctypes.c_char_p),
         "ar_last_status": ([], ctypes.c_int),
         "ar_plan_transfers": ([P, pi32, pi32, pi32, pi64, pi64, pi32, i64], i64),
@@ -188,6 +190,21 @@ def ar_plan_cost_alpha_beta_ex(plan, alpha_intra_s, alpha_cross_s, bw_intra_Bps,
     if t < 0:
         _raise()
     return t
+
+
+def ar_select_schedule(nranks, group_size, count, dtype, alpha_intra_s, alpha_cross_s, bw_intra_Bps,
+                       bw_cross_Bps, bw_group_egress_Bps=0.0, egress_share=1.0, candidates=None):
+    """(schedule name, modelled seconds) of the fastest candidate."""
+    mask = 0
+    for c in (candidates or SCHEDULES):
+        mask |= 1 << _code(SCHEDULES, c)
+    c = ar_cost_params_t(alpha_intra_s, alpha_cross_s, bw_intra_Bps, bw_cross_Bps, bw_group_egress_Bps, egress_share)
+    t = ctypes.c_double()
+    best = lib().ar_select_schedule(nranks, group_size, count, _code(DTYPES, dtype), ctypes.byref(c), mask,
+                                    ctypes.byref(t))
+    if best < 0:
+        _raise()
+    return {v: k for k, v in SCHEDULES.items()}[best], t.value
 
 
 def ar_plan_destroy(plan):

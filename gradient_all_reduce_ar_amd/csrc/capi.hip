@@ -310,6 +310,38 @@ double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t 
                                 c->bw_group_egress_Bps, c->egress_share);
 }
 
+int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtype, const ar_cost_params_t *params,
+                       uint32_t candidates, double *best_s) {
+  if (!params) {
+    fail(AR_ERR_INVALID_ARG, "params is NULL");
+    return -1;
+  }
+  int best = -1;
+  double best_t = 0;
+  for (int sched = AR_RING; sched <= AR_DOUBLE_TREE; ++sched) {
+    if (!(candidates & (1u << sched))) continue;
+    ar::Plan p;
+    bool unsupported = false;
+    if (!ar::build_plan(p, nranks, group_size, static_cast<int64_t>(count), static_cast<ar::Dtype>(dtype),
+                        static_cast<ar::Sched>(sched), ar::kSteps, &unsupported).empty())
+      continue;
+    const double t = ar::cost_alpha_beta_ex(p, params->alpha_intra_s, params->alpha_cross_s, params->bw_intra_Bps,
+                                            params->bw_cross_Bps, params->bw_group_egress_Bps,
+                                            params->egress_share < 1 ? 1.0 : params->egress_share);
+    if (best < 0 || t < best_t) {
+      best = sched;
+      best_t = t;
+    }
+  }
+  if (best < 0) {
+    fail(AR_ERR_INVALID_ARG, "no candidate schedule fits these arguments");
+    return -1;
+  }
+  if (best_s) *best_s = best_t;
+  g_status = AR_OK;
+  return best;
+}
+
 void ar_plan_destroy(ar_plan_t *plan) {
   if (!plan) return;
   if (plan->prepared) (void)hipDeviceSynchronize();

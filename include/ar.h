@@ -199,6 +199,18 @@ typedef struct {
 
 double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t *params);
 
+/*
+ * Schedule selector (the choice NCCL makes per call from its alpha-beta
+ * tables: Primer ch. 4 section 4.3 "crossover"; Scaling ML systems ch. 06,
+ * "Algorithm crossover"): the schedule in `candidates` (bit 1 << schedule)
+ * with the lowest ar_plan_cost_alpha_beta_ex time for these sizes.
+ * Schedules that cannot serve nranks (power-of-two ones) are skipped.
+ * Returns the schedule and writes its time to *best_s (if not NULL), or -1
+ * on error (no candidate fits, bad arguments).  Host only.
+ */
+int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtype,
+                       const ar_cost_params_t *params, uint32_t candidates, double *best_s);
+
 /* Releases the plan and its device memory (synchronises the device first). */
 void ar_plan_destroy(ar_plan_t *plan);
 

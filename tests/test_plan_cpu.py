@@ -222,3 +222,56 @@ def test_large_plans_describe_but_do_not_run():
         B.ar_plan_destroy(mine)
     with pytest.raises(B.ArError):
         B.ar_plan_create(1025, 1, 10, "fp32", "ring")
+
+
+def _oracle_best(n, g, count, eb, cands, args):
+    best = None
+    for c in cands:
+        try:
+            t = oracle.cost_ex(n, count, eb, c, *args, group_size=g)
+        except oracle.OracleError:
+            continue
+        if best is None or t < best[1]:
+            best = (c, t)
+    return best
+
+
+def test_selector_matches_pages_and_oracle():
+    """The selector picks the cheapest candidate by the alpha-beta model:
+    Scaling ML systems ch. 06: 1 MB on 64 GPUs (alpha 10 us, beta 10 GB/s),
+    tree 1320 us beats ring 1456.9 us; with every schedule allowed the
+    butterfly (Rabenseifner) wins; Primer ch. 4: on 128 ranks (22 us, 50 GB/s)
+    recursive doubling wins below about 54 MB and the ring above; Data-center
+    networks 7.2.1: the 2x8 hierarchical all-reduce (1.3 ms) beats the ring
+    (7.6 ms) for the 192 MiB gradient."""
+    mb = 1_000_000
+    args = (10e-6, 10e-6, 10e9, 10e9, 0.0, 1.0)
+    name, t = B.ar_select_schedule(64, 1, mb // 4, "fp32", *args, candidates=["ring", "tree"])
+    assert name == "tree" and t * 1e6 == pytest.approx(1320.0)
+    name, t = B.ar_select_schedule(64, 1, mb // 4, "fp32", *args)
+    assert name == "rabenseifner"
+    ob = _oracle_best(64, 1, mb // 4, 4, list(B.SCHEDULES), args)
+    assert ob[0] == name and t == pytest.approx(ob[1], rel=1e-12)
+    a128 = (22e-6, 22e-6, 50e9, 50e9, 0.0, 1.0)
+    for size, want in ((40e6, "recursive_doubling"), (70e6, "ring")):
+        name, _ = B.ar_select_schedule(128, 1, int(size) // 4, "fp32", *a128, candidates=["ring", "recursive_doubling"])
+        assert name == want
+    name, t = B.ar_select_schedule(16, 8, 12288 * 4096, "fp32", 0.83e-6, 0.83e-6, 450e9, 50e9,
+                                   candidates=["ring", "hierarchical"])
+    assert name == "hierarchical" and t * 1e3 == pytest.approx(1.2995, rel=1e-3)
+    # power-of-two schedules are skipped for 12 ranks; none left is an error
+    name, _ = B.ar_select_schedule(12, 1, 1 << 20, "fp32", *args, candidates=["rabenseifner", "tree"])
+    assert name == "tree"
+    with pytest.raises(B.ArError):
+        B.ar_select_schedule(12, 1, 1 << 20, "fp32", *args, candidates=["rabenseifner"])
+
+
+@pytest.mark.parametrize("n", [2, 8, 16, 64, 100, 128, 1024])
+def test_selector_agrees_with_oracle_over_sizes(n):
+    cands = [c for c in B.SCHEDULES if c != "hierarchical"]
+    for size in (1e3, 1e5, 1e7, 1e9):
+        count = int(size) // 4
+        args = (5e-6, 5e-6, 50e9, 50e9, 0.0, 1.0)
+        name, t = B.ar_select_schedule(n, 1, count, "fp32", *args, candidates=cands)
+        ob = _oracle_best(n, 1, count, 4, cands, args)
+        assert t == pytest.approx(ob[1], rel=1e-12)
