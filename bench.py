@@ -111,7 +111,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS) + ["overlap"])
+    ap.add_argument("--compute-ratio", type=float, default=1.5,
+                    help="overlap workload: backward compute per bucket as a multiple of its all-reduce time")
     ap.add_argument("--exec", default="steps", choices=["steps", "steps_unfused", "onepass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the one-pass comparison run")
@@ -131,6 +133,8 @@ def main():
     from gradient_all_reduce_ar_amd import _binding as B
     from gradient_all_reduce_ar_amd import workloads
 
+    if args.workload == "overlap":
+        return overlap_main(args, B, workloads, np, torch)
     desc, sched, n, group, dtype, count = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -312,6 +316,95 @@ def main():
         B.ar_bucket_plan_destroy(plan)
     else:
         B.ar_plan_destroy(plan)
+    print(json.dumps(out), flush=True)
+
+
+def overlap_main(args, B, workloads, np, torch):
+    """Bucketed all-reduces overlapped with a simulated backward pass.
+
+    The backward of bucket b is a spin kernel on a producer stream lasting
+    compute_ratio times the bucket's measured all-reduce time (it uses no
+    memory bandwidth, like the non-contending compute of the overlap model),
+    after which the bucket's ready event is recorded.  The all-reduces run on
+    a second stream, each gated on its ready event (ar_bucket_allreduce_after).
+    Reported: the measured communication left after the backward ends, next
+    to the overlap model's prediction from the measured ready times and
+    per-bucket all-reduce times (Primer ch. 4 section 4.7, Figure 4.15).
+    """
+    n, sched, dtype = 16, "ring", "bf16"
+    sizes = workloads.bucketed_tensor_sizes(elem_bytes=2)
+    bp = B.ar_bucket_plan_create(n, 1, sizes, dtype, sched, 25 << 20)
+    offsets, arena = B.ar_bucket_layout(bp, len(sizes))
+    host = workloads.bucketed_arenas(n, sizes, offsets, arena, dtype="bf16")
+    bufs = [torch.from_numpy(h.view(np.int16)).cuda() for h in host]
+    nb = B.ar_bucket_count(bp)
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    # 1) per-bucket all-reduce times, back to back, no gating
+    done = [torch.cuda.Event(enable_timing=True) for _ in range(nb)]
+    start = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        B.ar_bucket_allreduce(bp, bufs, consumer)
+    torch.cuda.synchronize()
+    comm = np.zeros(nb)
+    for _ in range(args.steps):
+        start.record(consumer)
+        B.ar_bucket_allreduce_after(bp, bufs, consumer, None, done)
+        torch.cuda.synchronize()
+        prev = start
+        for b in range(nb):
+            comm[b] += prev.elapsed_time(done[b]) / args.steps
+            prev = done[b]
+    # 2) spin-kernel cycles per ms
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(producer):
+        torch.cuda._sleep(1_000_000)
+        t0.record(producer)
+        torch.cuda._sleep(20_000_000)
+        t1.record(producer)
+    torch.cuda.synchronize()
+    cycles_per_ms = 20_000_000 / t0.elapsed_time(t1)
+    # 3) overlapped runs
+    ready = [torch.cuda.Event(enable_timing=True) for _ in range(nb)]
+    exposed_meas, exposed_model, step_meas = [], [], []
+    for it in range(args.steps + args.warmup):
+        torch.cuda.synchronize()
+        begin = torch.cuda.Event(enable_timing=True)
+        bwd_end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(producer):
+            begin.record(producer)
+            for b in range(nb):
+                torch.cuda._sleep(max(1, int(args.compute_ratio * comm[b] * cycles_per_ms)))
+                ready[b].record(producer)
+            bwd_end.record(producer)
+        consumer.wait_event(begin)
+        B.ar_bucket_allreduce_after(bp, bufs, consumer, ready, done)
+        torch.cuda.synchronize()
+        if it < args.warmup:
+            continue
+        r = [begin.elapsed_time(e) for e in ready]
+        comp_end = begin.elapsed_time(bwd_end)
+        comm_end = begin.elapsed_time(done[-1])
+        exposed_meas.append(max(0.0, comm_end - comp_end))
+        step_meas.append(max(comp_end, comm_end))
+        _, ex = B.ar_overlap_step_time([x * 1e-3 for x in r], [c * 1e-3 for c in comm], comp_end * 1e-3, 0.0)
+        exposed_model.append(ex * 1e3)
+    S = int(np.sum(sizes)) * 2
+    out = {
+        "metric": "exposed all-reduce time after backward (bucketed, overlapped)",
+        "value": round(float(np.median(exposed_meas)), 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(np.median(step_meas)), 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (f32 accumulate)", "data": "synthetic",
+        "config": {"workload": "ring all-reduce, 16 ranks, 300 lognormal bf16 tensors in 25 MiB buckets, each "
+                               "gated on its bucket's backward (spin kernel of compute_ratio x its all-reduce time)",
+                   "buckets": nb, "bytes_per_rank": S, "compute_ratio": args.compute_ratio,
+                   "allreduce_ms_per_bucket": [round(c, 4) for c in comm],
+                   "allreduce_ms_total": round(float(comm.sum()), 4),
+                   "exposed_ms_model": round(float(np.median(exposed_model)), 4),
+                   "backward_ms": round(float(np.median([s_ - e_ for s_, e_ in zip(step_meas, exposed_meas)])), 4),
+                   "last_bucket_allreduce_ms": round(float(comm[-1]), 4)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    B.ar_bucket_plan_destroy(bp)
     print(json.dumps(out), flush=True)
 
 

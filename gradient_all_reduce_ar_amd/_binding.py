@@ -104,6 +104,9 @@ def _declare(L):
         "ar_bucket_range": ([P, i32, psz, psz], ctypes.c_int),
         "ar_bucket_set_exec": ([P, ctypes.c_int], ctypes.c_int),
         "ar_bucket_allreduce": ([P, P, P], ctypes.c_int),
+        "ar_bucket_allreduce_after": ([P, P, P, P, P], ctypes.c_int),
+        "ar_overlap_step_time": ([ctypes.c_int, ctypes.POINTER(dbl), ctypes.POINTER(dbl), dbl, dbl,
+                                  ctypes.POINTER(dbl)], dbl),
         "ar_bucket_stats": ([P], ar_stats_t),
         "ar_bucket_plan_destroy": ([P], None),
     }
@@ -313,6 +316,45 @@ def ar_bucket_set_exec(bp, exec_mode):
 def ar_bucket_allreduce(bp, rank_arenas, stream=None):
     arr = _ptr_array(rank_arenas)
     _check(lib().ar_bucket_allreduce(bp, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def _event(e):
+    if e is None:
+        return None
+    if hasattr(e, "cuda_event"):
+        if not e.cuda_event:
+            e.record()  # torch creates the underlying event on its first record
+        return e.cuda_event
+    return int(e)
+
+
+def ar_bucket_allreduce_after(bp, rank_arenas, stream=None, ready_events=None, done_events=None):
+    """ready_events / done_events: per bucket, torch.cuda.Event, raw hipEvent_t ints, or None."""
+    arr = _ptr_array(rank_arenas)
+    nb = ar_bucket_count(bp)
+
+    def evs(lst):
+        if lst is None:
+            return None
+        if len(lst) != nb:
+            raise ValueError(f"need {nb} events, got {len(lst)}")
+        a = (ctypes.c_void_p * max(nb, 1))(*[_event(e) for e in lst])
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    _check(lib().ar_bucket_allreduce_after(bp, ctypes.cast(arr, ctypes.c_void_p), _stream(stream),
+                                           evs(ready_events), evs(done_events)))
+
+
+def ar_overlap_step_time(ready_s, comm_s, compute_end_s, update_s):
+    """(step seconds, exposed seconds) of the overlap model."""
+    n = len(ready_s)
+    r = (ctypes.c_double * max(n, 1))(*ready_s)
+    c = (ctypes.c_double * max(n, 1))(*comm_s)
+    exp = ctypes.c_double()
+    t = lib().ar_overlap_step_time(n, r, c, compute_end_s, update_s, ctypes.byref(exp))
+    if t < 0:
+        _raise()
+    return t, exp.value
 
 
 def ar_bucket_stats(bp):

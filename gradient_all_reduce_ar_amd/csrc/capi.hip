@@ -509,6 +509,25 @@ ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
 }
 
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream) {
+  return ar_bucket_allreduce_after(bp, rank_arenas, stream, nullptr, nullptr);
+}
+
+double ar_overlap_step_time(int nchunks, const double *ready_s, const double *comm_s, double compute_end_s,
+                            double update_s, double *exposed_s) {
+  if (nchunks < 0 || (nchunks > 0 && (!ready_s || !comm_s)) || update_s < 0) {
+    fail(AR_ERR_INVALID_ARG, "bad overlap-model arguments");
+    return -1.0;
+  }
+  for (int k = 0; k < nchunks; ++k)
+    if (comm_s[k] < 0) {
+      fail(AR_ERR_INVALID_ARG, "negative communication time");
+      return -1.0;
+    }
+  return ar::overlap_step_time(nchunks, ready_s, comm_s, compute_end_s, update_s, exposed_s);
+}
+
+ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
+                                      void *const *ready_events, void *const *done_events) {
   if (!bp || !rank_arenas) return fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
   // one scratch shared by all buckets: they run one after another on one stream
   size_t need = 0;
@@ -536,8 +555,17 @@ ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, 
     pl->external_scratch_bytes = bp->scratch_bytes;
     for (int r = 0; r < bp->nranks; ++r)
       ptrs[r] = static_cast<char *>(rank_arenas[r]) + bp->bucket_offset[b] * eb;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ready_events && ready_events[b]) {
+      hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ready_events[b]), 0);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
     const ar_status_t st = ar_allreduce(pl, ptrs.data(), stream);
     if (st != AR_OK) return fail(st, "bucket " + std::to_string(b) + ": " + g_err);
+    if (done_events && done_events[b]) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(done_events[b]), s);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
   }
   return AR_OK;
 }

@@ -603,6 +603,18 @@ std::string check_hazards(const Plan &p) {
   return "";
 }
 
+double overlap_step_time(int nchunks, const double *ready, const double *comm, double compute_end, double update,
+                         double *exposed) {
+  // [PRIMER] 4.7, Figure 4.15: a chunk's collective starts once backward has
+  // produced the chunk and the previous collective is done; the update waits
+  // for the compute and for the last collective.
+  double end = 0.0;
+  for (int k = 0; k < nchunks; ++k) end = std::max(end, ready[k]) + comm[k];
+  const double done = std::max(compute_end, end);
+  if (exposed) *exposed = std::max(0.0, end - compute_end);
+  return done + update;
+}
+
 void assign_buckets(const std::vector<int64_t> &tensor_counts, int64_t cap_elems, int64_t align_elems,
                     std::vector<int64_t> &tensor_offsets, std::vector<int64_t> &bucket_offset,
                     std::vector<int64_t> &bucket_count, int64_t &arena_count) {

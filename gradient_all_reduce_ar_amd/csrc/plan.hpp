@@ -107,6 +107,10 @@ double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross,
 // another op of the same launch reads or writes.  Empty string if clean.
 std::string check_hazards(const Plan &p);
 
+// Overlap model (see ar_overlap_step_time).
+double overlap_step_time(int nchunks, const double *ready, const double *comm, double compute_end, double update,
+                         double *exposed);
+
 // Bucket fuser: assigns tensors (element counts) to buckets in reverse
 // tensor order under `cap_elems`; fills per-tensor arena offsets, bucket
 // ranges and the arena length.  Buckets start on `align_elems` boundaries.

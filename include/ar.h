@@ -279,6 +279,27 @@ ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec);
 /* All-reduces every bucket of the nranks arenas (16-byte aligned device
  * pointers of arena_count elements), in place, on `stream`. */
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream);
+/* Overlap with the backward pass (Scaling ML systems ch. 06, "Overlap layer
+ * by layer" and "Bucket fusion"; Primer ch. 4 section 4.7): like
+ * ar_bucket_allreduce, but bucket b's all-reduce first waits on
+ * ready_events[b] (a hipEvent_t the producer of its gradients recorded, on
+ * any stream; NULL = ready now), and done_events[b] (if the array and the
+ * entry are not NULL) is recorded on `stream` after it.  So each bucket
+ * starts when it is ready and the previous bucket's all-reduce is done, as in
+ * Figure 4.15.  Both arrays have ar_bucket_count entries. */
+ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
+                                      void *const *ready_events, void *const *done_events);
+
+/* The overlap model of Primer ch. 4 section 4.7 (Figure 4.15) and
+ * Data-center networks 7.6.2: chunk k's collective starts at
+ * max(ready_s[k], end of chunk k-1's collective) and lasts comm_s[k]; the
+ * step ends update_s after both the compute (compute_end_s) and the last
+ * collective are done.  Returns the step time; *exposed_s (if not NULL)
+ * receives the communication left after the compute ends.  Host only;
+ * negative on bad arguments. */
+double ar_overlap_step_time(int nchunks, const double *ready_s, const double *comm_s, double compute_end_s,
+                            double update_s, double *exposed_s);
+
 /* Sum of the per-bucket statistics (bytes, steps, launches). */
 ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp);
 void ar_bucket_plan_destroy(ar_bucket_plan_t *bp);
