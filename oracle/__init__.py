@@ -58,6 +58,8 @@ def _bind(L):
     L.aro_cost.restype = dbl
     L.aro_cost_ex.argtypes = [i32, i32, i64, i32, i32, dbl, dbl, dbl, dbl, dbl, dbl]
     L.aro_cost_ex.restype = dbl
+    L.aro_run_int8ef.argtypes = [i32, i32, i64, i32, P, P, i32]
+    L.aro_run_int8ef.restype = i32
     L.aro_run.argtypes = [i32, i32, i64, i32, i32, P, i32]
     L.aro_run.restype = i32
     return L
@@ -139,4 +141,25 @@ def run(bufs, dtype, schedule, group_size=1, max_steps=-1, L=None):
                    ctypes.cast(arr, ctypes.c_void_p), max_steps)
     if rc != 0:
         raise OracleError(f"aro_run failed ({rc})")
+    return bufs
+
+
+QBLOCK = 128
+
+
+def run_int8ef(bufs, schedule, errs=None, group_size=1, max_steps=-1, L=None):
+    """Blockwise-INT8 all-reduce with error feedback, in place on float32
+    host arrays; errs (float32 arrays, updated in place) or None."""
+    L = L or lib()
+    n = len(bufs)
+    count = len(bufs[0]) if n else 0
+    for b in list(bufs) + list(errs or []):
+        if b.dtype != np.float32 or not b.flags.c_contiguous or len(b) != count:
+            raise OracleError("buffers must be contiguous float32 arrays of equal length")
+    ab = (ctypes.c_void_p * max(n, 1))(*[b.ctypes.data for b in bufs])
+    ae = (ctypes.c_void_p * max(n, 1))(*[e.ctypes.data for e in errs]) if errs is not None else None
+    rc = L.aro_run_int8ef(n, group_size, count, _SCHED[schedule], ctypes.cast(ab, ctypes.c_void_p),
+                          ctypes.cast(ae, ctypes.c_void_p) if ae is not None else None, max_steps)
+    if rc != 0:
+        raise OracleError(f"aro_run_int8ef failed ({rc})")
     return bufs

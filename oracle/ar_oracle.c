@@ -38,6 +38,7 @@
  *         REDUCE widens both operands, adds in fp32 and rounds the sum to
  *         bf16 at once -- what a wire of bf16 values gives.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -624,6 +625,137 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
   if (dtype != ARO_FP32)
     for (int r = 0; r < nranks; ++r) free(w[r]);
   free(w);
+  free(L.m);
+  return err ? -3 : 0;
+}
+
+
+/* ---------------------------------------------------------------------- */
+/* Compressed all-reduce: blockwise INT8 with error feedback.             */
+/* ---------------------------------------------------------------------- */
+/*
+ * [SCALING] "Gradient compression": INT8 quantization with a scale
+ * s = max|g| / 127, q = round(g / s), decoded as q * s; "Blockwise
+ * quantization": one fp32 scale per block of b elements (message
+ * d + 4d/b bytes); "Error feedback": every worker keeps e_t and sends
+ * v_t = C(g_t + e_t), then e_{t+1} = g_t + e_t - v_t.
+ *
+ * Readings (the pages leave them open): b = 128; round = to nearest, ties
+ * to even; a block of zeros has scale 0 and codes 0.  Every message of the
+ * schedule carries codes and scales: a REDUCE receiver decodes the message
+ * and its own codes, adds in fp32 and re-encodes the sum; a COPY forwards
+ * codes.  The schedule is built over blocks (chunk boundaries fall between
+ * blocks).  At the end every rank decodes its codes into its buffer.
+ */
+#define ARO_QB 128
+
+static void q_encode(const float *x, int n, int8_t *q, float *scale) {
+  float m = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    if (a > m) m = a;
+  }
+  float s = m / 127.0f;
+  *scale = s;
+  for (int i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      q[i] = 0;
+      continue;
+    }
+    float r = rintf(x[i] / s);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    q[i] = (int8_t)r;
+  }
+}
+
+static float q_decode(int8_t q, float s) { return (float)q * s; }
+
+/*
+ * bufs[r]: fp32 gradient of rank r (count elements), replaced by the
+ * decoded result; errs[r]: its fp32 error accumulator, updated in place
+ * (errs == NULL: no error feedback, e = 0).  Returns 0 or a negative code.
+ */
+int aro_run_int8ef(int nranks, int group_size, long long count, int schedule, float **bufs, float **errs,
+                   int max_steps) {
+  int64_t nblk = (count + ARO_QB - 1) / ARO_QB;
+  aro_list L;
+  int rc = build(&L, nranks, group_size, nblk, schedule);
+  if (rc) return rc;
+  int nsteps = (max_steps >= 0 && max_steps < L.nsteps) ? max_steps : L.nsteps;
+  int8_t **q = (int8_t **)calloc((size_t)nranks, sizeof(int8_t *));
+  float **sc = (float **)calloc((size_t)nranks, sizeof(float *));
+  float *x = (float *)malloc(sizeof(float) * ARO_QB);
+  int err = !q || !sc || !x;
+  for (int r = 0; r < nranks && !err; ++r) {
+    q[r] = (int8_t *)malloc((size_t)(count > 0 ? count : 1));
+    sc[r] = (float *)malloc(sizeof(float) * (size_t)(nblk > 0 ? nblk : 1));
+    if (!q[r] || !sc[r]) err = 1;
+  }
+  /* each rank compresses g + e and keeps the residual */
+  for (int r = 0; r < nranks && !err; ++r)
+    for (int64_t b = 0; b < nblk; ++b) {
+      int64_t lo = b * ARO_QB;
+      int n = (int)((count - lo) < ARO_QB ? (count - lo) : ARO_QB);
+      for (int i = 0; i < n; ++i) x[i] = bufs[r][lo + i] + (errs ? errs[r][lo + i] : 0.0f);
+      q_encode(x, n, q[r] + lo, &sc[r][b]);
+      if (errs)
+        for (int i = 0; i < n; ++i) errs[r][lo + i] = x[i] - q_decode(q[r][lo + i], sc[r][b]);
+    }
+  /* the schedule over blocks; payload copies first, then the receivers */
+  int8_t *pq = NULL;
+  float *ps = NULL;
+  if (!err) {
+    pq = (int8_t *)malloc((size_t)(nranks > 0 ? nranks : 1) * (size_t)(count > 0 ? count : 1));
+    ps = (float *)malloc(sizeof(float) * (size_t)(nranks > 0 ? nranks : 1) * (size_t)(nblk > 0 ? nblk : 1));
+    if (!pq || !ps) err = 1;
+  }
+  int64_t j0 = 0;
+  while (!err && j0 < L.n && L.m[j0].step < nsteps) {
+    int64_t j1 = j0;
+    while (j1 < L.n && L.m[j1].step == L.m[j0].step) ++j1;
+    int64_t eoff = 0, boff = 0;
+    for (int64_t j = j0; j < j1; ++j) {
+      const aro_msg *m = &L.m[j];
+      int64_t elo = m->lo * ARO_QB, ehi = m->hi * ARO_QB < count ? m->hi * ARO_QB : count;
+      memcpy(pq + eoff, q[m->src] + elo, (size_t)(ehi > elo ? ehi - elo : 0));
+      memcpy(ps + boff, sc[m->src] + m->lo, sizeof(float) * (size_t)(m->hi - m->lo));
+      eoff += ehi > elo ? ehi - elo : 0;
+      boff += m->hi - m->lo;
+    }
+    eoff = 0;
+    boff = 0;
+    for (int64_t j = j0; j < j1; ++j) {
+      const aro_msg *m = &L.m[j];
+      for (int64_t b = m->lo; b < m->hi; ++b, ++boff) {
+        int64_t lo = b * ARO_QB;
+        int n = (int)((count - lo) < ARO_QB ? (count - lo) : ARO_QB);
+        if (m->kind == ARO_REDUCE) {
+          for (int i = 0; i < n; ++i)
+            x[i] = q_decode(pq[eoff + i], ps[boff]) + q_decode(q[m->dst][lo + i], sc[m->dst][b]);
+          q_encode(x, n, q[m->dst] + lo, &sc[m->dst][b]);
+        } else {
+          memcpy(q[m->dst] + lo, pq + eoff, (size_t)n);
+          sc[m->dst][b] = ps[boff];
+        }
+        eoff += n;
+      }
+    }
+    j0 = j1;
+  }
+  /* every rank decodes what it holds */
+  for (int r = 0; r < nranks && !err; ++r)
+    for (int64_t b = 0; b < nblk; ++b)
+      for (int64_t e = b * ARO_QB; e < count && e < (b + 1) * ARO_QB; ++e) bufs[r][e] = q_decode(q[r][e], sc[r][b]);
+  free(pq);
+  free(ps);
+  for (int r = 0; r < nranks; ++r) {
+    if (q) free(q[r]);
+    if (sc) free(sc[r]);
+  }
+  free(q);
+  free(sc);
+  free(x);
   free(L.m);
   return err ? -3 : 0;
 }

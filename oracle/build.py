@@ -17,7 +17,7 @@ CFLAGS = ["-O2", "-std=gnu11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contr
 
 
 def build(out=LIB, extra=()):
-    cmd = ["gcc", *CFLAGS, *extra, "-o", out, SRC]
+    cmd = ["gcc", *CFLAGS, *extra, "-o", out, SRC, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 

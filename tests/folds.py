@@ -81,37 +81,42 @@ def dtree_fold(vals, half, add=add32):
     return add(vals[n - 1], sub(n // 2 - 1, n // 2))
 
 
+def fold_at(col, e, count, schedule, group_size=1, add=add32):
+    """The sum one schedule forms at position e of `count` positions from
+    the per-rank values col[r] (scalars, or equal-length vectors)."""
+    n = len(col)
+    if n == 1:
+        return np.float32(col[0])
+    if schedule == "ring":
+        c, _ = chunk_of(e, count, n)
+        return ring_fold(col, c, add)
+    if schedule in ("rabenseifner", "recursive_doubling"):
+        return tree_fold(col, add)
+    if schedule == "tree":
+        return binomial_fold(col, add)
+    if schedule == "double_tree":
+        return dtree_fold(col, 0 if e < count // 2 else 1, add)
+    if schedule == "hierarchical":
+        g_sz = group_size
+        m_groups = n // g_sz
+        k, slo = chunk_of(e, count, g_sz)
+        _, shi = part(count, g_sz, k)
+        partials = []
+        for g in range(m_groups):
+            local = [col[g * g_sz + l] for l in range(g_sz)]
+            partials.append(ring_fold(local, k + 1, add) if g_sz > 1 else np.float32(local[0]))
+        j, _ = chunk_of(e - slo, shi - slo, m_groups)
+        return ring_fold(partials, j, add) if m_groups > 1 else partials[0]
+    raise ValueError(schedule)
+
+
 def expected_fp32(xs, schedule, group_size=1, add=add32):
     """xs: list of N float32 arrays.  Returns the float32 result array."""
     n = len(xs)
     count = len(xs[0])
     out = np.zeros(count, np.float32)
     for e in range(count):
-        col = [xs[r][e] for r in range(n)]
-        if n == 1:
-            out[e] = col[0]
-        elif schedule == "ring":
-            c, _ = chunk_of(e, count, n)
-            out[e] = ring_fold(col, c, add)
-        elif schedule in ("rabenseifner", "recursive_doubling"):
-            out[e] = tree_fold(col, add)
-        elif schedule == "tree":
-            out[e] = binomial_fold(col, add)
-        elif schedule == "double_tree":
-            out[e] = dtree_fold(col, 0 if e < count // 2 else 1, add)
-        elif schedule == "hierarchical":
-            g_sz = group_size
-            m_groups = n // g_sz
-            k, slo = chunk_of(e, count, g_sz)
-            _, shi = part(count, g_sz, k)
-            partials = []
-            for g in range(m_groups):
-                local = [col[g * g_sz + l] for l in range(g_sz)]
-                partials.append(ring_fold(local, k + 1, add) if g_sz > 1 else np.float32(local[0]))
-            j, _ = chunk_of(e - slo, shi - slo, m_groups)
-            out[e] = ring_fold(partials, j, add) if m_groups > 1 else partials[0]
-        else:
-            raise ValueError(schedule)
+        out[e] = fold_at([xs[r][e] for r in range(n)], e, count, schedule, group_size, add)
     return out
 
 
@@ -147,3 +152,45 @@ def expected_bf16_each(bits_list, schedule, group_size=1):
         return np.asarray(bits_list[0], np.uint16).copy()
     xs = [widen(b) for b in bits_list]
     return to_bf16_bits(expected_fp32(xs, schedule, group_size, add=add_bf16_each))
+
+
+QBLOCK = 128
+
+
+def int8_roundtrip(x):
+    """Blockwise INT8 encode then decode of one block (float32 vector):
+    s = max|x| / 127, q = round-half-even(x / s) clamped to [-127, 127],
+    value q * s; a block of zeros stays zero."""
+    x = np.asarray(x, np.float32)
+    s = np.float32(np.max(np.abs(x)) / np.float32(127.0)) if len(x) else np.float32(0)
+    if s == 0:
+        return np.zeros_like(x)
+    q = np.clip(np.rint(x / s), -127, 127).astype(np.float32)
+    return (q * s).astype(np.float32)
+
+
+def expected_int8ef(xs, schedule, errs=None, group_size=1):
+    """Block-level closed form of the compressed all-reduce: every leaf is
+    round-tripped g + e, every partial sum of the schedule's fold is
+    round-tripped, blocks play the role of elements in the chunk partition.
+    Returns (result, new_errors)."""
+    n = len(xs)
+    count = len(xs[0])
+    nblk = (count + QBLOCK - 1) // QBLOCK
+    out = np.zeros(count, np.float32)
+    new_errs = [np.zeros(count, np.float32) for _ in range(n)]
+
+    def add(a, b):
+        return int8_roundtrip((np.asarray(a, np.float32) + np.asarray(b, np.float32)).astype(np.float32))
+
+    for blk in range(nblk):
+        lo, hi = blk * QBLOCK, min(count, (blk + 1) * QBLOCK)
+        col = []
+        for r in range(n):
+            x = xs[r][lo:hi] + (errs[r][lo:hi] if errs is not None else np.float32(0))
+            x = x.astype(np.float32)
+            v = int8_roundtrip(x)
+            new_errs[r][lo:hi] = (x - v).astype(np.float32)
+            col.append(v)
+        out[lo:hi] = fold_at(col, blk, nblk, schedule, group_size, add)
+    return out, new_errs

@@ -40,6 +40,14 @@ MUTANTS = {
     "cost_sum_not_max": ("if (t > worst[L.m[j].step]) worst[L.m[j].step] = t;", "worst[L.m[j].step] += t;"),
     "cross_group_label": ("if (L.m[j].src / group_size != L.m[j].dst / group_size) *cross_group_bytes += b;",
                           "if (L.m[j].src % group_size != L.m[j].dst % group_size) *cross_group_bytes += b;"),
+    "int8_ef_sign": ("errs[r][lo + i] = x[i] - q_decode(", "errs[r][lo + i] = -x[i] + q_decode("),
+    "int8_ef_dropped": ("x[i] = bufs[r][lo + i] + (errs ? errs[r][lo + i] : 0.0f);", "x[i] = bufs[r][lo + i];"),
+    "int8_truncate": ("float r = rintf(x[i] / s);", "float r = truncf(x[i] / s);"),
+    "int8_scale_255": ("float s = m / 127.0f;", "float s = m / 255.0f;"),
+    "int8_block_64": ("#define ARO_QB 128", "#define ARO_QB 64"),
+    "int8_dropped_own": ("x[i] = q_decode(pq[eoff + i], ps[boff]) + q_decode(q[m->dst][lo + i], sc[m->dst][b]);",
+                         "x[i] = q_decode(pq[eoff + i], ps[boff]);"),
+    "int8_scale_of_sender": ("sc[m->dst][b] = ps[boff];", "sc[m->dst][b] = sc[m->dst][b];"),
 }
 
 
@@ -52,9 +60,10 @@ def test_mutant_is_caught(name, tmp_path):
     mut.write_text(src.replace(old, new))
     lib = tmp_path / "libmutant.so"
     subprocess.run(["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-fno-fast-math",
-                    "-ffp-contract=off", "-w", "-o", str(lib), str(mut)], check=True)
+                    "-ffp-contract=off", "-w", "-o", str(lib), str(mut), "-lm"], check=True)
     env = dict(os.environ, ARO_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pages.py", "tests/test_oracle_bruteforce.py"],
+                        "tests/test_oracle_pages.py", "tests/test_oracle_bruteforce.py",
+                        "tests/test_oracle_int8ef.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
