@@ -15,19 +15,21 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libar.so")
 
 AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP = range(5)
-AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP = 0, 1, 2
+AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP, AR_INT8_EF = 0, 1, 2, 3
 AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER, AR_RECURSIVE_DOUBLING, AR_TREE, AR_DOUBLE_TREE = range(6)
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
 AR_MAX_RANKS = 64
 AR_MAX_PLAN_RANKS = 1024
 
-DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP}
+DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP, "int8_ef": AR_INT8_EF}
 SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER,
              "recursive_doubling": AR_RECURSIVE_DOUBLING, "tree": AR_TREE, "double_tree": AR_DOUBLE_TREE}
 EXECS = {"steps": AR_EXEC_STEPS, "steps_unfused": AR_EXEC_STEPS_UNFUSED, "onepass": AR_EXEC_ONEPASS}
 
 # kernel kind codes reported by ar_plan_launch_info
 KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE, KIND_DTREE = 0x100, 0x200, 0x300, 0x400, 0x500, 0x600
+KIND_QENCODE, KIND_QREDUCE, KIND_QCOPY, KIND_QDECODE = 0x700, 0x800, 0x900, 0xA00
+QBLOCK = 128
 LOC_SCRATCH = 1000
 
 
@@ -84,6 +86,7 @@ def _declare(L):
         "ar_plan_set_exec": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_prepare": ([P], ctypes.c_int),
         "ar_allreduce": ([P, P, P], ctypes.c_int),
+        "ar_allreduce_ef": ([P, P, P, P], ctypes.c_int),
         "ar_plan_stats": ([P], ar_stats_t),
         "ar_plan_cost_alpha_beta": ([P, dbl, dbl, dbl], dbl),
         "ar_plan_cost_alpha_beta_ex": ([P, ctypes.POINTER(ar_cost_params_t)], dbl),
@@ -105,6 +108,7 @@ def _declare(L):
         "ar_bucket_set_exec": ([P, ctypes.c_int], ctypes.c_int),
         "ar_bucket_allreduce": ([P, P, P], ctypes.c_int),
         "ar_bucket_allreduce_after": ([P, P, P, P, P], ctypes.c_int),
+        "ar_bucket_allreduce_ef": ([P, P, P, P, P, P], ctypes.c_int),
         "ar_overlap_step_time": ([ctypes.c_int, ctypes.POINTER(dbl), ctypes.POINTER(dbl), dbl, dbl,
                                   ctypes.POINTER(dbl)], dbl),
         "ar_bucket_stats": ([P], ar_stats_t),
@@ -172,6 +176,13 @@ def ar_plan_prepare(plan):
 def ar_allreduce(plan, rank_bufs, stream=None):
     arr = _ptr_array(rank_bufs)
     _check(lib().ar_allreduce(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def ar_allreduce_ef(plan, rank_bufs, error_bufs, stream=None):
+    """error_bufs: per-rank fp32 residual buffers, or None (no error feedback)."""
+    arr = _ptr_array(rank_bufs)
+    err = ctypes.cast(_ptr_array(error_bufs), ctypes.c_void_p) if error_bufs is not None else None
+    _check(lib().ar_allreduce_ef(plan, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream)))
 
 
 def ar_plan_stats(plan):
@@ -343,6 +354,23 @@ def ar_bucket_allreduce_after(bp, rank_arenas, stream=None, ready_events=None, d
 
     _check(lib().ar_bucket_allreduce_after(bp, ctypes.cast(arr, ctypes.c_void_p), _stream(stream),
                                            evs(ready_events), evs(done_events)))
+
+
+def ar_bucket_allreduce_ef(bp, rank_arenas, error_arenas, stream=None, ready_events=None, done_events=None):
+    arr = _ptr_array(rank_arenas)
+    err = ctypes.cast(_ptr_array(error_arenas), ctypes.c_void_p) if error_arenas is not None else None
+    nb = ar_bucket_count(bp)
+
+    def evs(lst):
+        if lst is None:
+            return None
+        if len(lst) != nb:
+            raise ValueError(f"need {nb} events, got {len(lst)}")
+        a = (ctypes.c_void_p * max(nb, 1))(*[_event(e) for e in lst])
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    _check(lib().ar_bucket_allreduce_ef(bp, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream),
+                                        evs(ready_events), evs(done_events)))
 
 
 def ar_overlap_step_time(ready_s, comm_s, compute_end_s, update_s):

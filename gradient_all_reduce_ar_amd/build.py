@@ -6,14 +6,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
-SOURCES = ["plan.cpp", "kernels.hip", "capi.hip"]
+SOURCES = ["plan.cpp", "kernels.hip", "qkernels.hip", "capi.hip"]
 
 # -ffp-contract=off and no fast-math: every add is one IEEE binary32 add.
 # -fno-gpu-flush-denormals-to-zero: fp32 denormals are kept on the device.
 # packed-fp32 ops are disabled: the kernels are built from scalar adds.
+# fp32 division on the device is correctly rounded (the INT8 quantizer).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]

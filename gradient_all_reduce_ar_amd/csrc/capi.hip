@@ -51,9 +51,8 @@ struct ar_plan {
   int64_t prof_logged = 0;          // calls recorded since the log was last read
   std::vector<hipEvent_t> events;   // prof_calls * (launches + 1)
 
-  size_t need_scratch_bytes() const {
-    return static_cast<size_t>(p.nslots) * static_cast<size_t>(p.slot_stride) * sizeof(float);
-  }
+  // fp32 partial-sum slots, or the INT8 code slots
+  size_t need_scratch_bytes() const { return static_cast<size_t>(ar::workspace_bytes(p)); }
 
   void release_device() {
     if (d_ops) (void)hipFree(d_ops);
@@ -79,6 +78,11 @@ struct ar_bucket_plan {
 };
 
 namespace {
+
+bool is_quant_kind(int32_t kind) {
+  const int32_t fam = kind & 0xF00;
+  return fam == ar::kKQEncode || fam == ar::kKQReduce || fam == ar::kKQCopy || fam == ar::kKQDecode;
+}
 
 // Bytes a launch writes (both outputs of fused ops).
 int64_t launch_written_bytes(const ar::Plan &p, const ar::Launch &L) {
@@ -108,9 +112,10 @@ ar_status_t prepare(ar_plan_t *pl) {
   for (const ar::Launch &L : pl->p.launches) {
     pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
     const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
-    const bool cold = ar_dev::is_cold(launch_written_bytes(pl->p, L), out_scratch);
+    const bool quant = is_quant_kind(L.kind);
+    const bool cold = !quant && ar_dev::is_cold(launch_written_bytes(pl->p, L), out_scratch);
     pl->cold.push_back(cold);
-    const int64_t tile = ar_dev::tile_elems(L.kind, cold);
+    const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold);
     int64_t gx = 0;
     for (const ar::Op &o : L.ops) {
       host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
@@ -156,22 +161,45 @@ ar_status_t prepare(ar_plan_t *pl) {
   return AR_OK;
 }
 
-ar_status_t check_rank_pointers(const ar_plan_t *pl, void *const *rank_bufs) {
-  if (!rank_bufs) return fail(AR_ERR_INVALID_ARG, "rank_bufs is NULL");
-  const int n = pl->p.nranks;
-  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::elem_bytes(pl->p.dtype));
-  if (bytes == 0) return AR_OK;  // nothing is read or written
+// Each of the nranks buffers holds `bytes` bytes: non-NULL, 16-byte aligned,
+// pairwise disjoint.
+ar_status_t check_buffers(int n, void *const *bufs, uint64_t bytes, const char *what) {
   for (int r = 0; r < n; ++r) {
-    const uintptr_t v = reinterpret_cast<uintptr_t>(rank_bufs[r]);
-    if (!v) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is NULL");
-    if (v % 16) return fail(AR_ERR_INVALID_ARG, "rank buffer " + std::to_string(r) + " is not 16-byte aligned");
+    const uintptr_t v = reinterpret_cast<uintptr_t>(bufs[r]);
+    if (!v) return fail(AR_ERR_INVALID_ARG, std::string(what) + " " + std::to_string(r) + " is NULL");
+    if (v % 16) return fail(AR_ERR_INVALID_ARG, std::string(what) + " " + std::to_string(r) + " is not 16-byte aligned");
   }
   for (int r = 0; r < n; ++r)
     for (int q = r + 1; q < n; ++q) {
-      const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
-      const uintptr_t b = reinterpret_cast<uintptr_t>(rank_bufs[q]);
+      const uintptr_t a = reinterpret_cast<uintptr_t>(bufs[r]);
+      const uintptr_t b = reinterpret_cast<uintptr_t>(bufs[q]);
       if (a < b + bytes && b < a + bytes)
-        return fail(AR_ERR_INVALID_ARG, "rank buffers " + std::to_string(r) + " and " + std::to_string(q) + " overlap");
+        return fail(AR_ERR_INVALID_ARG, std::string(what) + "s " + std::to_string(r) + " and " + std::to_string(q) +
+                                            " overlap");
+    }
+  return AR_OK;
+}
+
+ar_status_t check_rank_pointers(const ar_plan_t *pl, void *const *rank_bufs) {
+  if (!rank_bufs) return fail(AR_ERR_INVALID_ARG, "rank_bufs is NULL");
+  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::buffer_elem_bytes(pl->p.dtype));
+  if (bytes == 0) return AR_OK;  // nothing is read or written
+  return check_buffers(pl->p.nranks, rank_bufs, bytes, "rank buffer");
+}
+
+ar_status_t check_error_pointers(const ar_plan_t *pl, void *const *rank_bufs, void *const *error_bufs) {
+  const int n = pl->p.nranks;
+  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * 4;
+  if (bytes == 0) return AR_OK;
+  ar_status_t st = check_buffers(n, error_bufs, bytes, "error buffer");
+  if (st != AR_OK) return st;
+  for (int r = 0; r < n; ++r)
+    for (int q = 0; q < n; ++q) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
+      const uintptr_t b = reinterpret_cast<uintptr_t>(error_bufs[q]);
+      if (a < b + bytes && b < a + bytes)
+        return fail(AR_ERR_INVALID_ARG,
+                    "rank buffer " + std::to_string(r) + " and error buffer " + std::to_string(q) + " overlap");
     }
   return AR_OK;
 }
@@ -183,7 +211,7 @@ ar_stats_t stats_of(const ar::Plan &p) {
   s.steps = static_cast<uint32_t>(p.nsteps);
   s.launches = static_cast<uint32_t>(p.launches.size());
   s.count = static_cast<uint64_t>(p.count);
-  s.elem_bytes = static_cast<uint64_t>(ar::elem_bytes(p.dtype));
+  s.elem_bytes = static_cast<uint64_t>(ar::buffer_elem_bytes(p.dtype));
   s.bytes_sent = p.bytes_sent.data();
   for (uint64_t b : p.bytes_sent) {
     s.bytes_sent_max = std::max(s.bytes_sent_max, b);
@@ -191,7 +219,7 @@ ar_stats_t stats_of(const ar::Plan &p) {
   }
   s.cross_group_bytes_total = p.cross_group_bytes;
   s.hbm_bytes_model = p.hbm_bytes;
-  s.scratch_bytes = static_cast<uint64_t>(p.nslots) * static_cast<uint64_t>(p.slot_stride) * 4;
+  s.scratch_bytes = ar::workspace_bytes(p);
   s.exec = p.exec;
   return s;
 }
@@ -229,6 +257,8 @@ ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t d
 ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
   if (exec == static_cast<ar_exec_t>(plan->p.exec) && plan->prepared) return AR_OK;
+  if (plan->p.dtype == ar::kI8EF && exec == AR_EXEC_ONEPASS)
+    return fail(AR_ERR_UNSUPPORTED, "one-pass execution is not available for AR_INT8_EF");
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
@@ -245,21 +275,42 @@ ar_status_t ar_plan_prepare(ar_plan_t *plan) {
   return prepare(plan);
 }
 
-ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
+ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
   if (plan->p.nranks > ar::kMaxExecRanks)
     return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
+  const bool quant = plan->p.dtype == ar::kI8EF;
+  if (error_bufs && !quant) return fail(AR_ERR_INVALID_ARG, "error feedback needs an AR_INT8_EF plan");
   ar_status_t st = check_rank_pointers(plan, rank_bufs);
   if (st != AR_OK) return st;
+  if (error_bufs) {
+    st = check_error_pointers(plan, rank_bufs, error_bufs);
+    if (st != AR_OK) return st;
+  }
   st = prepare(plan);
   if (st != AR_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ar_dev::KArgs args{};
-  for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
-  args.scratch = plan->external_scratch ? plan->external_scratch : plan->scratch;
-  args.slot_stride = plan->p.slot_stride;
-  args.nranks = plan->p.nranks;
-  args.group_size = plan->p.group_size;
+  ar_dev::QArgs qargs{};
+  if (quant) {
+    for (int r = 0; r < plan->p.nranks; ++r) {
+      qargs.grad[r] = static_cast<float *>(rank_bufs[r]);
+      qargs.err[r] = error_bufs ? static_cast<float *>(error_bufs[r]) : nullptr;
+    }
+    char *ws = reinterpret_cast<char *>(plan->external_scratch ? plan->external_scratch : plan->scratch);
+    qargs.codes = reinterpret_cast<int8_t *>(ws);
+    qargs.scales = reinterpret_cast<float *>(ws + static_cast<int64_t>(plan->p.nranks) * plan->p.code_stride);
+    qargs.code_stride = plan->p.code_stride;
+    qargs.scale_stride = plan->p.scale_stride;
+    qargs.count = plan->p.count;
+    qargs.has_err = error_bufs != nullptr;
+  } else {
+    for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
+    args.scratch = plan->external_scratch ? plan->external_scratch : plan->scratch;
+    args.slot_stride = plan->p.slot_stride;
+    args.nranks = plan->p.nranks;
+    args.group_size = plan->p.group_size;
+  }
   const bool prof = plan->prof_calls > 0 && !plan->events.empty();
   hipEvent_t *ev = nullptr;
   if (prof) {
@@ -269,11 +320,19 @@ ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) 
   }
   for (size_t i = 0; i < plan->p.launches.size(); ++i) {
     const ar::Launch &L = plan->p.launches[i];
-    args.ops = plan->d_ops + plan->op_offset[i];
-    args.nops = static_cast<int32_t>(L.ops.size());
     const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
-    const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
-    hipError_t e = grid.x == 0 ? hipSuccess : ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
+    hipError_t e = hipSuccess;
+    if (grid.x == 0) {
+    } else if (quant) {
+      qargs.ops = plan->d_ops + plan->op_offset[i];
+      qargs.nops = static_cast<int32_t>(L.ops.size());
+      e = ar_dev::launch_q(L.kind, grid, qargs, s);
+    } else {
+      args.ops = plan->d_ops + plan->op_offset[i];
+      args.nops = static_cast<int32_t>(L.ops.size());
+      const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
+      e = ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
+    }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     if (prof) {
       e = hipEventRecord(ev[i + 1], s);
@@ -282,6 +341,10 @@ ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) 
   }
   if (prof) ++plan->prof_logged;
   return AR_OK;
+}
+
+ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
+  return ar_allreduce_ef(plan, rank_bufs, nullptr, stream);
 }
 
 ar_stats_t ar_plan_stats(const ar_plan_t *plan) {
@@ -437,7 +500,7 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
     fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
     return nullptr;
   }
-  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_BFLOAT16_EACH_STEP) {
+  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_BFLOAT16_EACH_STEP && dtype != AR_INT8_EF) {
     fail(AR_ERR_INVALID_ARG, "unknown dtype");
     return nullptr;
   }
@@ -449,7 +512,7 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
   bp->nranks = nranks;
   bp->group_size = group_size;
   bp->dtype = dtype;
-  const int64_t eb = dtype == AR_FLOAT32 ? 4 : 2;
+  const int64_t eb = ar::buffer_elem_bytes(static_cast<ar::Dtype>(dtype));
   std::vector<int64_t> counts(tensor_counts, tensor_counts + ntensors);
   for (int64_t c : counts)
     if (c < 0) {
@@ -509,7 +572,12 @@ ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
 }
 
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream) {
-  return ar_bucket_allreduce_after(bp, rank_arenas, stream, nullptr, nullptr);
+  return ar_bucket_allreduce_ef(bp, rank_arenas, nullptr, stream, nullptr, nullptr);
+}
+
+ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
+                                      void *const *ready_events, void *const *done_events) {
+  return ar_bucket_allreduce_ef(bp, rank_arenas, nullptr, stream, ready_events, done_events);
 }
 
 double ar_overlap_step_time(int nchunks, const double *ready_s, const double *comm_s, double compute_end_s,
@@ -526,9 +594,10 @@ double ar_overlap_step_time(int nchunks, const double *ready_s, const double *co
   return ar::overlap_step_time(nchunks, ready_s, comm_s, compute_end_s, update_s, exposed_s);
 }
 
-ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
-                                      void *const *ready_events, void *const *done_events) {
+ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arenas, void *const *error_arenas,
+                                   void *stream, void *const *ready_events, void *const *done_events) {
   if (!bp || !rank_arenas) return fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
+  if (error_arenas && bp->dtype != AR_INT8_EF) return fail(AR_ERR_INVALID_ARG, "error feedback needs AR_INT8_EF");
   // one scratch shared by all buckets: they run one after another on one stream
   size_t need = 0;
   for (ar_plan_t *pl : bp->plans) need = std::max(need, pl->need_scratch_bytes());
@@ -543,8 +612,8 @@ ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_ar
     if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("bucket scratch: ") + hipGetErrorString(e));
     bp->scratch_bytes = need;
   }
-  const int64_t eb = bp->dtype == AR_FLOAT32 ? 4 : 2;
-  std::vector<void *> ptrs(static_cast<size_t>(bp->nranks));
+  const int64_t eb = ar::buffer_elem_bytes(static_cast<ar::Dtype>(bp->dtype));
+  std::vector<void *> ptrs(static_cast<size_t>(bp->nranks)), eptrs(static_cast<size_t>(bp->nranks));
   for (size_t b = 0; b < bp->plans.size(); ++b) {
     ar_plan_t *pl = bp->plans[b];
     if (pl->external_scratch != bp->scratch) {
@@ -553,14 +622,16 @@ ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_ar
       pl->prepared = pl->prepared && pl->need_scratch_bytes() == 0;
     }
     pl->external_scratch_bytes = bp->scratch_bytes;
-    for (int r = 0; r < bp->nranks; ++r)
+    for (int r = 0; r < bp->nranks; ++r) {
       ptrs[r] = static_cast<char *>(rank_arenas[r]) + bp->bucket_offset[b] * eb;
+      if (error_arenas) eptrs[r] = static_cast<char *>(error_arenas[r]) + bp->bucket_offset[b] * eb;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (ready_events && ready_events[b]) {
       hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ready_events[b]), 0);
       if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     }
-    const ar_status_t st = ar_allreduce(pl, ptrs.data(), stream);
+    const ar_status_t st = ar_allreduce_ef(pl, ptrs.data(), error_arenas ? eptrs.data() : nullptr, stream);
     if (st != AR_OK) return fail(st, "bucket " + std::to_string(b) + ": " + g_err);
     if (done_events && done_events[b]) {
       hipError_t e = hipEventRecord(static_cast<hipEvent_t>(done_events[b]), s);
@@ -591,7 +662,7 @@ ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
   }
   s.nranks = bp->nranks;
   s.group_size = bp->group_size;
-  s.elem_bytes = bp->dtype == AR_FLOAT32 ? 4 : 2;
+  s.elem_bytes = static_cast<uint64_t>(ar::buffer_elem_bytes(static_cast<ar::Dtype>(bp->dtype)));
   s.bytes_sent = bp->bytes_sent.data();
   for (uint64_t b : bp->bytes_sent) {
     s.bytes_sent_max = std::max(s.bytes_sent_max, b);

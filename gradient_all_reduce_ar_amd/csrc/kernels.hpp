@@ -80,6 +80,27 @@ struct KArgs {
   int32_t nops;           // ops in this launch
 };
 
+// Arguments of the blockwise INT8 kernels (kI8EF plans).  Rank r's code slot
+// is codes + r * code_stride (one int8 per element, blocks of 128) and
+// scales + r * scale_stride (one fp32 per block).
+struct QArgs {
+  float *grad[kMaxRanks];  // the caller's fp32 rank buffers
+  float *err[kMaxRanks];   // error-feedback buffers (all NULL: none)
+  int8_t *codes;
+  float *scales;
+  int64_t code_stride, scale_stride;
+  int64_t count;           // elements per rank
+  const DevOp *ops;
+  int32_t nops;
+  int32_t has_err;
+};
+
+// Blocks per tile of the INT8 kernels.
+int64_t q_tile_blocks(int32_t kind);
+
+// Launches one INT8 kernel (encode, reduce, copy or decode) on stream s.
+hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s);
+
 // Whether a step launch takes the streaming (cold) shape: it writes more
 // into rank buffers than the Infinity Cache holds.
 bool is_cold(int64_t written_bytes, bool out_scratch);

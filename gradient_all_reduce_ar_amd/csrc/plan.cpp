@@ -14,7 +14,27 @@
 
 namespace ar {
 
-int64_t elem_bytes(Dtype d) { return d == kF32 ? 4 : 2; }
+int64_t elem_bytes(Dtype d) { return d == kF32 ? 4 : d == kI8EF ? 1 : 2; }
+
+int64_t buffer_elem_bytes(Dtype d) { return (d == kF32 || d == kI8EF) ? 4 : 2; }
+
+int64_t unit_elems(const Plan &p, int64_t lo, int64_t hi) {
+  if (p.dtype != kI8EF) return hi - lo;
+  const int64_t e0 = lo * kQBlock, e1 = std::min(hi * kQBlock, p.count);
+  return e1 > e0 ? e1 - e0 : 0;
+}
+
+uint64_t xfer_bytes(const Plan &p, const Transfer &x) {
+  const uint64_t e = static_cast<uint64_t>(unit_elems(p, x.lo, x.hi)) * static_cast<uint64_t>(elem_bytes(p.dtype));
+  return p.dtype == kI8EF ? e + 4 * static_cast<uint64_t>(x.hi - x.lo) : e;
+}
+
+uint64_t workspace_bytes(const Plan &p) {
+  if (p.dtype == kI8EF)
+    return static_cast<uint64_t>(p.nranks) *
+           (static_cast<uint64_t>(p.code_stride) + 4 * static_cast<uint64_t>(p.scale_stride));
+  return static_cast<uint64_t>(p.nslots) * static_cast<uint64_t>(p.slot_stride) * 4;
+}
 
 namespace {
 
@@ -251,6 +271,8 @@ struct PartialMap {
 std::string lower_steps(Plan &p, bool fuse) {
   p.launches.clear();
   const bool bf = p.dtype == kBF16;  // fp32 partials in scratch
+  const bool q = p.dtype == kI8EF;   // INT8 code slots in the workspace
+  const int32_t copy_fam = q ? kKQCopy : kKCopy;
   PartialMap partial(p.nranks);
   std::vector<bool> finals;  // per launch: all its reduces complete their range
   int max_slot = -1;
@@ -303,9 +325,19 @@ std::string lower_steps(Plan &p, bool fuse) {
         Op op{x.lo, x.hi, kLocNone, kLocNone, kLocNone, kLocNone, 0};
         int32_t kind;
         if (x.kind == kCopy) {
-          kind = kKCopy | static_cast<int32_t>(elem_bytes(p.dtype));
+          kind = q ? kKQCopy : kKCopy | static_cast<int32_t>(elem_bytes(p.dtype));
           op.a = x.src;
           op.o = x.dst;
+        } else if (q) {
+          // blockwise INT8: each rank's code slot holds its running sum
+          kind = kKQReduce;
+          op.a = x.src;
+          op.b = x.dst;
+          op.o = x.dst;
+          if (pair) {
+            op.o2 = x.src;
+            kind |= kFlagO2;
+          }
         } else if (!bf) {
           // fp32, or bf16 rounded at every add: the rank buffers hold the
           // partial sums themselves
@@ -367,7 +399,7 @@ std::string lower_steps(Plan &p, bool fuse) {
     std::vector<Launch> fused;
     for (size_t i = 0; i < p.launches.size(); ++i) {
       Launch &L = p.launches[i];
-      if (finals[i] && i + 1 < p.launches.size() && (p.launches[i + 1].kind & 0xF00) == kKCopy &&
+      if (finals[i] && i + 1 < p.launches.size() && (p.launches[i + 1].kind & 0xF00) == copy_fam &&
           p.launches[i + 1].ops.size() == L.ops.size()) {
         Launch trial = L;
         bool ok = true;
@@ -451,23 +483,33 @@ uint64_t loc_bytes(const Plan &p, int32_t loc, bool bf16_flag) {
 void compute_stats(Plan &p) {
   p.bytes_sent.assign(p.nranks, 0);
   p.cross_group_bytes = 0;
-  const uint64_t eb = static_cast<uint64_t>(elem_bytes(p.dtype));
   for (const Transfer &x : p.xfers) {
-    const uint64_t b = static_cast<uint64_t>(x.hi - x.lo) * eb;
+    const uint64_t b = xfer_bytes(p, x);
     p.bytes_sent[x.src] += b;
     if (x.src / p.group_size != x.dst / p.group_size) p.cross_group_bytes += b;
   }
+  const uint64_t eb = static_cast<uint64_t>(elem_bytes(p.dtype));
   uint64_t h = 0;
   for (const Launch &L : p.launches) {
     const int32_t fam = L.kind & 0xF00;
     for (const Op &op : L.ops) {
       const uint64_t len = static_cast<uint64_t>(op.hi - op.lo);
+      const uint64_t el = static_cast<uint64_t>(unit_elems(p, op.lo, op.hi));
+      const uint64_t outs = op.o2 != kLocNone ? 2 : 1;
       if (fam == kKReduce) {
         const bool obf = L.kind & kFlagOBf;
         h += len * (loc_bytes(p, op.a, L.kind & kFlagABf) + loc_bytes(p, op.b, L.kind & kFlagBBf) +
                     loc_bytes(p, op.o, obf) + loc_bytes(p, op.o2, obf));
       } else if (fam == kKCopy) {
         h += len * 2 * eb;
+      } else if (fam == kKQEncode) {
+        h += el * (4 + 4 + 1 + 4) + 4 * len;  // g, e in; codes, e out; scales
+      } else if (fam == kKQReduce) {
+        h += (el + 4 * len) * (2 + outs);
+      } else if (fam == kKQCopy) {
+        h += (el + 4 * len) * 2;
+      } else if (fam == kKQDecode) {
+        h += el * (1 + 4) + 4 * len;
       } else {
         h += len * 2 * eb * static_cast<uint64_t>(p.nranks);
       }
@@ -476,8 +518,29 @@ void compute_stats(Plan &p) {
   p.hbm_bytes = h;
 }
 
+// Blockwise INT8: encode every rank, run the schedule over code slots,
+// decode every rank.
+std::string lower_quantized(Plan &p, bool fuse) {
+  std::string err = lower_steps(p, fuse);
+  if (!err.empty()) return err;
+  p.nslots = 0;
+  if (p.count == 0) {
+    p.launches.clear();
+    return "";
+  }
+  Launch enc{kKQEncode, {}}, dec{kKQDecode, {}};
+  for (int r = 0; r < p.nranks; ++r) {
+    enc.ops.push_back({0, p.units, r, kLocNone, r, kLocNone, 0});
+    dec.ops.push_back({0, p.units, r, kLocNone, r, kLocNone, 0});
+  }
+  p.launches.insert(p.launches.begin(), std::move(enc));
+  p.launches.push_back(std::move(dec));
+  return "";
+}
+
 std::string lower(Plan &p, Exec exec) {
   p.exec = exec;
+  if (p.dtype == kI8EF && exec == kOnePass) return "one-pass execution is not available for the INT8 dtype";
   if (p.nranks > kMaxExecRanks) {  // described (stats, cost model) but not executable
     p.launches.clear();
     p.nslots = 0;
@@ -486,7 +549,8 @@ std::string lower(Plan &p, Exec exec) {
     return "";
   }
   std::string err;
-  if (exec == kOnePass) err = lower_onepass(p);
+  if (p.dtype == kI8EF) err = lower_quantized(p, exec == kSteps);
+  else if (exec == kOnePass) err = lower_onepass(p);
   else err = lower_steps(p, exec == kSteps);
   if (!err.empty()) return err;
   p.slot_stride = (p.count + 63) / 64 * 64;
@@ -502,7 +566,7 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   if (nranks < 1 || nranks > kMaxPlanRanks) return "nranks must be in [1, 1024]";
   if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
   if (count < 0) return "count must be >= 0";
-  if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each) return "unknown dtype";
+  if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each && dtype != kI8EF) return "unknown dtype";
   if (sched < kRing || sched > kDTree) return "unknown schedule";
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
   if ((sched == kRaben || sched == kRDouble || sched == kDTree) && (nranks & (nranks - 1))) {
@@ -515,12 +579,20 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   p.count = count;
   p.dtype = dtype;
   p.sched = sched;
-  if (sched == kRing) p.nsteps = build_ring(p.xfers, nranks, count);
-  else if (sched == kHier) p.nsteps = build_hier(p.xfers, nranks, group_size, count);
-  else if (sched == kRaben) p.nsteps = build_raben(p.xfers, nranks, count);
-  else if (sched == kRDouble) p.nsteps = build_rdouble(p.xfers, nranks, count);
-  else if (sched == kTree) p.nsteps = build_tree(p.xfers, nranks, count);
-  else p.nsteps = build_dtree(p.xfers, nranks, count);
+  // [SCALING] "Blockwise quantization": the INT8 schedule moves whole blocks,
+  // so its transfers are cut on block boundaries
+  const int64_t units = dtype == kI8EF ? (count + kQBlock - 1) / kQBlock : count;
+  p.units = units;
+  if (dtype == kI8EF) {
+    p.code_stride = (units * kQBlock + 255) / 256 * 256;
+    p.scale_stride = (units + 63) / 64 * 64;
+  }
+  if (sched == kRing) p.nsteps = build_ring(p.xfers, nranks, units);
+  else if (sched == kHier) p.nsteps = build_hier(p.xfers, nranks, group_size, units);
+  else if (sched == kRaben) p.nsteps = build_raben(p.xfers, nranks, units);
+  else if (sched == kRDouble) p.nsteps = build_rdouble(p.xfers, nranks, units);
+  else if (sched == kTree) p.nsteps = build_tree(p.xfers, nranks, units);
+  else p.nsteps = build_dtree(p.xfers, nranks, units);
   std::stable_sort(p.xfers.begin(), p.xfers.end(),
                    [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
   return lower(p, exec);
@@ -535,10 +607,9 @@ double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw
   // [DCN] 7.2.1: rounds run one after another; within a round the slowest
   // transfer sets the time, and every round pays its start-up alpha.
   std::vector<double> slowest(static_cast<size_t>(p.nsteps), 0.0);
-  const double eb = static_cast<double>(elem_bytes(p.dtype));
   for (const Transfer &x : p.xfers) {
     const bool cross = x.src / p.group_size != x.dst / p.group_size;
-    const double t = static_cast<double>(x.hi - x.lo) * eb / (cross ? bw_cross : bw_intra);
+    const double t = static_cast<double>(xfer_bytes(p, x)) / (cross ? bw_cross : bw_intra);
     slowest[x.step] = std::max(slowest[x.step], t);
   }
   double total = 0;
@@ -555,9 +626,8 @@ double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross,
   std::vector<double> link(static_cast<size_t>(p.nsteps), 0.0);
   std::vector<std::vector<double>> egress(static_cast<size_t>(p.nsteps), std::vector<double>(groups, 0.0));
   std::vector<bool> crosses(static_cast<size_t>(p.nsteps), false);
-  const double eb = static_cast<double>(elem_bytes(p.dtype));
   for (const Transfer &x : p.xfers) {
-    const double bytes = static_cast<double>(x.hi - x.lo) * eb;
+    const double bytes = static_cast<double>(xfer_bytes(p, x));
     const bool cross = x.src / p.group_size != x.dst / p.group_size;
     link[x.step] = std::max(link[x.step], bytes / (cross ? bw_cross : bw_intra));
     if (cross) {
@@ -580,7 +650,8 @@ std::string check_hazards(const Plan &p) {
   for (size_t li = 0; li < p.launches.size(); ++li) {
     const Launch &L = p.launches[li];
     const int32_t fam = L.kind & 0xF00;
-    if (fam != kKReduce && fam != kKCopy) continue;  // one-pass ops touch disjoint ranges by construction
+    if (fam != kKReduce && fam != kKCopy && fam != kKQReduce && fam != kKQCopy)
+      continue;  // one-pass, encode and decode ops touch disjoint ranges by construction
     std::vector<std::vector<Acc>> acc(L.ops.size());
     for (size_t i = 0; i < L.ops.size(); ++i) {
       const Op &o = L.ops[i];

@@ -14,8 +14,11 @@
 namespace ar {
 
 // kBF16: fp32 partial sums, one rounding per element; kBF16Each: every
-// partial sum rounded to bf16 as it is formed (bf16 on the wire).
-enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kBF16Each = 2 };
+// partial sum rounded to bf16 as it is formed (bf16 on the wire); kI8EF: fp32
+// buffers, every message blockwise INT8 codes plus one fp32 scale per block,
+// with error feedback (the schedule runs over blocks of kQBlock elements).
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kBF16Each = 2, kI8EF = 3 };
+constexpr int64_t kQBlock = 128;
 enum Sched : int32_t { kRing = 0, kHier = 1, kRaben = 2, kRDouble = 3, kTree = 4, kDTree = 5 };
 enum Exec : int32_t { kSteps = 0, kStepsUnfused = 1, kOnePass = 2 };
 enum XferKind : int32_t { kReduce = 0, kCopy = 1 };
@@ -50,6 +53,16 @@ constexpr int32_t kKHier = 0x400;
 constexpr int32_t kKTree = 0x500;
 constexpr int32_t kKDTree = 0x600;
 constexpr int32_t kFlagABf = 1, kFlagBBf = 2, kFlagOBf = 4, kFlagO2 = 8;
+//   Blockwise INT8 (kI8EF); op ranges count blocks, operands are ranks whose
+//   code slots (codes + scales in the plan's workspace) are meant:
+//   kKQEncode: codes[a] = Q(g_a + e_a), e_a = g_a + e_a - D(codes[a]).
+//   kKQReduce [| kFlagO2]: codes[o] (and codes[o2]) = Q(D(codes[a]) + D(codes[b])).
+//   kKQCopy: codes[o] = codes[a] (codes and scales).
+//   kKQDecode: g_a = D(codes[a]).
+constexpr int32_t kKQEncode = 0x700;
+constexpr int32_t kKQReduce = 0x800;
+constexpr int32_t kKQCopy = 0x900;
+constexpr int32_t kKQDecode = 0xA00;
 
 struct Op {
   int64_t lo, hi;
@@ -76,12 +89,24 @@ struct Plan {
   std::vector<Launch> launches;  // for `exec`
   int32_t nslots = 0;            // fp32 scratch slots used by `launches`
   int64_t slot_stride = 0;       // elements per slot (multiple of 64)
+  int64_t units = 0;             // what transfer ranges count: elements, or blocks (kI8EF)
+  int64_t code_stride = 0;       // kI8EF: bytes of codes per rank slot (multiple of 256)
+  int64_t scale_stride = 0;      // kI8EF: fp32 scales per rank slot (multiple of 64)
   std::vector<uint64_t> bytes_sent;
   uint64_t cross_group_bytes = 0;
   uint64_t hbm_bytes = 0;        // algorithmic device bytes of `launches`
 };
 
+// Bytes of one element on the wire (kI8EF: the code byte; scales extra).
 int64_t elem_bytes(Dtype d);
+// Bytes of one element of the caller's rank buffers.
+int64_t buffer_elem_bytes(Dtype d);
+// Bytes one transfer moves (kI8EF: codes plus 4 bytes of scale per block).
+uint64_t xfer_bytes(const Plan &p, const Transfer &x);
+// Elements covered by the unit range [lo, hi) of a plan.
+int64_t unit_elems(const Plan &p, int64_t lo, int64_t hi);
+// Device workspace of the plan in bytes (fp32 scratch, or kI8EF code slots).
+uint64_t workspace_bytes(const Plan &p);
 
 // Builds the transfers and the launches for `exec`.  Returns an empty string
 // on success, else the reason for failure; *unsupported is set when the

@@ -76,8 +76,23 @@ typedef enum {
 /* AR_BFLOAT16: fp32 partial sums, each element rounded once (see above).
  * AR_BFLOAT16_EACH_STEP: bf16 buffers whose every partial sum is rounded to
  * bf16 (nearest, ties to even) as it is formed, as when each message of the
- * schedule carries bf16 values; no scratch is used. */
-typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_BFLOAT16_EACH_STEP = 2 } ar_dtype_t;
+ * schedule carries bf16 values; no scratch is used.
+ * AR_INT8_EF: compressed all-reduce of fp32 buffers ("Collective
+ * communication", Scaling ML systems ch. 06, "Gradient compression":
+ * INT8 quantization, "Blockwise quantization", "Definition: error feedback
+ * mechanism").  Buffers are cut into blocks of 128 elements (the last may be
+ * short); a block x travels as codes q = round(x / s) (nearest, ties to even,
+ * clamped to [-127, 127]) and one fp32 scale s = max|x| / 127 (a zero block
+ * has s = 0 and codes 0), and is read back as q * s.  Each rank first encodes
+ * x = g + e (e = its error buffer, or 0) and, with error feedback, stores
+ * e = x - q * s.  Every message of the schedule carries codes and scales: a
+ * receiver decodes the message and its own codes, adds in fp32 and
+ * re-encodes the sum; forwarding copies codes.  At the end each rank's
+ * buffer holds the decoded codes it ends with (identical on every rank).
+ * The schedule runs over blocks; the codes live in plan-owned device memory
+ * (about 1.03 bytes per element per rank).  Inputs must be finite.  No
+ * one-pass mode. */
+typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_BFLOAT16_EACH_STEP = 2, AR_INT8_EF = 3 } ar_dtype_t;
 
 typedef enum {
   AR_RING = 0,
@@ -116,16 +131,18 @@ typedef struct {
   int32_t nranks, group_size;
   uint32_t steps;                   /* sequential rounds of the schedule            */
   uint32_t launches;                /* kernel launches per call in the exec mode    */
-  uint64_t count, elem_bytes;
+  uint64_t count, elem_bytes;       /* elem_bytes: of the rank buffers               */
   const uint64_t *bytes_sent;       /* [nranks], plan-owned: logical bytes each rank
-                                       sends, in the buffer's dtype                 */
+                                       sends, in the buffer's dtype (AR_INT8_EF: one
+                                       byte per element plus 4 per block)           */
   uint64_t bytes_sent_max, bytes_sent_total;
   uint64_t cross_group_bytes_total; /* bytes whose sender and receiver lie in
                                        different groups of group_size contiguous
                                        ranks (Data-center networks 7.2.1)          */
   uint64_t hbm_bytes_model;         /* device bytes read + written per call in the
                                        exec mode (algorithmic count)               */
-  uint64_t scratch_bytes;           /* fp32 partial-sum scratch the plan owns       */
+  uint64_t scratch_bytes;           /* device workspace the plan owns: fp32 partial
+                                       sums, or (AR_INT8_EF) codes and scales       */
   int32_t exec;                     /* ar_exec_t in effect                          */
 } ar_stats_t;
 
@@ -143,7 +160,8 @@ typedef struct {
 ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype,
                           ar_schedule_t schedule);
 
-/* Selects the execution mode (see ar_exec_t).  Host only. */
+/* Selects the execution mode (see ar_exec_t).  Host only.  AR_INT8_EF plans
+ * have no one-pass mode (AR_ERR_UNSUPPORTED). */
 ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
 
 /*
@@ -168,6 +186,19 @@ ar_status_t ar_plan_prepare(ar_plan_t *plan);
  * the plan's; AR_ERR_HIP if a launch fails.
  */
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream);
+
+/*
+ * Compressed all-reduce with error feedback (AR_INT8_EF plans; Scaling ML
+ * systems ch. 06, "Definition: error feedback mechanism": each worker keeps a
+ * residual e, sends C(g + e) and keeps g + e - C(g + e)).  error_bufs: host
+ * array of nranks device pointers to fp32 buffers of count elements, 16-byte
+ * aligned, disjoint from each other and from the rank buffers; each is read
+ * and overwritten with the rank's new residual.  error_bufs == NULL runs the
+ * compressed all-reduce without error feedback (as ar_allreduce does).
+ * Rank buffers as for ar_allreduce (fp32).  AR_ERR_INVALID_ARG for a plan of
+ * another dtype with error_bufs != NULL, and for bad pointers.
+ */
+ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream);
 
 /* Statistics of the plan (valid until the plan is destroyed or re-moded). */
 ar_stats_t ar_plan_stats(const ar_plan_t *plan);
@@ -221,8 +252,9 @@ ar_status_t ar_last_status(void);
 /* ---- Plan inspection (host only; used to check the planner on a CPU) ---- */
 
 /* Logical transfers of the schedule: per transfer its round, sender,
- * receiver, element range and kind (0 = reduce, 1 = copy).  Returns the total
- * number of transfers (writes at most cap), or -1 on error. */
+ * receiver, element range and kind (0 = reduce, 1 = copy); for AR_INT8_EF
+ * the range counts 128-element blocks.  Returns the total number of
+ * transfers (writes at most cap), or -1 on error. */
 int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, int32_t *dst,
                           int64_t *lo, int64_t *hi, int32_t *kind, int64_t cap);
 
@@ -231,7 +263,11 @@ int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, in
  * kernel kind code and op count.  ar_plan_launch_ops writes its ops: element
  * range [lo, hi), and operand locations a, b (inputs), o, o2 (outputs):
  * a location 0..nranks-1 is that rank's buffer, 1000+s is fp32 scratch slot s,
- * -1 is unused.  aux is the fold start (one-pass kernels).  Host only.
+ * -1 is unused.  aux is the fold start (one-pass kernels).  AR_INT8_EF plans
+ * use kinds 0x700 (encode rank a), 0x800 (o [and o2 with flag 8] = re-encoded
+ * decode(a) + decode(b)), 0x900 (copy a's codes to o) and 0xA00 (decode a
+ * into its buffer); their ranges count blocks and locations name ranks'
+ * code slots.  Host only.
  */
 int32_t ar_plan_num_launches(const ar_plan_t *plan);
 ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);
@@ -289,6 +325,12 @@ ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, 
  * Figure 4.15.  Both arrays have ar_bucket_count entries. */
 ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
                                       void *const *ready_events, void *const *done_events);
+/* The same for AR_INT8_EF bucket plans with error feedback: error_arenas
+ * (NULL = none) are nranks fp32 arenas laid out like the rank arenas, each
+ * bucket's range used as that bucket's error buffers (see ar_allreduce_ef).
+ * ready_events / done_events as above (either may be NULL). */
+ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arenas, void *const *error_arenas,
+                                   void *stream, void *const *ready_events, void *const *done_events);
 
 /* The overlap model of Primer ch. 4 section 4.7 (Figure 4.15) and
  * Data-center networks 7.6.2: chunk k's collective starts at

@@ -94,3 +94,59 @@ def run(plan, bufs, dtype, group_size):
                 for r in range(n):
                     bufs[r][lo:hi] = res
     return bufs
+
+
+def _q_block(x):
+    """Codes and scale of one block (numpy float32 arithmetic)."""
+    s = np.float32(np.max(np.abs(x)) / np.float32(127.0)) if len(x) else np.float32(0)
+    if s == 0:
+        return np.zeros(len(x), np.int8), s
+    return np.clip(np.rint(x / s), -127, 127).astype(np.int8), s
+
+
+def run_int8(plan, bufs, errs=None):
+    """Executes an int8_ef plan's launch list on float32 host arrays."""
+    n = len(bufs)
+    count = len(bufs[0])
+    Q = B.QBLOCK
+    nblk = (count + Q - 1) // Q
+    codes = [np.zeros(nblk * Q, np.int8) for _ in range(n)]
+    scales = [np.full(nblk, np.nan, np.float32) for _ in range(n)]
+
+    def dec(r, blk):
+        return (codes[r][blk * Q:(blk + 1) * Q].astype(np.float32) * scales[r][blk]).astype(np.float32)
+
+    def put(r, blk, x):
+        q, s = _q_block(x)
+        codes[r][blk * Q:(blk + 1) * Q] = q
+        scales[r][blk] = s
+
+    for i in range(B.ar_plan_num_launches(plan)):
+        kind, _ = B.ar_plan_launch_info(plan, i)
+        ops = B.ar_plan_launch_ops(plan, i)
+        fam = kind & 0xF00
+        for k in range(len(ops["lo"])):
+            lo, hi = int(ops["lo"][k]), int(ops["hi"][k])
+            a, b, o, o2 = (int(ops[x][k]) for x in ("a", "b", "o", "o2"))
+            for blk in range(lo, hi):
+                e0, e1 = blk * Q, min(count, (blk + 1) * Q)
+                if fam == B.KIND_QENCODE:
+                    x = np.zeros(Q, np.float32)
+                    x[:e1 - e0] = bufs[a][e0:e1] + (errs[a][e0:e1] if errs is not None else np.float32(0))
+                    put(a, blk, x)
+                    if errs is not None:
+                        errs[a][e0:e1] = (x[:e1 - e0] - dec(a, blk)[:e1 - e0]).astype(np.float32)
+                elif fam == B.KIND_QREDUCE:
+                    x = (dec(a, blk) + dec(b, blk)).astype(np.float32)
+                    x[e1 - e0:] = 0
+                    put(o, blk, x)
+                    if kind & 8:
+                        put(o2, blk, x)
+                elif fam == B.KIND_QCOPY:
+                    codes[o][e0:e0 + Q] = codes[a][e0:e0 + Q]
+                    scales[o][blk] = scales[a][blk]
+                elif fam == B.KIND_QDECODE:
+                    bufs[a][e0:e1] = dec(a, blk)[:e1 - e0]
+                else:
+                    raise AssertionError(f"kind {kind:#x} in an int8 plan")
+    return bufs

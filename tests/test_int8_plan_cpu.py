@@ -1,0 +1,154 @@
+"""The planner's blockwise INT8 (error-feedback) plans, checked on the CPU.
+
+* Transfers are the schedule's messages over 128-element blocks (the
+  oracle's message list for the block count).
+* Each message carries one byte per element plus a 4-byte scale per block
+  ("Collective communication", Scaling ML systems ch. 06, "Blockwise
+  quantization": d + 4d/b bytes, a 3.88x compression for b = 128).
+* The launch list, executed by the numpy interpreter, equals the oracle bit
+  for bit, residuals included, in both step modes.
+* Argument checks of ar_allreduce_ef run before anything is launched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_ar_amd import _binding as B
+from tests import plan_interp
+
+Q = B.QBLOCK
+SCHEDS = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
+         [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (6, 2), (8, 4), (16, 4), (9, 3))] + \
+         [("rabenseifner", n, 1) for n in (2, 4, 8, 16)] + \
+         [("recursive_doubling", n, 1) for n in (2, 4, 16)] + \
+         [("tree", n, 1) for n in (2, 3, 5, 8, 13)] + \
+         [("double_tree", n, 1) for n in (2, 4, 8, 16)]
+
+
+def _sorted(d):
+    order = np.lexsort((d["src"], d["step"]))
+    return {k: v[order] for k, v in d.items()}
+
+
+def _msg_bytes(count, lo, hi):
+    return max(0, min(hi * Q, count) - lo * Q) + 4 * (hi - lo)
+
+
+@pytest.mark.parametrize("sched,n,g", SCHEDS)
+def test_transfers_are_block_messages(sched, n, g):
+    for count in (0, 1, Q, Q + 1, 1000, 37 * Q + 5):
+        nblk = -(-count // Q)
+        p = B.ar_plan_create(n, g, count, "int8_ef", sched)
+        try:
+            mine = _sorted(B.ar_plan_transfers(p))
+            ref = _sorted(oracle.messages(n, nblk, sched, group_size=g))
+            for k in ("step", "src", "dst", "lo", "hi", "kind"):
+                np.testing.assert_array_equal(mine[k], ref[k], err_msg=f"{sched} n={n} count={count} {k}")
+            st = B.ar_plan_stats(p)
+            want = [0] * n
+            for s, lo, hi in zip(ref["src"], ref["lo"], ref["hi"]):
+                want[int(s)] += _msg_bytes(count, int(lo), int(hi))
+            assert st["bytes_sent"] == want
+            assert st["elem_bytes"] == 4
+            assert st["steps"] == oracle.stats(n, nblk, "fp32", sched, group_size=g)[2]
+        finally:
+            B.ar_plan_destroy(p)
+
+
+def test_page_compression_ratio():
+    """fp32 bytes over INT8 bytes of the same schedule: 4b / (b + 4) = 3.88."""
+    count = 4096 * Q
+    for sched in ("ring", "rabenseifner", "tree"):
+        pf = B.ar_plan_create(8, 1, count, "fp32", sched)
+        pq = B.ar_plan_create(8, 1, count, "int8_ef", sched)
+        try:
+            ratio = B.ar_plan_stats(pf)["bytes_sent_total"] / B.ar_plan_stats(pq)["bytes_sent_total"]
+        finally:
+            B.ar_plan_destroy(pf)
+            B.ar_plan_destroy(pq)
+        assert ratio == pytest.approx(4 * Q / (Q + 4), rel=1e-12)
+        assert round(ratio, 2) == 3.88
+
+
+def test_cost_model_prices_codes_and_scales():
+    n, count = 8, 1000 * Q + 17
+    p = B.ar_plan_create(n, 1, count, "int8_ef", "ring")
+    try:
+        ref = oracle.messages(n, -(-count // Q), "ring")
+        worst = {}
+        for st, lo, hi in zip(ref["step"], ref["lo"], ref["hi"]):
+            worst[int(st)] = max(worst.get(int(st), 0), _msg_bytes(count, int(lo), int(hi)) / 50e9)
+        want = sum(2e-6 + t for t in worst.values())
+        assert B.ar_plan_cost_alpha_beta(p, 2e-6, 50e9, 50e9) == pytest.approx(want, rel=1e-12)
+    finally:
+        B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n,g", SCHEDS)
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused"])
+def test_launch_list_matches_oracle(sched, n, g, mode):
+    rng = np.random.default_rng(n * 7 + g)
+    for count in (0, 3, Q, 5 * Q + 77, 11 * Q):
+        xs = [(rng.standard_normal(count) * np.exp(rng.standard_normal(count))).astype(np.float32)
+              for _ in range(n)]
+        es = [(rng.standard_normal(count) * 1e-2).astype(np.float32) for _ in range(n)]
+        for with_err in (False, True):
+            ref_b = [x.copy() for x in xs]
+            ref_e = [e.copy() for e in es] if with_err else None
+            oracle.run_int8ef(ref_b, sched, errs=ref_e, group_size=g)
+            p = B.ar_plan_create(n, g, count, "int8_ef", sched)
+            try:
+                B.ar_plan_set_exec(p, mode)
+                got_b = [x.copy() for x in xs]
+                got_e = [e.copy() for e in es] if with_err else None
+                plan_interp.run_int8(p, got_b, got_e)
+            finally:
+                B.ar_plan_destroy(p)
+            for r in range(n):
+                msg = f"{sched} n={n} g={g} {mode} count={count} err={with_err} rank={r}"
+                np.testing.assert_array_equal(got_b[r].view(np.uint32), ref_b[r].view(np.uint32), err_msg=msg)
+                if with_err:
+                    np.testing.assert_array_equal(got_e[r].view(np.uint32), ref_e[r].view(np.uint32), err_msg=msg)
+
+
+def test_launch_shape():
+    """Encode first, decode last, one launch per round in between (the
+    completing reduce fused with the first forwarding copy), workspace of
+    one code byte per element and one scale per block, per rank."""
+    n, count = 4, 10 * Q + 1
+    p = B.ar_plan_create(n, 1, count, "int8_ef", "ring")
+    try:
+        kinds = [B.ar_plan_launch_info(p, i)[0] for i in range(B.ar_plan_num_launches(p))]
+        assert kinds[0] == B.KIND_QENCODE and kinds[-1] == B.KIND_QDECODE
+        assert [k & 0xF00 for k in kinds[1:-1]] == [B.KIND_QREDUCE] * (n - 1) + [B.KIND_QCOPY] * (n - 2)
+        assert kinds[n - 1] & 8  # fused: the completing reduce also writes the next rank
+        st = B.ar_plan_stats(p)
+        nblk = 11
+        assert st["scratch_bytes"] == n * ((nblk * Q + 255) // 256 * 256 + 4 * ((nblk + 63) // 64 * 64))
+    finally:
+        B.ar_plan_destroy(p)
+
+
+def test_errors():
+    p = B.ar_plan_create(4, 1, 1024, "int8_ef", "ring")
+    pf = B.ar_plan_create(4, 1, 1024, "fp32", "ring")
+    try:
+        with pytest.raises(B.ArError) as ei:
+            B.ar_plan_set_exec(p, "onepass")
+        assert ei.value.status == B.AR_ERR_UNSUPPORTED
+        bufs = [1 << 20, 2 << 20, 3 << 20, 4 << 20]
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce_ef(pf, bufs, [5 << 20, 6 << 20, 7 << 20, 8 << 20])
+        assert ei.value.status == B.AR_ERR_INVALID_ARG and "INT8" in str(ei.value)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce_ef(p, bufs, [5 << 20, 0, 7 << 20, 8 << 20])
+        assert "error buffer 1 is NULL" in str(ei.value)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce_ef(p, bufs, [5 << 20, (6 << 20) + 8, 7 << 20, 8 << 20])
+        assert "aligned" in str(ei.value)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_allreduce_ef(p, bufs, [5 << 20, (2 << 20) + 1024, 7 << 20, 8 << 20])
+        assert "overlap" in str(ei.value)
+    finally:
+        B.ar_plan_destroy(p)
+        B.ar_plan_destroy(pf)
