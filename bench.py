@@ -1,6 +1,6 @@
 """Benchmark: 16-rank, 192 MiB-per-rank fp32 ring all-reduce on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5r16|c5g16|c5r64|c5g64]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c2q|c3|c3e|c4|c5r16|c5g16|c5r64|c5g64|overlap]
                 [--exec steps|steps_unfused|onepass]
 
 A step is one whole all-reduce (every launch of the schedule) over the N
@@ -38,6 +38,9 @@ WORKLOADS = {
            "fp32 accumulate", "ring", 16, 8, "bf16", 2 * 12288 * 4096),
     "c3e": ("ring all-reduce, 16 virtual ranks x 192 MiB bf16, N(0,1e-3), every partial sum rounded to bf16",
             "ring", 16, 8, "bf16_each", 2 * 12288 * 4096),
+    "c2q": ("ring all-reduce, 16 virtual ranks x 192 MiB fp32, blockwise INT8 messages (128-element blocks, "
+            "fp32 scales) with error feedback, N(0,1e-3) gradients and residuals",
+            "ring", 16, 8, "int8_ef", 12288 * 4096),
     "c4": ("hierarchical all-reduce, 2 groups x 8 ranks x 192 MiB fp32, N(0,1e-3)",
            "hierarchical", 16, 8, "fp32", 12288 * 4096),
     "c5r16": ("Rabenseifner, 16 ranks, bf16, 300 lognormal tensors in 25 MiB buckets", "rabenseifner", 16, 1,
@@ -49,7 +52,8 @@ WORKLOADS = {
 }
 
 KIND_NAMES = {0x100: "chunk_reduce", 0x200: "chunk_copy", 0x300: "onepass_ring", 0x400: "onepass_hier",
-              0x500: "onepass_tree"}
+              0x500: "onepass_tree", 0x600: "onepass_dtree", 0x700: "q_encode", 0x800: "q_reduce", 0x900: "q_copy",
+              0xA00: "q_decode"}
 
 
 def kernel_label(kind):
@@ -59,6 +63,12 @@ def kernel_label(kind):
         return f"chunk_reduce<{kind & 0xF}>"
     if fam == 0x200:
         return f"chunk_copy<{kind & 0xFF}>"
+    if fam == 0x800:
+        return f"q_reduce<{'true' if kind & 8 else 'false'}>"
+    if fam >= 0x700:
+        return KIND_NAMES[fam]
+    if kind & 3 == 3:  # one-pass fold of an INT8 plan
+        return "q_" + KIND_NAMES[fam]
     return f"{KIND_NAMES[fam]}<{'bf16' if kind & 1 else 'fp32'}>"
 
 
@@ -66,12 +76,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def launch_bytes(B, plan, i, nranks, elem):
+def launch_bytes(B, plan, i, nranks, elem, count):
     """Algorithmic device bytes of launch i (read + write of every operand)."""
     kind, _ = B.ar_plan_launch_info(plan, i)
     ops = B.ar_plan_launch_ops(plan, i)
     n = (ops["hi"] - ops["lo"]).astype("int64")
     fam = kind & 0xF00
+    if fam < B.KIND_QENCODE and fam not in (B.KIND_REDUCE, B.KIND_COPY) and kind & 3 == 3:
+        # one-pass INT8 fold: g, e in; e, result out, per rank; ranges count blocks
+        el = int(sum(max(0, min(int(h) * B.QBLOCK, count) - int(lo) * B.QBLOCK)
+                     for lo, h in zip(ops["lo"], ops["hi"])))
+        return el * 16 * nranks, kind
+    if fam >= B.KIND_QENCODE:
+        # blockwise INT8: op ranges count 128-element blocks
+        blocks = int(n.sum())
+        el = int(sum(max(0, min(int(h) * B.QBLOCK, count) - int(lo) * B.QBLOCK)
+                     for lo, h in zip(ops["lo"], ops["hi"])))
+        if fam == B.KIND_QENCODE:
+            return el * 13 + 4 * blocks, kind  # g, e in; codes, e out; scales
+        if fam == B.KIND_QREDUCE:
+            return (el + 4 * blocks) * (4 if kind & 8 else 3), kind
+        if fam == B.KIND_QCOPY:
+            return (el + 4 * blocks) * 2, kind
+        return el * 5 + 4 * blocks, kind  # decode: codes, scales in; fp32 out
     if fam == B.KIND_REDUCE:
         if elem == 4:
             per = 3 * 4 + (4 if kind & 8 else 0)
@@ -138,9 +165,10 @@ def main():
     desc, sched, n, group, dtype, count = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    elem = 4 if dtype == "fp32" else 2
-    view = np.float32 if dtype == "fp32" else np.int16
-    gen_dtype = "fp32" if dtype == "fp32" else "bf16"
+    quant = dtype == "int8_ef"
+    elem = 4 if dtype in ("fp32", "int8_ef") else 2
+    view = np.float32 if elem == 4 else np.int16
+    gen_dtype = "fp32" if elem == 4 else "bf16"
 
     if args.calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -167,12 +195,35 @@ def main():
         host = workloads.normal_inputs(n, count, seed=0, dtype=gen_dtype)
         count_logical = count
     bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
+    errs = None
+    if quant:
+        # every call multiplies the values by about N (in place); 28 calls from
+        # N(0, 1e-3) stay finite, the range the quantizer is defined on
+        if args.warmup + args.steps > 28:
+            print("c2q: warmup + steps must be <= 28 (values grow N-fold per in-place call and must stay "
+                  "finite)", file=sys.stderr)
+            sys.exit(2)
+        err_host = workloads.normal_inputs(n, count, seed=1, dtype="fp32")
+        errs = [torch.from_numpy(h).to(dev) for h in err_host]
     torch.cuda.synchronize()
+
+    def reset_inputs():
+        """Untimed: restore the initial values (before the comparison run)."""
+        for b_, h_ in zip(bufs, host):
+            b_.copy_(torch.from_numpy(h_.view(view)))
+        if quant:
+            for e_, h_ in zip(errs, err_host):
+                e_.copy_(torch.from_numpy(h_))
+        torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s: {desc}")
 
     stream = torch.cuda.current_stream(dev)
-    run = (lambda: B.ar_bucket_allreduce(plan, bufs, stream)) if bucketed else \
-        (lambda: B.ar_allreduce(plan, bufs, stream))
+    if bucketed:
+        run = lambda: B.ar_bucket_allreduce(plan, bufs, stream)  # noqa: E731
+    elif quant:
+        run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
+    else:
+        run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
     subplans = []
     if bucketed:
         # per-bucket plans are internal; profile by timing each call with events
@@ -210,7 +261,7 @@ def main():
     if not bucketed:
         times = B.ar_plan_launch_times(plan)
         nl = B.ar_plan_num_launches(plan)
-        lb = [launch_bytes(B, plan, i, n, elem) for i in range(nl)]
+        lb = [launch_bytes(B, plan, i, n, elem, count) for i in range(nl)]
         for call in times:
             for i, t in enumerate(call):
                 nbytes, kind = lb[i]
@@ -242,6 +293,7 @@ def main():
     if not args.no_extra and args.exec != "onepass" and not bucketed:
         B.ar_plan_set_profiling(plan, 0)
         B.ar_plan_set_exec(plan, "onepass")
+        reset_inputs()
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
@@ -261,7 +313,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        del bufs
+        del bufs, errs
         torch.cuda.empty_cache()
         if bucketed:
             sample_buckets = list(range(min(4, B.ar_bucket_count(plan))))
@@ -273,6 +325,12 @@ def main():
                 done += cnt
             cpu_s = time.perf_counter() - t_c
             sample = f"first {len(sample_buckets)} buckets ({done} elements per rank), one all-reduce each"
+        elif quant:
+            t_c = time.perf_counter()
+            oracle.run_int8ef(host, sched, errs=err_host, group_size=group)
+            cpu_s = time.perf_counter() - t_c
+            done = count
+            sample = "the whole workload, one compressed all-reduce with error feedback"
         else:
             t_c = time.perf_counter()
             oracle.run(host, dtype, sched, group_size=group)
@@ -294,7 +352,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16 (f32 accumulate)", "bf16_each": "bf16 (rounded each add)"}[dtype],
+        "dtype": {"fp32": "f32", "bf16": "bf16 (f32 accumulate)", "bf16_each": "bf16 (rounded each add)",
+                  "int8_ef": "int8 codes + f32 block scales (f32 add per hop)"}[dtype],
         "data": "synthetic",
         "config": {
             "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,
@@ -311,6 +370,12 @@ def main():
     }
     if extra:
         out["config"]["compare"] = extra
+    if quant:
+        pf = B.ar_plan_create(n, group, count, "fp32", sched)
+        sent_f32 = B.ar_plan_stats(pf)["bytes_sent_total"]
+        B.ar_plan_destroy(pf)
+        out["config"]["wire_bytes_total"] = stats["bytes_sent_total"]
+        out["config"]["wire_compression_vs_fp32"] = round(sent_f32 / stats["bytes_sent_total"], 4)
     if bucketed:
         out["config"]["buckets"] = B.ar_bucket_count(plan)
         B.ar_bucket_plan_destroy(plan)

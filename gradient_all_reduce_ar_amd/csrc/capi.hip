@@ -81,6 +81,8 @@ namespace {
 
 bool is_quant_kind(int32_t kind) {
   const int32_t fam = kind & 0xF00;
+  if (fam == ar::kKRing || fam == ar::kKHier || fam == ar::kKTree || fam == ar::kKDTree)
+    return (kind & 3) == ar::kI8EF;  // one-pass fold of an INT8 plan
   return fam == ar::kKQEncode || fam == ar::kKQReduce || fam == ar::kKQCopy || fam == ar::kKQDecode;
 }
 
@@ -257,8 +259,6 @@ ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t d
 ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
   if (exec == static_cast<ar_exec_t>(plan->p.exec) && plan->prepared) return AR_OK;
-  if (plan->p.dtype == ar::kI8EF && exec == AR_EXEC_ONEPASS)
-    return fail(AR_ERR_UNSUPPORTED, "one-pass execution is not available for AR_INT8_EF");
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
@@ -304,6 +304,8 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
     qargs.scale_stride = plan->p.scale_stride;
     qargs.count = plan->p.count;
     qargs.has_err = error_bufs != nullptr;
+    qargs.nranks = plan->p.nranks;
+    qargs.group_size = plan->p.group_size;
   } else {
     for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
     args.scratch = plan->external_scratch ? plan->external_scratch : plan->scratch;

@@ -93,12 +93,14 @@ struct QArgs {
   const DevOp *ops;
   int32_t nops;
   int32_t has_err;
+  int32_t nranks, group_size;
 };
 
 // Blocks per tile of the INT8 kernels.
 int64_t q_tile_blocks(int32_t kind);
 
-// Launches one INT8 kernel (encode, reduce, copy or decode) on stream s.
+// Launches one INT8 kernel (encode, reduce, copy, decode, or a one-pass fold
+// kind kKRing / kKHier / kKTree / kKDTree) on stream s.
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s);
 
 // Whether a step launch takes the streaming (cold) shape: it writes more

@@ -30,6 +30,7 @@ uint64_t xfer_bytes(const Plan &p, const Transfer &x) {
 }
 
 uint64_t workspace_bytes(const Plan &p) {
+  if (p.dtype == kI8EF && p.exec == kOnePass) return 0;  // codes stay in registers
   if (p.dtype == kI8EF)
     return static_cast<uint64_t>(p.nranks) *
            (static_cast<uint64_t>(p.code_stride) + 4 * static_cast<uint64_t>(p.scale_stride));
@@ -430,13 +431,15 @@ std::string lower_steps(Plan &p, bool fuse) {
 std::string lower_onepass(Plan &p) {
   p.launches.clear();
   p.nslots = 0;
-  if (p.nranks == 1 || p.count == 0) return "";
+  // INT8 plans encode and decode even on one rank; op ranges count p.units
+  // (elements, or blocks for INT8)
+  if ((p.nranks == 1 && p.dtype != kI8EF) || p.count == 0) return "";
   const int32_t dt = p.dtype;
-  if (p.sched == kRing) {
+  if (p.sched == kRing || p.nranks == 1) {
     // element in chunk c: ((x_c + x_{c+1}) + ...) + x_{c+N-1} -- chunk c is
     // first sent by rank c at reduce-scatter step 0 and gains one rank per step
     Launch L{kKRing | dt, {}};
-    const Cut cut{0, p.count, p.nranks};
+    const Cut cut{0, p.units, p.nranks};
     for (int c = 0; c < p.nranks; ++c)
       if (cut.hi(c) > cut.lo(c)) L.ops.push_back({cut.lo(c), cut.hi(c), kLocNone, kLocNone, kLocNone, kLocNone, c});
     p.launches.push_back(std::move(L));
@@ -445,7 +448,7 @@ std::string lower_onepass(Plan &p) {
     // j of the slice folds the group partials as a ring starting at group j
     const int G = p.group_size, M = p.nranks / p.group_size;
     Launch L{kKHier | dt, {}};
-    const Cut slices{0, p.count, G};
+    const Cut slices{0, p.units, G};
     for (int k = 0; k < G; ++k) {
       const Cut sub{slices.lo(k), slices.hi(k) - slices.lo(k), M};
       for (int jj = 0; jj < M; ++jj)
@@ -458,7 +461,7 @@ std::string lower_onepass(Plan &p) {
     // half h follows tree h: tree 1 = x_0 + D(N/2, N/2), tree 2 = x_{N-1} +
     // D(N/2 - 1, N/2), D(c, b) = (x_c + D(c - b/2, b/2)) + D(c + b/2, b/2)
     Launch L{kKDTree | dt, {}};
-    const Cut halves{0, p.count, 2};
+    const Cut halves{0, p.units, 2};
     for (int h = 0; h < 2; ++h)
       if (halves.hi(h) > halves.lo(h))
         L.ops.push_back({halves.lo(h), halves.hi(h), kLocNone, kLocNone, kLocNone, kLocNone, h});
@@ -468,7 +471,7 @@ std::string lower_onepass(Plan &p) {
     // ranks in index order, ((x0 + x1) + (x2 + x3)) + ...; the binomial tree
     // gives the same when N is 2^k and a left-complete tree otherwise
     Launch L{kKTree | dt, {}};
-    L.ops.push_back({0, p.count, kLocNone, kLocNone, kLocNone, kLocNone, 0});
+    L.ops.push_back({0, p.units, kLocNone, kLocNone, kLocNone, kLocNone, 0});
     p.launches.push_back(std::move(L));
   }
   return "";
@@ -510,6 +513,8 @@ void compute_stats(Plan &p) {
         h += (el + 4 * len) * 2;
       } else if (fam == kKQDecode) {
         h += el * (1 + 4) + 4 * len;
+      } else if (p.dtype == kI8EF) {
+        h += el * 16 * static_cast<uint64_t>(p.nranks);  // g, e in; e, result out, per rank
       } else {
         h += len * 2 * eb * static_cast<uint64_t>(p.nranks);
       }
@@ -540,7 +545,6 @@ std::string lower_quantized(Plan &p, bool fuse) {
 
 std::string lower(Plan &p, Exec exec) {
   p.exec = exec;
-  if (p.dtype == kI8EF && exec == kOnePass) return "one-pass execution is not available for the INT8 dtype";
   if (p.nranks > kMaxExecRanks) {  // described (stats, cost model) but not executable
     p.launches.clear();
     p.nslots = 0;
@@ -549,8 +553,8 @@ std::string lower(Plan &p, Exec exec) {
     return "";
   }
   std::string err;
-  if (p.dtype == kI8EF) err = lower_quantized(p, exec == kSteps);
-  else if (exec == kOnePass) err = lower_onepass(p);
+  if (exec == kOnePass) err = lower_onepass(p);
+  else if (p.dtype == kI8EF) err = lower_quantized(p, exec == kSteps);
   else err = lower_steps(p, exec == kSteps);
   if (!err.empty()) return err;
   p.slot_stride = (p.count + 63) / 64 * 64;

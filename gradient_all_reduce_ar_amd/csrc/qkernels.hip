@@ -6,18 +6,28 @@
 // q * s ("Blockwise quantization"); each worker sends C(g + e) and keeps
 // e = g + e - C(g + e) ("Definition: error feedback mechanism").
 //
-// Mapping.  Half a wavefront (32 lanes) owns one block, 4 consecutive
-// elements per lane, so a block's fp32 values are one 512-byte span (one
-// 16-byte access per lane) and its codes one 128-byte span (4 bytes per
-// lane); the block maximum is a 5-step butterfly within the half-wave.  A
-// 256-thread workgroup takes 8 blocks per pass and U passes (a tile of 8U
-// blocks), tiles aligned to 8U blocks in absolute block coordinates.
+// Mapping.  Encode and decode (fp32 side): half a wavefront (32 lanes) owns
+// one block, 4 consecutive elements per lane, so a block's fp32 values are
+// one 512-byte span (one 16-byte access per lane).  Reduce (codes only): 8
+// lanes own one block, 16 codes (one 16-byte access) per lane.  A block's
+// maximum is a DPP butterfly within its lanes (row permutes, plus one
+// swizzle across the two rows of a half-wave), on the bit patterns of |x|,
+// which order like the values.  Tiles are aligned to their block count in
+// absolute block coordinates.
 //
-// Exactness.  x / s and max|x| / 127 are IEEE divisions (the library is built
-// with correctly rounded fp32 division), rounding is rintf (nearest, ties to
-// even), decode is one fp32 multiply and every sum one fp32 add, with no
-// contraction: each code and scale equals a step-by-step execution of the
-// schedule on the CPU.  Elements past `count` in the last block count as 0.
+// Exactness.  The code of x is rint(RN(x / s)) with s = RN(max|x| / 127),
+// rounding to nearest even, clamped to [-127, 127]; s comes from an
+// fma-corrected product (see make_scale), the rare exact quotients below
+// from IEEE division (the library is built with correctly rounded fp32
+// division).  The kernels
+// reach it through t = x * rcp(s): |x / s| <= 127 (1 + 2^-24) and rcp is
+// within 1 ulp, so t is within 2^-22 |x / s| < 3.1e-5 of RN(x / s); when t
+// lies more than 2^-12 from a half-integer both round to the same integer,
+// otherwise (and when s is outside [2^-125, 2^125], where rcp could leave the
+// normal range) the code is taken from the exact division.  Decode is one
+// fp32 multiply and every sum one fp32 add, with no contraction: each code
+// and scale equals a step-by-step execution of the schedule on the CPU.
+// Elements past `count` in the last block count as 0.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -27,47 +37,101 @@
 #ifndef AR_Q_UNROLL
 #define AR_Q_UNROLL 2
 #endif
+#ifndef AR_Q_ENC_UNROLL
+#define AR_Q_ENC_UNROLL 1  // blocks per half-wave of the encode kernel
+#endif
+#ifndef AR_Q_OP_BLOCK
+#define AR_Q_OP_BLOCK 512  // threads per workgroup of the one-pass kernels
+#endif
+#ifndef AR_Q_FOLD_BATCH
+#define AR_Q_FOLD_BATCH 4  // ranks whose inputs the one-pass ring loads ahead
+#endif
 
 namespace ar_dev {
 
 namespace {
 
 constexpr int kQB = static_cast<int>(ar::kQBlock);  // elements per block
-constexpr int kHalf = 32;                            // lanes per block
+constexpr int kHalf = 32;                            // lanes per block (encode, decode)
 constexpr int kBlocksPerPass = AR_BLOCK / kHalf;     // 8
 constexpr int kU = AR_Q_UNROLL;
 constexpr int kTileBlocks = kBlocksPerPass * kU;
+constexpr int kEU = AR_Q_ENC_UNROLL;
+constexpr int kEncTileBlocks = kBlocksPerPass * kEU;
+constexpr int kRLanes = 8;                           // lanes per block (reduce): 16 codes each
+constexpr int kRBlocksPerPass = AR_BLOCK / kRLanes;  // 32
+constexpr int kRTileBlocks = kRBlocksPerPass * kU;
 constexpr int kCopyTileBlocks = AR_BLOCK * 16 / kQB;  // one 16-byte chunk of codes per thread
-static_assert(kQB == kHalf * 4, "a half-wave covers one block, 4 elements per lane");
+static_assert(kQB == kHalf * 4 && kQB == kRLanes * 16, "lane shapes cover one block");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float half_wave_max(float m) {
-#pragma unroll
-  for (int off = kHalf / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kHalf));
-  return m;
+// max(v, v of another lane) for a DPP lane pattern (all source lanes are
+// active: a block's lanes are live or idle together).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  return max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false)));
+}
+// Over each aligned group of 8 lanes: quad swaps 1 and 2, then the mirror
+// within each half-row.
+__device__ __forceinline__ uint32_t max8(uint32_t v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  return dpp_max<0x141>(v);  // row_half_mirror
+}
+// Over each aligned group of 32 lanes: then the row mirror and a swap of the
+// two rows.
+__device__ __forceinline__ uint32_t max32(uint32_t v) {
+  v = dpp_max<0x140>(max8(v));  // row_mirror
+  return max(v, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F)));  // lane ^ 16
 }
 
-__device__ __forceinline__ float abs_max4(const float x[4]) {
-  return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+// Scale of a block from the maximum |x| (bits) and its fast-path reciprocal.
+struct Scale {
+  float s, rs;
+  bool fast;
+};
+// s = RN(m / 127) without a division: q0 = RN(m * RN(1/127)) is within an
+// ulp, the fma residual m - 127 q0 is exact, and one fma correction rounds
+// to RN(m / 127) -- checked for every non-negative finite float m.
+__device__ __forceinline__ Scale make_scale(uint32_t max_bits) {
+  constexpr float kInv127 = 1.0f / 127.0f;
+  const float m = __uint_as_float(max_bits);
+  const float q0 = m * kInv127;
+  Scale r;
+  r.s = __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, m), kInv127, q0);
+  r.fast = r.s >= 0x1p-125f && r.s <= 0x1p125f;
+  r.rs = __builtin_amdgcn_rcpf(r.s);
+  return r;
 }
 
-// Codes of 4 values under scale s, packed little-endian into one word.
-__device__ __forceinline__ uint32_t quant4(const float x[4], float s, int q[4]) {
-  uint32_t packed = 0;
+// Codes (as floats, -127..127) of N values under scale sc; s == 0 gives 0.
+template <int N>
+__device__ __forceinline__ void quantize(const float *x, const Scale &sc, float *k) {
+  bool slow = !sc.fast;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int v = 0;
-    if (s != 0.0f) {
-      float r = rintf(x[k] / s);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      v = static_cast<int>(r);
-    }
-    q[k] = v;
-    packed |= (static_cast<uint32_t>(v) & 0xffu) << (8 * k);
+  for (int i = 0; i < N; ++i) {
+    const float t = x[i] * sc.rs;
+    k[i] = rintf(t);
+    slow |= fabsf(fabsf(t - k[i]) - 0.5f) < 0x1p-12f;
   }
-  return packed;
+  if (__builtin_expect(slow, 0)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) k[i] = sc.s == 0.0f ? 0.0f : rintf(x[i] / sc.s);
+  }
+  // clamp; + 0 turns a code of -0 into +0, as an integer code decodes
+#pragma unroll
+  for (int i = 0; i < N; ++i) k[i] = __builtin_amdgcn_fmed3f(k[i], -127.0f, 127.0f) + 0.0f;
+}
+
+__device__ __forceinline__ uint32_t pack4(const float *k) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= (static_cast<uint32_t>(static_cast<int>(k[i])) & 0xffu) << (8 * i);
+  return w;
 }
 
 __device__ __forceinline__ float code(uint32_t w, int k) {
@@ -114,13 +178,13 @@ __global__ void __launch_bounds__(AR_BLOCK) q_encode(QArgs a) {
   const float *g = a.grad[r];
   float *e = a.err[r];
   int8_t *codes = a.codes + r * a.code_stride;
-  float *sc = a.scales + r * a.scale_stride;
-  const int64_t t = op.lo / kTileBlocks + blockIdx.x;
-  float x[kU][4];
-  bool live[kU];
+  float *scl = a.scales + r * a.scale_stride;
+  const int64_t t = op.lo / kEncTileBlocks + blockIdx.x;
+  float x[kEU][4];
+  bool live[kEU];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+  for (int u = 0; u < kEU; ++u) {
+    const int64_t b = t * kEncTileBlocks + u * kBlocksPerPass + sub;
     live[u] = b >= op.lo && b < op.hi;
     const int64_t e0 = b * kQB + lane * 4;
     if (live[u]) {
@@ -134,18 +198,20 @@ __global__ void __launch_bounds__(AR_BLOCK) q_encode(QArgs a) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < kEU; ++u) {
     if (!live[u]) continue;  // uniform over the half-wave
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+    const int64_t b = t * kEncTileBlocks + u * kBlocksPerPass + sub;
     const int64_t e0 = b * kQB + lane * 4;
-    const float s = half_wave_max(abs_max4(x[u])) / 127.0f;
-    int q[4];
-    *reinterpret_cast<uint32_t *>(codes + e0) = quant4(x[u], s, q);
-    if (lane == 0) sc[b] = s;
+    const Scale sc = make_scale(
+        max32(max(max(abs_bits(x[u][0]), abs_bits(x[u][1])), max(abs_bits(x[u][2]), abs_bits(x[u][3])))));
+    float k[4];
+    quantize<4>(x[u], sc, k);
+    *reinterpret_cast<uint32_t *>(codes + e0) = pack4(k);
+    if (lane == 0) scl[b] = sc.s;
     if (a.has_err) {
       float res[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) res[k] = x[u][k] - static_cast<float>(q[k]) * s;
+      for (int i = 0; i < 4; ++i) res[i] = x[u][i] - k[i] * sc.s;
       store4<true>(e, e0, a.count, res);
     }
   }
@@ -156,43 +222,55 @@ __global__ void __launch_bounds__(AR_BLOCK) q_encode(QArgs a) {
 template <bool O2>
 __global__ void __launch_bounds__(AR_BLOCK) q_reduce(QArgs a) {
   const DevOp op = a.ops[blockIdx.y];
-  const int lane = threadIdx.x % kHalf, sub = threadIdx.x / kHalf;
+  const int lane = threadIdx.x % kRLanes, sub = threadIdx.x / kRLanes;
   const int8_t *ca = a.codes + op.a * a.code_stride;
   const int8_t *cb = a.codes + op.b * a.code_stride;
   const float *sa = a.scales + op.a * a.scale_stride;
   const float *sb = a.scales + op.b * a.scale_stride;
-  const int64_t t = op.lo / kTileBlocks + blockIdx.x;
-  uint32_t wa[kU], wb[kU];
+  const int64_t t = op.lo / kRTileBlocks + blockIdx.x;
+  u32x4 wa[kU], wb[kU];
   float fa[kU], fb[kU];
   bool live[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+    const int64_t b = t * kRTileBlocks + u * kRBlocksPerPass + sub;
     live[u] = b >= op.lo && b < op.hi;
     if (live[u]) {
-      const int64_t e0 = b * kQB + lane * 4;
-      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(ca + e0));
-      wb[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(cb + e0));
+      const int64_t e0 = b * kQB + lane * 16;
+      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ca + e0));
+      wb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cb + e0));
       fa[u] = sa[b];
       fb[u] = sb[b];
     }
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    if (!live[u]) continue;
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
-    const int64_t e0 = b * kQB + lane * 4;
-    float x[4];
+    if (!live[u]) continue;  // uniform over the block's 8 lanes
+    const int64_t b = t * kRTileBlocks + u * kRBlocksPerPass + sub;
+    const int64_t e0 = b * kQB + lane * 16;
+    float x[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = e0 + k < a.count ? code(wa[u], k) * fa[u] + code(wb[u], k) * fb[u] : 0.0f;
-    const float s = half_wave_max(abs_max4(x)) / 127.0f;
-    int q[4];
-    const uint32_t w = quant4(x, s, q);
-    *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w;
-    if (lane == 0) a.scales[op.o * a.scale_stride + b] = s;
+    for (int i = 0; i < 16; ++i) x[i] = code(wa[u][i / 4], i % 4) * fa[u] + code(wb[u][i / 4], i % 4) * fb[u];
+    if (e0 + 16 > a.count) {  // the ragged last block (the code slots are padded to whole blocks)
+      const int64_t valid = a.count - e0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i >= valid) x[i] = 0.0f;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, abs_bits(x[i]));
+    const Scale sc = make_scale(max8(m));
+    float k[16];
+    quantize<16>(x, sc, k);
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack4(k + 4 * j);
+    *reinterpret_cast<u32x4 *>(a.codes + op.o * a.code_stride + e0) = w;
+    if (lane == 0) a.scales[op.o * a.scale_stride + b] = sc.s;
     if constexpr (O2) {
-      *reinterpret_cast<uint32_t *>(a.codes + op.o2 * a.code_stride + e0) = w;
-      if (lane == 0) a.scales[op.o2 * a.scale_stride + b] = s;
+      *reinterpret_cast<u32x4 *>(a.codes + op.o2 * a.code_stride + e0) = w;
+      if (lane == 0) a.scales[op.o2 * a.scale_stride + b] = sc.s;
     }
   }
 }
@@ -244,9 +322,278 @@ __global__ void __launch_bounds__(AR_BLOCK) q_decode(QArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- one pass
+//
+// The whole compressed all-reduce in one launch: every half-wave owns one
+// block and folds the ranks' contributions in the schedule's order with the
+// step kernels' arithmetic -- a leaf is the round trip v = D(Q(g + e)) (its
+// residual g + e - v is stored), an inner node the round trip D(Q(a + b)) --
+// then writes the decoded sum to every rank.  The codes never leave
+// registers; each rank's g and e are read once and e and the result written
+// once.  Blocks are independent, so evaluating the fold depth first gives
+// the values of the round-by-round schedule.
+
+constexpr int kOPBlock = AR_Q_OP_BLOCK;       // threads per workgroup
+constexpr int kOPTileBlocks = kOPBlock / kHalf;  // one block per half-wave
+
+// v = D(Q(x)) in place (4 values per lane, 32 lanes per block).
+__device__ __forceinline__ void roundtrip4(float x[4]) {
+  const Scale sc =
+      make_scale(max32(max(max(abs_bits(x[0]), abs_bits(x[1])), max(abs_bits(x[2]), abs_bits(x[3])))));
+  float k[4];
+  quantize<4>(x, sc, k);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = k[i] * sc.s;
+}
+
+// Loads g_r (+ e_r) of this lane's 4 elements.
+__device__ __forceinline__ void leaf_load(const QArgs &a, int r, int64_t e0, float x[4]) {
+  load4(a.grad[r], e0, a.count, x);
+  if (a.has_err) {
+    float ev[4];
+    load4(a.err[r], e0, a.count, ev);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = x[i] + ev[i];
+  }
+}
+
+// x (= g_r + e_r) becomes v_r; the residual goes to e_r.
+__device__ __forceinline__ void leaf_finish(const QArgs &a, int r, int64_t e0, float x[4]) {
+  float v[4] = {x[0], x[1], x[2], x[3]};
+  roundtrip4(v);
+  if (a.has_err) {
+    float res[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) res[i] = x[i] - v[i];
+    store4<true>(a.err[r], e0, a.count, res);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = v[i];
+}
+
+__device__ __forceinline__ void leaf(const QArgs &a, int r, int64_t e0, float x[4]) {
+  leaf_load(a, r, e0, x);
+  leaf_finish(a, r, e0, x);
+}
+
+// acc = D(Q(acc + y)).
+__device__ __forceinline__ void qadd(float acc[4], const float y[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = acc[i] + y[i];
+  roundtrip4(acc);
+}
+
+__device__ __forceinline__ void store_result(const QArgs &a, int64_t e0, const float v[4]) {
+  for (int r = 0; r < a.nranks; ++r) store4<true>(a.grad[r], e0, a.count, v);
+}
+
+// Block coordinate of this half-wave, or -1 when its block is outside the op.
+__device__ __forceinline__ int64_t op_block(const DevOp &op) {
+  const int64_t b = (op.lo / kOPTileBlocks + blockIdx.x) * kOPTileBlocks + threadIdx.x / kHalf;
+  return b >= op.lo && b < op.hi ? b : -1;
+}
+
+// Ring: chunk c's blocks fold ranks c, c+1, ..., c+N-1 (aux = c), the order
+// in which the chunk travels round the ring in reduce-scatter.  FB ranks'
+// inputs are loaded ahead of their use.
+template <int FB>
+__global__ void __launch_bounds__(kOPBlock) q_onepass_ring(QArgs a) {
+  const DevOp op = a.ops[blockIdx.y];
+  const int64_t b = op_block(op);
+  if (b < 0) return;  // the whole half-wave
+  const int64_t e0 = b * kQB + (threadIdx.x % kHalf) * 4;
+  const int n = a.nranks;
+  float acc[4];
+  int r = op.aux;
+  for (int t0 = 0; t0 < n; t0 += FB) {
+    float x[FB][4];
+    int rr = r;
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+      if (t0 + i < n) leaf_load(a, rr, e0, x[i]);
+      rr = rr + 1 == n ? 0 : rr + 1;
+    }
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+      if (t0 + i >= n) break;
+      leaf_finish(a, r, e0, x[i]);
+      if (t0 + i == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = x[i][k];
+      } else {
+        qadd(acc, x[i]);
+      }
+      r = r + 1 == n ? 0 : r + 1;
+    }
+  }
+  store_result(a, e0, acc);
+}
+
+// Hierarchical (aux = ls | j << 8): for groups g = j, j+1, ... (mod M), the
+// group's partial folds local ranks ls, ls+1, ... (mod G); the partials fold
+// in that group order.
+__global__ void __launch_bounds__(kOPBlock) q_onepass_hier(QArgs a) {
+  const DevOp op = a.ops[blockIdx.y];
+  const int64_t b = op_block(op);
+  if (b < 0) return;
+  const int64_t e0 = b * kQB + (threadIdx.x % kHalf) * 4;
+  const int G = a.group_size, M = a.nranks / a.group_size;
+  const int ls = op.aux & 0xFF, j = op.aux >> 8;
+  float acc[4];
+  for (int mi = 0; mi < M; ++mi) {
+    const int g = (j + mi) % M;
+    float part[4];
+    leaf(a, g * G + ls, e0, part);
+    for (int t = 1; t < G; ++t) {
+      float y[4];
+      leaf(a, g * G + (ls + t) % G, e0, y);
+      qadd(part, y);
+    }
+    if (mi == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = part[k];
+    } else {
+      qadd(acc, part);
+    }
+  }
+  store_result(a, e0, acc);
+}
+
+// Tree over ranks in index order (balanced for N = 2^L, left-complete
+// binomial otherwise): batches of 8 ranks merge pairwise, a node without a
+// right neighbour is carried up unchanged, then the batch results merge the
+// same way.  NMAX = N rounded up to a power of two.
+template <int NMAX>
+__global__ void __launch_bounds__(kOPBlock) q_onepass_tree(QArgs a) {
+  constexpr int kB = NMAX < 8 ? NMAX : 8;
+  constexpr int kBatches = NMAX / kB;
+  const DevOp op = a.ops[blockIdx.y];
+  const int64_t b = op_block(op);
+  if (b < 0) return;
+  const int64_t e0 = b * kQB + (threadIdx.x % kHalf) * 4;
+  const int n = a.nranks;
+  float res[kBatches][4];
+#pragma unroll
+  for (int bi = 0; bi < kBatches; ++bi) {
+    if (bi * kB >= n) continue;
+    float v[kB][4];
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (bi * kB + i < n) leaf_load(a, bi * kB + i, e0, v[i]);
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (bi * kB + i < n) leaf_finish(a, bi * kB + i, e0, v[i]);
+#pragma unroll
+    for (int w = kB, span = 1; w > 1; w /= 2, span *= 2)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i)
+        if (bi * kB + (2 * i + 1) * span < n) {
+          qadd(v[2 * i], v[2 * i + 1]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[i][k] = v[2 * i][k];
+        } else if (i > 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[i][k] = v[2 * i][k];
+        }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) res[bi][k] = v[0][k];
+  }
+#pragma unroll
+  for (int w = kBatches, span = kB; w > 1; w /= 2, span *= 2)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i)
+      if ((2 * i + 1) * span < n) {
+        qadd(res[2 * i], res[2 * i + 1]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) res[i][k] = res[2 * i][k];
+      } else if (i > 0 && 2 * i * span < n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) res[i][k] = res[2 * i][k];
+      }
+  store_result(a, e0, res[0]);
+}
+
+// Double binary tree, one half per op (aux = 0: tree 1, 1: its mirror):
+// D(c, b) = (v_c + D(c - b/2, b/2)) + D(c + b/2, b/2), D(c, 1) = v_c; tree 1
+// gives v_0 + D(N/2, N/2), tree 2 gives v_{N-1} + D(N/2 - 1, N/2).
+template <int C, int B>
+struct QDTree {
+  static __device__ __forceinline__ void run(const QArgs &a, int64_t e0, float out[4]) {
+    leaf(a, C, e0, out);
+    if constexpr (B > 1) {
+      float lo[4], hi[4];
+      QDTree<C - B / 2, B / 2>::run(a, e0, lo);
+      QDTree<C + B / 2, B / 2>::run(a, e0, hi);
+      qadd(out, lo);
+      qadd(out, hi);
+    }
+  }
+};
+
+template <int N>
+__global__ void __launch_bounds__(kOPBlock) q_onepass_dtree(QArgs a) {
+  const DevOp op = a.ops[blockIdx.y];
+  const int64_t b = op_block(op);
+  if (b < 0) return;
+  const int64_t e0 = b * kQB + (threadIdx.x % kHalf) * 4;
+  float root[4], sub[4];
+  if (op.aux == 0) {
+    leaf(a, 0, e0, root);
+    QDTree<N / 2, N / 2>::run(a, e0, sub);
+  } else {
+    leaf(a, N - 1, e0, root);
+    QDTree<N / 2 - 1, N / 2>::run(a, e0, sub);
+  }
+  qadd(root, sub);
+  store_result(a, e0, root);
+}
+
+template <int NMAX>
+void launch_q_tree(dim3 grid, const QArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(q_onepass_tree<NMAX>, grid, dim3(kOPBlock), 0, s, a);
+}
+
+hipError_t launch_q_onepass(int32_t fam, dim3 grid, const QArgs &a, hipStream_t s) {
+  const int n = a.nranks;
+  switch (fam) {
+    case ar::kKRing: hipLaunchKernelGGL(q_onepass_ring<AR_Q_FOLD_BATCH>, grid, dim3(kOPBlock), 0, s, a); break;
+    case ar::kKHier: hipLaunchKernelGGL(q_onepass_hier, grid, dim3(kOPBlock), 0, s, a); break;
+    case ar::kKTree:
+      if (n <= 2) launch_q_tree<2>(grid, a, s);
+      else if (n <= 4) launch_q_tree<4>(grid, a, s);
+      else if (n <= 8) launch_q_tree<8>(grid, a, s);
+      else if (n <= 16) launch_q_tree<16>(grid, a, s);
+      else if (n <= 32) launch_q_tree<32>(grid, a, s);
+      else if (n <= 64) launch_q_tree<64>(grid, a, s);
+      else return hipErrorInvalidValue;
+      break;
+    case ar::kKDTree:
+      switch (n) {
+        case 2: hipLaunchKernelGGL(q_onepass_dtree<2>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(q_onepass_dtree<4>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 8: hipLaunchKernelGGL(q_onepass_dtree<8>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 16: hipLaunchKernelGGL(q_onepass_dtree<16>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 32: hipLaunchKernelGGL(q_onepass_dtree<32>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 64: hipLaunchKernelGGL(q_onepass_dtree<64>, grid, dim3(kOPBlock), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int64_t q_tile_blocks(int32_t kind) { return (kind & 0xF00) == ar::kKQCopy ? kCopyTileBlocks : kTileBlocks; }
+int64_t q_tile_blocks(int32_t kind) {
+  switch (kind & 0xF00) {
+    case ar::kKQCopy: return kCopyTileBlocks;
+    case ar::kKQReduce: return kRTileBlocks;
+    case ar::kKQEncode: return kEncTileBlocks;
+    case ar::kKQDecode: return kTileBlocks;
+    default: return kOPTileBlocks;
+  }
+}
 
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s) {
   switch (kind & 0xF00) {
@@ -257,7 +604,7 @@ hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s) {
       break;
     case ar::kKQCopy: hipLaunchKernelGGL(q_copy, grid, dim3(AR_BLOCK), 0, s, a); break;
     case ar::kKQDecode: hipLaunchKernelGGL(q_decode, grid, dim3(AR_BLOCK), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    default: return launch_q_onepass(kind & 0xF00, grid, a, s);
   }
   return hipGetLastError();
 }

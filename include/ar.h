@@ -89,9 +89,11 @@ typedef enum {
  * receiver decodes the message and its own codes, adds in fp32 and
  * re-encodes the sum; forwarding copies codes.  At the end each rank's
  * buffer holds the decoded codes it ends with (identical on every rank).
- * The schedule runs over blocks; the codes live in plan-owned device memory
- * (about 1.03 bytes per element per rank).  Inputs must be finite.  No
- * one-pass mode. */
+ * The schedule runs over blocks; in the step modes the codes live in
+ * plan-owned device memory (about 1.03 bytes per element per rank), in
+ * AR_EXEC_ONEPASS they stay in registers (each block folds every rank's
+ * contribution in the schedule's order, re-encoding every partial sum).
+ * Inputs must be finite. */
 typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_BFLOAT16_EACH_STEP = 2, AR_INT8_EF = 3 } ar_dtype_t;
 
 typedef enum {
@@ -160,8 +162,7 @@ typedef struct {
 ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype,
                           ar_schedule_t schedule);
 
-/* Selects the execution mode (see ar_exec_t).  Host only.  AR_INT8_EF plans
- * have no one-pass mode (AR_ERR_UNSUPPORTED). */
+/* Selects the execution mode (see ar_exec_t).  Host only. */
 ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
 
 /*
@@ -266,8 +267,8 @@ int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, in
  * -1 is unused.  aux is the fold start (one-pass kernels).  AR_INT8_EF plans
  * use kinds 0x700 (encode rank a), 0x800 (o [and o2 with flag 8] = re-encoded
  * decode(a) + decode(b)), 0x900 (copy a's codes to o) and 0xA00 (decode a
- * into its buffer); their ranges count blocks and locations name ranks'
- * code slots.  Host only.
+ * into its buffer), and in one-pass mode the fold kinds with dtype code 3;
+ * their ranges count blocks and locations name ranks' code slots.  Host only.
  */
 int32_t ar_plan_num_launches(const ar_plan_t *plan);
 ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);

@@ -104,7 +104,7 @@ def _q_block(x):
     return np.clip(np.rint(x / s), -127, 127).astype(np.int8), s
 
 
-def run_int8(plan, bufs, errs=None):
+def run_int8(plan, bufs, errs=None, group=1):
     """Executes an int8_ef plan's launch list on float32 host arrays."""
     n = len(bufs)
     count = len(bufs[0])
@@ -147,6 +147,62 @@ def run_int8(plan, bufs, errs=None):
                     scales[o][blk] = scales[a][blk]
                 elif fam == B.KIND_QDECODE:
                     bufs[a][e0:e1] = dec(a, blk)[:e1 - e0]
+                elif fam in (B.KIND_RING, B.KIND_HIER, B.KIND_TREE, B.KIND_DTREE):
+                    assert kind & 3 == 3, f"one-pass kind {kind:#x} without the INT8 code"
+                    _onepass_block(fam, int(ops["aux"][k]), blk, e0, e1, bufs, errs, group)
                 else:
                     raise AssertionError(f"kind {kind:#x} in an int8 plan")
     return bufs
+
+
+def _roundtrip(x):
+    q, s = _q_block(x)
+    return (q.astype(np.float32) * s).astype(np.float32)
+
+
+def _onepass_block(fam, aux, blk, e0, e1, bufs, errs, group):
+    """One block of a one-pass INT8 fold, in the order the kernel's aux
+    selects (the same orders as the fp32 one-pass kinds)."""
+    n = len(bufs)
+    Q = B.QBLOCK
+    leaves = []
+    for r in range(n):
+        x = np.zeros(Q, np.float32)
+        x[:e1 - e0] = bufs[r][e0:e1] + (errs[r][e0:e1] if errs is not None else np.float32(0))
+        v = _roundtrip(x)
+        if errs is not None:
+            errs[r][e0:e1] = (x - v)[:e1 - e0]
+        leaves.append(v)
+
+    def add(a, b):
+        return _roundtrip((a + b).astype(np.float32))
+
+    if fam == B.KIND_RING:
+        acc = leaves[aux % n]
+        for t in range(1, n):
+            acc = add(acc, leaves[(aux + t) % n])
+    elif fam == B.KIND_HIER:
+        G = group
+        M = n // G
+        ls, j = aux & 0xFF, aux >> 8
+        acc = None
+        for mi in range(M):
+            g = (j + mi) % M
+            part = leaves[g * G + ls]
+            for t in range(1, G):
+                part = add(part, leaves[g * G + (ls + t) % G])
+            acc = part if acc is None else add(acc, part)
+    elif fam == B.KIND_TREE:
+        level = leaves
+        while len(level) > 1:
+            level = [add(level[m], level[m + 1]) if m + 1 < len(level) else level[m]
+                     for m in range(0, len(level), 2)]
+        acc = level[0]
+    else:
+        def sub(c, b):
+            if b == 1:
+                return leaves[c]
+            return add(add(leaves[c], sub(c - b // 2, b // 2)), sub(c + b // 2, b // 2))
+        acc = add(leaves[0], sub(n // 2, n // 2)) if aux == 0 else add(leaves[n - 1], sub(n // 2 - 1, n // 2))
+    for r in range(n):
+        bufs[r][e0:e1] = acc[:e1 - e0]

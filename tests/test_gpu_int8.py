@@ -97,9 +97,10 @@ def test_small_sizes(sched, n, g):
     for count in (0, 1, 127, 128, 129, 5 * Q + 77, 100003):
         xs = _grads(n, count, seed=count + n)
         es = [(x * np.float32(0.01)).astype(np.float32) for x in _grads(n, count, seed=count + 1000)]
-        for mode in ("steps", "steps_unfused"):
+        for mode in ("steps", "steps_unfused", "onepass"):
             _case(xs, es, sched, g, mode)
         _case(xs, None, sched, g, "steps")
+        _case(xs, None, sched, g, "onepass")
 
 
 def test_error_feedback_over_calls():
@@ -110,11 +111,13 @@ def test_error_feedback_over_calls():
     xs = _grads(n, count, seed=7)
     es = [np.zeros(count, np.float32) for _ in range(n)]
     _case(xs, es, "ring", 1, "steps", calls=3)
+    _case(xs, es, "ring", 1, "onepass", calls=3)
 
 
 def test_special_blocks():
     """Zero blocks, one non-zero element per block, denormal scales, exact
-    ties of the rounding and values that reach the clamp."""
+    ties of the rounding, values that reach the clamp, and signed zeros (a
+    code of -0 decodes to +0; -0 - 0 keeps its sign in the residual)."""
     n, count = 4, 16 * Q + 9
     rng = np.random.default_rng(11)
     xs = [np.zeros(count, np.float32) for _ in range(n)]
@@ -125,9 +128,16 @@ def test_special_blocks():
         xs[r][4 * Q:5 * Q] = np.float32(127.0)
         xs[r][4 * Q + 1:4 * Q + 11] = np.arange(10, dtype=np.float32) + np.float32(0.5)  # ties
         xs[r][5 * Q:6 * Q] = (rng.standard_normal(Q) * 1e30).astype(np.float32)
+        xs[r][6 * Q:7 * Q] = rng.standard_normal(Q).astype(np.float32)
+        xs[r][6 * Q:6 * Q + 40:3] = -0.0                                    # -0 inside a block
+        xs[r][7 * Q:8 * Q] = -0.0                                            # a block of -0
     es = [np.zeros(count, np.float32) for _ in range(n)]
+    for r in range(n):
+        es[r][6 * Q:6 * Q + 40:3] = -0.0                                    # g + e = -0
+        es[r][7 * Q:8 * Q] = -0.0
     for sched, g in (("ring", 1), ("hierarchical", 2), ("rabenseifner", 1), ("tree", 1), ("double_tree", 1)):
-        _case(xs, es, sched, g, "steps")
+        for mode in ("steps", "onepass"):
+            _case(xs, es, sched, g, mode)
 
 
 def test_plan_reuse_and_bucketed_error_feedback():
@@ -165,10 +175,23 @@ def test_plan_reuse_and_bucketed_error_feedback():
 @pytest.mark.timeout(600)
 def test_full_size_ring_16_ranks_192mib():
     """16 ranks x 192 MiB of fp32 gradients (the benchmark's workload), ring,
-    steps mode, with error feedback: the whole result and residual of every
-    rank against the oracle."""
+    steps and one-pass, with error feedback: the whole result and residual of
+    every rank against the oracle."""
     n, count = 16, workloads.GATE_PROJ_ELEMS
     _say(f"case full int8_ef ring n={n} count={count}: inputs")
     xs = workloads.normal_inputs(n, count, seed=0, sigma=1.0, dtype="fp32")
     es = workloads.normal_inputs(n, count, seed=1, sigma=0.01, dtype="fp32")
-    _case(xs, es, "ring", 1, "steps")
+    for mode in ("steps", "onepass"):
+        _case(xs, es, "ring", 1, mode)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_hierarchical_and_tree_16_ranks():
+    """2 groups x 8 ranks hierarchical and the 16-rank double tree, 192 MiB
+    each, one-pass and steps, with error feedback."""
+    n, count = 16, workloads.GATE_PROJ_ELEMS
+    xs = workloads.normal_inputs(n, count, seed=2, sigma=1.0, dtype="fp32")
+    es = workloads.normal_inputs(n, count, seed=3, sigma=0.01, dtype="fp32")
+    for sched, g in (("hierarchical", 8), ("double_tree", 1)):
+        for mode in ("steps", "onepass"):
+            _case(xs, es, sched, g, mode)
