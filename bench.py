@@ -113,15 +113,20 @@ def launch_bytes(B, plan, i, nranks, elem, count):
     return int(n.sum()) * 2 * elem * nranks, kind
 
 
+def kernels_sha256():
+    """SHA-256 over the device kernel sources (kernels.hip, qkernels.hip, kernels.hpp)."""
+    csrc = os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("kernels.hip", "qkernels.hip", "kernels.hpp"))
+    return hashlib.sha256(src).hexdigest()
+
+
 def traffic_record(kernel_name, workload, exec_mode):
     """Counter-measured HBM bytes per launch from a committed rocprofv3 summary,
     if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    csrc = os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc")
-    src = open(os.path.join(csrc, "kernels.hip"), "rb").read() + open(os.path.join(csrc, "kernels.hpp"), "rb").read()
-    digest = hashlib.sha256(src).hexdigest()
+    digest = kernels_sha256()
     try:
         recs = json.load(open(path))
     except ValueError:
