@@ -10,6 +10,8 @@ Schedules and datatypes use the oracle's own numbering:
   dtype:    "fp32" (numpy float32 buffers) | "bf16" (numpy uint16 buffers of bf16 bits,
             fp32 partial sums, one rounding) | "bf16_each" (uint16 buffers, every
             partial sum rounded to bf16 as it is formed)
+run_int8ef: the compressed all-reduce (blockwise INT8 messages, error feedback)
+            on float32 buffers.
 """
 import ctypes
 import os

@@ -37,6 +37,14 @@
  *   bf16, rounded each step: every message carries bf16 bits, and every
  *         REDUCE widens both operands, adds in fp32 and rounds the sum to
  *         bf16 at once -- what a wire of bf16 values gives.
+ *   INT8 with error feedback (aro_run_int8ef, end of file): fp32 buffers;
+ *         every message carries blockwise INT8 codes and fp32 scales, the
+ *         schedule runs over 128-element blocks.
+ *
+ * Parity unpinned: the re-encoding of partial sums at every INT8 hop (how
+ * compressed messages are summed is not fixed by the pages); it is pinned
+ * only where it is exact, by error bounds, and by a closed form of the same
+ * reading.
  */
 #include <math.h>
 #include <stdint.h>
