@@ -72,6 +72,16 @@ def kernel_label(kind):
     return f"{KIND_NAMES[fam]}<{'bf16' if kind & 1 else 'fp32'}>"
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -290,8 +300,11 @@ def main():
                                                   "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
                                   for f, v in per_kind.items()})
         sum_launch_ms = sum(sum(c) for c in times) / max(len(times), 1)
+        per_call = sorted(sum(c) for c in times)  # launch intervals of each timed call
+        per_call_ms = {"median": round(per_call[len(per_call) // 2], 4), "min": round(per_call[0], 4)}
     else:
         sum_launch_ms = None
+        per_call_ms = None
 
     # ---- one-pass comparison on the same buffers (bit-identical results)
     extra = {}
@@ -312,6 +325,27 @@ def main():
         extra["onepass"] = {"ms_per_step": round(op_ms, 4), "busbw_GBps": round(op_alg * 2 * (n - 1) / n, 1),
                             "algbw_GBps": round(op_alg, 1),
                             "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
+
+    # ---- the same exec mode replayed as one HIP graph per call
+    if not args.no_extra:
+        if bucketed:
+            B.ar_bucket_set_graph(plan, True)
+        else:
+            B.ar_plan_set_profiling(plan, 0)
+            B.ar_plan_set_exec(plan, args.exec)
+            B.ar_plan_set_graph(plan, True)
+        reset_inputs()
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t_g) * 1e3 / max(args.steps, 1)
+        g_alg = S / (g_ms * 1e-3) / 1e9
+        extra["graph"] = {"exec": args.exec, "ms_per_step": round(g_ms, 4),
+                          "busbw_GBps": round(g_alg * 2 * (n - 1) / n, 1), "algbw_GBps": round(g_alg, 1)}
 
     # ---- CPU oracle on the same inputs (single-threaded C)
     cpu = None
@@ -344,7 +378,8 @@ def main():
             sample = "the whole workload, one all-reduce"
         cpu_alg = done * elem / cpu_s / 1e9
         cpu = {"value": round(cpu_alg * 2 * (n - 1) / n, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": sample, "seconds": round(cpu_s, 2), "host_cpus": os.cpu_count()}
+               "sample": sample, "seconds": round(cpu_s, 2), "host_cpus": os.cpu_count(),
+               "cpu_model": cpu_model(), "threads_used": 1}
 
     out = {
         "metric": METRIC,
@@ -369,6 +404,7 @@ def main():
             "launches_per_step": stats["launches"], "schedule_steps": stats["steps"],
             "event_ms_per_step": round(ev_ms, 4),
             "sum_of_launch_ms_per_step": None if sum_launch_ms is None else round(sum_launch_ms, 4),
+            "per_call_ms": per_call_ms,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

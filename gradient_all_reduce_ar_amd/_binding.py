@@ -100,6 +100,8 @@ def _declare(L):
         "ar_plan_launch_info": ([P, i32, pi32, pi32], ctypes.c_int),
         "ar_plan_launch_ops": ([P, i32, pi64, pi64, pi32, pi32, pi32, pi32, pi32], ctypes.c_int),
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_bucket_set_graph": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_launch_times": ([P, pf, i32, pi32], ctypes.c_int),
         "ar_bucket_plan_create": ([ctypes.c_int, ctypes.c_int, psz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz], P),
         "ar_bucket_layout": ([P, psz, psz], ctypes.c_int),
@@ -167,6 +169,10 @@ def ar_plan_create(nranks, group_size, count, dtype, schedule):
 
 def ar_plan_set_exec(plan, exec_mode):
     _check(lib().ar_plan_set_exec(plan, _code(EXECS, exec_mode)))
+
+
+def ar_plan_set_graph(plan, enable=True):
+    _check(lib().ar_plan_set_graph(plan, 1 if enable else 0))
 
 
 def ar_plan_prepare(plan):
@@ -318,6 +324,10 @@ def ar_bucket_range(bp, b):
     off, cnt = ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib().ar_bucket_range(bp, b, ctypes.byref(off), ctypes.byref(cnt)))
     return off.value, cnt.value
+
+
+def ar_bucket_set_graph(bp, enable=True):
+    _check(lib().ar_bucket_set_graph(bp, 1 if enable else 0))
 
 
 def ar_bucket_set_exec(bp, exec_mode):

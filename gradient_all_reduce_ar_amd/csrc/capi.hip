@@ -47,6 +47,16 @@ struct ar_plan {
   size_t scratch_bytes = 0;
   float *external_scratch = nullptr;
   size_t external_scratch_bytes = 0;
+  // Graph replay: one instantiated graph of the whole launch sequence per
+  // (rank pointers, error pointers, workspace) seen, at most kMaxGraphs.
+  struct GraphEntry {
+    std::vector<uintptr_t> key;
+    hipGraphExec_t exec;
+  };
+  static constexpr size_t kMaxGraphs = 8;
+  bool use_graph = false;
+  std::vector<GraphEntry> graphs;
+  hipStream_t capture_stream = nullptr;
   int32_t prof_calls = 0;           // capacity of the event log in calls
   int64_t prof_logged = 0;          // calls recorded since the log was last read
   std::vector<hipEvent_t> events;   // prof_calls * (launches + 1)
@@ -54,7 +64,16 @@ struct ar_plan {
   // fp32 partial-sum slots, or the INT8 code slots
   size_t need_scratch_bytes() const { return static_cast<size_t>(ar::workspace_bytes(p)); }
 
+  void drop_graphs() {
+    if (!graphs.empty()) (void)hipDeviceSynchronize();  // a replay may still be in flight
+    for (GraphEntry &g : graphs) (void)hipGraphExecDestroy(g.exec);
+    graphs.clear();
+  }
+
   void release_device() {
+    drop_graphs();
+    if (capture_stream) (void)hipStreamDestroy(capture_stream);
+    capture_stream = nullptr;
     if (d_ops) (void)hipFree(d_ops);
     if (scratch) (void)hipFree(scratch);
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
@@ -228,6 +247,92 @@ ar_stats_t stats_of(const ar::Plan &p) {
 
 }  // namespace
 
+namespace {
+
+// Launches every kernel of the plan on s (recording the profiling events
+// around them when prof is set).
+ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
+                    bool prof) {
+  hipEvent_t *ev = nullptr;
+  if (prof) {
+    ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * (plan->p.launches.size() + 1);
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  for (size_t i = 0; i < plan->p.launches.size(); ++i) {
+    const ar::Launch &L = plan->p.launches[i];
+    const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
+    hipError_t e = hipSuccess;
+    if (grid.x == 0) {
+    } else if (quant) {
+      qargs.ops = plan->d_ops + plan->op_offset[i];
+      qargs.nops = static_cast<int32_t>(L.ops.size());
+      e = ar_dev::launch_q(L.kind, grid, qargs, s);
+    } else {
+      args.ops = plan->d_ops + plan->op_offset[i];
+      args.nops = static_cast<int32_t>(L.ops.size());
+      const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
+      e = ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
+    }
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    if (prof) {
+      e = hipEventRecord(ev[i + 1], s);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+  }
+  if (prof) ++plan->prof_logged;
+  return AR_OK;
+}
+
+// Graph replay ([PRIMER] 4.8 / the persistent-collective idea of registering
+// an operation once for many calls): the launch sequence is captured once per
+// set of buffer pointers into a HIP graph and replayed with one launch.  The
+// graph holds kernel nodes only (no memset or copy nodes).
+ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, void *const *rank_bufs,
+                   void *const *error_bufs, hipStream_t s) {
+  std::vector<uintptr_t> key;
+  const int n = plan->p.nranks;
+  key.reserve(2 * n + 2);
+  for (int r = 0; r < n; ++r) key.push_back(reinterpret_cast<uintptr_t>(rank_bufs[r]));
+  for (int r = 0; r < n; ++r) key.push_back(error_bufs ? reinterpret_cast<uintptr_t>(error_bufs[r]) : 0);
+  key.push_back(reinterpret_cast<uintptr_t>(plan->external_scratch ? plan->external_scratch : plan->scratch));
+  key.push_back(reinterpret_cast<uintptr_t>(plan->d_ops));
+  for (ar_plan_t::GraphEntry &g : plan->graphs)
+    if (g.key == key) {
+      hipError_t e = hipGraphLaunch(g.exec, s);
+      return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
+    }
+  hipError_t e;
+  if (!plan->capture_stream) {
+    e = hipStreamCreateWithFlags(&plan->capture_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  }
+  e = hipStreamBeginCapture(plan->capture_stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  const ar_status_t st = enqueue(plan, quant, args, qargs, plan->capture_stream, false);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(plan->capture_stream, &graph);
+  if (st != AR_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+  if (plan->graphs.size() >= ar_plan_t::kMaxGraphs) {
+    (void)hipDeviceSynchronize();
+    (void)hipGraphExecDestroy(plan->graphs.front().exec);
+    plan->graphs.erase(plan->graphs.begin());
+  }
+  plan->graphs.push_back({std::move(key), exec});
+  e = hipGraphLaunch(exec, s);
+  return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *ar_last_error(void) { return g_err.c_str(); }
@@ -314,35 +419,9 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
     args.group_size = plan->p.group_size;
   }
   const bool prof = plan->prof_calls > 0 && !plan->events.empty();
-  hipEvent_t *ev = nullptr;
-  if (prof) {
-    ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * (plan->p.launches.size() + 1);
-    hipError_t e = hipEventRecord(ev[0], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  for (size_t i = 0; i < plan->p.launches.size(); ++i) {
-    const ar::Launch &L = plan->p.launches[i];
-    const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
-    hipError_t e = hipSuccess;
-    if (grid.x == 0) {
-    } else if (quant) {
-      qargs.ops = plan->d_ops + plan->op_offset[i];
-      qargs.nops = static_cast<int32_t>(L.ops.size());
-      e = ar_dev::launch_q(L.kind, grid, qargs, s);
-    } else {
-      args.ops = plan->d_ops + plan->op_offset[i];
-      args.nops = static_cast<int32_t>(L.ops.size());
-      const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
-      e = ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
-    }
-    if (e != hipSuccess) return hip_fail(e, "kernel launch");
-    if (prof) {
-      e = hipEventRecord(ev[i + 1], s);
-      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
-  }
-  if (prof) ++plan->prof_logged;
-  return AR_OK;
+  if (plan->use_graph && !prof && !plan->p.launches.empty())
+    return replay(plan, quant, args, qargs, rank_bufs, error_bufs, s);
+  return enqueue(plan, quant, args, qargs, s, prof);
 }
 
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
@@ -466,6 +545,13 @@ ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, in
   return AR_OK;
 }
 
+ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  plan->use_graph = enable != 0;
+  plan->drop_graphs();
+  return AR_OK;
+}
+
 ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls) {
   if (!plan || max_calls < 0) return fail(AR_ERR_INVALID_ARG, "bad profiling arguments");
   if (plan->prepared) (void)hipDeviceSynchronize();
@@ -561,6 +647,15 @@ ar_status_t ar_bucket_range(const ar_bucket_plan_t *bp, int32_t b, size_t *offse
     return fail(AR_ERR_INVALID_ARG, "bad bucket plan or index");
   if (offset) *offset = static_cast<size_t>(bp->bucket_offset[b]);
   if (count) *count = static_cast<size_t>(bp->bucket_count[b]);
+  return AR_OK;
+}
+
+ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  for (ar_plan_t *pl : bp->plans) {
+    const ar_status_t st = ar_plan_set_graph(pl, enable);
+    if (st != AR_OK) return st;
+  }
   return AR_OK;
 }
 

@@ -275,6 +275,21 @@ ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind,
 ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, int64_t *hi,
                                int32_t *a, int32_t *b, int32_t *o, int32_t *o2, int32_t *aux);
 
+/*
+ * Graph replay (host call, no device work).  With enable != 0, ar_allreduce
+ * and ar_allreduce_ef capture the plan's whole launch sequence into a HIP
+ * graph the first time they see a set of buffer pointers, and from then on
+ * replay it with one graph launch on the caller's stream (the pages'
+ * persistent collectives register an operation once for many calls --
+ * Scaling ML systems ch. 06, "collective semantics").  Up to 8 pointer sets are
+ * kept per plan; the oldest is dropped (after a device synchronisation) when
+ * a ninth appears.  The graphs hold kernel nodes only.  Results are
+ * bit-identical to eager calls.  While per-launch profiling is on
+ * (ar_plan_set_profiling), calls run eagerly.  Changing the exec mode or the
+ * profiling log, or calling this function, drops the cached graphs.
+ */
+ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable);
+
 /* ---- Timing ---- */
 
 /* Per-launch timing.  With max_calls > 0, each ar_allreduce records a HIP
@@ -313,6 +328,8 @@ int32_t ar_bucket_count(const ar_bucket_plan_t *bp);
 /* Element offset and length of bucket b in the arena. */
 ar_status_t ar_bucket_range(const ar_bucket_plan_t *bp, int32_t b, size_t *offset, size_t *count);
 ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec);
+/* Graph replay for every bucket's plan (see ar_plan_set_graph). */
+ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable);
 /* All-reduces every bucket of the nranks arenas (16-byte aligned device
  * pointers of arena_count elements), in place, on `stream`. */
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream);
