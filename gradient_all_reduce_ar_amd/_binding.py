@@ -101,6 +101,7 @@ def _declare(L):
         "ar_plan_launch_ops": ([P, i32, pi64, pi64, pi32, pi32, pi32, pi32, pi32], ctypes.c_int),
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_set_cache_bytes": ([P, sz], ctypes.c_int),
         "ar_bucket_set_graph": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_launch_times": ([P, pf, i32, pi32], ctypes.c_int),
         "ar_bucket_plan_create": ([ctypes.c_int, ctypes.c_int, psz, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz], P),
@@ -169,6 +170,10 @@ def ar_plan_create(nranks, group_size, count, dtype, schedule):
 
 def ar_plan_set_exec(plan, exec_mode):
     _check(lib().ar_plan_set_exec(plan, _code(EXECS, exec_mode)))
+
+
+def ar_plan_set_cache_bytes(plan, nbytes):
+    _check(lib().ar_plan_set_cache_bytes(plan, nbytes))
 
 
 def ar_plan_set_graph(plan, enable=True):

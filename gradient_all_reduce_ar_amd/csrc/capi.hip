@@ -134,7 +134,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
     const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
     const bool quant = is_quant_kind(L.kind);
-    const bool cold = !quant && ar_dev::is_cold(launch_written_bytes(pl->p, L), out_scratch);
+    const bool cold = !quant && !out_scratch && launch_written_bytes(pl->p, L) > pl->p.cache_bytes;
     pl->cold.push_back(cold);
     const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold);
     int64_t gx = 0;
@@ -366,6 +366,19 @@ ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
   if (exec == static_cast<ar_exec_t>(plan->p.exec) && plan->prepared) return AR_OK;
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
+  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
+  if (plan->prepared) (void)hipDeviceSynchronize();
+  plan->release_device();
+  plan->p = std::move(trial);
+  return AR_OK;
+}
+
+ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (bytes > static_cast<size_t>(INT64_MAX)) return fail(AR_ERR_INVALID_ARG, "cache size too large");
+  ar::Plan trial = plan->p;
+  trial.cache_bytes = static_cast<int64_t>(bytes);
+  const std::string err = ar::relower(trial, trial.exec);
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
   if (plan->prepared) (void)hipDeviceSynchronize();
   plan->release_device();

@@ -29,6 +29,7 @@ namespace ar_dev {
 namespace {
 
 constexpr int kBlock = AR_BLOCK;
+constexpr int kOPB = AR_ONEPASS_BLOCK;  // threads per workgroup of the one-pass kernels
 constexpr bool kOnePassNTS = AR_NTS_ONEPASS;
 
 // Native vector types: 16-byte and 8-byte accesses compile to single
@@ -274,7 +275,7 @@ __device__ __forceinline__ void load_units(const KArgs &args, int r, int64_t bas
   const char *p = static_cast<const char *>(args.rank[r]);
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u)
-    x[u] = load4<BF>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4);
+    x[u] = load4<BF>(p, base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4);
 }
 
 template <bool BF, int UNROLL>
@@ -287,14 +288,14 @@ __device__ __forceinline__ void store_all(const KArgs &args, int64_t base, const
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        store_bits4<kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4, bits[u]);
+        store_bits4<kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4, bits[u]);
     }
   } else {
     for (int r = 0; r < args.nranks; ++r) {
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        store4<false, kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4, acc[u]);
+        store4<false, kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4, acc[u]);
     }
   }
 }
@@ -370,8 +371,8 @@ __device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e
 
 // Ring: element in chunk c is ((x_c + x_{c+1}) + ...) + x_{c+N-1}; aux = c.
 template <bool BF, bool EACH, int UNROLL, int FB>
-__global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+__global__ __launch_bounds__(kOPB) void onepass_ring(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const BlockCoord bc = block_coord(args);
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
           store_all1(args, BF, e, ring_fold1(args, BF, EACH, 0, n, op.aux, n, e));
         }
@@ -397,8 +398,8 @@ __global__ __launch_bounds__(kBlock) void onepass_ring(KArgs args) {
 // x_{g,k}; sub-chunk j folds the group partials P_j + P_{j+1} + ... in ring
 // order.  aux = ((k + 1) mod G) | (j << 8).
 template <bool BF, bool EACH, int UNROLL, int FB>
-__global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+__global__ __launch_bounds__(kOPB) void onepass_hier(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const BlockCoord bc = block_coord(args);
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
           float acc = 0.f;
           int g = j;
@@ -446,10 +447,10 @@ __global__ __launch_bounds__(kBlock) void onepass_hier(KArgs args) {
 // doubling; otherwise it is the binomial tree's left-complete order.  Formed
 // batch by batch (8 ranks at a time); NMAX = N rounded up to a power of two.
 template <bool BF, bool EACH, int NMAX, int UNROLL>
-__global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
+__global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
   constexpr int kB = NMAX < 8 ? NMAX : 8;
   constexpr int kBatches = NMAX / kB;
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const int n = args.nranks;
   const BlockCoord bc = block_coord(args);
   const DevOp op = args.ops[bc.op];
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kBlock) void onepass_tree(KArgs args) {
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
           float level[NMAX];
           for (int r = 0; r < n; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
@@ -536,8 +537,8 @@ struct DTreeFold {
 };
 
 template <bool BF, bool EACH, int N, int UNROLL>
-__global__ __launch_bounds__(kBlock) void onepass_dtree(KArgs args) {
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+__global__ __launch_bounds__(kOPB) void onepass_dtree(KArgs args) {
+  constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const BlockCoord bc = block_coord(args);
   const DevOp op = args.ops[bc.op];
   const bool second = op.aux != 0;
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(kBlock) void onepass_dtree(KArgs args) {
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
+          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
           float v;
           if (!second)
@@ -587,7 +588,6 @@ constexpr int kUnrollCold = AR_COLD_UNROLL;
 constexpr int kOnePassUnrollF32 = AR_ONEPASS_UNROLL_F32, kFoldBatchF32 = AR_FOLD_BATCH_F32;
 constexpr int kOnePassUnrollBF16 = AR_ONEPASS_UNROLL_BF16, kFoldBatchBF16 = AR_FOLD_BATCH_BF16;
 constexpr bool kNtsRank = AR_NTS_RANK;
-constexpr int64_t kCacheBytes = AR_CACHE_BYTES;
 constexpr bool kNtsScratch = AR_NTS_SCRATCH;
 
 template <int FLAGS, int U>
@@ -615,12 +615,12 @@ hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
 template <bool BF, bool EACH>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
-  if (n <= 2) hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a);
-  else if (n <= 4) hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a);
-  else if (n <= 8) hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a);
-  else if (n <= 16) hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a);
-  else if (n <= 32) hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a);
-  else if (n <= 64) hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a);
+  if (n <= 2) hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 4) hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 8) hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 16) hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 32) hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 64) hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -629,12 +629,12 @@ template <bool BF, bool EACH>
 hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
   switch (n) {
-    case 2: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 2, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 4, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 8, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 16, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 32, U>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 64, U>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -652,14 +652,12 @@ dim3 grid_for(uint32_t tiles, uint32_t nops) {
 #endif
 }
 
-bool is_cold(int64_t written_bytes, bool out_scratch) { return !out_scratch && written_bytes > kCacheBytes; }
-
 int64_t tile_elems(int32_t kind, bool cold) {
   const int64_t u = cold ? kUnrollCold : kUnrollWarm;
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * u;
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
-    default: return static_cast<int64_t>(kBlock) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
+    default: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }
 }
 
@@ -691,19 +689,19 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
       return hipErrorInvalidValue;
     case kKindRing:
       if ((kind & 3) == 2)
-        hipLaunchKernelGGL((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else if ((kind & 3) == 1)
-        hipLaunchKernelGGL((onepass_ring<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_ring<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_ring<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_ring<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
       return hipGetLastError();
     case kKindHier:
       if ((kind & 3) == 2)
-        hipLaunchKernelGGL((onepass_hier<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_hier<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else if ((kind & 3) == 1)
-        hipLaunchKernelGGL((onepass_hier<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_hier<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_hier<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((onepass_hier<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
       return hipGetLastError();
     case kKindTree:
       if ((kind & 3) == 2) return launch_tree<true, true>(a.nranks, grid, a, s);

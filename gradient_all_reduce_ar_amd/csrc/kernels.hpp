@@ -19,6 +19,9 @@
 #ifndef AR_BLOCK
 #define AR_BLOCK 256
 #endif
+#ifndef AR_ONEPASS_BLOCK
+#define AR_ONEPASS_BLOCK AR_BLOCK
+#endif
 #ifndef AR_NTL
 #define AR_NTL 1
 #endif
@@ -42,9 +45,6 @@
 #endif
 #ifndef AR_COLD_UNROLL
 #define AR_COLD_UNROLL 1
-#endif
-#ifndef AR_CACHE_BYTES
-#define AR_CACHE_BYTES (256ll << 20)  // MI355X Infinity Cache (MALL) capacity
 #endif
 #ifndef AR_ONEPASS_UNROLL_F32
 #define AR_ONEPASS_UNROLL_F32 2
@@ -103,10 +103,6 @@ int64_t q_tile_blocks(int32_t kind);
 // kind kKRing / kKHier / kKTree / kKDTree) on stream s.
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s);
 
-// Whether a step launch takes the streaming (cold) shape: it writes more
-// into rank buffers than the Infinity Cache holds.
-bool is_cold(int64_t written_bytes, bool out_scratch);
-
 // Tile (elements per block) of a kernel kind in the warm or cold shape.
 int64_t tile_elems(int32_t kind, bool cold);
 
@@ -115,7 +111,8 @@ dim3 grid_for(uint32_t tiles, uint32_t nops);
 
 // Launches the kernel of `kind` on stream s.  out_scratch: the launch's
 // outputs are fp32 scratch slots (selects the store cache policy); cold: the
-// streaming shape (see is_cold).
+// streaming shape, taken by a launch that writes more into rank buffers than
+// the device cache holds (the executor decides).
 hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch, bool cold);
 
 }  // namespace ar_dev

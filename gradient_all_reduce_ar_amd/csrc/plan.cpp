@@ -269,6 +269,57 @@ struct PartialMap {
   }
 };
 
+// Launch order.  Rounds run in order; within the hierarchical schedule's
+// group phases (1: reduce-scatter, 3: all-gather) the groups are independent,
+// so when a round's writes exceed the device cache the phase runs group by
+// group instead (every round of group 0, then of group 1, ...): each launch
+// then writes one group's share, which the next round reads back from the
+// cache.  The bits are the same in either order.
+struct LaunchKey {
+  int32_t phase, group, step;
+  bool operator<(const LaunchKey &o) const {
+    return phase != o.phase ? phase < o.phase : group != o.group ? group < o.group : step < o.step;
+  }
+  bool operator==(const LaunchKey &o) const { return phase == o.phase && group == o.group && step == o.step; }
+};
+
+bool split_groups(const Plan &p) {
+  const int G = p.group_size, M = p.nranks / p.group_size;
+  if (p.sched != kHier || G < 2 || M < 2) return false;
+  // bytes a phase-1 round writes: N receivers x one slice, in what the
+  // round stores (fp32 partials for kBF16, codes for kI8EF)
+  const int64_t wb = p.dtype == kBF16Each ? 2 : p.dtype == kI8EF ? 1 : 4;
+  const int64_t slice = unit_elems(p, 0, p.units) / G;
+  return static_cast<int64_t>(p.nranks) * slice * wb > p.cache_bytes;
+}
+
+std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) {
+  const bool split = split_groups(p);
+  const int G = p.group_size, M = p.nranks / p.group_size;
+  const int p2 = G - 1, p3 = G - 1 + 2 * (M - 1);  // first rounds of phases 2 and 3
+  std::vector<std::pair<LaunchKey, size_t>> idx;
+  for (size_t i = 0; i < p.xfers.size(); ++i) {
+    const Transfer &x = p.xfers[i];
+    LaunchKey k{0, 0, x.step};
+    if (split) {
+      k.phase = x.step < p2 ? 0 : x.step < p3 ? 1 : 2;
+      if (k.phase != 1) k.group = x.src / G;
+    }
+    idx.push_back({k, i});
+  }
+  std::stable_sort(idx.begin(), idx.end(),
+                   [](const std::pair<LaunchKey, size_t> &a, const std::pair<LaunchKey, size_t> &b) {
+                     return a.first < b.first;
+                   });
+  std::vector<Transfer> out;
+  keys.clear();
+  for (const auto &e : idx) {
+    out.push_back(p.xfers[e.second]);
+    keys.push_back(e.first);
+  }
+  return out;
+}
+
 std::string lower_steps(Plan &p, bool fuse) {
   p.launches.clear();
   const bool bf = p.dtype == kBF16;  // fp32 partials in scratch
@@ -277,10 +328,12 @@ std::string lower_steps(Plan &p, bool fuse) {
   PartialMap partial(p.nranks);
   std::vector<bool> finals;  // per launch: all its reduces complete their range
   int max_slot = -1;
+  std::vector<LaunchKey> keys;
+  const std::vector<Transfer> xs = launch_order(p, keys);
   size_t j = 0;
-  while (j < p.xfers.size()) {
+  while (j < xs.size()) {
     size_t j1 = j;
-    while (j1 < p.xfers.size() && p.xfers[j1].step == p.xfers[j].step) ++j1;
+    while (j1 < xs.size() && keys[j1] == keys[j]) ++j1;
     // Reduces that exchange the same range in both directions (recursive
     // doubling) become one op writing the sum to both ranks (a + b == b + a
     // bit for bit); the k-th reduce into the same receiver range runs in the
@@ -289,13 +342,13 @@ std::string lower_steps(Plan &p, bool fuse) {
     // own receiver's accumulating sum.
     std::vector<size_t> items;
     for (size_t t = j; t < j1; ++t)
-      if (p.xfers[t].hi > p.xfers[t].lo) items.push_back(t);
+      if (xs[t].hi > xs[t].lo) items.push_back(t);
     std::vector<long> partner(items.size(), -1);
     for (size_t u = 0; u < items.size(); ++u) {
-      const Transfer &x = p.xfers[items[u]];
+      const Transfer &x = xs[items[u]];
       if (x.kind != kReduce || partner[u] >= 0) continue;
       for (size_t v = u + 1; v < items.size(); ++v) {
-        const Transfer &y = p.xfers[items[v]];
+        const Transfer &y = xs[items[v]];
         if (y.kind == kReduce && partner[v] < 0 && y.src == x.dst && y.dst == x.src && y.lo == x.lo && y.hi == x.hi) {
           partner[u] = static_cast<long>(v);
           partner[v] = static_cast<long>(u);
@@ -307,7 +360,7 @@ std::string lower_steps(Plan &p, bool fuse) {
     std::vector<int> sub(items.size(), 0);
     int nsub = 1;
     for (size_t u = 0; u < items.size(); ++u) {
-      const Transfer &x = p.xfers[items[u]];
+      const Transfer &x = xs[items[u]];
       if (x.kind != kReduce || (partner[u] >= 0 && partner[u] < static_cast<long>(u))) continue;
       int &cnt = heard[{x.dst, x.lo, x.hi}];
       sub[u] = cnt++;
@@ -321,7 +374,7 @@ std::string lower_steps(Plan &p, bool fuse) {
       std::vector<std::pair<int, std::pair<int64_t, int64_t>>> to_mark;
       for (size_t u = 0; u < items.size(); ++u) {
         if (sub[u] != sr || (partner[u] >= 0 && partner[u] < static_cast<long>(u))) continue;
-        const Transfer &x = p.xfers[items[u]];
+        const Transfer &x = xs[items[u]];
         const bool pair = partner[u] >= 0;
         Op op{x.lo, x.hi, kLocNone, kLocNone, kLocNone, kLocNone, 0};
         int32_t kind;

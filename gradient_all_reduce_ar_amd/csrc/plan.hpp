@@ -75,6 +75,7 @@ struct Launch {
   std::vector<Op> ops;
 };
 
+constexpr int64_t kDefaultCacheBytes = 256ll << 20;  // MI355X Infinity Cache (MALL)
 constexpr int32_t kMaxExecRanks = 64;    // ranks a plan can execute on the GPU
 constexpr int32_t kMaxPlanRanks = 1024;  // ranks a plan can describe (stats, cost)
 
@@ -90,6 +91,7 @@ struct Plan {
   int32_t nslots = 0;            // fp32 scratch slots used by `launches`
   int64_t slot_stride = 0;       // elements per slot (multiple of 64)
   int64_t units = 0;             // what transfer ranges count: elements, or blocks (kI8EF)
+  int64_t cache_bytes = kDefaultCacheBytes;  // device cache the launch order and shapes assume
   int64_t code_stride = 0;       // kI8EF: bytes of codes per rank slot (multiple of 256)
   int64_t scale_stride = 0;      // kI8EF: fp32 scales per rank slot (multiple of 64)
   std::vector<uint64_t> bytes_sent;
@@ -114,7 +116,7 @@ uint64_t workspace_bytes(const Plan &p);
 std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype,
                        Sched sched, Exec exec, bool *unsupported);
 
-// Re-lowers an existing plan for another exec mode.
+// Re-lowers an existing plan for another exec mode (its cache_bytes kept).
 std::string relower(Plan &p, Exec exec);
 
 // Per-round alpha-beta model over the transfers (seconds).

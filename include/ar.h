@@ -166,6 +166,18 @@ ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t d
 ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
 
 /*
+ * The device cache capacity (bytes) the plan's launch order and kernel
+ * shapes assume; default 256 MiB, MI355X's Infinity Cache.  A step launch
+ * that writes more than this into rank buffers takes the streaming kernel
+ * shape; and the hierarchical schedule runs its two group phases group by
+ * group (all rounds of group 0, then group 1, ...) when one round of a phase
+ * would write more than this, so that each round's output is still cached
+ * when the next round reads it.  Results are bit-identical for any value.
+ * Host only.
+ */
+ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes);
+
+/*
  * Allocates the plan's device op tables and, for bf16, its fp32 scratch on
  * the current HIP device, and uploads the tables (synchronously).  Called
  * implicitly by the first ar_allreduce; call it explicitly before capturing

@@ -150,3 +150,23 @@ def test_errors():
     finally:
         B.ar_plan_destroy(p)
         B.ar_plan_destroy(pf)
+
+
+@pytest.mark.parametrize("n,g", [(16, 8), (8, 4), (9, 3)])
+def test_group_by_group_order_int8(n, g):
+    rng = np.random.default_rng(n + g)
+    count = 9 * Q + 5
+    xs = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+    es = [(rng.standard_normal(count) * 1e-2).astype(np.float32) for _ in range(n)]
+    ref_b, ref_e = [x.copy() for x in xs], [e.copy() for e in es]
+    oracle.run_int8ef(ref_b, "hierarchical", errs=ref_e, group_size=g)
+    p = B.ar_plan_create(n, g, count, "int8_ef", "hierarchical")
+    try:
+        B.ar_plan_set_cache_bytes(p, 16)
+        got_b, got_e = [x.copy() for x in xs], [e.copy() for e in es]
+        plan_interp.run_int8(p, got_b, got_e, g)
+    finally:
+        B.ar_plan_destroy(p)
+    for r in range(n):
+        np.testing.assert_array_equal(got_b[r].view(np.uint32), ref_b[r].view(np.uint32))
+        np.testing.assert_array_equal(got_e[r].view(np.uint32), ref_e[r].view(np.uint32))

@@ -275,3 +275,50 @@ def test_selector_agrees_with_oracle_over_sizes(n):
         name, t = B.ar_select_schedule(n, 1, count, "fp32", *args, candidates=cands)
         ob = _oracle_best(n, 1, count, 4, cands, args)
         assert t == pytest.approx(ob[1], rel=1e-12)
+
+
+HIER_SPLIT = [(16, 8), (16, 4), (8, 4), (6, 3), (9, 3), (12, 3), (64, 8)]
+
+
+@pytest.mark.parametrize("n,g", HIER_SPLIT)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused"])
+def test_group_by_group_order_matches_oracle(n, g, dtype, mode):
+    """With a cache smaller than one round's writes, the hierarchical group
+    phases run group by group; the results are the oracle's bit for bit."""
+    for count in (37, 1031):
+        xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
+        ref = oracle.run([x.copy() for x in xs], dtype, "hierarchical", group_size=g)
+        p = _plan(n, g, count, dtype, "hierarchical")
+        try:
+            B.ar_plan_set_exec(p, mode)
+            B.ar_plan_set_cache_bytes(p, 64)
+            got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+            n_launch = B.ar_plan_num_launches(p)
+        finally:
+            B.ar_plan_destroy(p)
+        bv = np.uint32 if dtype == "fp32" else np.uint16
+        for r in range(n):
+            np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv), err_msg=f"n={n} g={g} {dtype} {mode} r={r}")
+        m = n // g
+        fused = mode == "steps"
+        assert n_launch == 2 * m * (g - 1) + 2 * (m - 1) - (1 if fused else 0)
+
+
+def test_group_by_group_order_shape():
+    """C4 shape at its real size: the default 256 MiB cache is smaller than a
+    phase-1 round's 384 MiB of writes, so group 0's seven rounds come first,
+    then group 1's; phase 2 is one fused launch; phase 3 likewise by group.
+    A large cache keeps the round-by-round order (15 launches)."""
+    p = _plan(16, 8, 12288 * 4096, "fp32", "hierarchical")
+    try:
+        first_rank = [int(B.ar_plan_launch_ops(p, i)["a"].min()) for i in range(B.ar_plan_num_launches(p))]
+        nops = [B.ar_plan_launch_info(p, i)[1] for i in range(B.ar_plan_num_launches(p))]
+        assert first_rank == [0] * 7 + [8] * 7 + [0] + [0] * 7 + [8] * 7
+        assert nops == [8] * 14 + [16] + [8] * 14
+        model = B.ar_plan_stats(p)["hbm_bytes_model"]
+        B.ar_plan_set_cache_bytes(p, 1 << 30)
+        assert B.ar_plan_num_launches(p) == 15
+        assert B.ar_plan_stats(p)["hbm_bytes_model"] == model
+    finally:
+        B.ar_plan_destroy(p)
