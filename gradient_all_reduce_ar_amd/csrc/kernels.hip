@@ -40,8 +40,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming accesses.  Every input byte is read once per kernel, so loads
 // carry the non-temporal hint (AR_NTL).  Stores carry it where measurement
-// says it pays: into fp32 scratch and in the one-pass kernels, not into rank
-// buffers written by a step (AR_NTS_*).  The hints never change results.
+// says it pays: in the one-pass kernels, whose output nothing reads back,
+// but not into rank buffers or fp32 scratch written by a step, which the
+// next step reads from the cache (AR_NTS_*).  The hints never change results.
 template <typename T>
 __device__ __forceinline__ T ld(const char *p) {
 #if AR_NTL

@@ -29,7 +29,7 @@
 #define AR_NTS_RANK 0
 #endif
 #ifndef AR_NTS_SCRATCH
-#define AR_NTS_SCRATCH 1
+#define AR_NTS_SCRATCH 0
 #endif
 #ifndef AR_NTS_ONEPASS
 #define AR_NTS_ONEPASS 1

@@ -269,12 +269,18 @@ struct PartialMap {
   }
 };
 
-// Launch order.  Rounds run in order; within the hierarchical schedule's
-// group phases (1: reduce-scatter, 3: all-gather) the groups are independent,
-// so when a round's writes exceed the device cache the phase runs group by
-// group instead (every round of group 0, then of group 1, ...): each launch
-// then writes one group's share, which the next round reads back from the
-// cache.  The bits are the same in either order.
+// Launch order.  Rounds run in order, and every round of a schedule writes
+// what the next one reads.  When a round writes more than the device cache
+// holds, that output would stream from DRAM again, so the planner reorders
+// (the bits are the same in any of these orders, since each element's fold
+// depends only on its own chunk's rounds):
+//  * hierarchical: the group phases (1: reduce-scatter, 3: all-gather) are
+//    independent across groups and run group by group (every round of group
+//    0, then of group 1, ...);
+//  * otherwise: the element range is cut into K pieces at the same offsets
+//    on every rank and the whole schedule runs on piece 0, then piece 1, ...
+//    (each transfer restricted to the piece), K the smallest count whose
+//    rounds fit in the cache.
 struct LaunchKey {
   int32_t phase, group, step;
   bool operator<(const LaunchKey &o) const {
@@ -283,38 +289,63 @@ struct LaunchKey {
   bool operator==(const LaunchKey &o) const { return phase == o.phase && group == o.group && step == o.step; }
 };
 
+// Bytes a round stores per element it writes: fp32 (or fp32 partials of
+// kBF16), bf16, or INT8 codes.
+int64_t round_write_bytes(const Plan &p) { return p.dtype == kBF16Each ? 2 : p.dtype == kI8EF ? 1 : 4; }
+
 bool split_groups(const Plan &p) {
   const int G = p.group_size, M = p.nranks / p.group_size;
   if (p.sched != kHier || G < 2 || M < 2) return false;
-  // bytes a phase-1 round writes: N receivers x one slice, in what the
-  // round stores (fp32 partials for kBF16, codes for kI8EF)
-  const int64_t wb = p.dtype == kBF16Each ? 2 : p.dtype == kI8EF ? 1 : 4;
-  const int64_t slice = unit_elems(p, 0, p.units) / G;
-  return static_cast<int64_t>(p.nranks) * slice * wb > p.cache_bytes;
+  const int64_t slice = unit_elems(p, 0, p.units) / G;  // a phase-1 round: N receivers x one slice
+  return static_cast<int64_t>(p.nranks) * slice * round_write_bytes(p) > p.cache_bytes;
+}
+
+int split_pieces(const Plan &p) {
+  if (p.sched == kHier || p.units == 0) return 1;
+  std::vector<int64_t> per_round(static_cast<size_t>(p.nsteps), 0);
+  for (const Transfer &x : p.xfers) per_round[x.step] += unit_elems(p, x.lo, x.hi);
+  int64_t worst = 0;
+  for (int64_t v : per_round) worst = std::max(worst, v);
+  const int64_t bytes = worst * round_write_bytes(p);
+  const int64_t k = p.cache_bytes > 0 ? (bytes + p.cache_bytes - 1) / p.cache_bytes : 64;
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
 }
 
 std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) {
-  const bool split = split_groups(p);
-  const int G = p.group_size, M = p.nranks / p.group_size;
-  const int p2 = G - 1, p3 = G - 1 + 2 * (M - 1);  // first rounds of phases 2 and 3
-  std::vector<std::pair<LaunchKey, size_t>> idx;
-  for (size_t i = 0; i < p.xfers.size(); ++i) {
-    const Transfer &x = p.xfers[i];
-    LaunchKey k{0, 0, x.step};
-    if (split) {
-      k.phase = x.step < p2 ? 0 : x.step < p3 ? 1 : 2;
-      if (k.phase != 1) k.group = x.src / G;
+  std::vector<std::pair<LaunchKey, Transfer>> idx;
+  const int pieces = split_pieces(p);
+  if (pieces > 1) {
+    // piece boundaries on multiples of 64 units (whole tiles stay whole)
+    std::vector<int64_t> cut;
+    for (int k = 0; k <= pieces; ++k) cut.push_back(k == pieces ? p.units : (p.units * k / pieces) / 64 * 64);
+    for (int k = 0; k < pieces; ++k)
+      for (const Transfer &x : p.xfers) {
+        Transfer y = x;
+        y.lo = std::max(x.lo, cut[k]);
+        y.hi = std::min(x.hi, cut[k + 1]);
+        if (y.hi > y.lo) idx.push_back({LaunchKey{k, 0, x.step}, y});
+      }
+  } else {
+    const bool split = split_groups(p);
+    const int G = p.group_size, M = p.nranks / p.group_size;
+    const int p2 = G - 1, p3 = G - 1 + 2 * (M - 1);  // first rounds of phases 2 and 3
+    for (const Transfer &x : p.xfers) {
+      LaunchKey k{0, 0, x.step};
+      if (split) {
+        k.phase = x.step < p2 ? 0 : x.step < p3 ? 1 : 2;
+        if (k.phase != 1) k.group = x.src / G;
+      }
+      idx.push_back({k, x});
     }
-    idx.push_back({k, i});
   }
   std::stable_sort(idx.begin(), idx.end(),
-                   [](const std::pair<LaunchKey, size_t> &a, const std::pair<LaunchKey, size_t> &b) {
+                   [](const std::pair<LaunchKey, Transfer> &a, const std::pair<LaunchKey, Transfer> &b) {
                      return a.first < b.first;
                    });
   std::vector<Transfer> out;
   keys.clear();
   for (const auto &e : idx) {
-    out.push_back(p.xfers[e.second]);
+    out.push_back(e.second);
     keys.push_back(e.first);
   }
   return out;

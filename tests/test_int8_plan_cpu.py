@@ -170,3 +170,25 @@ def test_group_by_group_order_int8(n, g):
     for r in range(n):
         np.testing.assert_array_equal(got_b[r].view(np.uint32), ref_b[r].view(np.uint32))
         np.testing.assert_array_equal(got_e[r].view(np.uint32), ref_e[r].view(np.uint32))
+
+
+@pytest.mark.parametrize("sched,n,g", [("ring", 4, 1), ("rabenseifner", 8, 1), ("tree", 5, 1), ("double_tree", 4, 1)])
+def test_piece_by_piece_order_int8(sched, n, g):
+    rng = np.random.default_rng(n + 31)
+    count = 300 * Q + 5  # pieces are cut on multiples of 64 blocks
+    xs = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+    es = [(rng.standard_normal(count) * 1e-2).astype(np.float32) for _ in range(n)]
+    ref_b, ref_e = [x.copy() for x in xs], [e.copy() for e in es]
+    oracle.run_int8ef(ref_b, sched, errs=ref_e, group_size=g)
+    p = B.ar_plan_create(n, g, count, "int8_ef", sched)
+    try:
+        n0 = B.ar_plan_num_launches(p)
+        B.ar_plan_set_cache_bytes(p, 64)
+        assert B.ar_plan_num_launches(p) > n0  # the schedule now runs piece by piece
+        got_b, got_e = [x.copy() for x in xs], [e.copy() for e in es]
+        plan_interp.run_int8(p, got_b, got_e, g)
+    finally:
+        B.ar_plan_destroy(p)
+    for r in range(n):
+        np.testing.assert_array_equal(got_b[r].view(np.uint32), ref_b[r].view(np.uint32))
+        np.testing.assert_array_equal(got_e[r].view(np.uint32), ref_e[r].view(np.uint32))

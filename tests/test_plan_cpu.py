@@ -322,3 +322,43 @@ def test_group_by_group_order_shape():
         assert B.ar_plan_stats(p)["hbm_bytes_model"] == model
     finally:
         B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n,g", [s for s in SCHEDS if s[0] != "hierarchical"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+def test_piece_by_piece_order_matches_oracle(sched, n, g, dtype):
+    """With a cache smaller than one round's writes, the schedule runs on
+    element pieces one after another; the results are the oracle's bit for
+    bit (including pieces that cut through chunks)."""
+    for count in (37, 5000):
+        xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
+        ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+        for mode in ("steps", "steps_unfused"):
+            p = _plan(n, g, count, dtype, sched)
+            try:
+                B.ar_plan_set_exec(p, mode)
+                B.ar_plan_set_cache_bytes(p, 2048)
+                got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+            finally:
+                B.ar_plan_destroy(p)
+            bv = np.uint32 if dtype == "fp32" else np.uint16
+            for r in range(n):
+                np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv),
+                                              err_msg=f"{sched} n={n} {dtype} {mode} count={count} r={r}")
+
+
+def test_piece_counts():
+    """C3 (bf16 ring, fp32 partials: 403 MB written per round) runs in two
+    pieces; C2 (fp32 ring, 201 MB per round) in one."""
+    p3 = _plan(16, 8, 2 * 12288 * 4096, "bf16", "ring")
+    p2 = _plan(16, 8, 12288 * 4096, "fp32", "ring")
+    try:
+        assert B.ar_plan_num_launches(p2) == 29
+        assert B.ar_plan_num_launches(p3) == 2 * 29
+        lo = [int(B.ar_plan_launch_ops(p3, i)["lo"].min()) for i in range(58)]
+        hi = [int(B.ar_plan_launch_ops(p3, i)["hi"].max()) for i in range(58)]
+        half = (2 * 12288 * 4096 // 2) // 64 * 64
+        assert max(hi[:29]) <= half and min(lo[29:]) >= half
+    finally:
+        B.ar_plan_destroy(p3)
+        B.ar_plan_destroy(p2)
