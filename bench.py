@@ -64,7 +64,11 @@ def kernel_label(kind):
     if fam == 0x200:
         return f"chunk_copy<{kind & 0xFF}>"
     if fam == 0x800:
+        if kind & 0x13:  # fused hop: raw operands or final decode
+            return f"q_hop<{kind & 0xFF}>"
         return f"q_reduce<{'true' if kind & 8 else 'false'}>"
+    if fam == 0x900 and kind & 16:
+        return f"q_copy_dec<{'false' if kind & 32 else 'true'}>"
     if fam >= 0x700:
         return KIND_NAMES[fam]
     if kind & 3 == 3:  # one-pass fold of an INT8 plan
@@ -105,9 +109,16 @@ def launch_bytes(B, plan, i, nranks, elem, count):
         if fam == B.KIND_QENCODE:
             return el * 13 + 4 * blocks, kind  # g, e in; codes, e out; scales
         if fam == B.KIND_QREDUCE:
-            return (el + 4 * blocks) * (4 if kind & 8 else 3), kind
+            outs = 2 if kind & 8 else 1
+            nb = sum(el * 12 if kind & raw else el + 4 * blocks for raw in (1, 2))  # own g, e / codes in
+            if not kind & 32:
+                nb += (el + 4 * blocks) * outs  # codes and scales out
+            if kind & 16:
+                nb += el * 4 * outs  # final values decoded into the buffers
+            return nb, kind
         if fam == B.KIND_QCOPY:
-            return (el + 4 * blocks) * 2, kind
+            nb = (el + 4 * blocks) * (1 if kind & 32 else 2) + (el * 4 if kind & 16 else 0)
+            return nb, kind
         return el * 5 + 4 * blocks, kind  # decode: codes, scales in; fp32 out
     if fam == B.KIND_REDUCE:
         if elem == 4:

@@ -592,9 +592,15 @@ void compute_stats(Plan &p) {
       } else if (fam == kKQEncode) {
         h += el * (4 + 4 + 1 + 4) + 4 * len;  // g, e in; codes, e out; scales
       } else if (fam == kKQReduce) {
-        h += (el + 4 * len) * (2 + outs);
+        const int32_t f = L.kind;
+        for (int32_t raw : {f & kQFlagARaw, f & kQFlagBRaw})
+          h += raw ? el * 12 : el + 4 * len;  // own g, e in and e out, or codes and scale in
+        if (!(f & kQFlagNoCode)) h += (el + 4 * len) * outs;
+        if (f & kQFlagDec) h += el * 4 * outs;
       } else if (fam == kKQCopy) {
-        h += (el + 4 * len) * 2;
+        h += el + 4 * len;
+        if (!(L.kind & kQFlagNoCode)) h += el + 4 * len;
+        if (L.kind & kQFlagDec) h += el * 4;
       } else if (fam == kKQDecode) {
         h += el * (1 + 4) + 4 * len;
       } else if (p.dtype == kI8EF) {
@@ -607,8 +613,123 @@ void compute_stats(Plan &p) {
   p.hbm_bytes = h;
 }
 
+// Unit ranges per rank (a small interval list).
+struct RangeSet {
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> r;
+  explicit RangeSet(int n) : r(n) {}
+  void add(int q, int64_t lo, int64_t hi) { r[q].push_back({lo, hi}); }
+  bool overlaps(int q, int64_t lo, int64_t hi) const {
+    for (const auto &x : r[q])
+      if (x.first < hi && lo < x.second) return true;
+    return false;
+  }
+  bool covers(int q, int64_t lo, int64_t hi) const {  // union of the ranges covers [lo, hi)
+    std::vector<std::pair<int64_t, int64_t>> v = r[q];
+    std::sort(v.begin(), v.end());
+    int64_t at = lo;
+    for (const auto &x : v)
+      if (x.first <= at) at = std::max(at, x.second);
+    return at >= hi;
+  }
+};
+
+// Fused INT8 step lowering: the first reduce that touches a rank's range
+// encodes g + e itself (the residual is written there), and the last write
+// of a rank's range also decodes it into the rank's buffer, so no separate
+// encode or decode pass runs.  Returns false (launches untouched) when the
+// schedule does not have that shape: an operand range partly consumed, a
+// copy of codes never written, fused outputs that disagree, or a rank range
+// never consumed or never finished.
+bool fuse_quantized(Plan &p) {
+  const int n = p.nranks;
+  struct Tag {
+    int32_t flags;
+  };
+  std::vector<std::vector<Tag>> tags(p.launches.size());
+  PartialMap consumed(n), written(n);
+  RangeSet raw_used(n);
+  for (size_t i = 0; i < p.launches.size(); ++i) {
+    const Launch &L = p.launches[i];
+    const int32_t fam = L.kind & 0xF00;
+    for (const Op &o : L.ops) {
+      int32_t f = 0;
+      auto operand = [&](int q, int32_t raw_flag) -> bool {
+        if (written.state(q, o.lo, o.hi) == 1) return true;  // codes present
+        if (written.state(q, o.lo, o.hi) != 0 || consumed.state(q, o.lo, o.hi) != 0) return false;
+        f |= raw_flag;
+        return true;
+      };
+      if (fam == kKQReduce) {
+        if (!operand(o.a, kQFlagARaw) || !operand(o.b, kQFlagBRaw)) return false;
+      } else if (fam == kKQCopy) {
+        if (written.state(o.a, o.lo, o.hi) != 1) return false;
+      } else {
+        return false;
+      }
+      tags[i].push_back({f});
+    }
+    // marks after the launch: its ops are hazard-free among themselves
+    for (size_t k = 0; k < L.ops.size(); ++k) {
+      const Op &o = L.ops[k];
+      if (tags[i][k].flags & kQFlagARaw) {
+        consumed.mark(o.a, o.lo, o.hi);
+        raw_used.add(o.a, o.lo, o.hi);
+      }
+      if (tags[i][k].flags & kQFlagBRaw) {
+        consumed.mark(o.b, o.lo, o.hi);
+        raw_used.add(o.b, o.lo, o.hi);
+      }
+      written.mark(o.o, o.lo, o.hi);
+      if (o.o2 != kLocNone) written.mark(o.o2, o.lo, o.hi);
+    }
+  }
+  // backward: is an output the last write of that range, is it read later?
+  RangeSet later_write(n), later_read(n), finished(n);
+  for (size_t i = p.launches.size(); i-- > 0;) {
+    const Launch &L = p.launches[i];
+    const bool reduce = (L.kind & 0xF00) == kKQReduce;
+    for (size_t k = 0; k < L.ops.size(); ++k) {
+      const Op &o = L.ops[k];
+      const bool fin = !later_write.overlaps(o.o, o.lo, o.hi);
+      bool need = later_read.overlaps(o.o, o.lo, o.hi);
+      if (o.o2 != kLocNone) {
+        if (fin != !later_write.overlaps(o.o2, o.lo, o.hi)) return false;
+        need = need || later_read.overlaps(o.o2, o.lo, o.hi);  // codes go to both or neither
+      }
+      if (fin) tags[i][k].flags |= kQFlagDec | (need ? 0 : kQFlagNoCode);
+    }
+    for (size_t k = 0; k < L.ops.size(); ++k) {
+      const Op &o = L.ops[k];
+      later_write.add(o.o, o.lo, o.hi);
+      if (o.o2 != kLocNone) later_write.add(o.o2, o.lo, o.hi);
+      if (tags[i][k].flags & kQFlagDec) {
+        finished.add(o.o, o.lo, o.hi);
+        if (o.o2 != kLocNone) finished.add(o.o2, o.lo, o.hi);
+      }
+      if (!reduce || !(tags[i][k].flags & kQFlagARaw)) later_read.add(o.a, o.lo, o.hi);
+      if (reduce && !(tags[i][k].flags & kQFlagBRaw)) later_read.add(o.b, o.lo, o.hi);
+    }
+  }
+  for (int q = 0; q < n; ++q)
+    if (!raw_used.covers(q, 0, p.units) || !finished.covers(q, 0, p.units)) return false;
+  // split each launch into launches of uniform flags
+  std::vector<Launch> out;
+  for (size_t i = 0; i < p.launches.size(); ++i) {
+    std::map<int32_t, Launch> by;
+    for (size_t k = 0; k < p.launches[i].ops.size(); ++k) {
+      Launch &L = by[tags[i][k].flags];
+      L.kind = p.launches[i].kind | tags[i][k].flags;
+      L.ops.push_back(p.launches[i].ops[k]);
+    }
+    for (auto &kv : by) out.push_back(std::move(kv.second));
+  }
+  p.launches = std::move(out);
+  return true;
+}
+
 // Blockwise INT8: encode every rank, run the schedule over code slots,
-// decode every rank.
+// decode every rank -- or, fused, with the encode and decode folded into the
+// schedule's first and last touches of each range.
 std::string lower_quantized(Plan &p, bool fuse) {
   std::string err = lower_steps(p, fuse);
   if (!err.empty()) return err;
@@ -616,6 +737,11 @@ std::string lower_quantized(Plan &p, bool fuse) {
   if (p.count == 0) {
     p.launches.clear();
     return "";
+  }
+  if (fuse && p.nranks > 1) {
+    const std::vector<Launch> keep = p.launches;
+    if (fuse_quantized(p)) return "";
+    p.launches = keep;
   }
   Launch enc{kKQEncode, {}}, dec{kKQDecode, {}};
   for (int r = 0; r < p.nranks; ++r) {

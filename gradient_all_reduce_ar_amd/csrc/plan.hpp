@@ -59,10 +59,16 @@ constexpr int32_t kFlagABf = 1, kFlagBBf = 2, kFlagOBf = 4, kFlagO2 = 8;
 //   kKQReduce [| kFlagO2]: codes[o] (and codes[o2]) = Q(D(codes[a]) + D(codes[b])).
 //   kKQCopy: codes[o] = codes[a] (codes and scales).
 //   kKQDecode: g_a = D(codes[a]).
+//   Flags of the fused step lowering (no separate encode or decode launch):
+//   kQFlagARaw / kQFlagBRaw: that operand is the rank's own g + e, encoded
+//   in the kernel (residual written back); kQFlagDec: the outputs are the
+//   ranks' final codes and are also decoded into their buffers; kQFlagNoCode:
+//   nothing reads those codes later, so they are not stored.
 constexpr int32_t kKQEncode = 0x700;
 constexpr int32_t kKQReduce = 0x800;
 constexpr int32_t kKQCopy = 0x900;
 constexpr int32_t kKQDecode = 0xA00;
+constexpr int32_t kQFlagARaw = 1, kQFlagBRaw = 2, kQFlagDec = 16, kQFlagNoCode = 32;
 
 struct Op {
   int64_t lo, hi;

@@ -275,6 +275,146 @@ __global__ void __launch_bounds__(AR_BLOCK) q_reduce(QArgs a) {
   }
 }
 
+// Fused hop (kQFlag* in F, kFlagO2): an operand is either a rank's codes
+// or, raw, the rank's own g + e, encoded here (its residual stored); the
+// re-encoded sum goes to o (and o2) as codes unless nothing reads them
+// later, and, for a rank's final codes, also decoded into its buffer.  Half a
+// wavefront per block, 4 elements per lane (the fp32 side sets the shape).
+template <int F>
+__device__ __forceinline__ void hop_operand(const QArgs &a, int r, int64_t b, int64_t e0, int lane, float v[4]) {
+  if constexpr (F != 0) {
+    float x[4];
+    load4(a.grad[r], e0, a.count, x);
+    if (a.has_err) {
+      float ev[4];
+      load4(a.err[r], e0, a.count, ev);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = x[i] + ev[i];
+    }
+    const Scale sc =
+        make_scale(max32(max(max(abs_bits(x[0]), abs_bits(x[1])), max(abs_bits(x[2]), abs_bits(x[3])))));
+    float k[4];
+    quantize<4>(x, sc, k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = k[i] * sc.s;
+    if (a.has_err) {
+      float res[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) res[i] = x[i] - v[i];
+      store4<true>(a.err[r], e0, a.count, res);
+    }
+  } else {
+    (void)lane;
+    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(a.codes + r * a.code_stride + e0));
+    const float s = a.scales[r * a.scale_stride + b];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = code(w, i) * s;
+  }
+}
+
+template <int F>
+__global__ void __launch_bounds__(AR_BLOCK) q_hop(QArgs a) {
+  constexpr bool kO2 = F & ar::kFlagO2, kDec = F & ar::kQFlagDec, kCode = !(F & ar::kQFlagNoCode);
+  const DevOp op = a.ops[blockIdx.y];
+  const int lane = threadIdx.x % kHalf, sub = threadIdx.x / kHalf;
+  const int64_t t = op.lo / kEncTileBlocks + blockIdx.x;
+#pragma unroll
+  for (int u = 0; u < kEU; ++u) {
+    const int64_t b = t * kEncTileBlocks + u * kBlocksPerPass + sub;
+    if (b < op.lo || b >= op.hi) continue;  // uniform over the half-wave
+    const int64_t e0 = b * kQB + lane * 4;
+    float va[4], vb[4], x[4];
+    hop_operand<F & ar::kQFlagARaw>(a, op.a, b, e0, lane, va);
+    hop_operand<F & ar::kQFlagBRaw>(a, op.b, b, e0, lane, vb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = e0 + i < a.count ? va[i] + vb[i] : 0.0f;
+    const Scale sc =
+        make_scale(max32(max(max(abs_bits(x[0]), abs_bits(x[1])), max(abs_bits(x[2]), abs_bits(x[3])))));
+    float k[4];
+    quantize<4>(x, sc, k);
+    if constexpr (kCode) {
+      const uint32_t w = pack4(k);
+      *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w;
+      if (lane == 0) a.scales[op.o * a.scale_stride + b] = sc.s;
+      if constexpr (kO2) {
+        *reinterpret_cast<uint32_t *>(a.codes + op.o2 * a.code_stride + e0) = w;
+        if (lane == 0) a.scales[op.o2 * a.scale_stride + b] = sc.s;
+      }
+    }
+    if constexpr (kDec) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = k[i] * sc.s;
+      store4<false>(a.grad[op.o], e0, a.count, v);
+      if constexpr (kO2) store4<false>(a.grad[op.o2], e0, a.count, v);
+    }
+  }
+}
+
+// A copy that delivers a rank's final codes: decoded into its buffer, and
+// stored as codes too unless nothing forwards them later.
+template <bool CODE>
+__global__ void __launch_bounds__(AR_BLOCK) q_copy_dec(QArgs a) {
+  const DevOp op = a.ops[blockIdx.y];
+  const int lane = threadIdx.x % kHalf, sub = threadIdx.x / kHalf;
+  const int64_t t = op.lo / kTileBlocks + blockIdx.x;
+  uint32_t w[kU];
+  float s[kU];
+  bool live[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+    live[u] = b >= op.lo && b < op.hi;
+    if (live[u]) {
+      w[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t *>(a.codes + op.a * a.code_stride + b * kQB + lane * 4));
+      s[u] = a.scales[op.a * a.scale_stride + b];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if (!live[u]) continue;
+    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+    const int64_t e0 = b * kQB + lane * 4;
+    if constexpr (CODE) {
+      *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w[u];
+      if (lane == 0) a.scales[op.o * a.scale_stride + b] = s[u];
+    }
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = code(w[u], k) * s[u];
+    store4<false>(a.grad[op.o], e0, a.count, x);
+  }
+}
+
+template <int F>
+void launch_hop(dim3 grid, const QArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(q_hop<F>, grid, dim3(AR_BLOCK), 0, s, a);
+}
+
+// The fused hop variants the planner emits: operand encodings x (O2) x
+// (decode, with or without stored codes).
+hipError_t launch_hop_kind(int32_t f, dim3 grid, const QArgs &a, hipStream_t s) {
+  constexpr int R = ar::kQFlagARaw, Rb = ar::kQFlagBRaw, O2 = ar::kFlagO2, D = ar::kQFlagDec,
+                N = ar::kQFlagNoCode;
+  switch (f) {
+#define AR_HOP_CASES(RAW)                                             \
+  case (RAW): launch_hop<(RAW)>(grid, a, s); break;                   \
+  case (RAW) | O2: launch_hop<(RAW) | O2>(grid, a, s); break;         \
+  case (RAW) | D: launch_hop<(RAW) | D>(grid, a, s); break;           \
+  case (RAW) | D | O2: launch_hop<(RAW) | D | O2>(grid, a, s); break; \
+  case (RAW) | D | N: launch_hop<(RAW) | D | N>(grid, a, s); break;   \
+  case (RAW) | D | N | O2: launch_hop<(RAW) | D | N | O2>(grid, a, s); break;
+    AR_HOP_CASES(0)
+    AR_HOP_CASES(R)
+    AR_HOP_CASES(Rb)
+    AR_HOP_CASES(R | Rb)
+#undef AR_HOP_CASES
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // codes[o] = codes[a]: 16 bytes of codes per thread, one scale per thread
 // of the first kCopyTileBlocks threads.
 __global__ void __launch_bounds__(AR_BLOCK) q_copy(QArgs a) {
@@ -587,8 +727,9 @@ hipError_t launch_q_onepass(int32_t fam, dim3 grid, const QArgs &a, hipStream_t 
 
 int64_t q_tile_blocks(int32_t kind) {
   switch (kind & 0xF00) {
-    case ar::kKQCopy: return kCopyTileBlocks;
-    case ar::kKQReduce: return kRTileBlocks;
+    case ar::kKQCopy: return (kind & ar::kQFlagDec) ? kTileBlocks : kCopyTileBlocks;
+    case ar::kKQReduce:
+      return (kind & (ar::kQFlagARaw | ar::kQFlagBRaw | ar::kQFlagDec)) ? kEncTileBlocks : kRTileBlocks;
     case ar::kKQEncode: return kEncTileBlocks;
     case ar::kKQDecode: return kTileBlocks;
     default: return kOPTileBlocks;
@@ -599,10 +740,18 @@ hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s) {
   switch (kind & 0xF00) {
     case ar::kKQEncode: hipLaunchKernelGGL(q_encode, grid, dim3(AR_BLOCK), 0, s, a); break;
     case ar::kKQReduce:
+      if (kind & (ar::kQFlagARaw | ar::kQFlagBRaw | ar::kQFlagDec)) return launch_hop_kind(kind & 0xFF, grid, a, s);
       if (kind & ar::kFlagO2) hipLaunchKernelGGL(q_reduce<true>, grid, dim3(AR_BLOCK), 0, s, a);
       else hipLaunchKernelGGL(q_reduce<false>, grid, dim3(AR_BLOCK), 0, s, a);
       break;
-    case ar::kKQCopy: hipLaunchKernelGGL(q_copy, grid, dim3(AR_BLOCK), 0, s, a); break;
+    case ar::kKQCopy:
+      if (kind & ar::kQFlagDec) {
+        if (kind & ar::kQFlagNoCode) hipLaunchKernelGGL(q_copy_dec<false>, grid, dim3(AR_BLOCK), 0, s, a);
+        else hipLaunchKernelGGL(q_copy_dec<true>, grid, dim3(AR_BLOCK), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(q_copy, grid, dim3(AR_BLOCK), 0, s, a);
+      }
+      break;
     case ar::kKQDecode: hipLaunchKernelGGL(q_decode, grid, dim3(AR_BLOCK), 0, s, a); break;
     default: return launch_q_onepass(kind & 0xF00, grid, a, s);
   }

@@ -137,14 +137,33 @@ def run_int8(plan, bufs, errs=None, group=1):
                     if errs is not None:
                         errs[a][e0:e1] = (x[:e1 - e0] - dec(a, blk)[:e1 - e0]).astype(np.float32)
                 elif fam == B.KIND_QREDUCE:
-                    x = (dec(a, blk) + dec(b, blk)).astype(np.float32)
+                    def operand(r, raw):
+                        if not raw:
+                            return dec(r, blk)
+                        # the rank's own g + e, encoded here; residual written back
+                        xr = np.zeros(Q, np.float32)
+                        xr[:e1 - e0] = bufs[r][e0:e1] + (errs[r][e0:e1] if errs is not None else np.float32(0))
+                        v = _roundtrip(xr)
+                        if errs is not None:
+                            errs[r][e0:e1] = (xr - v)[:e1 - e0]
+                        return v
+                    x = (operand(a, kind & 1) + operand(b, kind & 2)).astype(np.float32)
                     x[e1 - e0:] = 0
-                    put(o, blk, x)
-                    if kind & 8:
-                        put(o2, blk, x)
+                    outs = [o] + ([o2] if kind & 8 else [])
+                    q, sc = _q_block(x)
+                    for r in outs:
+                        if not kind & 32:  # codes stored unless nothing reads them later
+                            codes[r][blk * Q:(blk + 1) * Q] = q
+                            scales[r][blk] = sc
+                        if kind & 16:      # final codes decoded into the rank's buffer
+                            bufs[r][e0:e1] = (q.astype(np.float32) * sc)[:e1 - e0]
                 elif fam == B.KIND_QCOPY:
-                    codes[o][e0:e0 + Q] = codes[a][e0:e0 + Q]
-                    scales[o][blk] = scales[a][blk]
+                    q, sc = codes[a][e0:e0 + Q].copy(), scales[a][blk]
+                    if not kind & 32:
+                        codes[o][e0:e0 + Q] = q
+                        scales[o][blk] = sc
+                    if kind & 16:
+                        bufs[o][e0:e1] = (q.astype(np.float32) * sc)[:e1 - e0]
                 elif fam == B.KIND_QDECODE:
                     bufs[a][e0:e1] = dec(a, blk)[:e1 - e0]
                 elif fam in (B.KIND_RING, B.KIND_HIER, B.KIND_TREE, B.KIND_DTREE):

@@ -113,16 +113,25 @@ def test_launch_list_matches_oracle(sched, n, g, mode):
 
 
 def test_launch_shape():
-    """Encode first, decode last, one launch per round in between (the
-    completing reduce fused with the first forwarding copy), workspace of
-    one code byte per element and one scale per block, per rank."""
+    """Unfused steps: encode first, decode last, one launch per round in
+    between (the completing reduce fused with the first forwarding copy).
+    Fused steps (the default): round 0 encodes both operands in the kernel,
+    later reduce-scatter rounds encode the receiver's own contribution, the
+    completing round and the all-gather copies decode the final codes into
+    the buffers, and the last copy stores no codes.  Workspace: one code byte
+    per element and one scale per block, per rank."""
     n, count = 4, 10 * Q + 1
     p = B.ar_plan_create(n, 1, count, "int8_ef", "ring")
     try:
+        B.ar_plan_set_exec(p, "steps_unfused")
         kinds = [B.ar_plan_launch_info(p, i)[0] for i in range(B.ar_plan_num_launches(p))]
         assert kinds[0] == B.KIND_QENCODE and kinds[-1] == B.KIND_QDECODE
-        assert [k & 0xF00 for k in kinds[1:-1]] == [B.KIND_QREDUCE] * (n - 1) + [B.KIND_QCOPY] * (n - 2)
-        assert kinds[n - 1] & 8  # fused: the completing reduce also writes the next rank
+        assert [k & 0xF00 for k in kinds[1:-1]] == [B.KIND_QREDUCE] * (n - 1) + [B.KIND_QCOPY] * (n - 1)
+        B.ar_plan_set_exec(p, "steps")
+        kinds = [B.ar_plan_launch_info(p, i)[0] for i in range(B.ar_plan_num_launches(p))]
+        R = B.KIND_QREDUCE
+        assert kinds == [R | 3] + [R | 2] * (n - 3) + [R | 2 | 8 | 16] + \
+            [B.KIND_QCOPY | 16] * (n - 3) + [B.KIND_QCOPY | 16 | 32]
         st = B.ar_plan_stats(p)
         nblk = 11
         assert st["scratch_bytes"] == n * ((nblk * Q + 255) // 256 * 256 + 4 * ((nblk + 63) // 64 * 64))
