@@ -40,6 +40,12 @@
 #ifndef AR_Q_ENC_UNROLL
 #define AR_Q_ENC_UNROLL 1  // blocks per half-wave of the encode kernel
 #endif
+#ifndef AR_Q_HOP_UNROLL
+#define AR_Q_HOP_UNROLL 1  // blocks per half-wave of the fused hop kernel
+#endif
+#ifndef AR_Q_COPYDEC_UNROLL
+#define AR_Q_COPYDEC_UNROLL 2  // blocks per half-wave of the decoding copy
+#endif
 #ifndef AR_Q_OP_BLOCK
 #define AR_Q_OP_BLOCK 512  // threads per workgroup of the one-pass kernels
 #endif
@@ -58,6 +64,10 @@ constexpr int kU = AR_Q_UNROLL;
 constexpr int kTileBlocks = kBlocksPerPass * kU;
 constexpr int kEU = AR_Q_ENC_UNROLL;
 constexpr int kEncTileBlocks = kBlocksPerPass * kEU;
+constexpr int kHU = AR_Q_HOP_UNROLL;
+constexpr int kHopTileBlocks = kBlocksPerPass * kHU;
+constexpr int kCU = AR_Q_COPYDEC_UNROLL;
+constexpr int kCopyDecTileBlocks = kBlocksPerPass * kCU;
 constexpr int kRLanes = 8;                           // lanes per block (reduce): 16 codes each
 constexpr int kRBlocksPerPass = AR_BLOCK / kRLanes;  // 32
 constexpr int kRTileBlocks = kRBlocksPerPass * kU;
@@ -280,52 +290,77 @@ __global__ void __launch_bounds__(AR_BLOCK) q_reduce(QArgs a) {
 // re-encoded sum goes to o (and o2) as codes unless nothing reads them
 // later, and, for a rank's final codes, also decoded into its buffer.  Half a
 // wavefront per block, 4 elements per lane (the fp32 side sets the shape).
-template <int F>
-__device__ __forceinline__ void hop_operand(const QArgs &a, int r, int64_t b, int64_t e0, int lane, float v[4]) {
-  if constexpr (F != 0) {
-    float x[4];
-    load4(a.grad[r], e0, a.count, x);
+// The loads of all kHU blocks of a lane are issued before any arithmetic.
+struct HopIn {
+  float x[4];   // raw: g + e
+  uint32_t w;   // coded: 4 codes
+  float s;      // coded: the block's scale
+};
+
+template <bool RAW>
+__device__ __forceinline__ void hop_load(const QArgs &a, int r, int64_t b, int64_t e0, HopIn &in) {
+  if constexpr (RAW) {
+    load4(a.grad[r], e0, a.count, in.x);
     if (a.has_err) {
       float ev[4];
       load4(a.err[r], e0, a.count, ev);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = x[i] + ev[i];
+      for (int i = 0; i < 4; ++i) in.x[i] = in.x[i] + ev[i];
     }
-    const Scale sc =
-        make_scale(max32(max(max(abs_bits(x[0]), abs_bits(x[1])), max(abs_bits(x[2]), abs_bits(x[3])))));
+  } else {
+    in.w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(a.codes + r * a.code_stride + e0));
+    in.s = a.scales[r * a.scale_stride + b];
+  }
+}
+
+template <bool RAW>
+__device__ __forceinline__ void hop_value(const QArgs &a, int r, int64_t e0, const HopIn &in, float v[4]) {
+  if constexpr (RAW) {
+    const Scale sc = make_scale(
+        max32(max(max(abs_bits(in.x[0]), abs_bits(in.x[1])), max(abs_bits(in.x[2]), abs_bits(in.x[3])))));
     float k[4];
-    quantize<4>(x, sc, k);
+    quantize<4>(in.x, sc, k);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = k[i] * sc.s;
     if (a.has_err) {
       float res[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) res[i] = x[i] - v[i];
+      for (int i = 0; i < 4; ++i) res[i] = in.x[i] - v[i];
       store4<true>(a.err[r], e0, a.count, res);
     }
   } else {
-    (void)lane;
-    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(a.codes + r * a.code_stride + e0));
-    const float s = a.scales[r * a.scale_stride + b];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = code(w, i) * s;
+    for (int i = 0; i < 4; ++i) v[i] = code(in.w, i) * in.s;
   }
 }
 
 template <int F>
 __global__ void __launch_bounds__(AR_BLOCK) q_hop(QArgs a) {
   constexpr bool kO2 = F & ar::kFlagO2, kDec = F & ar::kQFlagDec, kCode = !(F & ar::kQFlagNoCode);
+  constexpr bool kRawA = F & ar::kQFlagARaw, kRawB = F & ar::kQFlagBRaw;
   const DevOp op = a.ops[blockIdx.y];
   const int lane = threadIdx.x % kHalf, sub = threadIdx.x / kHalf;
-  const int64_t t = op.lo / kEncTileBlocks + blockIdx.x;
+  const int64_t t = op.lo / kHopTileBlocks + blockIdx.x;
+  HopIn ia[kHU], ib[kHU];
+  bool live[kHU];
 #pragma unroll
-  for (int u = 0; u < kEU; ++u) {
-    const int64_t b = t * kEncTileBlocks + u * kBlocksPerPass + sub;
-    if (b < op.lo || b >= op.hi) continue;  // uniform over the half-wave
+  for (int u = 0; u < kHU; ++u) {
+    const int64_t b = t * kHopTileBlocks + u * kBlocksPerPass + sub;
+    live[u] = b >= op.lo && b < op.hi;
+    if (live[u]) {
+      const int64_t e0 = b * kQB + lane * 4;
+      hop_load<kRawA>(a, op.a, b, e0, ia[u]);
+      hop_load<kRawB>(a, op.b, b, e0, ib[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kHU; ++u) {
+    if (!live[u]) continue;  // uniform over the half-wave
+    const int64_t b = t * kHopTileBlocks + u * kBlocksPerPass + sub;
     const int64_t e0 = b * kQB + lane * 4;
     float va[4], vb[4], x[4];
-    hop_operand<F & ar::kQFlagARaw>(a, op.a, b, e0, lane, va);
-    hop_operand<F & ar::kQFlagBRaw>(a, op.b, b, e0, lane, vb);
+    hop_value<kRawA>(a, op.a, e0, ia[u], va);
+    hop_value<kRawB>(a, op.b, e0, ib[u], vb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = e0 + i < a.count ? va[i] + vb[i] : 0.0f;
     const Scale sc =
@@ -357,13 +392,13 @@ template <bool CODE>
 __global__ void __launch_bounds__(AR_BLOCK) q_copy_dec(QArgs a) {
   const DevOp op = a.ops[blockIdx.y];
   const int lane = threadIdx.x % kHalf, sub = threadIdx.x / kHalf;
-  const int64_t t = op.lo / kTileBlocks + blockIdx.x;
-  uint32_t w[kU];
-  float s[kU];
-  bool live[kU];
+  const int64_t t = op.lo / kCopyDecTileBlocks + blockIdx.x;
+  uint32_t w[kCU];
+  float s[kCU];
+  bool live[kCU];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+  for (int u = 0; u < kCU; ++u) {
+    const int64_t b = t * kCopyDecTileBlocks + u * kBlocksPerPass + sub;
     live[u] = b >= op.lo && b < op.hi;
     if (live[u]) {
       w[u] = __builtin_nontemporal_load(
@@ -372,9 +407,9 @@ __global__ void __launch_bounds__(AR_BLOCK) q_copy_dec(QArgs a) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < kCU; ++u) {
     if (!live[u]) continue;
-    const int64_t b = t * kTileBlocks + u * kBlocksPerPass + sub;
+    const int64_t b = t * kCopyDecTileBlocks + u * kBlocksPerPass + sub;
     const int64_t e0 = b * kQB + lane * 4;
     if constexpr (CODE) {
       *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w[u];
@@ -727,9 +762,9 @@ hipError_t launch_q_onepass(int32_t fam, dim3 grid, const QArgs &a, hipStream_t 
 
 int64_t q_tile_blocks(int32_t kind) {
   switch (kind & 0xF00) {
-    case ar::kKQCopy: return (kind & ar::kQFlagDec) ? kTileBlocks : kCopyTileBlocks;
+    case ar::kKQCopy: return (kind & ar::kQFlagDec) ? kCopyDecTileBlocks : kCopyTileBlocks;
     case ar::kKQReduce:
-      return (kind & (ar::kQFlagARaw | ar::kQFlagBRaw | ar::kQFlagDec)) ? kEncTileBlocks : kRTileBlocks;
+      return (kind & (ar::kQFlagARaw | ar::kQFlagBRaw | ar::kQFlagDec)) ? kHopTileBlocks : kRTileBlocks;
     case ar::kKQEncode: return kEncTileBlocks;
     case ar::kKQDecode: return kTileBlocks;
     default: return kOPTileBlocks;
