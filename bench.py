@@ -13,9 +13,12 @@ Prints ONE JSON line.  value = busbw = algbw * 2(N-1)/N with algbw = S / T
 (S = bytes per rank, GB = 1e9; the nccl-tests convention of the AI training
 network primer, ch. 4 section 4.8).  roofline: the kernel kind with the
 largest share of GPU time, its algorithmic bytes per launch over its mean
-launch duration (HIP events recorded by the library around every launch of
-the timed calls, on the call's stream), against 8 TB/s.  cpu_baseline: the
-CPU oracle (plain single-threaded C) timed on the host on the same inputs.
+launch duration (a start and a stop HIP event that every launch of the timed
+calls records as part of its dispatch, on the call's stream), against
+8 TB/s.  Those events cost a few microseconds per launch, so config.compare
+also times the same calls without them (eager, and replayed as HIP graphs).
+cpu_baseline: the CPU oracle (plain single-threaded C) timed on the host on
+the same inputs.
 """
 import argparse
 import hashlib
@@ -250,11 +253,7 @@ def main():
         run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
     else:
         run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
-    subplans = []
-    if bucketed:
-        # per-bucket plans are internal; profile by timing each call with events
-        pass
-    else:
+    if not bucketed:
         B.ar_plan_set_profiling(plan, max(args.steps, 1))
 
     for _ in range(args.warmup):
@@ -337,26 +336,28 @@ def main():
                             "algbw_GBps": round(op_alg, 1),
                             "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
 
-    # ---- the same exec mode replayed as one HIP graph per call
+    # ---- the same exec mode without the per-launch events (eager, then as one
+    # HIP graph per call): the events of the timed run cost a few us per launch
     if not args.no_extra:
-        if bucketed:
-            B.ar_bucket_set_graph(plan, True)
-        else:
-            B.ar_plan_set_profiling(plan, 0)
-            B.ar_plan_set_exec(plan, args.exec)
-            B.ar_plan_set_graph(plan, True)
-        reset_inputs()
-        for _ in range(args.warmup):
-            run()
-        torch.cuda.synchronize()
-        t_g = time.perf_counter()
-        for _ in range(args.steps):
-            run()
-        torch.cuda.synchronize()
-        g_ms = (time.perf_counter() - t_g) * 1e3 / max(args.steps, 1)
-        g_alg = S / (g_ms * 1e-3) / 1e9
-        extra["graph"] = {"exec": args.exec, "ms_per_step": round(g_ms, 4),
-                          "busbw_GBps": round(g_alg * 2 * (n - 1) / n, 1), "algbw_GBps": round(g_alg, 1)}
+        for name, graph in (("without_launch_events", False), ("graph", True)):
+            if bucketed:
+                B.ar_bucket_set_graph(plan, graph)
+            else:
+                B.ar_plan_set_profiling(plan, 0)
+                B.ar_plan_set_exec(plan, args.exec)
+                B.ar_plan_set_graph(plan, graph)
+            reset_inputs()
+            for _ in range(args.warmup):
+                run()
+            torch.cuda.synchronize()
+            t_g = time.perf_counter()
+            for _ in range(args.steps):
+                run()
+            torch.cuda.synchronize()
+            g_ms = (time.perf_counter() - t_g) * 1e3 / max(args.steps, 1)
+            g_alg = S / (g_ms * 1e-3) / 1e9
+            extra[name] = {"exec": args.exec, "ms_per_step": round(g_ms, 4),
+                           "busbw_GBps": round(g_alg * 2 * (n - 1) / n, 1), "algbw_GBps": round(g_alg, 1)}
 
     # ---- CPU oracle on the same inputs (single-threaded C)
     cpu = None
@@ -409,6 +410,7 @@ def main():
         "config": {
             "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,
             "count_per_rank": count_logical, "bytes_per_rank": S, "exec": args.exec,
+            "executor": "eager launches with a HIP event after each (for the roofline)",
             "algbw_GBps": round(algbw, 1), "busbw_GBps": round(busbw, 1),
             "hbm_model_bytes": stats["hbm_bytes_model"], "hbm_model_GBps": round(model_gbps, 1),
             "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),

@@ -59,7 +59,7 @@ struct ar_plan {
   hipStream_t capture_stream = nullptr;
   int32_t prof_calls = 0;           // capacity of the event log in calls
   int64_t prof_logged = 0;          // calls recorded since the log was last read
-  std::vector<hipEvent_t> events;   // prof_calls * (launches + 1)
+  std::vector<hipEvent_t> events;   // prof_calls * launches * 2 (start, stop)
 
   // fp32 partial-sum slots, or the INT8 code slots
   size_t need_scratch_bytes() const { return static_cast<size_t>(ar::workspace_bytes(p)); }
@@ -168,7 +168,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     return fail(AR_ERR_INVALID_ARG, "external scratch too small");
   }
   if (pl->prof_calls > 0) {
-    pl->events.resize(static_cast<size_t>(pl->prof_calls) * (pl->p.launches.size() + 1));
+    pl->events.resize(static_cast<size_t>(pl->prof_calls) * pl->p.launches.size() * 2);
     for (hipEvent_t &ev : pl->events) {
       e = hipEventCreate(&ev);
       if (e != hipSuccess) {
@@ -249,22 +249,26 @@ ar_stats_t stats_of(const ar::Plan &p) {
 
 namespace {
 
-// Launches every kernel of the plan on s (recording the profiling events
-// around them when prof is set).
+// Launches every kernel of the plan on s (each timed by its own start and
+// stop events when prof is set).
 ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
                     bool prof) {
   hipEvent_t *ev = nullptr;
-  if (prof) {
-    ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * (plan->p.launches.size() + 1);
-    hipError_t e = hipEventRecord(ev[0], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
+  if (prof) ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * plan->p.launches.size() * 2;
   for (size_t i = 0; i < plan->p.launches.size(); ++i) {
     const ar::Launch &L = plan->p.launches[i];
     const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
     hipError_t e = hipSuccess;
     if (grid.x == 0) {
-    } else if (quant) {
+      if (prof) {  // nothing to launch: an empty interval
+        e = hipEventRecord(ev[2 * i], s);
+        if (e == hipSuccess) e = hipEventRecord(ev[2 * i + 1], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      }
+      continue;
+    }
+    ar_dev::t_launch_events = prof ? ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]} : ar_dev::LaunchEvents{};
+    if (quant) {
       qargs.ops = plan->d_ops + plan->op_offset[i];
       qargs.nops = static_cast<int32_t>(L.ops.size());
       e = ar_dev::launch_q(L.kind, grid, qargs, s);
@@ -274,13 +278,9 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
       const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
       e = ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
     }
+    ar_dev::t_launch_events = ar_dev::LaunchEvents{};
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
-    if (prof) {
-      e = hipEventRecord(ev[i + 1], s);
-      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
   }
-  if (prof) ++plan->prof_logged;
   return AR_OK;
 }
 
@@ -432,9 +432,13 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
     args.group_size = plan->p.group_size;
   }
   const bool prof = plan->prof_calls > 0 && !plan->events.empty();
-  if (plan->use_graph && !prof && !plan->p.launches.empty())
-    return replay(plan, quant, args, qargs, rank_bufs, error_bufs, s);
-  return enqueue(plan, quant, args, qargs, s, prof);
+  // per-launch events need eager launches (event records captured into a
+  // graph cannot be timed), so profiling keeps calls eager
+  st = plan->use_graph && !prof && !plan->p.launches.empty()
+           ? replay(plan, quant, args, qargs, rank_bufs, error_bufs, s)
+           : enqueue(plan, quant, args, qargs, s, prof);
+  if (st == AR_OK && prof) ++plan->prof_logged;
+  return st;
 }
 
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
@@ -583,9 +587,9 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
   if (!ms || cap < *n) return AR_OK;  // size query
   const int64_t first = plan->prof_logged - calls;
   for (int64_t c = 0; c < calls; ++c) {
-    const hipEvent_t *ev = plan->events.data() + ((first + c) % plan->prof_calls) * (L + 1);
+    const hipEvent_t *ev = plan->events.data() + ((first + c) % plan->prof_calls) * L * 2;
     for (int64_t i = 0; i < L; ++i) {
-      hipError_t e = hipEventElapsedTime(&ms[c * L + i], ev[i], ev[i + 1]);
+      hipError_t e = hipEventElapsedTime(&ms[c * L + i], ev[2 * i], ev[2 * i + 1]);
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     }
   }

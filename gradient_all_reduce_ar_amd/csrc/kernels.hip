@@ -26,6 +26,8 @@
 
 namespace ar_dev {
 
+thread_local LaunchEvents t_launch_events;
+
 namespace {
 
 constexpr int kBlock = AR_BLOCK;
@@ -594,9 +596,9 @@ constexpr bool kNtsScratch = AR_NTS_SCRATCH;
 template <int FLAGS, int U>
 hipError_t launch_reduce_u(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
   if ((out_scratch && kNtsScratch) || (!out_scratch && kNtsRank))
-    hipLaunchKernelGGL((chunk_reduce<FLAGS, U, true>), grid, dim3(kBlock), 0, s, a);
+    AR_LAUNCH((chunk_reduce<FLAGS, U, true>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_reduce<FLAGS, U, false>), grid, dim3(kBlock), 0, s, a);
+    AR_LAUNCH((chunk_reduce<FLAGS, U, false>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -608,20 +610,20 @@ hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s, bool out_scra
 
 template <int ES>
 hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
-  if (cold) hipLaunchKernelGGL((chunk_copy<ES, kUnrollCold, kNtsRank>), grid, dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL((chunk_copy<ES, kUnrollWarm, kNtsRank>), grid, dim3(kBlock), 0, s, a);
+  if (cold) AR_LAUNCH((chunk_copy<ES, kUnrollCold, kNtsRank>), grid, dim3(kBlock), 0, s, a);
+  else AR_LAUNCH((chunk_copy<ES, kUnrollWarm, kNtsRank>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template <bool BF, bool EACH>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
-  if (n <= 2) hipLaunchKernelGGL((onepass_tree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 4) hipLaunchKernelGGL((onepass_tree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 8) hipLaunchKernelGGL((onepass_tree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 16) hipLaunchKernelGGL((onepass_tree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 32) hipLaunchKernelGGL((onepass_tree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 64) hipLaunchKernelGGL((onepass_tree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a);
+  if (n <= 2) AR_LAUNCH((onepass_tree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 4) AR_LAUNCH((onepass_tree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 8) AR_LAUNCH((onepass_tree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 16) AR_LAUNCH((onepass_tree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 32) AR_LAUNCH((onepass_tree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a);
+  else if (n <= 64) AR_LAUNCH((onepass_tree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -630,12 +632,12 @@ template <bool BF, bool EACH>
 hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
   switch (n) {
-    case 2: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((onepass_dtree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 2: AR_LAUNCH((onepass_dtree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 4: AR_LAUNCH((onepass_dtree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 8: AR_LAUNCH((onepass_dtree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 16: AR_LAUNCH((onepass_dtree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 32: AR_LAUNCH((onepass_dtree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a); break;
+    case 64: AR_LAUNCH((onepass_dtree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -690,19 +692,19 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
       return hipErrorInvalidValue;
     case kKindRing:
       if ((kind & 3) == 2)
-        hipLaunchKernelGGL((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else if ((kind & 3) == 1)
-        hipLaunchKernelGGL((onepass_ring<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_ring<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_ring<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_ring<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
       return hipGetLastError();
     case kKindHier:
       if ((kind & 3) == 2)
-        hipLaunchKernelGGL((onepass_hier<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_hier<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else if ((kind & 3) == 1)
-        hipLaunchKernelGGL((onepass_hier<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_hier<true, false, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);
       else
-        hipLaunchKernelGGL((onepass_hier<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
+        AR_LAUNCH((onepass_hier<false, false, kOnePassUnrollF32, kFoldBatchF32>), grid, dim3(kOPB), 0, s, a);
       return hipGetLastError();
     case kKindTree:
       if ((kind & 3) == 2) return launch_tree<true, true>(a.nranks, grid, a, s);

@@ -1,6 +1,7 @@
 // kernels.hpp -- interface between the executor and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -53,7 +54,21 @@
 #define AR_ONEPASS_UNROLL_BF16 1
 #endif
 
+// Kernel launch on stream S that records ar_dev::t_launch_events.
+#define AR_LAUNCH(K, G, B, SH, S, ...)                                                                       \
+  hipExtLaunchKernelGGL(K, G, B, SH, S, ::ar_dev::t_launch_events.start, ::ar_dev::t_launch_events.stop, 0, \
+                        __VA_ARGS__)
+
 namespace ar_dev {
+
+// Events the next kernel launch of this thread records its start and end on
+// (both NULL: no timing).  The executor sets them around each launch when the
+// profiling log is on; the timestamps come from the dispatch itself, so no
+// extra packet sits between two kernels.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents t_launch_events;
 
 constexpr int kMaxRanks = 64;
 constexpr int32_t kLocScratchDev = ar::kLocScratch;

@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(AR_BLOCK) q_copy_dec(QArgs a) {
 
 template <int F>
 void launch_hop(dim3 grid, const QArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(q_hop<F>, grid, dim3(AR_BLOCK), 0, s, a);
+  AR_LAUNCH(q_hop<F>, grid, dim3(AR_BLOCK), 0, s, a);
 }
 
 // The fused hop variants the planner emits: operand encodings x (O2) x
@@ -725,14 +725,14 @@ __global__ void __launch_bounds__(kOPBlock) q_onepass_dtree(QArgs a) {
 
 template <int NMAX>
 void launch_q_tree(dim3 grid, const QArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(q_onepass_tree<NMAX>, grid, dim3(kOPBlock), 0, s, a);
+  AR_LAUNCH(q_onepass_tree<NMAX>, grid, dim3(kOPBlock), 0, s, a);
 }
 
 hipError_t launch_q_onepass(int32_t fam, dim3 grid, const QArgs &a, hipStream_t s) {
   const int n = a.nranks;
   switch (fam) {
-    case ar::kKRing: hipLaunchKernelGGL(q_onepass_ring<AR_Q_FOLD_BATCH>, grid, dim3(kOPBlock), 0, s, a); break;
-    case ar::kKHier: hipLaunchKernelGGL(q_onepass_hier, grid, dim3(kOPBlock), 0, s, a); break;
+    case ar::kKRing: AR_LAUNCH(q_onepass_ring<AR_Q_FOLD_BATCH>, grid, dim3(kOPBlock), 0, s, a); break;
+    case ar::kKHier: AR_LAUNCH(q_onepass_hier, grid, dim3(kOPBlock), 0, s, a); break;
     case ar::kKTree:
       if (n <= 2) launch_q_tree<2>(grid, a, s);
       else if (n <= 4) launch_q_tree<4>(grid, a, s);
@@ -744,12 +744,12 @@ hipError_t launch_q_onepass(int32_t fam, dim3 grid, const QArgs &a, hipStream_t 
       break;
     case ar::kKDTree:
       switch (n) {
-        case 2: hipLaunchKernelGGL(q_onepass_dtree<2>, grid, dim3(kOPBlock), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(q_onepass_dtree<4>, grid, dim3(kOPBlock), 0, s, a); break;
-        case 8: hipLaunchKernelGGL(q_onepass_dtree<8>, grid, dim3(kOPBlock), 0, s, a); break;
-        case 16: hipLaunchKernelGGL(q_onepass_dtree<16>, grid, dim3(kOPBlock), 0, s, a); break;
-        case 32: hipLaunchKernelGGL(q_onepass_dtree<32>, grid, dim3(kOPBlock), 0, s, a); break;
-        case 64: hipLaunchKernelGGL(q_onepass_dtree<64>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 2: AR_LAUNCH(q_onepass_dtree<2>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 4: AR_LAUNCH(q_onepass_dtree<4>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 8: AR_LAUNCH(q_onepass_dtree<8>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 16: AR_LAUNCH(q_onepass_dtree<16>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 32: AR_LAUNCH(q_onepass_dtree<32>, grid, dim3(kOPBlock), 0, s, a); break;
+        case 64: AR_LAUNCH(q_onepass_dtree<64>, grid, dim3(kOPBlock), 0, s, a); break;
         default: return hipErrorInvalidValue;
       }
       break;
@@ -773,21 +773,21 @@ int64_t q_tile_blocks(int32_t kind) {
 
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s) {
   switch (kind & 0xF00) {
-    case ar::kKQEncode: hipLaunchKernelGGL(q_encode, grid, dim3(AR_BLOCK), 0, s, a); break;
+    case ar::kKQEncode: AR_LAUNCH(q_encode, grid, dim3(AR_BLOCK), 0, s, a); break;
     case ar::kKQReduce:
       if (kind & (ar::kQFlagARaw | ar::kQFlagBRaw | ar::kQFlagDec)) return launch_hop_kind(kind & 0xFF, grid, a, s);
-      if (kind & ar::kFlagO2) hipLaunchKernelGGL(q_reduce<true>, grid, dim3(AR_BLOCK), 0, s, a);
-      else hipLaunchKernelGGL(q_reduce<false>, grid, dim3(AR_BLOCK), 0, s, a);
+      if (kind & ar::kFlagO2) AR_LAUNCH(q_reduce<true>, grid, dim3(AR_BLOCK), 0, s, a);
+      else AR_LAUNCH(q_reduce<false>, grid, dim3(AR_BLOCK), 0, s, a);
       break;
     case ar::kKQCopy:
       if (kind & ar::kQFlagDec) {
-        if (kind & ar::kQFlagNoCode) hipLaunchKernelGGL(q_copy_dec<false>, grid, dim3(AR_BLOCK), 0, s, a);
-        else hipLaunchKernelGGL(q_copy_dec<true>, grid, dim3(AR_BLOCK), 0, s, a);
+        if (kind & ar::kQFlagNoCode) AR_LAUNCH(q_copy_dec<false>, grid, dim3(AR_BLOCK), 0, s, a);
+        else AR_LAUNCH(q_copy_dec<true>, grid, dim3(AR_BLOCK), 0, s, a);
       } else {
-        hipLaunchKernelGGL(q_copy, grid, dim3(AR_BLOCK), 0, s, a);
+        AR_LAUNCH(q_copy, grid, dim3(AR_BLOCK), 0, s, a);
       }
       break;
-    case ar::kKQDecode: hipLaunchKernelGGL(q_decode, grid, dim3(AR_BLOCK), 0, s, a); break;
+    case ar::kKQDecode: AR_LAUNCH(q_decode, grid, dim3(AR_BLOCK), 0, s, a); break;
     default: return launch_q_onepass(kind & 0xF00, grid, a, s);
   }
   return hipGetLastError();

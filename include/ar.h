@@ -304,15 +304,17 @@ ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable);
 
 /* ---- Timing ---- */
 
-/* Per-launch timing.  With max_calls > 0, each ar_allreduce records a HIP
- * event on its stream before its first launch and after every launch, into a
- * log holding the events of the last max_calls calls (older calls are
- * overwritten); max_calls = 0 turns it off.  Events are allocated here, not
+/* Per-launch timing.  With max_calls > 0, each ar_allreduce launches every
+ * kernel with a start and a stop HIP event that the dispatch itself records
+ * (hipExtLaunchKernel; no extra packet between kernels), into a log holding
+ * the events of the last max_calls calls (older calls are overwritten);
+ * max_calls = 0 turns it off.  Events are allocated at the next prepare, not
  * on the hot path. */
 ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls);
 
 /* Durations in ms of every launch of the logged calls, oldest call first:
- * ms[c * launches + i] is launch i of logged call c.  The caller must have
+ * ms[c * launches + i] is launch i of logged call c, from the kernel's start
+ * to its end.  The caller must have
  * synchronised the stream.  *n receives calls * launches; the log is then
  * cleared. */
 ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n);
