@@ -263,11 +263,22 @@ def main():
         B.ar_plan_launch_times(plan)  # clear the warm-up entries
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if bucketed:
+        # one event after each bucket of each timed call (per-bucket times)
+        nb = B.ar_bucket_count(plan)
+        bucket_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)] for _ in range(args.steps)]
+        for call in bucket_ev:
+            for e in call:
+                e.record(stream)  # creates the underlying events outside the timed region
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        run()
+    for c in range(args.steps):
+        if bucketed:
+            bucket_ev[c][0].record(stream)
+            B.ar_bucket_allreduce_after(plan, bufs, stream, None, bucket_ev[c][1:])
+        else:
+            run()
     ev1.record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
@@ -279,6 +290,16 @@ def main():
     algbw = S / (ms * 1e-3) / 1e9
     busbw = algbw * 2 * (n - 1) / n
     stats = B.ar_bucket_stats(plan) if bucketed else B.ar_plan_stats(plan)
+    per_bucket = None
+    if bucketed:
+        per_bucket = []
+        for b in range(nb):
+            t_b = sorted(call[b].elapsed_time(call[b + 1]) for call in bucket_ev)
+            _, cnt = B.ar_bucket_range(plan, b)
+            med = t_b[len(t_b) // 2]
+            alg_b = cnt * elem / (med * 1e-3) / 1e9
+            per_bucket.append({"bucket": b, "bytes_per_rank": cnt * elem, "median_ms": round(med, 4),
+                               "algbw_GBps": round(alg_b, 1), "busbw_GBps": round(alg_b * 2 * (n - 1) / n, 1)})
     model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
 
     roofline = None
@@ -432,6 +453,7 @@ def main():
         out["config"]["wire_compression_vs_fp32"] = round(sent_f32 / stats["bytes_sent_total"], 4)
     if bucketed:
         out["config"]["buckets"] = B.ar_bucket_count(plan)
+        out["config"]["per_bucket"] = per_bucket
         B.ar_bucket_plan_destroy(plan)
     else:
         B.ar_plan_destroy(plan)
