@@ -13,10 +13,12 @@ Prints ONE JSON line.  value = busbw = algbw * 2(N-1)/N with algbw = S / T
 (S = bytes per rank, GB = 1e9; the nccl-tests convention of the AI training
 network primer, ch. 4 section 4.8).  roofline: the kernel kind with the
 largest share of GPU time, its algorithmic bytes per launch over its mean
-launch duration (a start and a stop HIP event that every launch of the timed
-calls records as part of its dispatch, on the call's stream), against
-8 TB/s.  Those events cost a few microseconds per launch, so config.compare
-also times the same calls without them (eager, and replayed as HIP graphs).
+launch duration (a start and a stop HIP event that the timed launches record
+as part of their dispatch, on the call's stream), against 8 TB/s.  Each call
+times about four of its launches, in rotation, so every launch position is
+timed over the run while the events barely perturb the calls;
+config.compare also times the same calls with no events at all (eager, and
+replayed as HIP graphs).
 cpu_baseline: the CPU oracle (plain single-threaded C) timed on the host on
 the same inputs.
 """
@@ -253,8 +255,13 @@ def main():
         run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
     else:
         run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
+    period = None
     if not bucketed:
+        # time about four launches per call (every launch over `period` calls),
+        # so the timing events barely perturb the calls they time
+        period = max(1, B.ar_plan_num_launches(plan) // 4)
         B.ar_plan_set_profiling(plan, max(args.steps, 1))
+        B.ar_plan_set_profiling_period(plan, period)
 
     for _ in range(args.warmup):
         run()
@@ -305,18 +312,23 @@ def main():
     roofline = None
     per_kind = {}
     if not bucketed:
-        times = B.ar_plan_launch_times(plan)
+        times = B.ar_plan_launch_times(plan)  # -1: launch not timed in that call (sampling)
         nl = B.ar_plan_num_launches(plan)
         lb = [launch_bytes(B, plan, i, n, elem, count) for i in range(nl)]
+        per_call_count = {}
+        for nbytes, kind in lb:
+            per_call_count[kind] = per_call_count.get(kind, 0) + 1
         for call in times:
             for i, t in enumerate(call):
+                if t < 0:
+                    continue
                 nbytes, kind = lb[i]
-                k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "kinds": set()})
+                k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0})
                 k["ms"] += t
                 k["launches"] += 1
                 k["bytes"] += nbytes
-                k["kinds"].add(hex(kind))
-        dom = max(per_kind, key=lambda f: per_kind[f]["ms"])
+        # the kernel with the largest share of a call's GPU time
+        dom = max(per_kind, key=lambda f: per_kind[f]["ms"] / per_kind[f]["launches"] * per_call_count[f])
         d = per_kind[dom]
         avg_ms = d["ms"] / d["launches"]
         bytes_per_launch = d["bytes"] / d["launches"]
@@ -326,16 +338,18 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "kernel": kernel_label(dom),
                     "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                    "launches_timed": d["launches"]}
-        log("per kernel:", {kernel_label(f): {"ms_total": round(v["ms"], 3), "launches": v["launches"],
+                    "launches_timed": d["launches"], "profiling_period": period}
+        log("per kernel:", {kernel_label(f): {"ms_timed": round(v["ms"], 3), "launches_timed": v["launches"],
                                                   "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
                                   for f, v in per_kind.items()})
-        sum_launch_ms = sum(sum(c) for c in times) / max(len(times), 1)
-        per_call = sorted(sum(c) for c in times)  # launch intervals of each timed call
-        per_call_ms = {"median": round(per_call[len(per_call) // 2], 4), "min": round(per_call[0], 4)}
+        # kernel time per call: each launch's mean over the calls that timed it
+        means = []
+        for i in range(nl):
+            ts = [call[i] for call in times if call[i] >= 0]
+            means.append(sum(ts) / len(ts) if ts else None)
+        sum_launch_ms = sum(means) if all(m is not None for m in means) else None
     else:
         sum_launch_ms = None
-        per_call_ms = None
 
     # ---- one-pass comparison on the same buffers (bit-identical results)
     extra = {}
@@ -445,8 +459,7 @@ def main():
             "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),
             "launches_per_step": stats["launches"], "schedule_steps": stats["steps"],
             "event_ms_per_step": round(ev_ms, 4),
-            "sum_of_launch_ms_per_step": None if sum_launch_ms is None else round(sum_launch_ms, 4),
-            "per_call_ms": per_call_ms,
+            "kernel_ms_per_step": None if sum_launch_ms is None else round(sum_launch_ms, 4),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -100,6 +100,7 @@ def _declare(L):
         "ar_plan_launch_info": ([P, i32, pi32, pi32], ctypes.c_int),
         "ar_plan_launch_ops": ([P, i32, pi64, pi64, pi32, pi32, pi32, pi32, pi32], ctypes.c_int),
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_set_profiling_period": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_cache_bytes": ([P, sz], ctypes.c_int),
         "ar_bucket_set_graph": ([P, ctypes.c_int], ctypes.c_int),
@@ -289,8 +290,12 @@ def ar_plan_set_profiling(plan, max_calls):
     _check(lib().ar_plan_set_profiling(plan, int(max_calls)))
 
 
+def ar_plan_set_profiling_period(plan, period):
+    _check(lib().ar_plan_set_profiling_period(plan, int(period)))
+
+
 def ar_plan_launch_times(plan):
-    """Per-launch ms of the logged calls, as a list of per-call lists."""
+    """Per-launch ms of the logged calls, as a list of per-call lists (-1: not timed)."""
     n = ctypes.c_int32()
     _check(lib().ar_plan_launch_times(plan, None, 0, ctypes.byref(n)))
     buf = (ctypes.c_float * max(n.value, 1))()

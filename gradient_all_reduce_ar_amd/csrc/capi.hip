@@ -60,6 +60,8 @@ struct ar_plan {
   int32_t prof_calls = 0;           // capacity of the event log in calls
   int64_t prof_logged = 0;          // calls recorded since the log was last read
   std::vector<hipEvent_t> events;   // prof_calls * launches * 2 (start, stop)
+  int32_t prof_period = 1;          // call c times launch i iff (i + c) % period == 0
+  std::vector<uint8_t> sampled;     // prof_calls * launches: the launch was timed
 
   // fp32 partial-sum slots, or the INT8 code slots
   size_t need_scratch_bytes() const { return static_cast<size_t>(ar::workspace_bytes(p)); }
@@ -168,6 +170,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     return fail(AR_ERR_INVALID_ARG, "external scratch too small");
   }
   if (pl->prof_calls > 0) {
+    pl->sampled.assign(static_cast<size_t>(pl->prof_calls) * pl->p.launches.size(), 0);
     pl->events.resize(static_cast<size_t>(pl->prof_calls) * pl->p.launches.size() * 2);
     for (hipEvent_t &ev : pl->events) {
       e = hipEventCreate(&ev);
@@ -254,20 +257,28 @@ namespace {
 ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
                     bool prof) {
   hipEvent_t *ev = nullptr;
-  if (prof) ev = plan->events.data() + (plan->prof_logged % plan->prof_calls) * plan->p.launches.size() * 2;
+  uint8_t *mark = nullptr;
+  const int64_t call = plan->prof_logged;
+  if (prof) {
+    const size_t slot = static_cast<size_t>(call % plan->prof_calls);
+    ev = plan->events.data() + slot * plan->p.launches.size() * 2;
+    mark = plan->sampled.data() + slot * plan->p.launches.size();
+  }
   for (size_t i = 0; i < plan->p.launches.size(); ++i) {
     const ar::Launch &L = plan->p.launches[i];
     const dim3 grid = ar_dev::grid_for(plan->grid_x[i], static_cast<uint32_t>(L.ops.size()));
     hipError_t e = hipSuccess;
+    const bool timed = prof && (static_cast<int64_t>(i) + call) % plan->prof_period == 0;
+    if (prof) mark[i] = timed;
     if (grid.x == 0) {
-      if (prof) {  // nothing to launch: an empty interval
+      if (timed) {  // nothing to launch: an empty interval
         e = hipEventRecord(ev[2 * i], s);
         if (e == hipSuccess) e = hipEventRecord(ev[2 * i + 1], s);
         if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
       }
       continue;
     }
-    ar_dev::t_launch_events = prof ? ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]} : ar_dev::LaunchEvents{};
+    ar_dev::t_launch_events = timed ? ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]} : ar_dev::LaunchEvents{};
     if (quant) {
       qargs.ops = plan->d_ops + plan->op_offset[i];
       qargs.nops = static_cast<int32_t>(L.ops.size());
@@ -578,6 +589,12 @@ ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls) {
   return AR_OK;
 }
 
+ar_status_t ar_plan_set_profiling_period(ar_plan_t *plan, int period) {
+  if (!plan || period < 1) return fail(AR_ERR_INVALID_ARG, "bad profiling period");
+  plan->prof_period = period;
+  return AR_OK;
+}
+
 ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n) {
   if (!plan || !n) return fail(AR_ERR_INVALID_ARG, "bad arguments");
   if (plan->prof_calls <= 0) return fail(AR_ERR_INVALID_ARG, "profiling is off");
@@ -587,8 +604,14 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
   if (!ms || cap < *n) return AR_OK;  // size query
   const int64_t first = plan->prof_logged - calls;
   for (int64_t c = 0; c < calls; ++c) {
-    const hipEvent_t *ev = plan->events.data() + ((first + c) % plan->prof_calls) * L * 2;
+    const size_t slot = static_cast<size_t>((first + c) % plan->prof_calls);
+    const hipEvent_t *ev = plan->events.data() + slot * L * 2;
+    const uint8_t *mark = plan->sampled.data() + slot * L;
     for (int64_t i = 0; i < L; ++i) {
+      if (!mark[i]) {
+        ms[c * L + i] = -1.0f;  // not timed in this call
+        continue;
+      }
       hipError_t e = hipEventElapsedTime(&ms[c * L + i], ev[2 * i], ev[2 * i + 1]);
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     }

@@ -312,9 +312,14 @@ ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable);
  * on the hot path. */
 ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls);
 
+/* Samples the log: with period P > 1, logged call c times only the launches
+ * i with (i + c) mod P == 0 (fewer events per call; over P consecutive calls
+ * every launch is timed once).  Default 1: every launch.  Host only. */
+ar_status_t ar_plan_set_profiling_period(ar_plan_t *plan, int period);
+
 /* Durations in ms of every launch of the logged calls, oldest call first:
  * ms[c * launches + i] is launch i of logged call c, from the kernel's start
- * to its end.  The caller must have
+ * to its end, or -1 if the profiling period left it untimed.  The caller must have
  * synchronised the stream.  *n receives calls * launches; the log is then
  * cleared. */
 ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n);

@@ -127,6 +127,20 @@ def test_plan_reuse_streams_and_profiling():
         times = B.ar_plan_launch_times(plan)
         assert len(times) == 3 and all(len(t) == B.ar_plan_num_launches(plan) for t in times)
         assert all(ms > 0 for t in times for ms in t)
+        # sampled log: period 3 over 3 calls times every launch exactly once
+        B.ar_plan_set_profiling_period(plan, 3)
+        xs = workloads.normal_inputs(n, count, seed=9, dtype="bf16")
+        bufs = to_device(xs, "bf16")
+        for _ in range(3):
+            B.ar_allreduce(plan, bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        times = B.ar_plan_launch_times(plan)
+        nl = B.ar_plan_num_launches(plan)
+        assert len(times) == 3
+        for i in range(nl):
+            timed = [t[i] for t in times if t[i] >= 0]
+            assert len(timed) == 1 and timed[0] > 0
+            assert all(t[i] == -1 for t in times if t[i] < 0)
     finally:
         B.ar_plan_destroy(plan)
 

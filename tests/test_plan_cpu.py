@@ -362,3 +362,14 @@ def test_piece_counts():
     finally:
         B.ar_plan_destroy(p3)
         B.ar_plan_destroy(p2)
+
+
+def test_profiling_period_is_checked_on_the_host():
+    p = B.ar_plan_create(4, 1, 1024, "fp32", "ring")
+    try:
+        B.ar_plan_set_profiling_period(p, 5)
+        with pytest.raises(B.ArError) as ei:
+            B.ar_plan_set_profiling_period(p, 0)
+        assert ei.value.status == B.AR_ERR_INVALID_ARG
+    finally:
+        B.ar_plan_destroy(p)
