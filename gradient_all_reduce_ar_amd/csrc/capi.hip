@@ -144,7 +144,11 @@ ar_status_t prepare(ar_plan_t *pl) {
       host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
       gx = std::max(gx, (o.hi + tile - 1) / tile - o.lo / tile);
     }
-    if (gx * static_cast<int64_t>(L.ops.size()) > 0x7fffffff) return fail(AR_ERR_UNSUPPORTED, "op too large for one grid");
+    // a dispatch holds at most 2^32 - 1 work-items per grid dimension (here
+    // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
+    const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
+    if (gx * threads > 0x7fffffff || L.ops.size() > 65535)
+      return fail(AR_ERR_UNSUPPORTED, "op too large for one launch grid");
     pl->grid_x.push_back(static_cast<uint32_t>(gx));
   }
   if (!host_ops.empty()) {

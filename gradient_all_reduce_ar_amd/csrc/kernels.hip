@@ -655,6 +655,11 @@ dim3 grid_for(uint32_t tiles, uint32_t nops) {
 #endif
 }
 
+int block_threads(int32_t kind) {
+  const int32_t fam = kind & 0xF00;
+  return (fam == kKindReduce || fam == kKindCopy) ? kBlock : kOPB;
+}
+
 int64_t tile_elems(int32_t kind, bool cold) {
   const int64_t u = cold ? kUnrollCold : kUnrollWarm;
   switch (kind & 0xF00) {

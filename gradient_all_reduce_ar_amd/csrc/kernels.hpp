@@ -114,12 +114,18 @@ struct QArgs {
 // Blocks per tile of the INT8 kernels.
 int64_t q_tile_blocks(int32_t kind);
 
+// Threads per workgroup of an INT8 kernel kind.
+int q_block_threads(int32_t kind);
+
 // Launches one INT8 kernel (encode, reduce, copy, decode, or a one-pass fold
 // kind kKRing / kKHier / kKTree / kKDTree) on stream s.
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s);
 
 // Tile (elements per block) of a kernel kind in the warm or cold shape.
 int64_t tile_elems(int32_t kind, bool cold);
+
+// Threads per workgroup of a kernel kind.
+int block_threads(int32_t kind);
 
 // Grid of a launch whose ops span at most `tiles` tiles each.
 dim3 grid_for(uint32_t tiles, uint32_t nops);

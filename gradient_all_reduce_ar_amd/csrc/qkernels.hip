@@ -771,6 +771,16 @@ int64_t q_tile_blocks(int32_t kind) {
   }
 }
 
+int q_block_threads(int32_t kind) {
+  switch (kind & 0xF00) {
+    case ar::kKQCopy:
+    case ar::kKQReduce:
+    case ar::kKQEncode:
+    case ar::kKQDecode: return AR_BLOCK;
+    default: return kOPBlock;
+  }
+}
+
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s) {
   switch (kind & 0xF00) {
     case ar::kKQEncode: AR_LAUNCH(q_encode, grid, dim3(AR_BLOCK), 0, s, a); break;

@@ -95,3 +95,24 @@ def bucketed_arenas(nranks, sizes, offsets, arena_count, seed=0, sigma=1e-3, dty
             a[offsets[t]:offsets[t] + int(c)] = bucketed_tensor_values(r, t, c, seed, sigma, dtype)
         return a
     return _per_rank(fill, nranks)
+
+
+def device_rank(r, count, seed=0, sigma=1e-3, dtype="fp32", heavy=False, device="cuda:0"):
+    """Rank r's input drawn on the device (for buffers too large to stage
+    through host memory): x ~ N(0, sigma) fp32 from torch's generator seeded
+    with (seed, r); heavy=True multiplies each value by exp(N(0, 1)) so that
+    magnitudes vary over several decades.  bf16 is torch's conversion of the
+    fp32 draw, returned as int16 storage."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(r))
+    x = torch.randn(int(count), generator=g, device=device, dtype=torch.float32)
+    x.mul_(sigma)
+    if heavy:
+        y = torch.randn(int(count), generator=g, device=device, dtype=torch.float32)
+        x.mul_(y.exp_())
+        del y
+    if dtype == "fp32":
+        return x
+    return x.to(torch.bfloat16).view(torch.int16)

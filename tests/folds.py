@@ -160,12 +160,14 @@ QBLOCK = 128
 def int8_roundtrip(x):
     """Blockwise INT8 encode then decode of one block (float32 vector):
     s = max|x| / 127, q = round-half-even(x / s) clamped to [-127, 127],
-    value q * s; a block of zeros stays zero."""
+    value q * s (a zero code gives +0); a block of zeros stays zero."""
     x = np.asarray(x, np.float32)
     s = np.float32(np.max(np.abs(x)) / np.float32(127.0)) if len(x) else np.float32(0)
     if s == 0:
         return np.zeros_like(x)
-    q = np.clip(np.rint(x / s), -127, 127).astype(np.float32)
+    # the code is an integer (int8 has no negative zero), so a zero code
+    # decodes to +0
+    q = np.clip(np.rint(x / s), -127, 127).astype(np.int8).astype(np.float32)
     return (q * s).astype(np.float32)
 
 

@@ -1,0 +1,144 @@
+"""GPU parity beyond 2^32 elements per rank.
+
+Buffers of 2^32 + 2^20 + 77 elements per rank (17.2 GB of fp32) put element
+offsets, chunk bounds and byte offsets past both the signed and the unsigned
+32-bit range, so every index path of the kernels and the planner is
+exercised at its widest.  The inputs
+are drawn on the device (too large to stage through host memory); the check
+gathers, before and after the call, the elements around every chunk bound of
+every partition the schedules use, around 2^31 and 2^32, at the ragged tail and at
+random positions, and compares them bit for bit with the closed-form folds of
+`tests/folds.py` (the per-element sum order of each schedule, pinned against
+the oracle on the CPU).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from gradient_all_reduce_ar_amd import _binding as B
+from gradient_all_reduce_ar_amd import workloads
+from tests import folds
+
+pytestmark = pytest.mark.gpu
+
+COUNT = (1 << 32) + (1 << 20) + 77
+Q = B.QBLOCK
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _positions(count, unit, rng, window=130, nrand=20000):
+    """Sorted unique positions (elements, or INT8 blocks when unit=128) near
+    every bound part(count, k, c) for k <= 16, near 2^31 / unit and
+    2^32 / unit, at both ends and at random."""
+    n_units = (count + unit - 1) // unit
+    marks = {0, n_units, (1 << 31) // unit, (1 << 32) // unit}
+    for k in range(1, 17):
+        for c in range(k + 1):
+            marks.add((c * n_units) // k)
+            marks.add((c * (n_units // 2)) // k)  # halves of halves (Rabenseifner)
+    pos = set()
+    for m in marks:
+        pos.update(range(max(0, m - window), min(n_units, m + window)))
+    pos.update(int(v) for v in rng.integers(0, n_units, nrand))
+    return np.array(sorted(pos), np.int64)
+
+
+def _gather(ts, idx):
+    import torch
+
+    it = torch.from_numpy(idx).to(ts[0].device)
+    return [t.index_select(0, it).cpu().numpy() for t in ts]
+
+
+def _block_elems(blocks, count):
+    e = (blocks[:, None] * Q + np.arange(Q)[None, :]).reshape(-1)
+    return e[e < count]
+
+
+@pytest.mark.parametrize("sched,n,g,dtype,mode", [
+    ("ring", 4, 1, "fp32", "steps"),
+    ("ring", 4, 1, "fp32", "onepass"),
+    ("hierarchical", 4, 2, "bf16", "steps"),
+    ("rabenseifner", 4, 1, "fp32", "steps"),
+    ("double_tree", 2, 1, "bf16_each", "onepass"),
+])
+def test_beyond_2_32_elements(sched, n, g, dtype, mode):
+    import torch
+
+    _say(f"large {sched} n={n} g={g} {dtype} {mode} count={COUNT}")
+    gen = "fp32" if dtype == "fp32" else "bf16"
+    bufs = [workloads.device_rank(r, COUNT, seed=11, sigma=1.0, dtype=gen) for r in range(n)]
+    idx = _positions(COUNT, 1, np.random.default_rng(3))
+    before = _gather(bufs, idx)
+    plan = B.ar_plan_create(n, g, COUNT, dtype, sched)
+    try:
+        B.ar_plan_set_exec(plan, mode)
+        B.ar_allreduce(plan, bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+    finally:
+        B.ar_plan_destroy(plan)
+    after = _gather(bufs, idx)
+    del bufs
+    torch.cuda.empty_cache()
+    if dtype == "fp32":
+        want = np.array([folds.fold_at([before[r][i] for r in range(n)], int(e), COUNT, sched, g)
+                         for i, e in enumerate(idx)], np.float32).view(np.uint32)
+        got = [a.view(np.uint32) for a in after]
+    else:
+        vals = [folds.widen(b.view(np.uint16)) for b in before]
+        add = folds.add_bf16_each if dtype == "bf16_each" else folds.add32
+        acc = np.array([folds.fold_at([vals[r][i] for r in range(n)], int(e), COUNT, sched, g, add)
+                        for i, e in enumerate(idx)], np.float32)
+        want = folds.to_bf16_bits(acc)
+        got = [a.view(np.uint16) for a in after]
+    for r in range(n):
+        bad = np.flatnonzero(got[r] != want)
+        assert bad.size == 0, f"rank {r}: {bad.size} of {idx.size} sampled elements differ, first at {idx[bad[:5]]}"
+
+
+@pytest.mark.parametrize("mode", ["steps", "onepass"])
+def test_int8_ef_beyond_2_32_elements(mode):
+    import torch
+
+    n, sched = 3, "ring"
+    _say(f"large int8_ef {sched} n={n} {mode} count={COUNT}")
+    nblk = (COUNT + Q - 1) // Q
+    blocks = _positions(COUNT, Q, np.random.default_rng(4), window=3, nrand=2000)
+    idx = _block_elems(blocks, COUNT)
+    grads = [workloads.device_rank(r, COUNT, seed=12, sigma=1.0, heavy=True) for r in range(n)]
+    errs = [workloads.device_rank(r, COUNT, seed=13, sigma=1e-2) for r in range(n)]
+    g0, e0 = _gather(grads, idx), _gather(errs, idx)
+    plan = B.ar_plan_create(n, 1, COUNT, "int8_ef", sched)
+    try:
+        B.ar_plan_set_exec(plan, mode)
+        B.ar_allreduce_ef(plan, grads, errs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+    finally:
+        B.ar_plan_destroy(plan)
+    g1, e1 = _gather(grads, idx), _gather(errs, idx)
+    del grads, errs
+    torch.cuda.empty_cache()
+
+    def add(a, b):
+        return folds.int8_roundtrip((np.asarray(a, np.float32) + np.asarray(b, np.float32)).astype(np.float32))
+
+    start = 0
+    for blk in blocks:
+        width = min(COUNT, (int(blk) + 1) * Q) - int(blk) * Q
+        sl = slice(start, start + width)
+        start += width
+        col = []
+        for r in range(n):
+            x = (g0[r][sl] + e0[r][sl]).astype(np.float32)
+            v = folds.int8_roundtrip(x)
+            want_e = (x - v).astype(np.float32)
+            assert np.array_equal(e1[r][sl].view(np.uint32), want_e.view(np.uint32)), f"residual rank {r} block {blk}"
+            col.append(v)
+        want = np.asarray(folds.fold_at(col, int(blk), nblk, sched, 1, add), np.float32)
+        for r in range(n):
+            assert np.array_equal(g1[r][sl].view(np.uint32), want.view(np.uint32)), f"result rank {r} block {blk}"

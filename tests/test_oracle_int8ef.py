@@ -189,8 +189,10 @@ def test_matches_block_level_closed_form(schedule, n, g):
         errs = [e.copy() for e in es]
         oracle.run_int8ef(bufs, schedule, errs=errs, group_size=g)
         for r in range(n):
-            np.testing.assert_array_equal(bufs[r], want, err_msg=f"{schedule} n={n} count={count} rank={r}")
-            np.testing.assert_array_equal(errs[r], want_e[r])
+            # bit patterns: a decoded zero code is +0 on both sides
+            np.testing.assert_array_equal(bufs[r].view(np.uint32), want.view(np.uint32),
+                                          err_msg=f"{schedule} n={n} count={count} rank={r}")
+            np.testing.assert_array_equal(errs[r].view(np.uint32), want_e[r].view(np.uint32))
 
 
 @pytest.mark.parametrize("schedule,n,g", SCHEDS)
