@@ -220,11 +220,14 @@ def main():
         offsets, arena = B.ar_bucket_layout(plan, len(sizes))
         host = workloads.bucketed_arenas(n, sizes, offsets, arena, dtype=gen_dtype)
         count_logical = int(sum(int(c) for c in sizes))
+        # the buckets' all-reduces in shared launches: the plan that runs them
+        lplan = B.ar_bucket_batched_plan(plan)
     else:
         plan = B.ar_plan_create(n, group, count, dtype, sched)
         B.ar_plan_set_exec(plan, args.exec)
         host = workloads.normal_inputs(n, count, seed=0, dtype=gen_dtype)
         count_logical = count
+        lplan = plan
     bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
     errs = None
     if quant:
@@ -255,37 +258,23 @@ def main():
         run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
     else:
         run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
-    period = None
-    if not bucketed:
-        # time about four launches per call (every launch over `period` calls),
-        # so the timing events barely perturb the calls they time
-        period = max(1, B.ar_plan_num_launches(plan) // 4)
-        B.ar_plan_set_profiling(plan, max(args.steps, 1))
-        B.ar_plan_set_profiling_period(plan, period)
+    # time about four launches per call (every launch over `period` calls),
+    # so the timing events barely perturb the calls they time
+    period = max(1, B.ar_plan_num_launches(lplan) // 4)
+    B.ar_plan_set_profiling(lplan, max(args.steps, 1))
+    B.ar_plan_set_profiling_period(lplan, period)
 
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    if not bucketed:
-        B.ar_plan_launch_times(plan)  # clear the warm-up entries
+    B.ar_plan_launch_times(lplan)  # clear the warm-up entries
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if bucketed:
-        # one event after each bucket of each timed call (per-bucket times)
-        nb = B.ar_bucket_count(plan)
-        bucket_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)] for _ in range(args.steps)]
-        for call in bucket_ev:
-            for e in call:
-                e.record(stream)  # creates the underlying events outside the timed region
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record(stream)
     for c in range(args.steps):
-        if bucketed:
-            bucket_ev[c][0].record(stream)
-            B.ar_bucket_allreduce_after(plan, bufs, stream, None, bucket_ev[c][1:])
-        else:
-            run()
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
@@ -296,9 +285,71 @@ def main():
     S = count_logical * elem
     algbw = S / (ms * 1e-3) / 1e9
     busbw = algbw * 2 * (n - 1) / n
-    stats = B.ar_bucket_stats(plan) if bucketed else B.ar_plan_stats(plan)
+    stats = B.ar_plan_stats(lplan)
+    model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
+
+    roofline = None
+    per_kind = {}
+    times = B.ar_plan_launch_times(lplan)  # -1: launch not timed in that call (sampling)
+    nl = B.ar_plan_num_launches(lplan)
+    lb = [launch_bytes(B, lplan, i, n, elem, count) for i in range(nl)]
+    per_call_count = {}
+    for nbytes, kind in lb:
+        per_call_count[kind] = per_call_count.get(kind, 0) + 1
+    for call in times:
+        for i, t in enumerate(call):
+            if t < 0:
+                continue
+            nbytes, kind = lb[i]
+            k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0})
+            k["ms"] += t
+            k["launches"] += 1
+            k["bytes"] += nbytes
+    # the kernel with the largest share of a call's GPU time
+    dom = max(per_kind, key=lambda f: per_kind[f]["ms"] / per_kind[f]["launches"] * per_call_count[f])
+    d = per_kind[dom]
+    avg_ms = d["ms"] / d["launches"]
+    bytes_per_launch = d["bytes"] / d["launches"]
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    traffic = traffic_record(kernel_label(dom), args.workload, args.exec)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": kernel_label(dom),
+                "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                "launches_timed": d["launches"], "profiling_period": period}
+    log("per kernel:", {kernel_label(f): {"ms_timed": round(v["ms"], 3), "launches_timed": v["launches"],
+                                          "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                          for f, v in per_kind.items()})
+    # kernel time per call: each launch's mean over the calls that timed it
+    means = []
+    for i in range(nl):
+        ts = [call[i] for call in times if call[i] >= 0]
+        means.append(sum(ts) / len(ts) if ts else None)
+    sum_launch_ms = sum(means) if all(m is not None for m in means) else None
+    B.ar_plan_set_profiling(lplan, 0)
+
+    # ---- buckets one by one, each with its own launches and a HIP event after
+    # it (per-bucket times)
     per_bucket = None
+    extra = {}
     if bucketed:
+        nb = B.ar_bucket_count(plan)
+        B.ar_bucket_set_batching(plan, False)
+        bucket_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)] for _ in range(args.steps)]
+        for call in bucket_ev:
+            for e in call:
+                e.record(stream)  # creates the underlying events outside the timed region
+        reset_inputs()
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t_b0 = time.perf_counter()
+        for c in range(args.steps):
+            bucket_ev[c][0].record(stream)
+            B.ar_bucket_allreduce_after(plan, bufs, stream, None, bucket_ev[c][1:])
+        torch.cuda.synchronize()
+        obo_ms = (time.perf_counter() - t_b0) * 1e3 / max(args.steps, 1)
+        B.ar_bucket_set_batching(plan, True)
         per_bucket = []
         for b in range(nb):
             t_b = sorted(call[b].elapsed_time(call[b + 1]) for call in bucket_ev)
@@ -307,55 +358,18 @@ def main():
             alg_b = cnt * elem / (med * 1e-3) / 1e9
             per_bucket.append({"bucket": b, "bytes_per_rank": cnt * elem, "median_ms": round(med, 4),
                                "algbw_GBps": round(alg_b, 1), "busbw_GBps": round(alg_b * 2 * (n - 1) / n, 1)})
-    model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
-
-    roofline = None
-    per_kind = {}
-    if not bucketed:
-        times = B.ar_plan_launch_times(plan)  # -1: launch not timed in that call (sampling)
-        nl = B.ar_plan_num_launches(plan)
-        lb = [launch_bytes(B, plan, i, n, elem, count) for i in range(nl)]
-        per_call_count = {}
-        for nbytes, kind in lb:
-            per_call_count[kind] = per_call_count.get(kind, 0) + 1
-        for call in times:
-            for i, t in enumerate(call):
-                if t < 0:
-                    continue
-                nbytes, kind = lb[i]
-                k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0})
-                k["ms"] += t
-                k["launches"] += 1
-                k["bytes"] += nbytes
-        # the kernel with the largest share of a call's GPU time
-        dom = max(per_kind, key=lambda f: per_kind[f]["ms"] / per_kind[f]["launches"] * per_call_count[f])
-        d = per_kind[dom]
-        avg_ms = d["ms"] / d["launches"]
-        bytes_per_launch = d["bytes"] / d["launches"]
-        achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
-        traffic = traffic_record(kernel_label(dom), args.workload, args.exec)
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                    "kernel": kernel_label(dom),
-                    "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                    "launches_timed": d["launches"], "profiling_period": period}
-        log("per kernel:", {kernel_label(f): {"ms_timed": round(v["ms"], 3), "launches_timed": v["launches"],
-                                                  "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
-                                  for f, v in per_kind.items()})
-        # kernel time per call: each launch's mean over the calls that timed it
-        means = []
-        for i in range(nl):
-            ts = [call[i] for call in times if call[i] >= 0]
-            means.append(sum(ts) / len(ts) if ts else None)
-        sum_launch_ms = sum(means) if all(m is not None for m in means) else None
-    else:
-        sum_launch_ms = None
+        obo_alg = S / (obo_ms * 1e-3) / 1e9
+        extra["buckets_one_by_one"] = {
+            "ms_per_step": round(obo_ms, 4), "busbw_GBps": round(obo_alg * 2 * (n - 1) / n, 1),
+            "algbw_GBps": round(obo_alg, 1), "launches_per_step": B.ar_bucket_stats(plan)["launches"]}
 
     # ---- one-pass comparison on the same buffers (bit-identical results)
-    extra = {}
-    if not args.no_extra and args.exec != "onepass" and not bucketed:
-        B.ar_plan_set_profiling(plan, 0)
-        B.ar_plan_set_exec(plan, "onepass")
+    if not args.no_extra and args.exec != "onepass":
+        if bucketed:
+            B.ar_bucket_set_exec(plan, "onepass")
+            lplan = None  # rebuilt for the new mode
+        else:
+            B.ar_plan_set_exec(plan, "onepass")
         reset_inputs()
         for _ in range(args.warmup):
             run()
@@ -366,7 +380,7 @@ def main():
         torch.cuda.synchronize()
         op_ms = (time.perf_counter() - t_a) * 1e3 / max(args.steps, 1)
         op_alg = S / (op_ms * 1e-3) / 1e9
-        op_stats = B.ar_plan_stats(plan)
+        op_stats = B.ar_plan_stats(B.ar_bucket_batched_plan(plan) if bucketed else plan)
         extra["onepass"] = {"ms_per_step": round(op_ms, 4), "busbw_GBps": round(op_alg * 2 * (n - 1) / n, 1),
                             "algbw_GBps": round(op_alg, 1),
                             "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
@@ -376,6 +390,7 @@ def main():
     if not args.no_extra:
         for name, graph in (("without_launch_events", False), ("graph", True)):
             if bucketed:
+                B.ar_bucket_set_exec(plan, args.exec)
                 B.ar_bucket_set_graph(plan, graph)
             else:
                 B.ar_plan_set_profiling(plan, 0)
@@ -453,7 +468,8 @@ def main():
         "config": {
             "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,
             "count_per_rank": count_logical, "bytes_per_rank": S, "exec": args.exec,
-            "executor": "eager launches with a HIP event after each (for the roofline)",
+            "executor": ("buckets batched: every bucket's all-reduce in shared launches, " if bucketed else "")
+            + f"eager launches, about four per call timed by HIP events (every launch over {period} calls)",
             "algbw_GBps": round(algbw, 1), "busbw_GBps": round(busbw, 1),
             "hbm_model_bytes": stats["hbm_bytes_model"], "hbm_model_GBps": round(model_gbps, 1),
             "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),
@@ -474,7 +490,7 @@ def main():
         out["config"]["wire_compression_vs_fp32"] = round(sent_f32 / stats["bytes_sent_total"], 4)
     if bucketed:
         out["config"]["buckets"] = B.ar_bucket_count(plan)
-        out["config"]["per_bucket"] = per_bucket
+        out["config"]["per_bucket_one_by_one"] = per_bucket
         B.ar_bucket_plan_destroy(plan)
     else:
         B.ar_plan_destroy(plan)

@@ -110,6 +110,9 @@ def _declare(L):
         "ar_bucket_count": ([P], i32),
         "ar_bucket_range": ([P, i32, psz, psz], ctypes.c_int),
         "ar_bucket_set_exec": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_bucket_set_batching": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_bucket_set_cache_bytes": ([P, sz], ctypes.c_int),
+        "ar_bucket_batched_plan": ([P], P),
         "ar_bucket_allreduce": ([P, P, P], ctypes.c_int),
         "ar_bucket_allreduce_after": ([P, P, P, P, P], ctypes.c_int),
         "ar_bucket_allreduce_ef": ([P, P, P, P, P, P], ctypes.c_int),
@@ -342,6 +345,22 @@ def ar_bucket_set_graph(bp, enable=True):
 
 def ar_bucket_set_exec(bp, exec_mode):
     _check(lib().ar_bucket_set_exec(bp, _code(EXECS, exec_mode)))
+
+
+def ar_bucket_set_cache_bytes(bp, nbytes):
+    _check(lib().ar_bucket_set_cache_bytes(bp, int(nbytes)))
+
+
+def ar_bucket_set_batching(bp, enable=True):
+    _check(lib().ar_bucket_set_batching(bp, 1 if enable else 0))
+
+
+def ar_bucket_batched_plan(bp):
+    """The bucket plan's batched plan (owned by bp: never destroy it)."""
+    p = lib().ar_bucket_batched_plan(bp)
+    if not p:
+        _raise()
+    return p
 
 
 def ar_bucket_allreduce(bp, rank_arenas, stream=None):

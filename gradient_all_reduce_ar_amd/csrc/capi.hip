@@ -96,6 +96,11 @@ struct ar_bucket_plan {
   std::vector<uint64_t> bytes_sent;
   float *scratch = nullptr;
   size_t scratch_bytes = 0;
+  // Batched execution: every bucket's all-reduce in shared launches (one
+  // plan over the whole arena, built on first use).
+  bool batch = true;
+  bool use_graph = false;
+  ar_plan_t *merged = nullptr;
 };
 
 namespace {
@@ -105,17 +110,6 @@ bool is_quant_kind(int32_t kind) {
   if (fam == ar::kKRing || fam == ar::kKHier || fam == ar::kKTree || fam == ar::kKDTree)
     return (kind & 3) == ar::kI8EF;  // one-pass fold of an INT8 plan
   return fam == ar::kKQEncode || fam == ar::kKQReduce || fam == ar::kKQCopy || fam == ar::kKQDecode;
-}
-
-// Bytes a launch writes (both outputs of fused ops).
-int64_t launch_written_bytes(const ar::Plan &p, const ar::Launch &L) {
-  const int32_t fam = L.kind & 0xF00;
-  int64_t elems = 0;
-  for (const ar::Op &o : L.ops) elems += (o.hi - o.lo) * ((o.o2 != ar::kLocNone) ? 2 : 1);
-  int64_t eb = ar::elem_bytes(p.dtype);
-  if (fam == ar::kKReduce && p.dtype == ar::kBF16 && !(L.kind & ar::kFlagOBf)) eb = 4;  // fp32 partials
-  if (fam != ar::kKReduce && fam != ar::kKCopy) elems *= p.nranks;
-  return elems * eb;
 }
 
 ar_status_t prepare(ar_plan_t *pl) {
@@ -136,7 +130,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
     const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
     const bool quant = is_quant_kind(L.kind);
-    const bool cold = !quant && !out_scratch && launch_written_bytes(pl->p, L) > pl->p.cache_bytes;
+    const bool cold = !quant && !out_scratch && ar::launch_write_bytes(pl->p, L) > pl->p.cache_bytes;
     pl->cold.push_back(cold);
     const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold);
     int64_t gx = 0;
@@ -626,6 +620,44 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
 
 // ---------------------------------------------------------------- buckets
 
+}  // extern "C"
+
+namespace {
+
+void drop_merged(ar_bucket_plan_t *bp) {
+  if (bp->merged) ar_plan_destroy(bp->merged);
+  bp->merged = nullptr;
+}
+
+// The batched plan of a bucket plan, built on first use (NULL for INT8).
+ar_plan_t *merged_plan(ar_bucket_plan_t *bp) {
+  if (bp->merged) return bp->merged;
+  if (bp->dtype == AR_INT8_EF) {
+    fail(AR_ERR_UNSUPPORTED, "INT8 buckets run one by one");
+    return nullptr;
+  }
+  std::vector<const ar::Plan *> parts;
+  for (ar_plan_t *pl : bp->plans) parts.push_back(&pl->p);
+  auto *m = new (std::nothrow) ar_plan_t;
+  if (!m) {
+    fail(AR_ERR_OOM, "host allocation failed");
+    return nullptr;
+  }
+  const std::string err = ar::merge_segments(m->p, parts, bp->bucket_offset, bp->arena_count);
+  if (!err.empty()) {
+    delete m;
+    fail(AR_ERR_INVALID_ARG, "batched buckets: " + err);
+    return nullptr;
+  }
+  m->use_graph = bp->use_graph;
+  bp->merged = m;
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
 ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t *tensor_counts, int ntensors,
                                         ar_dtype_t dtype, ar_schedule_t schedule, size_t bucket_cap_bytes) {
   if (ntensors < 0 || (ntensors > 0 && !tensor_counts) || bucket_cap_bytes == 0) {
@@ -700,6 +732,8 @@ ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable) {
     const ar_status_t st = ar_plan_set_graph(pl, enable);
     if (st != AR_OK) return st;
   }
+  bp->use_graph = enable != 0;
+  if (bp->merged) return ar_plan_set_graph(bp->merged, enable);
   return AR_OK;
 }
 
@@ -709,7 +743,44 @@ ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
     const ar_status_t st = ar_plan_set_exec(pl, exec);
     if (st != AR_OK) return st;
   }
+  if (bp->merged) {
+    (void)hipDeviceSynchronize();  // its launches may still be in flight
+    drop_merged(bp);
+  }
   return AR_OK;
+}
+
+ar_status_t ar_bucket_set_cache_bytes(ar_bucket_plan_t *bp, size_t bytes) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  for (ar_plan_t *pl : bp->plans) {
+    const ar_status_t st = ar_plan_set_cache_bytes(pl, bytes);
+    if (st != AR_OK) return st;
+  }
+  if (bp->merged) {
+    (void)hipDeviceSynchronize();  // its launches may still be in flight
+    drop_merged(bp);
+  }
+  return AR_OK;
+}
+
+ar_status_t ar_bucket_set_batching(ar_bucket_plan_t *bp, int enable) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  bp->batch = enable != 0;
+  return AR_OK;
+}
+
+ar_plan_t *ar_bucket_batched_plan(ar_bucket_plan_t *bp) {
+  if (!bp) {
+    fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+    return nullptr;
+  }
+  if (bp->plans.empty()) {
+    fail(AR_ERR_INVALID_ARG, "bucket plan has no buckets");
+    return nullptr;
+  }
+  ar_plan_t *m = merged_plan(bp);
+  if (m) g_status = AR_OK;
+  return m;
 }
 
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream) {
@@ -739,6 +810,12 @@ ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arena
                                    void *stream, void *const *ready_events, void *const *done_events) {
   if (!bp || !rank_arenas) return fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
   if (error_arenas && bp->dtype != AR_INT8_EF) return fail(AR_ERR_INVALID_ARG, "error feedback needs AR_INT8_EF");
+  if (bp->plans.empty()) return AR_OK;
+  if (bp->batch && bp->dtype != AR_INT8_EF && !ready_events && !done_events) {
+    ar_plan_t *m = merged_plan(bp);
+    if (!m) return g_status;
+    return ar_allreduce(m, rank_arenas, stream);
+  }
   // one scratch shared by all buckets: they run one after another on one stream
   size_t need = 0;
   for (ar_plan_t *pl : bp->plans) need = std::max(need, pl->need_scratch_bytes());
@@ -814,6 +891,7 @@ ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
 
 void ar_bucket_plan_destroy(ar_bucket_plan_t *bp) {
   if (!bp) return;
+  drop_merged(bp);
   for (ar_plan_t *pl : bp->plans) {
     pl->external_scratch = nullptr;
     ar_plan_destroy(pl);

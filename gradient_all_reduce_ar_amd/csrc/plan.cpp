@@ -859,6 +859,89 @@ double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross,
   return total;
 }
 
+int64_t launch_write_bytes(const Plan &p, const Launch &L) {
+  const int32_t fam = L.kind & 0xF00;
+  int64_t elems = 0;
+  for (const Op &o : L.ops) elems += unit_elems(p, o.lo, o.hi) * ((o.o2 != kLocNone) ? 2 : 1);
+  int64_t eb = buffer_elem_bytes(p.dtype);
+  if (fam == kKReduce && p.dtype == kBF16 && !(L.kind & kFlagOBf)) eb = 4;  // fp32 partials
+  if (fam == kKQReduce || fam == kKQCopy || fam == kKQEncode) eb = 1;       // codes
+  if (fam == kKRing || fam == kKHier || fam == kKTree || fam == kKDTree) elems *= p.nranks;
+  return elems * eb;
+}
+
+std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, const std::vector<int64_t> &offsets,
+                           int64_t count) {
+  if (parts.empty() || parts.size() != offsets.size()) return "no segments";
+  const Plan &p0 = *parts[0];
+  if (p0.dtype == kI8EF) return "INT8 plans are not merged";
+  int64_t end = 0;
+  for (size_t k = 0; k < parts.size(); ++k) {
+    const Plan &q = *parts[k];
+    if (q.nranks != p0.nranks || q.group_size != p0.group_size || q.dtype != p0.dtype || q.sched != p0.sched ||
+        q.exec != p0.exec)
+      return "segments differ in ranks, dtype, schedule or exec mode";
+    if (offsets[k] < end || q.count < 0 || offsets[k] > count - q.count) return "segments overlap or exceed the buffer";
+    end = offsets[k] + q.count;
+  }
+  Plan m;
+  m.nranks = p0.nranks;
+  m.group_size = p0.group_size;
+  m.count = count;
+  m.units = count;
+  m.dtype = p0.dtype;
+  m.sched = p0.sched;
+  m.exec = p0.exec;
+  m.cache_bytes = p0.cache_bytes;
+  for (size_t k = 0; k < parts.size(); ++k) {
+    m.nsteps = std::max(m.nsteps, parts[k]->nsteps);
+    m.nslots = std::max(m.nslots, parts[k]->nslots);
+    for (Transfer x : parts[k]->xfers) {
+      x.lo += offsets[k];
+      x.hi += offsets[k];
+      m.xfers.push_back(x);
+    }
+  }
+  std::stable_sort(m.xfers.begin(), m.xfers.end(), [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
+  // batches of consecutive segments
+  std::vector<size_t> first{0};
+  int64_t fill = 0;
+  for (size_t k = 0; k < parts.size(); ++k) {
+    int64_t widest = 0;
+    for (const Launch &L : parts[k]->launches) widest = std::max(widest, launch_write_bytes(*parts[k], L));
+    if (m.exec != kOnePass && fill > 0 && fill + widest > m.cache_bytes) {
+      first.push_back(k);
+      fill = 0;
+    }
+    fill += widest;
+  }
+  first.push_back(parts.size());
+  for (size_t b = 0; b + 1 < first.size(); ++b) {
+    std::vector<size_t> next(parts.size(), 0);  // next launch of each segment of the batch
+    for (;;) {
+      int32_t kind = -1;
+      for (size_t k = first[b]; k < first[b + 1] && kind < 0; ++k)
+        if (next[k] < parts[k]->launches.size()) kind = parts[k]->launches[next[k]].kind;
+      if (kind < 0) break;
+      Launch L{kind, {}};
+      for (size_t k = first[b]; k < first[b + 1]; ++k) {
+        if (next[k] >= parts[k]->launches.size() || parts[k]->launches[next[k]].kind != kind) continue;
+        for (Op o : parts[k]->launches[next[k]].ops) {
+          o.lo += offsets[k];
+          o.hi += offsets[k];
+          L.ops.push_back(o);
+        }
+        ++next[k];
+      }
+      m.launches.push_back(std::move(L));
+    }
+  }
+  m.slot_stride = (count + 63) / 64 * 64;
+  compute_stats(m);
+  out = std::move(m);
+  return "";
+}
+
 std::string check_hazards(const Plan &p) {
   struct Acc { int32_t loc; int64_t lo, hi; bool write; };
   for (size_t li = 0; li < p.launches.size(); ++li) {

@@ -136,6 +136,26 @@ double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw
 double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross, double bw_intra, double bw_cross,
                           double bw_egress, double egress_share);
 
+// Bytes one launch writes (both outputs of fused ops; fp32 partials of
+// kBF16 reduces; every rank's output of a one-pass fold).
+int64_t launch_write_bytes(const Plan &p, const Launch &L);
+
+// Several independent all-reduces of one kind side by side.  Segment k is an
+// all-reduce planned as parts[k] (parts[k]->count elements) at element offset
+// offsets[k] of every rank buffer; the segments are disjoint and lie within
+// [0, count).  Segments are taken in order into batches: in the step modes a
+// batch holds as many segments as fit, by their widest launch, in
+// cache_bytes (at least one); in the one-pass mode every segment is in one
+// batch.  Within a batch the launch lists are merged in order: the next
+// merged launch takes the next launch of every segment whose next launch has
+// the kind of the first unfinished segment's next launch, so segments with
+// equal launch lists share every launch.  Each segment's launches keep their
+// order and every element its segment's arithmetic, so the result is that of
+// the segments run one after another.  fp32 and bf16 plans only (INT8 blocks
+// are counted per segment).  Empty string on success.
+std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, const std::vector<int64_t> &offsets,
+                           int64_t count);
+
 // Checks that within every launch no op writes a (location, range) that
 // another op of the same launch reads or writes.  Empty string if clean.
 std::string check_hazards(const Plan &p);

@@ -333,6 +333,17 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
  * assignment order; every bucket starts 256-byte aligned in a per-rank
  * arena.  One all-reduce plan runs per bucket, in bucket order, on one
  * stream; the gaps between buckets are never touched.
+ *
+ * Batched execution (the default for fp32 and bf16 dtypes when no events
+ * are given): the buckets' all-reduces share launches.  Buckets are taken in
+ * order into batches whose widest round writes at most the plan's assumed
+ * device cache (ar_plan_set_cache_bytes; every bucket in one batch in the
+ * one-pass mode), and launch i of a batch runs launch i of each of its
+ * buckets, so a batch costs the launches of one bucket.  Every bucket is
+ * still its own all-reduce with its own partition and summation order: the
+ * result is bit for bit that of the buckets run one by one.  The batched
+ * plan owns an fp32 scratch covering the whole arena for bf16
+ * (nslots x arena_count x 4 bytes).
  */
 typedef struct ar_bucket_plan ar_bucket_plan_t;
 
@@ -347,10 +358,26 @@ int32_t ar_bucket_count(const ar_bucket_plan_t *bp);
 /* Element offset and length of bucket b in the arena. */
 ar_status_t ar_bucket_range(const ar_bucket_plan_t *bp, int32_t b, size_t *offset, size_t *count);
 ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec);
-/* Graph replay for every bucket's plan (see ar_plan_set_graph). */
+/* Graph replay for every bucket's plan and the batched plan (see
+ * ar_plan_set_graph). */
 ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable);
+/* ar_plan_set_cache_bytes for every bucket's plan; the batched plan is
+ * rebuilt with the new size on its next use.  Host only. */
+ar_status_t ar_bucket_set_cache_bytes(ar_bucket_plan_t *bp, size_t bytes);
+/* enable = 0: ar_bucket_allreduce runs the buckets one by one, each with its
+ * own launches; non-zero (default): batched.  Host only. */
+ar_status_t ar_bucket_set_batching(ar_bucket_plan_t *bp, int enable);
+/* The batched plan (built on first use, owned by bp, valid until the exec
+ * mode changes or bp is destroyed), for inspection, profiling and graph
+ * settings through the ar_plan_* calls: its count is the arena length and
+ * its launches are what batched ar_bucket_allreduce runs.  NULL, with
+ * AR_ERR_UNSUPPORTED, for AR_INT8_EF (INT8 buckets always run one by one);
+ * NULL with AR_ERR_INVALID_ARG for a plan without buckets.  Not to be passed
+ * to ar_plan_destroy. */
+ar_plan_t *ar_bucket_batched_plan(ar_bucket_plan_t *bp);
 /* All-reduces every bucket of the nranks arenas (16-byte aligned device
- * pointers of arena_count elements), in place, on `stream`. */
+ * pointers of arena_count elements), in place, on `stream` (batched unless
+ * turned off or AR_INT8_EF). */
 ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream);
 /* Overlap with the backward pass (Scaling ML systems ch. 06, "Overlap layer
  * by layer" and "Bucket fusion"; Primer ch. 4 section 4.7): like
@@ -359,7 +386,8 @@ ar_status_t ar_bucket_allreduce(ar_bucket_plan_t *bp, void *const *rank_arenas, 
  * any stream; NULL = ready now), and done_events[b] (if the array and the
  * entry are not NULL) is recorded on `stream` after it.  So each bucket
  * starts when it is ready and the previous bucket's all-reduce is done, as in
- * Figure 4.15.  Both arrays have ar_bucket_count entries. */
+ * Figure 4.15.  Both arrays have ar_bucket_count entries.  With either array
+ * given, the buckets run one by one (not batched). */
 ar_status_t ar_bucket_allreduce_after(ar_bucket_plan_t *bp, void *const *rank_arenas, void *stream,
                                       void *const *ready_events, void *const *done_events);
 /* The same for AR_INT8_EF bucket plans with error feedback: error_arenas
@@ -379,7 +407,9 @@ ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arena
 double ar_overlap_step_time(int nchunks, const double *ready_s, const double *comm_s, double compute_end_s,
                             double update_s, double *exposed_s);
 
-/* Sum of the per-bucket statistics (bytes, steps, launches). */
+/* Sum of the per-bucket statistics (bytes, steps, launches) of the buckets
+ * run one by one (the batched plan's own statistics, launches included,
+ * come from ar_plan_stats on ar_bucket_batched_plan). */
 ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp);
 void ar_bucket_plan_destroy(ar_bucket_plan_t *bp);
 

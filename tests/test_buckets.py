@@ -76,35 +76,188 @@ def test_reverse_order_and_c5_shape():
         B.ar_bucket_plan_destroy(bp)
 
 
+BATCH_CASES = [("ring", 4, 1), ("ring", 5, 1), ("hierarchical", 8, 4), ("hierarchical", 6, 3),
+               ("rabenseifner", 8, 1), ("recursive_doubling", 4, 1), ("tree", 5, 1), ("double_tree", 8, 1)]
+
+
+def _small_bucket_case(seed):
+    rng = np.random.default_rng(seed)
+    return [int(s) for s in rng.integers(1, 3000, 40)] + [0, 1, 7]
+
+
+@pytest.mark.parametrize("sched,n,g", BATCH_CASES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused", "onepass"])
+def test_batched_plan_matches_oracle(sched, n, g, dtype, mode):
+    """The batched launch list (every bucket's all-reduce in shared
+    launches), run over the whole arenas by the numpy interpreter, equals
+    the oracle bucket by bucket, bit for bit, and leaves the gaps alone.
+    Several cache sizes make one batch, a few, or one bucket per batch."""
+    from tests import plan_interp
+
+    eb = 4 if dtype == "fp32" else 2
+    sizes = _small_bucket_case(n * 31 + g)
+    bp = B.ar_bucket_plan_create(n, g, sizes, dtype, sched, 8 << 10)
+    try:
+        B.ar_bucket_set_exec(bp, mode)
+        offs, arena = B.ar_bucket_layout(bp, len(sizes))
+        nb = B.ar_bucket_count(bp)
+        ranges = [B.ar_bucket_range(bp, b) for b in range(nb)]
+        gen = "fp32" if dtype == "fp32" else "bf16"
+        host = workloads.bucketed_arenas(n, sizes, offs, arena, sigma=1.0, dtype=gen)
+        refs = [oracle.run([h[off:off + cnt].copy() for h in host], dtype, sched, group_size=g)
+                for off, cnt in ranges]
+        per_bucket = B.ar_bucket_stats(bp)["launches"]
+        for cache in (None, 3000 * eb, 1):
+            if cache is not None:
+                B.ar_bucket_set_cache_bytes(bp, cache)
+            m = B.ar_bucket_batched_plan(bp)
+            nl = B.ar_plan_num_launches(m)
+            assert nl <= B.ar_bucket_stats(bp)["launches"]
+            if cache == 1 and mode != "onepass":
+                assert nl == B.ar_bucket_stats(bp)["launches"]  # one bucket per batch
+            if cache is None:
+                assert nl < per_bucket or per_bucket <= 1
+            got = plan_interp.run(m, [h.copy() for h in host], dtype, g)
+            bv = np.uint32 if dtype == "fp32" else np.uint16
+            covered = np.zeros(arena, bool)
+            for b, (off, cnt) in enumerate(ranges):
+                covered[off:off + cnt] = True
+                for r in range(n):
+                    np.testing.assert_array_equal(got[r][off:off + cnt].view(bv), refs[b][r].view(bv),
+                                                  err_msg=f"cache={cache} bucket {b} rank {r}")
+            for r in range(n):
+                assert np.array_equal(got[r][~covered].view(bv), host[r][~covered].view(bv))
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+def test_batched_plan_c5_launches():
+    """C5 shape: 12 buckets of at most 25 MiB at 16 ranks.  In the step mode
+    the buckets form batches whose widest round (the fp32 partials, N chunks
+    x 4 B) fits 256 MiB; a batch takes the launches of one bucket.  One-pass:
+    one launch for everything."""
+    sizes = [int(s) for s in workloads.bucketed_tensor_sizes()]
+    bp = B.ar_bucket_plan_create(16, 1, sizes, "bf16", "ring", CAP)
+    try:
+        nb = B.ar_bucket_count(bp)
+        cnts = [B.ar_bucket_range(bp, b)[1] for b in range(nb)]
+        batches, fill = 1, 0
+        for c in cnts:
+            w = 4 * c  # a reduce-scatter round writes every element once as an fp32 partial
+            if fill and fill + w > 256 << 20:
+                batches, fill = batches + 1, 0
+            fill += w
+        m = B.ar_bucket_batched_plan(bp)
+        assert B.ar_bucket_stats(bp)["launches"] == 29 * nb
+        assert B.ar_plan_num_launches(m) == 29 * batches and batches < nb
+        st = B.ar_plan_stats(m)
+        assert st["count"] == B.ar_bucket_layout(bp, len(sizes))[1]
+        assert st["bytes_sent_total"] == B.ar_bucket_stats(bp)["bytes_sent_total"]
+        assert st["hbm_bytes_model"] == B.ar_bucket_stats(bp)["hbm_bytes_model"]
+        B.ar_bucket_set_exec(bp, "onepass")
+        assert B.ar_plan_num_launches(B.ar_bucket_batched_plan(bp)) == 1
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+def test_batched_plan_errors():
+    bp = B.ar_bucket_plan_create(4, 1, [300, 500], "int8_ef", "ring", CAP)
+    try:
+        with pytest.raises(B.ArError) as ei:
+            B.ar_bucket_batched_plan(bp)
+        assert ei.value.status == B.AR_ERR_UNSUPPORTED
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+    bp = B.ar_bucket_plan_create(4, 1, [], "fp32", "ring", CAP)
+    try:
+        with pytest.raises(B.ArError):
+            B.ar_bucket_batched_plan(bp)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
 @pytest.mark.gpu
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("n,sched", [(16, "rabenseifner"), (16, "ring"), (64, "rabenseifner"), (64, "ring")])
 def test_bucketed_bf16_parity(n, sched):
     """C5: 300 lognormal bf16 tensors per rank, 25 MiB buckets, one
-    all-reduce per bucket; bit-exact per bucket against the oracle, all ranks
-    identical, gaps between buckets untouched."""
+    all-reduce per bucket, batched (the default) and one by one; bit-exact
+    per bucket against the oracle, all ranks identical, gaps between buckets
+    untouched."""
     import torch
 
-    print(f"case bucketed n={n} {sched}", flush=True)
     sizes = [int(s) for s in workloads.bucketed_tensor_sizes()]
     bp = B.ar_bucket_plan_create(n, 1, sizes, "bf16", sched, CAP)
     try:
         offs, arena = B.ar_bucket_layout(bp, len(sizes))
         host = workloads.bucketed_arenas(n, sizes, offs, arena)
-        bufs = [torch.from_numpy(h.view(np.int16)).to("cuda:0") for h in host]
-        B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        for r in range(1, n):
-            assert torch.equal(bufs[r], bufs[0]), f"rank {r} differs from rank 0"
-        got = bufs[0].cpu().numpy().view(np.uint16)
-        del bufs
-        covered = np.zeros(arena, bool)
-        for b in range(B.ar_bucket_count(bp)):
-            off, cnt = B.ar_bucket_range(bp, b)
-            covered[off:off + cnt] = True
-            ref = oracle.run([h[off:off + cnt].copy() for h in host], "bf16", sched)
-            assert np.array_equal(got[off:off + cnt], ref[0]), f"bucket {b}"
-            print(f"  bucket {b}: {cnt} elements bit-exact", flush=True)
-        assert np.all(got[~covered] == 0)
+        nb = B.ar_bucket_count(bp)
+        refs = {}
+        for batch in (True, False):
+            print(f"case bucketed n={n} {sched} batched={batch}", flush=True)
+            B.ar_bucket_set_batching(bp, batch)
+            bufs = [torch.from_numpy(h.view(np.int16)).to("cuda:0") for h in host]
+            B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            for r in range(1, n):
+                assert torch.equal(bufs[r], bufs[0]), f"rank {r} differs from rank 0"
+            got = bufs[0].cpu().numpy().view(np.uint16)
+            del bufs
+            covered = np.zeros(arena, bool)
+            for b in range(nb):
+                off, cnt = B.ar_bucket_range(bp, b)
+                covered[off:off + cnt] = True
+                if b not in refs:
+                    refs[b] = oracle.run([h[off:off + cnt].copy() for h in host], "bf16", sched)[0]
+                assert np.array_equal(got[off:off + cnt], refs[b]), f"bucket {b} batched={batch}"
+            print(f"  {nb} buckets bit-exact", flush=True)
+            assert np.all(got[~covered] == 0)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("sched,n,g", BATCH_CASES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+def test_batched_small_gpu(sched, n, g, dtype):
+    """Batched buckets on the GPU at small sizes, every exec mode, eager and
+    replayed as a graph (three replays, each checked), against the oracle."""
+    import torch
+
+    sizes = _small_bucket_case(n * 31 + g)
+    bp = B.ar_bucket_plan_create(n, g, sizes, dtype, sched, 8 << 10)
+    try:
+        offs, arena = B.ar_bucket_layout(bp, len(sizes))
+        ranges = [B.ar_bucket_range(bp, b) for b in range(B.ar_bucket_count(bp))]
+        gen = "fp32" if dtype == "fp32" else "bf16"
+        host = workloads.bucketed_arenas(n, sizes, offs, arena, sigma=1.0, dtype=gen)
+        refs = [oracle.run([h[off:off + cnt].copy() for h in host], dtype, sched, group_size=g)
+                for off, cnt in ranges]
+        sv = np.float32 if dtype == "fp32" else np.int16
+        bv = np.uint32 if dtype == "fp32" else np.uint16
+        for mode in ("steps", "steps_unfused", "onepass"):
+            B.ar_bucket_set_exec(bp, mode)
+            for graph in (False, True):
+                B.ar_bucket_set_graph(bp, graph)
+                for cache in (None, 3000 * (4 if dtype == "fp32" else 2)):
+                    if cache is not None:
+                        B.ar_bucket_set_cache_bytes(bp, cache)
+                    print(f"case batched {sched} n={n} g={g} {dtype} {mode} graph={graph} cache={cache}",
+                          flush=True)
+                    bufs = [torch.from_numpy(h.view(sv)).to("cuda:0") for h in host]
+                    for rep in range(3 if graph else 1):
+                        if rep:
+                            for t, h in zip(bufs, host):
+                                t.copy_(torch.from_numpy(h.view(sv)))
+                            torch.cuda.synchronize()
+                        B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
+                        torch.cuda.synchronize()
+                        got = [t.cpu().numpy().view(bv) for t in bufs]
+                        for b, (off, cnt) in enumerate(ranges):
+                            for r in range(n):
+                                assert np.array_equal(got[r][off:off + cnt], refs[b][r].view(bv)), \
+                                    f"bucket {b} rank {r} replay {rep}"
+                B.ar_bucket_set_cache_bytes(bp, 256 << 20)
     finally:
         B.ar_bucket_plan_destroy(bp)
