@@ -449,10 +449,62 @@ __global__ __launch_bounds__(kOPB) void onepass_hier(KArgs args) {
 // For N = 2^L this is the balanced tree of Rabenseifner and recursive
 // doubling; otherwise it is the binomial tree's left-complete order.  Formed
 // batch by batch (8 ranks at a time); NMAX = N rounded up to a power of two.
-template <bool BF, bool EACH, int NMAX, int UNROLL>
+// The balanced tree over the ranks in index order, folded as a binary
+// counter: leaf r joins, from the nearest outward, the sums of the complete
+// aligned blocks that end just before it -- one per trailing one bit of r --
+// and the joined block waits in slot k (k = the number of those bits) for
+// its right sibling; after leaf NMAX - 1 slot log2(NMAX) holds the root.
+// Only log2(NMAX) partial sums are live at a time and every slot index is a
+// compile-time constant, so the slots stay in registers.
+//
+// For N below the power of two NMAX the leaves N .. NMAX-1 are -0, the
+// exact identity of IEEE addition (x + -0 = x for every x, signed zeros
+// included, and x is already a bf16 value where each add is rounded): a
+// block of padding sums to -0 and a block with a valid prefix sums to that
+// prefix's subtree, which gives exactly the binomial (left-complete) tree --
+// neighbours paired level by level, an unpaired last node carried up.
+template <bool EACH, int L, int UNROLL>
+__device__ __forceinline__ void tree_push(float4 (&slot)[L + 1][UNROLL], int r, float4 (&x)[UNROLL]) {
+#pragma unroll
+  for (int k = 0; k <= L; ++k) {
+    if ((r >> k) & 1) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) x[u] = fold4<EACH>(slot[k][u], x[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) slot[k][u] = x[u];
+      return;
+    }
+  }
+}
+
+template <bool EACH, int L>
+__device__ __forceinline__ void tree_push1(float (&slot)[L + 1], int r, float x) {
+#pragma unroll
+  for (int k = 0; k <= L; ++k) {
+    if ((r >> k) & 1) {
+      x = fold1(EACH, slot[k], x);
+    } else {
+      slot[k] = x;
+      return;
+    }
+  }
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Makes v's value materialise here (an empty asm that reads and writes it).
+__device__ __forceinline__ void pin(float4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// One-pass tree fold; NMAX (a power of two) >= args.nranks > NMAX / 2, and
+// PAD = (args.nranks < NMAX).  kB ranks' loads are in flight at a time;
+// padding leaves load nothing.
+template <bool BF, bool EACH, int NMAX, bool PAD, int UNROLL, int kB>
 __global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
-  constexpr int kB = NMAX < 8 ? NMAX : 8;
-  constexpr int kBatches = NMAX / kB;
+  constexpr int L = ilog2(NMAX);
+  constexpr int kBatch = NMAX < kB ? NMAX : kB;
   constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const int n = args.nranks;
   const BlockCoord bc = block_coord(args);
@@ -461,52 +513,54 @@ __global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
     const int64_t base = t * kTile;
     if (base >= op.lo && base + kTile <= op.hi) {
-      float4 res[kBatches][UNROLL];
+      float4 slot[L + 1][UNROLL];
 #pragma unroll
-      for (int bi = 0; bi < kBatches; ++bi) {
-        if (bi * kB >= n) continue;
-        float4 v[kB][UNROLL];
+      for (int bi = 0; bi < NMAX / kBatch; ++bi) {
+        float4 v[kBatch][UNROLL];
+        if (!PAD || (bi + 1) * kBatch <= NMAX / 2 || (bi + 1) * kBatch <= n) {
 #pragma unroll
-        for (int i = 0; i < kB; ++i)
-          if (bi * kB + i < n) load_units<BF, UNROLL>(args, bi * kB + i, base, v[i]);
+          for (int q = 0; q < kBatch; ++q) load_units<BF, UNROLL>(args, bi * kBatch + q, base, v[q]);
+        } else if (bi * kBatch < n) {
+          // the batch holding leaf n
 #pragma unroll
-        for (int w = kB, span = 1; w > 1; w /= 2, span *= 2)
+          for (int q = 0; q < kBatch; ++q) {
+            if (bi * kBatch + q < n) {
+              load_units<BF, UNROLL>(args, bi * kBatch + q, base, v[q]);
+            } else {
 #pragma unroll
-          for (int i = 0; i < w / 2; ++i)
-            if (bi * kB + (2 * i + 1) * span < n) {
-#pragma unroll
-              for (int u = 0; u < UNROLL; ++u) v[i][u] = fold4<EACH>(v[2 * i][u], v[2 * i + 1][u]);
-            } else if (i > 0) {
-#pragma unroll
-              for (int u = 0; u < UNROLL; ++u) v[i][u] = v[2 * i][u];
+              for (int u = 0; u < UNROLL; ++u) v[q][u] = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
             }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) res[bi][u] = v[0][u];
-      }
-#pragma unroll
-      for (int w = kBatches, span = kB; w > 1; w /= 2, span *= 2)
-#pragma unroll
-        for (int i = 0; i < w / 2; ++i)
-          if ((2 * i + 1) * span < n) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) res[i][u] = fold4<EACH>(res[2 * i][u], res[2 * i + 1][u]);
-          } else if (i > 0 && 2 * i * span < n) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) res[i][u] = res[2 * i][u];
           }
-      store_all<BF, UNROLL>(args, base, res[0]);
+        } else {  // all padding: nothing to load
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[q][u] = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) tree_push<EACH, L, UNROLL>(slot, bi * kBatch + q, v[q]);
+        // Finish this batch's adds before the next batch's loads: the live
+        // partial sums (one per set bit of the leaves done) are pinned here,
+        // and no load moves above this point.  Otherwise the compiler issues
+        // all NMAX loads first and every leaf stays live in registers.
+#pragma unroll
+        for (int j = 0; j <= L; ++j)
+          if ((((bi + 1) * kBatch) >> j) & 1)
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) pin(slot[j][u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      store_all<BF, UNROLL>(args, base, slot[L]);
     } else {
       for (int u = 0; u < UNROLL; ++u)
         for (int k = 0; k < 4; ++k) {
           const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
           if (e < op.lo || e >= op.hi) continue;
-          float level[NMAX];
-          for (int r = 0; r < n; ++r) level[r] = load1<BF>(static_cast<const char *>(args.rank[r]), e);
-          for (int w = NMAX, span = 1; w > 1; w /= 2, span *= 2)
-            for (int i = 0; i < w / 2; ++i)
-              if ((2 * i + 1) * span < n) level[i] = fold1(EACH, level[2 * i], level[2 * i + 1]);
-              else if (2 * i * span < n) level[i] = level[2 * i];
-          store_all1(args, BF, e, level[0]);
+          float slot[L + 1];
+#pragma unroll
+          for (int r = 0; r < NMAX; ++r)
+            tree_push1<EACH, L>(slot, r, r < n ? load1<BF>(static_cast<const char *>(args.rank[r]), e) : -0.0f);
+          store_all1(args, BF, e, slot[L]);
         }
     }
   }
@@ -590,6 +644,10 @@ constexpr int kUnrollCold = AR_COLD_UNROLL;
 // bf16 1 unit x 16 ranks
 constexpr int kOnePassUnrollF32 = AR_ONEPASS_UNROLL_F32, kFoldBatchF32 = AR_FOLD_BATCH_F32;
 constexpr int kOnePassUnrollBF16 = AR_ONEPASS_UNROLL_BF16, kFoldBatchBF16 = AR_FOLD_BATCH_BF16;
+// tree folds (measured): fp32 2 units x 8 ranks in flight, bf16 1 unit x 16
+// ranks (they also hold log2 N partial sums)
+constexpr int kTreeUnrollF32 = AR_TREE_UNROLL_F32, kTreeBatchF32 = AR_TREE_BATCH_F32;
+constexpr int kTreeUnrollBF16 = AR_TREE_UNROLL_BF16, kTreeBatchBF16 = AR_TREE_BATCH_BF16;
 constexpr bool kNtsRank = AR_NTS_RANK;
 constexpr bool kNtsScratch = AR_NTS_SCRATCH;
 
@@ -617,14 +675,23 @@ hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
 
 template <bool BF, bool EACH>
 hipError_t launch_tree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
-  constexpr int U = BF ? kOnePassUnrollBF16 : kOnePassUnrollF32;
-  if (n <= 2) AR_LAUNCH((onepass_tree<BF, EACH, 2, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 4) AR_LAUNCH((onepass_tree<BF, EACH, 4, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 8) AR_LAUNCH((onepass_tree<BF, EACH, 8, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 16) AR_LAUNCH((onepass_tree<BF, EACH, 16, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 32) AR_LAUNCH((onepass_tree<BF, EACH, 32, U>), grid, dim3(kOPB), 0, s, a);
-  else if (n <= 64) AR_LAUNCH((onepass_tree<BF, EACH, 64, U>), grid, dim3(kOPB), 0, s, a);
-  else return hipErrorInvalidValue;
+  constexpr int U = BF ? kTreeUnrollBF16 : kTreeUnrollF32;
+  constexpr int B = BF ? kTreeBatchBF16 : kTreeBatchF32;
+  switch (n) {
+    case 2: AR_LAUNCH((onepass_tree<BF, EACH, 2, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    case 4: AR_LAUNCH((onepass_tree<BF, EACH, 4, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    case 8: AR_LAUNCH((onepass_tree<BF, EACH, 8, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    case 16: AR_LAUNCH((onepass_tree<BF, EACH, 16, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    case 32: AR_LAUNCH((onepass_tree<BF, EACH, 32, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    case 64: AR_LAUNCH((onepass_tree<BF, EACH, 64, false, U, B>), grid, dim3(kOPB), 0, s, a); break;
+    default:
+      if (n == 3) AR_LAUNCH((onepass_tree<BF, EACH, 4, true, U, B>), grid, dim3(kOPB), 0, s, a);
+      else if (n < 8) AR_LAUNCH((onepass_tree<BF, EACH, 8, true, U, B>), grid, dim3(kOPB), 0, s, a);
+      else if (n < 16) AR_LAUNCH((onepass_tree<BF, EACH, 16, true, U, B>), grid, dim3(kOPB), 0, s, a);
+      else if (n < 32) AR_LAUNCH((onepass_tree<BF, EACH, 32, true, U, B>), grid, dim3(kOPB), 0, s, a);
+      else if (n < 64) AR_LAUNCH((onepass_tree<BF, EACH, 64, true, U, B>), grid, dim3(kOPB), 0, s, a);
+      else return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -665,6 +732,7 @@ int64_t tile_elems(int32_t kind, bool cold) {
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * u;
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
+    case kKindTree: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kTreeUnrollBF16 : kTreeUnrollF32);
     default: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }
 }

@@ -53,6 +53,18 @@
 #ifndef AR_ONEPASS_UNROLL_BF16
 #define AR_ONEPASS_UNROLL_BF16 1
 #endif
+#ifndef AR_TREE_UNROLL_F32
+#define AR_TREE_UNROLL_F32 2
+#endif
+#ifndef AR_TREE_UNROLL_BF16
+#define AR_TREE_UNROLL_BF16 1
+#endif
+#ifndef AR_TREE_BATCH_F32
+#define AR_TREE_BATCH_F32 8
+#endif
+#ifndef AR_TREE_BATCH_BF16
+#define AR_TREE_BATCH_BF16 16
+#endif
 
 // Kernel launch on stream S that records ar_dev::t_launch_events.
 #define AR_LAUNCH(K, G, B, SH, S, ...)                                                                       \

@@ -200,3 +200,7 @@ def test_full_double_tree_bf16_16x192MiB():
 
 def test_full_ring_bf16_each_step_16x192MiB():
     _full("bf16_each", "ring", 8, ["steps", "onepass"])
+
+
+def test_full_rabenseifner_bf16_16x192MiB():
+    _full("bf16", "rabenseifner", 1, ["steps", "onepass"])
