@@ -562,6 +562,16 @@ __device__ __forceinline__ void store_result(const QArgs &a, int64_t e0, const f
   for (int r = 0; r < a.nranks; ++r) store4<true>(a.grad[r], e0, a.count, v);
 }
 
+// The same for exactly N ranks: every argument index is a compile-time
+// constant, so a large unrolled kernel can keep its arguments in registers
+// (a runtime index makes the compiler copy the whole argument block to
+// private memory and read every pointer back from there).
+template <int N>
+__device__ __forceinline__ void store_result_n(const QArgs &a, int64_t e0, const float v[4]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) store4<true>(a.grad[r], e0, a.count, v);
+}
+
 // Block coordinate of this half-wave, or -1 when its block is outside the op.
 __device__ __forceinline__ int64_t op_block(const DevOp &op) {
   const int64_t b = (op.lo / kOPTileBlocks + blockIdx.x) * kOPTileBlocks + threadIdx.x / kHalf;
@@ -696,11 +706,13 @@ struct QDTree {
   static __device__ __forceinline__ void run(const QArgs &a, int64_t e0, float out[4]) {
     leaf(a, C, e0, out);
     if constexpr (B > 1) {
-      float lo[4], hi[4];
-      QDTree<C - B / 2, B / 2>::run(a, e0, lo);
-      QDTree<C + B / 2, B / 2>::run(a, e0, hi);
-      qadd(out, lo);
-      qadd(out, hi);
+      // own + lower child, then + higher child; the higher subtree is
+      // evaluated after the first add, so one child's values are live at a time
+      float sub[4];
+      QDTree<C - B / 2, B / 2>::run(a, e0, sub);
+      qadd(out, sub);
+      QDTree<C + B / 2, B / 2>::run(a, e0, sub);
+      qadd(out, sub);
     }
   }
 };
@@ -720,7 +732,7 @@ __global__ void __launch_bounds__(kOPBlock) q_onepass_dtree(QArgs a) {
     QDTree<N / 2 - 1, N / 2>::run(a, e0, sub);
   }
   qadd(root, sub);
-  store_result(a, e0, root);
+  store_result_n<N>(a, e0, root);
 }
 
 template <int NMAX>

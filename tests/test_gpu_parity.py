@@ -51,7 +51,7 @@ SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
         [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (8, 4), (16, 8), (16, 4), (12, 3), (8, 8), (8, 1))] + \
         [("rabenseifner", n, 1) for n in (2, 4, 8, 16, 64)] + \
         [("recursive_doubling", n, 1) for n in (2, 8, 64)] + \
-        [("tree", n, 1) for n in (2, 5, 8, 13, 64)] + \
+        [("tree", n, 1) for n in (2, 5, 8, 13, 24, 40, 64)] + \
         [("double_tree", n, 1) for n in (2, 8, 16, 64)]
 
 
