@@ -355,11 +355,21 @@ __device__ __forceinline__ float ring_fold1(const KArgs &args, bool bf, bool eac
     const char *p = static_cast<const char *>(args.rank[rank0 + r]);
     return bf ? load1<true>(p, e) : load1<false>(p, e);
   };
+  // ranks are loaded 8 at a time (independent loads in flight), then folded
+  // in order
   int r = first;
-  float acc = ld(r);
-  for (int t = 1; t < count; ++t) {
-    r = (r + 1 == wrap_n) ? 0 : r + 1;
-    acc = fold1(each, acc, ld(r));
+  float acc = 0.0f;
+  for (int t = 0; t < count; t += 8) {
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (t + q < count) {
+        x[q] = ld(r);
+        r = (r + 1 == wrap_n) ? 0 : r + 1;
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (t + q < count) acc = (t + q == 0) ? x[q] : fold1(each, acc, x[q]);
   }
   return acc;
 }
@@ -387,12 +397,23 @@ __global__ __launch_bounds__(kOPB) void onepass_ring(KArgs args) {
       ring_fold_units<BF, EACH, UNROLL, FB>(args, 0, n, op.aux, n, base, acc, true);
       store_all<BF, UNROLL>(args, base, acc);
     } else {
-      for (int u = 0; u < UNROLL; ++u)
+      // a partial tile: 4-element units inside the op take the vector fold,
+      // the units it cuts take the per-element one
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t ubase = base + static_cast<int64_t>(u) * kOPB * 4;
+        const int64_t e0 = ubase + static_cast<int64_t>(threadIdx.x) * 4;
+        if (e0 >= op.lo && e0 + 4 <= op.hi) {
+          float4 acc[1];
+          ring_fold_units<BF, EACH, 1, FB>(args, 0, n, op.aux, n, ubase, acc, true);
+          store_all<BF, 1>(args, ubase, acc);
+          continue;
+        }
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
+          const int64_t e = e0 + k;
           if (e < op.lo || e >= op.hi) continue;
           store_all1(args, BF, e, ring_fold1(args, BF, EACH, 0, n, op.aux, n, e));
         }
+      }
     }
   }
 }
@@ -427,9 +448,25 @@ __global__ __launch_bounds__(kOPB) void onepass_hier(KArgs args) {
       }
       store_all<BF, UNROLL>(args, base, acc);
     } else {
-      for (int u = 0; u < UNROLL; ++u)
+      // a partial tile: 4-element units inside the op take the vector fold,
+      // the units it cuts take the per-element one
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t ubase = base + static_cast<int64_t>(u) * kOPB * 4;
+        const int64_t e0 = ubase + static_cast<int64_t>(threadIdx.x) * 4;
+        if (e0 >= op.lo && e0 + 4 <= op.hi) {
+          float4 acc[1];
+          int g = j;
+          for (int m = 0; m < M; ++m) {
+            float4 part[1];
+            ring_fold_units<BF, EACH, 1, FB>(args, g * G, G, lstart, G, ubase, part, true);
+            acc[0] = (m == 0) ? part[0] : fold4<EACH>(acc[0], part[0]);
+            g = (g + 1 == M) ? 0 : g + 1;
+          }
+          store_all<BF, 1>(args, ubase, acc);
+          continue;
+        }
         for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4 + k;
+          const int64_t e = e0 + k;
           if (e < op.lo || e >= op.hi) continue;
           float acc = 0.f;
           int g = j;
@@ -440,6 +477,7 @@ __global__ __launch_bounds__(kOPB) void onepass_hier(KArgs args) {
           }
           store_all1(args, BF, e, acc);
         }
+      }
     }
   }
 }
