@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kBlock = AR_BLOCK;
 constexpr int kOPB = AR_ONEPASS_BLOCK;  // threads per workgroup of the one-pass kernels
-constexpr bool kOnePassNTS = AR_NTS_ONEPASS;
+constexpr int kCpolOnePassF32 = AR_CPOL_ONEPASS_F32, kCpolOnePassBF16 = AR_CPOL_ONEPASS_BF16;
 
 // Native vector types: 16-byte and 8-byte accesses compile to single
 // global_load/store_dwordx4 / dwordx2 instructions.
@@ -41,10 +41,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming accesses.  Every input byte is read once per kernel, so loads
-// carry the non-temporal hint (AR_NTL).  Stores carry it where measurement
-// says it pays: in the one-pass kernels, whose output nothing reads back,
-// but not into rank buffers or fp32 scratch written by a step, which the
-// next step reads from the cache (AR_NTS_*).  The hints never change results.
+// carry the non-temporal hint (AR_NTL).  Full-tile stores take a cache
+// policy (AR_CPOL_*; measured on MI355X): sc1 into rank buffers and fp32
+// scratch written by a step (the next step reads them back through the
+// device cache; sc1 was 5% faster than the default policy for a ring
+// reduce step and 2% for a copy step, non-temporal stores 7% slower), and
+// nt (fp32) or nt + sc1 (bf16) in the one-pass kernels, whose output
+// nothing reads back.  The hints never change results.
 template <typename T>
 __device__ __forceinline__ T ld(const char *p) {
 #if AR_NTL
@@ -53,10 +56,26 @@ __device__ __forceinline__ T ld(const char *p) {
   return *reinterpret_cast<const T *>(p);
 #endif
 }
-template <bool NT, typename T>
-__device__ __forceinline__ void st(char *p, T v) {
-  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<T *>(p));
-  else *reinterpret_cast<T *>(p) = v;
+// Stores v at byte offset `off` (per lane) from the wave-uniform address
+// `ubase` with cache policy CPOL.  Policies with sc1 go through a buffer
+// store, the one vector store that takes the policy bits from the program;
+// its resource is built from ubase (uniform, so it lives in scalar
+// registers) and covers 2^31 - 1 bytes, far more than a tile.
+constexpr int kBufferRsrcFlags = 0x00020000;  // resource word 3: 32-bit data format
+template <int CPOL, typename T>
+__device__ __forceinline__ void st_cp(char *ubase, uint32_t off, T v) {
+  if constexpr ((CPOL & 16) == 0) {
+    if constexpr (CPOL & 2) __builtin_nontemporal_store(v, reinterpret_cast<T *>(ubase + off));
+    else *reinterpret_cast<T *>(ubase + off) = v;
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ubase, 0, 0x7fffffff, kBufferRsrcFlags);
+    if constexpr (sizeof(T) == 16) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL);
+    } else {
+      static_assert(sizeof(T) == 8, "16- or 8-byte stores");
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, CPOL);
+    }
+  }
 }
 
 // Block -> (op, tile).  With AR_GRID_INTERLEAVE the ops of a launch are
@@ -135,20 +154,24 @@ __device__ __forceinline__ u32x2 pack4(float4 v) {
   return r;
 }
 
-template <bool NT>
-__device__ __forceinline__ void store_bits4(char *base, int64_t e, u32x2 bits) { st<NT, u32x2>(base + e * 2, bits); }
+// 4-element units at element tile0 + lane (tile0 wave-uniform, lane per
+// lane) of the buffer at base.
+template <int CPOL>
+__device__ __forceinline__ void store_bits4(char *base, int64_t tile0, uint32_t lane, u32x2 bits) {
+  st_cp<CPOL, u32x2>(base + tile0 * 2, lane * 2, bits);
+}
 
-template <bool BF, bool NT>
-__device__ __forceinline__ void store4(char *base, int64_t e, float4 v) {
+template <bool BF, int CPOL>
+__device__ __forceinline__ void store4(char *base, int64_t tile0, uint32_t lane, float4 v) {
   if constexpr (BF) {
-    store_bits4<NT>(base, e, pack4(v));
+    store_bits4<CPOL>(base, tile0, lane, pack4(v));
   } else {
     f32x4 w;
     w.x = v.x;
     w.y = v.y;
     w.z = v.z;
     w.w = v.w;
-    st<NT, f32x4>(base + e * 4, w);
+    st_cp<CPOL, f32x4>(base + tile0 * 4, lane * 4, w);
   }
 }
 
@@ -180,9 +203,10 @@ __device__ __forceinline__ float fold1(bool each, float a, float b) {
 // Chunk reduce: o[e] = a[e] + b[e] over the op's range, optionally also
 // written to o2 (the fused forwarding copy of the chunk just completed).
 // FLAGS: 1 a is bf16, 2 b is bf16, 4 outputs are bf16 (rounded once), 8 o2.
-// NTS: non-temporal stores (the host sets it when the outputs are scratch).
+// CP: cache policy of the full-tile stores (the host picks it for rank or
+// scratch outputs).
 // ---------------------------------------------------------------------------
-template <int FLAGS, int UNROLL, bool NTS>
+template <int FLAGS, int UNROLL, int CP>
 __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
@@ -205,15 +229,15 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * 4;
         const float4 s = add4(a[u], b[u]);
         if constexpr (kOBf) {
           const u32x2 bits = pack4(s);
-          store_bits4<NTS>(O, e, bits);
-          if constexpr (kO2) store_bits4<NTS>(O2, e, bits);
+          store_bits4<CP>(O, base, lane, bits);
+          if constexpr (kO2) store_bits4<CP>(O2, base, lane, bits);
         } else {
-          store4<false, NTS>(O, e, s);
-          if constexpr (kO2) store4<false, NTS>(O2, e, s);
+          store4<false, CP>(O, base, lane, s);
+          if constexpr (kO2) store4<false, CP>(O2, base, lane, s);
         }
       }
     } else {
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
 // ---------------------------------------------------------------------------
 // Chunk copy: o[e] = a[e], bit copy of ES-byte elements in 16-byte units.
 // ---------------------------------------------------------------------------
-template <int ES, int UNROLL, bool NTS>
+template <int ES, int UNROLL, int CP>
 __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
   constexpr int64_t kPerUnit = 16 / ES;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPerUnit * UNROLL;
@@ -253,8 +277,8 @@ __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit;
-        st<NTS, u32x4>(O + e * ES, v[u]);
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+        st_cp<CP, u32x4>(O + base * ES, lane * ES, v[u]);
       }
     } else {
       for (int u = 0; u < UNROLL; ++u)
@@ -291,14 +315,14 @@ __device__ __forceinline__ void store_all(const KArgs &args, int64_t base, const
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        store_bits4<kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4, bits[u]);
+        store_bits4<kCpolOnePassBF16>(p, base, (static_cast<uint32_t>(u) * kOPB + threadIdx.x) * 4, bits[u]);
     }
   } else {
     for (int r = 0; r < args.nranks; ++r) {
       char *p = static_cast<char *>(args.rank[r]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        store4<false, kOnePassNTS>(p, base + (static_cast<int64_t>(u) * kOPB + threadIdx.x) * 4, acc[u]);
+        store4<false, kCpolOnePassF32>(p, base, (static_cast<uint32_t>(u) * kOPB + threadIdx.x) * 4, acc[u]);
     }
   }
 }
@@ -686,15 +710,15 @@ constexpr int kOnePassUnrollBF16 = AR_ONEPASS_UNROLL_BF16, kFoldBatchBF16 = AR_F
 // ranks (they also hold log2 N partial sums)
 constexpr int kTreeUnrollF32 = AR_TREE_UNROLL_F32, kTreeBatchF32 = AR_TREE_BATCH_F32;
 constexpr int kTreeUnrollBF16 = AR_TREE_UNROLL_BF16, kTreeBatchBF16 = AR_TREE_BATCH_BF16;
-constexpr bool kNtsRank = AR_NTS_RANK;
-constexpr bool kNtsScratch = AR_NTS_SCRATCH;
+constexpr int kCpolRank = AR_CPOL_RANK;
+constexpr int kCpolScratch = AR_CPOL_SCRATCH;
 
 template <int FLAGS, int U>
 hipError_t launch_reduce_u(dim3 grid, const KArgs &a, hipStream_t s, bool out_scratch) {
-  if ((out_scratch && kNtsScratch) || (!out_scratch && kNtsRank))
-    AR_LAUNCH((chunk_reduce<FLAGS, U, true>), grid, dim3(kBlock), 0, s, a);
+  if (out_scratch)
+    AR_LAUNCH((chunk_reduce<FLAGS, U, kCpolScratch>), grid, dim3(kBlock), 0, s, a);
   else
-    AR_LAUNCH((chunk_reduce<FLAGS, U, false>), grid, dim3(kBlock), 0, s, a);
+    AR_LAUNCH((chunk_reduce<FLAGS, U, kCpolRank>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -706,8 +730,8 @@ hipError_t launch_reduce(dim3 grid, const KArgs &a, hipStream_t s, bool out_scra
 
 template <int ES>
 hipError_t launch_copy(dim3 grid, const KArgs &a, hipStream_t s, bool cold) {
-  if (cold) AR_LAUNCH((chunk_copy<ES, kUnrollCold, kNtsRank>), grid, dim3(kBlock), 0, s, a);
-  else AR_LAUNCH((chunk_copy<ES, kUnrollWarm, kNtsRank>), grid, dim3(kBlock), 0, s, a);
+  if (cold) AR_LAUNCH((chunk_copy<ES, kUnrollCold, kCpolRank>), grid, dim3(kBlock), 0, s, a);
+  else AR_LAUNCH((chunk_copy<ES, kUnrollWarm, kCpolRank>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -26,14 +26,20 @@
 #ifndef AR_NTL
 #define AR_NTL 1
 #endif
-#ifndef AR_NTS_RANK
-#define AR_NTS_RANK 0
+// Cache policy of the vector stores (bits of the store instruction: 2 nt,
+// 16 sc1): into rank buffers and fp32 scratch by the step kernels, and into
+// rank buffers by the fp32 and bf16 one-pass kernels.
+#ifndef AR_CPOL_RANK
+#define AR_CPOL_RANK 16
 #endif
-#ifndef AR_NTS_SCRATCH
-#define AR_NTS_SCRATCH 0
+#ifndef AR_CPOL_SCRATCH
+#define AR_CPOL_SCRATCH 16
 #endif
-#ifndef AR_NTS_ONEPASS
-#define AR_NTS_ONEPASS 1
+#ifndef AR_CPOL_ONEPASS_F32
+#define AR_CPOL_ONEPASS_F32 2
+#endif
+#ifndef AR_CPOL_ONEPASS_BF16
+#define AR_CPOL_ONEPASS_BF16 18
 #endif
 #ifndef AR_FOLD_BATCH_F32
 #define AR_FOLD_BATCH_F32 8
