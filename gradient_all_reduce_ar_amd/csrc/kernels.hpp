@@ -35,6 +35,25 @@
 #ifndef AR_CPOL_SCRATCH
 #define AR_CPOL_SCRATCH 16
 #endif
+// The same for the INT8 kernels: codes (read by the next round), decoded
+// values written into the rank buffers by the step kernels, residuals
+// written by the step kernels, and the one-pass kernels' residuals and
+// results.
+#ifndef AR_QCPOL_CODE
+#define AR_QCPOL_CODE 16
+#endif
+#ifndef AR_QCPOL_DEC
+#define AR_QCPOL_DEC 18
+#endif
+#ifndef AR_QCPOL_RES
+#define AR_QCPOL_RES 18
+#endif
+#ifndef AR_QCPOL_RES_ONEPASS
+#define AR_QCPOL_RES_ONEPASS 2
+#endif
+#ifndef AR_QCPOL_OUT
+#define AR_QCPOL_OUT 2
+#endif
 #ifndef AR_CPOL_ONEPASS_F32
 #define AR_CPOL_ONEPASS_F32 2
 #endif

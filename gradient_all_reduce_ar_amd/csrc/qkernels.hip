@@ -72,6 +72,10 @@ constexpr int kRLanes = 8;                           // lanes per block (reduce)
 constexpr int kRBlocksPerPass = AR_BLOCK / kRLanes;  // 32
 constexpr int kRTileBlocks = kRBlocksPerPass * kU;
 constexpr int kCopyTileBlocks = AR_BLOCK * 16 / kQB;  // one 16-byte chunk of codes per thread
+static_assert(8192 % (kTileBlocks * kQB) == 0 && 8192 % (kEncTileBlocks * kQB) == 0 &&
+                  8192 % (kHopTileBlocks * kQB) == 0 && 8192 % (kCopyDecTileBlocks * kQB) == 0 &&
+                  8192 % (kRTileBlocks * kQB) == 0 && 8192 % (kCopyTileBlocks * kQB) == 0,
+              "every INT8 tile lies inside one aligned store window");
 static_assert(kQB == kHalf * 4 && kQB == kRLanes * 16, "lane shapes cover one block");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -163,7 +167,38 @@ __device__ __forceinline__ void load4(const float *p, int64_t e0, int64_t count,
   }
 }
 
-template <bool NT>
+// Stores with a cache policy (bits of the store instruction: 2 nt, 16 sc1;
+// see the step kernels).  Policies with sc1 go through a buffer store, whose
+// resource must be wave-uniform: it is built from the start of the aligned
+// window of kStoreWindow elements that holds the lane's element.  Every
+// INT8 kernel's tile lies inside one such window (checked below), so all
+// lanes of a workgroup share it, and readfirstlane makes that visible to the
+// compiler.
+constexpr int64_t kStoreWindow = 8192;
+constexpr int kQRsrcFlags = 0x00020000;  // resource word 3: 32-bit data format
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// T (4 or 16 bytes) at element e0 of the element array p (element size ES).
+template <int CPOL, int ES, typename T>
+__device__ __forceinline__ void st_q(char *p, int64_t e0, T v) {
+  if constexpr ((CPOL & 16) == 0) {
+    if constexpr (CPOL & 2) __builtin_nontemporal_store(v, reinterpret_cast<T *>(p + e0 * ES));
+    else *reinterpret_cast<T *>(p + e0 * ES) = v;
+  } else {
+    const int64_t w0 = uniform64(e0 & ~(kStoreWindow - 1));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p + w0 * ES, 0, 0x7fffffff, kQRsrcFlags);
+    const int off = static_cast<int>((e0 - w0) * ES);
+    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL);
+    else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, CPOL);
+  }
+}
+
+template <int CPOL>
 __device__ __forceinline__ void store4(float *p, int64_t e0, int64_t count, const float x[4]) {
   if (e0 + 4 <= count) {
     f32x4 v;
@@ -171,14 +206,25 @@ __device__ __forceinline__ void store4(float *p, int64_t e0, int64_t count, cons
     v.y = x[1];
     v.z = x[2];
     v.w = x[3];
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p + e0));
-    else *reinterpret_cast<f32x4 *>(p + e0) = v;
+    st_q<CPOL, 4>(reinterpret_cast<char *>(p), e0, v);
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (e0 + k < count) p[e0 + k] = x[k];
   }
 }
+
+// 4 (uint32_t) or 16 (u32x4) codes at element e0 of a code slot.
+template <int CPOL, typename T>
+__device__ __forceinline__ void store_codes(int8_t *codes, int64_t e0, T w) {
+  st_q<CPOL, 1>(reinterpret_cast<char *>(codes), e0, w);
+}
+
+// (measured on MI355X, 16 ranks x 192 MiB: sc1 codes, nt + sc1 decoded
+// values and residuals took the fused ring steps from 2.55 to 2.36 ms;
+// the one-pass kernels are fastest with plain nt)
+constexpr int kQCpolCode = AR_QCPOL_CODE, kQCpolDec = AR_QCPOL_DEC, kQCpolRes = AR_QCPOL_RES,
+              kQCpolResOnePass = AR_QCPOL_RES_ONEPASS, kQCpolOut = AR_QCPOL_OUT;
 
 // codes[r] = Q(g_r + e_r); e_r = (g_r + e_r) - D(codes[r]).
 __global__ void __launch_bounds__(AR_BLOCK) q_encode(QArgs a) {
@@ -216,13 +262,13 @@ __global__ void __launch_bounds__(AR_BLOCK) q_encode(QArgs a) {
         max32(max(max(abs_bits(x[u][0]), abs_bits(x[u][1])), max(abs_bits(x[u][2]), abs_bits(x[u][3])))));
     float k[4];
     quantize<4>(x[u], sc, k);
-    *reinterpret_cast<uint32_t *>(codes + e0) = pack4(k);
+    store_codes<kQCpolCode>(codes, e0, pack4(k));
     if (lane == 0) scl[b] = sc.s;
     if (a.has_err) {
       float res[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) res[i] = x[u][i] - k[i] * sc.s;
-      store4<true>(e, e0, a.count, res);
+      store4<kQCpolRes>(e, e0, a.count, res);
     }
   }
 }
@@ -276,10 +322,10 @@ __global__ void __launch_bounds__(AR_BLOCK) q_reduce(QArgs a) {
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = pack4(k + 4 * j);
-    *reinterpret_cast<u32x4 *>(a.codes + op.o * a.code_stride + e0) = w;
+    store_codes<kQCpolCode>(a.codes + op.o * a.code_stride, e0, w);
     if (lane == 0) a.scales[op.o * a.scale_stride + b] = sc.s;
     if constexpr (O2) {
-      *reinterpret_cast<u32x4 *>(a.codes + op.o2 * a.code_stride + e0) = w;
+      store_codes<kQCpolCode>(a.codes + op.o2 * a.code_stride, e0, w);
       if (lane == 0) a.scales[op.o2 * a.scale_stride + b] = sc.s;
     }
   }
@@ -326,7 +372,7 @@ __device__ __forceinline__ void hop_value(const QArgs &a, int r, int64_t e0, con
       float res[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) res[i] = in.x[i] - v[i];
-      store4<true>(a.err[r], e0, a.count, res);
+      store4<kQCpolRes>(a.err[r], e0, a.count, res);
     }
   } else {
 #pragma unroll
@@ -369,10 +415,10 @@ __global__ void __launch_bounds__(AR_BLOCK) q_hop(QArgs a) {
     quantize<4>(x, sc, k);
     if constexpr (kCode) {
       const uint32_t w = pack4(k);
-      *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w;
+      store_codes<kQCpolCode>(a.codes + op.o * a.code_stride, e0, w);
       if (lane == 0) a.scales[op.o * a.scale_stride + b] = sc.s;
       if constexpr (kO2) {
-        *reinterpret_cast<uint32_t *>(a.codes + op.o2 * a.code_stride + e0) = w;
+        store_codes<kQCpolCode>(a.codes + op.o2 * a.code_stride, e0, w);
         if (lane == 0) a.scales[op.o2 * a.scale_stride + b] = sc.s;
       }
     }
@@ -380,8 +426,8 @@ __global__ void __launch_bounds__(AR_BLOCK) q_hop(QArgs a) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = k[i] * sc.s;
-      store4<false>(a.grad[op.o], e0, a.count, v);
-      if constexpr (kO2) store4<false>(a.grad[op.o2], e0, a.count, v);
+      store4<kQCpolDec>(a.grad[op.o], e0, a.count, v);
+      if constexpr (kO2) store4<kQCpolDec>(a.grad[op.o2], e0, a.count, v);
     }
   }
 }
@@ -412,13 +458,13 @@ __global__ void __launch_bounds__(AR_BLOCK) q_copy_dec(QArgs a) {
     const int64_t b = t * kCopyDecTileBlocks + u * kBlocksPerPass + sub;
     const int64_t e0 = b * kQB + lane * 4;
     if constexpr (CODE) {
-      *reinterpret_cast<uint32_t *>(a.codes + op.o * a.code_stride + e0) = w[u];
+      store_codes<kQCpolCode>(a.codes + op.o * a.code_stride, e0, w[u]);
       if (lane == 0) a.scales[op.o * a.scale_stride + b] = s[u];
     }
     float x[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = code(w[u], k) * s[u];
-    store4<false>(a.grad[op.o], e0, a.count, x);
+    store4<kQCpolDec>(a.grad[op.o], e0, a.count, x);
   }
 }
 
@@ -459,7 +505,7 @@ __global__ void __launch_bounds__(AR_BLOCK) q_copy(QArgs a) {
   if (b >= op.lo && b < op.hi) {
     const int64_t off = t * kCopyTileBlocks * kQB + threadIdx.x * 16;
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.codes + op.a * a.code_stride + off));
-    *reinterpret_cast<u32x4 *>(a.codes + op.o * a.code_stride + off) = v;
+    store_codes<kQCpolCode>(a.codes + op.o * a.code_stride, off, v);
   }
   const int64_t bs = t * kCopyTileBlocks + threadIdx.x;
   if (threadIdx.x < kCopyTileBlocks && bs >= op.lo && bs < op.hi)
@@ -493,7 +539,7 @@ __global__ void __launch_bounds__(AR_BLOCK) q_decode(QArgs a) {
     float x[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = code(w[u], k) * s[u];
-    store4<false>(a.grad[r], b * kQB + lane * 4, a.count, x);
+    store4<kQCpolDec>(a.grad[r], b * kQB + lane * 4, a.count, x);
   }
 }
 
@@ -510,6 +556,7 @@ __global__ void __launch_bounds__(AR_BLOCK) q_decode(QArgs a) {
 
 constexpr int kOPBlock = AR_Q_OP_BLOCK;       // threads per workgroup
 constexpr int kOPTileBlocks = kOPBlock / kHalf;  // one block per half-wave
+static_assert(kStoreWindow % (kOPTileBlocks * kQB) == 0, "every one-pass tile lies inside one store window");
 
 // v = D(Q(x)) in place (4 values per lane, 32 lanes per block).
 __device__ __forceinline__ void roundtrip4(float x[4]) {
@@ -540,7 +587,7 @@ __device__ __forceinline__ void leaf_finish(const QArgs &a, int r, int64_t e0, f
     float res[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) res[i] = x[i] - v[i];
-    store4<true>(a.err[r], e0, a.count, res);
+    store4<kQCpolResOnePass>(a.err[r], e0, a.count, res);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = v[i];
@@ -559,7 +606,7 @@ __device__ __forceinline__ void qadd(float acc[4], const float y[4]) {
 }
 
 __device__ __forceinline__ void store_result(const QArgs &a, int64_t e0, const float v[4]) {
-  for (int r = 0; r < a.nranks; ++r) store4<true>(a.grad[r], e0, a.count, v);
+  for (int r = 0; r < a.nranks; ++r) store4<kQCpolOut>(a.grad[r], e0, a.count, v);
 }
 
 // The same for exactly N ranks: every argument index is a compile-time
@@ -569,7 +616,7 @@ __device__ __forceinline__ void store_result(const QArgs &a, int64_t e0, const f
 template <int N>
 __device__ __forceinline__ void store_result_n(const QArgs &a, int64_t e0, const float v[4]) {
 #pragma unroll
-  for (int r = 0; r < N; ++r) store4<true>(a.grad[r], e0, a.count, v);
+  for (int r = 0; r < N; ++r) store4<kQCpolOut>(a.grad[r], e0, a.count, v);
 }
 
 // Block coordinate of this half-wave, or -1 when its block is outside the op.
