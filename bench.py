@@ -140,10 +140,19 @@ def launch_bytes(B, plan, i, nranks, elem, count):
 
 
 def kernels_sha256():
-    """SHA-256 over the device kernel sources (kernels.hip, qkernels.hip, kernels.hpp)."""
+    """SHA-256 over the code of the device kernel sources (kernels.hip,
+    qkernels.hip, kernels.hpp) with comments and blank space removed, so that
+    editing a comment does not invalidate counters taken on the same code."""
+    import re
+
     csrc = os.path.join(ROOT, "gradient_all_reduce_ar_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("kernels.hip", "qkernels.hip", "kernels.hpp"))
-    return hashlib.sha256(src).hexdigest()
+    code = []
+    for f in ("kernels.hip", "qkernels.hip", "kernels.hpp"):
+        text = open(os.path.join(csrc, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        code.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def traffic_record(kernel_name, workload, exec_mode):

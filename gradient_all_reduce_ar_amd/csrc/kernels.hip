@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kOPB) void onepass_dtree(KArgs args) {
 // for launches that write more into rank buffers than the 256 MB Infinity
 // Cache holds, so that the next step streams from DRAM; the 2-unit shape is
 // faster for smaller launches, whose inputs the previous step left in the
-// cache, and for launches writing fp32 scratch with non-temporal stores.
+// cache (checked again with the sc1 store policy).
 constexpr int kUnrollWarm = AR_REDUCE_UNROLL;
 constexpr int kUnrollCold = AR_COLD_UNROLL;
 // one-pass shapes per dtype (measured): fp32 2 units x 8 ranks in flight,
