@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     ar_bucket_range, ar_bucket_set_batching, ar_bucket_set_cache_bytes, ar_bucket_set_exec, ar_bucket_set_graph,
     ar_bucket_stats, ar_last_error, ar_last_status, ar_overlap_step_time, ar_plan_cost_alpha_beta,
     ar_plan_cost_alpha_beta_ex, ar_plan_create, ar_plan_destroy, ar_plan_launch_info, ar_plan_launch_ops,
-    ar_plan_launch_times, ar_plan_num_launches, ar_plan_prepare, ar_plan_set_cache_bytes, ar_plan_set_exec,
-    ar_plan_set_graph, ar_plan_set_profiling, ar_plan_set_profiling_period, ar_plan_stats, ar_plan_transfers,
-    ar_select_schedule,
+    ar_plan_launch_scratch, ar_plan_launch_times, ar_plan_num_launches, ar_plan_prepare,
+    ar_plan_set_cache_bytes, ar_plan_set_exec, ar_plan_set_graph, ar_plan_set_profiling,
+    ar_plan_set_profiling_period, ar_plan_stats, ar_plan_transfers, ar_select_schedule,
 )

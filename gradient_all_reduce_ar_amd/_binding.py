@@ -99,6 +99,7 @@ def _declare(L):
         "ar_plan_num_launches": ([P], i32),
         "ar_plan_launch_info": ([P, i32, pi32, pi32], ctypes.c_int),
         "ar_plan_launch_ops": ([P, i32, pi64, pi64, pi32, pi32, pi32, pi32, pi32], ctypes.c_int),
+        "ar_plan_launch_scratch": ([P, i32, pi64, pi64], ctypes.c_int),
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_profiling_period": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
@@ -287,6 +288,13 @@ def ar_plan_launch_ops(plan, i):
     _check(lib().ar_plan_launch_ops(plan, i, c(cols["lo"], ctypes.c_int64), c(cols["hi"], ctypes.c_int64),
                                     *[c(cols[k], ctypes.c_int32) for k in ("a", "b", "o", "o2", "aux")]))
     return {k: v[:nops] for k, v in cols.items()}
+
+
+def ar_plan_launch_scratch(plan, i):
+    """(shift, slot_stride) of launch i's fp32 scratch addressing."""
+    shift, stride = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ar_plan_launch_scratch(plan, i, ctypes.byref(shift), ctypes.byref(stride)))
+    return shift.value, stride.value
 
 
 def ar_plan_set_profiling(plan, max_calls):

@@ -254,6 +254,7 @@ namespace {
 // stop events when prof is set).
 ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
                     bool prof) {
+  float *const scratch_base = args.scratch;
   hipEvent_t *ev = nullptr;
   uint8_t *mark = nullptr;
   const int64_t call = plan->prof_logged;
@@ -284,6 +285,10 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
     } else {
       args.ops = plan->d_ops + plan->op_offset[i];
       args.nops = static_cast<int32_t>(L.ops.size());
+      // slot index e - shift: the kernels add e to this base (integer
+      // arithmetic; every address they form lies inside the scratch)
+      args.scratch = reinterpret_cast<float *>(reinterpret_cast<uintptr_t>(scratch_base) -
+                                               static_cast<uintptr_t>(L.scratch_shift) * sizeof(float));
       const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
       e = ar_dev::launch(L.kind, grid, args, s, out_scratch, plan->cold[i]);
     }
@@ -568,6 +573,14 @@ ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, in
     if (o2) o2[k] = ops[k].o2;
     if (aux) aux[k] = ops[k].aux;
   }
+  return AR_OK;
+}
+
+ar_status_t ar_plan_launch_scratch(const ar_plan_t *plan, int32_t i, int64_t *shift, int64_t *slot_stride) {
+  if (!plan || i < 0 || i >= static_cast<int32_t>(plan->p.launches.size()))
+    return fail(AR_ERR_INVALID_ARG, "bad plan or launch index");
+  if (shift) *shift = plan->p.launches[i].scratch_shift;
+  if (slot_stride) *slot_stride = plan->p.slot_stride;
   return AR_OK;
 }
 

@@ -916,14 +916,19 @@ std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, co
     fill += widest;
   }
   first.push_back(parts.size());
+  int64_t extent = 0;  // widest batch, in elements: the scratch slots hold one batch at a time
   for (size_t b = 0; b + 1 < first.size(); ++b) {
+    const int64_t lo = offsets[first[b]];
+    int64_t hi = lo;
+    for (size_t k = first[b]; k < first[b + 1]; ++k) hi = std::max(hi, offsets[k] + parts[k]->count);
+    extent = std::max(extent, hi - lo);
     std::vector<size_t> next(parts.size(), 0);  // next launch of each segment of the batch
     for (;;) {
       int32_t kind = -1;
       for (size_t k = first[b]; k < first[b + 1] && kind < 0; ++k)
         if (next[k] < parts[k]->launches.size()) kind = parts[k]->launches[next[k]].kind;
       if (kind < 0) break;
-      Launch L{kind, {}};
+      Launch L{kind, {}, lo};
       for (size_t k = first[b]; k < first[b + 1]; ++k) {
         if (next[k] >= parts[k]->launches.size() || parts[k]->launches[next[k]].kind != kind) continue;
         for (Op o : parts[k]->launches[next[k]].ops) {
@@ -936,7 +941,7 @@ std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, co
       m.launches.push_back(std::move(L));
     }
   }
-  m.slot_stride = (count + 63) / 64 * 64;
+  m.slot_stride = (extent + 63) / 64 * 64;
   compute_stats(m);
   out = std::move(m);
   return "";

@@ -79,6 +79,9 @@ struct Op {
 struct Launch {
   int32_t kind;
   std::vector<Op> ops;
+  // fp32 scratch: element e of a slot lives at index e - scratch_shift
+  // (a merged plan's batches reuse the same slot memory one after another)
+  int64_t scratch_shift = 0;
 };
 
 constexpr int64_t kDefaultCacheBytes = 256ll << 20;  // MI355X Infinity Cache (MALL)

@@ -286,6 +286,11 @@ int32_t ar_plan_num_launches(const ar_plan_t *plan);
 ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);
 ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, int64_t *hi,
                                int32_t *a, int32_t *b, int32_t *o, int32_t *o2, int32_t *aux);
+/* fp32 scratch addressing of launch i: element e of slot s is float
+ * s * slot_stride + e - shift of the scratch.  shift is 0 except in a
+ * batched bucket plan, whose batches reuse the slots one after another
+ * (shift = the batch's first arena element).  Host only. */
+ar_status_t ar_plan_launch_scratch(const ar_plan_t *plan, int32_t i, int64_t *shift, int64_t *slot_stride);
 
 /*
  * Graph replay (host call, no device work).  With enable != 0, ar_allreduce
@@ -341,9 +346,9 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
  * one-pass mode), and launch i of a batch runs launch i of each of its
  * buckets, so a batch costs the launches of one bucket.  Every bucket is
  * still its own all-reduce with its own partition and summation order: the
- * result is bit for bit that of the buckets run one by one.  The batched
- * plan owns an fp32 scratch covering the whole arena for bf16
- * (nslots x arena_count x 4 bytes).
+ * result is bit for bit that of the buckets run one by one.  For bf16 the
+ * batched plan owns an fp32 scratch that the batches reuse one after
+ * another (nslots x the widest batch's extent x 4 bytes).
  */
 typedef struct ar_bucket_plan ar_bucket_plan_t;
 

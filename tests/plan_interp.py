@@ -12,19 +12,27 @@ from gradient_all_reduce_ar_amd import _binding as B
 from tests.folds import to_bf16_bits, widen
 
 
-def _read(loc, lo, hi, bf_flag, bufs, scratch, fp32_mode):
+def _slot_range(lo, hi, shift, stride):
+    """Slot indices of elements [lo, hi): e - shift, which must lie in the slot."""
+    assert 0 <= lo - shift and hi - shift <= stride, (lo, hi, shift, stride)
+    return lo - shift, hi - shift
+
+
+def _read(loc, lo, hi, bf_flag, bufs, scratch, fp32_mode, shift=0, stride=None):
     if loc >= B.LOC_SCRATCH:
-        return scratch[loc - B.LOC_SCRATCH][lo:hi].copy()
+        a, b = _slot_range(lo, hi, shift, stride)
+        return scratch[loc - B.LOC_SCRATCH][a:b].copy()
     if fp32_mode:
         return bufs[loc][lo:hi].copy()
     assert bf_flag, "bf16 plan reads a rank buffer as fp32"
     return widen(bufs[loc][lo:hi])
 
 
-def _write(loc, lo, hi, vals, out_bf, bufs, scratch, fp32_mode):
+def _write(loc, lo, hi, vals, out_bf, bufs, scratch, fp32_mode, shift=0, stride=None):
     if loc >= B.LOC_SCRATCH:
         assert not out_bf
-        scratch[loc - B.LOC_SCRATCH][lo:hi] = vals
+        a, b = _slot_range(lo, hi, shift, stride)
+        scratch[loc - B.LOC_SCRATCH][a:b] = vals
     elif fp32_mode:
         bufs[loc][lo:hi] = vals
     else:
@@ -37,22 +45,25 @@ def run(plan, bufs, dtype, group_size):
     count = len(bufs[0])
     n = len(bufs)
     stats = B.ar_plan_stats(plan)
-    nslots = stats["scratch_bytes"] // (4 * max(1, ((count + 63) // 64) * 64)) if count else 0
-    scratch = [np.full(count, np.nan, np.float32) for _ in range(nslots)]
-    for i in range(B.ar_plan_num_launches(plan)):
+    nl = B.ar_plan_num_launches(plan)
+    stride = B.ar_plan_launch_scratch(plan, 0)[1] if nl else 0
+    nslots = stats["scratch_bytes"] // (4 * stride) if stride else 0
+    scratch = [np.full(stride, np.nan, np.float32) for _ in range(nslots)]
+    for i in range(nl):
         kind, _ = B.ar_plan_launch_info(plan, i)
         ops = B.ar_plan_launch_ops(plan, i)
+        shift, _ = B.ar_plan_launch_scratch(plan, i)
         fam = kind & 0xF00
         for k in range(len(ops["lo"])):
             lo, hi = int(ops["lo"][k]), int(ops["hi"][k])
             a, b, o, o2, aux = (int(ops[x][k]) for x in ("a", "b", "o", "o2", "aux"))
             if fam == B.KIND_REDUCE:
-                va = _read(a, lo, hi, kind & 1, bufs, scratch, fp32_mode)
-                vb = _read(b, lo, hi, kind & 2, bufs, scratch, fp32_mode)
+                va = _read(a, lo, hi, kind & 1, bufs, scratch, fp32_mode, shift, stride)
+                vb = _read(b, lo, hi, kind & 2, bufs, scratch, fp32_mode, shift, stride)
                 s = (va + vb).astype(np.float32)
-                _write(o, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode)
+                _write(o, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode, shift, stride)
                 if kind & 8:
-                    _write(o2, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode)
+                    _write(o2, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode, shift, stride)
             elif fam == B.KIND_COPY:
                 bufs[o][lo:hi] = bufs[a][lo:hi]
             else:

@@ -161,6 +161,25 @@ def test_batched_plan_c5_launches():
         B.ar_bucket_plan_destroy(bp)
 
 
+def test_batched_plan_reuses_scratch():
+    """The batches run one after another, so the fp32 partial-sum slots of a
+    batched bf16 plan span the widest batch, not the whole arena (C5,
+    Rabenseifner at 64 ranks: N/2 slots)."""
+    sizes = [int(s) for s in workloads.bucketed_tensor_sizes()]
+    bp = B.ar_bucket_plan_create(64, 1, sizes, "bf16", "rabenseifner", CAP)
+    try:
+        _, arena = B.ar_bucket_layout(bp, len(sizes))
+        m = B.ar_bucket_batched_plan(bp)
+        shifts = sorted({B.ar_plan_launch_scratch(m, i)[0] for i in range(B.ar_plan_num_launches(m))})
+        stride = B.ar_plan_launch_scratch(m, 0)[1]
+        ranges = [B.ar_bucket_range(bp, b) for b in range(B.ar_bucket_count(bp))]
+        assert shifts[0] == 0 and set(shifts) <= {off for off, _ in ranges}
+        assert max(c for _, c in ranges) <= stride < arena // 4
+        assert B.ar_plan_stats(m)["scratch_bytes"] == 32 * stride * 4
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
 def test_batched_plan_errors():
     bp = B.ar_bucket_plan_create(4, 1, [300, 500], "int8_ef", "ring", CAP)
     try:
