@@ -1,6 +1,6 @@
 """Benchmark: 16-rank, 192 MiB-per-rank fp32 ring all-reduce on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c2q|c3|c3e|c4|c5r16|c5g16|c5r64|c5g64|overlap]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|c2|c2q|c3|c3e|c4|c5r16|c5g16|c5r64|c5g64|overlap]
                 [--exec steps|steps_unfused|onepass]
 
 A step is one whole all-reduce (every launch of the schedule) over the N
@@ -37,6 +37,8 @@ METRIC = "effective busbw GB/s and % of HBM peak, 16-rank 192 MiB all-reduce"
 
 WORKLOADS = {
     # name: (description, schedule, nranks, group, dtype, count or None for bucketed)
+    "c1": ("ring all-reduce, 4 virtual ranks x 4096 fp32 (16 KiB each), U[-1,1) (a case that stays in cache)",
+           "ring", 4, 1, "fp32", 4096),
     "c2": ("ring all-reduce, 16 virtual ranks x 192 MiB fp32 (50,331,648 elements each), N(0,1e-3)",
            "ring", 16, 8, "fp32", 12288 * 4096),
     "c3": ("ring all-reduce, 16 virtual ranks x 192 MiB bf16 (100,663,296 elements each), N(0,1e-3), "
@@ -234,7 +236,10 @@ def main():
     else:
         plan = B.ar_plan_create(n, group, count, dtype, sched)
         B.ar_plan_set_exec(plan, args.exec)
-        host = workloads.normal_inputs(n, count, seed=0, dtype=gen_dtype)
+        if args.workload == "c1":
+            host = workloads.uniform_inputs(n, count, seed=0)
+        else:
+            host = workloads.normal_inputs(n, count, seed=0, dtype=gen_dtype)
         count_logical = count
         lplan = plan
     bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
