@@ -141,7 +141,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     // a dispatch holds at most 2^32 - 1 work-items per grid dimension (here
     // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
     const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
-    if (gx * threads > 0x7fffffff || L.ops.size() > 65535)
+    if (gx * threads > 0x7fffffff || static_cast<int64_t>(L.ops.size()) > ar::kMaxLaunchOps)
       return fail(AR_ERR_UNSUPPORTED, "op too large for one launch grid");
     pl->grid_x.push_back(static_cast<uint32_t>(gx));
   }

@@ -903,17 +903,25 @@ std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, co
     }
   }
   std::stable_sort(m.xfers.begin(), m.xfers.end(), [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
-  // batches of consecutive segments
+  // batches of consecutive segments: the widest rounds of a batch write at
+  // most cache_bytes together, and a merged launch carries at most
+  // kMaxLaunchOps ops (launch i of a batch holds launch i of each segment)
   std::vector<size_t> first{0};
-  int64_t fill = 0;
+  int64_t fill = 0, fill_ops = 0;
   for (size_t k = 0; k < parts.size(); ++k) {
-    int64_t widest = 0;
-    for (const Launch &L : parts[k]->launches) widest = std::max(widest, launch_write_bytes(*parts[k], L));
-    if (m.exec != kOnePass && fill > 0 && fill + widest > m.cache_bytes) {
+    int64_t widest = 0, most_ops = 0;
+    for (const Launch &L : parts[k]->launches) {
+      widest = std::max(widest, launch_write_bytes(*parts[k], L));
+      most_ops = std::max(most_ops, static_cast<int64_t>(L.ops.size()));
+    }
+    const bool bytes_full = m.exec != kOnePass && fill > 0 && fill + widest > m.cache_bytes;
+    if (k > first.back() && (bytes_full || fill_ops + most_ops > kMaxLaunchOps)) {
       first.push_back(k);
       fill = 0;
+      fill_ops = 0;
     }
     fill += widest;
+    fill_ops += most_ops;
   }
   first.push_back(parts.size());
   int64_t extent = 0;  // widest batch, in elements: the scratch slots hold one batch at a time
@@ -1000,7 +1008,7 @@ void assign_buckets(const std::vector<int64_t> &tensor_counts, int64_t cap_elems
   int64_t cursor = 0, fill = -1;  // fill < 0: no open bucket
   for (int t = n - 1; t >= 0; --t) {
     const int64_t c = tensor_counts[t];
-    if (fill >= 0 && fill > 0 && fill + c > cap_elems) {  // close the open bucket
+    if (fill > 0 && fill + c > cap_elems) {  // close the open bucket (a lone tensor may exceed the cap)
       bucket_count.push_back(fill);
       cursor = bucket_offset.back() + fill;
       fill = -1;

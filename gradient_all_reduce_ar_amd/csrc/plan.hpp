@@ -86,6 +86,7 @@ struct Launch {
 
 constexpr int64_t kDefaultCacheBytes = 256ll << 20;  // MI355X Infinity Cache (MALL)
 constexpr int32_t kMaxExecRanks = 64;    // ranks a plan can execute on the GPU
+constexpr int64_t kMaxLaunchOps = 65535;  // ops of one launch: workgroups along grid y
 constexpr int32_t kMaxPlanRanks = 1024;  // ranks a plan can describe (stats, cost)
 
 struct Plan {

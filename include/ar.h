@@ -342,9 +342,11 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
  * Batched execution (the default for fp32 and bf16 dtypes when no events
  * are given): the buckets' all-reduces share launches.  Buckets are taken in
  * order into batches whose widest round writes at most the plan's assumed
- * device cache (ar_plan_set_cache_bytes; every bucket in one batch in the
- * one-pass mode), and launch i of a batch runs launch i of each of its
- * buckets, so a batch costs the launches of one bucket.  Every bucket is
+ * device cache (ar_plan_set_cache_bytes; no such limit in the one-pass
+ * mode) and whose launches hold at most 65535 ops (the workgroups one
+ * launch grid holds along the ops: 4095 buckets at 16 ranks), and launch i
+ * of a batch runs launch i of each of its buckets, so a batch costs the
+ * launches of one bucket.  Every bucket is
  * still its own all-reduce with its own partition and summation order: the
  * result is bit for bit that of the buckets run one by one.  For bf16 the
  * batched plan owns an fp32 scratch that the batches reuse one after

@@ -180,6 +180,44 @@ def test_batched_plan_reuses_scratch():
         B.ar_bucket_plan_destroy(bp)
 
 
+@pytest.mark.parametrize("exec_mode", ["steps", "onepass"])
+def test_batched_plan_op_cap(exec_mode):
+    """Many tiny buckets: a merged launch holds launch i of every bucket of its
+    batch, so the batches also close before a launch would exceed 65535 ops
+    (the workgroups one launch grid holds along the ops).  The merged plan
+    still holds exactly the buckets' ops, shifted to their arena offsets."""
+    sizes = [64] * 5000  # 5000 buckets of 256 B, 16 ops per ring round each
+    bp = B.ar_bucket_plan_create(16, 1, sizes, "fp32", "ring", 256)
+    try:
+        B.ar_bucket_set_exec(bp, exec_mode)
+        m = B.ar_bucket_batched_plan(bp)
+        nl = B.ar_plan_num_launches(m)
+        nops = [B.ar_plan_launch_info(m, i)[1] for i in range(nl)]
+        assert max(nops) <= 65535
+        per_bucket = 29 if exec_mode == "steps" else 1
+        assert nl == per_bucket * 2  # 4095 buckets x 16 ops, then the other 905
+        assert sum(nops) == 5000 * 16 * per_bucket
+        got = set()
+        for i in range(nl):
+            ops = B.ar_plan_launch_ops(m, i)
+            got.update(zip(ops["lo"].tolist(), ops["hi"].tolist(), ops["a"].tolist(), ops["o"].tolist()))
+        want = set()
+        for b in range(B.ar_bucket_count(bp)):
+            off, cnt = B.ar_bucket_range(bp, b)
+            p = B.ar_plan_create(16, 1, cnt, "fp32", "ring")
+            try:
+                B.ar_plan_set_exec(p, exec_mode)
+                for i in range(B.ar_plan_num_launches(p)):
+                    ops = B.ar_plan_launch_ops(p, i)
+                    want.update(zip((ops["lo"] + off).tolist(), (ops["hi"] + off).tolist(), ops["a"].tolist(),
+                                    ops["o"].tolist()))
+            finally:
+                B.ar_plan_destroy(p)
+        assert got == want
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
 def test_batched_plan_errors():
     bp = B.ar_bucket_plan_create(4, 1, [300, 500], "int8_ef", "ring", CAP)
     try:
@@ -278,5 +316,33 @@ def test_batched_small_gpu(sched, n, g, dtype):
                                 assert np.array_equal(got[r][off:off + cnt], refs[b][r].view(bv)), \
                                     f"bucket {b} rank {r} replay {rep}"
                 B.ar_bucket_set_cache_bytes(bp, 256 << 20)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+@pytest.mark.gpu
+def test_many_tiny_buckets_gpu():
+    """5000 buckets of 64 fp32 elements at 16 ranks: the batched launches are
+    capped at 65535 ops, so the call runs (two batches) and every bucket
+    matches the oracle, in the step and the one-pass modes."""
+    import torch
+
+    sizes = [64] * 5000
+    bp = B.ar_bucket_plan_create(16, 1, sizes, "fp32", "ring", 256)
+    try:
+        offs, arena = B.ar_bucket_layout(bp, len(sizes))
+        ranges = [B.ar_bucket_range(bp, b) for b in range(B.ar_bucket_count(bp))]
+        host = workloads.bucketed_arenas(16, sizes, offs, arena, sigma=1.0, dtype="fp32")
+        refs = [oracle.run([h[off:off + cnt].copy() for h in host], "fp32", "ring") for off, cnt in ranges]
+        for mode in ("steps", "onepass"):
+            B.ar_bucket_set_exec(bp, mode)
+            print(f"case many tiny buckets fp32 ring n=16 {mode}", flush=True)
+            bufs = [torch.from_numpy(h).to("cuda:0") for h in host]
+            B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            got = [t.cpu().numpy().view(np.uint32) for t in bufs]
+            for b, (off, cnt) in enumerate(ranges):
+                for r in range(16):
+                    assert np.array_equal(got[r][off:off + cnt], refs[b][r].view(np.uint32)), f"bucket {b} rank {r}"
     finally:
         B.ar_bucket_plan_destroy(bp)
