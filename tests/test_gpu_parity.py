@@ -145,6 +145,66 @@ def test_plan_reuse_streams_and_profiling():
         B.ar_plan_destroy(plan)
 
 
+def test_plans_on_host_threads():
+    """Distinct plans driven from distinct host threads at once, each on its
+    own stream (two of them replaying HIP graphs, captured while the other
+    threads launch): every call of every thread matches the oracle.  Buffers
+    and outputs are allocated before the threads start."""
+    import threading
+
+    import torch
+
+    n, count, reps = 8, 200003, 4
+    cases = [("ring", "fp32", 1, False), ("hierarchical", "bf16", 4, True), ("rabenseifner", "fp32", 1, True),
+             ("tree", "bf16_each", 1, False)]
+    work = []
+    for k, (sched, dtype, g, graph) in enumerate(cases):
+        xs = workloads.normal_inputs(n, count, seed=50 + k, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
+        ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+        pristine = to_device(xs, dtype)
+        bufs = [t.clone() for t in pristine]
+        outs = [[torch.empty_like(t) for t in bufs] for _ in range(reps)]
+        work.append(dict(sched=sched, dtype=dtype, g=g, graph=graph, ref=ref, pristine=pristine, bufs=bufs,
+                         outs=outs, stream=torch.cuda.Stream(), plan=None, err=None))
+    torch.cuda.synchronize()
+
+    def body(w):
+        try:
+            w["plan"] = B.ar_plan_create(n, w["g"], count, w["dtype"], w["sched"])
+            B.ar_plan_set_graph(w["plan"], w["graph"])
+            s = w["stream"]
+            with torch.cuda.stream(s):
+                for rep in range(reps):
+                    for b, p in zip(w["bufs"], w["pristine"]):
+                        b.copy_(p)
+                    B.ar_allreduce(w["plan"], w["bufs"], s)
+                    for o, b in zip(w["outs"][rep], w["bufs"]):
+                        o.copy_(b)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            w["err"] = e
+
+    _say(f"case host threads: {len(cases)} plans, {reps} calls each")
+    threads = [threading.Thread(target=body, args=(w,)) for w in work]
+    try:
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+        for w in work:
+            assert w["err"] is None, f"{w['sched']} {w['dtype']}: {w['err']}"
+            for rep in range(reps):
+                got = to_host_bits(w["outs"][rep], w["dtype"])
+                for r in range(n):
+                    assert np.array_equal(got[r], w["ref"][r].view(bits_view(w["dtype"]))), \
+                        (w["sched"], w["dtype"], rep, r)
+    finally:
+        for w in work:
+            if w["plan"] is not None:
+                B.ar_plan_destroy(w["plan"])
+
+
 # ------------------------------------------------------------- full sizes
 
 E32 = workloads.GATE_PROJ_ELEMS
