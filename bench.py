@@ -11,14 +11,15 @@ per call; the kernels' work does not depend on the values.
 
 Prints ONE JSON line.  value = busbw = algbw * 2(N-1)/N with algbw = S / T
 (S = bytes per rank, GB = 1e9; the nccl-tests convention of the AI training
-network primer, ch. 4 section 4.8).  roofline: the kernel kind with the
-largest share of GPU time, its algorithmic bytes per launch over its mean
-launch duration (a start and a stop HIP event that the timed launches record
-as part of their dispatch, on the call's stream), against 8 TB/s.  Each call
-times about four of its launches, in rotation, so every launch position is
-timed over the run while the events barely perturb the calls;
-config.compare also times the same calls with no events at all (eager, and
-replayed as HIP graphs).
+network primer, ch. 4 section 4.8), from K calls with no profiling.
+roofline: from a second run of the same K calls (inputs restored first), the
+kernel kind with the largest share of GPU time, its algorithmic bytes per
+launch over its mean launch duration (a start and a stop HIP event that the
+launches record as part of their dispatch, on the call's stream), against
+8 TB/s.  Each call of that run times about four of its launches, in
+rotation, so every launch position is timed over the run while the events
+barely perturb the calls (config.compare.with_launch_events gives that run's
+time per call); config.compare also times the calls replayed as HIP graphs.
 cpu_baseline: the CPU oracle (plain single-threaded C) timed on the host on
 the same inputs.
 """
@@ -272,17 +273,10 @@ def main():
         run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
     else:
         run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
-    # time about four launches per call (every launch over `period` calls),
-    # so the timing events barely perturb the calls they time
-    period = max(1, B.ar_plan_num_launches(lplan) // 4)
-    B.ar_plan_set_profiling(lplan, max(args.steps, 1))
-    B.ar_plan_set_profiling_period(lplan, period)
-
+    # ---- the timed run: the calls as a user makes them (no profiling)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    B.ar_plan_launch_times(lplan)  # clear the warm-up entries
-
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -295,6 +289,24 @@ def main():
     wall_ms = (t_end - t_start) * 1e3 / max(args.steps, 1)
     ev_ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
     ms = wall_ms
+
+    # ---- the roofline run: the same calls again (inputs restored, untimed),
+    # about four launches per call timed by start/stop events that the
+    # launches record as part of their dispatch (every launch over `period`
+    # calls), so the events barely perturb the calls they time
+    period = max(1, B.ar_plan_num_launches(lplan) // 4)
+    B.ar_plan_set_profiling(lplan, max(args.steps, 1))
+    B.ar_plan_set_profiling_period(lplan, period)
+    reset_inputs()
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    B.ar_plan_launch_times(lplan)  # clear the warm-up entries
+    t_p = time.perf_counter()
+    for c in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    prof_ms = (time.perf_counter() - t_p) * 1e3 / max(args.steps, 1)
 
     S = count_logical * elem
     algbw = S / (ms * 1e-3) / 1e9
@@ -341,11 +353,15 @@ def main():
         means.append(sum(ts) / len(ts) if ts else None)
     sum_launch_ms = sum(means) if all(m is not None for m in means) else None
     B.ar_plan_set_profiling(lplan, 0)
+    extra = {}
+    prof_alg = count_logical * elem / (prof_ms * 1e-3) / 1e9
+    extra["with_launch_events"] = {"exec": args.exec, "ms_per_step": round(prof_ms, 4),
+                                   "busbw_GBps": round(prof_alg * 2 * (n - 1) / n, 1),
+                                   "algbw_GBps": round(prof_alg, 1)}
 
     # ---- buckets one by one, each with its own launches and a HIP event after
     # it (per-bucket times)
     per_bucket = None
-    extra = {}
     if bucketed:
         nb = B.ar_bucket_count(plan)
         B.ar_bucket_set_batching(plan, False)
@@ -399,10 +415,9 @@ def main():
                             "algbw_GBps": round(op_alg, 1),
                             "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
 
-    # ---- the same exec mode without the per-launch events (eager, then as one
-    # HIP graph per call): the events of the timed run cost a few us per launch
+    # ---- the same exec mode replayed as one HIP graph per call
     if not args.no_extra:
-        for name, graph in (("without_launch_events", False), ("graph", True)):
+        for name, graph in (("graph", True),):
             if bucketed:
                 B.ar_bucket_set_exec(plan, args.exec)
                 B.ar_bucket_set_graph(plan, graph)
@@ -483,7 +498,8 @@ def main():
             "workload": desc, "schedule": sched, "nranks": n, "group_size": group, "dtype": dtype,
             "count_per_rank": count_logical, "bytes_per_rank": S, "exec": args.exec,
             "executor": ("buckets batched: every bucket's all-reduce in shared launches, " if bucketed else "")
-            + f"eager launches, about four per call timed by HIP events (every launch over {period} calls)",
+            + f"eager launches; the roofline from a second run of the same calls, about four launches per "
+            f"call timed by HIP events (every launch over {period} calls)",
             "algbw_GBps": round(algbw, 1), "busbw_GBps": round(busbw, 1),
             "hbm_model_bytes": stats["hbm_bytes_model"], "hbm_model_GBps": round(model_gbps, 1),
             "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),
