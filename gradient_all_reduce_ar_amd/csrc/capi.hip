@@ -138,6 +138,10 @@ ar_status_t prepare(ar_plan_t *pl) {
       host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
       gx = std::max(gx, (o.hi + tile - 1) / tile - o.lo / tile);
     }
+    if (!quant) {  // blocks that walk several tiles
+      const int64_t tpb = ar_dev::tiles_per_block(L.kind, pl->p.nranks);
+      gx = (gx + tpb - 1) / tpb;
+    }
     // a dispatch holds at most 2^32 - 1 work-items per grid dimension (here
     // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
     const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);

@@ -78,6 +78,9 @@
 #ifndef AR_ONEPASS_UNROLL_BF16
 #define AR_ONEPASS_UNROLL_BF16 1
 #endif
+#ifndef AR_ONEPASS_MIN_BLOCK_BYTES  // bytes a one-pass block reads at least (0: one tile per block)
+#define AR_ONEPASS_MIN_BLOCK_BYTES 16384
+#endif
 #ifndef AR_TREE_UNROLL_F32
 #define AR_TREE_UNROLL_F32 2
 #endif
@@ -163,6 +166,12 @@ int64_t tile_elems(int32_t kind, bool cold);
 
 // Threads per workgroup of a kernel kind.
 int block_threads(int32_t kind);
+
+// Tiles each block of a launch walks (the kernels loop over an op's tiles
+// with the grid's stride): more than one for the one-pass ring and
+// hierarchical folds when a tile of all ranks is little data (bf16 at 2 or 4
+// ranks), so a block is not dispatched for a few KiB.
+int64_t tiles_per_block(int32_t kind, int32_t nranks);
 
 // Grid of a launch whose ops span at most `tiles` tiles each.
 dim3 grid_for(uint32_t tiles, uint32_t nops);
