@@ -240,7 +240,7 @@ int build_dtree(std::vector<Transfer> &out, int n, int64_t count) {
 // only when their partial ranges can never overlap while both are live:
 //   ring: one live partial per chunk (it travels round the ring) -> 1 slot;
 //   hierarchical: per group, partials of distinct slices           -> M slots;
-//   Rabenseifner: ranks 2m and 2m+1 keep disjoint halves from round 1 on
+//   Rabenseifner: ranks 2m and 2m+1 keep disjoint halves from the first halving round on
 //                 and later ranges nest inside those halves         -> N/2 slots;
 //   recursive doubling and the trees: one slot per rank              -> N slots.
 int slot_of(const Plan &p, int r) {
