@@ -48,6 +48,18 @@ MUTANTS = {
     "int8_dropped_own": ("x[i] = q_decode(pq[eoff + i], ps[boff]) + q_decode(q[m->dst][lo + i], sc[m->dst][b]);",
                          "x[i] = q_decode(pq[eoff + i], ps[boff]);"),
     "int8_scale_of_sender": ("sc[m->dst][b] = ps[boff];", "sc[m->dst][b] = sc[m->dst][b];"),
+    "rdouble_bit_order": ("push(L, k, i, i ^ (1 << k), 0, count, ARO_REDUCE, k == lg - 1)",
+                          "push(L, k, i, i ^ (1 << (lg - 1 - k)), 0, count, ARO_REDUCE, k == lg - 1)"),
+    "tree_reduce_parent": ("push(L, step, i, i - (1 << k), 0, count, ARO_REDUCE, k == lg - 1)",
+                           "push(L, step, i, i - 1, 0, count, ARO_REDUCE, k == lg - 1)"),
+    "tree_bcast_edge": ("if ((i & ((2 << k) - 1)) == 0 && i + (1 << k) < N)",
+                        "if ((i & ((2 << k) - 1)) == 0 && i + (1 << k) < N - 1)"),
+    "dtree_mirror_dst": ("int dst = t == 0 ? par : N - 1 - par;", "int dst = t == 0 ? par : par;"),
+    "dtree_half": ("int64_t half = part_lo(count, 2, 1);", "int64_t half = part_lo(count, 4, 1);"),
+    "dtree_child_order": ("for (int round = 0; round < lg; ++round)\n    for (int s = 0; s < N; ++s)\n"
+                          "      for (int t = 0; t < 2; ++t) {\n        /* in tree 2",
+                          "for (int round = 0; round < lg; ++round)\n    for (int s = N - 1; s >= 0; --s)\n"
+                          "      for (int t = 0; t < 2; ++t) {\n        /* in tree 2"),
 }
 
 
