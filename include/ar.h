@@ -169,11 +169,13 @@ ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
  * The device cache capacity (bytes) the plan's launch order and kernel
  * shapes assume; default 256 MiB, MI355X's Infinity Cache.  A step launch
  * that writes more than this into rank buffers takes the streaming kernel
- * shape; and the hierarchical schedule runs its two group phases group by
+ * shape; the hierarchical schedule runs its two group phases group by
  * group (all rounds of group 0, then group 1, ...) when one round of a phase
- * would write more than this, so that each round's output is still cached
- * when the next round reads it.  Results are bit-identical for any value.
- * Host only.
+ * would write more than this, and the other schedules cut the element range
+ * into the fewest pieces (the same offsets on every rank) whose rounds write
+ * at most this and run the whole schedule piece after piece, so that each
+ * round's output is still cached when the next round reads it.  Results are
+ * bit-identical for any value.  Host only.
  */
 ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes);
 
@@ -181,8 +183,11 @@ ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes);
  * Allocates the plan's device op tables and, for bf16, its fp32 scratch on
  * the current HIP device, and uploads the tables (synchronously).  Called
  * implicitly by the first ar_allreduce; call it explicitly before capturing
- * ar_allreduce into a HIP graph.  AR_ERR_OOM / AR_ERR_HIP on failure.  A plan
- * is bound to the device current at its first prepare.
+ * ar_allreduce into a HIP graph.  AR_ERR_OOM / AR_ERR_HIP on failure;
+ * AR_ERR_UNSUPPORTED for a plan of more than 64 ranks (planned for its
+ * statistics and cost model only) or a launch beyond one dispatch's limits
+ * (more than 65535 ops, or one op of more tiles than 2^31 - 1 work-items
+ * hold).  A plan is bound to the device current at its first prepare.
  */
 ar_status_t ar_plan_prepare(ar_plan_t *plan);
 
@@ -195,8 +200,9 @@ ar_status_t ar_plan_prepare(ar_plan_t *plan);
  * the result is visible after stream synchronisation (the initiating call of
  * a collective returns before completion -- Scaling ML systems ch. 06).
  * Calls that share a plan must not overlap in time (they share scratch).
- * AR_ERR_INVALID_ARG for NULL/misaligned pointers or a different device than
- * the plan's; AR_ERR_HIP if a launch fails.
+ * AR_ERR_INVALID_ARG for NULL/misaligned/overlapping pointers or a
+ * different device than the plan's; the errors of ar_plan_prepare on the
+ * first call; AR_ERR_HIP if a launch fails.
  */
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream);
 
