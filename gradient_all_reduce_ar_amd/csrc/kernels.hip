@@ -22,6 +22,8 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 #include "kernels.hpp"
 
@@ -561,6 +563,19 @@ __device__ __forceinline__ void pin(float4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1: a loop whose
+// index is a compile-time constant in every body, however large the body
+// (a long unrolled loop may otherwise stay a loop, and arrays indexed by its
+// counter then leave registers).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // One-pass tree fold; NMAX (a power of two) >= args.nranks > NMAX / 2, and
 // PAD = (args.nranks < NMAX).  kB ranks' loads are in flight at a time;
 // padding leaves load nothing.
@@ -577,8 +592,8 @@ __global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
     const int64_t base = t * kTile;
     if (base >= op.lo && base + kTile <= op.hi) {
       float4 slot[L + 1][UNROLL];
-#pragma unroll
-      for (int bi = 0; bi < NMAX / kBatch; ++bi) {
+      static_for<NMAX / kBatch>([&](auto bic) {
+        constexpr int bi = decltype(bic)::value;
         float4 v[kBatch][UNROLL];
         if (!PAD || (bi + 1) * kBatch <= NMAX / 2 || (bi + 1) * kBatch <= n) {
 #pragma unroll
@@ -612,7 +627,7 @@ __global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) pin(slot[j][u]);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
       store_all<BF, UNROLL>(args, base, slot[L]);
     } else {
       for (int u = 0; u < UNROLL; ++u)
