@@ -277,10 +277,11 @@ struct PartialMap {
 //  * hierarchical: the group phases (1: reduce-scatter, 3: all-gather) are
 //    independent across groups and run group by group (every round of group
 //    0, then of group 1, ...);
-//  * otherwise: the element range is cut into K pieces at the same offsets
-//    on every rank and the whole schedule runs on piece 0, then piece 1, ...
+//  * and, for every schedule, when a launch still writes more than the
+//    cache: the element range is cut into K pieces at the same offsets on
+//    every rank and the whole schedule runs on piece 0, then piece 1, ...
 //    (each transfer restricted to the piece), K the smallest count whose
-//    rounds fit in the cache.
+//    launches fit in the cache.
 struct LaunchKey {
   int32_t phase, group, step;
   bool operator<(const LaunchKey &o) const {
@@ -300,12 +301,29 @@ bool split_groups(const Plan &p) {
   return static_cast<int64_t>(p.nranks) * slice * round_write_bytes(p) > p.cache_bytes;
 }
 
+// The launch a transfer belongs to before any piece cut: its round, and for
+// a split hierarchical schedule also its phase and, in phases 1 and 3, its
+// group.
+LaunchKey group_key(const Plan &p, const Transfer &x, bool split) {
+  LaunchKey k{0, 0, x.step};
+  if (split) {
+    const int G = p.group_size, M = p.nranks / p.group_size;
+    const int p2 = G - 1, p3 = G - 1 + 2 * (M - 1);  // first rounds of phases 2 and 3
+    k.phase = x.step < p2 ? 0 : x.step < p3 ? 1 : 2;
+    if (k.phase != 1) k.group = x.src / G;
+  }
+  return k;
+}
+
+// Pieces: the fewest whose widest launch (after the group split) writes at
+// most the cache.
 int split_pieces(const Plan &p) {
-  if (p.sched == kHier || p.units == 0) return 1;
-  std::vector<int64_t> per_round(static_cast<size_t>(p.nsteps), 0);
-  for (const Transfer &x : p.xfers) per_round[x.step] += unit_elems(p, x.lo, x.hi);
+  if (p.units == 0) return 1;
+  const bool split = split_groups(p);
+  std::map<LaunchKey, int64_t> per_launch;
+  for (const Transfer &x : p.xfers) per_launch[group_key(p, x, split)] += unit_elems(p, x.lo, x.hi);
   int64_t worst = 0;
-  for (int64_t v : per_round) worst = std::max(worst, v);
+  for (const auto &e : per_launch) worst = std::max(worst, e.second);
   const int64_t bytes = worst * round_write_bytes(p);
   const int64_t k = p.cache_bytes > 0 ? (bytes + p.cache_bytes - 1) / p.cache_bytes : 64;
   return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
@@ -314,6 +332,7 @@ int split_pieces(const Plan &p) {
 std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) {
   std::vector<std::pair<LaunchKey, Transfer>> idx;
   const int pieces = split_pieces(p);
+  const bool split = split_groups(p);
   if (pieces > 1) {
     // piece boundaries on multiples of 64 units (whole tiles stay whole)
     std::vector<int64_t> cut;
@@ -323,20 +342,12 @@ std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) 
         Transfer y = x;
         y.lo = std::max(x.lo, cut[k]);
         y.hi = std::min(x.hi, cut[k + 1]);
-        if (y.hi > y.lo) idx.push_back({LaunchKey{k, 0, x.step}, y});
+        LaunchKey key = group_key(p, x, split);
+        key.phase += 3 * k;  // piece-major, then phase, group, round
+        if (y.hi > y.lo) idx.push_back({key, y});
       }
   } else {
-    const bool split = split_groups(p);
-    const int G = p.group_size, M = p.nranks / p.group_size;
-    const int p2 = G - 1, p3 = G - 1 + 2 * (M - 1);  // first rounds of phases 2 and 3
-    for (const Transfer &x : p.xfers) {
-      LaunchKey k{0, 0, x.step};
-      if (split) {
-        k.phase = x.step < p2 ? 0 : x.step < p3 ? 1 : 2;
-        if (k.phase != 1) k.group = x.src / G;
-      }
-      idx.push_back({k, x});
-    }
+    for (const Transfer &x : p.xfers) idx.push_back({group_key(p, x, split), x});
   }
   std::stable_sort(idx.begin(), idx.end(),
                    [](const std::pair<LaunchKey, Transfer> &a, const std::pair<LaunchKey, Transfer> &b) {

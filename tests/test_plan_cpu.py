@@ -285,24 +285,38 @@ HIER_SPLIT = [(16, 8), (16, 4), (8, 4), (6, 3), (9, 3), (12, 3), (64, 8)]
 @pytest.mark.parametrize("mode", ["steps", "steps_unfused"])
 def test_group_by_group_order_matches_oracle(n, g, dtype, mode):
     """With a cache smaller than one round's writes, the hierarchical group
-    phases run group by group; the results are the oracle's bit for bit."""
+    phases run group by group, and with a cache smaller than one group's
+    round the range is also cut into pieces; the results are the oracle's
+    bit for bit."""
+    m = n // g
+    fused = mode == "steps"
+    rounds = 2 * m * (g - 1) + 2 * (m - 1) - (1 if fused else 0)  # launches of one piece, group by group
     for count in (37, 1031):
         xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
         ref = oracle.run([x.copy() for x in xs], dtype, "hierarchical", group_size=g)
-        p = _plan(n, g, count, dtype, "hierarchical")
-        try:
-            B.ar_plan_set_exec(p, mode)
-            B.ar_plan_set_cache_bytes(p, 64)
-            got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
-            n_launch = B.ar_plan_num_launches(p)
-        finally:
-            B.ar_plan_destroy(p)
-        bv = np.uint32 if dtype == "fp32" else np.uint16
-        for r in range(n):
-            np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv), err_msg=f"n={n} g={g} {dtype} {mode} r={r}")
-        m = n // g
-        fused = mode == "steps"
-        assert n_launch == 2 * m * (g - 1) + 2 * (m - 1) - (1 if fused else 0)
+        for cache in (64, 1 << 30):
+            p = _plan(n, g, count, dtype, "hierarchical")
+            try:
+                B.ar_plan_set_exec(p, mode)
+                B.ar_plan_set_cache_bytes(p, cache)
+                got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+                n_launch = B.ar_plan_num_launches(p)
+                one_group = 0  # launches whose receivers all lie in one group (phases 1 and 3)
+                for i in range(n_launch):
+                    ops = B.ar_plan_launch_ops(p, i)
+                    ranks = {int(r) for key in ("a", "b", "o", "o2") for r in ops[key] if 0 <= r < B.LOC_SCRATCH}
+                    one_group += len({r // g for r in ranks}) == 1
+            finally:
+                B.ar_plan_destroy(p)
+            bv = np.uint32 if dtype == "fp32" else np.uint16
+            for r in range(n):
+                np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv),
+                                              err_msg=f"n={n} g={g} {dtype} {mode} cache={cache} r={r}")
+            if cache == 64 and m > 1:
+                # every group's phase-1 and phase-3 rounds in launches of their own, in every piece
+                assert n_launch >= rounds and n_launch % rounds == 0 and one_group >= 2 * m * (g - 1)
+            if cache == 1 << 30:
+                assert n_launch == 2 * (g - 1) + 2 * (m - 1) - (1 if fused else 0)
 
 
 def test_group_by_group_order_shape():
