@@ -66,6 +66,9 @@
 #ifndef AR_FOLD_BATCH_BF16
 #define AR_FOLD_BATCH_BF16 16
 #endif
+#ifndef AR_FOLD_BATCH_HIER_BF16
+#define AR_FOLD_BATCH_HIER_BF16 8
+#endif
 #ifndef AR_REDUCE_UNROLL
 #define AR_REDUCE_UNROLL 2
 #endif
