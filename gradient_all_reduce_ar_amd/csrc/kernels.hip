@@ -244,14 +244,33 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
         }
       }
     } else {
-      for (int u = 0; u < UNROLL; ++u)
-        for (int k = 0; k < 4; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4 + k;
-          if (e < op.lo || e >= op.hi) continue;
-          const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
-          store1<kOBf>(O, e, s);
-          if constexpr (kO2) store1<kOBf>(O2, e, s);
+      // a tile cut by the op's range: the 4-element units inside the op take
+      // the vector path, the units it cuts the per-element one
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * 4;
+        const int64_t e0 = base + lane;
+        if (e0 >= op.lo && e0 + 4 <= op.hi) {
+          const float4 s = add4(load4<kABf>(A, e0), load4<kBBf>(B, e0));
+          if constexpr (kOBf) {
+            const u32x2 bits = pack4(s);
+            store_bits4<CP>(O, base, lane, bits);
+            if constexpr (kO2) store_bits4<CP>(O2, base, lane, bits);
+          } else {
+            store4<false, CP>(O, base, lane, s);
+            if constexpr (kO2) store4<false, CP>(O2, base, lane, s);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int64_t e = e0 + k;
+            if (e < op.lo || e >= op.hi) continue;
+            const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
+            store1<kOBf>(O, e, s);
+            if constexpr (kO2) store1<kOBf>(O2, e, s);
+          }
         }
+      }
     }
   }
 }
@@ -284,12 +303,23 @@ __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
         st_cp<CP, u32x4>(O + base * ES, lane * ES, v[u]);
       }
     } else {
-      for (int u = 0; u < UNROLL; ++u)
-        for (int k = 0; k < kPerUnit; ++k) {
-          const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kPerUnit + k;
-          if (e < op.lo || e >= op.hi) continue;
-          *reinterpret_cast<Elem *>(O + e * ES) = *reinterpret_cast<const Elem *>(A + e * ES);
+      // a tile cut by the op's range: whole 16-byte units inside the op are
+      // copied as units, the units it cuts element by element
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * kPerUnit;
+        const int64_t e0 = base + lane;
+        if (e0 >= op.lo && e0 + kPerUnit <= op.hi) {
+          st_cp<CP, u32x4>(O + base * ES, lane * ES, ld<u32x4>(A + e0 * ES));
+        } else {
+#pragma unroll
+          for (int k = 0; k < kPerUnit; ++k) {
+            const int64_t e = e0 + k;
+            if (e < op.lo || e >= op.hi) continue;
+            *reinterpret_cast<Elem *>(O + e * ES) = *reinterpret_cast<const Elem *>(A + e * ES);
+          }
         }
+      }
     }
   }
 }

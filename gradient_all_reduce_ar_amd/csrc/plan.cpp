@@ -14,6 +14,13 @@
 
 namespace ar {
 
+#ifndef AR_SLOT_PAD
+#define AR_SLOT_PAD 0
+#endif
+// Elements per fp32 scratch slot: the slot's extent rounded up to 64 (each
+// slot starts 256-byte aligned), plus AR_SLOT_PAD.
+int64_t slot_stride_for(int64_t elems) { return (elems + 63) / 64 * 64 + AR_SLOT_PAD; }
+
 int64_t elem_bytes(Dtype d) { return d == kF32 ? 4 : d == kI8EF ? 1 : 2; }
 
 int64_t buffer_elem_bytes(Dtype d) { return (d == kF32 || d == kI8EF) ? 4 : 2; }
@@ -778,7 +785,7 @@ std::string lower(Plan &p, Exec exec) {
   else if (p.dtype == kI8EF) err = lower_quantized(p, exec == kSteps);
   else err = lower_steps(p, exec == kSteps);
   if (!err.empty()) return err;
-  p.slot_stride = (p.count + 63) / 64 * 64;
+  p.slot_stride = slot_stride_for(p.count);
   compute_stats(p);
   return check_hazards(p);
 }
@@ -960,7 +967,7 @@ std::string merge_segments(Plan &out, const std::vector<const Plan *> &parts, co
       m.launches.push_back(std::move(L));
     }
   }
-  m.slot_stride = (extent + 63) / 64 * 64;
+  m.slot_stride = slot_stride_for(extent);
   compute_stats(m);
   out = std::move(m);
   return "";
