@@ -301,6 +301,12 @@ struct LaunchKey {
 // kBF16), bf16, or INT8 codes.
 int64_t round_write_bytes(const Plan &p) { return p.dtype == kBF16Each ? 2 : p.dtype == kI8EF ? 1 : 4; }
 
+// The same for one transfer: kBF16 reduces store fp32 partials, its copies
+// bf16 values.
+int64_t transfer_write_bytes(const Plan &p, const Transfer &x) {
+  return p.dtype == kBF16 && x.kind != kReduce ? 2 : round_write_bytes(p);
+}
+
 bool split_groups(const Plan &p) {
   const int G = p.group_size, M = p.nranks / p.group_size;
   if (p.sched != kHier || G < 2 || M < 2) return false;
@@ -336,11 +342,72 @@ int split_pieces(const Plan &p) {
   return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
 }
 
+// Pieces a round needs so that what it writes fits the cache.
+int round_pieces(const Plan &p, int64_t bytes) {
+  const int64_t k = p.cache_bytes > 0 ? (bytes + p.cache_bytes - 1) / p.cache_bytes : 64;
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
+}
+
+// Rounds of a non-hierarchical schedule in blocks that run piece by piece.
+// A round whose output does not fit the cache shares its block with the next
+// round, which reads that output, and the last reduce round with the copy
+// round fused into it; a block takes the largest piece count its rounds'
+// outputs need (the last round's output is read by no later round and needs
+// none).  A schedule whose rounds shrink and grow, like Rabenseifner's, so
+// splits only its wide rounds; the ring, whose rounds are all alike, runs
+// piece by piece throughout or not at all.  Returns, per round, its block's
+// piece count and first phase.
+void round_blocks(const Plan &p, std::vector<int> &block_k, std::vector<int> &block_phase) {
+  const int ns = p.nsteps;
+  std::vector<int64_t> per_round(static_cast<size_t>(ns), 0);  // bytes each round writes
+  std::vector<bool> reduces(static_cast<size_t>(ns), false);
+  for (const Transfer &x : p.xfers) {
+    per_round[x.step] += unit_elems(p, x.lo, x.hi) * transfer_write_bytes(p, x);
+    if (x.kind == kReduce) reduces[x.step] = true;
+  }
+  std::vector<int> own(static_cast<size_t>(ns), 1);
+  std::vector<bool> link(static_cast<size_t>(ns), false);  // round r shares its block with round r + 1
+  for (int r = 0; r + 1 < ns; ++r) {
+    own[r] = round_pieces(p, per_round[r]);
+    link[r] = own[r] > 1 || (reduces[r] && !reduces[r + 1]);
+  }
+  block_k.assign(static_cast<size_t>(ns), 1);
+  block_phase.assign(static_cast<size_t>(ns), 0);
+  int phase = 0;
+  for (int r = 0; r < ns;) {
+    int r1 = r, k = own[r];
+    while (link[r1]) k = std::max(k, own[++r1]);
+    for (int q = r; q <= r1; ++q) {
+      block_k[q] = k;
+      block_phase[q] = phase;
+    }
+    phase += k;
+    r = r1 + 1;
+  }
+}
+
 std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) {
   std::vector<std::pair<LaunchKey, Transfer>> idx;
-  const int pieces = split_pieces(p);
   const bool split = split_groups(p);
-  if (pieces > 1) {
+  const int pieces = p.sched == kHier ? split_pieces(p) : 1;
+  if (p.sched != kHier && p.units > 0) {
+    std::vector<int> block_k, block_phase;
+    round_blocks(p, block_k, block_phase);
+    for (const Transfer &x : p.xfers) {
+      const int k = block_k[x.step];
+      if (k == 1) {
+        idx.push_back({LaunchKey{block_phase[x.step], 0, x.step}, x});
+        continue;
+      }
+      // piece boundaries on multiples of 64 units (whole tiles stay whole)
+      for (int q = 0; q < k; ++q) {
+        Transfer y = x;
+        y.lo = std::max(x.lo, (p.units * q / k) / 64 * 64);
+        y.hi = std::min(x.hi, q + 1 == k ? p.units : (p.units * (q + 1) / k) / 64 * 64);
+        if (y.hi > y.lo) idx.push_back({LaunchKey{block_phase[x.step] + q, 0, x.step}, y});
+      }
+    }
+  } else if (pieces > 1) {
     // piece boundaries on multiples of 64 units (whole tiles stay whole)
     std::vector<int64_t> cut;
     for (int k = 0; k <= pieces; ++k) cut.push_back(k == pieces ? p.units : (p.units * k / pieces) / 64 * 64);

@@ -362,20 +362,44 @@ def test_piece_by_piece_order_matches_oracle(sched, n, g, dtype):
 
 
 def test_piece_counts():
-    """C3 (bf16 ring, fp32 partials: 403 MB written per round) runs in two
-    pieces; C2 (fp32 ring, 201 MB per round) in one."""
+    """C3 (bf16 ring): every reduce-scatter round writes 403 MB of fp32
+    partials, more than the 256 MiB cache, so the reduce-scatter (with the
+    fused first all-gather round) runs on two halves of the range, one after
+    the other; the all-gather rounds copy 201 MB of bf16 each and run whole.
+    C2 (fp32 ring, 201 MB per round) runs in one piece."""
     p3 = _plan(16, 8, 2 * 12288 * 4096, "bf16", "ring")
     p2 = _plan(16, 8, 12288 * 4096, "fp32", "ring")
     try:
         assert B.ar_plan_num_launches(p2) == 29
-        assert B.ar_plan_num_launches(p3) == 2 * 29
-        lo = [int(B.ar_plan_launch_ops(p3, i)["lo"].min()) for i in range(58)]
-        hi = [int(B.ar_plan_launch_ops(p3, i)["hi"].max()) for i in range(58)]
+        n3 = B.ar_plan_num_launches(p3)
+        assert n3 == 2 * 15 + 14
+        lo = [int(B.ar_plan_launch_ops(p3, i)["lo"].min()) for i in range(n3)]
+        hi = [int(B.ar_plan_launch_ops(p3, i)["hi"].max()) for i in range(n3)]
+        kinds = [B.ar_plan_launch_info(p3, i)[0] for i in range(n3)]
         half = (2 * 12288 * 4096 // 2) // 64 * 64
-        assert max(hi[:29]) <= half and min(lo[29:]) >= half
+        assert max(hi[:15]) <= half and min(lo[15:30]) >= half
+        assert kinds[14] == kinds[29] and kinds[14] & 8  # the fused reduce + copy ends each half
+        assert all(k & 0xF00 == B.KIND_COPY for k in kinds[30:])
+        assert all(lo[i] == 0 and hi[i] == 2 * 12288 * 4096 for i in range(30, n3))
     finally:
         B.ar_plan_destroy(p3)
         B.ar_plan_destroy(p2)
+
+
+def test_piece_blocks_follow_round_sizes():
+    """Rabenseifner's rounds halve and then double: at 16 x 192 MiB fp32 the
+    first halving round writes 1.6 GB, so the halving rounds and the fused
+    first doubling round run in 6 pieces (4 launches each), then the doubling
+    rounds whose outputs exceed the cache (0.4, 0.8 GB) in 3 pieces, each
+    with the round that reads its output; the bytes do not change."""
+    p = _plan(16, 1, 12288 * 4096, "fp32", "rabenseifner")
+    try:
+        assert B.ar_plan_num_launches(p) == 6 * 4 + 3 * 3
+        assert B.ar_plan_stats(p)["hbm_bytes_model"] == (5 * 16 - 6) * 4 * 12288 * 4096
+        B.ar_plan_set_cache_bytes(p, 1 << 40)
+        assert B.ar_plan_num_launches(p) == 7
+    finally:
+        B.ar_plan_destroy(p)
 
 
 def test_profiling_period_is_checked_on_the_host():
