@@ -284,11 +284,12 @@ struct PartialMap {
 //  * hierarchical: the group phases (1: reduce-scatter, 3: all-gather) are
 //    independent across groups and run group by group (every round of group
 //    0, then of group 1, ...);
-//  * and, for every schedule, when a launch still writes more than the
-//    cache: the element range is cut into K pieces at the same offsets on
-//    every rank and the whole schedule runs on piece 0, then piece 1, ...
-//    (each transfer restricted to the piece), K the smallest count whose
-//    launches fit in the cache.
+//  * and, when a launch still writes more than the cache, the element range
+//    is cut into K pieces at the same offsets on every rank and the rounds
+//    concerned run on piece 0, then piece 1, ... (each transfer restricted
+//    to the piece): for the hierarchical schedule all its rounds, K the
+//    smallest count whose launches fit; for the others each block of rounds
+//    that must stay together (round_blocks), the rest running whole.
 struct LaunchKey {
   int32_t phase, group, step;
   bool operator<(const LaunchKey &o) const {
