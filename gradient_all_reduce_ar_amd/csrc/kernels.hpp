@@ -72,6 +72,12 @@
 #ifndef AR_REDUCE_UNROLL
 #define AR_REDUCE_UNROLL 2
 #endif
+#ifndef AR_REDUCE_UNROLL_BF16
+#define AR_REDUCE_UNROLL_BF16 4
+#endif
+#ifndef AR_COLD_UNROLL_BF16
+#define AR_COLD_UNROLL_BF16 2
+#endif
 #ifndef AR_COLD_UNROLL
 #define AR_COLD_UNROLL 1
 #endif
