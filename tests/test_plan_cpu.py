@@ -341,24 +341,30 @@ def test_group_by_group_order_shape():
 @pytest.mark.parametrize("sched,n,g", [s for s in SCHEDS if s[0] != "hierarchical"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
 def test_piece_by_piece_order_matches_oracle(sched, n, g, dtype):
-    """With a cache smaller than one round's writes, the schedule runs on
-    element pieces one after another; the results are the oracle's bit for
-    bit (including pieces that cut through chunks)."""
+    """With a cache smaller than some rounds' writes, those rounds run on
+    element pieces one after another (the others whole); the results are the
+    oracle's bit for bit (including pieces that cut through chunks).  The
+    cache sizes span every round split, some split, none split."""
     for count in (37, 5000):
         xs = workloads.normal_inputs(n, count, seed=count + n, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
         ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
         for mode in ("steps", "steps_unfused"):
-            p = _plan(n, g, count, dtype, sched)
-            try:
-                B.ar_plan_set_exec(p, mode)
-                B.ar_plan_set_cache_bytes(p, 2048)
-                got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
-            finally:
-                B.ar_plan_destroy(p)
-            bv = np.uint32 if dtype == "fp32" else np.uint16
-            for r in range(n):
-                np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv),
-                                              err_msg=f"{sched} n={n} {dtype} {mode} count={count} r={r}")
+            launches = []
+            for cache in (2048, 6 * count, 24 * count, 1 << 30):
+                p = _plan(n, g, count, dtype, sched)
+                try:
+                    B.ar_plan_set_exec(p, mode)
+                    B.ar_plan_set_cache_bytes(p, cache)
+                    got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+                    launches.append(B.ar_plan_num_launches(p))
+                finally:
+                    B.ar_plan_destroy(p)
+                bv = np.uint32 if dtype == "fp32" else np.uint16
+                for r in range(n):
+                    np.testing.assert_array_equal(got[r].view(bv), ref[r].view(bv),
+                                                  err_msg=f"{sched} n={n} {dtype} {mode} count={count} cache={cache} r={r}")
+            # a larger cache never needs more launches
+            assert launches == sorted(launches, reverse=True), launches
 
 
 def test_piece_counts():
