@@ -287,9 +287,7 @@ struct PartialMap {
 //  * and, when a launch still writes more than the cache, the element range
 //    is cut into K pieces at the same offsets on every rank and the rounds
 //    concerned run on piece 0, then piece 1, ... (each transfer restricted
-//    to the piece): for the hierarchical schedule all its rounds, K the
-//    smallest count whose launches fit; for the others each block of rounds
-//    that must stay together (round_blocks), the rest running whole.
+//    to the piece), block by block (launch_blocks), the other rounds whole.
 struct LaunchKey {
   int32_t phase, group, step;
   bool operator<(const LaunchKey &o) const {
@@ -329,100 +327,71 @@ LaunchKey group_key(const Plan &p, const Transfer &x, bool split) {
   return k;
 }
 
-// Pieces: the fewest whose widest launch (after the group split) writes at
-// most the cache.
-int split_pieces(const Plan &p) {
-  if (p.units == 0) return 1;
-  const bool split = split_groups(p);
-  std::map<LaunchKey, int64_t> per_launch;
-  for (const Transfer &x : p.xfers) per_launch[group_key(p, x, split)] += unit_elems(p, x.lo, x.hi);
-  int64_t worst = 0;
-  for (const auto &e : per_launch) worst = std::max(worst, e.second);
-  const int64_t bytes = worst * round_write_bytes(p);
-  const int64_t k = p.cache_bytes > 0 ? (bytes + p.cache_bytes - 1) / p.cache_bytes : 64;
-  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
-}
-
-// Pieces a round needs so that what it writes fits the cache.
+// Pieces a launch round needs so that what it writes fits the cache.
 int round_pieces(const Plan &p, int64_t bytes) {
   const int64_t k = p.cache_bytes > 0 ? (bytes + p.cache_bytes - 1) / p.cache_bytes : 64;
   return static_cast<int>(std::min<int64_t>(std::max<int64_t>(k, 1), 64));
 }
 
-// Rounds of a non-hierarchical schedule in blocks that run piece by piece.
-// A round whose output does not fit the cache shares its block with the next
-// round, which reads that output, and the last reduce round with the copy
-// round fused into it; a block takes the largest piece count its rounds'
-// outputs need (the last round's output is read by no later round and needs
-// none).  A schedule whose rounds shrink and grow, like Rabenseifner's, so
-// splits only its wide rounds; the ring, whose rounds are all alike, runs
-// piece by piece throughout or not at all.  Returns, per round, its block's
-// piece count and first phase.
-void round_blocks(const Plan &p, std::vector<int> &block_k, std::vector<int> &block_phase) {
-  const int ns = p.nsteps;
-  std::vector<int64_t> per_round(static_cast<size_t>(ns), 0);  // bytes each round writes
-  std::vector<bool> reduces(static_cast<size_t>(ns), false);
+// Launch rounds (the group keys, in order) in blocks that run piece by
+// piece.  A round whose output does not fit the cache shares its block with
+// the next round of its chain (same phase and group), which reads that
+// output, and the last reduce round with the copy round fused into it; a
+// block takes the largest piece count its rounds' outputs need.  A round
+// whose output the next round does not read (the last of a chain) needs no
+// pieces for it.  A schedule whose rounds shrink and grow, like
+// Rabenseifner's, so splits only its wide rounds; the ring, whose rounds are
+// all alike, runs piece by piece throughout or not at all.  Maps each launch
+// round to its block's piece count and first phase.
+std::map<LaunchKey, std::pair<int, int>> launch_blocks(const Plan &p, bool split) {
+  std::map<LaunchKey, int64_t> bytes;  // what each launch round writes
+  std::map<LaunchKey, bool> reduces;
   for (const Transfer &x : p.xfers) {
-    per_round[x.step] += unit_elems(p, x.lo, x.hi) * transfer_write_bytes(p, x);
-    if (x.kind == kReduce) reduces[x.step] = true;
+    const LaunchKey k = group_key(p, x, split);
+    bytes[k] += unit_elems(p, x.lo, x.hi) * transfer_write_bytes(p, x);
+    if (x.kind == kReduce) reduces[k] = true;
   }
-  std::vector<int> own(static_cast<size_t>(ns), 1);
-  std::vector<bool> link(static_cast<size_t>(ns), false);  // round r shares its block with round r + 1
-  for (int r = 0; r + 1 < ns; ++r) {
-    own[r] = round_pieces(p, per_round[r]);
-    link[r] = own[r] > 1 || (reduces[r] && !reduces[r + 1]);
+  std::vector<LaunchKey> order;
+  for (const auto &e : bytes) order.push_back(e.first);
+  const size_t n = order.size();
+  std::vector<int> own(n, 1);
+  std::vector<bool> link(n, false);  // round i shares its block with round i + 1
+  for (size_t i = 0; i + 1 < n; ++i) {
+    if (order[i].phase != order[i + 1].phase || order[i].group != order[i + 1].group) continue;
+    own[i] = round_pieces(p, bytes[order[i]]);
+    link[i] = own[i] > 1 || (reduces[order[i]] && !reduces[order[i + 1]]);
   }
-  block_k.assign(static_cast<size_t>(ns), 1);
-  block_phase.assign(static_cast<size_t>(ns), 0);
+  std::map<LaunchKey, std::pair<int, int>> out;
   int phase = 0;
-  for (int r = 0; r < ns;) {
-    int r1 = r, k = own[r];
-    while (link[r1]) k = std::max(k, own[++r1]);
-    for (int q = r; q <= r1; ++q) {
-      block_k[q] = k;
-      block_phase[q] = phase;
-    }
+  for (size_t i = 0; i < n;) {
+    size_t i1 = i;
+    int k = own[i];
+    while (link[i1]) k = std::max(k, own[++i1]);
+    for (size_t q = i; q <= i1; ++q) out[order[q]] = {k, phase};
     phase += k;
-    r = r1 + 1;
+    i = i1 + 1;
   }
+  return out;
 }
 
 std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) {
   std::vector<std::pair<LaunchKey, Transfer>> idx;
   const bool split = split_groups(p);
-  const int pieces = p.sched == kHier ? split_pieces(p) : 1;
-  if (p.sched != kHier && p.units > 0) {
-    std::vector<int> block_k, block_phase;
-    round_blocks(p, block_k, block_phase);
-    for (const Transfer &x : p.xfers) {
-      const int k = block_k[x.step];
-      if (k == 1) {
-        idx.push_back({LaunchKey{block_phase[x.step], 0, x.step}, x});
-        continue;
-      }
-      // piece boundaries on multiples of 64 units (whole tiles stay whole)
-      for (int q = 0; q < k; ++q) {
-        Transfer y = x;
-        y.lo = std::max(x.lo, (p.units * q / k) / 64 * 64);
-        y.hi = std::min(x.hi, q + 1 == k ? p.units : (p.units * (q + 1) / k) / 64 * 64);
-        if (y.hi > y.lo) idx.push_back({LaunchKey{block_phase[x.step] + q, 0, x.step}, y});
-      }
+  const std::map<LaunchKey, std::pair<int, int>> blocks = launch_blocks(p, split);
+  for (const Transfer &x : p.xfers) {
+    const std::pair<int, int> &b = blocks.at(group_key(p, x, split));
+    const int k = b.first;
+    if (k == 1) {
+      idx.push_back({LaunchKey{b.second, 0, x.step}, x});
+      continue;
     }
-  } else if (pieces > 1) {
     // piece boundaries on multiples of 64 units (whole tiles stay whole)
-    std::vector<int64_t> cut;
-    for (int k = 0; k <= pieces; ++k) cut.push_back(k == pieces ? p.units : (p.units * k / pieces) / 64 * 64);
-    for (int k = 0; k < pieces; ++k)
-      for (const Transfer &x : p.xfers) {
-        Transfer y = x;
-        y.lo = std::max(x.lo, cut[k]);
-        y.hi = std::min(x.hi, cut[k + 1]);
-        LaunchKey key = group_key(p, x, split);
-        key.phase += 3 * k;  // piece-major, then phase, group, round
-        if (y.hi > y.lo) idx.push_back({key, y});
-      }
-  } else {
-    for (const Transfer &x : p.xfers) idx.push_back({group_key(p, x, split), x});
+    for (int q = 0; q < k; ++q) {
+      Transfer y = x;
+      y.lo = std::max(x.lo, (p.units * q / k) / 64 * 64);
+      y.hi = std::min(x.hi, q + 1 == k ? p.units : (p.units * (q + 1) / k) / 64 * 64);
+      if (y.hi > y.lo) idx.push_back({LaunchKey{b.second + q, 0, x.step}, y});
+    }
   }
   std::stable_sort(idx.begin(), idx.end(),
                    [](const std::pair<LaunchKey, Transfer> &a, const std::pair<LaunchKey, Transfer> &b) {
