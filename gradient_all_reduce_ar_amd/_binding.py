@@ -102,6 +102,10 @@ def _declare(L):
         "ar_plan_launch_scratch": ([P, i32, pi64, pi64], ctypes.c_int),
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_profiling_period": ([P, ctypes.c_int], ctypes.c_int),
+        "ar_plan_set_profiling_evict": ([P, P, sz], ctypes.c_int),
+        "ar_plan_launch_shape": ([P, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(ctypes.c_uint32), pi32],
+                                 ctypes.c_int),
+        "ar_hbm_probe": ([P, i32, P, i32, sz, i32, i32, P], ctypes.c_int),
         "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_cache_bytes": ([P, sz], ctypes.c_int),
         "ar_bucket_set_graph": ([P, ctypes.c_int], ctypes.c_int),
@@ -160,6 +164,43 @@ def _ptr_array(bufs):
     return (ctypes.c_void_p * max(len(bufs), 1))(*[_ptr(b) for b in bufs])
 
 
+def _check_bufs(bufs, nranks, nbytes, what):
+    """The C calls read exactly nranks pointers from the host array and let
+    the kernels touch nbytes of each buffer, so a short list or a short
+    tensor would make them read or write past the end.  Raises ValueError
+    unless there are nranks buffers and every tensor among them is a
+    contiguous device tensor of at least nbytes.  Plain integers are device
+    addresses whose extent cannot be checked here."""
+    if bufs is None:
+        raise ValueError(f"{what}s: None")
+    if len(bufs) != nranks:
+        raise ValueError(f"{len(bufs)} {what}s for a plan of {nranks} ranks")
+    for r, b in enumerate(bufs):
+        if not hasattr(b, "data_ptr"):
+            continue
+        if not getattr(b, "is_cuda", False):
+            raise ValueError(f"{what} {r} is not a device tensor")
+        if not b.is_contiguous():
+            raise ValueError(f"{what} {r} is not contiguous")
+        have = b.numel() * b.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what} {r} holds {have} bytes; the plan reads and writes {nbytes}")
+
+
+def _plan_extent(plan):
+    """(nranks, bytes of each rank buffer, bytes of each error buffer)."""
+    s = lib().ar_plan_stats(plan)
+    return s.nranks, s.count * s.elem_bytes, s.count * 4
+
+
+def _bucket_extent(bp):
+    """(nranks, bytes of each rank arena, bytes of each error arena)."""
+    s = lib().ar_bucket_stats(bp)
+    arena = ctypes.c_size_t()
+    _check(lib().ar_bucket_layout(bp, None, ctypes.byref(arena)))
+    return s.nranks, arena.value * s.elem_bytes, arena.value * 4
+
+
 def _code(table, v):
     return table[v] if isinstance(v, str) else int(v)
 
@@ -190,12 +231,20 @@ def ar_plan_prepare(plan):
 
 
 def ar_allreduce(plan, rank_bufs, stream=None):
+    if plan:
+        n, nbytes, _ = _plan_extent(plan)
+        _check_bufs(rank_bufs, n, nbytes, "rank buffer")
     arr = _ptr_array(rank_bufs)
     _check(lib().ar_allreduce(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
 
 
 def ar_allreduce_ef(plan, rank_bufs, error_bufs, stream=None):
     """error_bufs: per-rank fp32 residual buffers, or None (no error feedback)."""
+    if plan:
+        n, nbytes, ebytes = _plan_extent(plan)
+        _check_bufs(rank_bufs, n, nbytes, "rank buffer")
+        if error_bufs is not None:
+            _check_bufs(error_bufs, n, ebytes, "error buffer")
     arr = _ptr_array(rank_bufs)
     err = ctypes.cast(_ptr_array(error_bufs), ctypes.c_void_p) if error_bufs is not None else None
     _check(lib().ar_allreduce_ef(plan, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream)))
@@ -305,6 +354,29 @@ def ar_plan_set_profiling_period(plan, period):
     _check(lib().ar_plan_set_profiling_period(plan, int(period)))
 
 
+def ar_plan_set_profiling_evict(plan, buf, nbytes):
+    """Cold-cache timing: every timed launch is preceded by a fill of nbytes of buf."""
+    _check(lib().ar_plan_set_profiling_evict(plan, _ptr(buf) or None, int(nbytes)))
+
+
+def ar_plan_launch_shape(plan, i):
+    """dict(cold, units, cpol, batch, grid_x, threads) of launch i's kernel."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    gx, th = ctypes.c_uint32(), ctypes.c_int32()
+    _check(lib().ar_plan_launch_shape(plan, i, *[ctypes.byref(x) for x in v], ctypes.byref(gx), ctypes.byref(th)))
+    return {"cold": v[0].value, "units": v[1].value, "cpol": v[2].value, "batch": v[3].value,
+            "grid_x": gx.value, "threads": th.value}
+
+
+def ar_hbm_probe(srcs, dsts, nbytes, units=2, policy=1, stream=None):
+    """Each 16-byte unit of every dst gets the fp32 sum of that unit of every
+    src (policy 0 plain, 1 nt loads + sc1 stores, 2 nt loads and stores)."""
+    sa = (ctypes.c_void_p * max(len(srcs), 1))(*[_ptr(b) for b in srcs])
+    da = (ctypes.c_void_p * max(len(dsts), 1))(*[_ptr(b) for b in dsts])
+    _check(lib().ar_hbm_probe(ctypes.cast(sa, ctypes.c_void_p), len(srcs), ctypes.cast(da, ctypes.c_void_p),
+                              len(dsts), int(nbytes), int(units), int(policy), _stream(stream)))
+
+
 def ar_plan_launch_times(plan):
     """Per-launch ms of the logged calls, as a list of per-call lists (-1: not timed)."""
     n = ctypes.c_int32()
@@ -372,6 +444,9 @@ def ar_bucket_batched_plan(bp):
 
 
 def ar_bucket_allreduce(bp, rank_arenas, stream=None):
+    if bp:
+        n, nbytes, _ = _bucket_extent(bp)
+        _check_bufs(rank_arenas, n, nbytes, "rank arena")
     arr = _ptr_array(rank_arenas)
     _check(lib().ar_bucket_allreduce(bp, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
 
@@ -388,6 +463,9 @@ def _event(e):
 
 def ar_bucket_allreduce_after(bp, rank_arenas, stream=None, ready_events=None, done_events=None):
     """ready_events / done_events: per bucket, torch.cuda.Event, raw hipEvent_t ints, or None."""
+    if bp:
+        n, nbytes, _ = _bucket_extent(bp)
+        _check_bufs(rank_arenas, n, nbytes, "rank arena")
     arr = _ptr_array(rank_arenas)
     nb = ar_bucket_count(bp)
 
@@ -404,6 +482,11 @@ def ar_bucket_allreduce_after(bp, rank_arenas, stream=None, ready_events=None, d
 
 
 def ar_bucket_allreduce_ef(bp, rank_arenas, error_arenas, stream=None, ready_events=None, done_events=None):
+    if bp:
+        n, nbytes, ebytes = _bucket_extent(bp)
+        _check_bufs(rank_arenas, n, nbytes, "rank arena")
+        if error_arenas is not None:
+            _check_bufs(error_arenas, n, ebytes, "error arena")
     arr = _ptr_array(rank_arenas)
     err = ctypes.cast(_ptr_array(error_arenas), ctypes.c_void_p) if error_arenas is not None else None
     nb = ar_bucket_count(bp)
