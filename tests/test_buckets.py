@@ -257,9 +257,12 @@ def test_bucketed_bf16_parity(n, sched):
         host = workloads.bucketed_arenas(n, sizes, offs, arena)
         nb = B.ar_bucket_count(bp)
         refs = {}
-        for batch in (True, False):
-            print(f"case bucketed n={n} {sched} batched={batch}", flush=True)
+        # batched and one by one in the step mode; the one-pass mode (every
+        # bucket in one launch) as the benchmark's comparison runs it
+        for batch, mode in ((True, "steps"), (False, "steps"), (True, "onepass")):
+            print(f"case bucketed n={n} {sched} batched={batch} {mode}", flush=True)
             B.ar_bucket_set_batching(bp, batch)
+            B.ar_bucket_set_exec(bp, mode)
             bufs = [torch.from_numpy(h.view(np.int16)).to("cuda:0") for h in host]
             B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
             torch.cuda.synchronize()
@@ -273,7 +276,7 @@ def test_bucketed_bf16_parity(n, sched):
                 covered[off:off + cnt] = True
                 if b not in refs:
                     refs[b] = oracle.run([h[off:off + cnt].copy() for h in host], "bf16", sched)[0]
-                assert np.array_equal(got[off:off + cnt], refs[b]), f"bucket {b} batched={batch}"
+                assert np.array_equal(got[off:off + cnt], refs[b]), f"bucket {b} batched={batch} {mode}"
             print(f"  {nb} buckets bit-exact", flush=True)
             assert np.all(got[~covered] == 0)
     finally:

@@ -84,8 +84,9 @@ def _grads(n, count, seed):
             for _ in range(n)]
 
 
-SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
-        [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (16, 8), (16, 4), (8, 1), (8, 8))] + \
+SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16, 32, 48, 64)] + \
+        [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (16, 8), (16, 4), (8, 1), (8, 8), (64, 8), (64, 16),
+                                             (32, 8), (48, 8))] + \
         [("rabenseifner", n, 1) for n in (2, 8, 16, 64)] + \
         [("recursive_doubling", n, 1) for n in (2, 8, 64)] + \
         [("tree", n, 1) for n in (2, 5, 13, 64)] + \

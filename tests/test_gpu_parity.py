@@ -27,10 +27,11 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _check(xs, dtype, sched, group, mode):
+def _check(xs, dtype, sched, group, mode, ref=None):
     _say(f"case {sched} n={len(xs)} g={group} count={len(xs[0])} {dtype} {mode}")
     got = gpu_allreduce(xs, dtype, sched, group, mode)
-    ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=group)
+    if ref is None:
+        ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=group)
     bv = bits_view(dtype)
     for r in range(len(xs)):
         if not np.array_equal(got[r], ref[r].view(bv)):
@@ -47,8 +48,13 @@ def test_c1_ring_fp32_n4():
         _check(xs, "fp32", "ring", 1, mode)
 
 
-SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16)] + \
-        [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (8, 4), (16, 8), (16, 4), (12, 3), (8, 8), (8, 1))] + \
+# Up to 64 ranks: the ring's one-pass fold runs full batches of 16 ranks plus
+# a predicated remainder (32, 48, 64), and the hierarchical shapes include
+# 8 groups of 8 (the 8 nodes x 8 GPUs case of Scaling ML systems ch. 06,
+# "Hierarchical bandwidth multiplier") and groups of 16.
+SMALL = [("ring", n, 1) for n in (1, 2, 3, 4, 5, 8, 16, 32, 48, 64)] + \
+        [("hierarchical", n, g) for n, g in ((4, 2), (6, 3), (8, 4), (16, 8), (16, 4), (12, 3), (8, 8), (8, 1),
+                                             (64, 8), (64, 16), (32, 8), (48, 8))] + \
         [("rabenseifner", n, 1) for n in (2, 4, 8, 16, 64)] + \
         [("recursive_doubling", n, 1) for n in (2, 8, 64)] + \
         [("tree", n, 1) for n in (2, 5, 8, 13, 24, 40, 64)] + \
@@ -62,8 +68,9 @@ def test_small_sizes_all_modes(sched, n, g, dtype):
     # spans several 4096-element tiles per op with a ragged tail
     for count in (0, 1, 5, 4099, 100003):
         xs = workloads.normal_inputs(n, count, seed=count, sigma=1.0, dtype="fp32" if dtype == "fp32" else "bf16")
+        ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
         for mode in MODES:
-            _check(xs, dtype, sched, g, mode)
+            _check(xs, dtype, sched, g, mode, ref)
 
 
 def test_special_values_fp32():

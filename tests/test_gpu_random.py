@@ -26,7 +26,7 @@ def _draw(rng):
         n = int(2 ** rng.integers(0, 7))
         g = 1
     else:
-        n = int(rng.integers(1, 25))
+        n = int(rng.integers(1, 65))
         divisors = [d for d in range(1, n + 1) if n % d == 0]
         g = int(divisors[rng.integers(len(divisors))]) if sched == "hierarchical" else 1
     dtype = ["fp32", "bf16", "bf16_each", "int8_ef"][rng.integers(4)]
