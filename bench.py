@@ -64,12 +64,18 @@ KIND_NAMES = {0x100: "chunk_reduce", 0x200: "chunk_copy", 0x300: "onepass_ring",
               0xA00: "q_decode"}
 
 
-def kernel_label(kind):
-    """Kernel name with its template arguments, as rocprofv3 reports it."""
+def kernel_label(kind, shape=None, nranks=None):
+    """Kernel name with its template arguments, as rocprofv3 reports it
+    (shape: ar_plan_launch_shape of a launch of this kind; without it the
+    step kernels are named by their flags only)."""
     fam = kind & 0xF00
     if fam == 0x100:
+        if shape:
+            return f"chunk_reduce<{kind & 0xF}, {shape['units']}, {shape['cpol']}>"
         return f"chunk_reduce<{kind & 0xF}>"
     if fam == 0x200:
+        if shape:
+            return f"chunk_copy<{kind & 0xFF}, {shape['units']}, {shape['cpol']}>"
         return f"chunk_copy<{kind & 0xFF}>"
     if fam == 0x800:
         if kind & 0x13:  # fused hop: raw operands or final decode
@@ -81,7 +87,29 @@ def kernel_label(kind):
         return KIND_NAMES[fam]
     if kind & 3 == 3:  # one-pass fold of an INT8 plan
         return "q_" + KIND_NAMES[fam]
+    bf, each = ("true" if kind & 3 else "false"), ("true" if kind & 3 == 2 else "false")
+    if shape and fam in (0x300, 0x400):
+        return f"{KIND_NAMES[fam]}<{bf}, {each}, {shape['units']}, {shape['batch']}>"
+    if shape and fam == 0x500 and nranks:
+        nmax = 1 << max(0, (nranks - 1).bit_length())
+        return f"onepass_tree<{bf}, {each}, {nmax}, {'true' if nranks < nmax else 'false'}, {shape['units']}, " \
+               f"{shape['batch']}>"
+    if shape and fam == 0x600 and nranks:
+        return f"onepass_dtree<{bf}, {each}, {nranks}, {shape['units']}>"
     return f"{KIND_NAMES[fam]}<{'bf16' if kind & 1 else 'fp32'}>"
+
+
+def read_share(kind, elem):
+    """Fraction of a step or one-pass kernel's algorithmic bytes that are reads."""
+    fam = kind & 0xF00
+    if fam == 0x100:
+        if elem == 4:
+            rd, wr = 8, 4 * (2 if kind & 8 else 1)
+        else:
+            rd = (2 if kind & 1 else 4) + (2 if kind & 2 else 4)
+            wr = (2 if kind & 4 else 4) * (2 if kind & 8 else 1)
+        return rd / (rd + wr)
+    return 0.5  # copies and one-pass folds read as much as they write
 
 
 def cpu_model():
@@ -176,6 +204,57 @@ def traffic_record(kernel_name, workload, exec_mode):
     return None
 
 
+def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=None, gib=4, reps=5):
+    """Attainable HBM bandwidth of this GPU for the kernels' read/write mixes,
+    measured with the library's own probe kernel (ar_hbm_probe) on buffers of
+    `gib` GiB of random fp32 (far larger than the 256 MB device cache): for
+    each mix the best of 1, 2 and 4 units per thread and of the three cache
+    policies, each the median of `reps` event-timed launches after two
+    untimed ones.  With rank_bufs, also the one-pass mix on the workload's
+    own buffers: every rank read and every rank written, in place (each
+    launch on the inputs restored by `restore`, outside its events)."""
+    nbytes = gib << 30
+    bufs = [torch.randn(nbytes // 4, device=dev) for _ in range(4)]
+    torch.cuda.synchronize()
+    mixes = [("read 1:0", bufs[:1], [], nbytes), ("write 0:1", [], bufs[:1], nbytes),
+             ("copy 1:1", bufs[:1], bufs[1:2], nbytes), ("reduce 2:1", bufs[:2], bufs[2:3], nbytes),
+             ("reduce 2:2", bufs[:2], bufs[2:4], nbytes)]
+    if rank_bufs is not None and len(rank_bufs) <= 64 and rank_bytes % 16 == 0 and rank_bytes >= (64 << 20):
+        mixes.append((f"fold {len(rank_bufs)}:{len(rank_bufs)}", rank_bufs, rank_bufs, rank_bytes))
+    out = {}
+    for name, src, dst, nb in mixes:
+        best = None
+        for units in (1, 2, 4):
+            for policy in (0, 1, 2):
+                ts = []
+                for r in range(reps + 2):
+                    if restore is not None and src is rank_bufs:
+                        restore()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    B.ar_hbm_probe(src, dst, nb, units, policy, stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if r >= 2:
+                        ts.append(e0.elapsed_time(e1))
+                ts.sort()
+                med = ts[len(ts) // 2]
+                gbps = (len(src) + len(dst)) * nb / (med * 1e-3) / 1e9
+                if best is None or gbps > best["GBps"]:
+                    best = {"GBps": round(gbps, 1), "ms": round(med, 4), "units": units, "policy": policy,
+                            "read_share": len(src) / (len(src) + len(dst)), "bytes": (len(src) + len(dst)) * nb}
+        out[name] = best
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def attainable_for(ceil, share):
+    """The probe mix whose read share is nearest a kernel's."""
+    name = min(ceil, key=lambda k: abs(ceil[k]["read_share"] - share))
+    return name, ceil[name]["GBps"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,7 +265,8 @@ def main():
                     help="overlap workload: backward compute per bucket as a multiple of its all-reduce time")
     ap.add_argument("--exec", default="steps", choices=["steps", "steps_unfused", "onepass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the one-pass comparison run")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the one-pass, graph, cold-cache and ceiling runs")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 1 GiB device-to-device torch copy three times, so that "
                          "hardware counters of the same run can be scaled by a copy of known size")
@@ -222,7 +302,7 @@ def main():
         del src, dst
         log("calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
 
-    # ---- inputs, resident in HBM before timing
+    # ---- inputs, resident in HBM before timing, with pristine device copies
     t0 = time.time()
     bucketed = count is None
     if bucketed:
@@ -244,7 +324,8 @@ def main():
         count_logical = count
         lplan = plan
     bufs = [torch.from_numpy(h.view(view)).to(dev) for h in host]
-    errs = None
+    pristine = [b.clone() for b in bufs]
+    errs = perrs = None
     if quant:
         # every call multiplies the values by about N (in place); 28 calls from
         # N(0, 1e-3) stay finite, the range the quantizer is defined on
@@ -254,15 +335,16 @@ def main():
             sys.exit(2)
         err_host = workloads.normal_inputs(n, count, seed=1, dtype="fp32")
         errs = [torch.from_numpy(h).to(dev) for h in err_host]
+        perrs = [e.clone() for e in errs]
     torch.cuda.synchronize()
 
     def reset_inputs():
-        """Untimed: restore the initial values (before the comparison run)."""
-        for b_, h_ in zip(bufs, host):
-            b_.copy_(torch.from_numpy(h_.view(view)))
+        """Untimed: restore the initial values from the pristine device copies."""
+        for b_, p_ in zip(bufs, pristine):
+            b_.copy_(p_)
         if quant:
-            for e_, h_ in zip(errs, err_host):
-                e_.copy_(torch.from_numpy(h_))
+            for e_, p_ in zip(errs, perrs):
+                e_.copy_(p_)
         torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s: {desc}")
 
@@ -273,7 +355,8 @@ def main():
         run = lambda: B.ar_allreduce_ef(plan, bufs, errs, stream)  # noqa: E731
     else:
         run = lambda: B.ar_allreduce(plan, bufs, stream)  # noqa: E731
-    # ---- the timed run: the calls as a user makes them (no profiling)
+    # ---- the timed run: the calls as a user makes them (no profiling), back
+    # to back between two device synchronisations
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -290,74 +373,130 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
     ms = wall_ms
 
+    # ---- per-call times (the nccl-tests convention): every call on the
+    # pristine inputs, restored before it outside the timed interval, timed by
+    # a HIP event pair around the call
+    call_ms = []
+    for c in range(args.steps):
+        reset_inputs()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        run()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        call_ms.append(c0.elapsed_time(c1))
+    call_sorted = sorted(call_ms)
+    median_ms = call_sorted[len(call_sorted) // 2] if len(call_sorted) % 2 else \
+        0.5 * (call_sorted[len(call_sorted) // 2 - 1] + call_sorted[len(call_sorted) // 2])
+    min_ms = call_sorted[0]
+
     # ---- the roofline run: the same calls again (inputs restored, untimed),
     # about four launches per call timed by start/stop events that the
     # launches record as part of their dispatch (every launch over `period`
     # calls), so the events barely perturb the calls they time
-    period = max(1, B.ar_plan_num_launches(lplan) // 4)
-    B.ar_plan_set_profiling(lplan, max(args.steps, 1))
-    B.ar_plan_set_profiling_period(lplan, period)
-    reset_inputs()
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    B.ar_plan_launch_times(lplan)  # clear the warm-up entries
-    t_p = time.perf_counter()
-    for c in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    prof_ms = (time.perf_counter() - t_p) * 1e3 / max(args.steps, 1)
-
-    S = count_logical * elem
-    algbw = S / (ms * 1e-3) / 1e9
-    busbw = algbw * 2 * (n - 1) / n
-    stats = B.ar_plan_stats(lplan)
-    model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
-
-    roofline = None
-    per_kind = {}
-    times = B.ar_plan_launch_times(lplan)  # -1: launch not timed in that call (sampling)
     nl = B.ar_plan_num_launches(lplan)
+    shapes = [B.ar_plan_launch_shape(lplan, i) for i in range(nl)]
     lb = [launch_bytes(B, lplan, i, n, elem, count) for i in range(nl)]
+    keys = [(kind, shapes[i]["cold"], shapes[i]["units"]) for i, (_, kind) in enumerate(lb)]
+    labels = {k: kernel_label(k[0], shapes[i], n) for i, k in enumerate(keys)}
+    period = max(1, nl // 4)
+
+    def timed_run(evict=None):
+        """Per-kernel-shape totals of one profiled run of W + K calls."""
+        B.ar_plan_set_profiling(lplan, max(args.steps, 1))
+        B.ar_plan_set_profiling_period(lplan, period)
+        B.ar_plan_set_profiling_evict(lplan, evict, evict.numel() * 4 if evict is not None else 0)
+        reset_inputs()
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        B.ar_plan_launch_times(lplan)  # clear the warm-up entries
+        t_p = time.perf_counter()
+        for c in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        run_ms = (time.perf_counter() - t_p) * 1e3 / max(args.steps, 1)
+        times = B.ar_plan_launch_times(lplan)  # -1: launch not timed in that call (sampling)
+        per = {}
+        for call in times:
+            for i, t in enumerate(call):
+                if t < 0:
+                    continue
+                k = per.setdefault(keys[i], {"ms": 0.0, "launches": 0, "bytes": 0})
+                k["ms"] += t
+                k["launches"] += 1
+                k["bytes"] += lb[i][0]
+        means = []
+        for i in range(nl):
+            ts = [call[i] for call in times if call[i] >= 0]
+            means.append(sum(ts) / len(ts) if ts else None)
+        B.ar_plan_set_profiling_evict(lplan, None, 0)
+        B.ar_plan_set_profiling(lplan, 0)
+        return per, run_ms, means
+
+    per_kind, prof_ms, means = timed_run()
     per_call_count = {}
-    for nbytes, kind in lb:
-        per_call_count[kind] = per_call_count.get(kind, 0) + 1
-    for call in times:
-        for i, t in enumerate(call):
-            if t < 0:
-                continue
-            nbytes, kind = lb[i]
-            k = per_kind.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0})
-            k["ms"] += t
-            k["launches"] += 1
-            k["bytes"] += nbytes
+    for k in keys:
+        per_call_count[k] = per_call_count.get(k, 0) + 1
     # the kernel with the largest share of a call's GPU time
     dom = max(per_kind, key=lambda f: per_kind[f]["ms"] / per_kind[f]["launches"] * per_call_count[f])
     d = per_kind[dom]
     avg_ms = d["ms"] / d["launches"]
     bytes_per_launch = d["bytes"] / d["launches"]
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
-    traffic = traffic_record(kernel_label(dom), args.workload, args.exec)
+    traffic = traffic_record(labels[dom], args.workload, args.exec)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": kernel_label(dom),
+                "kernel": labels[dom],
                 "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes_per_launch": int(bytes_per_launch),
                 "launches_timed": d["launches"], "profiling_period": period}
-    log("per kernel:", {kernel_label(f): {"ms_timed": round(v["ms"], 3), "launches_timed": v["launches"],
-                                          "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
-                          for f, v in per_kind.items()})
-    # kernel time per call: each launch's mean over the calls that timed it
-    means = []
-    for i in range(nl):
-        ts = [call[i] for call in times if call[i] >= 0]
-        means.append(sum(ts) / len(ts) if ts else None)
     sum_launch_ms = sum(means) if all(m is not None for m in means) else None
-    B.ar_plan_set_profiling(lplan, 0)
     extra = {}
     prof_alg = count_logical * elem / (prof_ms * 1e-3) / 1e9
     extra["with_launch_events"] = {"exec": args.exec, "ms_per_step": round(prof_ms, 4),
                                    "busbw_GBps": round(prof_alg * 2 * (n - 1) / n, 1),
                                    "algbw_GBps": round(prof_alg, 1)}
+
+    # ---- cold cache: the same profiled calls with 1 GiB written just before
+    # every timed launch, so that the launch reads nothing from the device
+    # cache; and the attainable bandwidth of each read/write mix on buffers far
+    # larger than the cache
+    per_cold, ceil = {}, None
+    if not args.no_extra:
+        evict = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        per_cold, _, _ = timed_run(evict)
+        del evict
+        torch.cuda.empty_cache()
+        ceil = probe_ceilings(B, torch, dev, stream, None if bucketed or quant else bufs, count_logical * elem,
+                              reset_inputs)
+    per_kernel = []
+    for k, v in sorted(per_kind.items(), key=lambda kv: -kv[1]["ms"] / kv[1]["launches"] * per_call_count[kv[0]]):
+        rate = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+        row = {"kernel": labels[k], "launches_per_call": per_call_count[k],
+               "bytes_per_launch": int(v["bytes"] / v["launches"]),
+               "warm_ms": round(v["ms"] / v["launches"], 5), "warm_GBps": round(rate, 1),
+               "warm_frac_of_peak": round(rate / HBM_PEAK_GBPS, 4)}
+        c = per_cold.get(k)
+        if c:
+            crate = c["bytes"] / (c["ms"] * 1e-3) / 1e9
+            row.update({"cold_ms": round(c["ms"] / c["launches"], 5), "cold_GBps": round(crate, 1),
+                        "cold_frac_of_peak": round(crate / HBM_PEAK_GBPS, 4)})
+        if ceil:
+            probe, att = attainable_for(ceil, read_share(k[0], elem))
+            row.update({"attainable_probe": probe, "attainable_GBps": att,
+                        "warm_frac_of_attainable": round(rate / att, 4)})
+            if c:
+                row["cold_frac_of_attainable"] = round(crate / att, 4)
+        per_kernel.append(row)
+        if k == dom:
+            if ceil:
+                roofline.update({"attainable_GBps": row["attainable_GBps"], "attainable_probe": probe,
+                                 "frac_of_attainable": row["warm_frac_of_attainable"]})
+            if c:
+                roofline["cold"] = {"avg_launch_ms": row["cold_ms"], "achieved": row["cold_GBps"],
+                                    "frac": row["cold_frac_of_peak"],
+                                    "frac_of_attainable": row.get("cold_frac_of_attainable")}
+    log("per kernel:", json.dumps(per_kernel))
 
     # ---- buckets one by one, each with its own launches and a HIP event after
     # it (per-bucket times)
@@ -388,11 +527,12 @@ def main():
             alg_b = cnt * elem / (med * 1e-3) / 1e9
             per_bucket.append({"bucket": b, "bytes_per_rank": cnt * elem, "median_ms": round(med, 4),
                                "algbw_GBps": round(alg_b, 1), "busbw_GBps": round(alg_b * 2 * (n - 1) / n, 1)})
-        obo_alg = S / (obo_ms * 1e-3) / 1e9
+        obo_alg = count_logical * elem / (obo_ms * 1e-3) / 1e9
         extra["buckets_one_by_one"] = {
             "ms_per_step": round(obo_ms, 4), "busbw_GBps": round(obo_alg * 2 * (n - 1) / n, 1),
             "algbw_GBps": round(obo_alg, 1), "launches_per_step": B.ar_bucket_stats(plan)["launches"]}
 
+    S = count_logical * elem
     # ---- one-pass comparison on the same buffers (bit-identical results)
     if not args.no_extra and args.exec != "onepass":
         if bucketed:
@@ -411,9 +551,15 @@ def main():
         op_ms = (time.perf_counter() - t_a) * 1e3 / max(args.steps, 1)
         op_alg = S / (op_ms * 1e-3) / 1e9
         op_stats = B.ar_plan_stats(B.ar_bucket_batched_plan(plan) if bucketed else plan)
+        op_gbps = op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9
         extra["onepass"] = {"ms_per_step": round(op_ms, 4), "busbw_GBps": round(op_alg * 2 * (n - 1) / n, 1),
-                            "algbw_GBps": round(op_alg, 1),
-                            "hbm_model_GBps": round(op_stats["hbm_bytes_model"] / (op_ms * 1e-3) / 1e9, 1)}
+                            "algbw_GBps": round(op_alg, 1), "hbm_model_GBps": round(op_gbps, 1),
+                            "hbm_model_frac_of_peak": round(op_gbps / HBM_PEAK_GBPS, 4)}
+        if ceil:
+            fold = [k for k in ceil if k.startswith("fold")]
+            extra["onepass"]["frac_of_copy_ceiling"] = round(op_gbps / ceil["copy 1:1"]["GBps"], 4)
+            if fold:
+                extra["onepass"]["frac_of_fold_probe"] = round(op_gbps / ceil[fold[0]]["GBps"], 4)
 
     # ---- the same exec mode replayed as one HIP graph per call
     if not args.no_extra:
@@ -443,7 +589,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        del bufs, errs
+        del bufs, errs, pristine, perrs
         torch.cuda.empty_cache()
         # repeat whole oracle runs (fresh copies of the inputs, copied outside
         # the timing) until about 10 s of CPU work, at most 30 s
@@ -480,6 +626,17 @@ def main():
                "sample": sample, "seconds": round(cpu_s, 2), "host_cpus": os.cpu_count(),
                "cpu_model": cpu_model(), "threads_used": 1}
 
+    algbw = S / (ms * 1e-3) / 1e9
+    busbw = algbw * 2 * (n - 1) / n
+    stats = B.ar_plan_stats(B.ar_bucket_batched_plan(plan) if bucketed else plan)
+    if bucketed:
+        B.ar_bucket_set_exec(plan, args.exec)
+        stats = B.ar_plan_stats(B.ar_bucket_batched_plan(plan))
+    else:
+        B.ar_plan_set_exec(plan, args.exec)
+        stats = B.ar_plan_stats(plan)
+    model_gbps = stats["hbm_bytes_model"] / (ms * 1e-3) / 1e9
+    med_alg = S / (median_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(busbw, 1),
@@ -501,15 +658,23 @@ def main():
             + f"eager launches; the roofline from a second run of the same calls, about four launches per "
             f"call timed by HIP events (every launch over {period} calls)",
             "algbw_GBps": round(algbw, 1), "busbw_GBps": round(busbw, 1),
+            "median_ms": round(median_ms, 4), "min_ms": round(min_ms, 4),
+            "median_busbw_GBps": round(med_alg * 2 * (n - 1) / n, 1),
+            "per_call_protocol": f"{args.steps} calls, each on the inputs restored from pristine device copies "
+                                 "outside its HIP-event interval",
             "hbm_model_bytes": stats["hbm_bytes_model"], "hbm_model_GBps": round(model_gbps, 1),
             "hbm_model_frac_of_peak": round(model_gbps / HBM_PEAK_GBPS, 4),
             "launches_per_step": stats["launches"], "schedule_steps": stats["steps"],
             "event_ms_per_step": round(ev_ms, 4),
             "kernel_ms_per_step": None if sum_launch_ms is None else round(sum_launch_ms, 4),
+            "per_kernel": per_kernel,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if ceil:
+        out["config"]["hbm_ceiling"] = {k: {"GBps": v["GBps"], "units": v["units"], "policy": v["policy"]}
+                                        for k, v in ceil.items()}
     if extra:
         out["config"]["compare"] = extra
     if quant:

@@ -4,10 +4,14 @@
 // tables to the device and, for bf16, allocates the fp32 partial-sum
 // scratch.  ar_allreduce then launches one kernel per launch of the plan on
 // the caller's stream, passing the caller's rank pointers by value; nothing
-// is allocated or copied on the hot path.
+// is allocated or copied on the hot path.  After each call an event is
+// recorded on the caller's stream, so that changing or destroying the plan
+// waits for the plan's own work only, never for the whole device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -40,9 +44,16 @@ struct ar_plan {
   int device = -1;
   bool prepared = false;
   ar_dev::DevOp *d_ops = nullptr;
-  std::vector<int64_t> op_offset;  // per launch: index of its first op in d_ops
-  std::vector<uint32_t> grid_x;    // per launch
-  std::vector<uint8_t> cold;       // per launch: streaming kernel shape
+  // Host side of the launches, computed whenever the plan is lowered (no
+  // device work): the op table's contents, and per launch its first op in
+  // the table, its grid width and kernel shape.  launch_err says why the
+  // launches cannot run (empty: they can); table_id names this lowering.
+  std::vector<ar_dev::DevOp> host_ops;
+  std::vector<int64_t> op_offset;
+  std::vector<uint32_t> grid_x;
+  std::vector<uint8_t> cold;       // streaming kernel shape
+  std::string launch_err;
+  uint64_t table_id = 0;
   float *scratch = nullptr;        // owned unless external_scratch
   size_t scratch_bytes = 0;
   float *external_scratch = nullptr;
@@ -56,26 +67,55 @@ struct ar_plan {
   static constexpr size_t kMaxGraphs = 8;
   bool use_graph = false;
   std::vector<GraphEntry> graphs;
-  hipStream_t capture_stream = nullptr;
+  hipStream_t own_stream = nullptr;  // non-blocking: op-table upload and graph capture
   int32_t prof_calls = 0;           // capacity of the event log in calls
   int64_t prof_logged = 0;          // calls recorded since the log was last read
   std::vector<hipEvent_t> events;   // prof_calls * launches * 2 (start, stop)
   int32_t prof_period = 1;          // call c times launch i iff (i + c) % period == 0
   std::vector<uint8_t> sampled;     // prof_calls * launches: the launch was timed
+  void *evict_buf = nullptr;        // written before every timed launch (cold-cache timing)
+  int64_t evict_bytes = 0;
+  // Completion marks: for each stream the plan has run on, an event recorded
+  // after the last call on that stream (none while the stream is being
+  // captured by the caller).
+  struct DoneMark {
+    hipStream_t stream;
+    hipEvent_t event;
+  };
+  static constexpr size_t kMaxMarks = 16;
+  std::vector<DoneMark> marks;
+  // The last (rank pointers, error pointers) set that passed the pointer
+  // checks (checked_n entries; 0: none); the same set is not checked again.
+  std::array<uintptr_t, 2 * ar::kMaxExecRanks> checked{};
+  int checked_n = 0;
 
   // fp32 partial-sum slots, or the INT8 code slots
   size_t need_scratch_bytes() const { return static_cast<size_t>(ar::workspace_bytes(p)); }
 
+  // Waits until every call made on this plan has finished on the device.
+  void wait_idle() {
+    for (DoneMark &m : marks) (void)hipEventSynchronize(m.event);
+  }
+
   void drop_graphs() {
-    if (!graphs.empty()) (void)hipDeviceSynchronize();  // a replay may still be in flight
+    if (!graphs.empty()) wait_idle();  // a replay may still be in flight
     for (GraphEntry &g : graphs) (void)hipGraphExecDestroy(g.exec);
     graphs.clear();
   }
 
+  void release_marks() {
+    wait_idle();
+    for (DoneMark &m : marks) (void)hipEventDestroy(m.event);
+    marks.clear();
+  }
+
+  // Frees the device tables, scratch, graphs and profiling events, after
+  // the plan's calls in flight have finished.
   void release_device() {
+    wait_idle();
     drop_graphs();
-    if (capture_stream) (void)hipStreamDestroy(capture_stream);
-    capture_stream = nullptr;
+    if (own_stream) (void)hipStreamDestroy(own_stream);
+    own_stream = nullptr;
     if (d_ops) (void)hipFree(d_ops);
     if (scratch) (void)hipFree(scratch);
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
@@ -112,22 +152,19 @@ bool is_quant_kind(int32_t kind) {
   return fam == ar::kKQEncode || fam == ar::kKQReduce || fam == ar::kKQCopy || fam == ar::kKQDecode;
 }
 
-ar_status_t prepare(ar_plan_t *pl) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (pl->prepared) {
-    if (dev != pl->device) return fail(AR_ERR_INVALID_ARG, "plan was prepared on another device");
-    return AR_OK;
-  }
-  pl->release_device();
-  pl->device = dev;
-  std::vector<ar_dev::DevOp> host_ops;
+std::atomic<uint64_t> g_next_table_id{1};
+
+// Host side of the launches of pl->p (see ar_plan::host_ops).  Called after
+// every change of pl->p; touches no device.
+void lower_launches(ar_plan_t *pl) {
+  pl->host_ops.clear();
   pl->op_offset.clear();
   pl->grid_x.clear();
   pl->cold.clear();
+  pl->launch_err.clear();
+  pl->table_id = g_next_table_id.fetch_add(1);
   for (const ar::Launch &L : pl->p.launches) {
-    pl->op_offset.push_back(static_cast<int64_t>(host_ops.size()));
+    pl->op_offset.push_back(static_cast<int64_t>(pl->host_ops.size()));
     const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
     const bool quant = is_quant_kind(L.kind);
     const bool cold = !quant && !out_scratch && ar::launch_write_bytes(pl->p, L) > pl->p.cache_bytes;
@@ -135,7 +172,7 @@ ar_status_t prepare(ar_plan_t *pl) {
     const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold);
     int64_t gx = 0;
     for (const ar::Op &o : L.ops) {
-      host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
+      pl->host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
       gx = std::max(gx, (o.hi + tile - 1) / tile - o.lo / tile);
     }
     if (!quant) {  // blocks that walk several tiles
@@ -146,13 +183,49 @@ ar_status_t prepare(ar_plan_t *pl) {
     // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
     const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
     if (gx * threads > 0x7fffffff || static_cast<int64_t>(L.ops.size()) > ar::kMaxLaunchOps)
-      return fail(AR_ERR_UNSUPPORTED, "op too large for one launch grid");
-    pl->grid_x.push_back(static_cast<uint32_t>(gx));
+      pl->launch_err = "op too large for one launch grid";
+    pl->grid_x.push_back(static_cast<uint32_t>(std::min<int64_t>(gx, 0x7fffffff)));
   }
+}
+
+// Copies the op table to pl->d_ops on the plan's own stream and waits for it.
+hipError_t upload_ops(ar_plan_t *pl) {
+  hipError_t e = hipSuccess;
+  if (!pl->own_stream) {
+    e = hipStreamCreateWithFlags(&pl->own_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  hipEvent_t done = nullptr;
+  e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(pl->d_ops, pl->host_ops.data(), pl->host_ops.size() * sizeof(ar_dev::DevOp),
+                     hipMemcpyHostToDevice, pl->own_stream);
+  if (e == hipSuccess) e = hipEventRecord(done, pl->own_stream);
+  if (e == hipSuccess) e = hipEventSynchronize(done);
+  (void)hipEventDestroy(done);
+  return e;
+}
+
+ar_status_t prepare(ar_plan_t *pl) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (pl->prepared) {
+    if (dev != pl->device) return fail(AR_ERR_INVALID_ARG, "plan was prepared on another device");
+    return AR_OK;
+  }
+  if (!pl->launch_err.empty()) return fail(AR_ERR_UNSUPPORTED, pl->launch_err);
+  pl->release_device();
+  pl->device = dev;
+  const std::vector<ar_dev::DevOp> &host_ops = pl->host_ops;
   if (!host_ops.empty()) {
     e = hipMalloc(reinterpret_cast<void **>(&pl->d_ops), host_ops.size() * sizeof(ar_dev::DevOp));
     if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("op table allocation: ") + hipGetErrorString(e));
-    e = hipMemcpy(pl->d_ops, host_ops.data(), host_ops.size() * sizeof(ar_dev::DevOp), hipMemcpyHostToDevice);
+    // The upload runs on the plan's own non-blocking stream and is waited for
+    // with an event: a synchronous hipMemcpy goes through the legacy default
+    // stream, which invalidates a graph capture that another host thread has
+    // in progress (hipErrorStreamCaptureImplicit, measured on MI355X).
+    e = upload_ops(pl);
     if (e != hipSuccess) {
       pl->release_device();
       return hip_fail(e, "op table upload");
@@ -187,47 +260,87 @@ ar_status_t prepare(ar_plan_t *pl) {
   return AR_OK;
 }
 
-// Each of the nranks buffers holds `bytes` bytes: non-NULL, 16-byte aligned,
-// pairwise disjoint.
-ar_status_t check_buffers(int n, void *const *bufs, uint64_t bytes, const char *what) {
-  for (int r = 0; r < n; ++r) {
-    const uintptr_t v = reinterpret_cast<uintptr_t>(bufs[r]);
-    if (!v) return fail(AR_ERR_INVALID_ARG, std::string(what) + " " + std::to_string(r) + " is NULL");
-    if (v % 16) return fail(AR_ERR_INVALID_ARG, std::string(what) + " " + std::to_string(r) + " is not 16-byte aligned");
-  }
-  for (int r = 0; r < n; ++r)
-    for (int q = r + 1; q < n; ++q) {
-      const uintptr_t a = reinterpret_cast<uintptr_t>(bufs[r]);
-      const uintptr_t b = reinterpret_cast<uintptr_t>(bufs[q]);
-      if (a < b + bytes && b < a + bytes)
-        return fail(AR_ERR_INVALID_ARG, std::string(what) + "s " + std::to_string(r) + " and " + std::to_string(q) +
-                                            " overlap");
-    }
-  return AR_OK;
-}
-
-ar_status_t check_rank_pointers(const ar_plan_t *pl, void *const *rank_bufs) {
+// Pointer checks of a call: every rank buffer (count elements of the
+// buffer dtype) and every error buffer (count fp32) is non-NULL, 16-byte
+// aligned, and overlaps no other buffer of the call.  Overlap is found by
+// sorting the buffers by address (O(N log N)).  A set that passed is kept on
+// the plan and not checked again, so repeated calls with the same buffers
+// cost N pointer compares.
+ar_status_t check_pointers(ar_plan_t *pl, void *const *rank_bufs, void *const *error_bufs) {
   if (!rank_bufs) return fail(AR_ERR_INVALID_ARG, "rank_bufs is NULL");
-  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::buffer_elem_bytes(pl->p.dtype));
-  if (bytes == 0) return AR_OK;  // nothing is read or written
-  return check_buffers(pl->p.nranks, rank_bufs, bytes, "rank buffer");
+  const int n = pl->p.nranks;
+  const uint64_t rbytes =
+      static_cast<uint64_t>(pl->p.count) * static_cast<uint64_t>(ar::buffer_elem_bytes(pl->p.dtype));
+  if (rbytes == 0) return AR_OK;  // nothing is read or written
+  const uint64_t ebytes = static_cast<uint64_t>(pl->p.count) * 4;
+  std::array<uintptr_t, 2 * ar::kMaxExecRanks> &key = pl->checked;
+  bool same = pl->checked_n == 2 * n;
+  for (int r = 0; same && r < n; ++r)
+    same = key[r] == reinterpret_cast<uintptr_t>(rank_bufs[r]) &&
+           key[n + r] == (error_bufs ? reinterpret_cast<uintptr_t>(error_bufs[r]) : 0);
+  if (same) return AR_OK;
+  struct Extent {
+    uintptr_t lo, hi;
+    int idx;  // rank r, or n + r for error buffer r
+  };
+  std::array<Extent, 2 * ar::kMaxExecRanks> ex;  // on the stack: no allocation on this path
+  const int next = error_bufs ? 2 * n : n;
+  auto name = [n](int idx) {
+    return idx < n ? "rank buffer " + std::to_string(idx) : "error buffer " + std::to_string(idx - n);
+  };
+  for (int k = 0; k < next; ++k) {
+    const uintptr_t v = reinterpret_cast<uintptr_t>(k < n ? rank_bufs[k] : error_bufs[k - n]);
+    if (!v) return fail(AR_ERR_INVALID_ARG, name(k) + " is NULL");
+    if (v % 16) return fail(AR_ERR_INVALID_ARG, name(k) + " is not 16-byte aligned");
+    ex[k] = {v, v + (k < n ? rbytes : ebytes), k};
+  }
+  std::sort(ex.begin(), ex.begin() + next, [](const Extent &a, const Extent &b) { return a.lo < b.lo; });
+  int far = 0;  // the extent reaching furthest among those before i
+  for (int i = 1; i < next; ++i) {
+    if (ex[i].lo < ex[far].hi) {
+      const int a = std::min(ex[far].idx, ex[i].idx), b = std::max(ex[far].idx, ex[i].idx);
+      if (b < n)
+        return fail(AR_ERR_INVALID_ARG, "rank buffers " + std::to_string(a) + " and " + std::to_string(b) + " overlap");
+      if (a >= n)
+        return fail(AR_ERR_INVALID_ARG,
+                    "error buffers " + std::to_string(a - n) + " and " + std::to_string(b - n) + " overlap");
+      return fail(AR_ERR_INVALID_ARG, name(a) + " and " + name(b) + " overlap");
+    }
+    if (ex[i].hi > ex[far].hi) far = i;
+  }
+  for (int r = 0; r < n; ++r) {
+    key[r] = reinterpret_cast<uintptr_t>(rank_bufs[r]);
+    key[n + r] = error_bufs ? reinterpret_cast<uintptr_t>(error_bufs[r]) : 0;
+  }
+  pl->checked_n = 2 * n;
+  return AR_OK;
 }
 
-ar_status_t check_error_pointers(const ar_plan_t *pl, void *const *rank_bufs, void *const *error_bufs) {
-  const int n = pl->p.nranks;
-  const uint64_t bytes = static_cast<uint64_t>(pl->p.count) * 4;
-  if (bytes == 0) return AR_OK;
-  ar_status_t st = check_buffers(n, error_bufs, bytes, "error buffer");
-  if (st != AR_OK) return st;
-  for (int r = 0; r < n; ++r)
-    for (int q = 0; q < n; ++q) {
-      const uintptr_t a = reinterpret_cast<uintptr_t>(rank_bufs[r]);
-      const uintptr_t b = reinterpret_cast<uintptr_t>(error_bufs[q]);
-      if (a < b + bytes && b < a + bytes)
-        return fail(AR_ERR_INVALID_ARG,
-                    "rank buffer " + std::to_string(r) + " and error buffer " + std::to_string(q) + " overlap");
+// Records the completion mark of a call on stream s (after its launches).
+// Nothing is recorded while the caller captures s into a graph of its own:
+// such work runs when the caller launches that graph.
+ar_status_t mark_done(ar_plan_t *pl, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone) return AR_OK;
+  ar_plan_t::DoneMark *m = nullptr;
+  for (ar_plan_t::DoneMark &d : pl->marks)
+    if (d.stream == s) m = &d;
+  if (!m) {
+    if (pl->marks.size() >= ar_plan_t::kMaxMarks) {  // retire the oldest stream's mark
+      (void)hipEventSynchronize(pl->marks.front().event);
+      (void)hipEventDestroy(pl->marks.front().event);
+      pl->marks.erase(pl->marks.begin());
     }
-  return AR_OK;
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    pl->marks.push_back({s, ev});
+    m = &pl->marks.back();
+  }
+  e = hipEventRecord(m->event, s);
+  return e == hipSuccess ? AR_OK : hip_fail(e, "hipEventRecord");
 }
 
 ar_stats_t stats_of(const ar::Plan &p) {
@@ -257,7 +370,7 @@ namespace {
 // Launches every kernel of the plan on s (each timed by its own start and
 // stop events when prof is set).
 ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
-                    bool prof) {
+                    bool prof, const ar_dev::DevOp *table) {
   float *const scratch_base = args.scratch;
   hipEvent_t *ev = nullptr;
   uint8_t *mark = nullptr;
@@ -281,13 +394,21 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
       }
       continue;
     }
+    if (timed && plan->evict_bytes > 0) {
+      // evict the device cache, outside the launch's events: plain loads of
+      // the eviction buffer fill the cache with clean lines, so the timed
+      // launch pays no write-back of an eviction's dirty data
+      const void *src = plan->evict_buf;
+      e = ar_dev::hbm_probe(&src, 1, nullptr, 0, plan->evict_bytes, 2, 0, s);
+      if (e != hipSuccess) return hip_fail(e, "cache eviction read");
+    }
     ar_dev::t_launch_events = timed ? ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]} : ar_dev::LaunchEvents{};
     if (quant) {
-      qargs.ops = plan->d_ops + plan->op_offset[i];
+      qargs.ops = table + plan->op_offset[i];
       qargs.nops = static_cast<int32_t>(L.ops.size());
       e = ar_dev::launch_q(L.kind, grid, qargs, s);
     } else {
-      args.ops = plan->d_ops + plan->op_offset[i];
+      args.ops = table + plan->op_offset[i];
       args.nops = static_cast<int32_t>(L.ops.size());
       // slot index e - shift: the kernels add e to this base (integer
       // arithmetic; every address they form lies inside the scratch)
@@ -321,15 +442,15 @@ ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QAr
       return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
     }
   hipError_t e;
-  if (!plan->capture_stream) {
-    e = hipStreamCreateWithFlags(&plan->capture_stream, hipStreamNonBlocking);
+  if (!plan->own_stream) {
+    e = hipStreamCreateWithFlags(&plan->own_stream, hipStreamNonBlocking);
     if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
   }
-  e = hipStreamBeginCapture(plan->capture_stream, hipStreamCaptureModeThreadLocal);
+  e = hipStreamBeginCapture(plan->own_stream, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-  const ar_status_t st = enqueue(plan, quant, args, qargs, plan->capture_stream, false);
+  const ar_status_t st = enqueue(plan, quant, args, qargs, plan->own_stream, false, plan->d_ops);
   hipGraph_t graph = nullptr;
-  e = hipStreamEndCapture(plan->capture_stream, &graph);
+  e = hipStreamEndCapture(plan->own_stream, &graph);
   if (st != AR_OK) {
     if (graph) (void)hipGraphDestroy(graph);
     return st;
@@ -340,13 +461,50 @@ ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QAr
   (void)hipGraphDestroy(graph);
   if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
   if (plan->graphs.size() >= ar_plan_t::kMaxGraphs) {
-    (void)hipDeviceSynchronize();
+    plan->wait_idle();  // the oldest graph may still be running
     (void)hipGraphExecDestroy(plan->graphs.front().exec);
     plan->graphs.erase(plan->graphs.begin());
   }
   plan->graphs.push_back({std::move(key), exec});
   e = hipGraphLaunch(exec, s);
   return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+// Argument checks shared by the all-reduce calls.
+ar_status_t check_call(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->p.nranks > ar::kMaxExecRanks)
+    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
+  if (error_bufs && plan->p.dtype != ar::kI8EF)
+    return fail(AR_ERR_INVALID_ARG, "error feedback needs an AR_INT8_EF plan");
+  return check_pointers(plan, rank_bufs, error_bufs);
+}
+
+// Kernel arguments of a call: the caller's buffers and the plan's
+// workspace (fp32 partial-sum slots, or the INT8 code slots and scales).
+void fill_args(const ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, float *workspace,
+               ar_dev::KArgs &args, ar_dev::QArgs &qargs) {
+  if (plan->p.dtype == ar::kI8EF) {
+    for (int r = 0; r < plan->p.nranks; ++r) {
+      qargs.grad[r] = static_cast<float *>(rank_bufs[r]);
+      qargs.err[r] = error_bufs ? static_cast<float *>(error_bufs[r]) : nullptr;
+    }
+    char *ws = reinterpret_cast<char *>(workspace);
+    qargs.codes = reinterpret_cast<int8_t *>(ws);
+    qargs.scales = reinterpret_cast<float *>(ws + static_cast<int64_t>(plan->p.nranks) * plan->p.code_stride);
+    qargs.code_stride = plan->p.code_stride;
+    qargs.scale_stride = plan->p.scale_stride;
+    qargs.count = plan->p.count;
+    qargs.has_err = error_bufs != nullptr;
+    qargs.nranks = plan->p.nranks;
+    qargs.group_size = plan->p.group_size;
+  } else {
+    for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
+    args.scratch = workspace;
+    args.slot_stride = plan->p.slot_stride;
+    args.nranks = plan->p.nranks;
+    args.group_size = plan->p.group_size;
+  }
 }
 
 }  // namespace
@@ -375,6 +533,7 @@ ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t d
     fail(unsupported ? AR_ERR_UNSUPPORTED : AR_ERR_INVALID_ARG, err);
     return nullptr;
   }
+  lower_launches(pl);
   g_status = AR_OK;
   return pl;
 }
@@ -385,9 +544,9 @@ ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
-  if (plan->prepared) (void)hipDeviceSynchronize();
-  plan->release_device();
+  plan->release_device();  // waits for the plan's calls in flight
   plan->p = std::move(trial);
+  lower_launches(plan);
   return AR_OK;
 }
 
@@ -398,9 +557,9 @@ ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes) {
   trial.cache_bytes = static_cast<int64_t>(bytes);
   const std::string err = ar::relower(trial, trial.exec);
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
-  if (plan->prepared) (void)hipDeviceSynchronize();
-  plan->release_device();
+  plan->release_device();  // waits for the plan's calls in flight
   plan->p = std::move(trial);
+  lower_launches(plan);
   return AR_OK;
 }
 
@@ -412,50 +571,24 @@ ar_status_t ar_plan_prepare(ar_plan_t *plan) {
 }
 
 ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
-  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->p.nranks > ar::kMaxExecRanks)
-    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
-  const bool quant = plan->p.dtype == ar::kI8EF;
-  if (error_bufs && !quant) return fail(AR_ERR_INVALID_ARG, "error feedback needs an AR_INT8_EF plan");
-  ar_status_t st = check_rank_pointers(plan, rank_bufs);
+  ar_status_t st = check_call(plan, rank_bufs, error_bufs);
   if (st != AR_OK) return st;
-  if (error_bufs) {
-    st = check_error_pointers(plan, rank_bufs, error_bufs);
-    if (st != AR_OK) return st;
-  }
   st = prepare(plan);
   if (st != AR_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool quant = plan->p.dtype == ar::kI8EF;
   ar_dev::KArgs args{};
   ar_dev::QArgs qargs{};
-  if (quant) {
-    for (int r = 0; r < plan->p.nranks; ++r) {
-      qargs.grad[r] = static_cast<float *>(rank_bufs[r]);
-      qargs.err[r] = error_bufs ? static_cast<float *>(error_bufs[r]) : nullptr;
-    }
-    char *ws = reinterpret_cast<char *>(plan->external_scratch ? plan->external_scratch : plan->scratch);
-    qargs.codes = reinterpret_cast<int8_t *>(ws);
-    qargs.scales = reinterpret_cast<float *>(ws + static_cast<int64_t>(plan->p.nranks) * plan->p.code_stride);
-    qargs.code_stride = plan->p.code_stride;
-    qargs.scale_stride = plan->p.scale_stride;
-    qargs.count = plan->p.count;
-    qargs.has_err = error_bufs != nullptr;
-    qargs.nranks = plan->p.nranks;
-    qargs.group_size = plan->p.group_size;
-  } else {
-    for (int r = 0; r < plan->p.nranks; ++r) args.rank[r] = rank_bufs[r];
-    args.scratch = plan->external_scratch ? plan->external_scratch : plan->scratch;
-    args.slot_stride = plan->p.slot_stride;
-    args.nranks = plan->p.nranks;
-    args.group_size = plan->p.group_size;
-  }
+  fill_args(plan, rank_bufs, error_bufs, plan->external_scratch ? plan->external_scratch : plan->scratch, args,
+            qargs);
   const bool prof = plan->prof_calls > 0 && !plan->events.empty();
   // per-launch events need eager launches (event records captured into a
   // graph cannot be timed), so profiling keeps calls eager
   st = plan->use_graph && !prof && !plan->p.launches.empty()
            ? replay(plan, quant, args, qargs, rank_bufs, error_bufs, s)
-           : enqueue(plan, quant, args, qargs, s, prof);
+           : enqueue(plan, quant, args, qargs, s, prof, plan->d_ops);
   if (st == AR_OK && prof) ++plan->prof_logged;
+  if (st == AR_OK && !plan->p.launches.empty()) st = mark_done(plan, s);
   return st;
 }
 
@@ -523,8 +656,8 @@ int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtyp
 
 void ar_plan_destroy(ar_plan_t *plan) {
   if (!plan) return;
-  if (plan->prepared) (void)hipDeviceSynchronize();
   plan->release_device();
+  plan->release_marks();
   delete plan;
 }
 
@@ -597,8 +730,7 @@ ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable) {
 
 ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls) {
   if (!plan || max_calls < 0) return fail(AR_ERR_INVALID_ARG, "bad profiling arguments");
-  if (plan->prepared) (void)hipDeviceSynchronize();
-  plan->release_device();
+  plan->release_device();  // waits for the plan's calls in flight
   plan->prof_calls = max_calls;
   plan->prof_logged = 0;
   return AR_OK;
@@ -608,6 +740,47 @@ ar_status_t ar_plan_set_profiling_period(ar_plan_t *plan, int period) {
   if (!plan || period < 1) return fail(AR_ERR_INVALID_ARG, "bad profiling period");
   plan->prof_period = period;
   return AR_OK;
+}
+
+ar_status_t ar_plan_set_profiling_evict(ar_plan_t *plan, void *buf, size_t bytes) {
+  if (!plan || (bytes > 0 && !buf) || bytes % 16 || bytes > static_cast<size_t>(INT64_MAX))
+    return fail(AR_ERR_INVALID_ARG, "bad eviction buffer");
+  plan->evict_buf = bytes ? buf : nullptr;
+  plan->evict_bytes = static_cast<int64_t>(bytes);
+  return AR_OK;
+}
+
+ar_status_t ar_plan_launch_shape(const ar_plan_t *plan, int32_t i, int32_t *cold, int32_t *units, int32_t *cpol,
+                                 int32_t *batch, uint32_t *grid_x, int32_t *threads) {
+  if (!plan || i < 0 || i >= static_cast<int32_t>(plan->p.launches.size()))
+    return fail(AR_ERR_INVALID_ARG, "bad plan or launch index");
+  const ar::Launch &L = plan->p.launches[i];
+  const bool quant = is_quant_kind(L.kind);
+  const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
+  const ar_dev::KernelShape ks = quant ? ar_dev::KernelShape{0, 0, 0}
+                                       : ar_dev::kernel_shape(L.kind, plan->cold[i] != 0, out_scratch);
+  if (cold) *cold = plan->cold[i];
+  if (units) *units = ks.units;
+  if (cpol) *cpol = ks.cpol;
+  if (batch) *batch = ks.batch;
+  if (grid_x) *grid_x = plan->grid_x[i];
+  if (threads) *threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
+  return AR_OK;
+}
+
+ar_status_t ar_hbm_probe(const void *const *src, int32_t nsrc, void *const *dst, int32_t ndst, size_t bytes,
+                         int32_t units, int32_t policy, void *stream) {
+  if (nsrc < 0 || ndst < 0 || nsrc > ar_dev::kProbeMax || ndst > ar_dev::kProbeMax || (nsrc > 0 && !src) ||
+      (ndst > 0 && !dst) || bytes % 16 || bytes > static_cast<size_t>(INT64_MAX) ||
+      (units != 1 && units != 2 && units != 4) || policy < 0 || policy > 2)
+    return fail(AR_ERR_INVALID_ARG, "bad probe arguments");
+  for (int i = 0; i < nsrc; ++i)
+    if (!src[i] || reinterpret_cast<uintptr_t>(src[i]) % 16) return fail(AR_ERR_INVALID_ARG, "bad probe source");
+  for (int i = 0; i < ndst; ++i)
+    if (!dst[i] || reinterpret_cast<uintptr_t>(dst[i]) % 16) return fail(AR_ERR_INVALID_ARG, "bad probe destination");
+  const hipError_t e = ar_dev::hbm_probe(src, nsrc, dst, ndst, static_cast<int64_t>(bytes), units, policy,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AR_OK : hip_fail(e, "probe launch");
 }
 
 ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n) {
@@ -666,6 +839,7 @@ ar_plan_t *merged_plan(ar_bucket_plan_t *bp) {
     fail(AR_ERR_INVALID_ARG, "batched buckets: " + err);
     return nullptr;
   }
+  lower_launches(m);
   m->use_graph = bp->use_graph;
   bp->merged = m;
   return m;
@@ -760,10 +934,7 @@ ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
     const ar_status_t st = ar_plan_set_exec(pl, exec);
     if (st != AR_OK) return st;
   }
-  if (bp->merged) {
-    (void)hipDeviceSynchronize();  // its launches may still be in flight
-    drop_merged(bp);
-  }
+  drop_merged(bp);  // waits for its launches in flight
   return AR_OK;
 }
 
@@ -773,10 +944,7 @@ ar_status_t ar_bucket_set_cache_bytes(ar_bucket_plan_t *bp, size_t bytes) {
     const ar_status_t st = ar_plan_set_cache_bytes(pl, bytes);
     if (st != AR_OK) return st;
   }
-  if (bp->merged) {
-    (void)hipDeviceSynchronize();  // its launches may still be in flight
-    drop_merged(bp);
-  }
+  drop_merged(bp);  // waits for its launches in flight
   return AR_OK;
 }
 
@@ -838,7 +1006,7 @@ ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arena
   for (ar_plan_t *pl : bp->plans) need = std::max(need, pl->need_scratch_bytes());
   if (need > bp->scratch_bytes) {
     if (bp->scratch) {
-      (void)hipDeviceSynchronize();
+      for (ar_plan_t *pl : bp->plans) pl->wait_idle();  // the buckets that used it
       (void)hipFree(bp->scratch);
       bp->scratch = nullptr;
       bp->scratch_bytes = 0;
@@ -911,12 +1079,9 @@ void ar_bucket_plan_destroy(ar_bucket_plan_t *bp) {
   drop_merged(bp);
   for (ar_plan_t *pl : bp->plans) {
     pl->external_scratch = nullptr;
-    ar_plan_destroy(pl);
+    ar_plan_destroy(pl);  // waits for the bucket's calls
   }
-  if (bp->scratch) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(bp->scratch);
-  }
+  if (bp->scratch) (void)hipFree(bp->scratch);
   delete bp;
 }
 

@@ -7,12 +7,13 @@
 // independent 16-byte loads in flight, and no LDS or MFMA is involved --
 // nothing is reused, so staging through LDS would only add a round trip.
 //
-// Launch geometry: every block takes one tile of one op (one transfer of the
-// step; see block_coord for the block -> (op, tile) order); a tile walks the op's element range in
-// tiles that are aligned to the tile size in absolute element coordinates,
-// so every rank buffer, every scratch slot and every vector access of a tile
-// share the same alignment.  Only the first and last tile of an op can be
-// partial; they take a per-element path.
+// Launch geometry: a block works on one op (one transfer of the step; see
+// block_coord) and walks its element range in tiles that are aligned to the
+// tile size in absolute element coordinates, so every rank buffer, every
+// scratch slot and every vector access of a tile share the same alignment.
+// Only the first and last tile of an op can be cut by its range; there the
+// vector units inside the op still move as vectors and only the units the
+// range cuts go element by element.
 //
 // Summation order.  Each output element is produced by exactly one thread
 // from its inputs in the schedule's order with IEEE binary32 adds (packed
@@ -81,32 +82,15 @@ __device__ __forceinline__ void st_cp(char *ubase, uint32_t off, T v) {
   }
 }
 
-// Block -> (op, tile).  With AR_GRID_INTERLEAVE the ops of a launch are
-// interleaved block by block, so the resident blocks stream from every op at
-// once; otherwise blockIdx.y is the op and blockIdx.x the tile.
-// A block handles tiles tile, tile + stride, ... of its op (grid-stride when
-// the grid is capped by AR_PERSIST_X blocks per op).
+// Block -> (op, tile): blockIdx.y is the op and blockIdx.x the first tile; a
+// block handles tiles tile, tile + stride, ... of its op (the host launches
+// fewer blocks than tiles where a block should walk several).
 struct BlockCoord {
   int op;
   int64_t tile, stride;
 };
-__device__ __forceinline__ BlockCoord block_coord(const KArgs &a) {
-#if AR_GRID_INTERLEAVE
-  return {static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.nops)),
-          static_cast<int64_t>(blockIdx.x / static_cast<uint32_t>(a.nops)),
-          static_cast<int64_t>(gridDim.x / static_cast<uint32_t>(a.nops))};
-#elif AR_XCD_REMAP
-  // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; this
-  // remap hands each XCD one contiguous run of (op, tile) pairs instead.
-  (void)a;
-  const uint32_t total = gridDim.x * gridDim.y;
-  uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
-  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
-  return {static_cast<int>(lin / gridDim.x), static_cast<int64_t>(lin % gridDim.x), static_cast<int64_t>(gridDim.x)};
-#else
-  (void)a;
+__device__ __forceinline__ BlockCoord block_coord() {
   return {static_cast<int>(blockIdx.y), static_cast<int64_t>(blockIdx.x), static_cast<int64_t>(gridDim.x)};
-#endif
 }
 
 __device__ __forceinline__ const char *src_ptr(const KArgs &a, int32_t loc) {
@@ -213,7 +197,7 @@ template <int FLAGS, int UNROLL, int CP>
 __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   const char *A = src_ptr(args, op.a);
@@ -283,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void chunk_copy(KArgs args) {
   constexpr int64_t kPerUnit = 16 / ES;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPerUnit * UNROLL;
   using Elem = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   const char *A = src_ptr(args, op.a);
@@ -443,7 +427,7 @@ __device__ __forceinline__ void store_all1(const KArgs &args, bool bf, int64_t e
 template <bool BF, bool EACH, int UNROLL, int FB>
 __global__ __launch_bounds__(kOPB) void onepass_ring(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
@@ -481,7 +465,7 @@ __global__ __launch_bounds__(kOPB) void onepass_ring(KArgs args) {
 template <bool BF, bool EACH, int UNROLL, int FB>
 __global__ __launch_bounds__(kOPB) void onepass_hier(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
@@ -615,7 +599,7 @@ __global__ __launch_bounds__(kOPB) void onepass_tree(KArgs args) {
   constexpr int kBatch = NMAX < kB ? NMAX : kB;
   constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
   const int n = args.nranks;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
@@ -704,7 +688,7 @@ struct DTreeFold {
 template <bool BF, bool EACH, int N, int UNROLL>
 __global__ __launch_bounds__(kOPB) void onepass_dtree(KArgs args) {
   constexpr int64_t kTile = static_cast<int64_t>(kOPB) * 4 * UNROLL;
-  const BlockCoord bc = block_coord(args);
+  const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const bool second = op.aux != 0;
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
@@ -829,17 +813,116 @@ hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// HBM probe (see hbm_probe): one block per tile of U 16-byte units per
+// thread, sources loaded 8 at a time.  POL 0: plain loads and stores (they
+// allocate in the caches); 1: non-temporal loads, sc1 stores (the step
+// kernels); 2: non-temporal loads and stores (the fp32 one-pass kernels).
+struct ProbeArgs {
+  const char *src[kProbeMax];
+  char *dst[kProbeMax];
+  int32_t nsrc, ndst;
+  int64_t units;  // 16-byte units per buffer
+};
+template <int POL>
+__device__ __forceinline__ f32x4 probe_ld(const char *p) {
+  if constexpr (POL == 0) return *reinterpret_cast<const f32x4 *>(p);
+  else return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+template <int U, int POL>
+__global__ __launch_bounds__(kBlock) void hbm_probe_kernel(ProbeArgs a) {
+  constexpr int kCp = POL == 0 ? 0 : POL == 1 ? 16 : 2;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBlock * U;
+  f32x4 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= a.nsrc; s += 8) {
+    f32x4 x[8][U];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = t0 + static_cast<int64_t>(u) * kBlock + threadIdx.x;
+        x[q][u] = i < a.units ? probe_ld<POL>(a.src[s + q] + i * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] += x[q][u];
+  }
+  for (; s < a.nsrc; ++s)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = t0 + static_cast<int64_t>(u) * kBlock + threadIdx.x;
+      if (i < a.units) acc[u] += probe_ld<POL>(a.src[s] + i * 16);
+    }
+  for (int d = 0; d < a.ndst; ++d)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = t0 + static_cast<int64_t>(u) * kBlock + threadIdx.x;
+      if (i < a.units) st_cp<kCp, f32x4>(a.dst[d] + t0 * 16, static_cast<uint32_t>(i - t0) * 16, acc[u]);
+    }
+  if (a.ndst == 0) {  // keep the loads: their sum is used by an empty asm
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" ::"v"(acc[u].x), "v"(acc[u].y), "v"(acc[u].z), "v"(acc[u].w));
+  }
+}
+
+template <int U>
+void launch_probe(int pol, dim3 grid, const ProbeArgs &a, hipStream_t s) {
+  if (pol == 0) AR_LAUNCH((hbm_probe_kernel<U, 0>), grid, dim3(kBlock), 0, s, a);
+  else if (pol == 1) AR_LAUNCH((hbm_probe_kernel<U, 1>), grid, dim3(kBlock), 0, s, a);
+  else AR_LAUNCH((hbm_probe_kernel<U, 2>), grid, dim3(kBlock), 0, s, a);
+}
 
 }  // namespace
 
-dim3 grid_for(uint32_t tiles, uint32_t nops) {
-  if (AR_PERSIST_X > 0 && tiles > static_cast<uint32_t>(AR_PERSIST_X)) tiles = AR_PERSIST_X;
-#if AR_GRID_INTERLEAVE
-  return dim3(tiles * nops, 1);
-#else
-  return dim3(tiles, nops);
-#endif
+hipError_t hbm_probe(const void *const *src, int nsrc, void *const *dst, int ndst, int64_t bytes, int units,
+                     int policy, hipStream_t s) {
+  if (nsrc < 0 || ndst < 0 || nsrc > kProbeMax || ndst > kProbeMax || bytes < 0 || bytes % 16 || policy < 0 ||
+      policy > 2)
+    return hipErrorInvalidValue;
+  ProbeArgs a{};
+  for (int i = 0; i < nsrc; ++i) a.src[i] = static_cast<const char *>(src[i]);
+  for (int i = 0; i < ndst; ++i) a.dst[i] = static_cast<char *>(dst[i]);
+  a.nsrc = nsrc;
+  a.ndst = ndst;
+  a.units = bytes / 16;
+  const int64_t tile = static_cast<int64_t>(kBlock) * units;
+  const int64_t blocks = (a.units + tile - 1) / tile;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff / kBlock) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  switch (units) {
+    case 1: launch_probe<1>(policy, grid, a, s); break;
+    case 2: launch_probe<2>(policy, grid, a, s); break;
+    case 4: launch_probe<4>(policy, grid, a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
+
+KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch) {
+  switch (kind & 0xF00) {
+    case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0};
+    case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0};
+    case kKindRing:
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchBF16}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32};
+    case kKindHier:
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchHierBF16}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32};
+    case kKindTree:
+      return (kind & 3) ? KernelShape{kTreeUnrollBF16, kCpolOnePassBF16, kTreeBatchBF16}
+                        : KernelShape{kTreeUnrollF32, kCpolOnePassF32, kTreeBatchF32};
+    case kKindDTree:
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, 0}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, 0};
+  }
+  return {0, 0, 0};
+}
+
+dim3 grid_for(uint32_t tiles, uint32_t nops) { return dim3(tiles, nops); }
 
 int block_threads(int32_t kind) {
   const int32_t fam = kind & 0xF00;

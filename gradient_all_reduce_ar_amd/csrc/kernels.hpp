@@ -8,15 +8,6 @@
 
 #include "plan.hpp"
 
-#ifndef AR_PERSIST_X
-#define AR_PERSIST_X 0  // > 0: at most this many blocks per op, each looping over tiles
-#endif
-#ifndef AR_XCD_REMAP
-#define AR_XCD_REMAP 0
-#endif
-#ifndef AR_GRID_INTERLEAVE
-#define AR_GRID_INTERLEAVE 0
-#endif
 #ifndef AR_BLOCK
 #define AR_BLOCK 256
 #endif
@@ -184,6 +175,27 @@ int64_t tiles_per_block(int32_t kind, int32_t nranks);
 
 // Grid of a launch whose ops span at most `tiles` tiles each.
 dim3 grid_for(uint32_t tiles, uint32_t nops);
+
+// Template shape of the kernel a launch of `kind` runs: units each thread
+// moves per tile (16-byte fp32 or 8-byte bf16 units), the store cache
+// policy (bits of the store instruction: 2 nt, 16 sc1) and, for the
+// one-pass folds, the ranks whose loads are in flight together (0 for the
+// step kernels).
+struct KernelShape {
+  int units, cpol, batch;
+};
+KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch);
+
+// HBM probe: over `bytes` of every buffer (a multiple of 16), each 16-byte
+// unit of every destination receives the fp32 sum of that unit of every
+// source (nsrc = 0: zeros, a fill; ndst = 0: reads only).  units: 1, 2 or 4
+// 16-byte units per thread per tile.  policy 0: plain loads and stores (they
+// allocate in the caches); 1: non-temporal loads and sc1 stores (the step
+// kernels); 2: non-temporal loads and stores (the fp32 one-pass kernels).
+// Up to kProbeMax buffers of each kind.
+constexpr int kProbeMax = 64;
+hipError_t hbm_probe(const void *const *src, int nsrc, void *const *dst, int ndst, int64_t bytes, int units,
+                     int policy, hipStream_t s);
 
 // Launches the kernel of `kind` on stream s.  out_scratch: the launch's
 // outputs are fp32 scratch slots (selects the store cache policy); cold: the

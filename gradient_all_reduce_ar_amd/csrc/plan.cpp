@@ -385,7 +385,10 @@ std::vector<Transfer> launch_order(const Plan &p, std::vector<LaunchKey> &keys) 
       idx.push_back({LaunchKey{b.second, 0, x.step}, x});
       continue;
     }
-    // piece boundaries on multiples of 64 units (whole tiles stay whole)
+    // piece boundaries on multiples of 64 units: 256-byte aligned for every
+    // operand dtype.  A boundary may still fall inside a kernel tile (1024 to
+    // 4096 elements); that tile's units inside the piece still move as
+    // vectors, so a cut costs one partial tile per op.
     for (int q = 0; q < k; ++q) {
       Transfer y = x;
       y.lo = std::max(x.lo, (p.units * q / k) / 64 * 64);

@@ -167,15 +167,23 @@ ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec);
 
 /*
  * The device cache capacity (bytes) the plan's launch order and kernel
- * shapes assume; default 256 MiB, MI355X's Infinity Cache.  A step launch
- * that writes more than this into rank buffers takes the streaming kernel
- * shape; the hierarchical schedule runs its two group phases group by
- * group (all rounds of group 0, then group 1, ...) when one round of a phase
- * would write more than this, and the other schedules cut the element range
- * into the fewest pieces (the same offsets on every rank) whose rounds write
- * at most this and run the whole schedule piece after piece, so that each
- * round's output is still cached when the next round reads it.  Results are
- * bit-identical for any value.  Host only.
+ * shapes assume; default 256 MiB, MI355X's Infinity Cache.  Every round of a
+ * schedule writes what the next round of its chain reads (Primer ch. 4
+ * sections 4.2-4.4: each step forwards what the previous one produced), and
+ * that output is still cached only if it fits:
+ *   - a step launch that writes more than this into rank buffers takes the
+ *     streaming kernel shape;
+ *   - the hierarchical schedule runs its two group phases group by group
+ *     (all rounds of group 0, then group 1, ...) when one round of a phase
+ *     would write more than this;
+ *   - then, for every schedule, a launch round whose output still exceeds
+ *     this runs together with the next round of its chain (the round that
+ *     reads it; the last reduce round also with the copy round fused into
+ *     it) as one block, and the block runs piece by piece: the element
+ *     range is cut into the fewest pieces (multiples of 64 elements, the
+ *     same offsets on every rank) whose rounds write at most this.  The
+ *     other rounds run whole.
+ * Results are bit-identical for any value.  Host only.
  */
 ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes);
 
@@ -261,7 +269,11 @@ double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t 
 int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtype,
                        const ar_cost_params_t *params, uint32_t candidates, double *best_s);
 
-/* Releases the plan and its device memory (synchronises the device first). */
+/* Releases the plan and its device memory, after waiting for the plan's own
+ * calls in flight (ar_allreduce / ar_allreduce_ef / the bucket calls; each
+ * call records an event on its stream, except while the caller captures that
+ * stream into a graph of its own -- such work the caller finishes before
+ * destroying the plan). */
 void ar_plan_destroy(ar_plan_t *plan);
 
 /* Thread-local message and status of the last failing call. */
@@ -292,6 +304,15 @@ int32_t ar_plan_num_launches(const ar_plan_t *plan);
 ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);
 ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, int64_t *hi,
                                int32_t *a, int32_t *b, int32_t *o, int32_t *o2, int32_t *aux);
+/* Kernel shape of launch i: *cold = 1 for the streaming shape (the launch
+ * writes more into rank buffers than the assumed device cache), the units
+ * each thread moves per tile (16-byte fp32 or 8-byte bf16 units), the store
+ * cache policy (bits of the store instruction: 2 non-temporal, 16 sc1), the
+ * ranks a one-pass fold loads together (0 for step kernels), the workgroups
+ * along the tiles and the threads per workgroup (INT8 kernels: units, cpol
+ * and batch 0).  Host only. */
+ar_status_t ar_plan_launch_shape(const ar_plan_t *plan, int32_t i, int32_t *cold, int32_t *units, int32_t *cpol,
+                                 int32_t *batch, uint32_t *grid_x, int32_t *threads);
 /* fp32 scratch addressing of launch i: element e of slot s is float
  * s * slot_stride + e - shift of the scratch.  shift is 0 except in a
  * batched bucket plan, whose batches reuse the slots one after another
@@ -328,12 +349,39 @@ ar_status_t ar_plan_set_profiling(ar_plan_t *plan, int max_calls);
  * every launch is timed once).  Default 1: every launch.  Host only. */
 ar_status_t ar_plan_set_profiling_period(ar_plan_t *plan, int period);
 
+/* Cold-cache timing: with bytes > 0, every launch that the profiling log
+ * times is preceded on the call's stream by a kernel that reads `bytes` of
+ * buf with plain (cache-allocating) loads (device memory the caller owns,
+ * 16-byte aligned, a multiple of 16 bytes; make it several times the device
+ * cache, e.g. 1 GiB), so that the timed launch finds none of its inputs in
+ * the cache (MI355X's 256 MB Infinity Cache) and no dirty lines to write
+ * back.  The read runs outside the launch's own start and stop events.
+ * bytes = 0 (default) turns it off.  Results are unchanged.  Host only. */
+ar_status_t ar_plan_set_profiling_evict(ar_plan_t *plan, void *buf, size_t bytes);
+
 /* Durations in ms of every launch of the logged calls, oldest call first:
  * ms[c * launches + i] is launch i of logged call c, from the kernel's start
  * to its end, or -1 if the profiling period left it untimed.  The caller must have
  * synchronised the stream.  *n receives calls * launches; the log is then
  * cleared. */
 ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_t *n);
+
+/*
+ * HBM probe, the attainable-bandwidth reference of the kernels above (Primer
+ * ch. 4 section 4.8 judges a collective against what its path can carry):
+ * over `bytes` of every buffer (16-byte aligned pointers, bytes a multiple of
+ * 16), each 16-byte unit of each of the ndst destinations receives the fp32
+ * sum of that unit of the nsrc sources, with the access pattern of the step
+ * kernels (`units` 16-byte units per thread per tile, 1, 2 or 4).  policy 0:
+ * plain loads and stores (they allocate in the device caches); 1:
+ * non-temporal loads and sc1 stores (the step kernels' policy); 2:
+ * non-temporal loads and stores (the fp32 one-pass kernels').  nsrc = 1,
+ * ndst = 1 is a copy; 2, 1 a reduce step's mix; 0, 1 a fill (writes zeros);
+ * k, 0 only reads.  At most 64 buffers of each kind; a destination may equal
+ * a source (in place).  Enqueued on `stream`.
+ */
+ar_status_t ar_hbm_probe(const void *const *src, int32_t nsrc, void *const *dst, int32_t ndst, size_t bytes,
+                         int32_t units, int32_t policy, void *stream);
 
 /* ---- Bucket fuser (Scaling ML systems ch. 06, "Bucket fusion") ----
  *
