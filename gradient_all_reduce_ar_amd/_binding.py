@@ -20,6 +20,7 @@ AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER, AR_RECURSIVE_DOUBLING, AR_TREE, AR_DO
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
 AR_MAX_RANKS = 64
 AR_MAX_PLAN_RANKS = 1024
+AR_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH_STEP, "int8_ef": AR_INT8_EF}
 SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER,
@@ -87,6 +88,7 @@ def _declare(L):
         "ar_plan_prepare": ([P], ctypes.c_int),
         "ar_allreduce": ([P, P, P], ctypes.c_int),
         "ar_allreduce_ef": ([P, P, P, P], ctypes.c_int),
+        "ar_allreduce_noalloc": ([P, P, P, P], ctypes.c_int),
         "ar_plan_stats": ([P], ar_stats_t),
         "ar_plan_cost_alpha_beta": ([P, dbl, dbl, dbl], dbl),
         "ar_plan_cost_alpha_beta_ex": ([P, ctypes.POINTER(ar_cost_params_t)], dbl),
@@ -248,6 +250,19 @@ def ar_allreduce_ef(plan, rank_bufs, error_bufs, stream=None):
     arr = _ptr_array(rank_bufs)
     err = ctypes.cast(_ptr_array(error_bufs), ctypes.c_void_p) if error_bufs is not None else None
     _check(lib().ar_allreduce_ef(plan, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream)))
+
+
+def ar_allreduce_noalloc(plan, rank_bufs, error_bufs=None, stream=None):
+    """The all-reduce with its device workspace in the library's fixed array
+    (AR_NOALLOC_SCRATCH_BYTES per GPU): allocates nothing."""
+    if plan:
+        n, nbytes, ebytes = _plan_extent(plan)
+        _check_bufs(rank_bufs, n, nbytes, "rank buffer")
+        if error_bufs is not None:
+            _check_bufs(error_bufs, n, ebytes, "error buffer")
+    arr = _ptr_array(rank_bufs)
+    err = ctypes.cast(_ptr_array(error_bufs), ctypes.c_void_p) if error_bufs is not None else None
+    _check(lib().ar_allreduce_noalloc(plan, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream)))
 
 
 def ar_plan_stats(plan):

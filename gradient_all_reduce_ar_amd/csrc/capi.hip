@@ -14,6 +14,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -507,6 +508,43 @@ void fill_args(const ar_plan_t *plan, void *const *rank_bufs, void *const *error
   }
 }
 
+// ---- Allocation-free calls (ar_allreduce_noalloc) ----
+//
+// Their device workspace is `scratch`, a file-scope device array that each
+// GPU holds from the library's load until the process ends: the op table of
+// the plan last run on that GPU at its start, then the plan's fp32 partial
+// sums or INT8 code slots (256-byte aligned).  In host code `scratch` names
+// a host-side stand-in, not the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[AR_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_noalloc_mu;
+char *g_noalloc_base[kMaxDevices];                   // per device: the address of `scratch`
+std::atomic<uint64_t> g_noalloc_owner[kMaxDevices];  // per device: table_id of the op table held, 0 none
+
+// Device address of `scratch` on device dev (looked up on the first call
+// there, with dev current).
+ar_status_t noalloc_base(int dev, char **base) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(AR_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_base[dev]) {
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the allocation-free scratch");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256)
+      return fail(AR_ERR_HIP, "allocation-free scratch has no 256-byte aligned device address");
+    g_noalloc_base[dev] = static_cast<char *>(ptr);
+  }
+  *base = g_noalloc_base[dev];
+  return AR_OK;
+}
+
+// Bytes of the op table at the start of the array (a multiple of 256).
+uint64_t noalloc_table_bytes(const ar_plan_t *plan) {
+  return (plan->host_ops.size() * sizeof(ar_dev::DevOp) + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -590,6 +628,44 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
   if (st == AR_OK && prof) ++plan->prof_logged;
   if (st == AR_OK && !plan->p.launches.empty()) st = mark_done(plan, s);
   return st;
+}
+
+ar_status_t ar_allreduce_noalloc(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
+  ar_status_t st = check_call(plan, rank_bufs, error_bufs);
+  if (st != AR_OK) return st;
+  if (!plan->launch_err.empty()) return fail(AR_ERR_UNSUPPORTED, plan->launch_err);
+  const uint64_t table_bytes = noalloc_table_bytes(plan);
+  const uint64_t need = table_bytes + ar::workspace_bytes(plan->p);
+  if (need > AR_NOALLOC_SCRATCH_BYTES)
+    return fail(AR_ERR_INVALID_ARG, "plan needs " + std::to_string(need) +
+                                        " bytes of device workspace (op table and scratch); the allocation-free "
+                                        "call holds at most " + std::to_string(AR_NOALLOC_SCRATCH_BYTES));
+  if (plan->p.launches.empty() || plan->p.count == 0) return AR_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  char *base = nullptr;
+  st = noalloc_base(dev, &base);
+  if (st != AR_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto *table = reinterpret_cast<ar_dev::DevOp *>(base);
+  // The op table is written (by kernels whose arguments carry the ops) when
+  // another plan's table is in the array, and always while the caller
+  // captures s into a graph, so that the graph carries it.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone || g_noalloc_owner[dev].load() != plan->table_id) {
+    g_noalloc_owner[dev].store(0);
+    e = ar_dev::write_ops(table, plan->host_ops.data(), static_cast<int64_t>(plan->host_ops.size()), s);
+    if (e != hipSuccess) return hip_fail(e, "op table write");
+    g_noalloc_owner[dev].store(plan->table_id);
+  }
+  const bool quant = plan->p.dtype == ar::kI8EF;
+  ar_dev::KArgs args{};
+  ar_dev::QArgs qargs{};
+  fill_args(plan, rank_bufs, error_bufs, reinterpret_cast<float *>(base + table_bytes), args, qargs);
+  return enqueue(plan, quant, args, qargs, s, false, table);
 }
 
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {

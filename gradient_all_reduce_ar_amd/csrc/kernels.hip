@@ -875,7 +875,31 @@ void launch_probe(int pol, dim3 grid, const ProbeArgs &a, hipStream_t s) {
   else AR_LAUNCH((hbm_probe_kernel<U, 2>), grid, dim3(kBlock), 0, s, a);
 }
 
+// Op-table writer: up to kOpsPerWrite ops travel by value in the kernel
+// arguments (1.9 KiB) and thread i stores op i.
+constexpr int kOpsPerWrite = 48;
+struct OpBatch {
+  DevOp ops[kOpsPerWrite];
+  int32_t n;
+};
+__global__ __launch_bounds__(64) void write_op_table(DevOp *dst, OpBatch b) {
+  const int i = static_cast<int>(threadIdx.x);
+  if (i < b.n) dst[i] = b.ops[i];
+}
+
 }  // namespace
+
+hipError_t write_ops(DevOp *dst, const DevOp *src, int64_t n, hipStream_t s) {
+  for (int64_t k = 0; k < n; k += kOpsPerWrite) {
+    OpBatch b;
+    b.n = static_cast<int32_t>(std::min<int64_t>(kOpsPerWrite, n - k));
+    for (int32_t i = 0; i < b.n; ++i) b.ops[i] = src[k + i];
+    hipLaunchKernelGGL(write_op_table, dim3(1), dim3(64), 0, s, dst + k, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t hbm_probe(const void *const *src, int nsrc, void *const *dst, int ndst, int64_t bytes, int units,
                      int policy, hipStream_t s) {

@@ -176,6 +176,11 @@ int64_t tiles_per_block(int32_t kind, int32_t nranks);
 // Grid of a launch whose ops span at most `tiles` tiles each.
 dim3 grid_for(uint32_t tiles, uint32_t nops);
 
+// Writes the n ops at src (host memory) into the device op table at dst with
+// kernels whose arguments carry the ops (no copy engine, no staging memory;
+// a stream capture records them as kernel nodes).
+hipError_t write_ops(DevOp *dst, const DevOp *src, int64_t n, hipStream_t s);
+
 // Template shape of the kernel a launch of `kind` runs: units each thread
 // moves per tile (16-byte fp32 or 8-byte bf16 units), the store cache
 // policy (bits of the store instruction: 2 nt, 16 sc1) and, for the

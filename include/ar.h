@@ -269,11 +269,45 @@ double ar_plan_cost_alpha_beta_ex(const ar_plan_t *plan, const ar_cost_params_t 
 int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtype,
                        const ar_cost_params_t *params, uint32_t candidates, double *best_s);
 
+/*
+ * All-reduce that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, checks and results as ar_allreduce_ef
+ * (error_bufs == NULL for every dtype but AR_INT8_EF with error feedback);
+ * bit-identical to ar_allreduce / ar_allreduce_ef on the same plan.
+ *
+ * The plan's device workspace -- its op table, then its fp32 partial sums
+ * (AR_BFLOAT16) or INT8 code slots (AR_INT8_EF) -- lives in one array of
+ * AR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * from its load until the process ends, instead of in memory the plan
+ * allocates; the call never allocates or frees device memory, creates no
+ * event and copies nothing through the copy engines.  The op table is written
+ * into the array by small kernel launches when the array holds another
+ * plan's table (and always while `stream` is being captured, so a captured
+ * graph carries it); no part of the array needs to start at zero.
+ *
+ * All calls on one GPU share its array and leave their contents in it:
+ * allocation-free calls that overlap in time on one GPU race, whatever their
+ * plans and streams (run them in one stream or order them), and a captured
+ * graph of this call must not overlap another allocation-free call on that
+ * GPU either.  Graph replay (ar_plan_set_graph) and the profiling log do not
+ * apply: the launches are enqueued eagerly on `stream`.  Destroying or
+ * re-moding the plan does not wait for these calls: synchronise `stream`
+ * first.
+ *
+ * Errors: as ar_allreduce_ef; AR_ERR_INVALID_ARG (before any device work)
+ * when the op table (40 bytes per op, rounded up to 256) plus the workspace
+ * (ar_plan_stats().scratch_bytes) exceed AR_NOALLOC_SCRATCH_BYTES, e.g. a bf16
+ * ring plan of more than about 16.7 M elements per rank.
+ */
+#define AR_NOALLOC_SCRATCH_BYTES (64ull << 20)
+ar_status_t ar_allreduce_noalloc(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream);
+
 /* Releases the plan and its device memory, after waiting for the plan's own
  * calls in flight (ar_allreduce / ar_allreduce_ef / the bucket calls; each
  * call records an event on its stream, except while the caller captures that
- * stream into a graph of its own -- such work the caller finishes before
- * destroying the plan). */
+ * stream into a graph of its own -- such work, and allocation-free calls,
+ * the caller finishes before destroying the plan). */
 void ar_plan_destroy(ar_plan_t *plan);
 
 /* Thread-local message and status of the last failing call. */
