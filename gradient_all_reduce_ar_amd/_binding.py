@@ -265,6 +265,30 @@ def ar_allreduce_noalloc(plan, rank_bufs, error_bufs=None, stream=None):
     _check(lib().ar_allreduce_noalloc(plan, ctypes.cast(arr, ctypes.c_void_p), err, _stream(stream)))
 
 
+def prepared_call(plan, rank_bufs, error_bufs=None, stream=None, noalloc=False):
+    """A zero-argument callable that runs ar_allreduce_ef (or, with noalloc,
+    ar_allreduce_noalloc) on these buffers: the arguments are checked and
+    marshalled once, for loops that repeat the same call.  The tensors must
+    keep their storage while the callable is used (it holds references to
+    them)."""
+    n, nbytes, ebytes = _plan_extent(plan)
+    _check_bufs(rank_bufs, n, nbytes, "rank buffer")
+    if error_bufs is not None:
+        _check_bufs(error_bufs, n, ebytes, "error buffer")
+    arr = ctypes.cast(_ptr_array(rank_bufs), ctypes.c_void_p)
+    err = ctypes.cast(_ptr_array(error_bufs), ctypes.c_void_p) if error_bufs is not None else None
+    fn = lib().ar_allreduce_noalloc if noalloc else lib().ar_allreduce_ef
+    st = _stream(stream)
+    keep = (list(rank_bufs), None if error_bufs is None else list(error_bufs), arr, err)
+
+    def call():
+        if fn(plan, arr, err, st) != AR_OK:
+            _raise()
+
+    call.keep = keep
+    return call
+
+
 def ar_plan_stats(plan):
     s = lib().ar_plan_stats(plan)
     return s.to_dict()

@@ -317,31 +317,34 @@ ar_status_t check_pointers(ar_plan_t *pl, void *const *rank_bufs, void *const *e
   return AR_OK;
 }
 
-// Records the completion mark of a call on stream s (after its launches).
-// Nothing is recorded while the caller captures s into a graph of its own:
-// such work runs when the caller launches that graph.
-ar_status_t mark_done(ar_plan_t *pl, hipStream_t s) {
+// The completion mark of stream s: the event a call on s records after its
+// last launch (see enqueue and replay), created on the plan's first call on
+// s.  *ev = NULL while the caller captures s into a graph of its own: such
+// work runs when the caller launches that graph.  The event is created with
+// timing so that a kernel dispatch can record it.
+ar_status_t done_mark(ar_plan_t *pl, hipStream_t s, hipEvent_t *ev) {
+  *ev = nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(s, &cs);
   if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
   if (cs != hipStreamCaptureStatusNone) return AR_OK;
-  ar_plan_t::DoneMark *m = nullptr;
   for (ar_plan_t::DoneMark &d : pl->marks)
-    if (d.stream == s) m = &d;
-  if (!m) {
-    if (pl->marks.size() >= ar_plan_t::kMaxMarks) {  // retire the oldest stream's mark
-      (void)hipEventSynchronize(pl->marks.front().event);
-      (void)hipEventDestroy(pl->marks.front().event);
-      pl->marks.erase(pl->marks.begin());
+    if (d.stream == s) {
+      *ev = d.event;
+      return AR_OK;
     }
-    hipEvent_t ev = nullptr;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-    pl->marks.push_back({s, ev});
-    m = &pl->marks.back();
+  if (pl->marks.size() >= ar_plan_t::kMaxMarks) {  // retire the oldest stream's mark
+    (void)hipEventSynchronize(pl->marks.front().event);
+    (void)hipEventDestroy(pl->marks.front().event);
+    pl->marks.erase(pl->marks.begin());
   }
-  e = hipEventRecord(m->event, s);
-  return e == hipSuccess ? AR_OK : hip_fail(e, "hipEventRecord");
+  e = hipEventCreate(ev);
+  if (e != hipSuccess) {
+    *ev = nullptr;
+    return hip_fail(e, "hipEventCreate");
+  }
+  pl->marks.push_back({s, *ev});
+  return AR_OK;
 }
 
 ar_stats_t stats_of(const ar::Plan &p) {
@@ -370,9 +373,16 @@ namespace {
 
 // Launches every kernel of the plan on s (each timed by its own start and
 // stop events when prof is set).
+// done (if not NULL) is recorded when the call's last kernel ends: by that
+// kernel's own dispatch (no packet of its own), or after it when the kernel
+// is timed or nothing is launched.
 ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, hipStream_t s,
-                    bool prof, const ar_dev::DevOp *table) {
+                    bool prof, const ar_dev::DevOp *table, hipEvent_t done) {
   float *const scratch_base = args.scratch;
+  size_t last = plan->p.launches.size();  // the last launch with work
+  for (size_t i = 0; i < plan->p.launches.size(); ++i)
+    if (plan->grid_x[i] > 0 && !plan->p.launches[i].ops.empty()) last = i;
+  bool marked = false;
   hipEvent_t *ev = nullptr;
   uint8_t *mark = nullptr;
   const int64_t call = plan->prof_logged;
@@ -396,14 +406,17 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
       continue;
     }
     if (timed && plan->evict_bytes > 0) {
-      // evict the device cache, outside the launch's events: plain loads of
-      // the eviction buffer fill the cache with clean lines, so the timed
-      // launch pays no write-back of an eviction's dirty data
-      const void *src = plan->evict_buf;
-      e = ar_dev::hbm_probe(&src, 1, nullptr, 0, plan->evict_bytes, 2, 0, s);
-      if (e != hipSuccess) return hip_fail(e, "cache eviction read");
+      // evict the device cache, outside the launch's events, with plain
+      // stores: on MI355X only stores allocate in the Infinity Cache (a read
+      // or a non-temporal fill of 1 GiB left the next launch's time
+      // unchanged; a plain-store fill did not)
+      e = ar_dev::hbm_probe(nullptr, 0, &plan->evict_buf, 1, plan->evict_bytes, 2, 0, s);
+      if (e != hipSuccess) return hip_fail(e, "cache eviction write");
     }
-    ar_dev::t_launch_events = timed ? ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]} : ar_dev::LaunchEvents{};
+    if (timed) ar_dev::t_launch_events = ar_dev::LaunchEvents{ev[2 * i], ev[2 * i + 1]};
+    else if (i == last && done) ar_dev::t_launch_events = ar_dev::LaunchEvents{nullptr, done};
+    else ar_dev::t_launch_events = ar_dev::LaunchEvents{};
+    marked = marked || (i == last && done && !timed);
     if (quant) {
       qargs.ops = table + plan->op_offset[i];
       qargs.nops = static_cast<int32_t>(L.ops.size());
@@ -421,6 +434,10 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
     ar_dev::t_launch_events = ar_dev::LaunchEvents{};
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
   }
+  if (done && !marked) {
+    const hipError_t e = hipEventRecord(done, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
   return AR_OK;
 }
 
@@ -429,7 +446,7 @@ ar_status_t enqueue(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QA
 // set of buffer pointers into a HIP graph and replayed with one launch.  The
 // graph holds kernel nodes only (no memset or copy nodes).
 ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QArgs &qargs, void *const *rank_bufs,
-                   void *const *error_bufs, hipStream_t s) {
+                   void *const *error_bufs, hipStream_t s, hipEvent_t mark) {
   std::vector<uintptr_t> key;
   const int n = plan->p.nranks;
   key.reserve(2 * n + 2);
@@ -440,6 +457,7 @@ ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QAr
   for (ar_plan_t::GraphEntry &g : plan->graphs)
     if (g.key == key) {
       hipError_t e = hipGraphLaunch(g.exec, s);
+      if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
       return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
     }
   hipError_t e;
@@ -449,7 +467,7 @@ ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QAr
   }
   e = hipStreamBeginCapture(plan->own_stream, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-  const ar_status_t st = enqueue(plan, quant, args, qargs, plan->own_stream, false, plan->d_ops);
+  const ar_status_t st = enqueue(plan, quant, args, qargs, plan->own_stream, false, plan->d_ops, nullptr);
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(plan->own_stream, &graph);
   if (st != AR_OK) {
@@ -468,6 +486,7 @@ ar_status_t replay(ar_plan_t *plan, bool quant, ar_dev::KArgs &args, ar_dev::QAr
   }
   plan->graphs.push_back({std::move(key), exec});
   e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
   return e == hipSuccess ? AR_OK : hip_fail(e, "hipGraphLaunch");
 }
 
@@ -620,13 +639,17 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
   fill_args(plan, rank_bufs, error_bufs, plan->external_scratch ? plan->external_scratch : plan->scratch, args,
             qargs);
   const bool prof = plan->prof_calls > 0 && !plan->events.empty();
+  hipEvent_t mark = nullptr;
+  if (!plan->p.launches.empty()) {
+    st = done_mark(plan, s, &mark);
+    if (st != AR_OK) return st;
+  }
   // per-launch events need eager launches (event records captured into a
   // graph cannot be timed), so profiling keeps calls eager
   st = plan->use_graph && !prof && !plan->p.launches.empty()
-           ? replay(plan, quant, args, qargs, rank_bufs, error_bufs, s)
-           : enqueue(plan, quant, args, qargs, s, prof, plan->d_ops);
+           ? replay(plan, quant, args, qargs, rank_bufs, error_bufs, s, mark)
+           : enqueue(plan, quant, args, qargs, s, prof, plan->d_ops, mark);
   if (st == AR_OK && prof) ++plan->prof_logged;
-  if (st == AR_OK && !plan->p.launches.empty()) st = mark_done(plan, s);
   return st;
 }
 
@@ -665,7 +688,7 @@ ar_status_t ar_allreduce_noalloc(ar_plan_t *plan, void *const *rank_bufs, void *
   ar_dev::KArgs args{};
   ar_dev::QArgs qargs{};
   fill_args(plan, rank_bufs, error_bufs, reinterpret_cast<float *>(base + table_bytes), args, qargs);
-  return enqueue(plan, quant, args, qargs, s, false, table);
+  return enqueue(plan, quant, args, qargs, s, false, table, nullptr);
 }
 
 ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
