@@ -12,9 +12,11 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libar.so")
+# AR_LIB names another build of the same sources (the sanitizer build of the
+# CPU tests); there is no other implementation to fall back to.
+LIB_PATH = os.environ.get("AR_LIB") or os.path.join(_HERE, "libar.so")
 
-AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP = range(5)
+AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_OOM, AR_ERR_HIP, AR_ERR_GUARD = range(6)
 AR_FLOAT32, AR_BFLOAT16, AR_BFLOAT16_EACH_STEP, AR_INT8_EF = 0, 1, 2, 3
 AR_RING, AR_HIERARCHICAL, AR_RABENSEIFNER, AR_RECURSIVE_DOUBLING, AR_TREE, AR_DOUBLE_TREE = range(6)
 AR_EXEC_STEPS, AR_EXEC_STEPS_UNFUSED, AR_EXEC_ONEPASS = 0, 1, 2
@@ -105,6 +107,11 @@ def _declare(L):
         "ar_plan_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_profiling_period": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_set_profiling_evict": ([P, P, sz], ctypes.c_int),
+        "ar_plan_describe": ([P, ctypes.c_char_p, sz], i64),
+        "ar_plan_set_guard": ([P, sz], ctypes.c_int),
+        "ar_plan_check_guards": ([P], ctypes.c_int),
+        "ar_bucket_set_guard": ([P, sz], ctypes.c_int),
+        "ar_bucket_check_guards": ([P], ctypes.c_int),
         "ar_plan_launch_shape": ([P, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(ctypes.c_uint32), pi32],
                                  ctypes.c_int),
         "ar_hbm_probe": ([P, i32, P, i32, sz, i32, i32, P], ctypes.c_int),
@@ -391,6 +398,35 @@ def ar_plan_set_profiling(plan, max_calls):
 
 def ar_plan_set_profiling_period(plan, period):
     _check(lib().ar_plan_set_profiling_period(plan, int(period)))
+
+
+def ar_plan_describe(plan):
+    """The plan's configuration, step list and launches (with mean launch
+    times from the profiling log) as a dict."""
+    import json
+
+    n = lib().ar_plan_describe(plan, None, 0)
+    if n < 0:
+        _raise()
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().ar_plan_describe(plan, buf, n + 1)
+    return json.loads(buf.value.decode())
+
+
+def ar_plan_set_guard(plan, nbytes):
+    _check(lib().ar_plan_set_guard(plan, int(nbytes)))
+
+
+def ar_plan_check_guards(plan):
+    _check(lib().ar_plan_check_guards(plan))
+
+
+def ar_bucket_set_guard(bp, nbytes):
+    _check(lib().ar_bucket_set_guard(bp, int(nbytes)))
+
+
+def ar_bucket_check_guards(bp):
+    _check(lib().ar_bucket_check_guards(bp))
 
 
 def ar_plan_set_profiling_evict(plan, buf, nbytes):

@@ -6,6 +6,12 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (device code unchanged), for the CPU tests of the planner and the C ABI.
+# Load it with AR_LIB=<path> and the clang ASan runtime preloaded.
+LIB_SANITIZED = os.path.join(HERE, "libar_sanitized.so")
+SANITIZE_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined " \
+                 "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer".split()
 SOURCES = ["plan.cpp", "kernels.hip", "qkernels.hip", "capi.hip"]
 
 # -ffp-contract=off and no fast-math: every add is one IEEE binary32 add.
@@ -21,13 +27,14 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(out=LIB, defines=(), verbose=False):
+def build(out=LIB, defines=(), verbose=False, sanitize=False):
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     objs = []
     tmpdir = os.path.join(HERE, "_build")
     os.makedirs(tmpdir, exist_ok=True)
     defs = [f"-D{d}" for d in defines]
-    cmd = [hipcc, *HIPCC_FLAGS, *defs, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+    san = SANITIZE_FLAGS if sanitize else []
+    cmd = [hipcc, *HIPCC_FLAGS, *san, *defs, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd))
     r = subprocess.run(cmd, capture_output=True, text=True)

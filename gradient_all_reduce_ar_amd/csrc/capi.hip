@@ -13,6 +13,8 @@
 #include <array>
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -24,6 +26,17 @@
 #include "plan.hpp"
 
 namespace {
+
+// The value of a C enum argument as an integer, read from its bytes: a
+// caller may pass any int, and loading a value outside the enumerators as
+// the C++ enum type is undefined behaviour.  The planner validates it.
+template <class E>
+int32_t raw_enum(const E &v) {
+  static_assert(sizeof(E) == sizeof(int32_t), "C enums are int-sized");
+  int32_t r;
+  std::memcpy(&r, &v, sizeof r);
+  return r;
+}
 
 thread_local std::string g_err;
 thread_local ar_status_t g_status = AR_OK;
@@ -57,8 +70,11 @@ struct ar_plan {
   uint64_t table_id = 0;
   float *scratch = nullptr;        // owned unless external_scratch
   size_t scratch_bytes = 0;
+  char *scratch_alloc = nullptr;   // the allocation holding scratch between its guard zones
+  size_t guard_bytes = 0;          // guard zone on each side of the owned scratch
   float *external_scratch = nullptr;
   size_t external_scratch_bytes = 0;
+  bool trace = false;              // AR_TRACE: dump the plan and its launch times at destroy
   // Graph replay: one instantiated graph of the whole launch sequence per
   // (rank pointers, error pointers, workspace) seen, at most kMaxGraphs.
   struct GraphEntry {
@@ -118,7 +134,8 @@ struct ar_plan {
     if (own_stream) (void)hipStreamDestroy(own_stream);
     own_stream = nullptr;
     if (d_ops) (void)hipFree(d_ops);
-    if (scratch) (void)hipFree(scratch);
+    if (scratch_alloc) (void)hipFree(scratch_alloc);
+    scratch_alloc = nullptr;
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     d_ops = nullptr;
     scratch = nullptr;
@@ -130,13 +147,16 @@ struct ar_plan {
 
 struct ar_bucket_plan {
   int nranks = 0, group_size = 1;
-  ar_dtype_t dtype = AR_FLOAT32;
+  ar::Dtype dtype = ar::kF32;
   std::vector<int64_t> tensor_offsets, bucket_offset, bucket_count;
   int64_t arena_count = 0;
   std::vector<ar_plan_t *> plans;
   std::vector<uint64_t> bytes_sent;
   float *scratch = nullptr;
   size_t scratch_bytes = 0;
+  char *scratch_alloc = nullptr;  // the allocation holding scratch between its guard zones
+  size_t guard_bytes = 0;
+  hipStream_t own_stream = nullptr;  // non-blocking: guard fills and checks
   // Batched execution: every bucket's all-reduce in shared launches (one
   // plan over the whole arena, built on first use).
   bool batch = true;
@@ -207,6 +227,59 @@ hipError_t upload_ops(ar_plan_t *pl) {
   return e;
 }
 
+// Guard zones (a debug aid): a device workspace of `bytes` is allocated with
+// `guard` extra bytes on each side, filled with kGuardByte, which no kernel
+// may touch.  Fills and checks run on a non-blocking stream of the owner and
+// are waited for with an event (see upload_ops).
+constexpr unsigned char kGuardByte = 0xA7;
+
+hipError_t wait_on(hipStream_t s) {
+  hipEvent_t done = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(done, s);
+  if (e == hipSuccess) e = hipEventSynchronize(done);
+  (void)hipEventDestroy(done);
+  return e;
+}
+
+hipError_t own_stream_of(hipStream_t *s) {
+  return *s ? hipSuccess : hipStreamCreateWithFlags(s, hipStreamNonBlocking);
+}
+
+hipError_t guarded_alloc(size_t bytes, size_t guard, hipStream_t *s, char **alloc) {
+  *alloc = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(alloc), bytes + 2 * guard);
+  if (e != hipSuccess || guard == 0) return e;
+  e = own_stream_of(s);
+  if (e == hipSuccess) e = hipMemsetAsync(*alloc, kGuardByte, guard, *s);
+  if (e == hipSuccess) e = hipMemsetAsync(*alloc + guard + bytes, kGuardByte, guard, *s);
+  if (e == hipSuccess) e = wait_on(*s);
+  if (e != hipSuccess) {
+    (void)hipFree(*alloc);
+    *alloc = nullptr;
+  }
+  return e;
+}
+
+// AR_OK if both guard zones of the allocation still hold kGuardByte.
+ar_status_t check_guard(const char *alloc, size_t bytes, size_t guard, hipStream_t *s, const char *what) {
+  if (!alloc || guard == 0) return AR_OK;
+  std::vector<unsigned char> h(2 * guard);
+  hipError_t e = own_stream_of(s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), alloc, guard, hipMemcpyDeviceToHost, *s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data() + guard, alloc + guard + bytes, guard, hipMemcpyDeviceToHost, *s);
+  if (e == hipSuccess) e = wait_on(*s);
+  if (e != hipSuccess) return hip_fail(e, "guard read");
+  for (size_t i = 0; i < h.size(); ++i)
+    if (h[i] != kGuardByte)
+      return fail(AR_ERR_GUARD, std::string(what) + ": guard byte " +
+                                    (i < guard ? std::to_string(guard - i) + " before the start"
+                                               : std::to_string(i - guard) + " after the end") +
+                                    " was overwritten");
+  return AR_OK;
+}
+
 ar_status_t prepare(ar_plan_t *pl) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -221,7 +294,11 @@ ar_status_t prepare(ar_plan_t *pl) {
   const std::vector<ar_dev::DevOp> &host_ops = pl->host_ops;
   if (!host_ops.empty()) {
     e = hipMalloc(reinterpret_cast<void **>(&pl->d_ops), host_ops.size() * sizeof(ar_dev::DevOp));
-    if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("op table allocation: ") + hipGetErrorString(e));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      pl->d_ops = nullptr;
+      return fail(AR_ERR_OOM, std::string("op table allocation: ") + hipGetErrorString(e));
+    }
     // The upload runs on the plan's own non-blocking stream and is waited for
     // with an event: a synchronous hipMemcpy goes through the legacy default
     // stream, which invalidates a graph capture that another host thread has
@@ -234,11 +311,13 @@ ar_status_t prepare(ar_plan_t *pl) {
   }
   const size_t need = pl->need_scratch_bytes();
   if (need > 0 && !pl->external_scratch) {
-    e = hipMalloc(reinterpret_cast<void **>(&pl->scratch), need);
+    e = guarded_alloc(need, pl->guard_bytes, &pl->own_stream, &pl->scratch_alloc);
     if (e != hipSuccess) {
+      (void)hipGetLastError();  // clear the sticky allocation error
       pl->release_device();
       return fail(AR_ERR_OOM, std::string("scratch allocation: ") + hipGetErrorString(e));
     }
+    pl->scratch = reinterpret_cast<float *>(pl->scratch_alloc + pl->guard_bytes);
     pl->scratch_bytes = need;
   }
   if (need > 0 && pl->external_scratch && pl->external_scratch_bytes < need) {
@@ -564,14 +643,111 @@ uint64_t noalloc_table_bytes(const ar_plan_t *plan) {
   return (plan->host_ops.size() * sizeof(ar_dev::DevOp) + 255) / 256 * 256;
 }
 
-}  // namespace
+const char *const kDtypeNames[] = {"fp32", "bf16", "bf16_each", "int8_ef"};
+const char *const kSchedNames[] = {"ring", "hierarchical", "rabenseifner", "recursive_doubling", "tree",
+                                   "double_tree"};
+const char *const kExecNames[] = {"steps", "steps_unfused", "onepass"};
 
-extern "C" {
+// The plan as JSON: its configuration, its schedule step by step (every
+// transfer: sender, receiver, range, 0 reduce / 1 copy) and its launches
+// (kernel kind, ops, shape, element range, bytes written, and the mean
+// duration in ms over the profiling log's calls that timed the launch, or
+// null).
+std::string describe(const ar_plan_t *pl) {
+  const ar::Plan &p = pl->p;
+  std::string j = "{";
+  auto kv = [&j](const char *k, const std::string &v, bool comma = true) {
+    j += std::string("\"") + k + "\": " + v + (comma ? ", " : "");
+  };
+  auto q = [](const char *v) { return std::string("\"") + v + "\""; };
+  kv("nranks", std::to_string(p.nranks));
+  kv("group_size", std::to_string(p.group_size));
+  kv("count", std::to_string(p.count));
+  kv("dtype", q(kDtypeNames[p.dtype]));
+  kv("schedule", q(kSchedNames[p.sched]));
+  kv("exec", q(kExecNames[p.exec]));
+  kv("steps", std::to_string(p.nsteps));
+  kv("hbm_bytes_model", std::to_string(p.hbm_bytes));
+  j += "\"step_list\": [";
+  for (size_t i = 0; i < p.xfers.size(); ++i) {
+    const ar::Transfer &x = p.xfers[i];
+    const bool first = i == 0 || p.xfers[i - 1].step != x.step;
+    const bool last = i + 1 == p.xfers.size() || p.xfers[i + 1].step != x.step;
+    if (first) j += std::string(i ? ", " : "") + "{\"step\": " + std::to_string(x.step) + ", \"transfers\": [";
+    j += "[" + std::to_string(x.src) + ", " + std::to_string(x.dst) + ", " + std::to_string(x.lo) + ", " +
+         std::to_string(x.hi) + ", " + std::to_string(x.kind) + "]" + (last ? "]}" : ", ");
+  }
+  j += "], \"launch_list\": [";
+  const size_t L = p.launches.size();
+  const int64_t calls = pl->prof_calls > 0 ? std::min<int64_t>(pl->prof_logged, pl->prof_calls) : 0;
+  for (size_t i = 0; i < L; ++i) {
+    const ar::Launch &la = p.launches[i];
+    int64_t lo = INT64_MAX, hi = 0;
+    for (const ar::Op &o : la.ops) {
+      lo = std::min(lo, o.lo);
+      hi = std::max(hi, o.hi);
+    }
+    double sum = 0;
+    int timed = 0;
+    for (int64_t c = 0; c < calls && !pl->events.empty(); ++c) {
+      const size_t slot = static_cast<size_t>((pl->prof_logged - calls + c) % pl->prof_calls);
+      if (!pl->sampled[slot * L + i]) continue;
+      float ms = 0;
+      if (hipEventElapsedTime(&ms, pl->events[(slot * L + i) * 2], pl->events[(slot * L + i) * 2 + 1]) ==
+          hipSuccess) {
+        sum += ms;
+        ++timed;
+      }
+    }
+    char buf[64];
+    std::snprintf(buf, sizeof buf, "%.5f", timed ? sum / timed : 0.0);
+    j += std::string(i ? ", " : "") + "{\"launch\": " + std::to_string(i) + ", \"kind\": " +
+         std::to_string(la.kind) + ", \"ops\": " + std::to_string(la.ops.size()) + ", \"cold\": " +
+         std::to_string(pl->cold[i]) + ", \"grid_x\": " + std::to_string(pl->grid_x[i]) + ", \"lo\": " +
+         std::to_string(la.ops.empty() ? 0 : lo) + ", \"hi\": " + std::to_string(hi) + ", \"write_bytes\": " +
+         std::to_string(ar::launch_write_bytes(p, la)) + ", \"ms\": " + (timed ? buf : "null") + "}";
+  }
+  j += "]}";
+  return j;
+}
 
-const char *ar_last_error(void) { return g_err.c_str(); }
-ar_status_t ar_last_status(void) { return g_status; }
+// AR_TRACE=1 writes the description of every plan at its destruction to
+// stderr; AR_TRACE=<path> appends it to that file, one line per plan.
+void trace_dump(const ar_plan_t *pl) {
+  const char *t = std::getenv("AR_TRACE");
+  if (!t || !*t || std::strcmp(t, "0") == 0) return;
+  const std::string j = describe(pl) + "\n";
+  if (std::strcmp(t, "1") == 0) {
+    std::fputs(j.c_str(), stderr);
+    return;
+  }
+  if (FILE *f = std::fopen(t, "a")) {
+    std::fputs(j.c_str(), f);
+    std::fclose(f);
+  }
+}
 
-ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype, ar_schedule_t schedule) {
+bool trace_enabled() {
+  const char *t = std::getenv("AR_TRACE");
+  return t && *t && std::strcmp(t, "0") != 0;
+}
+
+// ar_plan_set_exec with the mode as an integer.
+ar_status_t set_exec(ar_plan_t *plan, int32_t exec) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  const ar::Exec mode = static_cast<ar::Exec>(exec);
+  if (mode == plan->p.exec && plan->prepared) return AR_OK;
+  ar::Plan trial = plan->p;
+  const std::string err = ar::relower(trial, mode);
+  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
+  plan->release_device();  // waits for the plan's calls in flight
+  plan->p = std::move(trial);
+  lower_launches(plan);
+  return AR_OK;
+}
+
+// ar_plan_create with the enum arguments as integers.
+ar_plan_t *create_plan(int nranks, int group_size, size_t count, int32_t dtype, int32_t schedule) {
   if (count > static_cast<size_t>(INT64_MAX / 8)) {
     fail(AR_ERR_INVALID_ARG, "count too large");
     return nullptr;
@@ -591,21 +767,26 @@ ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t d
     return nullptr;
   }
   lower_launches(pl);
+  if (trace_enabled()) {  // per-launch timing of the last 16 calls, dumped at destroy
+    pl->trace = true;
+    pl->prof_calls = 16;
+  }
   g_status = AR_OK;
   return pl;
 }
 
-ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) {
-  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
-  if (exec == static_cast<ar_exec_t>(plan->p.exec) && plan->prepared) return AR_OK;
-  ar::Plan trial = plan->p;
-  const std::string err = ar::relower(trial, static_cast<ar::Exec>(exec));
-  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
-  plan->release_device();  // waits for the plan's calls in flight
-  plan->p = std::move(trial);
-  lower_launches(plan);
-  return AR_OK;
+}  // namespace
+
+extern "C" {
+
+const char *ar_last_error(void) { return g_err.c_str(); }
+ar_status_t ar_last_status(void) { return g_status; }
+
+ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype, ar_schedule_t schedule) {
+  return create_plan(nranks, group_size, count, raw_enum(dtype), raw_enum(schedule));
 }
+
+ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) { return set_exec(plan, raw_enum(exec)); }
 
 ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
@@ -733,8 +914,9 @@ int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtyp
     if (!(candidates & (1u << sched))) continue;
     ar::Plan p;
     bool unsupported = false;
-    if (!ar::build_plan(p, nranks, group_size, static_cast<int64_t>(count), static_cast<ar::Dtype>(dtype),
-                        static_cast<ar::Sched>(sched), ar::kSteps, &unsupported).empty())
+    if (!ar::build_plan(p, nranks, group_size, static_cast<int64_t>(count),
+                        static_cast<ar::Dtype>(raw_enum(dtype)), static_cast<ar::Sched>(sched), ar::kSteps,
+                        &unsupported).empty())
       continue;
     const double t = ar::cost_alpha_beta_ex(p, params->alpha_intra_s, params->alpha_cross_s, params->bw_intra_Bps,
                                             params->bw_cross_Bps, params->bw_group_egress_Bps,
@@ -755,6 +937,10 @@ int ar_select_schedule(int nranks, int group_size, size_t count, ar_dtype_t dtyp
 
 void ar_plan_destroy(ar_plan_t *plan) {
   if (!plan) return;
+  if (plan->trace) {
+    plan->wait_idle();
+    trace_dump(plan);
+  }
   plan->release_device();
   plan->release_marks();
   delete plan;
@@ -841,6 +1027,36 @@ ar_status_t ar_plan_set_profiling_period(ar_plan_t *plan, int period) {
   return AR_OK;
 }
 
+int64_t ar_plan_describe(const ar_plan_t *plan, char *buf, size_t cap) {
+  if (!plan) {
+    fail(AR_ERR_INVALID_ARG, "plan is NULL");
+    return -1;
+  }
+  auto *mut = const_cast<ar_plan_t *>(plan);
+  mut->wait_idle();  // the profiling log's events must have completed
+  const std::string j = describe(plan);
+  if (buf && cap > 0) {
+    const size_t n = std::min(cap - 1, j.size());
+    std::memcpy(buf, j.data(), n);
+    buf[n] = 0;
+  }
+  return static_cast<int64_t>(j.size());
+}
+
+ar_status_t ar_plan_set_guard(ar_plan_t *plan, size_t bytes) {
+  if (!plan || bytes % 256 || bytes > (size_t{1} << 30)) return fail(AR_ERR_INVALID_ARG, "bad guard size");
+  plan->release_device();  // waits for the plan's calls in flight
+  plan->guard_bytes = bytes;
+  return AR_OK;
+}
+
+ar_status_t ar_plan_check_guards(ar_plan_t *plan) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  plan->wait_idle();
+  return check_guard(plan->scratch_alloc, plan->scratch_bytes, plan->guard_bytes, &plan->own_stream,
+                     "plan scratch");
+}
+
 ar_status_t ar_plan_set_profiling_evict(ar_plan_t *plan, void *buf, size_t bytes) {
   if (!plan || (bytes > 0 && !buf) || bytes % 16 || bytes > static_cast<size_t>(INT64_MAX))
     return fail(AR_ERR_INVALID_ARG, "bad eviction buffer");
@@ -913,6 +1129,21 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
 
 namespace {
 
+// Frees the scratch the buckets share, after the buckets that used it.
+void release_bucket_scratch(ar_bucket_plan_t *bp) {
+  if (!bp->scratch_alloc) return;
+  for (ar_plan_t *pl : bp->plans) pl->wait_idle();
+  (void)hipFree(bp->scratch_alloc);
+  bp->scratch_alloc = nullptr;
+  bp->scratch = nullptr;
+  bp->scratch_bytes = 0;
+  for (ar_plan_t *pl : bp->plans) {  // their device state pointed at it
+    pl->external_scratch = nullptr;
+    pl->external_scratch_bytes = 0;
+    pl->prepared = pl->prepared && pl->need_scratch_bytes() == 0;
+  }
+}
+
 void drop_merged(ar_bucket_plan_t *bp) {
   if (bp->merged) ar_plan_destroy(bp->merged);
   bp->merged = nullptr;
@@ -921,7 +1152,7 @@ void drop_merged(ar_bucket_plan_t *bp) {
 // The batched plan of a bucket plan, built on first use (NULL for INT8).
 ar_plan_t *merged_plan(ar_bucket_plan_t *bp) {
   if (bp->merged) return bp->merged;
-  if (bp->dtype == AR_INT8_EF) {
+  if (bp->dtype == ar::kI8EF) {
     fail(AR_ERR_UNSUPPORTED, "INT8 buckets run one by one");
     return nullptr;
   }
@@ -940,6 +1171,7 @@ ar_plan_t *merged_plan(ar_bucket_plan_t *bp) {
   }
   lower_launches(m);
   m->use_graph = bp->use_graph;
+  m->guard_bytes = bp->guard_bytes;
   bp->merged = m;
   return m;
 }
@@ -954,7 +1186,8 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
     fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
     return nullptr;
   }
-  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_BFLOAT16_EACH_STEP && dtype != AR_INT8_EF) {
+  const auto dt = static_cast<ar::Dtype>(raw_enum(dtype));
+  if (dt != ar::kF32 && dt != ar::kBF16 && dt != ar::kBF16Each && dt != ar::kI8EF) {
     fail(AR_ERR_INVALID_ARG, "unknown dtype");
     return nullptr;
   }
@@ -965,8 +1198,8 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
   }
   bp->nranks = nranks;
   bp->group_size = group_size;
-  bp->dtype = dtype;
-  const int64_t eb = ar::buffer_elem_bytes(static_cast<ar::Dtype>(dtype));
+  bp->dtype = dt;
+  const int64_t eb = ar::buffer_elem_bytes(dt);
   std::vector<int64_t> counts(tensor_counts, tensor_counts + ntensors);
   for (int64_t c : counts)
     if (c < 0) {
@@ -978,7 +1211,8 @@ ar_bucket_plan_t *ar_bucket_plan_create(int nranks, int group_size, const size_t
                      bp->bucket_offset, bp->bucket_count, bp->arena_count);
   bp->bytes_sent.assign(nranks > 0 ? nranks : 0, 0);
   for (size_t b = 0; b < bp->bucket_count.size(); ++b) {
-    ar_plan_t *pl = ar_plan_create(nranks, group_size, static_cast<size_t>(bp->bucket_count[b]), dtype, schedule);
+    ar_plan_t *pl = create_plan(nranks, group_size, static_cast<size_t>(bp->bucket_count[b]), dt,
+                                raw_enum(schedule));
     if (!pl) {
       const ar_status_t st = g_status;
       const std::string msg = g_err;
@@ -1030,7 +1264,7 @@ ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable) {
 ar_status_t ar_bucket_set_exec(ar_bucket_plan_t *bp, ar_exec_t exec) {
   if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
   for (ar_plan_t *pl : bp->plans) {
-    const ar_status_t st = ar_plan_set_exec(pl, exec);
+    const ar_status_t st = set_exec(pl, raw_enum(exec));
     if (st != AR_OK) return st;
   }
   drop_merged(bp);  // waits for its launches in flight
@@ -1045,6 +1279,28 @@ ar_status_t ar_bucket_set_cache_bytes(ar_bucket_plan_t *bp, size_t bytes) {
   }
   drop_merged(bp);  // waits for its launches in flight
   return AR_OK;
+}
+
+ar_status_t ar_bucket_set_guard(ar_bucket_plan_t *bp, size_t bytes) {
+  if (!bp || bytes % 256 || bytes > (size_t{1} << 30)) return fail(AR_ERR_INVALID_ARG, "bad guard size");
+  release_bucket_scratch(bp);
+  bp->guard_bytes = bytes;
+  for (ar_plan_t *pl : bp->plans) {
+    const ar_status_t st = ar_plan_set_guard(pl, bytes);
+    if (st != AR_OK) return st;
+  }
+  if (bp->merged) return ar_plan_set_guard(bp->merged, bytes);
+  return AR_OK;
+}
+
+ar_status_t ar_bucket_check_guards(ar_bucket_plan_t *bp) {
+  if (!bp) return fail(AR_ERR_INVALID_ARG, "bucket plan is NULL");
+  for (ar_plan_t *pl : bp->plans) pl->wait_idle();
+  ar_status_t st = check_guard(bp->scratch_alloc, bp->scratch_bytes, bp->guard_bytes, &bp->own_stream,
+                               "bucket scratch");
+  for (size_t b = 0; st == AR_OK && b < bp->plans.size(); ++b) st = ar_plan_check_guards(bp->plans[b]);
+  if (st == AR_OK && bp->merged) st = ar_plan_check_guards(bp->merged);
+  return st;
 }
 
 ar_status_t ar_bucket_set_batching(ar_bucket_plan_t *bp, int enable) {
@@ -1093,9 +1349,9 @@ double ar_overlap_step_time(int nchunks, const double *ready_s, const double *co
 ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arenas, void *const *error_arenas,
                                    void *stream, void *const *ready_events, void *const *done_events) {
   if (!bp || !rank_arenas) return fail(AR_ERR_INVALID_ARG, "bad bucket arguments");
-  if (error_arenas && bp->dtype != AR_INT8_EF) return fail(AR_ERR_INVALID_ARG, "error feedback needs AR_INT8_EF");
+  if (error_arenas && bp->dtype != ar::kI8EF) return fail(AR_ERR_INVALID_ARG, "error feedback needs AR_INT8_EF");
   if (bp->plans.empty()) return AR_OK;
-  if (bp->batch && bp->dtype != AR_INT8_EF && !ready_events && !done_events) {
+  if (bp->batch && bp->dtype != ar::kI8EF && !ready_events && !done_events) {
     ar_plan_t *m = merged_plan(bp);
     if (!m) return g_status;
     return ar_allreduce(m, rank_arenas, stream);
@@ -1104,17 +1360,16 @@ ar_status_t ar_bucket_allreduce_ef(ar_bucket_plan_t *bp, void *const *rank_arena
   size_t need = 0;
   for (ar_plan_t *pl : bp->plans) need = std::max(need, pl->need_scratch_bytes());
   if (need > bp->scratch_bytes) {
-    if (bp->scratch) {
-      for (ar_plan_t *pl : bp->plans) pl->wait_idle();  // the buckets that used it
-      (void)hipFree(bp->scratch);
-      bp->scratch = nullptr;
-      bp->scratch_bytes = 0;
+    release_bucket_scratch(bp);
+    hipError_t e = guarded_alloc(need, bp->guard_bytes, &bp->own_stream, &bp->scratch_alloc);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(AR_ERR_OOM, std::string("bucket scratch: ") + hipGetErrorString(e));
     }
-    hipError_t e = hipMalloc(reinterpret_cast<void **>(&bp->scratch), need);
-    if (e != hipSuccess) return fail(AR_ERR_OOM, std::string("bucket scratch: ") + hipGetErrorString(e));
+    bp->scratch = reinterpret_cast<float *>(bp->scratch_alloc + bp->guard_bytes);
     bp->scratch_bytes = need;
   }
-  const int64_t eb = ar::buffer_elem_bytes(static_cast<ar::Dtype>(bp->dtype));
+  const int64_t eb = ar::buffer_elem_bytes(bp->dtype);
   std::vector<void *> ptrs(static_cast<size_t>(bp->nranks)), eptrs(static_cast<size_t>(bp->nranks));
   for (size_t b = 0; b < bp->plans.size(); ++b) {
     ar_plan_t *pl = bp->plans[b];
@@ -1164,7 +1419,7 @@ ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
   }
   s.nranks = bp->nranks;
   s.group_size = bp->group_size;
-  s.elem_bytes = static_cast<uint64_t>(ar::buffer_elem_bytes(static_cast<ar::Dtype>(bp->dtype)));
+  s.elem_bytes = static_cast<uint64_t>(ar::buffer_elem_bytes(bp->dtype));
   s.bytes_sent = bp->bytes_sent.data();
   for (uint64_t b : bp->bytes_sent) {
     s.bytes_sent_max = std::max(s.bytes_sent_max, b);
@@ -1176,11 +1431,12 @@ ar_stats_t ar_bucket_stats(const ar_bucket_plan_t *bp) {
 void ar_bucket_plan_destroy(ar_bucket_plan_t *bp) {
   if (!bp) return;
   drop_merged(bp);
+  release_bucket_scratch(bp);  // waits for the buckets' calls
   for (ar_plan_t *pl : bp->plans) {
     pl->external_scratch = nullptr;
-    ar_plan_destroy(pl);  // waits for the bucket's calls
+    ar_plan_destroy(pl);
   }
-  if (bp->scratch) (void)hipFree(bp->scratch);
+  if (bp->own_stream) (void)hipStreamDestroy(bp->own_stream);
   delete bp;
 }
 

@@ -70,7 +70,8 @@ typedef enum {
   AR_ERR_INVALID_ARG = 1, /* bad argument: sizes, NULL or misaligned pointers */
   AR_ERR_UNSUPPORTED = 2, /* e.g. Rabenseifner with N not a power of two       */
   AR_ERR_OOM = 3,         /* device scratch or table allocation failed         */
-  AR_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed         */
+  AR_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed         */
+  AR_ERR_GUARD = 5        /* a guard zone around device workspace was written  */
 } ar_status_t;
 
 /* AR_BFLOAT16: fp32 partial sums, each element rounded once (see above).
@@ -368,6 +369,36 @@ ar_status_t ar_plan_launch_scratch(const ar_plan_t *plan, int32_t i, int64_t *sh
  */
 ar_status_t ar_plan_set_graph(ar_plan_t *plan, int enable);
 
+/* ---- Debug aids ---- */
+
+/*
+ * The plan as JSON (NUL-terminated, truncated to cap - 1 bytes): its
+ * configuration; its schedule step by step ("step_list": per step, every
+ * transfer as [sender, receiver, lo, hi, kind], kind 0 reduce / 1 copy, the
+ * step list of Primer ch. 4 Figure 4.2 for a ring); and its launches
+ * ("launch_list": kernel kind code, ops, streaming shape, grid width,
+ * element range, bytes written, and the mean duration in ms over the
+ * profiling log's calls that timed it, or null).  Returns the full length
+ * (call with cap = 0 to size the buffer), -1 on error.  Waits for the
+ * plan's calls in flight.
+ * With the environment variable AR_TRACE=1 every plan keeps a profiling log
+ * of its last 16 calls (calls run eagerly) and writes this description to
+ * stderr when it is destroyed; AR_TRACE=<path> appends it to that file, one
+ * line per plan.  Results are unchanged.
+ */
+int64_t ar_plan_describe(const ar_plan_t *plan, char *buf, size_t cap);
+
+/*
+ * Guard zones around the plan's device scratch (fp32 partial sums, INT8
+ * code slots): with bytes > 0 (a multiple of 256, at most 1 GiB) the scratch
+ * is allocated at the next prepare with `bytes` extra on each side, filled
+ * with 0xA7.  ar_plan_check_guards waits for the plan's calls and returns
+ * AR_ERR_GUARD, naming the first overwritten byte, if a kernel wrote into
+ * either zone.  A debug aid for tests; results are unchanged.
+ */
+ar_status_t ar_plan_set_guard(ar_plan_t *plan, size_t bytes);
+ar_status_t ar_plan_check_guards(ar_plan_t *plan);
+
 /* ---- Timing ---- */
 
 /* Per-launch timing.  With max_calls > 0, each ar_allreduce launches every
@@ -461,6 +492,11 @@ ar_status_t ar_bucket_set_graph(ar_bucket_plan_t *bp, int enable);
 /* ar_plan_set_cache_bytes for every bucket's plan; the batched plan is
  * rebuilt with the new size on its next use.  Host only. */
 ar_status_t ar_bucket_set_cache_bytes(ar_bucket_plan_t *bp, size_t bytes);
+/* Guard zones (see ar_plan_set_guard) around the scratch the buckets share
+ * when run one by one, and around every bucket's and the batched plan's own
+ * scratch; the check covers all of them. */
+ar_status_t ar_bucket_set_guard(ar_bucket_plan_t *bp, size_t bytes);
+ar_status_t ar_bucket_check_guards(ar_bucket_plan_t *bp);
 /* enable = 0: ar_bucket_allreduce runs the buckets one by one, each with its
  * own launches; non-zero (default): batched.  Host only. */
 ar_status_t ar_bucket_set_batching(ar_bucket_plan_t *bp, int enable);

@@ -22,5 +22,20 @@ def build(out=LIB, extra=()):
     return out
 
 
+# The same oracle with AddressSanitizer and UndefinedBehaviorSanitizer, built
+# with ROCm's clang so that it shares one sanitizer runtime with the
+# instrumented planner library (load it with ARO_LIB=<path>).
+LIB_SANITIZED = os.path.join(HERE, "liboracle_sanitized.so")
+CLANG = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+
+
+def build_sanitized(out=LIB_SANITIZED):
+    cmd = [CLANG, "-O1", "-g", "-std=gnu11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-Wall", "-Wextra", "-Werror", "-o", out, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build())

@@ -1,0 +1,210 @@
+"""Guard canaries and the allocation-failure path, on the GPU.
+
+Canaries: every rank buffer (and, for INT8 with error feedback, every error
+buffer) is a view into a larger allocation whose 4 KiB before and after it
+hold a fixed pattern; the plan's own scratch (fp32 partial sums, INT8 code
+slots) and the scratch that bucketed all-reduces share get guard zones of
+their own (ar_plan_set_guard / ar_bucket_set_guard).  A ragged case of every
+schedule in every exec mode runs, its result is checked against the oracle,
+and every guard must still hold its pattern.
+
+Allocation failure: a plan whose scratch cannot fit in device memory is
+refused with AR_ERR_OOM when it prepares, leaves the device's free memory
+as it was, can still be destroyed, and the next plan runs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_ar_amd import _binding as B
+from gradient_all_reduce_ar_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096          # bytes of canary on each side of a buffer
+PATTERN = 0x5B        # canary byte of the rank and error buffers
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _guarded(host, view):
+    """Device buffers holding `host`, each a view with GUARD canary bytes on
+    both sides inside one allocation; returns (views, allocations)."""
+    import torch
+
+    g = GUARD // np.dtype(view).itemsize
+    allocs, views = [], []
+    for h in host:
+        raw = np.full((len(h) + 2 * g) * np.dtype(view).itemsize, PATTERN, np.uint8).view(view)
+        raw[g:g + len(h)] = np.ascontiguousarray(h).view(view)
+        t = torch.from_numpy(raw).to("cuda:0")
+        allocs.append(t)
+        views.append(t[g:g + len(h)])
+    return views, allocs
+
+
+def _canaries_intact(allocs, count, what):
+    for r, t in enumerate(allocs):
+        b = t.cpu().numpy().view(np.uint8)
+        inner = count * t.element_size()
+        assert np.all(b[:GUARD] == PATTERN), f"{what}: canary before buffer {r} overwritten"
+        assert np.all(b[GUARD + inner:] == PATTERN), f"{what}: canary after buffer {r} overwritten"
+
+
+CASES = [("ring", 5, 1), ("hierarchical", 6, 3), ("rabenseifner", 8, 1), ("recursive_doubling", 8, 1),
+         ("tree", 5, 1), ("double_tree", 8, 1)]
+
+
+@pytest.mark.parametrize("sched,n,g", CASES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each", "int8_ef"])
+def test_canaries_every_schedule_and_mode(sched, n, g, dtype):
+    import torch
+
+    count = 100003
+    for mode in ("steps", "steps_unfused", "onepass"):
+        what = f"{sched} n={n} g={g} {dtype} {mode}"
+        _say(f"case guards {what}")
+        p = B.ar_plan_create(n, g, count, dtype, sched)
+        try:
+            B.ar_plan_set_exec(p, mode)
+            B.ar_plan_set_guard(p, 1 << 16)
+            if dtype == "int8_ef":
+                rng = np.random.default_rng(n)
+                xs = [(rng.standard_normal(count) * np.exp(rng.standard_normal(count))).astype(np.float32)
+                      for _ in range(n)]
+                es = [(rng.standard_normal(count) * 1e-2).astype(np.float32) for _ in range(n)]
+                bufs, allocs = _guarded(xs, np.float32)
+                errs, eallocs = _guarded(es, np.float32)
+                B.ar_allreduce_ef(p, bufs, errs, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                rb, re_ = [x.copy() for x in xs], [e.copy() for e in es]
+                oracle.run_int8ef(rb, sched, errs=re_, group_size=g)
+                for r in range(n):
+                    assert np.array_equal(bufs[r].cpu().numpy().view(np.uint32), rb[r].view(np.uint32)), what
+                    assert np.array_equal(errs[r].cpu().numpy().view(np.uint32), re_[r].view(np.uint32)), what
+                _canaries_intact(eallocs, count, what + " error buffers")
+            else:
+                gen = "fp32" if dtype == "fp32" else "bf16"
+                view = np.float32 if dtype == "fp32" else np.int16
+                xs = workloads.normal_inputs(n, count, seed=n, sigma=1.0, dtype=gen)
+                bufs, allocs = _guarded(xs, view)
+                B.ar_allreduce(p, bufs, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+                bv = np.uint32 if dtype == "fp32" else np.uint16
+                for r in range(n):
+                    assert np.array_equal(bufs[r].cpu().numpy().view(bv), ref[r].view(bv)), what
+            _canaries_intact(allocs, count, what + " rank buffers")
+            B.ar_plan_check_guards(p)
+        finally:
+            B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n", [("ring", 8), ("rabenseifner", 8)])
+def test_canaries_bucketed(sched, n):
+    """Bucketed bf16 arenas, batched and one by one: the arenas' canaries and
+    the guard zones of the shared and the batched plans' scratch hold."""
+    import torch
+
+    sizes = [300, 5000, 17, 2048, 999, 70000, 4, 40000]
+    bp = B.ar_bucket_plan_create(n, 1, sizes, "bf16", sched, 16 << 10)
+    try:
+        B.ar_bucket_set_guard(bp, 1 << 16)
+        offs, arena = B.ar_bucket_layout(bp, len(sizes))
+        host = workloads.bucketed_arenas(n, sizes, offs, arena, sigma=1.0)
+        refs = []
+        for b in range(B.ar_bucket_count(bp)):
+            off, cnt = B.ar_bucket_range(bp, b)
+            refs.append((off, cnt, oracle.run([h[off:off + cnt].copy() for h in host], "bf16", sched)))
+        for batch in (True, False):
+            for mode in ("steps", "onepass"):
+                what = f"bucketed {sched} n={n} batched={batch} {mode}"
+                _say(f"case guards {what}")
+                B.ar_bucket_set_batching(bp, batch)
+                B.ar_bucket_set_exec(bp, mode)
+                bufs, allocs = _guarded([h.view(np.int16) for h in host], np.int16)
+                if batch:
+                    B.ar_bucket_allreduce(bp, bufs, torch.cuda.current_stream())
+                else:
+                    B.ar_bucket_allreduce_after(bp, bufs, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                for off, cnt, ref in refs:
+                    for r in range(n):
+                        got = bufs[r][off:off + cnt].cpu().numpy().view(np.uint16)
+                        assert np.array_equal(got, ref[r]), what
+                _canaries_intact(allocs, arena, what)
+                B.ar_bucket_check_guards(bp)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+
+
+def test_scratch_allocation_failure_returns_oom_and_leaks_nothing():
+    """A bf16 Rabenseifner plan of 64 ranks x 2^34 elements needs 32 fp32
+    slots of 2^34 elements (2 TiB): its prepare fails with AR_ERR_OOM, the
+    device's free memory is unchanged, the plan can be destroyed, and a
+    small plan then runs.  The bucketed path's shared scratch fails the same
+    way before any launch (its arenas are never touched)."""
+    import torch
+
+    from tests.gpu_util import gpu_allreduce
+
+    def small_run():
+        xs = workloads.normal_inputs(4, 4099, seed=3, sigma=1.0, dtype="bf16")
+        got = gpu_allreduce(xs, "bf16", "rabenseifner")
+        ref = oracle.run([x.copy() for x in xs], "bf16", "rabenseifner")
+        for r in range(4):
+            assert np.array_equal(got[r], ref[r])
+
+    small_run()  # the library's code and static data are resident before free memory is read
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    p = B.ar_plan_create(64, 1, 1 << 34, "bf16", "rabenseifner")
+    try:
+        assert B.ar_plan_stats(p)["scratch_bytes"] >= 2 << 40
+        with pytest.raises(B.ArError) as ei:
+            B.ar_plan_prepare(p)
+        assert ei.value.status == B.AR_ERR_OOM, str(ei.value)
+        with pytest.raises(B.ArError) as ei:  # and again: nothing was left half-built
+            B.ar_plan_prepare(p)
+        assert ei.value.status == B.AR_ERR_OOM
+    finally:
+        B.ar_plan_destroy(p)
+    bp = B.ar_bucket_plan_create(64, 1, [1 << 34], "bf16", "rabenseifner", 25 << 20)
+    try:
+        fake = [(r + 1) << 40 for r in range(64)]  # never dereferenced: the scratch fails first
+        for batch in (True, False):  # the batched plan's scratch, then the buckets' shared scratch
+            B.ar_bucket_set_batching(bp, batch)
+            with pytest.raises(B.ArError) as ei:
+                B.ar_bucket_allreduce_after(bp, fake, torch.cuda.current_stream())
+            assert ei.value.status == B.AR_ERR_OOM, str(ei.value)
+    finally:
+        B.ar_bucket_plan_destroy(bp)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert abs(free1 - free0) <= 16 << 20, (free0, free1)
+    small_run()
+
+
+def test_trace_reports_launch_times():
+    """With the profiling log on, the plan description carries a mean
+    duration for every launch."""
+    import torch
+
+    n, count = 8, 1 << 20
+    p = B.ar_plan_create(n, 1, count, "fp32", "ring")
+    try:
+        B.ar_plan_set_profiling(p, 4)
+        bufs = [torch.randn(count, device="cuda:0") for _ in range(n)]
+        for _ in range(3):
+            B.ar_allreduce(p, bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        d = B.ar_plan_describe(p)
+        assert len(d["launch_list"]) == B.ar_plan_num_launches(p)
+        assert all(la["ms"] is not None and la["ms"] > 0 for la in d["launch_list"])
+    finally:
+        B.ar_plan_destroy(p)
