@@ -268,8 +268,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the one-pass, graph, cold-cache and ceiling runs")
     ap.add_argument("--calibrate", action="store_true",
-                    help="first run a plain 1 GiB device-to-device torch copy three times, so that "
-                         "hardware counters of the same run can be scaled by a copy of known size")
+                    help="first copy 1 GiB three times with the library's probe kernel (ar_hbm_probe, one "
+                         "source, one destination), so that hardware counters of the same run can be scaled "
+                         "by a kernel of known traffic (1 GiB read, 1 GiB written per launch)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -297,10 +298,10 @@ def main():
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            B.ar_hbm_probe([src], [dst], 1 << 30, 2, 1, torch.cuda.current_stream(dev))
         torch.cuda.synchronize()
         del src, dst
-        log("calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
+        log("calibration: 3 probe copies of 1 GiB (hbm_probe_kernel<2, 1>: read 1 GiB + write 1 GiB each)")
 
     # ---- inputs, resident in HBM before timing, with pristine device copies
     t0 = time.time()

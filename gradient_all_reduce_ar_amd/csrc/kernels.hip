@@ -191,12 +191,61 @@ __device__ __forceinline__ float fold1(bool each, float a, float b) {
 // written to o2 (the fused forwarding copy of the chunk just completed).
 // FLAGS: 1 a is bf16, 2 b is bf16, 4 outputs are bf16 (rounded once), 8 o2.
 // CP: cache policy of the full-tile stores (the host picks it for rank or
-// scratch outputs).
+// scratch outputs).  A thread moves units of E elements: 4 (one 16-byte
+// access per fp32 operand, 8 bytes per bf16 one), or 8 when every operand is
+// bf16 (16-byte accesses).  An fp32 operand next to a bf16 one stays at 4
+// elements per unit: with 8, each of its two 16-byte loads per lane would
+// cover only half of every line (a 32-byte lane stride), and such reduces
+// ran at half speed on MI355X (C3 reduce-scatter step 71 -> 153 us).
 // ---------------------------------------------------------------------------
+template <int E>
+struct Unit {
+  float4 v[E / 4];
+};
+
+template <bool BF, int E>
+__device__ __forceinline__ Unit<E> load_unit(const char *base, int64_t e) {
+  Unit<E> r;
+  if constexpr (BF && E == 8) {
+    const u32x4 w = ld<u32x4>(base + e * 2);
+    r.v[0] = make_float4(widen(w.x & 0xffffu), widen(w.x >> 16), widen(w.y & 0xffffu), widen(w.y >> 16));
+    r.v[1] = make_float4(widen(w.z & 0xffffu), widen(w.z >> 16), widen(w.w & 0xffffu), widen(w.w >> 16));
+  } else {
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) r.v[k] = load4<BF>(base, e + 4 * k);
+  }
+  return r;
+}
+
+template <int E>
+__device__ __forceinline__ Unit<E> add_unit(const Unit<E> &a, const Unit<E> &b) {
+  Unit<E> r;
+#pragma unroll
+  for (int k = 0; k < E / 4; ++k) r.v[k] = add4(a.v[k], b.v[k]);
+  return r;
+}
+
+// Stores a unit at element tile0 + lane (tile0 wave-uniform) with policy CP.
+template <bool BF, int E, int CP>
+__device__ __forceinline__ void store_unit(char *base, int64_t tile0, uint32_t lane, const Unit<E> &x) {
+  if constexpr (BF && E == 8) {
+    const u32x2 lo = pack4(x.v[0]), hi = pack4(x.v[1]);
+    st_cp<CP, u32x4>(base + tile0 * 2, lane * 2, u32x4{lo.x, lo.y, hi.x, hi.y});
+  } else if constexpr (BF) {
+    store_bits4<CP>(base, tile0, lane, pack4(x.v[0]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) store4<false, CP>(base, tile0, lane + 4 * k, x.v[k]);
+  }
+}
+
+constexpr int reduce_unit_elems(int flags) { return (flags & 7) == 7 && AR_BF16_UNIT == 8 ? 8 : 4; }
+
 template <int FLAGS, int UNROLL, int CP>
 __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   constexpr bool kABf = FLAGS & 1, kBBf = FLAGS & 2, kOBf = FLAGS & 4, kO2 = FLAGS & 8;
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * 4 * UNROLL;
+  constexpr int kE = reduce_unit_elems(FLAGS);
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kE * UNROLL;
   const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
   const int64_t t_end = (op.hi + kTile - 1) / kTile;
@@ -207,46 +256,34 @@ __global__ __launch_bounds__(kBlock) void chunk_reduce(KArgs args) {
   for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
     const int64_t base = t * kTile;
     if (base >= op.lo && base + kTile <= op.hi) {
-      float4 a[UNROLL], b[UNROLL];
+      Unit<kE> a[UNROLL], b[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * 4;
-        a[u] = load4<kABf>(A, e);
-        b[u] = load4<kBBf>(B, e);
+        const int64_t e = base + (static_cast<int64_t>(u) * kBlock + threadIdx.x) * kE;
+        a[u] = load_unit<kABf, kE>(A, e);
+        b[u] = load_unit<kBBf, kE>(B, e);
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * 4;
-        const float4 s = add4(a[u], b[u]);
-        if constexpr (kOBf) {
-          const u32x2 bits = pack4(s);
-          store_bits4<CP>(O, base, lane, bits);
-          if constexpr (kO2) store_bits4<CP>(O2, base, lane, bits);
-        } else {
-          store4<false, CP>(O, base, lane, s);
-          if constexpr (kO2) store4<false, CP>(O2, base, lane, s);
-        }
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * kE;
+        const Unit<kE> s = add_unit(a[u], b[u]);
+        store_unit<kOBf, kE, CP>(O, base, lane, s);
+        if constexpr (kO2) store_unit<kOBf, kE, CP>(O2, base, lane, s);
       }
     } else {
-      // a tile cut by the op's range: the 4-element units inside the op take
-      // the vector path, the units it cuts the per-element one
+      // a tile cut by the op's range: the units inside the op take the
+      // vector path, the units it cuts the per-element one
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * 4;
+        const uint32_t lane = (static_cast<uint32_t>(u) * kBlock + threadIdx.x) * kE;
         const int64_t e0 = base + lane;
-        if (e0 >= op.lo && e0 + 4 <= op.hi) {
-          const float4 s = add4(load4<kABf>(A, e0), load4<kBBf>(B, e0));
-          if constexpr (kOBf) {
-            const u32x2 bits = pack4(s);
-            store_bits4<CP>(O, base, lane, bits);
-            if constexpr (kO2) store_bits4<CP>(O2, base, lane, bits);
-          } else {
-            store4<false, CP>(O, base, lane, s);
-            if constexpr (kO2) store4<false, CP>(O2, base, lane, s);
-          }
+        if (e0 >= op.lo && e0 + kE <= op.hi) {
+          const Unit<kE> s = add_unit(load_unit<kABf, kE>(A, e0), load_unit<kBBf, kE>(B, e0));
+          store_unit<kOBf, kE, CP>(O, base, lane, s);
+          if constexpr (kO2) store_unit<kOBf, kE, CP>(O2, base, lane, s);
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < kE; ++k) {
             const int64_t e = e0 + k;
             if (e < op.lo || e >= op.hi) continue;
             const float s = load1<kABf>(A, e) + load1<kBBf>(B, e);
@@ -736,8 +773,12 @@ constexpr int kUnrollCold = AR_COLD_UNROLL;
 // unit is 8 bytes, half an fp32 unit, so twice the units keep as many bytes
 // in flight (bf16 rounded at each add, ring 16 x 192 MiB 2.13 -> 2.09 ms,
 // 64 ranks 2.52 -> 2.48 ms).
+// With 8-element units (a bf16 operand) half as many units keep the same
+// elements per thread.
 constexpr int reduce_unroll(int flags, bool cold) {
-  return (flags & 7) == 7 ? (cold ? AR_COLD_UNROLL_BF16 : AR_REDUCE_UNROLL_BF16) : (cold ? kUnrollCold : kUnrollWarm);
+  const int u = (flags & 7) == 7 ? (cold ? AR_COLD_UNROLL_BF16 : AR_REDUCE_UNROLL_BF16) : (cold ? kUnrollCold : kUnrollWarm);
+  const int per = reduce_unit_elems(flags) / 4;
+  return u / per > 0 ? u / per : 1;
 }
 // one-pass shapes per dtype (measured): fp32 2 units x 8 ranks in flight,
 // bf16 1 unit x 16 ranks
@@ -956,7 +997,7 @@ int block_threads(int32_t kind) {
 int64_t tile_elems(int32_t kind, bool cold) {
   const int64_t u = cold ? kUnrollCold : kUnrollWarm;
   switch (kind & 0xF00) {
-    case kKindReduce: return static_cast<int64_t>(kBlock) * 4 * reduce_unroll(kind & 0xF, cold);
+    case kKindReduce: return static_cast<int64_t>(kBlock) * reduce_unit_elems(kind & 0xF) * reduce_unroll(kind & 0xF, cold);
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
     case kKindTree: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kTreeUnrollBF16 : kTreeUnrollF32);
     default: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);

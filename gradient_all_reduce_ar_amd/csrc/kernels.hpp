@@ -63,6 +63,11 @@
 #ifndef AR_REDUCE_UNROLL
 #define AR_REDUCE_UNROLL 2
 #endif
+// Elements per unit of a reduce whose operands are all bf16: 8 (16-byte
+// accesses) or 4 (8-byte).
+#ifndef AR_BF16_UNIT
+#define AR_BF16_UNIT 8
+#endif
 #ifndef AR_REDUCE_UNROLL_BF16
 #define AR_REDUCE_UNROLL_BF16 4
 #endif
