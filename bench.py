@@ -220,7 +220,15 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
              ("copy 1:1", bufs[:1], bufs[1:2], nbytes), ("reduce 2:1", bufs[:2], bufs[2:3], nbytes),
              ("reduce 2:2", bufs[:2], bufs[2:4], nbytes)]
     if rank_bufs is not None and len(rank_bufs) <= 64 and rank_bytes % 16 == 0 and rank_bytes >= (64 << 20):
-        mixes.append((f"fold {len(rank_bufs)}:{len(rank_bufs)}", rank_bufs, rank_bufs, rank_bytes))
+        # the one-pass mix (every rank read, every rank written, in place) and
+        # its parts: reads of every rank, writes to every rank, a fold into one
+        # rank, a fan-out from one rank to the others
+        n = len(rank_bufs)
+        mixes += [(f"fold {n}:{n}", rank_bufs, rank_bufs, rank_bytes),
+                  (f"read {n}:0", rank_bufs, [], rank_bytes),
+                  (f"write 0:{n}", [], rank_bufs, rank_bytes),
+                  (f"fold {n}:1", rank_bufs, rank_bufs[:1], rank_bytes),
+                  (f"fan 1:{n - 1}", rank_bufs[:1], rank_bufs[1:], rank_bytes)]
     out = {}
     for name, src, dst, nb in mixes:
         best = None
@@ -228,7 +236,7 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
             for policy in (0, 1, 2):
                 ts = []
                 for r in range(reps + 2):
-                    if restore is not None and src is rank_bufs:
+                    if restore is not None and rank_bufs is not None and any(b is rank_bufs[0] for b in dst):
                         restore()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
@@ -249,9 +257,23 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
     return out
 
 
-def attainable_for(ceil, share):
-    """The probe mix whose read share is nearest a kernel's."""
-    name = min(ceil, key=lambda k: abs(ceil[k]["read_share"] - share))
+def attainable_for(ceil, kind, elem, nranks):
+    """The probe mix with a kernel's streams: two sources into one output for
+    a reduce, into two for the fused reduce + forward, one into one for a copy,
+    every rank into every rank for a one-pass fold; otherwise (the INT8
+    kernels) the two-buffer mix whose read share is nearest the kernel's."""
+    fam = kind & 0xF00
+    fold = f"fold {nranks}:{nranks}"
+    if fam == 0x100:
+        name = "reduce 2:2" if kind & 8 else "reduce 2:1"
+    elif fam == 0x200:
+        name = "copy 1:1"
+    elif fam in (0x300, 0x400, 0x500, 0x600) and kind & 3 != 3 and fold in ceil:
+        name = fold
+    else:
+        share = read_share(kind, elem)
+        big = [k for k in ceil if k in ("read 1:0", "write 0:1", "copy 1:1", "reduce 2:1", "reduce 2:2")]
+        name = min(big, key=lambda k: abs(ceil[k]["read_share"] - share))
     return name, ceil[name]["GBps"]
 
 
@@ -260,7 +282,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS) + ["overlap"])
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS) + ["overlap", "latency"])
     ap.add_argument("--compute-ratio", type=float, default=1.5,
                     help="overlap workload: backward compute per bucket as a multiple of its all-reduce time")
     ap.add_argument("--exec", default="steps", choices=["steps", "steps_unfused", "onepass"])
@@ -286,6 +308,8 @@ def main():
 
     if args.workload == "overlap":
         return overlap_main(args, B, workloads, np, torch)
+    if args.workload == "latency":
+        return latency_main(args, B, np, torch)
     desc, sched, n, group, dtype, count = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -436,9 +460,10 @@ def main():
         return per, run_ms, means
 
     per_kind, prof_ms, means = timed_run()
-    per_call_count = {}
-    for k in keys:
+    per_call_count, per_call_bytes = {}, {}
+    for i, k in enumerate(keys):
         per_call_count[k] = per_call_count.get(k, 0) + 1
+        per_call_bytes[k] = per_call_bytes.get(k, 0) + lb[i][0]
     # the kernel with the largest share of a call's GPU time
     dom = max(per_kind, key=lambda f: per_kind[f]["ms"] / per_kind[f]["launches"] * per_call_count[f])
     d = per_kind[dom]
@@ -471,19 +496,28 @@ def main():
         ceil = probe_ceilings(B, torch, dev, stream, None if bucketed or quant else bufs, count_logical * elem,
                               reset_inputs)
     per_kernel = []
-    for k, v in sorted(per_kind.items(), key=lambda kv: -kv[1]["ms"] / kv[1]["launches"] * per_call_count[kv[0]]):
+
+    def share_of_call(k):
+        v = per_kind.get(k)
+        return v["ms"] / v["launches"] * per_call_count[k] if v else 0.0
+
+    for k in sorted(per_call_count, key=lambda k: -share_of_call(k)):
+        v = per_kind.get(k)
+        row = {"kernel": labels[k], "launches_per_call": per_call_count[k], "bytes_per_call": per_call_bytes[k]}
+        if not v:  # no launch of this shape was timed (sampling over few calls)
+            per_kernel.append(row)
+            continue
         rate = v["bytes"] / (v["ms"] * 1e-3) / 1e9
-        row = {"kernel": labels[k], "launches_per_call": per_call_count[k],
-               "bytes_per_launch": int(v["bytes"] / v["launches"]),
-               "warm_ms": round(v["ms"] / v["launches"], 5), "warm_GBps": round(rate, 1),
-               "warm_frac_of_peak": round(rate / HBM_PEAK_GBPS, 4)}
+        row.update({"bytes_per_launch": int(v["bytes"] / v["launches"]),
+                    "warm_ms": round(v["ms"] / v["launches"], 5), "warm_GBps": round(rate, 1),
+                    "warm_frac_of_peak": round(rate / HBM_PEAK_GBPS, 4)})
         c = per_cold.get(k)
         if c:
             crate = c["bytes"] / (c["ms"] * 1e-3) / 1e9
             row.update({"cold_ms": round(c["ms"] / c["launches"], 5), "cold_GBps": round(crate, 1),
                         "cold_frac_of_peak": round(crate / HBM_PEAK_GBPS, 4)})
         if ceil:
-            probe, att = attainable_for(ceil, read_share(k[0], elem))
+            probe, att = attainable_for(ceil, k[0], elem, n)
             row.update({"attainable_probe": probe, "attainable_GBps": att,
                         "warm_frac_of_attainable": round(rate / att, 4)})
             if c:
@@ -557,7 +591,7 @@ def main():
                             "algbw_GBps": round(op_alg, 1), "hbm_model_GBps": round(op_gbps, 1),
                             "hbm_model_frac_of_peak": round(op_gbps / HBM_PEAK_GBPS, 4)}
         if ceil:
-            fold = [k for k in ceil if k.startswith("fold")]
+            fold = [k for k in ceil if k == f"fold {n}:{n}"]
             extra["onepass"]["frac_of_copy_ceiling"] = round(op_gbps / ceil["copy 1:1"]["GBps"], 4)
             if fold:
                 extra["onepass"]["frac_of_fold_probe"] = round(op_gbps / ceil[fold[0]]["GBps"], 4)
@@ -690,6 +724,62 @@ def main():
         B.ar_bucket_plan_destroy(plan)
     else:
         B.ar_plan_destroy(plan)
+    print(json.dumps(out), flush=True)
+
+
+def latency_main(args, B, np, torch):
+    """Time per all-reduce by message size: 16 ranks of fp32, per rank 4 KiB,
+    1 MiB and 16 MiB, for the ring, hierarchical 2 x 8, Rabenseifner and
+    recursive doubling, in the step mode (eager, and replayed as a HIP graph)
+    and the one-pass mode.  Each figure is the mean over back-to-back calls
+    made through a prepared call (arguments checked and marshalled once), so
+    it is the library's own cost per call: the launches' host and device
+    start-up (the alpha of the pages' cost model on one GPU) plus the bytes.
+    The step-mode points are also fitted to launches x alpha + model bytes / B."""
+    n = 16
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream(dev)
+    rows = []
+    for per_rank in (4096, 1 << 20, 16 << 20):
+        count = per_rank // 4
+        bufs = [torch.randn(count, device=dev) for _ in range(n)]
+        for sched, g in (("ring", 1), ("hierarchical", 8), ("rabenseifner", 1), ("recursive_doubling", 1)):
+            for mode, graph in (("steps", False), ("steps", True), ("onepass", False)):
+                p = B.ar_plan_create(n, g, count, "fp32", sched)
+                B.ar_plan_set_exec(p, mode)
+                B.ar_plan_set_graph(p, graph)
+                call = B.prepared_call(p, bufs, None, s)
+                reps = 400 if per_rank <= (1 << 20) else 100
+                for _ in range(20):
+                    call()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    call()
+                torch.cuda.synchronize()
+                us = (time.perf_counter() - t0) / reps * 1e6
+                st = B.ar_plan_stats(p)
+                B.ar_plan_destroy(p)
+                rows.append({"bytes_per_rank": per_rank, "schedule": sched, "exec": mode, "graph": graph,
+                             "launches": st["launches"], "hbm_model_bytes": st["hbm_bytes_model"],
+                             "us_per_call": round(us, 2)})
+                log(json.dumps(rows[-1]))
+        del bufs
+    # least squares over the eager step-mode points: us = launches * alpha + bytes / B
+    pts = [r for r in rows if r["exec"] == "steps" and not r["graph"]]
+    A = np.array([[r["launches"], r["hbm_model_bytes"] / 1e9] for r in pts], dtype=np.float64)
+    y = np.array([r["us_per_call"] for r in pts], dtype=np.float64)
+    (alpha_us, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
+    one = [r["us_per_call"] for r in rows if r["exec"] == "onepass" and r["bytes_per_rank"] == 4096]
+    out = {"metric": "all-reduce time per call, 16 ranks fp32, 4 KiB per rank, one-pass mode", "value": min(one),
+           "unit": "us", "n_gpus": 1, "steps": None, "warmup": 20, "ms_per_step": round(min(one) / 1e3, 5),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "latency sweep: 16 ranks fp32, 4 KiB / 1 MiB / 16 MiB per rank, ring, "
+                                  "hierarchical 2x8, Rabenseifner, recursive doubling; step mode eager and graph, "
+                                  "one-pass", "rows": rows,
+                      "fit_alpha_us_per_launch": round(float(alpha_us), 3),
+                      "fit_bandwidth_GBps": round(1e6 / float(inv_b), 1) if inv_b > 0 else None},
+           "roofline": None, "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 
