@@ -204,7 +204,43 @@ def traffic_record(kernel_name, workload, exec_mode):
     return None
 
 
-def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=None, gib=4, reps=5):
+def probe_best(B, torch, stream, src, dst, nb, reps=5, restore=None):
+    """Best rate over 1, 2, 4 units per thread and the three cache policies
+    of the probe on these buffers (median of `reps` launches after two)."""
+    best = None
+    for units in (1, 2, 4):
+        for policy in (0, 1, 2):
+            ts = []
+            for r in range(reps + 2):
+                if restore is not None:
+                    restore()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                B.ar_hbm_probe(src, dst, nb, units, policy, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if r >= 2:
+                    ts.append(e0.elapsed_time(e1))
+            ts.sort()
+            med = ts[len(ts) // 2]
+            gbps = (len(src) + len(dst)) * nb / (med * 1e-3) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "ms": round(med, 4), "units": units, "policy": policy,
+                        "read_share": len(src) / (len(src) + len(dst)), "bytes": (len(src) + len(dst)) * nb}
+    return best
+
+
+def kernel_streams(kind):
+    """(sources, destinations) of a step kernel's launch, or None."""
+    fam = kind & 0xF00
+    if fam == 0x100:
+        return (2, 2) if kind & 8 else (2, 1)
+    if fam == 0x200:
+        return (1, 1)
+    return None
+
+
+def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=None, matched=(), gib=4, reps=5):
     """Attainable HBM bandwidth of this GPU for the kernels' read/write mixes,
     measured with the library's own probe kernel (ar_hbm_probe) on buffers of
     `gib` GiB of random fp32 (far larger than the 256 MB device cache): for
@@ -212,7 +248,11 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
     policies, each the median of `reps` event-timed launches after two
     untimed ones.  With rank_bufs, also the one-pass mix on the workload's
     own buffers: every rank read and every rank written, in place (each
-    launch on the inputs restored by `restore`, outside its events)."""
+    launch on the inputs restored by `restore`, outside its events).
+    matched: (name, sources, destinations, bytes per buffer) mixes measured
+    on the first bytes of the same buffers: a step kernel's streams at its
+    own launch size, so that the launch's start-up and drain weigh as they
+    do in the kernel."""
     nbytes = gib << 30
     bufs = [torch.randn(nbytes // 4, device=dev) for _ in range(4)]
     torch.cuda.synchronize()
@@ -231,27 +271,10 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
                   (f"fan 1:{n - 1}", rank_bufs[:1], rank_bufs[1:], rank_bytes)]
     out = {}
     for name, src, dst, nb in mixes:
-        best = None
-        for units in (1, 2, 4):
-            for policy in (0, 1, 2):
-                ts = []
-                for r in range(reps + 2):
-                    if restore is not None and rank_bufs is not None and any(b is rank_bufs[0] for b in dst):
-                        restore()
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    B.ar_hbm_probe(src, dst, nb, units, policy, stream)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    if r >= 2:
-                        ts.append(e0.elapsed_time(e1))
-                ts.sort()
-                med = ts[len(ts) // 2]
-                gbps = (len(src) + len(dst)) * nb / (med * 1e-3) / 1e9
-                if best is None or gbps > best["GBps"]:
-                    best = {"GBps": round(gbps, 1), "ms": round(med, 4), "units": units, "policy": policy,
-                            "read_share": len(src) / (len(src) + len(dst)), "bytes": (len(src) + len(dst)) * nb}
-        out[name] = best
+        writes_ranks = rank_bufs is not None and any(b is rank_bufs[0] for b in dst)
+        out[name] = probe_best(B, torch, stream, src, dst, nb, reps, restore if writes_ranks else None)
+    for name, ns, nd, nb in matched:
+        out[name] = probe_best(B, torch, stream, bufs[:ns], bufs[ns:ns + nd], min(nb, nbytes), reps)
     del bufs
     torch.cuda.empty_cache()
     return out
@@ -493,8 +516,14 @@ def main():
         per_cold, _, _ = timed_run(evict)
         del evict
         torch.cuda.empty_cache()
+        matched = []
+        for k in per_call_count:  # each step-kernel shape's streams at its mean launch size
+            st_ = kernel_streams(k[0])
+            if st_ and per_kind.get(k):
+                nb = per_call_bytes[k] // per_call_count[k] // sum(st_) // 16 * 16
+                matched.append((f"{labels[k]} size", st_[0], st_[1], nb))
         ceil = probe_ceilings(B, torch, dev, stream, None if bucketed or quant else bufs, count_logical * elem,
-                              reset_inputs)
+                              reset_inputs, matched)
     per_kernel = []
 
     def share_of_call(k):
@@ -522,11 +551,17 @@ def main():
                         "warm_frac_of_attainable": round(rate / att, 4)})
             if c:
                 row["cold_frac_of_attainable"] = round(crate / att, 4)
+            sm = ceil.get(f"{labels[k]} size")
+            if sm:  # the same streams at this launch's size
+                row.update({"size_matched_probe_GBps": sm["GBps"], "warm_frac_of_size_matched": round(rate / sm["GBps"], 4)})
         per_kernel.append(row)
         if k == dom:
             if ceil:
                 roofline.update({"attainable_GBps": row["attainable_GBps"], "attainable_probe": probe,
                                  "frac_of_attainable": row["warm_frac_of_attainable"]})
+                if "size_matched_probe_GBps" in row:
+                    roofline.update({"size_matched_GBps": row["size_matched_probe_GBps"],
+                                     "frac_of_size_matched": row["warm_frac_of_size_matched"]})
             if c:
                 roofline["cold"] = {"avg_launch_ms": row["cold_ms"], "achieved": row["cold_GBps"],
                                     "frac": row["cold_frac_of_peak"],
@@ -708,8 +743,8 @@ def main():
         "cpu_baseline": cpu,
     }
     if ceil:
-        out["config"]["hbm_ceiling"] = {k: {"GBps": v["GBps"], "units": v["units"], "policy": v["policy"]}
-                                        for k, v in ceil.items()}
+        out["config"]["hbm_ceiling"] = {k: {"GBps": v["GBps"], "units": v["units"], "policy": v["policy"],
+                                            "bytes": v["bytes"]} for k, v in ceil.items()}
     if extra:
         out["config"]["compare"] = extra
     if quant:
