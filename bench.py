@@ -88,6 +88,15 @@ def kernel_label(kind, shape=None, nranks=None):
     if kind & 3 == 3:  # one-pass fold of an INT8 plan
         return "q_" + KIND_NAMES[fam]
     bf, each = ("true" if kind & 3 else "false"), ("true" if kind & 3 == 2 else "false")
+    if shape and shape.get("lds_bytes"):  # the LDS-staged fold
+        if fam == 0x500 and nranks:
+            nmax = 1 << max(0, (nranks - 1).bit_length())
+            fold = f"TreeFold<{nmax}, {'true' if nranks < nmax else 'false'}>"
+        elif fam == 0x600 and nranks:
+            fold = f"DTreeFoldOp<{nranks}>"
+        else:
+            fold = {0x300: "RingFold", 0x400: "HierFold", 0x500: "TreeFold", 0x600: "DTreeFoldOp"}[fam]
+        return f"onepass_lds<{bf}, {each}, {shape['units']}, {shape['cpol']}, {fold}>"
     if shape and fam in (0x300, 0x400):
         return f"{KIND_NAMES[fam]}<{bf}, {each}, {shape['units']}, {shape['batch']}>"
     if shape and fam == 0x500 and nranks:
@@ -204,12 +213,13 @@ def traffic_record(kernel_name, workload, exec_mode):
     return None
 
 
-def probe_best(B, torch, stream, src, dst, nb, reps=5, restore=None):
+def probe_best(B, torch, stream, src, dst, nb, reps=5, restore=None, split=False):
     """Best rate over 1, 2, 4 units per thread and the three cache policies
-    of the probe on these buffers (median of `reps` launches after two)."""
+    of the probe on these buffers (median of `reps` launches after two);
+    split: each workgroup stores into one destination only."""
     best = None
     for units in (1, 2, 4):
-        for policy in (0, 1, 2):
+        for policy in ((4, 5, 6) if split else (0, 1, 2)):
             ts = []
             for r in range(reps + 2):
                 if restore is not None:
@@ -267,12 +277,14 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
         mixes += [(f"fold {n}:{n}", rank_bufs, rank_bufs, rank_bytes),
                   (f"read {n}:0", rank_bufs, [], rank_bytes),
                   (f"write 0:{n}", [], rank_bufs, rank_bytes),
+                  (f"write 0:{n} split", [], rank_bufs, rank_bytes),
                   (f"fold {n}:1", rank_bufs, rank_bufs[:1], rank_bytes),
                   (f"fan 1:{n - 1}", rank_bufs[:1], rank_bufs[1:], rank_bytes)]
     out = {}
     for name, src, dst, nb in mixes:
         writes_ranks = rank_bufs is not None and any(b is rank_bufs[0] for b in dst)
-        out[name] = probe_best(B, torch, stream, src, dst, nb, reps, restore if writes_ranks else None)
+        out[name] = probe_best(B, torch, stream, src, dst, nb, reps, restore if writes_ranks else None,
+                               split=name.endswith(" split"))
     for name, ns, nd, nb in matched:
         out[name] = probe_best(B, torch, stream, bufs[:ns], bufs[ns:ns + nd], min(nb, nbytes), reps)
     del bufs
@@ -630,6 +642,14 @@ def main():
             extra["onepass"]["frac_of_copy_ceiling"] = round(op_gbps / ceil["copy 1:1"]["GBps"], 4)
             if fold:
                 extra["onepass"]["frac_of_fold_probe"] = round(op_gbps / ceil[fold[0]]["GBps"], 4)
+            rd, wr = ceil.get(f"read {n}:0"), ceil.get(f"write 0:{n} split")
+            if rd and wr:
+                # the LDS-staged fold reads every rank and writes every rank, one
+                # buffer per wave: its two halves at their probe rates, one after
+                # the other
+                staged = 1.0 / (0.5 / rd["GBps"] + 0.5 / wr["GBps"])
+                extra["onepass"]["staged_phases_GBps"] = round(staged, 1)
+                extra["onepass"]["frac_of_staged_phases"] = round(op_gbps / staged, 4)
 
     # ---- the same exec mode replayed as one HIP graph per call
     if not args.no_extra:

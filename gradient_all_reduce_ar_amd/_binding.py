@@ -112,7 +112,7 @@ def _declare(L):
         "ar_plan_check_guards": ([P], ctypes.c_int),
         "ar_bucket_set_guard": ([P, sz], ctypes.c_int),
         "ar_bucket_check_guards": ([P], ctypes.c_int),
-        "ar_plan_launch_shape": ([P, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(ctypes.c_uint32), pi32],
+        "ar_plan_launch_shape": ([P, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(ctypes.c_uint32), pi32, pi32],
                                  ctypes.c_int),
         "ar_hbm_probe": ([P, i32, P, i32, sz, i32, i32, P], ctypes.c_int),
         "ar_plan_set_graph": ([P, ctypes.c_int], ctypes.c_int),
@@ -435,17 +435,19 @@ def ar_plan_set_profiling_evict(plan, buf, nbytes):
 
 
 def ar_plan_launch_shape(plan, i):
-    """dict(cold, units, cpol, batch, grid_x, threads) of launch i's kernel."""
+    """dict(cold, units, cpol, batch, grid_x, threads, lds_bytes) of launch i's kernel."""
     v = [ctypes.c_int32() for _ in range(4)]
-    gx, th = ctypes.c_uint32(), ctypes.c_int32()
-    _check(lib().ar_plan_launch_shape(plan, i, *[ctypes.byref(x) for x in v], ctypes.byref(gx), ctypes.byref(th)))
+    gx, th, lds = ctypes.c_uint32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ar_plan_launch_shape(plan, i, *[ctypes.byref(x) for x in v], ctypes.byref(gx), ctypes.byref(th),
+                                      ctypes.byref(lds)))
     return {"cold": v[0].value, "units": v[1].value, "cpol": v[2].value, "batch": v[3].value,
-            "grid_x": gx.value, "threads": th.value}
+            "grid_x": gx.value, "threads": th.value, "lds_bytes": lds.value}
 
 
 def ar_hbm_probe(srcs, dsts, nbytes, units=2, policy=1, stream=None):
     """Each 16-byte unit of every dst gets the fp32 sum of that unit of every
-    src (policy 0 plain, 1 nt loads + sc1 stores, 2 nt loads and stores)."""
+    src (policy 0 plain, 1 nt loads + sc1 stores, 2 nt loads and stores;
+    policy | 4: each workgroup stores one dst only)."""
     sa = (ctypes.c_void_p * max(len(srcs), 1))(*[_ptr(b) for b in srcs])
     da = (ctypes.c_void_p * max(len(dsts), 1))(*[_ptr(b) for b in dsts])
     _check(lib().ar_hbm_probe(ctypes.cast(sa, ctypes.c_void_p), len(srcs), ctypes.cast(da, ctypes.c_void_p),

@@ -190,7 +190,7 @@ void lower_launches(ar_plan_t *pl) {
     const bool quant = is_quant_kind(L.kind);
     const bool cold = !quant && !out_scratch && ar::launch_write_bytes(pl->p, L) > pl->p.cache_bytes;
     pl->cold.push_back(cold);
-    const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold);
+    const int64_t tile = quant ? ar_dev::q_tile_blocks(L.kind) : ar_dev::tile_elems(L.kind, cold, pl->p.nranks);
     int64_t gx = 0;
     for (const ar::Op &o : L.ops) {
       pl->host_ops.push_back({o.lo, o.hi, o.a, o.b, o.o, o.o2, o.aux, 0});
@@ -202,7 +202,10 @@ void lower_launches(ar_plan_t *pl) {
     }
     // a dispatch holds at most 2^32 - 1 work-items per grid dimension (here
     // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
-    const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
+    const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind, pl->p.nranks);
+    // the LDS-staged folds walk their op's tiles with the grid's stride, so
+    // a grid capped at the dispatch limit still covers every tile
+    if (!quant && ar_dev::lds_staged(L.kind, pl->p.nranks)) gx = std::min<int64_t>(gx, 0x7fffffff / threads);
     if (gx * threads > 0x7fffffff || static_cast<int64_t>(L.ops.size()) > ar::kMaxLaunchOps)
       pl->launch_err = "op too large for one launch grid";
     pl->grid_x.push_back(static_cast<uint32_t>(std::min<int64_t>(gx, 0x7fffffff)));
@@ -1066,20 +1069,21 @@ ar_status_t ar_plan_set_profiling_evict(ar_plan_t *plan, void *buf, size_t bytes
 }
 
 ar_status_t ar_plan_launch_shape(const ar_plan_t *plan, int32_t i, int32_t *cold, int32_t *units, int32_t *cpol,
-                                 int32_t *batch, uint32_t *grid_x, int32_t *threads) {
+                                 int32_t *batch, uint32_t *grid_x, int32_t *threads, int32_t *lds_bytes) {
   if (!plan || i < 0 || i >= static_cast<int32_t>(plan->p.launches.size()))
     return fail(AR_ERR_INVALID_ARG, "bad plan or launch index");
   const ar::Launch &L = plan->p.launches[i];
   const bool quant = is_quant_kind(L.kind);
   const bool out_scratch = !L.ops.empty() && L.ops[0].o >= ar::kLocScratch;
-  const ar_dev::KernelShape ks = quant ? ar_dev::KernelShape{0, 0, 0}
-                                       : ar_dev::kernel_shape(L.kind, plan->cold[i] != 0, out_scratch);
+  const ar_dev::KernelShape ks = quant ? ar_dev::KernelShape{0, 0, 0, 0}
+                                       : ar_dev::kernel_shape(L.kind, plan->cold[i] != 0, out_scratch, plan->p.nranks);
   if (cold) *cold = plan->cold[i];
   if (units) *units = ks.units;
   if (cpol) *cpol = ks.cpol;
   if (batch) *batch = ks.batch;
   if (grid_x) *grid_x = plan->grid_x[i];
-  if (threads) *threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind);
+  if (threads) *threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind, plan->p.nranks);
+  if (lds_bytes) *lds_bytes = ks.lds_bytes;
   return AR_OK;
 }
 
@@ -1087,7 +1091,8 @@ ar_status_t ar_hbm_probe(const void *const *src, int32_t nsrc, void *const *dst,
                          int32_t units, int32_t policy, void *stream) {
   if (nsrc < 0 || ndst < 0 || nsrc > ar_dev::kProbeMax || ndst > ar_dev::kProbeMax || (nsrc > 0 && !src) ||
       (ndst > 0 && !dst) || bytes % 16 || bytes > static_cast<size_t>(INT64_MAX) ||
-      (units != 1 && units != 2 && units != 4) || policy < 0 || policy > 2)
+      (units != 1 && units != 2 && units != 4) || policy < 0 || (policy & ~7) != 0 || (policy & 3) > 2 ||
+      ((policy & 4) && ndst < 1))
     return fail(AR_ERR_INVALID_ARG, "bad probe arguments");
   for (int i = 0; i < nsrc; ++i)
     if (!src[i] || reinterpret_cast<uintptr_t>(src[i]) % 16) return fail(AR_ERR_INVALID_ARG, "bad probe source");

@@ -761,6 +761,334 @@ __global__ __launch_bounds__(kOPB) void onepass_dtree(KArgs args) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged one-pass folds: gather, fold, scatter.
+//
+// The register folds above store every finished unit into all N ranks from
+// the thread that folded it, so each wave issues N stores per unit.  On
+// MI355X that store pattern is the limit: 16 buffers of 192 MiB written by
+// waves that store into all 16 take 0.55 ms (5.85 TB/s), written by waves
+// that each store into one buffer 0.47 ms (6.8 TB/s), with the same
+// addresses in flight.  Here a workgroup of min(N, W) waves (W = 16 or 8,
+// lds_waves) stages one tile of every rank in LDS:
+//   gather:  wave w loads the tile of ranks w, w + W, ... into LDS;
+//   fold:    thread j folds 4-byte word j (1 fp32 or 2 bf16 elements) over
+//            the ranks, reading LDS, in the schedule's order, and leaves the
+//            finished word in rank 0's LDS slot (only thread j touches
+//            column j);
+//   scatter: wave w stores the finished tile into ranks w, w + W, ...
+// Barriers separate the phases.  Each element is still produced by one
+// thread with the same adds in the same order as the register folds, so
+// the bits are the same.  A tile holds U 16-byte units per lane and rank
+// (U KiB per rank; fp32 4 elements per unit, bf16 8), so the staging area is
+// N * U KiB, at most 64 KiB.  Tiles that an op's range cuts (its first and
+// last) skip LDS: each word inside the op folds from HBM and is stored into
+// every rank, and the cut words go element by element through the same fold.
+// ---------------------------------------------------------------------------
+constexpr int kLdsUnits = AR_LDS_UNITS;  // 16-byte units per lane and rank in a tile, up to 32 ranks
+static_assert(kLdsUnits >= 1 && kLdsUnits * 32 <= 64, "a staged tile of 32 ranks fits in 64 KiB");
+
+// Size classes by rank count (up to 16, 32 or 64 ranks): units per lane and
+// rank in a tile, and the ranks one of W waves gathers and scatters at most.
+constexpr int lds_class(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+template <int NC, int W>
+struct LdsClass {
+  static constexpr int kU = NC > 32 ? 1 : kLdsUnits;
+  static constexpr int kRanksPerWave = (NC + W - 1) / W;
+};
+
+// 16-byte units: fp32 4 elements, bf16 8.
+template <bool BF>
+struct Unit16 {
+  static constexpr int kE = BF ? 8 : 4;   // elements per unit
+  static constexpr int kES = BF ? 2 : 4;  // bytes per element
+};
+
+// Packets a fold adds: an fp32 word (1 element) or a bf16 word (2), element
+// by element with fold1's rule.
+template <bool EACH>
+__device__ __forceinline__ float fold_p(float a, float b) { return fold1(EACH, a, b); }
+template <bool EACH>
+__device__ __forceinline__ float2 fold_p(float2 a, float2 b) {
+  return make_float2(fold1(EACH, a.x, b.x), fold1(EACH, a.y, b.y));
+}
+__device__ __forceinline__ void set_neg_zero(float &p) { p = -0.0f; }
+__device__ __forceinline__ void set_neg_zero(float2 &p) { p = make_float2(-0.0f, -0.0f); }
+__device__ __forceinline__ void pin(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(float2 &v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+
+// Sources of a fold, each giving rank r's packet: word j of the staged tile
+// (LDS), the word at element e of the rank buffer (HBM), element e (HBM).
+template <bool BF>
+__device__ __forceinline__ std::conditional_t<BF, float2, float> word_value(uint32_t w) {
+  if constexpr (BF) return make_float2(widen(w & 0xffffu), widen(w >> 16));
+  else return __uint_as_float(w);
+}
+template <bool BF>
+struct StagedWord {
+  using P = std::conditional_t<BF, float2, float>;
+  const uint32_t *words;
+  int per_rank;  // words per rank in the tile
+  int j;
+  __device__ __forceinline__ P operator()(int r) const { return word_value<BF>(words[r * per_rank + j]); }
+};
+template <bool BF>
+struct HbmWord {
+  using P = std::conditional_t<BF, float2, float>;
+  const KArgs &a;
+  int64_t e;
+  __device__ __forceinline__ P operator()(int r) const {
+    return word_value<BF>(*reinterpret_cast<const uint32_t *>(static_cast<const char *>(a.rank[r]) + e * (BF ? 2 : 4)));
+  }
+};
+template <bool BF>
+struct HbmElem {
+  using P = float;
+  const KArgs &a;
+  int64_t e;
+  __device__ __forceinline__ float operator()(int r) const { return load1<BF>(static_cast<const char *>(a.rank[r]), e); }
+};
+
+// Final bits of a word (bf16: rounded once, to nearest even).
+__device__ __forceinline__ uint32_t word_bits(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t word_bits(float2 v) { return narrow(v.x) | (narrow(v.y) << 16); }
+
+// acc = ((x_first + x_first+1) + ...) over `count` ranks of the block of
+// ranks starting at rank0, wrapping at wrap_n; four ranks' packets are read
+// together, then added in order.
+template <bool EACH, class Src>
+__device__ __forceinline__ void ring_fold_src(const Src &src, int rank0, int wrap_n, int first, int count,
+                                              typename Src::P &acc) {
+  using P = typename Src::P;
+  constexpr int kB = 4;
+  int r = first;
+  acc = src(rank0 + r);
+  int t = 1;
+  for (; t + kB <= count; t += kB) {
+    P x[kB];
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      r = (r + 1 == wrap_n) ? 0 : r + 1;
+      x[q] = src(rank0 + r);
+    }
+#pragma unroll
+    for (int q = 0; q < kB; ++q) acc = fold_p<EACH>(acc, x[q]);
+  }
+  for (; t < count; ++t) {
+    r = (r + 1 == wrap_n) ? 0 : r + 1;
+    acc = fold_p<EACH>(acc, src(rank0 + r));
+  }
+}
+
+// The schedules' folds of one packet, in the orders of the register kernels
+// above (op.aux as there).
+struct RingFold {
+  static constexpr int kClassMin = 16;
+  static constexpr bool kBalancedTree = false;
+  template <bool EACH, class Src>
+  static __device__ __forceinline__ void run(const KArgs &a, const DevOp &op, const Src &src, typename Src::P &acc) {
+    ring_fold_src<EACH>(src, 0, a.nranks, op.aux, a.nranks, acc);
+  }
+};
+
+struct HierFold {
+  static constexpr int kClassMin = 16;
+  static constexpr bool kBalancedTree = false;
+  template <bool EACH, class Src>
+  static __device__ __forceinline__ void run(const KArgs &a, const DevOp &op, const Src &src, typename Src::P &acc) {
+    const int G = a.group_size, M = a.nranks / G;
+    const int lstart = op.aux & 0xff;
+    int g = op.aux >> 8;
+    ring_fold_src<EACH>(src, g * G, G, lstart, G, acc);
+    for (int m = 1; m < M; ++m) {
+      g = (g + 1 == M) ? 0 : g + 1;
+      typename Src::P part;
+      ring_fold_src<EACH>(src, g * G, G, lstart, G, part);
+      acc = fold_p<EACH>(acc, part);
+    }
+  }
+};
+
+// Balanced tree over NMAX leaves in index order, folded as the binary
+// counter of tree_push (leaf r joins, from the nearest outward, the complete
+// aligned blocks that end just before it; the joined block waits in slot k
+// for its right sibling); leaves n .. NMAX - 1 are -0 when PAD.  Leaves come
+// in batches of 4 whose adds finish (the live partial sums pinned) before
+// the next batch's reads, so few packets are live at a time.
+template <bool EACH, int L, class P>
+__device__ __forceinline__ void tree_push_p(P (&slot)[L + 1], int r, P x) {
+#pragma unroll
+  for (int k = 0; k <= L; ++k) {
+    if ((r >> k) & 1) {
+      x = fold_p<EACH>(slot[k], x);
+    } else {
+      slot[k] = x;
+      return;
+    }
+  }
+}
+
+template <int NMAX, bool PAD>
+struct TreeFold {
+  static constexpr int kClassMin = NMAX;
+  static constexpr bool kBalancedTree = true;
+  template <bool EACH, class Src>
+  static __device__ __forceinline__ void run(const KArgs &a, const DevOp &, const Src &src, typename Src::P &acc) {
+    using P = typename Src::P;
+    constexpr int L = ilog2(NMAX), kB = NMAX < 4 ? NMAX : 4;
+    P slot[L + 1];
+    static_for<NMAX / kB>([&](auto bic) {
+      constexpr int bi = decltype(bic)::value;
+      P x[kB];
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        if (!PAD || bi * kB + q < a.nranks) x[q] = src(bi * kB + q);
+        else set_neg_zero(x[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < kB; ++q) tree_push_p<EACH, L>(slot, bi * kB + q, x[q]);
+#pragma unroll
+      for (int j = 0; j <= L; ++j)
+        if ((((bi + 1) * kB) >> j) & 1) pin(slot[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    acc = slot[L];
+  }
+};
+
+// Double binary tree: D(c, b) = (x_c + D(c - b/2, b/2)) + D(c + b/2, b/2).
+// x_c + D(c - b/2, b/2) is formed before the right subtree starts, so one
+// packet per level is live.  (Pinning finished subtrees as the balanced tree
+// does made the compiler spill at 32 and 64 ranks.)
+template <bool EACH, int C, int B>
+struct DTreeSrc {
+  template <class Src>
+  static __device__ __forceinline__ void run(const Src &src, typename Src::P &out) {
+    out = src(C);
+    if constexpr (B > 1) {
+      typename Src::P sub;
+      DTreeSrc<EACH, C - B / 2, B / 2>::run(src, sub);
+      out = fold_p<EACH>(out, sub);
+      DTreeSrc<EACH, C + B / 2, B / 2>::run(src, sub);
+      out = fold_p<EACH>(out, sub);
+    }
+  }
+};
+// op.aux = 0: tree 1, x_0 + D(N/2, N/2); 1: tree 2, x_{N-1} + D(N/2 - 1, N/2).
+template <int N>
+struct DTreeFoldOp {
+  static constexpr int kClassMin = N;
+  static constexpr bool kBalancedTree = false;
+  template <bool EACH, class Src>
+  static __device__ __forceinline__ void run(const KArgs &, const DevOp &op, const Src &src, typename Src::P &acc) {
+    typename Src::P sub;
+    if (op.aux == 0) {
+      acc = src(0);
+      DTreeSrc<EACH, N / 2, N / 2>::run(src, sub);
+    } else {
+      acc = src(N - 1);
+      DTreeSrc<EACH, N / 2 - 1, N / 2>::run(src, sub);
+    }
+    acc = fold_p<EACH>(acc, sub);
+  }
+};
+
+// NC: rank-count size class, W: waves per workgroup at most (LdsClass); CP:
+// store cache policy.
+template <bool BF, bool EACH, int NC, int W, int CP, class F>
+__global__ __launch_bounds__(64 * W) void onepass_lds(KArgs args) {
+  using U16 = Unit16<BF>;
+  constexpr int kE = U16::kE, kES = U16::kES;
+  constexpr int U = LdsClass<NC, W>::kU, kRPW = LdsClass<NC, W>::kRanksPerWave;
+  constexpr int kUnits = 64 * U;                                // units per rank in a tile
+  constexpr int kWords = kUnits * 4;                            // 4-byte words per rank in a tile
+  constexpr int64_t kTile = static_cast<int64_t>(kUnits) * kE;  // elements
+  extern __shared__ u32x4 stage[];                              // [nranks][kUnits]
+  const int n = args.nranks;
+  const int waves = static_cast<int>(blockDim.x >> 6);
+  // the wave index is uniform across the wave: with it in a scalar register
+  // the rank pointers come from scalar loads of the kernel arguments
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const BlockCoord bc = block_coord();
+  const DevOp op = args.ops[bc.op];
+  const int64_t t_end = (op.hi + kTile - 1) / kTile;
+  for (int64_t t = op.lo / kTile + bc.tile; t < t_end; t += bc.stride) {
+    const int64_t base = t * kTile;
+    if (base >= op.lo && base + kTile <= op.hi) {
+      // gather: every load of this wave in flight before the LDS writes
+      u32x4 x[kRPW][U];
+#pragma unroll
+      for (int k = 0; k < kRPW; ++k) {
+        const int r = wave + k * waves;
+        if (r < n) {
+          const char *p = static_cast<const char *>(args.rank[r]) + base * kES;
+#pragma unroll
+          for (int u = 0; u < U; ++u) x[k][u] = ld<u32x4>(p + (u * 64 + lane) * 16);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRPW; ++k) {
+        const int r = wave + k * waves;
+        if (r < n) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) stage[r * kUnits + u * 64 + lane] = x[k][u];
+        }
+      }
+      __syncthreads();
+      // fold: word j (4 bytes: 1 fp32 or 2 bf16 elements) of every rank,
+      // in the schedule's order, one thread per word
+      {
+        uint32_t *words = reinterpret_cast<uint32_t *>(stage);
+        for (int j = static_cast<int>(threadIdx.x); j < kWords; j += static_cast<int>(blockDim.x)) {
+          typename StagedWord<BF>::P acc;
+          F::template run<EACH>(args, op, StagedWord<BF>{words, kWords, j}, acc);
+          words[j] = word_bits(acc);
+        }
+      }
+      __syncthreads();
+      // scatter
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = stage[u * 64 + lane];
+#pragma unroll
+      for (int k = 0; k < kRPW; ++k) {
+        const int r = wave + k * waves;
+        if (r < n) {
+          char *p = static_cast<char *>(args.rank[r]) + base * kES;
+#pragma unroll
+          for (int u = 0; u < U; ++u) st_cp<CP, u32x4>(p, static_cast<uint32_t>(u * 64 + lane) * 16, v[u]);
+        }
+      }
+      // the next tile's gather overwrites rank 0's slot, which the scatter
+      // just read
+      if (t + bc.stride < t_end) __syncthreads();
+    } else {
+      // a tile the op's range cuts: words inside the op fold from HBM and go
+      // to every rank; the words it cuts go element by element
+      constexpr int kWE = kE / 4;  // elements per word
+      for (int j = static_cast<int>(threadIdx.x); j < kWords; j += static_cast<int>(blockDim.x)) {
+        const int64_t e0 = base + static_cast<int64_t>(j) * kWE;
+        if (e0 >= op.lo && e0 + kWE <= op.hi) {
+          typename HbmWord<BF>::P acc;
+          F::template run<EACH>(args, op, HbmWord<BF>{args, e0}, acc);
+          const uint32_t bits = word_bits(acc);
+          for (int r = 0; r < n; ++r)
+            *reinterpret_cast<uint32_t *>(static_cast<char *>(args.rank[r]) + e0 * kES) = bits;
+          continue;
+        }
+        for (int k = 0; k < kWE; ++k) {
+          const int64_t e = e0 + k;
+          if (e < op.lo || e >= op.hi) continue;
+          float acc;
+          F::template run<EACH>(args, op, HbmElem<BF>{args, e}, acc);
+          store_all1(args, BF, e, acc);
+        }
+      }
+    }
+  }
+}
+
 // Step kernels come in two shapes: 2 units per thread, and 1 unit per thread
 // (more waves in flight).  The 1-unit shape is faster (measured on MI355X)
 // for launches that write more into rank buffers than the 256 MB Infinity
@@ -854,10 +1182,114 @@ hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// LDS-staged folds: store policies, waves per workgroup and dynamic LDS
+// bytes (N * U KiB).
+constexpr int kCpolLdsF32 = AR_CPOL_LDS_F32, kCpolLdsBF16 = AR_CPOL_LDS_BF16;
+int lds_units_of(int n) { return n > 32 ? LdsClass<64, 8>::kU : LdsClass<32, 8>::kU; }
+size_t lds_bytes(int n) { return static_cast<size_t>(n) * 64 * lds_units_of(n) * 16; }
+// Workgroups of 16 waves (one rank each) for folds of up to 16 ranks in fp32
+// and in bf16 with one rounding, except the balanced tree in bf16; 8 waves
+// otherwise, so that more workgroups share a CU.  Measured on MI355X with
+// 16 x 192 MiB, 32 x 96 MiB and 64 x 48 MiB: fp32 at 16 ranks 5.6-5.7 TB/s
+// with 8 waves, 5.9-6.2 with 16; bf16 rounded at each add at 16 ranks
+// 5.2-5.6 with 16, 5.6-5.8 with 8; the bf16 tree at 16 ranks 5.2 with 16,
+// 5.6 with 8; above 16 ranks 8 waves were as fast or faster (up to 30% at
+// 64 ranks in bf16).
+int lds_waves(int32_t kind, int n) {
+  const int dt = kind & 3;
+  const bool tree = (kind & 0xF00) == kKindTree;
+  return (n <= 16 && (dt == 0 || (dt == 1 && !tree))) ? 16 : 8;
+}
+int lds_threads(int32_t kind, int n) { return 64 * std::max(1, std::min(n, lds_waves(kind, n))); }
+
+// F::kClassMin: the smallest size class the fold's rank count may take.
+template <bool BF, bool EACH, int NC, int W, class F>
+hipError_t launch_lds_cw(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  constexpr int CP = BF ? kCpolLdsBF16 : kCpolLdsF32;
+  constexpr int C = NC > F::kClassMin ? NC : F::kClassMin;
+  using LC = LdsClass<C, W>;
+  // the staging area holds U units per lane of every rank, and the waves
+  // cover every rank
+  const int threads = lds_threads(kind, a.nranks);
+  if (a.nranks < 1 || a.nranks > C || LC::kU != lds_units_of(a.nranks) || threads > 64 * W ||
+      LC::kRanksPerWave * (threads / 64) < a.nranks)
+    return hipErrorInvalidValue;
+  AR_LAUNCH((onepass_lds<BF, EACH, C, W, CP, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
+  return hipGetLastError();
+}
+// 16-wave workgroups exist only where lds_waves picks them (up to 16 ranks,
+// fp32, or bf16 rounded once outside the balanced tree).
+template <bool BF, bool EACH, int NC, class F>
+hipError_t launch_lds_c(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  if constexpr (NC <= 16 && F::kClassMin <= 16 && !EACH && !(BF && F::kBalancedTree)) {
+    if (lds_waves(kind, a.nranks) == 16) return launch_lds_cw<BF, EACH, NC, 16, F>(kind, grid, a, s);
+  }
+  return launch_lds_cw<BF, EACH, NC, 8, F>(kind, grid, a, s);
+}
+
+template <bool BF, bool EACH, class F>
+hipError_t launch_lds_n(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (lds_class(a.nranks)) {
+    case 16: return launch_lds_c<BF, EACH, 16, F>(kind, grid, a, s);
+    case 32: return launch_lds_c<BF, EACH, 32, F>(kind, grid, a, s);
+    default: return launch_lds_c<BF, EACH, 64, F>(kind, grid, a, s);
+  }
+}
+
+template <bool BF, bool EACH>
+hipError_t launch_lds_tree(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (a.nranks) {
+    case 2: return launch_lds_c<BF, EACH, 16, TreeFold<2, false>>(kind, grid, a, s);
+    case 4: return launch_lds_c<BF, EACH, 16, TreeFold<4, false>>(kind, grid, a, s);
+    case 8: return launch_lds_c<BF, EACH, 16, TreeFold<8, false>>(kind, grid, a, s);
+    case 16: return launch_lds_c<BF, EACH, 16, TreeFold<16, false>>(kind, grid, a, s);
+    case 32: return launch_lds_c<BF, EACH, 32, TreeFold<32, false>>(kind, grid, a, s);
+    case 64: return launch_lds_c<BF, EACH, 64, TreeFold<64, false>>(kind, grid, a, s);
+    default: break;
+  }
+  const int n = a.nranks;
+  if (n == 3) return launch_lds_c<BF, EACH, 16, TreeFold<4, true>>(kind, grid, a, s);
+  if (n < 8) return launch_lds_c<BF, EACH, 16, TreeFold<8, true>>(kind, grid, a, s);
+  if (n < 16) return launch_lds_c<BF, EACH, 16, TreeFold<16, true>>(kind, grid, a, s);
+  if (n < 32) return launch_lds_c<BF, EACH, 32, TreeFold<32, true>>(kind, grid, a, s);
+  if (n < 64) return launch_lds_c<BF, EACH, 64, TreeFold<64, true>>(kind, grid, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <bool BF, bool EACH>
+hipError_t launch_lds_dtree(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (a.nranks) {
+    case 2: return launch_lds_c<BF, EACH, 16, DTreeFoldOp<2>>(kind, grid, a, s);
+    case 4: return launch_lds_c<BF, EACH, 16, DTreeFoldOp<4>>(kind, grid, a, s);
+    case 8: return launch_lds_c<BF, EACH, 16, DTreeFoldOp<8>>(kind, grid, a, s);
+    case 16: return launch_lds_c<BF, EACH, 16, DTreeFoldOp<16>>(kind, grid, a, s);
+    case 32: return launch_lds_c<BF, EACH, 32, DTreeFoldOp<32>>(kind, grid, a, s);
+    case 64: return launch_lds_c<BF, EACH, 64, DTreeFoldOp<64>>(kind, grid, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The LDS-staged fold of a one-pass kind (fp32 0, bf16 1, bf16 rounded at
+// each add 2 in the low bits).
+template <bool BF, bool EACH>
+hipError_t launch_lds_kind(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  switch (kind & 0xF00) {
+    case kKindRing: return launch_lds_n<BF, EACH, RingFold>(kind, grid, a, s);
+    case kKindHier: return launch_lds_n<BF, EACH, HierFold>(kind, grid, a, s);
+    case kKindTree: return launch_lds_tree<BF, EACH>(kind, grid, a, s);
+    case kKindDTree: return launch_lds_dtree<BF, EACH>(kind, grid, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // HBM probe (see hbm_probe): one block per tile of U 16-byte units per
 // thread, sources loaded 8 at a time.  POL 0: plain loads and stores (they
 // allocate in the caches); 1: non-temporal loads, sc1 stores (the step
 // kernels); 2: non-temporal loads and stores (the fp32 one-pass kernels).
+// SPLIT: block b takes tile b / ndst and stores it into destination
+// b mod ndst only (reading every source for it), so that each wave stores
+// into one buffer, as the LDS-staged one-pass folds do; otherwise a block
+// stores its tile into every destination, as the register folds do.
 struct ProbeArgs {
   const char *src[kProbeMax];
   char *dst[kProbeMax];
@@ -869,10 +1301,13 @@ __device__ __forceinline__ f32x4 probe_ld(const char *p) {
   if constexpr (POL == 0) return *reinterpret_cast<const f32x4 *>(p);
   else return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
 }
-template <int U, int POL>
+template <int U, int POL, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void hbm_probe_kernel(ProbeArgs a) {
   constexpr int kCp = POL == 0 ? 0 : POL == 1 ? 16 : 2;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBlock * U;
+  const int64_t tile = SPLIT ? static_cast<int64_t>(blockIdx.x) / a.ndst : static_cast<int64_t>(blockIdx.x);
+  const int d0 = SPLIT ? static_cast<int>(static_cast<int64_t>(blockIdx.x) % a.ndst) : 0;
+  const int d1 = SPLIT ? d0 + 1 : a.ndst;
+  const int64_t t0 = tile * kBlock * U;
   f32x4 acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -897,7 +1332,7 @@ __global__ __launch_bounds__(kBlock) void hbm_probe_kernel(ProbeArgs a) {
       const int64_t i = t0 + static_cast<int64_t>(u) * kBlock + threadIdx.x;
       if (i < a.units) acc[u] += probe_ld<POL>(a.src[s] + i * 16);
     }
-  for (int d = 0; d < a.ndst; ++d)
+  for (int d = d0; d < d1; ++d)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = t0 + static_cast<int64_t>(u) * kBlock + threadIdx.x;
@@ -909,11 +1344,16 @@ __global__ __launch_bounds__(kBlock) void hbm_probe_kernel(ProbeArgs a) {
   }
 }
 
+template <int U, bool SPLIT>
+void launch_probe_s(int pol, dim3 grid, const ProbeArgs &a, hipStream_t s) {
+  if (pol == 0) AR_LAUNCH((hbm_probe_kernel<U, 0, SPLIT>), grid, dim3(kBlock), 0, s, a);
+  else if (pol == 1) AR_LAUNCH((hbm_probe_kernel<U, 1, SPLIT>), grid, dim3(kBlock), 0, s, a);
+  else AR_LAUNCH((hbm_probe_kernel<U, 2, SPLIT>), grid, dim3(kBlock), 0, s, a);
+}
 template <int U>
-void launch_probe(int pol, dim3 grid, const ProbeArgs &a, hipStream_t s) {
-  if (pol == 0) AR_LAUNCH((hbm_probe_kernel<U, 0>), grid, dim3(kBlock), 0, s, a);
-  else if (pol == 1) AR_LAUNCH((hbm_probe_kernel<U, 1>), grid, dim3(kBlock), 0, s, a);
-  else AR_LAUNCH((hbm_probe_kernel<U, 2>), grid, dim3(kBlock), 0, s, a);
+void launch_probe(int pol, bool split, dim3 grid, const ProbeArgs &a, hipStream_t s) {
+  if (split) launch_probe_s<U, true>(pol, grid, a, s);
+  else launch_probe_s<U, false>(pol, grid, a, s);
 }
 
 // Op-table writer: up to kOpsPerWrite ops travel by value in the kernel
@@ -944,8 +1384,10 @@ hipError_t write_ops(DevOp *dst, const DevOp *src, int64_t n, hipStream_t s) {
 
 hipError_t hbm_probe(const void *const *src, int nsrc, void *const *dst, int ndst, int64_t bytes, int units,
                      int policy, hipStream_t s) {
+  const int pol = policy & 3;
+  const bool split = (policy & 4) != 0;
   if (nsrc < 0 || ndst < 0 || nsrc > kProbeMax || ndst > kProbeMax || bytes < 0 || bytes % 16 || policy < 0 ||
-      policy > 2)
+      (policy & ~7) != 0 || pol > 2 || (split && ndst < 1))
     return hipErrorInvalidValue;
   ProbeArgs a{};
   for (int i = 0; i < nsrc; ++i) a.src[i] = static_cast<const char *>(src[i]);
@@ -954,48 +1396,58 @@ hipError_t hbm_probe(const void *const *src, int nsrc, void *const *dst, int nds
   a.ndst = ndst;
   a.units = bytes / 16;
   const int64_t tile = static_cast<int64_t>(kBlock) * units;
-  const int64_t blocks = (a.units + tile - 1) / tile;
+  const int64_t blocks = (a.units + tile - 1) / tile * (split ? ndst : 1);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff / kBlock) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(blocks));
   switch (units) {
-    case 1: launch_probe<1>(policy, grid, a, s); break;
-    case 2: launch_probe<2>(policy, grid, a, s); break;
-    case 4: launch_probe<4>(policy, grid, a, s); break;
+    case 1: launch_probe<1>(pol, split, grid, a, s); break;
+    case 2: launch_probe<2>(pol, split, grid, a, s); break;
+    case 4: launch_probe<4>(pol, split, grid, a, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch) {
+bool lds_staged(int32_t kind, int32_t nranks) {
+  const int32_t fam = kind & 0xF00;
+  return (fam == kKindRing || fam == kKindHier || fam == kKindTree || fam == kKindDTree) && (kind & 3) != 3 &&
+         nranks >= AR_LDS_MIN_RANKS && nranks <= kMaxRanks;
+}
+
+KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nranks) {
+  if (lds_staged(kind, nranks))
+    return {lds_units_of(nranks), (kind & 3) ? kCpolLdsBF16 : kCpolLdsF32, 0, static_cast<int>(lds_bytes(nranks))};
   switch (kind & 0xF00) {
-    case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0};
-    case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0};
+    case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0, 0};
+    case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0, 0};
     case kKindRing:
-      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchBF16}
-                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32};
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchBF16, 0}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32, 0};
     case kKindHier:
-      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchHierBF16}
-                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32};
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, kFoldBatchHierBF16, 0}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, kFoldBatchF32, 0};
     case kKindTree:
-      return (kind & 3) ? KernelShape{kTreeUnrollBF16, kCpolOnePassBF16, kTreeBatchBF16}
-                        : KernelShape{kTreeUnrollF32, kCpolOnePassF32, kTreeBatchF32};
+      return (kind & 3) ? KernelShape{kTreeUnrollBF16, kCpolOnePassBF16, kTreeBatchBF16, 0}
+                        : KernelShape{kTreeUnrollF32, kCpolOnePassF32, kTreeBatchF32, 0};
     case kKindDTree:
-      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, 0}
-                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, 0};
+      return (kind & 3) ? KernelShape{kOnePassUnrollBF16, kCpolOnePassBF16, 0, 0}
+                        : KernelShape{kOnePassUnrollF32, kCpolOnePassF32, 0, 0};
   }
-  return {0, 0, 0};
+  return {0, 0, 0, 0};
 }
 
 dim3 grid_for(uint32_t tiles, uint32_t nops) { return dim3(tiles, nops); }
 
-int block_threads(int32_t kind) {
+int block_threads(int32_t kind, int32_t nranks) {
   const int32_t fam = kind & 0xF00;
+  if (lds_staged(kind, nranks)) return lds_threads(kind, nranks);
   return (fam == kKindReduce || fam == kKindCopy) ? kBlock : kOPB;
 }
 
-int64_t tile_elems(int32_t kind, bool cold) {
+int64_t tile_elems(int32_t kind, bool cold, int32_t nranks) {
   const int64_t u = cold ? kUnrollCold : kUnrollWarm;
+  if (lds_staged(kind, nranks)) return static_cast<int64_t>(64) * lds_units_of(nranks) * ((kind & 3) ? 8 : 4);
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * reduce_unit_elems(kind & 0xF) * reduce_unroll(kind & 0xF, cold);
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
@@ -1009,10 +1461,12 @@ int64_t tiles_per_block(int32_t kind, int32_t nranks) {
   // tile) ran 14% faster with blocks of 8 tiles, at 4 ranks 3-8%; fp32 and 8
   // or more ranks did not change, and the tree kernels were slower (4 ranks
   // bf16: 7%), so only the ring and hierarchical folds walk several tiles.
+  // The LDS-staged folds take one tile per workgroup (a tile of every rank
+  // is at least 8 KiB there).
   const int32_t fam = kind & 0xF00;
-  if ((fam != kKindRing && fam != kKindHier) || AR_ONEPASS_MIN_BLOCK_BYTES <= 0) return 1;
+  if ((fam != kKindRing && fam != kKindHier) || AR_ONEPASS_MIN_BLOCK_BYTES <= 0 || lds_staged(kind, nranks)) return 1;
   // a one-pass tile reads one tile of every rank
-  const int64_t bytes = tile_elems(kind, false) * ((kind & 3) ? 2 : 4) * std::max(nranks, 1);
+  const int64_t bytes = tile_elems(kind, false, nranks) * ((kind & 3) ? 2 : 4) * std::max(nranks, 1);
   return std::max<int64_t>(1, AR_ONEPASS_MIN_BLOCK_BYTES / bytes);
 }
 
@@ -1042,6 +1496,16 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
       if ((kind & 0xFF) == 2) return launch_copy<2>(grid, a, s, cold);
       if ((kind & 0xFF) == 4) return launch_copy<4>(grid, a, s, cold);
       return hipErrorInvalidValue;
+    case kKindRing:
+    case kKindHier:
+    case kKindTree:
+    case kKindDTree:
+      if (!lds_staged(kind, a.nranks)) break;
+      if ((kind & 3) == 2) return launch_lds_kind<true, true>(kind, grid, a, s);
+      if ((kind & 3) == 1) return launch_lds_kind<true, false>(kind, grid, a, s);
+      return launch_lds_kind<false, false>(kind, grid, a, s);
+  }
+  switch (kind & 0xF00) {
     case kKindRing:
       if ((kind & 3) == 2)
         AR_LAUNCH((onepass_ring<true, true, kOnePassUnrollBF16, kFoldBatchBF16>), grid, dim3(kOPB), 0, s, a);

@@ -86,6 +86,22 @@
 #ifndef AR_ONEPASS_MIN_BLOCK_BYTES  // bytes a one-pass block reads at least (0: one tile per block)
 #define AR_ONEPASS_MIN_BLOCK_BYTES 16384
 #endif
+// LDS-staged one-pass folds (gather every rank's tile into LDS, fold, each
+// wave stores into its own ranks): used from AR_LDS_MIN_RANKS ranks up, with
+// AR_LDS_UNITS 16-byte units per lane and rank in a tile (1 above 32 ranks)
+// and these store policies.
+#ifndef AR_LDS_MIN_RANKS
+#define AR_LDS_MIN_RANKS 4
+#endif
+#ifndef AR_LDS_UNITS
+#define AR_LDS_UNITS 2
+#endif
+#ifndef AR_CPOL_LDS_F32
+#define AR_CPOL_LDS_F32 2
+#endif
+#ifndef AR_CPOL_LDS_BF16
+#define AR_CPOL_LDS_BF16 2
+#endif
 #ifndef AR_TREE_UNROLL_F32
 #define AR_TREE_UNROLL_F32 2
 #endif
@@ -166,11 +182,14 @@ int q_block_threads(int32_t kind);
 // kind kKRing / kKHier / kKTree / kKDTree) on stream s.
 hipError_t launch_q(int32_t kind, dim3 grid, const QArgs &a, hipStream_t s);
 
+// Whether a one-pass kind at nranks runs the LDS-staged fold.
+bool lds_staged(int32_t kind, int32_t nranks);
+
 // Tile (elements per block) of a kernel kind in the warm or cold shape.
-int64_t tile_elems(int32_t kind, bool cold);
+int64_t tile_elems(int32_t kind, bool cold, int32_t nranks);
 
 // Threads per workgroup of a kernel kind.
-int block_threads(int32_t kind);
+int block_threads(int32_t kind, int32_t nranks);
 
 // Tiles each block of a launch walks (the kernels loop over an op's tiles
 // with the grid's stride): more than one for the one-pass ring and
@@ -187,14 +206,15 @@ dim3 grid_for(uint32_t tiles, uint32_t nops);
 hipError_t write_ops(DevOp *dst, const DevOp *src, int64_t n, hipStream_t s);
 
 // Template shape of the kernel a launch of `kind` runs: units each thread
-// moves per tile (16-byte fp32 or 8-byte bf16 units), the store cache
-// policy (bits of the store instruction: 2 nt, 16 sc1) and, for the
-// one-pass folds, the ranks whose loads are in flight together (0 for the
-// step kernels).
+// moves per tile (16-byte fp32 or 8-byte bf16 units; 16-byte units per lane
+// and rank for the LDS-staged folds), the store cache policy (bits of the
+// store instruction: 2 nt, 16 sc1), for the register one-pass folds the
+// ranks whose loads are in flight together (0 otherwise), and the dynamic
+// LDS bytes per workgroup (0 except the LDS-staged folds).
 struct KernelShape {
-  int units, cpol, batch;
+  int units, cpol, batch, lds_bytes;
 };
-KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch);
+KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nranks);
 
 // HBM probe: over `bytes` of every buffer (a multiple of 16), each 16-byte
 // unit of every destination receives the fp32 sum of that unit of every

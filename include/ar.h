@@ -341,13 +341,16 @@ ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, in
                                int32_t *a, int32_t *b, int32_t *o, int32_t *o2, int32_t *aux);
 /* Kernel shape of launch i: *cold = 1 for the streaming shape (the launch
  * writes more into rank buffers than the assumed device cache), the units
- * each thread moves per tile (16-byte fp32 or 8-byte bf16 units), the store
+ * each thread moves per tile (16-byte fp32 or 8-byte bf16 units; for the
+ * LDS-staged one-pass folds, 16-byte units per lane and rank), the store
  * cache policy (bits of the store instruction: 2 non-temporal, 16 sc1), the
- * ranks a one-pass fold loads together (0 for step kernels), the workgroups
- * along the tiles and the threads per workgroup (INT8 kernels: units, cpol
- * and batch 0).  Host only. */
+ * ranks a register one-pass fold loads together (0 otherwise), the
+ * workgroups along the tiles, the threads per workgroup and the dynamic LDS
+ * bytes per workgroup (nonzero only for the LDS-staged one-pass folds, which
+ * stage a tile of every rank in LDS before folding it; INT8 kernels: units,
+ * cpol, batch and LDS bytes 0).  Any out pointer may be NULL.  Host only. */
 ar_status_t ar_plan_launch_shape(const ar_plan_t *plan, int32_t i, int32_t *cold, int32_t *units, int32_t *cpol,
-                                 int32_t *batch, uint32_t *grid_x, int32_t *threads);
+                                 int32_t *batch, uint32_t *grid_x, int32_t *threads, int32_t *lds_bytes);
 /* fp32 scratch addressing of launch i: element e of slot s is float
  * s * slot_stride + e - shift of the scratch.  shift is 0 except in a
  * batched bucket plan, whose batches reuse the slots one after another
@@ -442,10 +445,15 @@ ar_status_t ar_plan_launch_times(ar_plan_t *plan, float *ms, int32_t cap, int32_
  * kernels (`units` 16-byte units per thread per tile, 1, 2 or 4).  policy 0:
  * plain loads and stores (they allocate in the device caches); 1:
  * non-temporal loads and sc1 stores (the step kernels' policy); 2:
- * non-temporal loads and stores (the fp32 one-pass kernels').  nsrc = 1,
- * ndst = 1 is a copy; 2, 1 a reduce step's mix; 0, 1 a fill (writes zeros);
- * k, 0 only reads.  At most 64 buffers of each kind; a destination may equal
- * a source (in place).  Enqueued on `stream`.
+ * non-temporal loads and stores (the one-pass kernels').  policy | 4: each
+ * workgroup stores one destination only (workgroup b: tile b / ndst into
+ * destination b mod ndst, reading every source for it; ndst >= 1), so each
+ * wave writes one buffer, the store pattern of the LDS-staged one-pass
+ * folds; without it each workgroup stores its tile into every destination,
+ * the pattern of the register folds.  nsrc = 1, ndst = 1 is a copy; 2, 1 a
+ * reduce step's mix; 0, 1 a fill (writes zeros); k, 0 only reads.  At most
+ * 64 buffers of each kind; a destination may equal a source (in place).
+ * Enqueued on `stream`.
  */
 ar_status_t ar_hbm_probe(const void *const *src, int32_t nsrc, void *const *dst, int32_t ndst, size_t bytes,
                          int32_t units, int32_t policy, void *stream);

@@ -109,3 +109,18 @@ def test_exact_extent_passes_to_c(plan):
     bufs = [FakeTensor((1 << 30) + 64 * r, 2000, elem=2) for r in range(4)]
     with pytest.raises(B.ArError, match="overlap"):
         B.ar_allreduce(plan, bufs)
+
+
+@pytest.mark.parametrize("srcs,dsts,nbytes,units,policy", [
+    ([], [], 4096, 2, 4),              # one destination per workgroup needs a destination
+    ([1 << 30], [2 << 30], 4096, 3, 1),  # 1, 2 or 4 units per thread
+    ([1 << 30], [2 << 30], 4096, 2, 3),  # policies 0-2 (+4)
+    ([1 << 30], [2 << 30], 4096, 2, 8),
+    ([1 << 30], [2 << 30], 4008, 2, 1),  # bytes a multiple of 16
+    ([(1 << 30) + 8], [2 << 30], 4096, 2, 1),  # 16-byte aligned buffers
+])
+def test_probe_arguments_refused(srcs, dsts, nbytes, units, policy):
+    """The probe refuses bad arguments before it launches anything."""
+    with pytest.raises(B.ArError) as ei:
+        B.ar_hbm_probe(srcs, dsts, nbytes, units, policy)
+    assert ei.value.status == B.AR_ERR_INVALID_ARG
