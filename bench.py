@@ -88,15 +88,16 @@ def kernel_label(kind, shape=None, nranks=None):
     if kind & 3 == 3:  # one-pass fold of an INT8 plan
         return "q_" + KIND_NAMES[fam]
     bf, each = ("true" if kind & 3 else "false"), ("true" if kind & 3 == 2 else "false")
-    if shape and shape.get("lds_bytes"):  # the LDS-staged fold
-        if fam == 0x500 and nranks:
+    if shape and shape.get("lds_bytes") and nranks:  # the LDS-staged fold
+        ncls = 16 if nranks <= 16 else 32 if nranks <= 32 else 64  # the rank-count size class
+        if fam == 0x500:
             nmax = 1 << max(0, (nranks - 1).bit_length())
-            fold = f"TreeFold<{nmax}, {'true' if nranks < nmax else 'false'}>"
-        elif fam == 0x600 and nranks:
+            fold, ncls = f"TreeFold<{nmax}, {'true' if nranks < nmax else 'false'}>", max(ncls, nmax)
+        elif fam == 0x600:
             fold = f"DTreeFoldOp<{nranks}>"
         else:
-            fold = {0x300: "RingFold", 0x400: "HierFold", 0x500: "TreeFold", 0x600: "DTreeFoldOp"}[fam]
-        return f"onepass_lds<{bf}, {each}, {shape['units']}, {shape['cpol']}, {fold}>"
+            fold = {0x300: "RingFold", 0x400: "HierFold"}[fam]
+        return f"onepass_lds<{bf}, {each}, {ncls}, {shape['batch']}, {shape['cpol']}, {fold}>"
     if shape and fam in (0x300, 0x400):
         return f"{KIND_NAMES[fam]}<{bf}, {each}, {shape['units']}, {shape['batch']}>"
     if shape and fam == 0x500 and nranks:

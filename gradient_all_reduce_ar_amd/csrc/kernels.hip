@@ -1417,7 +1417,8 @@ bool lds_staged(int32_t kind, int32_t nranks) {
 
 KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nranks) {
   if (lds_staged(kind, nranks))
-    return {lds_units_of(nranks), (kind & 3) ? kCpolLdsBF16 : kCpolLdsF32, 0, static_cast<int>(lds_bytes(nranks))};
+    return {lds_units_of(nranks), (kind & 3) ? kCpolLdsBF16 : kCpolLdsF32, lds_waves(kind, nranks),
+            static_cast<int>(lds_bytes(nranks))};
   switch (kind & 0xF00) {
     case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0, 0};
     case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0, 0};

@@ -209,8 +209,9 @@ hipError_t write_ops(DevOp *dst, const DevOp *src, int64_t n, hipStream_t s);
 // moves per tile (16-byte fp32 or 8-byte bf16 units; 16-byte units per lane
 // and rank for the LDS-staged folds), the store cache policy (bits of the
 // store instruction: 2 nt, 16 sc1), for the register one-pass folds the
-// ranks whose loads are in flight together (0 otherwise), and the dynamic
-// LDS bytes per workgroup (0 except the LDS-staged folds).
+// ranks whose loads are in flight together and for the LDS-staged folds the
+// waves per workgroup at most (0 otherwise), and the dynamic LDS bytes per
+// workgroup (0 except the LDS-staged folds).
 struct KernelShape {
   int units, cpol, batch, lds_bytes;
 };

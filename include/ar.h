@@ -344,7 +344,8 @@ ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, in
  * each thread moves per tile (16-byte fp32 or 8-byte bf16 units; for the
  * LDS-staged one-pass folds, 16-byte units per lane and rank), the store
  * cache policy (bits of the store instruction: 2 non-temporal, 16 sc1), the
- * ranks a register one-pass fold loads together (0 otherwise), the
+ * ranks a register one-pass fold loads together or the waves per workgroup
+ * at most of an LDS-staged fold (0 otherwise), the
  * workgroups along the tiles, the threads per workgroup and the dynamic LDS
  * bytes per workgroup (nonzero only for the LDS-staged one-pass folds, which
  * stage a tile of every rank in LDS before folding it; INT8 kernels: units,
