@@ -786,6 +786,16 @@ __global__ __launch_bounds__(kOPB) void onepass_dtree(KArgs args) {
 // every rank, and the cut words go element by element through the same fold.
 // ---------------------------------------------------------------------------
 constexpr int kLdsUnits = AR_LDS_UNITS;  // 16-byte units per lane and rank in a tile, up to 32 ranks
+// Store policies of the scatter, measured on MI355X (16 ranks, in-place
+// calls back to back): where every rank's output fits in the 256 MB
+// Infinity Cache, sc1 stores leave it there for the next reader (fp32 ring
+// at 8-16 MiB per rank 50.6 -> 42.4 us and 100.2 -> 80.8 us against nt
+// stores); above it nt + sc1 was fastest (192 MiB per rank: 1,023 us
+// against 1,041 with nt and 1,061 with sc1).  The policy is a template
+// argument: with one kernel branching on a launch flag between the two
+// store loops, the balanced-tree folds ran 14% slower at 192 MiB per rank
+// (1,155 against 1,010 us) for reasons the code does not show.
+constexpr int kCpolLdsWarm = AR_CPOL_LDS_WARM, kCpolLdsCold = AR_CPOL_LDS_COLD;
 static_assert(kLdsUnits >= 1 && kLdsUnits * 32 <= 64, "a staged tile of 32 ranks fits in 64 KiB");
 
 // Size classes by rank count (up to 16, 32 or 64 ranks): units per lane and
@@ -994,7 +1004,7 @@ struct DTreeFoldOp {
 };
 
 // NC: rank-count size class, W: waves per workgroup at most (LdsClass); CP:
-// store cache policy.
+// the scatter's store policy (kCpolLdsWarm or kCpolLdsCold).
 template <bool BF, bool EACH, int NC, int W, int CP, class F>
 __global__ __launch_bounds__(64 * W) void onepass_lds(KArgs args) {
   using U16 = Unit16<BF>;
@@ -1182,9 +1192,7 @@ hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// LDS-staged folds: store policies, waves per workgroup and dynamic LDS
-// bytes (N * U KiB).
-constexpr int kCpolLdsF32 = AR_CPOL_LDS_F32, kCpolLdsBF16 = AR_CPOL_LDS_BF16;
+// LDS-staged folds: waves per workgroup and dynamic LDS bytes (N * U KiB).
 int lds_units_of(int n) { return n > 32 ? LdsClass<64, 8>::kU : LdsClass<32, 8>::kU; }
 size_t lds_bytes(int n) { return static_cast<size_t>(n) * 64 * lds_units_of(n) * 16; }
 // Workgroups of 16 waves (one rank each) for folds of up to 16 ranks in fp32
@@ -1205,7 +1213,6 @@ int lds_threads(int32_t kind, int n) { return 64 * std::max(1, std::min(n, lds_w
 // F::kClassMin: the smallest size class the fold's rank count may take.
 template <bool BF, bool EACH, int NC, int W, class F>
 hipError_t launch_lds_cw(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
-  constexpr int CP = BF ? kCpolLdsBF16 : kCpolLdsF32;
   constexpr int C = NC > F::kClassMin ? NC : F::kClassMin;
   using LC = LdsClass<C, W>;
   // the staging area holds U units per lane of every rank, and the waves
@@ -1214,7 +1221,10 @@ hipError_t launch_lds_cw(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s)
   if (a.nranks < 1 || a.nranks > C || LC::kU != lds_units_of(a.nranks) || threads > 64 * W ||
       LC::kRanksPerWave * (threads / 64) < a.nranks)
     return hipErrorInvalidValue;
-  AR_LAUNCH((onepass_lds<BF, EACH, C, W, CP, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
+  if (a.store_cold)
+    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsCold, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
+  else
+    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsWarm, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
   return hipGetLastError();
 }
 // 16-wave workgroups exist only where lds_waves picks them (up to 16 ranks,
@@ -1417,7 +1427,7 @@ bool lds_staged(int32_t kind, int32_t nranks) {
 
 KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nranks) {
   if (lds_staged(kind, nranks))
-    return {lds_units_of(nranks), (kind & 3) ? kCpolLdsBF16 : kCpolLdsF32, lds_waves(kind, nranks),
+    return {lds_units_of(nranks), cold ? kCpolLdsCold : kCpolLdsWarm, lds_waves(kind, nranks),
             static_cast<int>(lds_bytes(nranks))};
   switch (kind & 0xF00) {
     case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0, 0};
@@ -1502,9 +1512,13 @@ hipError_t launch(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s, bool o
     case kKindTree:
     case kKindDTree:
       if (!lds_staged(kind, a.nranks)) break;
-      if ((kind & 3) == 2) return launch_lds_kind<true, true>(kind, grid, a, s);
-      if ((kind & 3) == 1) return launch_lds_kind<true, false>(kind, grid, a, s);
-      return launch_lds_kind<false, false>(kind, grid, a, s);
+      {
+        KArgs b = a;
+        b.store_cold = cold ? 1 : 0;
+        if ((kind & 3) == 2) return launch_lds_kind<true, true>(kind, grid, b, s);
+        if ((kind & 3) == 1) return launch_lds_kind<true, false>(kind, grid, b, s);
+        return launch_lds_kind<false, false>(kind, grid, b, s);
+      }
   }
   switch (kind & 0xF00) {
     case kKindRing:

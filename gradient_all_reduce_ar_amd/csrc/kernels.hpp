@@ -88,19 +88,20 @@
 #endif
 // LDS-staged one-pass folds (gather every rank's tile into LDS, fold, each
 // wave stores into its own ranks): used from AR_LDS_MIN_RANKS ranks up, with
-// AR_LDS_UNITS 16-byte units per lane and rank in a tile (1 above 32 ranks)
-// and these store policies.
+// AR_LDS_UNITS 16-byte units per lane and rank in a tile (1 above 32 ranks),
+// and store policies for launches whose output fits in the assumed device
+// cache (warm: the next reader finds it there) or not (cold).
 #ifndef AR_LDS_MIN_RANKS
 #define AR_LDS_MIN_RANKS 4
 #endif
 #ifndef AR_LDS_UNITS
 #define AR_LDS_UNITS 2
 #endif
-#ifndef AR_CPOL_LDS_F32
-#define AR_CPOL_LDS_F32 2
+#ifndef AR_CPOL_LDS_WARM
+#define AR_CPOL_LDS_WARM 16
 #endif
-#ifndef AR_CPOL_LDS_BF16
-#define AR_CPOL_LDS_BF16 2
+#ifndef AR_CPOL_LDS_COLD
+#define AR_CPOL_LDS_COLD 18
 #endif
 #ifndef AR_TREE_UNROLL_F32
 #define AR_TREE_UNROLL_F32 2
@@ -154,6 +155,7 @@ struct KArgs {
   const DevOp *ops;       // this launch's ops
   int32_t nranks, group_size;
   int32_t nops;           // ops in this launch
+  int32_t store_cold;     // the launch writes more than the assumed device cache (host side only)
 };
 
 // Arguments of the blockwise INT8 kernels (kI8EF plans).  Rank r's code slot
