@@ -68,6 +68,44 @@ def test_replays_match_oracle(sched, n, g, dtype):
         B.ar_plan_destroy(p)
 
 
+@pytest.mark.parametrize("sched,n,g,dtype", [("ring", 16, 1, "fp32"), ("hierarchical", 16, 8, "bf16"),
+                                              ("rabenseifner", 16, 1, "bf16"), ("double_tree", 8, 1, "bf16_each"),
+                                              ("tree", 40, 1, "fp32")])
+@pytest.mark.parametrize("cold", [False, True])
+def test_onepass_replays_match_oracle(sched, n, g, dtype, cold):
+    """The LDS-staged one-pass folds replayed as graphs, with the store
+    policy of a launch that fits the assumed cache and (the cache assumed
+    at 64 KiB) of one that does not."""
+    import torch
+
+    count = 20011
+    gen = "fp32" if dtype == "fp32" else "bf16"
+    xs = workloads.normal_inputs(n, count, seed=n + 3, sigma=1.0, dtype=gen)
+    want = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+    bv = bits_view(dtype)
+    bufs = to_device(xs, dtype)
+    p = B.ar_plan_create(n, g, count, dtype, sched)
+    try:
+        B.ar_plan_set_exec(p, "onepass")
+        if cold:
+            B.ar_plan_set_cache_bytes(p, 64 << 10)
+        shape = B.ar_plan_launch_shape(p, 0)
+        assert shape["lds_bytes"] > 0 and shape["cold"] == int(cold)
+        B.ar_plan_set_graph(p, True)
+        s = torch.cuda.current_stream()
+        for rep in range(3):
+            _say(f"case graph onepass {sched} {dtype} n={n} cold={cold} rep={rep}")
+            _refill(bufs, xs, dtype)
+            B.ar_allreduce(p, bufs, s)
+            torch.cuda.synchronize()
+            got = to_host_bits(bufs, dtype)
+            for r in range(n):
+                np.testing.assert_array_equal(got[r], want[r].view(bv), err_msg=f"rep {rep} rank {r}")
+            _eager_noise()
+    finally:
+        B.ar_plan_destroy(p)
+
+
 def test_graph_cache_eviction_and_profiling_fallback():
     """Nine pointer sets on one plan (the first graph is evicted and later
     captured again); with profiling on the calls run eagerly and log every
