@@ -115,9 +115,13 @@ typedef enum {
  *                          and to the next rank).  Default.
  *   AR_EXEC_STEPS_UNFUSED  one kernel launch per step, no fusion.
  *   AR_EXEC_ONEPASS        one launch for the whole all-reduce: every element
- *                          is read once from each rank, folded in registers in
- *                          the schedule's exact order, and written once to
- *                          each rank.
+ *                          is read once from each rank, folded in the
+ *                          schedule's exact order, and written once to each
+ *                          rank.  From 4 ranks up (fp32 and bf16) a workgroup
+ *                          stages a tile of every rank in LDS, folds it one
+ *                          word per thread, and each wave stores its own
+ *                          ranks; otherwise, and for AR_INT8_EF, each thread
+ *                          folds in registers and stores into every rank.
  */
 typedef enum { AR_EXEC_STEPS = 0, AR_EXEC_STEPS_UNFUSED = 1, AR_EXEC_ONEPASS = 2 } ar_exec_t;
 
