@@ -293,13 +293,27 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
     return out
 
 
-def attainable_for(ceil, kind, elem, nranks):
+def staged_bound(ceil, nranks):
+    """GB/s of reading every rank and then writing every rank with each
+    workgroup storing one rank, at the probes' rates, one after the other
+    (the LDS-staged one-pass folds' two halves), or None."""
+    rd, wr = ceil.get(f"read {nranks}:0"), ceil.get(f"write 0:{nranks} split")
+    if not rd or not wr:
+        return None
+    return round(1.0 / (0.5 / rd["GBps"] + 0.5 / wr["GBps"]), 1)
+
+
+def attainable_for(ceil, kind, elem, nranks, staged=False):
     """The probe mix with a kernel's streams: two sources into one output for
     a reduce, into two for the fused reduce + forward, one into one for a copy,
-    every rank into every rank for a one-pass fold; otherwise (the INT8
-    kernels) the two-buffer mix whose read share is nearest the kernel's."""
+    every rank into every rank for a register one-pass fold, the read and the
+    split-write probes one after the other for an LDS-staged one (staged);
+    otherwise (the INT8 kernels) the two-buffer mix whose read share is
+    nearest the kernel's."""
     fam = kind & 0xF00
     fold = f"fold {nranks}:{nranks}"
+    if staged and staged_bound(ceil, nranks):
+        return f"read {nranks}:0 then write 0:{nranks} split", staged_bound(ceil, nranks)
     if fam == 0x100:
         name = "reduce 2:2" if kind & 8 else "reduce 2:1"
     elif fam == 0x200:
@@ -460,6 +474,7 @@ def main():
     lb = [launch_bytes(B, lplan, i, n, elem, count) for i in range(nl)]
     keys = [(kind, shapes[i]["cold"], shapes[i]["units"]) for i, (_, kind) in enumerate(lb)]
     labels = {k: kernel_label(k[0], shapes[i], n) for i, k in enumerate(keys)}
+    staged_keys = {k for i, k in enumerate(keys) if shapes[i].get("lds_bytes")}  # LDS-staged one-pass folds
     period = max(1, nl // 4)
 
     def timed_run(evict=None):
@@ -559,7 +574,7 @@ def main():
             row.update({"cold_ms": round(c["ms"] / c["launches"], 5), "cold_GBps": round(crate, 1),
                         "cold_frac_of_peak": round(crate / HBM_PEAK_GBPS, 4)})
         if ceil:
-            probe, att = attainable_for(ceil, k[0], elem, n)
+            probe, att = attainable_for(ceil, k[0], elem, n, staged=k in staged_keys)
             row.update({"attainable_probe": probe, "attainable_GBps": att,
                         "warm_frac_of_attainable": round(rate / att, 4)})
             if c:
@@ -643,13 +658,9 @@ def main():
             extra["onepass"]["frac_of_copy_ceiling"] = round(op_gbps / ceil["copy 1:1"]["GBps"], 4)
             if fold:
                 extra["onepass"]["frac_of_fold_probe"] = round(op_gbps / ceil[fold[0]]["GBps"], 4)
-            rd, wr = ceil.get(f"read {n}:0"), ceil.get(f"write 0:{n} split")
-            if rd and wr:
-                # the LDS-staged fold reads every rank and writes every rank, one
-                # buffer per wave: its two halves at their probe rates, one after
-                # the other
-                staged = 1.0 / (0.5 / rd["GBps"] + 0.5 / wr["GBps"])
-                extra["onepass"]["staged_phases_GBps"] = round(staged, 1)
+            staged = staged_bound(ceil, n)
+            if staged:  # the LDS-staged fold's two halves at their probe rates
+                extra["onepass"]["staged_phases_GBps"] = staged
                 extra["onepass"]["frac_of_staged_phases"] = round(op_gbps / staged, 4)
 
     # ---- the same exec mode replayed as one HIP graph per call
