@@ -66,6 +66,8 @@ def _block_elems(blocks, count):
     ("hierarchical", 4, 2, "bf16", "steps"),
     ("rabenseifner", 4, 1, "fp32", "steps"),
     ("double_tree", 2, 1, "bf16_each", "onepass"),
+    ("rabenseifner", 4, 1, "bf16", "onepass"),
+    ("hierarchical", 4, 2, "fp32", "onepass"),
 ])
 def test_beyond_2_32_elements(sched, n, g, dtype, mode):
     import torch
