@@ -258,7 +258,7 @@ def probe_ceilings(B, torch, dev, stream, rank_bufs=None, rank_bytes=0, restore=
     each mix the best of 1, 2 and 4 units per thread and of the three cache
     policies, each the median of `reps` event-timed launches after two
     untimed ones.  With rank_bufs, also the one-pass mix on the workload's
-    own buffers: every rank read and every rank written, in place (each
+    own buffers: every buffer read and every buffer written, in place (each
     launch on the inputs restored by `restore`, outside its events).
     matched: (name, sources, destinations, bytes per buffer) mixes measured
     on the first bytes of the same buffers: a step kernel's streams at its
@@ -303,22 +303,23 @@ def staged_bound(ceil, nranks):
     return round(1.0 / (0.5 / rd["GBps"] + 0.5 / wr["GBps"]), 1)
 
 
-def attainable_for(ceil, kind, elem, nranks, staged=False):
+def attainable_for(ceil, kind, elem, nbuf, staged=False):
     """The probe mix with a kernel's streams: two sources into one output for
     a reduce, into two for the fused reduce + forward, one into one for a copy,
-    every rank into every rank for a register one-pass fold, the read and the
-    split-write probes one after the other for an LDS-staged one (staged);
-    otherwise (the INT8 kernels) the two-buffer mix whose read share is
-    nearest the kernel's."""
+    every buffer into every buffer for a register one-pass fold (nbuf: the
+    rank buffers, and with error feedback the residual buffers too), the read
+    and the split-write probes one after the other for an LDS-staged one
+    (staged); otherwise (the INT8 step kernels) the two-buffer mix whose read
+    share is nearest the kernel's."""
     fam = kind & 0xF00
-    fold = f"fold {nranks}:{nranks}"
-    if staged and staged_bound(ceil, nranks):
-        return f"read {nranks}:0 then write 0:{nranks} split", staged_bound(ceil, nranks)
+    fold = f"fold {nbuf}:{nbuf}"
+    if staged and staged_bound(ceil, nbuf):
+        return f"read {nbuf}:0 then write 0:{nbuf} split", staged_bound(ceil, nbuf)
     if fam == 0x100:
         name = "reduce 2:2" if kind & 8 else "reduce 2:1"
     elif fam == 0x200:
         name = "copy 1:1"
-    elif fam in (0x300, 0x400, 0x500, 0x600) and kind & 3 != 3 and fold in ceil:
+    elif fam in (0x300, 0x400, 0x500, 0x600) and fold in ceil:
         name = fold
     else:
         share = read_share(kind, elem)
@@ -365,6 +366,7 @@ def main():
     torch.cuda.set_device(dev)
     quant = dtype == "int8_ef"
     elem = 4 if dtype in ("fp32", "int8_ef") else 2
+    nbuf = 2 * n if quant else n  # buffers a one-pass fold reads and writes in place
     view = np.float32 if elem == 4 else np.int16
     gen_dtype = "fp32" if elem == 4 else "bf16"
 
@@ -550,8 +552,11 @@ def main():
             if st_ and per_kind.get(k):
                 nb = per_call_bytes[k] // per_call_count[k] // sum(st_) // 16 * 16
                 matched.append((f"{labels[k]} size", st_[0], st_[1], nb))
-        ceil = probe_ceilings(B, torch, dev, stream, None if bucketed or quant else bufs, count_logical * elem,
-                              reset_inputs, matched)
+        # the one-pass mixes run on the workload's own buffers: the rank
+        # buffers, and with error feedback the residual buffers as well (the
+        # INT8 one-pass fold reads and writes both in place)
+        ceil = probe_ceilings(B, torch, dev, stream, None if bucketed else bufs + (errs if quant else []),
+                              count_logical * elem, reset_inputs, matched)
     per_kernel = []
 
     def share_of_call(k):
@@ -574,7 +579,7 @@ def main():
             row.update({"cold_ms": round(c["ms"] / c["launches"], 5), "cold_GBps": round(crate, 1),
                         "cold_frac_of_peak": round(crate / HBM_PEAK_GBPS, 4)})
         if ceil:
-            probe, att = attainable_for(ceil, k[0], elem, n, staged=k in staged_keys)
+            probe, att = attainable_for(ceil, k[0], elem, nbuf, staged=k in staged_keys)
             row.update({"attainable_probe": probe, "attainable_GBps": att,
                         "warm_frac_of_attainable": round(rate / att, 4)})
             if c:
@@ -654,11 +659,11 @@ def main():
                             "algbw_GBps": round(op_alg, 1), "hbm_model_GBps": round(op_gbps, 1),
                             "hbm_model_frac_of_peak": round(op_gbps / HBM_PEAK_GBPS, 4)}
         if ceil:
-            fold = [k for k in ceil if k == f"fold {n}:{n}"]
+            fold = [k for k in ceil if k == f"fold {nbuf}:{nbuf}"]
             extra["onepass"]["frac_of_copy_ceiling"] = round(op_gbps / ceil["copy 1:1"]["GBps"], 4)
             if fold:
                 extra["onepass"]["frac_of_fold_probe"] = round(op_gbps / ceil[fold[0]]["GBps"], 4)
-            staged = staged_bound(ceil, n)
+            staged = staged_bound(ceil, nbuf)
             if staged:  # the LDS-staged fold's two halves at their probe rates
                 extra["onepass"]["staged_phases_GBps"] = staged
                 extra["onepass"]["frac_of_staged_phases"] = round(op_gbps / staged, 4)
