@@ -110,6 +110,42 @@ def test_special_values_bf16(dtype):
                 assert same.all(), (sched, mode, r)
 
 
+SPECIAL_WIDE = [("ring", 16, 1), ("ring", 64, 1), ("hierarchical", 16, 8), ("hierarchical", 64, 8),
+                ("rabenseifner", 16, 1), ("rabenseifner", 64, 1), ("recursive_doubling", 4, 1),
+                ("recursive_doubling", 16, 1), ("tree", 5, 1), ("tree", 16, 1), ("tree", 40, 1),
+                ("double_tree", 4, 1), ("double_tree", 16, 1), ("double_tree", 64, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+@pytest.mark.parametrize("sched,n,g", SPECIAL_WIDE)
+def test_special_values_every_schedule(sched, n, g, dtype):
+    """The same special values through every schedule, at the rank counts
+    where the one-pass folds change shape: 16 ranks (one rank per wave), 64
+    (eight per wave, one unit per lane), and trees whose rank count is not a
+    power of two (missing leaves are -0, the identity of IEEE addition)."""
+    count = 4096 + 16
+    rng = np.random.default_rng(1000 + n)
+    if dtype == "fp32":
+        vals = np.array([1e-45, -1e-45, 1e-40, 0.0, -0.0, np.inf, -np.inf, 3e38, -3e38, 1.0, 2 ** -149], np.float32)
+        xs = [vals[rng.integers(0, len(vals), count)] for _ in range(n)]
+    else:
+        vals = np.array([1e-40, -1e-40, 0.0, -0.0, np.inf, -np.inf, 3.3e38, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8],
+                        np.float32)
+        xs = [workloads._to_bf16_bits(vals[rng.integers(0, len(vals), count)]) for _ in range(n)]
+    ref = oracle.run([x.copy() for x in xs], dtype, sched, group_size=g)
+    for mode in MODES:
+        _say(f"special {dtype} {sched} n={n} g={g} {mode}")
+        got = gpu_allreduce(xs, dtype, sched, g, mode)
+        for r in range(n):
+            if dtype == "fp32":
+                a, b = got[r].view(np.float32), ref[r]
+                same = (got[r] == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))
+            else:
+                a, b = widen(got[r]), widen(ref[r])
+                same = (got[r] == ref[r]) | (np.isnan(a) & np.isnan(b))
+            assert same.all(), (sched, n, mode, r, int(np.argmin(same)))
+
+
 def test_plan_reuse_streams_and_profiling():
     """One plan, several calls on different buffers and on a side stream; the
     profiling log reports one duration per launch per call."""
