@@ -64,6 +64,8 @@ def _bind(L):
     L.aro_run_int8ef.restype = i32
     L.aro_run.argtypes = [i32, i32, i64, i32, i32, P, i32]
     L.aro_run.restype = i32
+    L.aro_run_rounds.argtypes = [i32, i32, i64, i32, i32, P, i32, i32]
+    L.aro_run_rounds.restype = i32
     return L
 
 
@@ -144,6 +146,75 @@ def run(bufs, dtype, schedule, group_size=1, max_steps=-1, L=None):
     if rc != 0:
         raise OracleError(f"aro_run failed ({rc})")
     return bufs
+
+
+def run_rounds(bufs, dtype, schedule, group_size=1, first_step=0, end_step=-1, L=None):
+    """Runs rounds first_step .. end_step-1 in place (end_step < 0: to the
+    last round); the buffers stand for the state the earlier rounds left."""
+    L = L or lib()
+    want = np.float32 if dtype == "fp32" else np.uint16
+    n = len(bufs)
+    count = len(bufs[0]) if n else 0
+    for b in bufs:
+        if b.dtype != want or not b.flags.c_contiguous or len(b) != count:
+            raise OracleError("buffers must be contiguous, equal length, of the dtype's storage type")
+    arr = (ctypes.c_void_p * max(n, 1))(*[b.ctypes.data for b in bufs])
+    rc = L.aro_run_rounds(n, group_size, count, _DTYPE[dtype], _SCHED[schedule],
+                          ctypes.cast(arr, ctypes.c_void_p), first_step, end_step)
+    if rc != 0:
+        raise OracleError(f"aro_run_rounds failed ({rc})")
+    return bufs
+
+
+HALVES = ("ring", "hierarchical", "rabenseifner")
+
+
+def reduce_scatter_rounds(nranks, schedule, count=0, group_size=1, L=None):
+    """Number of leading rounds whose messages are reduces: the
+    reduce-scatter half ([PRIMER] 4.2; [SCALING] "Six basic primitives")."""
+    if schedule not in HALVES:
+        raise OracleError(f"{schedule} has no reduce-scatter half")
+    m = messages(nranks, count, schedule, group_size, L=L)
+    reduce_steps = sorted({int(s) for s, k in zip(m["step"], m["kind"]) if k == REDUCE})
+    if reduce_steps != list(range(len(reduce_steps))) or any(
+            k == REDUCE for s, k in zip(m["step"], m["kind"]) if s >= len(reduce_steps)):
+        raise OracleError("the reduce rounds are not a prefix of the schedule")
+    if any(k != REDUCE for s, k in zip(m["step"], m["kind"]) if s < len(reduce_steps)):
+        raise OracleError("a reduce round also copies")
+    return len(reduce_steps)
+
+
+def owned_ranges(nranks, count, schedule, group_size=1, L=None):
+    """[(lo, hi)] per rank: the range the receiver of each completing reduce
+    holds complete after the reduce-scatter half; everything for one rank."""
+    if schedule not in HALVES:
+        raise OracleError(f"{schedule} has no reduce-scatter half")
+    if nranks == 1:
+        return [(0, count)]
+    m = messages(nranks, count, schedule, group_size, L=L)
+    out = [None] * nranks
+    for dst, lo, hi, kind, done in zip(m["dst"], m["lo"], m["hi"], m["kind"], m["completes"]):
+        if kind == REDUCE and done:
+            if out[dst] is not None:
+                raise OracleError(f"rank {dst} completes two ranges")
+            out[dst] = (int(lo), int(hi))
+    if any(o is None for o in out):
+        raise OracleError("a rank completes no range")
+    return out
+
+
+def reduce_scatter(bufs, dtype, schedule, group_size=1, L=None):
+    """The reduce-scatter half in place; rank r's owned range then holds the
+    all-reduce's values."""
+    k = reduce_scatter_rounds(len(bufs), schedule, len(bufs[0]) if bufs else 0, group_size, L=L)
+    return run_rounds(bufs, dtype, schedule, group_size, 0, k, L=L)
+
+
+def allgather(bufs, dtype, schedule, group_size=1, L=None):
+    """The all-gather half in place: every rank's owned range goes to every
+    other rank."""
+    k = reduce_scatter_rounds(len(bufs), schedule, len(bufs[0]) if bufs else 0, group_size, L=L)
+    return run_rounds(bufs, dtype, schedule, group_size, k, -1, L=L)
 
 
 QBLOCK = 128

@@ -543,18 +543,24 @@ double aro_cost_ex(int nranks, int group_size, long long count, int elem_bytes, 
 }
 
 /*
- * Runs the schedule in place on host buffers bufs[0..nranks-1] (float* for
- * fp32, uint16_t* holding bf16 bits for bf16).  Only the first max_steps
- * rounds are simulated when max_steps >= 0 (used to inspect intermediate
- * states); max_steps < 0 runs all of them.  Returns 0, or a negative code.
+ * Runs rounds first_step .. end_step-1 of the schedule in place on host
+ * buffers bufs[0..nranks-1] (float* for fp32, uint16_t* holding bf16 bits
+ * for bf16); end_step < 0 runs to the last round.  The rounds before
+ * first_step are not simulated: the buffers stand for the state they left.
+ * [PRIMER] 4.2 and [SCALING] "Six basic primitives": the reduce rounds of
+ * the ring, hierarchical and Rabenseifner schedules are a reduce-scatter
+ * and the copy rounds after them an all-gather, so the two halves run as
+ * (0, k) and (k, -1) with k the number of reduce rounds.  Returns 0, or a
+ * negative code.
  */
-int aro_run(int nranks, int group_size, long long count, int dtype, int schedule,
-            void **bufs, int max_steps) {
+int aro_run_rounds(int nranks, int group_size, long long count, int dtype, int schedule,
+                   void **bufs, int first_step, int end_step) {
   if (dtype != ARO_FP32 && dtype != ARO_BF16 && dtype != ARO_BF16_EACH) return -1;
+  if (first_step < 0) return -1;
   aro_list L;
   int rc = build(&L, nranks, group_size, count, schedule);
   if (rc) return rc;
-  int nsteps = (max_steps >= 0 && max_steps < L.nsteps) ? max_steps : L.nsteps;
+  int nsteps = (end_step >= 0 && end_step < L.nsteps) ? end_step : L.nsteps;
 
   /* Working fp32 state of every rank: the buffers themselves for fp32, a
      widened copy for bf16. */
@@ -588,6 +594,7 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
     if (!pay || !pay16) err = 1;
   }
   int64_t j0 = 0;
+  while (j0 < L.n && L.m[j0].step < first_step) ++j0;
   while (!err && j0 < L.n && L.m[j0].step < nsteps) {
     int64_t j1 = j0;
     while (j1 < L.n && L.m[j1].step == L.m[j0].step) ++j1;
@@ -635,6 +642,13 @@ int aro_run(int nranks, int group_size, long long count, int dtype, int schedule
   free(w);
   free(L.m);
   return err ? -3 : 0;
+}
+
+/* The whole schedule, or its first max_steps rounds when max_steps >= 0
+   (used to inspect intermediate states). */
+int aro_run(int nranks, int group_size, long long count, int dtype, int schedule,
+            void **bufs, int max_steps) {
+  return aro_run_rounds(nranks, group_size, count, dtype, schedule, bufs, 0, max_steps);
 }
 
 

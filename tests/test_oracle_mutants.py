@@ -56,6 +56,10 @@ MUTANTS = {
                         "if ((i & ((2 << k) - 1)) == 0 && i + (1 << k) < N - 1)"),
     "dtree_mirror_dst": ("int dst = t == 0 ? par : N - 1 - par;", "int dst = t == 0 ? par : par;"),
     "dtree_half": ("int64_t half = part_lo(count, 2, 1);", "int64_t half = part_lo(count, 4, 1);"),
+    "rounds_start_late": ("while (j0 < L.n && L.m[j0].step < first_step) ++j0;",
+                          "while (j0 < L.n && L.m[j0].step <= first_step) ++j0;"),
+    "rounds_end_early": ("int nsteps = (end_step >= 0 && end_step < L.nsteps) ? end_step : L.nsteps;",
+                         "int nsteps = (end_step > 0 && end_step <= L.nsteps) ? end_step - 1 : L.nsteps;"),
     "dtree_child_order": ("for (int round = 0; round < lg; ++round)\n    for (int s = 0; s < N; ++s)\n"
                           "      for (int t = 0; t < 2; ++t) {\n        /* in tree 2",
                           "for (int round = 0; round < lg; ++round)\n    for (int s = N - 1; s >= 0; --s)\n"
@@ -76,6 +80,6 @@ def test_mutant_is_caught(name, tmp_path):
     env = dict(os.environ, ARO_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pages.py", "tests/test_oracle_bruteforce.py",
-                        "tests/test_oracle_int8ef.py"],
+                        "tests/test_oracle_int8ef.py", "tests/test_oracle_halves.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
