@@ -28,6 +28,8 @@ DTYPES = {"fp32": AR_FLOAT32, "bf16": AR_BFLOAT16, "bf16_each": AR_BFLOAT16_EACH
 SCHEDULES = {"ring": AR_RING, "hierarchical": AR_HIERARCHICAL, "rabenseifner": AR_RABENSEIFNER,
              "recursive_doubling": AR_RECURSIVE_DOUBLING, "tree": AR_TREE, "double_tree": AR_DOUBLE_TREE}
 EXECS = {"steps": AR_EXEC_STEPS, "steps_unfused": AR_EXEC_STEPS_UNFUSED, "onepass": AR_EXEC_ONEPASS}
+AR_ALLREDUCE, AR_REDUCE_SCATTER, AR_ALLGATHER = range(3)
+COLLECTIVES = {"allreduce": AR_ALLREDUCE, "reduce_scatter": AR_REDUCE_SCATTER, "allgather": AR_ALLGATHER}
 
 # kernel kind codes reported by ar_plan_launch_info
 KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE, KIND_DTREE = 0x100, 0x200, 0x300, 0x400, 0x500, 0x600
@@ -86,6 +88,10 @@ def _declare(L):
                            ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_size_t))
     sig = {
         "ar_plan_create": ([ctypes.c_int, ctypes.c_int, sz, ctypes.c_int, ctypes.c_int], P),
+        "ar_plan_create_collective": ([ctypes.c_int, ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_int], P),
+        "ar_plan_owned_range": ([P, ctypes.c_int, psz, psz], ctypes.c_int),
+        "ar_reduce_scatter": ([P, P, P], ctypes.c_int),
+        "ar_allgather": ([P, P, P], ctypes.c_int),
         "ar_plan_set_exec": ([P, ctypes.c_int], ctypes.c_int),
         "ar_plan_prepare": ([P], ctypes.c_int),
         "ar_allreduce": ([P, P, P], ctypes.c_int),
@@ -223,6 +229,22 @@ def ar_plan_create(nranks, group_size, count, dtype, schedule):
     return p
 
 
+def ar_plan_create_collective(nranks, group_size, count, dtype, schedule, collective):
+    """collective: "allreduce", "reduce_scatter" or "allgather"."""
+    p = lib().ar_plan_create_collective(nranks, group_size, count, _code(DTYPES, dtype), _code(SCHEDULES, schedule),
+                                        _code(COLLECTIVES, collective))
+    if not p:
+        _raise()
+    return p
+
+
+def ar_plan_owned_range(plan, rank):
+    """(lo, hi): the elements `rank` holds complete after the reduce-scatter."""
+    lo, hi = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().ar_plan_owned_range(plan, rank, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
 def ar_plan_set_exec(plan, exec_mode):
     _check(lib().ar_plan_set_exec(plan, _code(EXECS, exec_mode)))
 
@@ -245,6 +267,22 @@ def ar_allreduce(plan, rank_bufs, stream=None):
         _check_bufs(rank_bufs, n, nbytes, "rank buffer")
     arr = _ptr_array(rank_bufs)
     _check(lib().ar_allreduce(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def ar_reduce_scatter(plan, rank_bufs, stream=None):
+    if plan:
+        n, nbytes, _ = _plan_extent(plan)
+        _check_bufs(rank_bufs, n, nbytes, "rank buffer")
+    arr = _ptr_array(rank_bufs)
+    _check(lib().ar_reduce_scatter(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+def ar_allgather(plan, rank_bufs, stream=None):
+    if plan:
+        n, nbytes, _ = _plan_extent(plan)
+        _check_bufs(rank_bufs, n, nbytes, "rank buffer")
+    arr = _ptr_array(rank_bufs)
+    _check(lib().ar_allgather(plan, ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
 
 
 def ar_allreduce_ef(plan, rank_bufs, error_bufs, stream=None):

@@ -650,6 +650,7 @@ const char *const kDtypeNames[] = {"fp32", "bf16", "bf16_each", "int8_ef"};
 const char *const kSchedNames[] = {"ring", "hierarchical", "rabenseifner", "recursive_doubling", "tree",
                                    "double_tree"};
 const char *const kExecNames[] = {"steps", "steps_unfused", "onepass"};
+const char *const kCollNames[] = {"allreduce", "reduce_scatter", "allgather"};
 
 // The plan as JSON: its configuration, its schedule step by step (every
 // transfer: sender, receiver, range, 0 reduce / 1 copy) and its launches
@@ -669,6 +670,7 @@ std::string describe(const ar_plan_t *pl) {
   kv("dtype", q(kDtypeNames[p.dtype]));
   kv("schedule", q(kSchedNames[p.sched]));
   kv("exec", q(kExecNames[p.exec]));
+  kv("collective", q(kCollNames[p.coll]));
   kv("steps", std::to_string(p.nsteps));
   kv("hbm_bytes_model", std::to_string(p.hbm_bytes));
   j += "\"step_list\": [";
@@ -740,6 +742,8 @@ ar_status_t set_exec(ar_plan_t *plan, int32_t exec) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
   const ar::Exec mode = static_cast<ar::Exec>(exec);
   if (mode == plan->p.exec && plan->prepared) return AR_OK;
+  if (mode == ar::kOnePass && plan->p.coll != ar::kAllReduce)
+    return fail(AR_ERR_UNSUPPORTED, "reduce-scatter and all-gather plans run in the step modes");
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, mode);
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
@@ -749,8 +753,9 @@ ar_status_t set_exec(ar_plan_t *plan, int32_t exec) {
   return AR_OK;
 }
 
-// ar_plan_create with the enum arguments as integers.
-ar_plan_t *create_plan(int nranks, int group_size, size_t count, int32_t dtype, int32_t schedule) {
+// ar_plan_create_collective with the enum arguments as integers.
+ar_plan_t *create_plan(int nranks, int group_size, size_t count, int32_t dtype, int32_t schedule,
+                       int32_t coll = ar::kAllReduce) {
   if (count > static_cast<size_t>(INT64_MAX / 8)) {
     fail(AR_ERR_INVALID_ARG, "count too large");
     return nullptr;
@@ -763,7 +768,7 @@ ar_plan_t *create_plan(int nranks, int group_size, size_t count, int32_t dtype, 
   bool unsupported = false;
   const std::string err = ar::build_plan(pl->p, nranks, group_size, static_cast<int64_t>(count),
                                          static_cast<ar::Dtype>(dtype), static_cast<ar::Sched>(schedule),
-                                         ar::kSteps, &unsupported);
+                                         ar::kSteps, &unsupported, static_cast<ar::Coll>(coll));
   if (!err.empty()) {
     delete pl;
     fail(unsupported ? AR_ERR_UNSUPPORTED : AR_ERR_INVALID_ARG, err);
@@ -778,40 +783,8 @@ ar_plan_t *create_plan(int nranks, int group_size, size_t count, int32_t dtype, 
   return pl;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *ar_last_error(void) { return g_err.c_str(); }
-ar_status_t ar_last_status(void) { return g_status; }
-
-ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype, ar_schedule_t schedule) {
-  return create_plan(nranks, group_size, count, raw_enum(dtype), raw_enum(schedule));
-}
-
-ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) { return set_exec(plan, raw_enum(exec)); }
-
-ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes) {
-  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
-  if (bytes > static_cast<size_t>(INT64_MAX)) return fail(AR_ERR_INVALID_ARG, "cache size too large");
-  ar::Plan trial = plan->p;
-  trial.cache_bytes = static_cast<int64_t>(bytes);
-  const std::string err = ar::relower(trial, trial.exec);
-  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
-  plan->release_device();  // waits for the plan's calls in flight
-  plan->p = std::move(trial);
-  lower_launches(plan);
-  return AR_OK;
-}
-
-ar_status_t ar_plan_prepare(ar_plan_t *plan) {
-  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->p.nranks > ar::kMaxExecRanks)
-    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
-  return prepare(plan);
-}
-
-ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
+// One call of a plan on these buffers (its collective already checked).
+ar_status_t run_call(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
   ar_status_t st = check_call(plan, rank_bufs, error_bufs);
   if (st != AR_OK) return st;
   st = prepare(plan);
@@ -837,7 +810,81 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
   return st;
 }
 
+}  // namespace
+
+extern "C" {
+
+const char *ar_last_error(void) { return g_err.c_str(); }
+ar_status_t ar_last_status(void) { return g_status; }
+
+ar_plan_t *ar_plan_create(int nranks, int group_size, size_t count, ar_dtype_t dtype, ar_schedule_t schedule) {
+  return create_plan(nranks, group_size, count, raw_enum(dtype), raw_enum(schedule));
+}
+
+ar_plan_t *ar_plan_create_collective(int nranks, int group_size, size_t count, ar_dtype_t dtype,
+                                     ar_schedule_t schedule, ar_collective_t collective) {
+  return create_plan(nranks, group_size, count, raw_enum(dtype), raw_enum(schedule), raw_enum(collective));
+}
+
+ar_status_t ar_plan_set_exec(ar_plan_t *plan, ar_exec_t exec) { return set_exec(plan, raw_enum(exec)); }
+
+ar_status_t ar_plan_set_cache_bytes(ar_plan_t *plan, size_t bytes) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (bytes > static_cast<size_t>(INT64_MAX)) return fail(AR_ERR_INVALID_ARG, "cache size too large");
+  ar::Plan trial = plan->p;
+  trial.cache_bytes = static_cast<int64_t>(bytes);
+  const std::string err = ar::relower(trial, trial.exec);
+  if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);
+  plan->release_device();  // waits for the plan's calls in flight
+  plan->p = std::move(trial);
+  lower_launches(plan);
+  return AR_OK;
+}
+
+ar_status_t ar_plan_prepare(ar_plan_t *plan) {
+  if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->p.nranks > ar::kMaxExecRanks)
+    return fail(AR_ERR_UNSUPPORTED, "plans of more than 64 ranks describe a schedule but cannot run");
+  return prepare(plan);
+}
+
+ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
+  if (plan && plan->p.coll != ar::kAllReduce)
+    return fail(AR_ERR_INVALID_ARG, "this plan runs a reduce-scatter or an all-gather: call ar_reduce_scatter or "
+                                    "ar_allgather");
+  return run_call(plan, rank_bufs, error_bufs, stream);
+}
+
+ar_status_t ar_reduce_scatter(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
+  if (plan && plan->p.coll != ar::kReduceScatter)
+    return fail(AR_ERR_INVALID_ARG, "this plan does not run a reduce-scatter (ar_plan_create_collective)");
+  return run_call(plan, rank_bufs, nullptr, stream);
+}
+
+ar_status_t ar_allgather(ar_plan_t *plan, void *const *rank_bufs, void *stream) {
+  if (plan && plan->p.coll != ar::kAllGather)
+    return fail(AR_ERR_INVALID_ARG, "this plan does not run an all-gather (ar_plan_create_collective)");
+  return run_call(plan, rank_bufs, nullptr, stream);
+}
+
+ar_status_t ar_plan_owned_range(const ar_plan_t *plan, int rank, size_t *lo, size_t *hi) {
+  if (!plan || !lo || !hi) return fail(AR_ERR_INVALID_ARG, "NULL argument");
+  int64_t a = 0, b = 0;
+  if (!ar::owned_range(plan->p, rank, &a, &b))
+    return fail(plan->p.sched == ar::kRing || plan->p.sched == ar::kHier || plan->p.sched == ar::kRaben
+                    ? AR_ERR_INVALID_ARG
+                    : AR_ERR_UNSUPPORTED,
+                "rank out of range, or a schedule without a reduce-scatter half");
+  // INT8 plans count blocks of kQBlock elements
+  const int64_t scale = plan->p.dtype == ar::kI8EF ? ar::kQBlock : 1;
+  *lo = static_cast<size_t>(std::min(a * scale, plan->p.count));
+  *hi = static_cast<size_t>(std::min(b * scale, plan->p.count));
+  return AR_OK;
+}
+
 ar_status_t ar_allreduce_noalloc(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream) {
+  if (plan && plan->p.coll != ar::kAllReduce)
+    return fail(AR_ERR_INVALID_ARG, "the allocation-free call runs all-reduce plans");
   ar_status_t st = check_call(plan, rank_bufs, error_bufs);
   if (st != AR_OK) return st;
   if (!plan->launch_err.empty()) return fail(AR_ERR_UNSUPPORTED, plan->launch_err);

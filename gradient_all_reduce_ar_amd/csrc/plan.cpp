@@ -833,7 +833,7 @@ std::string lower(Plan &p, Exec exec) {
 }  // namespace
 
 std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype, Sched sched,
-                       Exec exec, bool *unsupported) {
+                       Exec exec, bool *unsupported, Coll coll) {
   *unsupported = false;
   if (nranks < 1 || nranks > kMaxPlanRanks) return "nranks must be in [1, 1024]";
   if (group_size < 1 || nranks % group_size) return "group_size must be >= 1 and divide nranks";
@@ -841,9 +841,18 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   if (dtype != kF32 && dtype != kBF16 && dtype != kBF16Each && dtype != kI8EF) return "unknown dtype";
   if (sched < kRing || sched > kDTree) return "unknown schedule";
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
+  if (coll != kAllReduce && coll != kReduceScatter && coll != kAllGather) return "unknown collective";
   if ((sched == kRaben || sched == kRDouble || sched == kDTree) && (nranks & (nranks - 1))) {
     *unsupported = true;
     return "this schedule needs a power-of-two number of ranks";
+  }
+  if (coll != kAllReduce) {
+    *unsupported = true;
+    if (sched != kRing && sched != kHier && sched != kRaben)
+      return "reduce-scatter and all-gather plans need the ring, hierarchical or Rabenseifner schedule";
+    if (dtype == kI8EF) return "reduce-scatter and all-gather plans are fp32 or bf16";
+    if (exec == kOnePass) return "reduce-scatter and all-gather plans run in the step modes";
+    *unsupported = false;
   }
   p = Plan{};
   p.nranks = nranks;
@@ -867,11 +876,40 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
   else p.nsteps = build_dtree(p.xfers, nranks, units);
   std::stable_sort(p.xfers.begin(), p.xfers.end(),
                    [](const Transfer &a, const Transfer &b) { return a.step < b.step; });
+  if (sched == kRing || sched == kHier || sched == kRaben) {
+    // the receiver of the reduce that completes a range owns it; one rank
+    // holds everything when there is no transfer
+    p.owned.assign(nranks, {0, nranks == 1 ? units : 0});
+    for (const Transfer &x : p.xfers)
+      if (x.kind == kReduce && x.final_sum) p.owned[x.dst] = {x.lo, x.hi};
+  }
+  p.coll = coll;
+  if (coll != kAllReduce) {
+    // one half of the schedule: its reduce rounds (the reduce-scatter) or its
+    // copy rounds (the all-gather), which are consecutive; the transfers keep
+    // the schedule's round numbers, so the launch order treats every round
+    // as it does in the whole all-reduce
+    const int32_t keep = coll == kReduceScatter ? kReduce : kCopy;
+    std::vector<Transfer> half;
+    for (const Transfer &x : p.xfers)
+      if (x.kind == keep) half.push_back(x);
+    p.xfers = std::move(half);
+    p.step0 = p.xfers.empty() ? 0 : p.xfers.front().step;
+    p.nsteps = p.xfers.empty() ? 0 : p.xfers.back().step - p.step0 + 1;
+  }
   return lower(p, exec);
+}
+
+bool owned_range(const Plan &p, int rank, int64_t *lo, int64_t *hi) {
+  if (rank < 0 || rank >= p.nranks || static_cast<int>(p.owned.size()) != p.nranks) return false;
+  *lo = p.owned[rank].first;
+  *hi = p.owned[rank].second;
+  return true;
 }
 
 std::string relower(Plan &p, Exec exec) {
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
+  if (exec == kOnePass && p.coll != kAllReduce) return "reduce-scatter and all-gather plans run in the step modes";
   return lower(p, exec);
 }
 
@@ -882,7 +920,7 @@ double cost_alpha_beta(const Plan &p, double alpha_s, double bw_intra, double bw
   for (const Transfer &x : p.xfers) {
     const bool cross = x.src / p.group_size != x.dst / p.group_size;
     const double t = static_cast<double>(xfer_bytes(p, x)) / (cross ? bw_cross : bw_intra);
-    slowest[x.step] = std::max(slowest[x.step], t);
+    slowest[x.step - p.step0] = std::max(slowest[x.step - p.step0], t);
   }
   double total = 0;
   for (double t : slowest) total += alpha_s + t;
@@ -901,10 +939,11 @@ double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross,
   for (const Transfer &x : p.xfers) {
     const double bytes = static_cast<double>(xfer_bytes(p, x));
     const bool cross = x.src / p.group_size != x.dst / p.group_size;
-    link[x.step] = std::max(link[x.step], bytes / (cross ? bw_cross : bw_intra));
+    const int r = x.step - p.step0;
+    link[r] = std::max(link[r], bytes / (cross ? bw_cross : bw_intra));
     if (cross) {
-      crosses[x.step] = true;
-      egress[x.step][x.src / p.group_size] += bytes * egress_share;
+      crosses[r] = true;
+      egress[r][x.src / p.group_size] += bytes * egress_share;
     }
   }
   double total = 0;

@@ -9,6 +9,7 @@
 
 #include <cstdint>
 #include <string>
+#include <utility>
 #include <vector>
 
 namespace ar {
@@ -21,6 +22,12 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kBF16Each = 2, kI8EF = 3 };
 constexpr int64_t kQBlock = 128;
 enum Sched : int32_t { kRing = 0, kHier = 1, kRaben = 2, kRDouble = 3, kTree = 4, kDTree = 5 };
 enum Exec : int32_t { kSteps = 0, kStepsUnfused = 1, kOnePass = 2 };
+// The collective a plan runs: the whole all-reduce, or one of its halves.
+// A reduce-scatter plan holds the schedule's reduce rounds only (after them
+// every rank holds one range of the buffer fully reduced), an all-gather
+// plan its copy rounds only (they spread each rank's range to every rank).
+// Ring, hierarchical and Rabenseifner schedules have both halves.
+enum Coll : int32_t { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 enum XferKind : int32_t { kReduce = 0, kCopy = 1 };
 
 // One message of the schedule: in round `step`, rank `src` sends elements
@@ -95,7 +102,9 @@ struct Plan {
   Dtype dtype = kF32;
   Sched sched = kRing;
   Exec exec = kSteps;
-  int32_t nsteps = 0;
+  Coll coll = kAllReduce;
+  int32_t nsteps = 0;            // rounds of the plan's collective
+  int32_t step0 = 0;             // schedule round of its first round (its transfers keep the schedule's numbering)
   std::vector<Transfer> xfers;   // ordered by step
   std::vector<Launch> launches;  // for `exec`
   int32_t nslots = 0;            // fp32 scratch slots used by `launches`
@@ -104,6 +113,7 @@ struct Plan {
   int64_t cache_bytes = kDefaultCacheBytes;  // device cache the launch order and shapes assume
   int64_t code_stride = 0;       // kI8EF: bytes of codes per rank slot (multiple of 256)
   int64_t scale_stride = 0;      // kI8EF: fp32 scales per rank slot (multiple of 64)
+  std::vector<std::pair<int64_t, int64_t>> owned;  // per rank: owned_range (ring, hierarchical, Rabenseifner)
   std::vector<uint64_t> bytes_sent;
   uint64_t cross_group_bytes = 0;
   uint64_t hbm_bytes = 0;        // algorithmic device bytes of `launches`
@@ -122,9 +132,17 @@ uint64_t workspace_bytes(const Plan &p);
 
 // Builds the transfers and the launches for `exec`.  Returns an empty string
 // on success, else the reason for failure; *unsupported is set when the
-// request is valid but not supported (Rabenseifner with N not 2^k).
+// request is valid but not supported (Rabenseifner with N not 2^k; a
+// reduce-scatter or all-gather of a schedule without those halves, of INT8,
+// or in the one-pass mode).
 std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype dtype,
-                       Sched sched, Exec exec, bool *unsupported);
+                       Sched sched, Exec exec, bool *unsupported, Coll coll = kAllReduce);
+
+// The unit range [*lo, *hi) that `rank` holds complete after the
+// reduce-scatter half of the plan's schedule (the receiver of the reduces
+// that complete a range), which is also what the all-gather half spreads
+// from it.  Ring, hierarchical and Rabenseifner plans; false otherwise.
+bool owned_range(const Plan &p, int rank, int64_t *lo, int64_t *hi);
 
 // Re-lowers an existing plan for another exec mode (its cache_bytes kept).
 std::string relower(Plan &p, Exec exec);

@@ -136,7 +136,7 @@ typedef struct ar_plan ar_plan_t;
 
 typedef struct {
   int32_t nranks, group_size;
-  uint32_t steps;                   /* sequential rounds of the schedule            */
+  uint32_t steps;                   /* sequential rounds of the plan's collective   */
   uint32_t launches;                /* kernel launches per call in the exec mode    */
   uint64_t count, elem_bytes;       /* elem_bytes: of the rank buffers               */
   const uint64_t *bytes_sent;       /* [nranks], plan-owned: logical bytes each rank
@@ -231,6 +231,73 @@ ar_status_t ar_allreduce(ar_plan_t *plan, void *const *rank_bufs, void *stream);
  * another dtype with error_bufs != NULL, and for bad pointers.
  */
 ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const *error_bufs, void *stream);
+
+/*
+ * The two halves of an all-reduce as collectives of their own.  Scaling ML
+ * systems ch. 06, "Six basic primitives": an all-reduce is a reduce-scatter
+ * followed by an all-gather, which is how the ring runs; FSDP calls the two
+ * halves separately (all-gather of parameter shards before a layer runs,
+ * reduce-scatter of gradients after the backward pass, each rank keeping its
+ * shard).  Primer ch. 4 section 4.2: after the N-1 reduce-scatter steps rank
+ * i holds chunk (i+1) mod N complete; each half sends (N-1)/N * S per rank.
+ *
+ *   AR_ALLREDUCE       the whole schedule (ar_plan_create).
+ *   AR_REDUCE_SCATTER  the schedule's reduce rounds only: ring steps
+ *                      0..N-2; hierarchical phase 1 and the reduce half of
+ *                      the cross-group ring (Primer 4.4); Rabenseifner's
+ *                      recursive halving (Primer 4.3).  Afterwards rank r's
+ *                      owned range (ar_plan_owned_range) holds the reduced
+ *                      values, with the same bits as the all-reduce gives
+ *                      there.  Its other elements hold what the schedule left
+ *                      in them: fp32 and AR_BFLOAT16_EACH_STEP partial sums,
+ *                      while AR_BFLOAT16 keeps its fp32 partials in the plan's
+ *                      scratch and leaves those elements unchanged.
+ *   AR_ALLGATHER       the schedule's copy rounds only: the cross-group
+ *                      ring's copy half and phase 3 for the hierarchical
+ *                      schedule, recursive doubling for Rabenseifner.  Each
+ *                      rank's owned range is read from that rank and written
+ *                      to every other rank; nothing else is read.
+ */
+typedef enum { AR_ALLREDUCE = 0, AR_REDUCE_SCATTER = 1, AR_ALLGATHER = 2 } ar_collective_t;
+
+/*
+ * ar_plan_create for one collective.  AR_REDUCE_SCATTER and AR_ALLGATHER
+ * plans take the ring, hierarchical or Rabenseifner schedule and fp32 or
+ * bf16 (either mode), and run in the step modes (the two are the same here:
+ * no reduce is followed by a copy); other schedules, AR_INT8_EF, and
+ * ar_plan_set_exec(AR_EXEC_ONEPASS) give AR_ERR_UNSUPPORTED.  Statistics,
+ * the cost models, graphs, profiling and guard zones cover the plan's own
+ * rounds.  The plan runs with ar_reduce_scatter or ar_allgather only
+ * (ar_allreduce, ar_allreduce_ef and ar_allreduce_noalloc refuse it with
+ * AR_ERR_INVALID_ARG); other errors as for ar_plan_create.
+ */
+ar_plan_t *ar_plan_create_collective(int nranks, int group_size, size_t count, ar_dtype_t dtype,
+                                     ar_schedule_t schedule, ar_collective_t collective);
+
+/*
+ * The element range [*lo, *hi) that `rank` holds complete after the
+ * reduce-scatter half of the plan's schedule: the range the receiver of each
+ * completing reduce owns, which the all-gather half spreads from it.  Ring:
+ * chunk (rank+1) mod N; Rabenseifner: the chunk whose index is `rank` with
+ * its log2 N bits reversed (Primer 4.3, Animation 4.2); hierarchical: within
+ * slice l = rank mod G, sub-chunk (g+1) mod M of the cross-group ring of
+ * group g = rank / G.  Chunks are part(count, K, c) =
+ * [floor(c*count/K), floor((c+1)*count/K)), so a range can be empty.  Any
+ * collective of these schedules; host only.  AR_ERR_INVALID_ARG for a rank
+ * outside [0, nranks) or NULL pointers, AR_ERR_UNSUPPORTED for other
+ * schedules.
+ */
+ar_status_t ar_plan_owned_range(const ar_plan_t *plan, int rank, size_t *lo, size_t *hi);
+
+/*
+ * Reduce-scatter and all-gather, in place, for plans of those collectives.
+ * Buffers, stream, errors and completion as for ar_allreduce.  Before
+ * ar_allgather each rank's owned range must hold its values; ar_reduce_scatter
+ * then ar_allgather on the same buffers give the all-reduce's bits in every
+ * element.
+ */
+ar_status_t ar_reduce_scatter(ar_plan_t *plan, void *const *rank_bufs, void *stream);
+ar_status_t ar_allgather(ar_plan_t *plan, void *const *rank_bufs, void *stream);
 
 /* Statistics of the plan (valid until the plan is destroyed or re-moded). */
 ar_stats_t ar_plan_stats(const ar_plan_t *plan);

@@ -1,0 +1,140 @@
+"""The library's reduce-scatter and all-gather plans against the oracle (no GPU).
+
+Owned ranges, transfers, statistics, and the launch lists run by the numpy
+interpreter (every element, bit for bit), plus the calls' refusals.  The
+oracle's halves themselves are pinned in test_oracle_halves.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_ar_amd import _binding as B
+from tests import plan_interp
+from tests.test_oracle_halves import CASES, _bits, _half_messages, _inputs, part
+
+
+def _coll_plan(n, g, count, dtype, sched, coll):
+    return B.ar_plan_create_collective(n, g, count, dtype, sched, coll)
+
+
+@pytest.mark.parametrize("sched,n,g", CASES)
+def test_plan_owned_ranges_equal_oracle(sched, n, g):
+    for count in (0, 1, n + 1, 1031):
+        want = oracle.owned_ranges(n, count, sched, group_size=g)
+        for coll in ("allreduce", "reduce_scatter", "allgather"):
+            p = _coll_plan(n, g, count, "fp32", sched, coll)
+            try:
+                assert [B.ar_plan_owned_range(p, r) for r in range(n)] == want
+            finally:
+                B.ar_plan_destroy(p)
+
+
+def _sorted(d):
+    order = np.lexsort((d["src"], d["step"]))
+    return {k: v[order] for k, v in d.items()}
+
+
+@pytest.mark.parametrize("sched,n,g", CASES)
+def test_plan_halves_transfers_and_stats_equal_oracle(sched, n, g):
+    for count in (0, 1, 97, 4096):
+        k, rs, ag = _half_messages(n, count, sched, g)
+        total = oracle.steps(n, sched, count, group_size=g)
+        whole = _coll_plan(n, g, count, "fp32", sched, "allreduce")
+        try:
+            cost_whole = B.ar_plan_cost_alpha_beta(whole, 1e-6, 400e9, 50e9)
+        finally:
+            B.ar_plan_destroy(whole)
+        cost = 0.0
+        for coll, ref, rounds in (("reduce_scatter", rs, k), ("allgather", ag, total - k)):
+            p = _coll_plan(n, g, count, "fp32", sched, coll)
+            try:
+                mine = _sorted(B.ar_plan_transfers(p))
+                ref = _sorted(ref)
+                for key in ("step", "src", "dst", "lo", "hi", "kind"):
+                    np.testing.assert_array_equal(mine[key], ref[key], err_msg=f"{sched} n={n} {coll} {key}")
+                st = B.ar_plan_stats(p)
+                assert st["steps"] == rounds
+                sent = np.bincount(ref["src"], weights=(ref["hi"] - ref["lo"]) * 4, minlength=n).astype(np.int64)
+                assert st["bytes_sent"] == sent.tolist()
+                cost += B.ar_plan_cost_alpha_beta(p, 1e-6, 400e9, 50e9)
+            finally:
+                B.ar_plan_destroy(p)
+        assert cost == pytest.approx(cost_whole, rel=1e-12)  # the rounds split between the halves
+
+
+@pytest.mark.parametrize("sched,n,g", CASES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused"])
+def test_plan_halves_launch_lists_equal_oracle(sched, n, g, dtype, mode):
+    """Reduce-scatter and all-gather launch lists, run by the interpreter,
+    give the oracle's halves bit for bit in every element, with a cache that
+    splits every round into pieces and with one that splits none."""
+    for count in (0, 37, 1031):
+        xs = _inputs(n, count, dtype, seed=count + 11 * n)
+        want_rs = oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g)
+        want_ag = oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)
+        for cache in (64, 1 << 30):
+            for coll, want in (("reduce_scatter", want_rs), ("allgather", want_ag)):
+                p = _coll_plan(n, g, count, dtype, sched, coll)
+                try:
+                    B.ar_plan_set_exec(p, mode)
+                    B.ar_plan_set_cache_bytes(p, cache)
+                    got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+                finally:
+                    B.ar_plan_destroy(p)
+                for r in range(n):
+                    np.testing.assert_array_equal(_bits(got[r], dtype), _bits(want[r], dtype),
+                                                  err_msg=f"{sched} n={n} {dtype} {mode} {coll} cache={cache} r={r}")
+
+
+def test_collective_plan_errors():
+    for sched in ("recursive_doubling", "tree", "double_tree"):
+        with pytest.raises(B.ArError) as e:
+            _coll_plan(4, 1, 100, "fp32", sched, "reduce_scatter")
+        assert e.value.status == B.AR_ERR_UNSUPPORTED
+    with pytest.raises(B.ArError) as e:
+        _coll_plan(4, 1, 1024, "int8_ef", "ring", "allgather")
+    assert e.value.status == B.AR_ERR_UNSUPPORTED
+    with pytest.raises(B.ArError) as e:
+        _coll_plan(4, 1, 100, "fp32", "ring", 7)
+    assert e.value.status == B.AR_ERR_INVALID_ARG
+    rs = _coll_plan(4, 1, 100, "fp32", "ring", "reduce_scatter")
+    ar = B.ar_plan_create(4, 1, 100, "fp32", "ring")
+    tree = B.ar_plan_create(4, 1, 100, "fp32", "tree")
+    try:
+        with pytest.raises(B.ArError) as e:
+            B.ar_plan_set_exec(rs, "onepass")
+        assert e.value.status == B.AR_ERR_UNSUPPORTED
+        assert B.ar_plan_stats(rs)["exec"] == B.AR_EXEC_STEPS  # the plan is unchanged
+        # a plan runs only through the call of its own collective; these
+        # refusals happen before any pointer is read or device call made
+        lib = B.lib()
+        assert lib.ar_allreduce(rs, None, None) == B.AR_ERR_INVALID_ARG
+        assert lib.ar_allreduce_ef(rs, None, None, None) == B.AR_ERR_INVALID_ARG
+        assert lib.ar_allreduce_noalloc(rs, None, None, None) == B.AR_ERR_INVALID_ARG
+        assert lib.ar_allgather(rs, None, None) == B.AR_ERR_INVALID_ARG
+        assert lib.ar_reduce_scatter(ar, None, None) == B.AR_ERR_INVALID_ARG
+        # owned ranges: ranks outside the plan, schedules without halves
+        with pytest.raises(B.ArError) as e:
+            B.ar_plan_owned_range(rs, 4)
+        assert e.value.status == B.AR_ERR_INVALID_ARG
+        with pytest.raises(B.ArError) as e:
+            B.ar_plan_owned_range(tree, 0)
+        assert e.value.status == B.AR_ERR_UNSUPPORTED
+        assert B.ar_plan_owned_range(ar, 0) == (25, 50)
+    finally:
+        for p in (rs, ar, tree):
+            B.ar_plan_destroy(p)
+
+
+def test_int8_allreduce_owned_ranges_count_elements():
+    """INT8 plans cut on 128-element blocks; the owned range is reported in
+    elements, clipped to the buffer."""
+    count = 1000  # 8 blocks, the last short
+    p = B.ar_plan_create(4, 1, count, "int8_ef", "ring")
+    try:
+        got = [B.ar_plan_owned_range(p, r) for r in range(4)]
+    finally:
+        B.ar_plan_destroy(p)
+    blocks = [part(8, 4, (r + 1) % 4) for r in range(4)]
+    assert got == [(min(lo * 128, count), min(hi * 128, count)) for lo, hi in blocks]
