@@ -668,6 +668,36 @@ def main():
                 extra["onepass"]["staged_phases_GBps"] = staged
                 extra["onepass"]["frac_of_staged_phases"] = round(op_gbps / staged, 4)
 
+    # ---- the schedule's two halves on their own (ar_reduce_scatter,
+    # ar_allgather), step mode, on the same buffers; nccl-tests convention:
+    # algbw = S / T with S the bytes of one rank's whole buffer, busbw =
+    # algbw * (N-1)/N (each half moves (N-1)/N * S per rank)
+    if not args.no_extra and not bucketed and not quant and sched in ("ring", "hierarchical", "rabenseifner"):
+        halves = {}
+        for coll, call in (("reduce_scatter", B.ar_reduce_scatter), ("allgather", B.ar_allgather)):
+            hp = B.ar_plan_create_collective(n, group, count, dtype, sched, coll)
+            try:
+                reset_inputs()
+                for _ in range(args.warmup):
+                    call(hp, bufs, stream)
+                torch.cuda.synchronize()
+                t_h = time.perf_counter()
+                for _ in range(args.steps):
+                    call(hp, bufs, stream)
+                torch.cuda.synchronize()
+                h_ms = (time.perf_counter() - t_h) * 1e3 / max(args.steps, 1)
+                h_st = B.ar_plan_stats(hp)
+            finally:
+                B.ar_plan_destroy(hp)
+            h_alg = S / (h_ms * 1e-3) / 1e9
+            h_gbps = h_st["hbm_bytes_model"] / (h_ms * 1e-3) / 1e9
+            halves[coll] = {"ms_per_call": round(h_ms, 4), "busbw_GBps": round(h_alg * (n - 1) / n, 1),
+                            "algbw_GBps": round(h_alg, 1), "launches": h_st["launches"], "rounds": h_st["steps"],
+                            "hbm_model_GBps": round(h_gbps, 1),
+                            "hbm_model_frac_of_peak": round(h_gbps / HBM_PEAK_GBPS, 4)}
+        extra["halves"] = halves
+        reset_inputs()
+
     # ---- the same exec mode replayed as one HIP graph per call
     if not args.no_extra:
         for name, graph in (("graph", True),):
