@@ -25,6 +25,7 @@ the same inputs.
 """
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -61,7 +62,7 @@ WORKLOADS = {
 
 KIND_NAMES = {0x100: "chunk_reduce", 0x200: "chunk_copy", 0x300: "onepass_ring", 0x400: "onepass_hier",
               0x500: "onepass_tree", 0x600: "onepass_dtree", 0x700: "q_encode", 0x800: "q_reduce", 0x900: "q_copy",
-              0xA00: "q_decode"}
+              0xA00: "q_decode", 0xB00: "onepass_fan"}
 
 
 def kernel_label(kind, shape=None, nranks=None):
@@ -83,6 +84,8 @@ def kernel_label(kind, shape=None, nranks=None):
         return f"q_reduce<{'true' if kind & 8 else 'false'}>"
     if fam == 0x900 and kind & 16:
         return f"q_copy_dec<{'false' if kind & 32 else 'true'}>"
+    if fam == 0xB00 and shape:
+        return f"onepass_fan<{kind & 0xFF}, {shape['cpol']}>"
     if fam >= 0x700:
         return KIND_NAMES[fam]
     if kind & 3 == 3:  # one-pass fold of an INT8 plan
@@ -674,9 +677,11 @@ def main():
     # algbw * (N-1)/N (each half moves (N-1)/N * S per rank)
     if not args.no_extra and not bucketed and not quant and sched in ("ring", "hierarchical", "rabenseifner"):
         halves = {}
-        for coll, call in (("reduce_scatter", B.ar_reduce_scatter), ("allgather", B.ar_allgather)):
+        for (coll, call), hmode in itertools.product((("reduce_scatter", B.ar_reduce_scatter),
+                                                      ("allgather", B.ar_allgather)), ("steps", "onepass")):
             hp = B.ar_plan_create_collective(n, group, count, dtype, sched, coll)
             try:
+                B.ar_plan_set_exec(hp, hmode)
                 reset_inputs()
                 for _ in range(args.warmup):
                     call(hp, bufs, stream)
@@ -691,7 +696,7 @@ def main():
                 B.ar_plan_destroy(hp)
             h_alg = S / (h_ms * 1e-3) / 1e9
             h_gbps = h_st["hbm_bytes_model"] / (h_ms * 1e-3) / 1e9
-            halves[coll] = {"ms_per_call": round(h_ms, 4), "busbw_GBps": round(h_alg * (n - 1) / n, 1),
+            halves[coll if hmode == "steps" else coll + "_onepass"] = {"ms_per_call": round(h_ms, 4), "busbw_GBps": round(h_alg * (n - 1) / n, 1),
                             "algbw_GBps": round(h_alg, 1), "launches": h_st["launches"], "rounds": h_st["steps"],
                             "hbm_model_GBps": round(h_gbps, 1),
                             "hbm_model_frac_of_peak": round(h_gbps / HBM_PEAK_GBPS, 4)}

@@ -34,6 +34,7 @@ COLLECTIVES = {"allreduce": AR_ALLREDUCE, "reduce_scatter": AR_REDUCE_SCATTER, "
 # kernel kind codes reported by ar_plan_launch_info
 KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE, KIND_DTREE = 0x100, 0x200, 0x300, 0x400, 0x500, 0x600
 KIND_QENCODE, KIND_QREDUCE, KIND_QCOPY, KIND_QDECODE = 0x700, 0x800, 0x900, 0xA00
+KIND_FAN = 0xB00
 QBLOCK = 128
 LOC_SCRATCH = 1000
 

@@ -203,9 +203,11 @@ void lower_launches(ar_plan_t *pl) {
     // a dispatch holds at most 2^32 - 1 work-items per grid dimension (here
     // 2^31 - 1 along the tiles) and 65535 workgroups along the ops
     const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind, pl->p.nranks);
-    // the LDS-staged folds walk their op's tiles with the grid's stride, so
-    // a grid capped at the dispatch limit still covers every tile
-    if (!quant && ar_dev::lds_staged(L.kind, pl->p.nranks)) gx = std::min<int64_t>(gx, 0x7fffffff / threads);
+    // the LDS-staged folds and the one-pass all-gather walk their op's tiles
+    // with the grid's stride, so a grid capped at the dispatch limit still
+    // covers every tile
+    if (!quant && (ar_dev::lds_staged(L.kind, pl->p.nranks) || (L.kind & 0xF00) == ar::kKFan))
+      gx = std::min<int64_t>(gx, 0x7fffffff / threads);
     if (gx * threads > 0x7fffffff || static_cast<int64_t>(L.ops.size()) > ar::kMaxLaunchOps)
       pl->launch_err = "op too large for one launch grid";
     pl->grid_x.push_back(static_cast<uint32_t>(std::min<int64_t>(gx, 0x7fffffff)));
@@ -742,8 +744,6 @@ ar_status_t set_exec(ar_plan_t *plan, int32_t exec) {
   if (!plan) return fail(AR_ERR_INVALID_ARG, "plan is NULL");
   const ar::Exec mode = static_cast<ar::Exec>(exec);
   if (mode == plan->p.exec && plan->prepared) return AR_OK;
-  if (mode == ar::kOnePass && plan->p.coll != ar::kAllReduce)
-    return fail(AR_ERR_UNSUPPORTED, "reduce-scatter and all-gather plans run in the step modes");
   ar::Plan trial = plan->p;
   const std::string err = ar::relower(trial, mode);
   if (!err.empty()) return fail(AR_ERR_INVALID_ARG, err);

@@ -577,6 +577,15 @@ std::string lower_onepass(Plan &p) {
   // (elements, or blocks for INT8)
   if ((p.nranks == 1 && p.dtype != kI8EF) || p.count == 0) return "";
   const int32_t dt = p.dtype;
+  if (p.coll == kAllGather) {
+    // every owned range goes from its owner to every other rank in one copy
+    Launch L{kKFan | static_cast<int32_t>(elem_bytes(p.dtype)), {}};
+    for (int r = 0; r < p.nranks; ++r)
+      if (p.owned[r].second > p.owned[r].first)
+        L.ops.push_back({p.owned[r].first, p.owned[r].second, r, kLocNone, kLocNone, kLocNone, 0});
+    p.launches.push_back(std::move(L));
+    return "";
+  }
   if (p.sched == kRing || p.nranks == 1) {
     // element in chunk c: ((x_c + x_{c+1}) + ...) + x_{c+N-1} -- chunk c is
     // first sent by rank c at reduce-scatter step 0 and gains one rank per step
@@ -615,6 +624,25 @@ std::string lower_onepass(Plan &p) {
     Launch L{kKTree | dt, {}};
     L.ops.push_back({0, p.units, kLocNone, kLocNone, kLocNone, kLocNone, 0});
     p.launches.push_back(std::move(L));
+  }
+  if (p.coll == kReduceScatter) {
+    // a reduce-scatter keeps each range on its owner: every op covers one
+    // owned range (the tree fold, one op over everything, is cut into them;
+    // its order does not depend on the range) and stores into that rank only
+    for (Launch &L : p.launches) {
+      if ((L.kind & 0xF00) == kKTree) {
+        L.ops.clear();
+        for (int r = 0; r < p.nranks; ++r)
+          if (p.owned[r].second > p.owned[r].first)
+            L.ops.push_back({p.owned[r].first, p.owned[r].second, kLocNone, kLocNone, r, kLocNone, 0});
+        continue;
+      }
+      for (Op &op : L.ops) {
+        for (int r = 0; r < p.nranks && op.o == kLocNone; ++r)
+          if (p.owned[r].first == op.lo && p.owned[r].second == op.hi) op.o = r;
+        if (op.o == kLocNone) return "internal: a one-pass op is not an owned range";
+      }
+    }
   }
   return "";
 }
@@ -663,8 +691,11 @@ void compute_stats(Plan &p) {
         h += el * (1 + 4) + 4 * len;
       } else if (p.dtype == kI8EF) {
         h += el * 16 * static_cast<uint64_t>(p.nranks);  // g, e in; e, result out, per rank
+      } else if (fam == kKFan) {
+        h += len * eb * static_cast<uint64_t>(p.nranks);  // the owner's range in, N - 1 copies out
       } else {
-        h += len * 2 * eb * static_cast<uint64_t>(p.nranks);
+        // every rank in; the result out to every rank, or to the owner only
+        h += len * eb * (static_cast<uint64_t>(p.nranks) + (op.o != kLocNone ? 1 : static_cast<uint64_t>(p.nranks)));
       }
     }
   }
@@ -851,7 +882,6 @@ std::string build_plan(Plan &p, int nranks, int group_size, int64_t count, Dtype
     if (sched != kRing && sched != kHier && sched != kRaben)
       return "reduce-scatter and all-gather plans need the ring, hierarchical or Rabenseifner schedule";
     if (dtype == kI8EF) return "reduce-scatter and all-gather plans are fp32 or bf16";
-    if (exec == kOnePass) return "reduce-scatter and all-gather plans run in the step modes";
     *unsupported = false;
   }
   p = Plan{};
@@ -909,7 +939,6 @@ bool owned_range(const Plan &p, int rank, int64_t *lo, int64_t *hi) {
 
 std::string relower(Plan &p, Exec exec) {
   if (exec != kSteps && exec != kStepsUnfused && exec != kOnePass) return "unknown exec mode";
-  if (exec == kOnePass && p.coll != kAllReduce) return "reduce-scatter and all-gather plans run in the step modes";
   return lower(p, exec);
 }
 
@@ -958,12 +987,17 @@ double cost_alpha_beta_ex(const Plan &p, double alpha_intra, double alpha_cross,
 
 int64_t launch_write_bytes(const Plan &p, const Launch &L) {
   const int32_t fam = L.kind & 0xF00;
+  const bool fold = fam == kKRing || fam == kKHier || fam == kKTree || fam == kKDTree;
   int64_t elems = 0;
-  for (const Op &o : L.ops) elems += unit_elems(p, o.lo, o.hi) * ((o.o2 != kLocNone) ? 2 : 1);
+  for (const Op &o : L.ops) {
+    const int64_t e = unit_elems(p, o.lo, o.hi);
+    if (fold) elems += e * (o.o != kLocNone ? 1 : p.nranks);  // the owner only, or every rank
+    else if (fam == kKFan) elems += e * (p.nranks - 1);
+    else elems += e * ((o.o2 != kLocNone) ? 2 : 1);
+  }
   int64_t eb = buffer_elem_bytes(p.dtype);
   if (fam == kKReduce && p.dtype == kBF16 && !(L.kind & kFlagOBf)) eb = 4;  // fp32 partials
   if (fam == kKQReduce || fam == kKQCopy || fam == kKQEncode) eb = 1;       // codes
-  if (fam == kKRing || fam == kKHier || fam == kKTree || fam == kKDTree) elems *= p.nranks;
   return elems * eb;
 }
 

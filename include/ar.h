@@ -107,7 +107,8 @@ typedef enum {
 } ar_schedule_t;
 
 /*
- * How a plan is executed.  Every mode gives bit-identical results.
+ * How a plan is executed.  Every mode gives bit-identical results (a
+ * reduce-scatter: on its owned ranges).
  *   AR_EXEC_STEPS          one kernel launch per step of the schedule; the
  *                          reduce-scatter step that completes a chunk is fused
  *                          with the all-gather step that first forwards it
@@ -122,6 +123,8 @@ typedef enum {
  *                          word per thread, and each wave stores its own
  *                          ranks; otherwise, and for AR_INT8_EF, each thread
  *                          folds in registers and stores into every rank.
+ *                          (For reduce-scatter and all-gather plans see
+ *                          ar_collective_t.)
  */
 typedef enum { AR_EXEC_STEPS = 0, AR_EXEC_STEPS_UNFUSED = 1, AR_EXEC_ONEPASS = 2 } ar_exec_t;
 
@@ -248,24 +251,31 @@ ar_status_t ar_allreduce_ef(ar_plan_t *plan, void *const *rank_bufs, void *const
  *                      recursive halving (Primer 4.3).  Afterwards rank r's
  *                      owned range (ar_plan_owned_range) holds the reduced
  *                      values, with the same bits as the all-reduce gives
- *                      there.  Its other elements hold what the schedule left
- *                      in them: fp32 and AR_BFLOAT16_EACH_STEP partial sums,
- *                      while AR_BFLOAT16 keeps its fp32 partials in the plan's
- *                      scratch and leaves those elements unchanged.
+ *                      there.  In the step modes its other elements hold
+ *                      what the schedule left in them: fp32 and
+ *                      AR_BFLOAT16_EACH_STEP partial sums, while AR_BFLOAT16
+ *                      keeps its fp32 partials in the plan's scratch and
+ *                      leaves those elements unchanged; AR_EXEC_ONEPASS folds
+ *                      each owned range from every rank in the schedule's
+ *                      order and stores it into its owner only, leaving every
+ *                      other element unchanged.
  *   AR_ALLGATHER       the schedule's copy rounds only: the cross-group
  *                      ring's copy half and phase 3 for the hierarchical
  *                      schedule, recursive doubling for Rabenseifner.  Each
  *                      rank's owned range is read from that rank and written
  *                      to every other rank; nothing else is read.
+ *                      AR_EXEC_ONEPASS does that in one launch: a workgroup
+ *                      reads a tile of an owned range once and each of its
+ *                      waves stores it into its own ranks.
  */
 typedef enum { AR_ALLREDUCE = 0, AR_REDUCE_SCATTER = 1, AR_ALLGATHER = 2 } ar_collective_t;
 
 /*
  * ar_plan_create for one collective.  AR_REDUCE_SCATTER and AR_ALLGATHER
  * plans take the ring, hierarchical or Rabenseifner schedule and fp32 or
- * bf16 (either mode), and run in the step modes (the two are the same here:
- * no reduce is followed by a copy); other schedules, AR_INT8_EF, and
- * ar_plan_set_exec(AR_EXEC_ONEPASS) give AR_ERR_UNSUPPORTED.  Statistics,
+ * bf16 (either mode), and run in every exec mode (AR_EXEC_STEPS and
+ * AR_EXEC_STEPS_UNFUSED are the same here: no reduce is followed by a copy);
+ * other schedules and AR_INT8_EF give AR_ERR_UNSUPPORTED.  Statistics,
  * the cost models, graphs, profiling and guard zones cover the plan's own
  * rounds.  The plan runs with ar_reduce_scatter or ar_allgather only
  * (ar_allreduce, ar_allreduce_ef and ar_allreduce_noalloc refuse it with

@@ -66,6 +66,10 @@ def run(plan, bufs, dtype, group_size):
                     _write(o2, lo, hi, s, bool(kind & 4), bufs, scratch, fp32_mode, shift, stride)
             elif fam == B.KIND_COPY:
                 bufs[o][lo:hi] = bufs[a][lo:hi]
+            elif fam == B.KIND_FAN:  # one-pass all-gather: rank a's range to every other rank
+                for r in range(n):
+                    if r != a:
+                        bufs[r][lo:hi] = bufs[a][lo:hi]
             else:
                 each = (kind & 3) == 2  # bf16 rounded at every add
 
@@ -102,7 +106,7 @@ def run(plan, bufs, dtype, group_size):
                             part = fold(part, cols[g * G + (ls + t) % G])
                         acc = part if acc is None else fold(acc, part)
                 res = acc if fp32_mode else to_bf16_bits(acc)
-                for r in range(n):
+                for r in (range(n) if o < 0 else (o,)):  # a reduce-scatter stores into the owner only
                     bufs[r][lo:hi] = res
     return bufs
 

@@ -3,9 +3,13 @@
 ar_reduce_scatter and ar_allgather run plans of one half of the ring,
 hierarchical and Rabenseifner schedules (Scaling ML systems ch. 06, "Six
 basic primitives": an all-reduce is a reduce-scatter followed by an
-all-gather).  Every element of every rank is compared with the oracle's
-half on the same seeded inputs (the reduce-scatter leaves partial sums or
-untouched inputs outside each owned range, and those are compared too);
+all-gather), in every exec mode: the step modes run the halves' rounds; the
+one-pass reduce-scatter folds each owned range from every rank and stores it
+into its owner only, and the one-pass all-gather copies each owned range
+from its owner to every other rank.  Every element of every rank is
+compared with the oracle on the same seeded inputs (outside the owned
+ranges, the step-mode reduce-scatter leaves partial sums or untouched
+inputs and the one-pass one untouched inputs, and those are compared too);
 the two halves in a row must give the all-reduce's bits, also at the
 16-rank 192 MiB size the benchmark uses.
 """
@@ -54,20 +58,26 @@ def test_halves_match_oracle(sched, n, g, dtype):
                                      dtype="fp32" if dtype == "fp32" else "bf16")
         want = {"reduce_scatter": oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g),
                 "allgather": oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)}
+        # the one-pass reduce-scatter stores only the owned ranges
+        want["reduce_scatter_onepass"] = [x.copy() for x in xs]
+        for r, (lo, hi) in enumerate(oracle.owned_ranges(n, count, sched, group_size=g)):
+            want["reduce_scatter_onepass"][r][lo:hi] = want["reduce_scatter"][r][lo:hi]
         for coll in ("reduce_scatter", "allgather"):
-            for mode in ("steps", "steps_unfused"):
+            for mode in ("steps", "steps_unfused", "onepass"):
                 _say(f"case {coll} {sched} n={n} g={g} count={count} {dtype} {mode}")
                 got = _run(xs, dtype, sched, g, coll, mode)
+                ref = want[coll + ("_onepass" if coll == "reduce_scatter" and mode == "onepass" else "")]
                 for r in range(n):
-                    if not np.array_equal(got[r], want[coll][r].view(bv)):
-                        bad = np.flatnonzero(got[r] != want[coll][r].view(bv))
+                    if not np.array_equal(got[r], ref[r].view(bv)):
+                        bad = np.flatnonzero(got[r] != ref[r].view(bv))
                         raise AssertionError(f"{coll} {sched} {dtype} {mode} n={n} rank {r}: {len(bad)} "
                                              f"elements differ, first at {bad[:5]}")
 
 
+@pytest.mark.parametrize("mode", ["steps", "onepass"])
 @pytest.mark.parametrize("sched,g,dtype", [("ring", 8, "fp32"), ("hierarchical", 8, "fp32"),
                                            ("rabenseifner", 1, "bf16"), ("ring", 8, "bf16_each")])
-def test_halves_in_a_row_equal_the_allreduce_16x192mib(sched, g, dtype):
+def test_halves_in_a_row_equal_the_allreduce_16x192mib(sched, g, dtype, mode):
     """At the benchmark's size (16 ranks x 192 MiB, in the launch order the
     default cache gives): reduce-scatter then all-gather on one set of
     buffers, the all-reduce on a copy; every element equal (compared on the
@@ -77,7 +87,7 @@ def test_halves_in_a_row_equal_the_allreduce_16x192mib(sched, g, dtype):
 
     n = 16
     count = 12288 * 4096 * (1 if dtype == "fp32" else 2)
-    _say(f"case halves-in-a-row {sched} g={g} {dtype} 16 x 192 MiB")
+    _say(f"case halves-in-a-row {sched} g={g} {dtype} {mode} 16 x 192 MiB")
     gen = torch.Generator(device="cuda:0").manual_seed(11)
     if dtype == "fp32":
         a = [torch.randn(count, device="cuda:0", generator=gen) * 1e-3 for _ in range(n)]
@@ -88,6 +98,8 @@ def test_halves_in_a_row_equal_the_allreduce_16x192mib(sched, g, dtype):
     plans = [B.ar_plan_create_collective(n, g, count, dtype, sched, c) for c in ("reduce_scatter", "allgather")]
     whole = B.ar_plan_create(n, g, count, dtype, sched)
     try:
+        for p in plans:
+            B.ar_plan_set_exec(p, mode)
         B.ar_reduce_scatter(plans[0], a, s)
         B.ar_allgather(plans[1], a, s)
         B.ar_allreduce(whole, b, s)

@@ -62,16 +62,29 @@ def test_plan_halves_transfers_and_stats_equal_oracle(sched, n, g):
         assert cost == pytest.approx(cost_whole, rel=1e-12)  # the rounds split between the halves
 
 
+def onepass_reduce_scatter_expected(xs, dtype, sched, g):
+    """The one-pass reduce-scatter: the oracle's values on each owned range,
+    every other element as it was (no partial sum is ever stored)."""
+    rs = oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g)
+    out = [x.copy() for x in xs]
+    for r, (lo, hi) in enumerate(oracle.owned_ranges(len(xs), len(xs[0]), sched, group_size=g)):
+        out[r][lo:hi] = rs[r][lo:hi]
+    return out
+
+
 @pytest.mark.parametrize("sched,n,g", CASES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_each"])
-@pytest.mark.parametrize("mode", ["steps", "steps_unfused"])
+@pytest.mark.parametrize("mode", ["steps", "steps_unfused", "onepass"])
 def test_plan_halves_launch_lists_equal_oracle(sched, n, g, dtype, mode):
     """Reduce-scatter and all-gather launch lists, run by the interpreter,
     give the oracle's halves bit for bit in every element, with a cache that
-    splits every round into pieces and with one that splits none."""
+    splits every round into pieces and with one that splits none.  The
+    one-pass reduce-scatter leaves the elements outside the owned ranges
+    untouched."""
     for count in (0, 37, 1031):
         xs = _inputs(n, count, dtype, seed=count + 11 * n)
-        want_rs = oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g)
+        want_rs = (onepass_reduce_scatter_expected(xs, dtype, sched, g) if mode == "onepass" else
+                   oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g))
         want_ag = oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)
         for cache in (64, 1 << 30):
             for coll, want in (("reduce_scatter", want_rs), ("allgather", want_ag)):
@@ -102,10 +115,6 @@ def test_collective_plan_errors():
     ar = B.ar_plan_create(4, 1, 100, "fp32", "ring")
     tree = B.ar_plan_create(4, 1, 100, "fp32", "tree")
     try:
-        with pytest.raises(B.ArError) as e:
-            B.ar_plan_set_exec(rs, "onepass")
-        assert e.value.status == B.AR_ERR_UNSUPPORTED
-        assert B.ar_plan_stats(rs)["exec"] == B.AR_EXEC_STEPS  # the plan is unchanged
         # a plan runs only through the call of its own collective; these
         # refusals happen before any pointer is read or device call made
         lib = B.lib()
@@ -124,6 +133,32 @@ def test_collective_plan_errors():
         assert B.ar_plan_owned_range(ar, 0) == (25, 50)
     finally:
         for p in (rs, ar, tree):
+            B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("sched,n,g", [("ring", 16, 1), ("hierarchical", 16, 8), ("rabenseifner", 16, 1),
+                                        ("ring", 3, 1), ("rabenseifner", 2, 1)])
+def test_onepass_halves_shape_and_bytes(sched, n, g):
+    """One launch each.  The reduce-scatter folds every owned range from all
+    ranks and writes it to its owner only: (N + 1) * S model bytes; the
+    all-gather copies each owned range from its owner to the N - 1 others:
+    N * S."""
+    count = 16 * 1000
+    for coll, kinds, model in (("reduce_scatter", {0x300, 0x400, 0x500}, (n + 1) * count * 4),
+                               ("allgather", {B.KIND_FAN}, n * count * 4)):
+        p = _coll_plan(n, g, count, "fp32", sched, coll)
+        try:
+            B.ar_plan_set_exec(p, "onepass")
+            assert B.ar_plan_num_launches(p) == 1
+            kind, nops = B.ar_plan_launch_info(p, 0)
+            assert kind & 0xF00 in kinds and nops == n
+            ops = B.ar_plan_launch_ops(p, 0)
+            owners = ops["o"] if coll == "reduce_scatter" else ops["a"]
+            assert sorted(int(x) for x in owners) == list(range(n))
+            for r, lo, hi in zip(owners, ops["lo"], ops["hi"]):
+                assert B.ar_plan_owned_range(p, int(r)) == (int(lo), int(hi))
+            assert B.ar_plan_stats(p)["hbm_bytes_model"] == model
+        finally:
             B.ar_plan_destroy(p)
 
 
