@@ -144,3 +144,59 @@ def test_int8_ef_beyond_2_32_elements(mode):
         want = np.asarray(folds.fold_at(col, int(blk), nblk, sched, 1, add), np.float32)
         for r in range(n):
             assert np.array_equal(g1[r][sl].view(np.uint32), want.view(np.uint32)), f"result rank {r} block {blk}"
+
+
+@pytest.mark.parametrize("sched,n,g,dtype,mode", [
+    ("ring", 4, 1, "fp32", "onepass"),
+    ("hierarchical", 4, 2, "bf16", "onepass"),
+    ("rabenseifner", 4, 1, "fp32", "steps"),
+])
+def test_halves_beyond_2_32_elements(sched, n, g, dtype, mode):
+    """Reduce-scatter, then all-gather, on buffers beyond 2^32 elements:
+    after the reduce-scatter every sampled element of a rank's owned range
+    holds the schedule's sum (and, in the one-pass mode, every other one its
+    input); after the all-gather every rank holds the sums everywhere."""
+    import torch
+
+    _say(f"large halves {sched} n={n} g={g} {dtype} {mode} count={COUNT}")
+    gen = "fp32" if dtype == "fp32" else "bf16"
+    bufs = [workloads.device_rank(r, COUNT, seed=13, sigma=1.0, dtype=gen) for r in range(n)]
+    idx = _positions(COUNT, 1, np.random.default_rng(4))
+    before = _gather(bufs, idx)
+    plans = [B.ar_plan_create_collective(n, g, COUNT, dtype, sched, c) for c in ("reduce_scatter", "allgather")]
+    try:
+        owned = [B.ar_plan_owned_range(plans[0], r) for r in range(n)]
+        for p in plans:
+            B.ar_plan_set_exec(p, mode)
+        B.ar_reduce_scatter(plans[0], bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        after_rs = _gather(bufs, idx)
+        B.ar_allgather(plans[1], bufs, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        after_ag = _gather(bufs, idx)
+    finally:
+        for p in plans:
+            B.ar_plan_destroy(p)
+    del bufs
+    torch.cuda.empty_cache()
+    if dtype == "fp32":
+        want = np.array([folds.fold_at([before[r][i] for r in range(n)], int(e), COUNT, sched, g)
+                         for i, e in enumerate(idx)], np.float32).view(np.uint32)
+        view = np.uint32
+    else:
+        vals = [folds.widen(b.view(np.uint16)) for b in before]
+        acc = np.array([folds.fold_at([vals[r][i] for r in range(n)], int(e), COUNT, sched, g, folds.add32)
+                        for i, e in enumerate(idx)], np.float32)
+        want = folds.to_bf16_bits(acc)
+        view = np.uint16
+    for r in range(n):
+        lo, hi = owned[r]
+        mine = (idx >= lo) & (idx < hi)
+        got = after_rs[r].view(view)
+        bad = np.flatnonzero(mine & (got != want))
+        assert bad.size == 0, f"reduce-scatter rank {r}: {bad.size} owned elements differ, first at {idx[bad[:5]]}"
+        if mode == "onepass":
+            bad = np.flatnonzero(~mine & (got != before[r].view(view)))
+            assert bad.size == 0, f"reduce-scatter rank {r}: {bad.size} other elements changed"
+        bad = np.flatnonzero(after_ag[r].view(view) != want)
+        assert bad.size == 0, f"all-gather rank {r}: {bad.size} of {idx.size} sampled elements differ"
