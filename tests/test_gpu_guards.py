@@ -105,6 +105,47 @@ def test_canaries_every_schedule_and_mode(sched, n, g, dtype):
             B.ar_plan_destroy(p)
 
 
+@pytest.mark.parametrize("sched,n,g", [("ring", 5, 1), ("hierarchical", 6, 3), ("rabenseifner", 8, 1)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_canaries_reduce_scatter_and_allgather(sched, n, g, dtype):
+    """The halves in every mode: canaries around the rank buffers and around
+    the plan's scratch (bf16 reduce-scatter partials) stay intact, and the
+    results are the oracle's."""
+    import torch
+
+    count = 100003
+    gen = "fp32" if dtype == "fp32" else "bf16"
+    view = np.float32 if dtype == "fp32" else np.int16
+    bv = np.uint32 if dtype == "fp32" else np.uint16
+    xs = workloads.normal_inputs(n, count, seed=n + 1, sigma=1.0, dtype=gen)
+    owned = oracle.owned_ranges(n, count, sched, group_size=g)
+    want = {"reduce_scatter": oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g),
+            "allgather": oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)}
+    for coll, call in (("reduce_scatter", B.ar_reduce_scatter), ("allgather", B.ar_allgather)):
+        for mode in ("steps", "onepass"):
+            what = f"{coll} {sched} n={n} g={g} {dtype} {mode}"
+            _say(f"case guards {what}")
+            p = B.ar_plan_create_collective(n, g, count, dtype, sched, coll)
+            try:
+                B.ar_plan_set_exec(p, mode)
+                B.ar_plan_set_guard(p, 1 << 16)
+                bufs, allocs = _guarded(xs, view)
+                call(p, bufs, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                for r in range(n):
+                    got = bufs[r].cpu().numpy().view(bv)
+                    ref = want[coll][r].view(bv)
+                    if coll == "reduce_scatter" and mode == "onepass":  # only the owned range changes
+                        lo, hi = owned[r]
+                        ref = xs[r].view(bv).copy()
+                        ref[lo:hi] = want[coll][r].view(bv)[lo:hi]
+                    assert np.array_equal(got, ref), what
+                _canaries_intact(allocs, count, what + " rank buffers")
+                B.ar_plan_check_guards(p)
+            finally:
+                B.ar_plan_destroy(p)
+
+
 @pytest.mark.parametrize("sched,n", [("ring", 8), ("rabenseifner", 8)])
 def test_canaries_bucketed(sched, n):
     """Bucketed bf16 arenas, batched and one by one: the arenas' canaries and

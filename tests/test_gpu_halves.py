@@ -117,8 +117,9 @@ def test_halves_in_a_row_equal_the_allreduce_16x192mib(sched, g, dtype, mode):
 
 
 def test_halves_graph_replays_and_empty_calls():
-    """Graph replay of a reduce-scatter plan gives the eager bits on every
-    replay; count 0 touches nothing (NULL pointers accepted)."""
+    """Graph replay of a reduce-scatter plan (steps) and of a one-pass
+    all-gather gives the eager bits on every replay; count 0 touches nothing
+    (NULL pointers accepted)."""
     import torch
 
     n, count = 16, 100003
@@ -136,6 +137,28 @@ def test_halves_graph_replays_and_empty_calls():
                 t.copy_(q)
             torch.cuda.synchronize()
             B.ar_reduce_scatter(p, bufs, s)
+            torch.cuda.synchronize()
+            got = to_host_bits(bufs, "fp32")
+            for r in range(n):
+                np.testing.assert_array_equal(got[r], want[r].view(np.uint32))
+    finally:
+        B.ar_plan_destroy(p)
+    # the one-pass all-gather (the fan-out kernel) replayed as a graph
+    xs = workloads.normal_inputs(n, count, seed=22, sigma=1.0, dtype="fp32")
+    want = oracle.allgather([x.copy() for x in xs], "fp32", "hierarchical", group_size=4)
+    p = B.ar_plan_create_collective(n, 4, count, "fp32", "hierarchical", "allgather")
+    try:
+        B.ar_plan_set_exec(p, "onepass")
+        B.ar_plan_set_graph(p, True)
+        bufs = to_device(xs, "fp32")
+        pristine = [t.clone() for t in bufs]
+        s = torch.cuda.current_stream()
+        for rep in range(3):
+            _say(f"case allgather onepass graph replay {rep}")
+            for t, q in zip(bufs, pristine):
+                t.copy_(q)
+            torch.cuda.synchronize()
+            B.ar_allgather(p, bufs, s)
             torch.cuda.synchronize()
             got = to_host_bits(bufs, "fp32")
             for r in range(n):
