@@ -4,8 +4,8 @@ and UndefinedBehaviorSanitizer.
 Both libraries are built again with the sanitizers (the library's host code
 only; device code is unchanged) by ROCm's clang, so that they share one
 sanitizer runtime, which is preloaded into a child pytest process that runs
-the CPU tests of the planner, the bucket fuser, the debug aids and the
-oracle against them.  Any sanitizer report aborts that process.
+the CPU tests of the planner (all-reduce and its halves), the bucket fuser,
+the debug aids and the oracle against them.  Any sanitizer report aborts that process.
 """
 import glob
 import os
@@ -22,7 +22,8 @@ from oracle import build as oracle_build  # noqa: E402
 
 SUBSET = ["test_plan_cpu.py", "test_plan_random.py", "test_int8_plan_cpu.py", "test_debug_cpu.py",
           "test_binding_checks.py", "test_buckets.py", "test_oracle_pages.py", "test_oracle_bruteforce.py",
-          "test_oracle_int8ef.py", "test_overlap.py", "test_zz_no_alloc.py"]
+          "test_oracle_int8ef.py", "test_oracle_halves.py", "test_halves_cpu.py", "test_overlap.py",
+          "test_zz_no_alloc.py"]
 
 
 def _stale(lib, sources):
