@@ -173,3 +173,22 @@ def test_int8_allreduce_owned_ranges_count_elements():
         B.ar_plan_destroy(p)
     blocks = [part(8, 4, (r + 1) % 4) for r in range(4)]
     assert got == [(min(lo * 128, count), min(hi * 128, count)) for lo, hi in blocks]
+
+
+def test_large_halves_describe_but_do_not_run():
+    """Reduce-scatter and all-gather plans of more than 64 ranks give their
+    transfers, owned ranges and statistics; running them is refused before
+    any device call."""
+    n, count = 256, 1 << 20
+    for coll, call, rounds in (("reduce_scatter", B.ar_reduce_scatter, n - 1), ("allgather", B.ar_allgather, n - 1)):
+        p = _coll_plan(n, 8, count, "fp32", "ring", coll)
+        try:
+            st = B.ar_plan_stats(p)
+            assert st["steps"] == rounds and st["launches"] == 0
+            assert st["bytes_sent"] == [(n - 1) * (count // n) * 4] * n
+            assert [B.ar_plan_owned_range(p, r) for r in (0, n - 1)] == [part(count, n, 1), part(count, n, 0)]
+            with pytest.raises(B.ArError) as ei:
+                call(p, [1 << 20] * n)
+            assert ei.value.status == B.AR_ERR_UNSUPPORTED
+        finally:
+            B.ar_plan_destroy(p)
