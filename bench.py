@@ -100,6 +100,8 @@ def kernel_label(kind, shape=None, nranks=None):
             fold = f"DTreeFoldOp<{nranks}>"
         else:
             fold = {0x300: "RingFold", 0x400: "HierFold"}[fam]
+        if kind & 0x1000 and nranks <= 16:  # a reduce-scatter fold: its own tiles
+            fold = f"OwnerTiles<{fold}>"
         return f"onepass_lds<{bf}, {each}, {ncls}, {shape['batch']}, {shape['cpol']}, {fold}>"
     if shape and fam in (0x300, 0x400):
         return f"{KIND_NAMES[fam]}<{bf}, {each}, {shape['units']}, {shape['batch']}>"

@@ -35,6 +35,7 @@ COLLECTIVES = {"allreduce": AR_ALLREDUCE, "reduce_scatter": AR_REDUCE_SCATTER, "
 KIND_REDUCE, KIND_COPY, KIND_RING, KIND_HIER, KIND_TREE, KIND_DTREE = 0x100, 0x200, 0x300, 0x400, 0x500, 0x600
 KIND_QENCODE, KIND_QREDUCE, KIND_QCOPY, KIND_QDECODE = 0x700, 0x800, 0x900, 0xA00
 KIND_FAN = 0xB00
+KIND_OWNER = 0x1000  # flag: a one-pass fold that stores each op's result into its owner only
 QBLOCK = 128
 LOC_SCRATCH = 1000
 

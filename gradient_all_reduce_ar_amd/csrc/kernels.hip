@@ -803,6 +803,18 @@ constexpr int kLdsUnits = AR_LDS_UNITS;  // 16-byte units per lane and rank in a
 // (1,155 against 1,010 us) for reasons the code does not show.
 constexpr int kCpolLdsWarm = AR_CPOL_LDS_WARM, kCpolLdsCold = AR_CPOL_LDS_COLD;
 static_assert(kLdsUnits >= 1 && kLdsUnits * 32 <= 64, "a staged tile of 32 ranks fits in 64 KiB");
+// Reduce-scatter folds (kKindOwner: each op's result goes to its owner only)
+// of 9 to 16 ranks in 16-wave workgroups (one rank per wave) stage 4 units
+// per lane and rank, 64 KiB at 16 ranks: each wave's gather reads 4 KiB runs
+// of its rank, and the scatter is one store per tile.  Measured on MI355X at
+// 16 x 192 MiB: ring fp32 590 -> 531 us, bf16 626 -> 539, hierarchical 2 x 8
+// fp32 647 -> 558, Rabenseifner fp32 578 -> 530; hierarchical 4 x 3 bf16 at
+// 96 MiB 284 -> 225.  With 8-wave workgroups (two ranks per wave: bf16
+// rounded at each add, the bf16 balanced tree) 4 units were 4-6% slower, at
+// 8 ranks within 3% either way.  The all-reduce folds, whose scatter stores
+// into every rank, were 5-22% slower with 4 units.
+constexpr int kLdsUnitsOwner = 4;
+static_assert(kLdsUnitsOwner * 16 <= 64, "a reduce-scatter tile of 16 ranks fits in 64 KiB");
 
 // Size classes by rank count (up to 16, 32 or 64 ranks): units per lane and
 // rank in a tile, and the ranks one of W waves gathers and scatters at most.
@@ -901,6 +913,8 @@ __device__ __forceinline__ void ring_fold_src(const Src &src, int rank0, int wra
 struct RingFold {
   static constexpr int kClassMin = 16;
   static constexpr bool kBalancedTree = false;
+  static constexpr bool kHalves = true;  // a reduce-scatter plan's fold too
+  static constexpr int kTileUnits = 0;  // the size class's units per lane and rank
   template <bool EACH, class Src>
   static __device__ __forceinline__ void run(const KArgs &a, const DevOp &op, const Src &src, typename Src::P &acc) {
     ring_fold_src<EACH>(src, 0, a.nranks, op.aux, a.nranks, acc);
@@ -910,6 +924,8 @@ struct RingFold {
 struct HierFold {
   static constexpr int kClassMin = 16;
   static constexpr bool kBalancedTree = false;
+  static constexpr bool kHalves = true;
+  static constexpr int kTileUnits = 0;
   template <bool EACH, class Src>
   static __device__ __forceinline__ void run(const KArgs &a, const DevOp &op, const Src &src, typename Src::P &acc) {
     const int G = a.group_size, M = a.nranks / G;
@@ -948,6 +964,8 @@ template <int NMAX, bool PAD>
 struct TreeFold {
   static constexpr int kClassMin = NMAX;
   static constexpr bool kBalancedTree = true;
+  static constexpr bool kHalves = true;
+  static constexpr int kTileUnits = 0;
   template <bool EACH, class Src>
   static __device__ __forceinline__ void run(const KArgs &a, const DevOp &, const Src &src, typename Src::P &acc) {
     using P = typename Src::P;
@@ -995,6 +1013,8 @@ template <int N>
 struct DTreeFoldOp {
   static constexpr int kClassMin = N;
   static constexpr bool kBalancedTree = false;
+  static constexpr bool kHalves = false;
+  static constexpr int kTileUnits = 0;
   template <bool EACH, class Src>
   static __device__ __forceinline__ void run(const KArgs &, const DevOp &op, const Src &src, typename Src::P &acc) {
     typename Src::P sub;
@@ -1010,12 +1030,14 @@ struct DTreeFoldOp {
 };
 
 // NC: rank-count size class, W: waves per workgroup at most (LdsClass); CP:
-// the scatter's store policy (kCpolLdsWarm or kCpolLdsCold).
+// the scatter's store policy (kCpolLdsWarm or kCpolLdsCold); F: the fold,
+// whose kTileUnits (unless 0) replaces the class's units per lane and rank.
 template <bool BF, bool EACH, int NC, int W, int CP, class F>
 __global__ __launch_bounds__(64 * W) void onepass_lds(KArgs args) {
   using U16 = Unit16<BF>;
   constexpr int kE = U16::kE, kES = U16::kES;
-  constexpr int U = LdsClass<NC, W>::kU, kRPW = LdsClass<NC, W>::kRanksPerWave;
+  constexpr int U = F::kTileUnits > 0 ? F::kTileUnits : LdsClass<NC, W>::kU;
+  constexpr int kRPW = LdsClass<NC, W>::kRanksPerWave;
   constexpr int kUnits = 64 * U;                                // units per rank in a tile
   constexpr int kWords = kUnits * 4;                            // 4-byte words per rank in a tile
   constexpr int64_t kTile = static_cast<int64_t>(kUnits) * kE;  // elements
@@ -1198,10 +1220,14 @@ hipError_t launch_dtree(int n, dim3 grid, const KArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// LDS-staged folds: waves per workgroup and dynamic LDS bytes (N * U KiB).
-int lds_units_of(int n) { return n > 32 ? LdsClass<64, 8>::kU : LdsClass<32, 8>::kU; }
-size_t lds_bytes(int n) { return static_cast<size_t>(n) * 64 * lds_units_of(n) * 16; }
-// Workgroups of 16 waves (one rank each) for folds of up to 16 ranks in fp32
+// A reduce-scatter plan's fold F, staged with kLdsUnitsOwner units per lane
+// and rank (9 to 16 ranks, 16-wave workgroups).
+template <class F>
+struct OwnerTiles : F {
+  static constexpr int kTileUnits = kLdsUnitsOwner;
+};
+
+// Waves per workgroup: 16 (one rank each) for folds of up to 16 ranks in fp32
 // and in bf16 with one rounding, except the balanced tree in bf16; 8 waves
 // otherwise, so that more workgroups share a CU.  Measured on MI355X with
 // 16 x 192 MiB, 32 x 96 MiB and 64 x 48 MiB: fp32 at 16 ranks 5.6-5.7 TB/s
@@ -1215,6 +1241,18 @@ int lds_waves(int32_t kind, int n) {
   return (n <= 16 && (dt == 0 || (dt == 1 && !tree))) ? 16 : 8;
 }
 int lds_threads(int32_t kind, int n) { return 64 * std::max(1, std::min(n, lds_waves(kind, n))); }
+
+// LDS-staged folds: units per lane and rank and dynamic LDS bytes (N * U
+// KiB); reduce-scatter folds of 9 to 16 ranks in 16-wave workgroups take
+// kLdsUnitsOwner.
+bool lds_owner_tiles(int32_t kind, int n) {
+  return (kind & kKindOwner) != 0 && n > 8 && n <= 16 && lds_waves(kind, n) == 16;
+}
+int lds_units_of(int32_t kind, int n) {
+  if (lds_owner_tiles(kind, n)) return kLdsUnitsOwner;
+  return n > 32 ? LdsClass<64, 8>::kU : LdsClass<32, 8>::kU;
+}
+size_t lds_bytes(int32_t kind, int n) { return static_cast<size_t>(n) * 64 * lds_units_of(kind, n) * 16; }
 
 // F::kClassMin: the smallest size class the fold's rank count may take.
 // One-pass all-gather (kKindFan | element bytes): op [lo, hi) of rank op.a
@@ -1290,19 +1328,38 @@ hipError_t launch_lds_cw(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s)
   // the staging area holds U units per lane of every rank, and the waves
   // cover every rank
   const int threads = lds_threads(kind, a.nranks);
-  if (a.nranks < 1 || a.nranks > C || LC::kU != lds_units_of(a.nranks) || threads > 64 * W ||
+  if (a.nranks < 1 || a.nranks > C || LC::kU != lds_units_of(kind, a.nranks) || threads > 64 * W ||
       LC::kRanksPerWave * (threads / 64) < a.nranks)
     return hipErrorInvalidValue;
+  const size_t lds = lds_bytes(kind, a.nranks);
   if (a.store_cold)
-    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsCold, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
+    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsCold, F>), grid, dim3(threads), lds, s, a);
   else
-    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsWarm, F>), grid, dim3(threads), lds_bytes(a.nranks), s, a);
+    AR_LAUNCH((onepass_lds<BF, EACH, C, W, kCpolLdsWarm, F>), grid, dim3(threads), lds, s, a);
+  return hipGetLastError();
+}
+// The reduce-scatter fold with its own tiles (16 waves; the store policy as
+// for the other folds).
+template <bool BF, bool EACH, class F>
+hipError_t launch_lds_owner(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  const int threads = lds_threads(kind, a.nranks);
+  if (!lds_owner_tiles(kind, a.nranks) || threads > 64 * 16 ||
+      LdsClass<16, 16>::kRanksPerWave * (threads / 64) < a.nranks)
+    return hipErrorInvalidValue;
+  const size_t lds = lds_bytes(kind, a.nranks);
+  if (a.store_cold)
+    AR_LAUNCH((onepass_lds<BF, EACH, 16, 16, kCpolLdsCold, OwnerTiles<F>>), grid, dim3(threads), lds, s, a);
+  else
+    AR_LAUNCH((onepass_lds<BF, EACH, 16, 16, kCpolLdsWarm, OwnerTiles<F>>), grid, dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 // 16-wave workgroups exist only where lds_waves picks them (up to 16 ranks,
 // fp32, or bf16 rounded once outside the balanced tree).
 template <bool BF, bool EACH, int NC, class F>
 hipError_t launch_lds_c(int32_t kind, dim3 grid, const KArgs &a, hipStream_t s) {
+  if constexpr (NC <= 16 && F::kClassMin == 16 && F::kHalves && !EACH && !(BF && F::kBalancedTree)) {
+    if (lds_owner_tiles(kind, a.nranks)) return launch_lds_owner<BF, EACH, F>(kind, grid, a, s);
+  }
   if constexpr (NC <= 16 && F::kClassMin <= 16 && !EACH && !(BF && F::kBalancedTree)) {
     if (lds_waves(kind, a.nranks) == 16) return launch_lds_cw<BF, EACH, NC, 16, F>(kind, grid, a, s);
   }
@@ -1499,8 +1556,8 @@ bool lds_staged(int32_t kind, int32_t nranks) {
 
 KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nranks) {
   if (lds_staged(kind, nranks))
-    return {lds_units_of(nranks), cold ? kCpolLdsCold : kCpolLdsWarm, lds_waves(kind, nranks),
-            static_cast<int>(lds_bytes(nranks))};
+    return {lds_units_of(kind, nranks), cold ? kCpolLdsCold : kCpolLdsWarm, lds_waves(kind, nranks),
+            static_cast<int>(lds_bytes(kind, nranks))};
   switch (kind & 0xF00) {
     case kKindFan:
       return {kFanUnits, kCpolFan, fan_threads(nranks) / 64,
@@ -1534,7 +1591,7 @@ int block_threads(int32_t kind, int32_t nranks) {
 
 int64_t tile_elems(int32_t kind, bool cold, int32_t nranks) {
   const int64_t u = cold ? kUnrollCold : kUnrollWarm;
-  if (lds_staged(kind, nranks)) return static_cast<int64_t>(64) * lds_units_of(nranks) * ((kind & 3) ? 8 : 4);
+  if (lds_staged(kind, nranks)) return static_cast<int64_t>(64) * lds_units_of(kind, nranks) * ((kind & 3) ? 8 : 4);
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * reduce_unit_elems(kind & 0xF) * reduce_unroll(kind & 0xF, cold);
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;

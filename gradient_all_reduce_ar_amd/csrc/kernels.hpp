@@ -141,6 +141,7 @@ constexpr int32_t kKindHier = ar::kKHier;
 constexpr int32_t kKindTree = ar::kKTree;
 constexpr int32_t kKindDTree = ar::kKDTree;
 constexpr int32_t kKindFan = ar::kKFan;
+constexpr int32_t kKindOwner = ar::kKOwner;
 
 // One op of a launch as the kernels read it (device table, 40 bytes).
 struct DevOp {

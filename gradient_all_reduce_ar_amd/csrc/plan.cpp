@@ -630,6 +630,7 @@ std::string lower_onepass(Plan &p) {
     // owned range (the tree fold, one op over everything, is cut into them;
     // its order does not depend on the range) and stores into that rank only
     for (Launch &L : p.launches) {
+      L.kind |= kKOwner;
       if ((L.kind & 0xF00) == kKTree) {
         L.ops.clear();
         for (int r = 0; r < p.nranks; ++r)

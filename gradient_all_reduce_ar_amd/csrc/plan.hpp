@@ -62,8 +62,10 @@ constexpr int32_t kKDTree = 0x600;
 //   kKFan | elem_bytes: one-pass all-gather, op [lo, hi) of rank a copied to
 //     every other rank.
 //   One-pass folds of a reduce-scatter plan store each op's result only
-//   into rank o (o = kLocNone: into every rank).
+//   into rank o (o = kLocNone: into every rank) and carry kKOwner, which
+//   selects the kernels' wider reduce-scatter tiles.
 constexpr int32_t kKFan = 0xB00;
+constexpr int32_t kKOwner = 0x1000;
 constexpr int32_t kFlagABf = 1, kFlagBBf = 2, kFlagOBf = 4, kFlagO2 = 8;
 //   Blockwise INT8 (kI8EF); op ranges count blocks, operands are ranks whose
 //   code slots (codes + scales in the plan's workspace) are meant:

@@ -414,7 +414,10 @@ int64_t ar_plan_transfers(const ar_plan_t *plan, int32_t *step, int32_t *src, in
  * use kinds 0x700 (encode rank a), 0x800 (o [and o2 with flag 8] = re-encoded
  * decode(a) + decode(b)), 0x900 (copy a's codes to o) and 0xA00 (decode a
  * into its buffer), and in one-pass mode the fold kinds with dtype code 3;
- * their ranges count blocks and locations name ranks' code slots.  Host only.
+ * their ranges count blocks and locations name ranks' code slots.  The
+ * one-pass all-gather is kind 0xB00 | element bytes (op range of rank a to
+ * every other rank); a one-pass reduce-scatter fold carries flag 0x1000
+ * (each op's result goes to rank o only).  Host only.
  */
 int32_t ar_plan_num_launches(const ar_plan_t *plan);
 ar_status_t ar_plan_launch_info(const ar_plan_t *plan, int32_t i, int32_t *kind, int32_t *nops);

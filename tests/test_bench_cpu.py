@@ -82,3 +82,9 @@ def test_kernel_labels():
         "onepass_lds<true, false, 16, 8, 18, TreeFold<8, true>>"
     assert bench.kernel_label(0x600 | 2, dict(lds, batch=8), 64) == \
         "onepass_lds<true, true, 64, 8, 18, DTreeFoldOp<64>>"
+    # reduce-scatter folds (flag 0x1000) of up to 16 ranks run their own tiles
+    own = {"units": 4, "batch": 16, "cpol": 16, "lds_bytes": 65536}
+    assert bench.kernel_label(0x1300, own, 16) == "onepass_lds<false, false, 16, 16, 16, OwnerTiles<RingFold>>"
+    assert bench.kernel_label(0x1500 | 1, dict(own, batch=8), 16) == \
+        "onepass_lds<true, false, 16, 8, 16, OwnerTiles<TreeFold<16, false>>>"
+    assert bench.kernel_label(0x1300, dict(lds, batch=8), 32) == "onepass_lds<false, false, 32, 8, 18, RingFold>"

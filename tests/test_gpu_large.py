@@ -150,6 +150,7 @@ def test_int8_ef_beyond_2_32_elements(mode):
     ("ring", 4, 1, "fp32", "onepass"),
     ("hierarchical", 4, 2, "bf16", "onepass"),
     ("rabenseifner", 4, 1, "fp32", "steps"),
+    ("ring", 9, 1, "bf16", "onepass"),  # the reduce-scatter's own tiles (9 to 16 ranks)
 ])
 def test_halves_beyond_2_32_elements(sched, n, g, dtype, mode):
     """Reduce-scatter, then all-gather, on buffers beyond 2^32 elements:

@@ -84,3 +84,58 @@ def test_grid_covers_every_tile():
         assert sh["grid_x"] == need
     finally:
         B.ar_plan_destroy(p)
+
+
+def _rs_shape(n, count, dtype, sched, g=1):
+    p = B.ar_plan_create_collective(n, g, count, dtype, sched, "reduce_scatter")
+    try:
+        B.ar_plan_set_exec(p, "onepass")
+        assert B.ar_plan_num_launches(p) == 1
+        kind, _ = B.ar_plan_launch_info(p, 0)
+        return kind, B.ar_plan_launch_shape(p, 0), B.ar_plan_launch_ops(p, 0)
+    finally:
+        B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("n,dtype,sched,g,waves,units", [
+    (16, "fp32", "ring", 1, 16, 4), (16, "bf16", "ring", 1, 16, 4), (16, "fp32", "hierarchical", 8, 16, 4),
+    (12, "bf16", "hierarchical", 3, 16, 4), (16, "fp32", "rabenseifner", 1, 16, 4), (9, "fp32", "ring", 1, 16, 4),
+    (16, "bf16_each", "ring", 1, 8, 2),      # 8-wave workgroups keep the class's tiles
+    (16, "bf16", "rabenseifner", 1, 8, 2),   # (the bf16 balanced tree: 8 waves)
+    (8, "fp32", "ring", 1, 16, 2), (4, "fp32", "ring", 1, 16, 2),  # 8 ranks and fewer too
+])
+def test_reduce_scatter_tiles(n, dtype, sched, g, waves, units):
+    """A one-pass reduce-scatter carries the owner flag; from 9 to 16 ranks
+    in 16-wave workgroups it stages 4 units per lane and rank (N * 4 KiB of
+    LDS).  Its stores take sc1, or nt + sc1 where its output (one rank's
+    size: the owned ranges) overflows the assumed 256 MiB cache.  The grid
+    covers every tile of the owned ranges."""
+    es = 4 if dtype == "fp32" else 2
+    for count, cold in (((1 << 20) // es, 0), ((512 << 20) // es, 1)):  # 1 or 512 MiB per rank
+        kind, sh, ops = _rs_shape(n, count, dtype, sched, g)
+        assert kind & B.KIND_OWNER
+        assert sh["units"] == units and sh["lds_bytes"] == n * units * 1024
+        assert sh["batch"] == waves and sh["threads"] == 64 * min(n, waves)
+        assert sh["cpol"] == (18 if cold else 16) and sh["cold"] == cold
+        tile = 64 * units * (4 if dtype == "fp32" else 8)
+        assert sh["grid_x"] == max((hi + tile - 1) // tile - lo // tile for lo, hi in zip(ops["lo"], ops["hi"]))
+
+
+def test_reduce_scatter_above_16_ranks_keeps_the_class_tiles():
+    """Above 16 ranks the reduce-scatter fold stages what the all-reduce's
+    size class does (2 units up to 32 ranks, 1 above)."""
+    for n, units in ((32, 2), (64, 1)):
+        kind, sh, _ = _rs_shape(n, 1 << 18, "fp32", "ring")
+        assert kind & B.KIND_OWNER
+        assert sh["units"] == units and sh["lds_bytes"] == n * units * 1024
+
+
+def test_allreduce_and_allgather_carry_no_owner_flag():
+    for coll in ("allreduce", "allgather"):
+        p = B.ar_plan_create_collective(16, 1, 1 << 18, "fp32", "ring", coll)
+        try:
+            B.ar_plan_set_exec(p, "onepass")
+            kind, _ = B.ar_plan_launch_info(p, 0)
+            assert not kind & B.KIND_OWNER
+        finally:
+            B.ar_plan_destroy(p)
