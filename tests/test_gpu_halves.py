@@ -25,7 +25,7 @@ from tests.gpu_util import bits_view, to_device, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("ring", n, 1) for n in (1, 2, 3, 4, 16, 64)] + \
+CASES = [("ring", n, 1) for n in (1, 2, 3, 4, 13, 16, 64)] + \
         [("hierarchical", n, g) for n, g in ((4, 4), (8, 1), (12, 3), (16, 8), (64, 8))] + \
         [("rabenseifner", n, 1) for n in (2, 16, 64)]
 
