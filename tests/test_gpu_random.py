@@ -79,3 +79,64 @@ def test_random_cases(batch):
                     assert np.array_equal(got[r], ref[r].view(bv)), what
         finally:
             B.ar_plan_destroy(p)
+
+
+HALF_SCHEDS = ["ring", "hierarchical", "rabenseifner"]
+
+
+def _draw_half(rng):
+    sched = HALF_SCHEDS[rng.integers(len(HALF_SCHEDS))]
+    if sched == "rabenseifner":
+        n, g = int(2 ** rng.integers(0, 7)), 1
+    else:
+        n = int(rng.integers(1, 65))
+        divisors = [d for d in range(1, n + 1) if n % d == 0]
+        g = int(divisors[rng.integers(len(divisors))]) if sched == "hierarchical" else 1
+    dtype = ["fp32", "bf16", "bf16_each"][rng.integers(3)]
+    mode = ["steps", "steps_unfused", "onepass"][rng.integers(3)]
+    coll = ["reduce_scatter", "allgather"][rng.integers(2)]
+    count = int(rng.integers(0, 300000 // max(1, n // 8)))
+    cache = [None, None, 1 << 16, 1 << 20][rng.integers(4)]
+    return sched, n, g, dtype, mode, coll, count, cache
+
+
+@pytest.mark.parametrize("batch", range(4))
+def test_random_halves(batch):
+    """Seeded draws of reduce-scatter and all-gather plans (schedule, ranks,
+    group, size, dtype, exec mode, assumed cache size) against the oracle's
+    halves, every element of every rank bit for bit (the one-pass
+    reduce-scatter: the oracle's values on the owned ranges, the inputs
+    elsewhere)."""
+    import torch
+
+    from tests.test_halves_cpu import onepass_reduce_scatter_expected
+
+    for k in range(20):
+        case = batch * 20 + k
+        rng = np.random.default_rng([11, case])
+        sched, n, g, dtype, mode, coll, count, cache = _draw_half(rng)
+        what = f"random halves case {case}: {coll} {sched} n={n} g={g} {dtype} {mode} count={count} cache={cache}"
+        print(what, flush=True)
+        sys.stdout.flush()
+        gen = "fp32" if dtype == "fp32" else "bf16"
+        xs = workloads.normal_inputs(n, count, seed=1000 + case, sigma=1.0, dtype=gen)
+        if coll == "allgather":
+            ref = oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)
+        elif mode == "onepass":
+            ref = onepass_reduce_scatter_expected(xs, dtype, sched, g)
+        else:
+            ref = oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g)
+        p = B.ar_plan_create_collective(n, g, count, dtype, sched, coll)
+        try:
+            B.ar_plan_set_exec(p, mode)
+            if cache is not None:
+                B.ar_plan_set_cache_bytes(p, cache)
+            bufs = to_device(xs, dtype)
+            (B.ar_reduce_scatter if coll == "reduce_scatter" else B.ar_allgather)(p, bufs, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+        finally:
+            B.ar_plan_destroy(p)
+        got = to_host_bits(bufs, dtype)
+        bv = bits_view(dtype)
+        for r in range(n):
+            assert np.array_equal(got[r], ref[r].view(bv)), f"{what}: rank {r}"

@@ -192,3 +192,42 @@ def test_large_halves_describe_but_do_not_run():
             assert ei.value.status == B.AR_ERR_UNSUPPORTED
         finally:
             B.ar_plan_destroy(p)
+
+
+def test_random_halves_launch_lists():
+    """Seeded draws (schedule, ranks up to 64, group, size, dtype, exec mode,
+    assumed cache size, collective): the launch list, run by the interpreter,
+    gives the oracle's half bit for bit in every element."""
+    scheds = ["ring", "hierarchical", "rabenseifner"]
+    for case in range(60):
+        rng = np.random.default_rng([13, case])
+        sched = scheds[rng.integers(3)]
+        if sched == "rabenseifner":
+            n, g = int(2 ** rng.integers(0, 7)), 1
+        else:
+            n = int(rng.integers(1, 65))
+            divisors = [d for d in range(1, n + 1) if n % d == 0]
+            g = int(divisors[rng.integers(len(divisors))]) if sched == "hierarchical" else 1
+        dtype = ["fp32", "bf16", "bf16_each"][rng.integers(3)]
+        mode = ["steps", "steps_unfused", "onepass"][rng.integers(3)]
+        coll = ["reduce_scatter", "allgather"][rng.integers(2)]
+        count = int(rng.integers(0, 3000))
+        cache = [None, 1 << 10, 1 << 14][rng.integers(3)]
+        what = f"case {case}: {coll} {sched} n={n} g={g} {dtype} {mode} count={count} cache={cache}"
+        xs = _inputs(n, count, dtype, seed=2000 + case)
+        if coll == "allgather":
+            want = oracle.allgather([x.copy() for x in xs], dtype, sched, group_size=g)
+        elif mode == "onepass":
+            want = onepass_reduce_scatter_expected(xs, dtype, sched, g)
+        else:
+            want = oracle.reduce_scatter([x.copy() for x in xs], dtype, sched, group_size=g)
+        p = _coll_plan(n, g, count, dtype, sched, coll)
+        try:
+            B.ar_plan_set_exec(p, mode)
+            if cache is not None:
+                B.ar_plan_set_cache_bytes(p, cache)
+            got = plan_interp.run(p, [x.copy() for x in xs], dtype, g)
+        finally:
+            B.ar_plan_destroy(p)
+        for r in range(n):
+            np.testing.assert_array_equal(_bits(got[r], dtype), _bits(want[r], dtype), err_msg=f"{what} r={r}")
