@@ -1257,15 +1257,27 @@ size_t lds_bytes(int32_t kind, int n) { return static_cast<size_t>(n) * 64 * lds
 // F::kClassMin: the smallest size class the fold's rank count may take.
 // One-pass all-gather (kKindFan | element bytes): op [lo, hi) of rank op.a
 // goes to every other rank.  A workgroup of W = min(N, kFanWaves) waves
-// takes a tile of W * kFanUnits KiB: wave w loads its kFanUnits 16-byte units
-// per lane of the tile from rank a into LDS, and after a barrier each wave
-// stores the whole tile into its own ranks w, w + W, ... except a.  The owner
-// is read once and every wave stores into N / W buffers.  Tiles that the
-// op's range cuts copy element by element.  CP: the store policy
-// (kCpolFan).
+// loads a tile of rank a into LDS, and after a barrier each wave stores the
+// whole tile into its own ranks w, w + W, ... except a.  The owner is read
+// once and every wave stores into N / W buffers.  Tiles that the op's range
+// cuts copy element by element.  CP: the store policy (kCpolFan).
+// The tile is 4 KiB up to 16 ranks (kFanSmallUnits, one wave's store per
+// rank is 4 KiB) and W * kFanUnits KiB above (wave w loads its kFanUnits
+// units per lane).  Measured on MI355X, ring fp32: 4 KiB tiles against
+// 32 KiB took 514 against 618 us at 16 x 192 MiB (bf16 519 against 622),
+// 258 against 314 at 8 x 192 MiB, 132 against 140 at 4 x 192 MiB and 88
+// against 99 at 16 x 32 MiB; 2, 1 and 8 KiB were slower than 4 at 16 ranks
+// (604, 823 and 602 us), and so were 8 or 4 waves (595 and 607).  At 32 and
+// 64 ranks 4 KiB was 2-5% slower than 32 KiB.
 constexpr int kFanUnits = AR_LDS_UNITS;
 constexpr int kFanWaves = 16;
+constexpr int kFanSmallUnits = 256;
 constexpr int kCpolFan = AR_CPOL_LDS_WARM;
+static_assert(kFanSmallUnits <= kFanWaves * kFanUnits * 64, "the small tile fits the stage");
+// 16-byte units of a fan-out tile at n ranks with `waves` waves per workgroup.
+__host__ __device__ constexpr int fan_tile_units(int n, int waves) {
+  return n <= 16 ? kFanSmallUnits : waves * kFanUnits * 64;
+}
 template <int ES, int CP>
 __global__ __launch_bounds__(64 * kFanWaves) void onepass_fan(KArgs args) {
   constexpr int kE = 16 / ES;  // elements per unit
@@ -1275,7 +1287,7 @@ __global__ __launch_bounds__(64 * kFanWaves) void onepass_fan(KArgs args) {
   const int waves = static_cast<int>(blockDim.x >> 6);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = static_cast<int>(threadIdx.x & 63);
-  const int units = waves * kFanUnits * 64;  // 16-byte units per tile
+  const int units = fan_tile_units(n, waves);  // 16-byte units per tile
   const int64_t tile = static_cast<int64_t>(units) * kE;
   const BlockCoord bc = block_coord();
   const DevOp op = args.ops[bc.op];
@@ -1285,10 +1297,15 @@ __global__ __launch_bounds__(64 * kFanWaves) void onepass_fan(KArgs args) {
     const int64_t base = t * tile;
     if (base >= op.lo && base + tile <= op.hi) {
       const char *p = src + base * ES;
+      if (n <= 16) {
+        for (int q = static_cast<int>(threadIdx.x); q < units; q += static_cast<int>(blockDim.x))
+          stage[q] = ld<u32x4>(p + q * 16);
+      } else {
 #pragma unroll
-      for (int u = 0; u < kFanUnits; ++u) {
-        const int q = (wave * kFanUnits + u) * 64 + lane;
-        stage[q] = ld<u32x4>(p + q * 16);
+        for (int u = 0; u < kFanUnits; ++u) {
+          const int q = (wave * kFanUnits + u) * 64 + lane;
+          stage[q] = ld<u32x4>(p + q * 16);
+        }
       }
       __syncthreads();
       for (int r = wave; r < n; r += waves) {
@@ -1313,8 +1330,7 @@ int fan_threads(int32_t nranks) { return 64 * std::min(std::max(nranks, 1), kFan
 
 // Measured at 16 ranks (32 and 192 MiB per rank): sc1 stores were 3% faster
 // than nt + sc1 and 1-8% faster than plain nt at both sizes, so the fan-out
-// takes them whatever its size; 1 or 4 units per lane and 8 waves per
-// workgroup were within 2%.
+// takes them whatever its size.
 template <int ES>
 hipError_t launch_fan(dim3 grid, const KArgs &a, hipStream_t s) {
   AR_LAUNCH((onepass_fan<ES, kCpolFan>), grid, dim3(fan_threads(a.nranks)), 0, s, a);
@@ -1559,8 +1575,8 @@ KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nran
     return {lds_units_of(kind, nranks), cold ? kCpolLdsCold : kCpolLdsWarm, lds_waves(kind, nranks),
             static_cast<int>(lds_bytes(kind, nranks))};
   switch (kind & 0xF00) {
-    case kKindFan:
-      return {kFanUnits, kCpolFan, fan_threads(nranks) / 64,
+    case kKindFan:  // units: the tile's 16-byte units per lane of one wave
+      return {fan_tile_units(nranks, fan_threads(nranks) / 64) / 64, kCpolFan, fan_threads(nranks) / 64,
               kFanWaves * kFanUnits * 1024};  // the stage is static: its full size
     case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0, 0};
     case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0, 0};
@@ -1595,7 +1611,8 @@ int64_t tile_elems(int32_t kind, bool cold, int32_t nranks) {
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * reduce_unit_elems(kind & 0xF) * reduce_unroll(kind & 0xF, cold);
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
-    case kKindFan: return static_cast<int64_t>(fan_threads(nranks)) * kFanUnits * (16 / (kind & 0xFF));
+    case kKindFan:
+      return static_cast<int64_t>(fan_tile_units(nranks, fan_threads(nranks) / 64)) * (16 / (kind & 0xFF));
     case kKindTree: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kTreeUnrollBF16 : kTreeUnrollF32);
     default: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }

@@ -433,7 +433,10 @@ ar_status_t ar_plan_launch_ops(const ar_plan_t *plan, int32_t i, int64_t *lo, in
  * workgroups along the tiles, the threads per workgroup and the dynamic LDS
  * bytes per workgroup (nonzero only for the LDS-staged one-pass folds, which
  * stage a tile of every rank in LDS before folding it; INT8 kernels: units,
- * cpol, batch and LDS bytes 0).  Any out pointer may be NULL.  Host only. */
+ * cpol, batch and LDS bytes 0).  The one-pass all-gather reports its tile's
+ * 16-byte units per lane of one wave (each wave stores the whole tile into
+ * its ranks), its waves per workgroup as batch and its static LDS stage.
+ * Any out pointer may be NULL.  Host only. */
 ar_status_t ar_plan_launch_shape(const ar_plan_t *plan, int32_t i, int32_t *cold, int32_t *units, int32_t *cpol,
                                  int32_t *batch, uint32_t *grid_x, int32_t *threads, int32_t *lds_bytes);
 /* fp32 scratch addressing of launch i: element e of slot s is float

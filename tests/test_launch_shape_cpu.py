@@ -139,3 +139,28 @@ def test_allreduce_and_allgather_carry_no_owner_flag():
             assert not kind & B.KIND_OWNER
         finally:
             B.ar_plan_destroy(p)
+
+
+@pytest.mark.parametrize("n,dtype,waves,units", [
+    (16, "fp32", 16, 4), (16, "bf16", 16, 4), (8, "fp32", 8, 4), (2, "bf16", 2, 4),  # 4 KiB tiles
+    (32, "fp32", 16, 32), (64, "bf16", 16, 32),                                       # 32 KiB tiles
+])
+def test_allgather_fan_tiles(n, dtype, waves, units):
+    """The one-pass all-gather stages 4 KiB of the owner per workgroup up to
+    16 ranks and 32 KiB above; the grid covers every tile of the owned
+    ranges."""
+    es = 4 if dtype == "fp32" else 2
+    count = (3 << 20) // es + 5
+    p = B.ar_plan_create_collective(n, 1, count, dtype, "ring", "allgather")
+    try:
+        B.ar_plan_set_exec(p, "onepass")
+        kind, _ = B.ar_plan_launch_info(p, 0)
+        assert kind == B.KIND_FAN | es
+        sh = B.ar_plan_launch_shape(p, 0)
+        ops = B.ar_plan_launch_ops(p, 0)
+    finally:
+        B.ar_plan_destroy(p)
+    assert sh["units"] == units and sh["batch"] == waves and sh["threads"] == 64 * waves
+    assert sh["cpol"] == 16 and sh["lds_bytes"] == 32768
+    tile = units * 64 * (16 // es)
+    assert sh["grid_x"] == max((hi + tile - 1) // tile - lo // tile for lo, hi in zip(ops["lo"], ops["hi"]))
