@@ -1268,7 +1268,7 @@ size_t lds_bytes(int32_t kind, int n) { return static_cast<size_t>(n) * 64 * lds
 // 258 against 314 at 8 x 192 MiB, 132 against 140 at 4 x 192 MiB and 88
 // against 99 at 16 x 32 MiB; 2, 1 and 8 KiB were slower than 4 at 16 ranks
 // (604, 823 and 602 us), and so were 8 or 4 waves (595 and 607).  At 32 and
-// 64 ranks 4 KiB was 2-5% slower than 32 KiB.
+// 64 ranks 4 KiB was 2-5% slower than 32 KiB, 8 and 16 KiB within 2%.
 constexpr int kFanUnits = AR_LDS_UNITS;
 constexpr int kFanWaves = 16;
 constexpr int kFanSmallUnits = 256;
