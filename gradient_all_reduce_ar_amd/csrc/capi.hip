@@ -205,9 +205,13 @@ void lower_launches(ar_plan_t *pl) {
     const int64_t threads = quant ? ar_dev::q_block_threads(L.kind) : ar_dev::block_threads(L.kind, pl->p.nranks);
     // the LDS-staged folds and the one-pass all-gather walk their op's tiles
     // with the grid's stride, so a grid capped at the dispatch limit still
-    // covers every tile
-    if (!quant && (ar_dev::lds_staged(L.kind, pl->p.nranks) || (L.kind & 0xF00) == ar::kKFan))
-      gx = std::min<int64_t>(gx, 0x7fffffff / threads);
+    // covers every tile; the all-gather's grid is its tiles times its
+    // destination groups, and stays a multiple of them
+    const bool fan = !quant && (L.kind & 0xF00) == ar::kKFan;
+    const int64_t groups = fan ? ar_dev::fan_groups(pl->p.nranks) : 1;
+    gx *= groups;
+    if (!quant && (ar_dev::lds_staged(L.kind, pl->p.nranks) || fan))
+      gx = std::min<int64_t>(gx, 0x7fffffff / threads / groups * groups);
     if (gx * threads > 0x7fffffff || static_cast<int64_t>(L.ops.size()) > ar::kMaxLaunchOps)
       pl->launch_err = "op too large for one launch grid";
     pl->grid_x.push_back(static_cast<uint32_t>(std::min<int64_t>(gx, 0x7fffffff)));

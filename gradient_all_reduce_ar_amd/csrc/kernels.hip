@@ -1257,27 +1257,26 @@ size_t lds_bytes(int32_t kind, int n) { return static_cast<size_t>(n) * 64 * lds
 // F::kClassMin: the smallest size class the fold's rank count may take.
 // One-pass all-gather (kKindFan | element bytes): op [lo, hi) of rank op.a
 // goes to every other rank.  A workgroup of W = min(N, kFanWaves) waves
-// loads a tile of rank a into LDS, and after a barrier each wave stores the
-// whole tile into its own ranks w, w + W, ... except a.  The owner is read
-// once and every wave stores into N / W buffers.  Tiles that the op's range
-// cuts copy element by element.  CP: the store policy (kCpolFan).
-// The tile is 4 KiB up to 16 ranks (kFanSmallUnits, one wave's store per
-// rank is 4 KiB) and W * kFanUnits KiB above (wave w loads its kFanUnits
-// units per lane).  Measured on MI355X, ring fp32: 4 KiB tiles against
-// 32 KiB took 514 against 618 us at 16 x 192 MiB (bf16 519 against 622),
-// 258 against 314 at 8 x 192 MiB, 132 against 140 at 4 x 192 MiB and 88
-// against 99 at 16 x 32 MiB; 2, 1 and 8 KiB were slower than 4 at 16 ranks
-// (604, 823 and 602 us), and so were 8 or 4 waves (595 and 607).  At 32 and
-// 64 ranks 4 KiB was 2-5% slower than 32 KiB, 8 and 16 KiB within 2%.
+// loads a 4 KiB tile of rank a into LDS, and after a barrier each wave
+// stores the whole tile into one rank other than a.  Above W ranks the
+// destinations are split into G = ceil(N / W) groups of W, and G
+// workgroups take each tile, one per group (the owner's tile is read G
+// times).  Tiles that the op's range cuts copy element by element.  CP: the
+// store policy (kCpolFan).
+// Measured on MI355X, ring fp32, against 32 KiB tiles each wave stored into
+// N / W ranks: 514 against 618 us at 16 x 192 MiB (bf16 519 against 622),
+// 258 against 314 at 8 x 192 MiB, 132 against 140 at 4 x 192 MiB, 88
+// against 99 at 16 x 32 MiB, 559 against 616 at 32 x 96 MiB, and within
+// 1% at 64 x 48 MiB (605 against 598; without the groups, 4 KiB tiles were
+// 2-5% slower there).  2, 1 and 8 KiB tiles were slower than 4 at 16 ranks
+// (604, 823 and 602 us), and so were 8 or 4 waves (595 and 607).
 constexpr int kFanUnits = AR_LDS_UNITS;
 constexpr int kFanWaves = 16;
-constexpr int kFanSmallUnits = 256;
+constexpr int kFanTileUnits = 256;  // 16-byte units per tile
 constexpr int kCpolFan = AR_CPOL_LDS_WARM;
-static_assert(kFanSmallUnits <= kFanWaves * kFanUnits * 64, "the small tile fits the stage");
-// 16-byte units of a fan-out tile at n ranks with `waves` waves per workgroup.
-__host__ __device__ constexpr int fan_tile_units(int n, int waves) {
-  return n <= 16 ? kFanSmallUnits : waves * kFanUnits * 64;
-}
+static_assert(kFanTileUnits <= kFanWaves * kFanUnits * 64, "the tile fits the stage");
+// Workgroups per tile: one per group of `waves` destination ranks.
+__host__ __device__ constexpr int fan_groups_of(int n, int waves) { return n > waves ? (n + waves - 1) / waves : 1; }
 template <int ES, int CP>
 __global__ __launch_bounds__(64 * kFanWaves) void onepass_fan(KArgs args) {
   constexpr int kE = 16 / ES;  // elements per unit
@@ -1287,39 +1286,39 @@ __global__ __launch_bounds__(64 * kFanWaves) void onepass_fan(KArgs args) {
   const int waves = static_cast<int>(blockDim.x >> 6);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = static_cast<int>(threadIdx.x & 63);
-  const int units = fan_tile_units(n, waves);  // 16-byte units per tile
-  const int64_t tile = static_cast<int64_t>(units) * kE;
+  constexpr int units = kFanTileUnits;
+  constexpr int64_t tile = static_cast<int64_t>(units) * kE;
   const BlockCoord bc = block_coord();
+  // workgroup x takes tile x / G of the op for destination group x mod G
+  // (the grid is G times the tiles)
+  // (32-bit: the grid holds fewer than 2^31 workgroups)
+  const uint32_t groups = static_cast<uint32_t>(fan_groups_of(n, waves));
+  const uint32_t x = static_cast<uint32_t>(bc.tile), gx = static_cast<uint32_t>(bc.stride);
+  const int g = groups > 1 ? static_cast<int>(x % groups) : 0;
+  const int64_t t0 = groups > 1 ? x / groups : x, stride = groups > 1 ? gx / groups : gx;
+  const int r_lo = g * waves, r_hi = r_lo + waves < n ? r_lo + waves : n;
   const DevOp op = args.ops[bc.op];
   const char *src = static_cast<const char *>(args.rank[op.a]);
   const int64_t t_end = (op.hi + tile - 1) / tile;
-  for (int64_t t = op.lo / tile + bc.tile; t < t_end; t += bc.stride) {
+  for (int64_t t = op.lo / tile + t0; t < t_end; t += stride) {
     const int64_t base = t * tile;
     if (base >= op.lo && base + tile <= op.hi) {
       const char *p = src + base * ES;
-      if (n <= 16) {
-        for (int q = static_cast<int>(threadIdx.x); q < units; q += static_cast<int>(blockDim.x))
-          stage[q] = ld<u32x4>(p + q * 16);
-      } else {
-#pragma unroll
-        for (int u = 0; u < kFanUnits; ++u) {
-          const int q = (wave * kFanUnits + u) * 64 + lane;
-          stage[q] = ld<u32x4>(p + q * 16);
-        }
-      }
+      for (int q = static_cast<int>(threadIdx.x); q < units; q += static_cast<int>(blockDim.x))
+        stage[q] = ld<u32x4>(p + q * 16);
       __syncthreads();
-      for (int r = wave; r < n; r += waves) {
+      for (int r = r_lo + wave; r < r_hi; r += waves) {
         if (r == op.a) continue;
         char *d = static_cast<char *>(args.rank[r]) + base * ES;
         for (int q = lane; q < units; q += 64) st_cp<CP, u32x4>(d, static_cast<uint32_t>(q) * 16, stage[q]);
       }
       // the next tile's loads overwrite the stage this tile's stores read
-      if (t + bc.stride < t_end) __syncthreads();
+      if (t + stride < t_end) __syncthreads();
     } else {
       const int64_t e0 = base > op.lo ? base : op.lo, e1 = base + tile < op.hi ? base + tile : op.hi;
       for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
         const E x = *reinterpret_cast<const E *>(src + e * ES);
-        for (int r = 0; r < n; ++r)
+        for (int r = r_lo; r < r_hi; ++r)
           if (r != op.a) *reinterpret_cast<E *>(static_cast<char *>(args.rank[r]) + e * ES) = x;
       }
     }
@@ -1576,7 +1575,7 @@ KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nran
             static_cast<int>(lds_bytes(kind, nranks))};
   switch (kind & 0xF00) {
     case kKindFan:  // units: the tile's 16-byte units per lane of one wave
-      return {fan_tile_units(nranks, fan_threads(nranks) / 64) / 64, kCpolFan, fan_threads(nranks) / 64,
+      return {kFanTileUnits / 64, kCpolFan, fan_threads(nranks) / 64,
               kFanWaves * kFanUnits * 1024};  // the stage is static: its full size
     case kKindReduce: return {reduce_unroll(kind & 0xF, cold), out_scratch ? kCpolScratch : kCpolRank, 0, 0};
     case kKindCopy: return {cold ? kUnrollCold : kUnrollWarm, kCpolRank, 0, 0};
@@ -1598,6 +1597,8 @@ KernelShape kernel_shape(int32_t kind, bool cold, bool out_scratch, int32_t nran
 
 dim3 grid_for(uint32_t tiles, uint32_t nops) { return dim3(tiles, nops); }
 
+int fan_groups(int32_t nranks) { return fan_groups_of(nranks, fan_threads(nranks) / 64); }
+
 int block_threads(int32_t kind, int32_t nranks) {
   const int32_t fam = kind & 0xF00;
   if (lds_staged(kind, nranks)) return lds_threads(kind, nranks);
@@ -1611,8 +1612,7 @@ int64_t tile_elems(int32_t kind, bool cold, int32_t nranks) {
   switch (kind & 0xF00) {
     case kKindReduce: return static_cast<int64_t>(kBlock) * reduce_unit_elems(kind & 0xF) * reduce_unroll(kind & 0xF, cold);
     case kKindCopy: return static_cast<int64_t>(kBlock) * (16 / (kind & 0xFF)) * u;
-    case kKindFan:
-      return static_cast<int64_t>(fan_tile_units(nranks, fan_threads(nranks) / 64)) * (16 / (kind & 0xFF));
+    case kKindFan: return static_cast<int64_t>(kFanTileUnits) * (16 / (kind & 0xFF));
     case kKindTree: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kTreeUnrollBF16 : kTreeUnrollF32);
     default: return static_cast<int64_t>(kOPB) * 4 * ((kind & 3) ? kOnePassUnrollBF16 : kOnePassUnrollF32);
   }

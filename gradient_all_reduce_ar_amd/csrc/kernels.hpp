@@ -195,6 +195,11 @@ int64_t tile_elems(int32_t kind, bool cold, int32_t nranks);
 // Threads per workgroup of a kernel kind.
 int block_threads(int32_t kind, int32_t nranks);
 
+// Workgroups per tile of a one-pass all-gather (kKindFan) at nranks: each
+// stores the tile into one group of up to 16 ranks, one rank per wave, so
+// its launch grid is that many times its tiles.
+int fan_groups(int32_t nranks);
+
 // Tiles each block of a launch walks (the kernels loop over an op's tiles
 // with the grid's stride): more than one for the one-pass ring and
 // hierarchical folds when a tile of all ranks is little data (bf16 at 2 or 4

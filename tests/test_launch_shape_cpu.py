@@ -141,14 +141,15 @@ def test_allreduce_and_allgather_carry_no_owner_flag():
             B.ar_plan_destroy(p)
 
 
-@pytest.mark.parametrize("n,dtype,waves,units", [
-    (16, "fp32", 16, 4), (16, "bf16", 16, 4), (8, "fp32", 8, 4), (2, "bf16", 2, 4),  # 4 KiB tiles
-    (32, "fp32", 16, 32), (64, "bf16", 16, 32),                                       # 32 KiB tiles
+@pytest.mark.parametrize("n,dtype,waves,groups", [
+    (16, "fp32", 16, 1), (16, "bf16", 16, 1), (8, "fp32", 8, 1), (2, "bf16", 2, 1),
+    (17, "fp32", 16, 2), (32, "fp32", 16, 2), (48, "bf16", 16, 3), (64, "bf16", 16, 4),
 ])
-def test_allgather_fan_tiles(n, dtype, waves, units):
-    """The one-pass all-gather stages 4 KiB of the owner per workgroup up to
-    16 ranks and 32 KiB above; the grid covers every tile of the owned
-    ranges."""
+def test_allgather_fan_tiles(n, dtype, waves, groups):
+    """The one-pass all-gather stages 4 KiB of the owner per workgroup, each
+    wave storing it into one rank; above 16 ranks the destinations split into
+    groups of 16, one workgroup per group and tile, so the grid covers every
+    tile of the owned ranges that many times."""
     es = 4 if dtype == "fp32" else 2
     count = (3 << 20) // es + 5
     p = B.ar_plan_create_collective(n, 1, count, dtype, "ring", "allgather")
@@ -160,7 +161,8 @@ def test_allgather_fan_tiles(n, dtype, waves, units):
         ops = B.ar_plan_launch_ops(p, 0)
     finally:
         B.ar_plan_destroy(p)
-    assert sh["units"] == units and sh["batch"] == waves and sh["threads"] == 64 * waves
+    assert sh["units"] == 4 and sh["batch"] == waves and sh["threads"] == 64 * waves
     assert sh["cpol"] == 16 and sh["lds_bytes"] == 32768
-    tile = units * 64 * (16 // es)
-    assert sh["grid_x"] == max((hi + tile - 1) // tile - lo // tile for lo, hi in zip(ops["lo"], ops["hi"]))
+    tile = 4 * 64 * (16 // es)
+    tiles = max((hi + tile - 1) // tile - lo // tile for lo, hi in zip(ops["lo"], ops["hi"]))
+    assert sh["grid_x"] == tiles * groups
